@@ -1,0 +1,166 @@
+/*
+ * eblc.h -- C ABI of libeblc.so, an error-bounded lossy compressor for float32 fields on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The interface is shaped like the provider ABI described on the "DevitoComp provider
+ * interface" page (devitocodes.com, DevitoPRO extension docs): a plan is created once with
+ * the tensor's dims/strides and an options string carrying the error tolerance; the plan
+ * reports limits (maximum compressed size, payload alignment, sidecar size); compress and
+ * decompress run on a caller-supplied stream.  The names are this library's own.
+ *
+ * Method (one fixed chain; "Pipeline Specialization Internals", FZGPUModules site):
+ *   linear quantization with step 2*eb (inv2eb = 1/(2*eb)) checked against the exact
+ *   reconstruction -> 1-D Lorenzo deltas reset at every block -> zigzag -> one bit width per
+ *   32-value segment and fixed-length bit packing -> outliers (values that cannot be coded)
+ *   escape to a side list of (u32 index, f32 bits) ordered by index -> an exclusive scan of
+ *   the variable segment sizes and compaction into one self-describing stream.  Decompress is
+ *   the exact inverse.
+ *
+ * Stream (little-endian, every section 16-byte aligned, pad bytes zero):
+ *   [0,128)            header (magic "EBLC", version 1, mode, rank, dims, n, eb, step,
+ *                      outlier count, section offsets, total length)
+ *   [128, +nseg)       one width byte per 32-value segment (nseg = ceil(n/32))
+ *   payload            sum(widths) little-endian u32 words
+ *   outlier indices    m x u32, strictly ascending
+ *   outlier values     m x u32 (raw float32 bits)
+ * A RAW stream (bound unusable or 0, more outliers than side_max, or a coded stream that
+ * would be larger than the input) holds the header followed by the input bytes.
+ *
+ * Threading: a plan is used by one host thread at a time; distinct plans may run
+ * concurrently on distinct streams.  All device pointers must come from hipMalloc (or
+ * torch) on the plan's device and be 16-byte aligned.
+ */
+#ifndef EBLC_H
+#define EBLC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ABI version; a header and a library of different versions must not be mixed ("Provider
+ * layout": a private header implements the same ABI version as the public one). */
+#define EBLC_ABI_VERSION 1
+
+typedef struct eblc_plan eblc_plan_t; /* opaque; owned by the library */
+
+/* Status codes.  UNSUPPORTED is the provider interface's answer for an execution kind or a
+ * tensor layout the provider does not handle ("Provider layout": providers may support any
+ * subset of the execution kinds). */
+typedef enum {
+    EBLC_OK = 0,
+    EBLC_UNSUPPORTED = 1,      /* execution kind, dtype, rank or strides not handled */
+    EBLC_INVALID_ARGUMENT = 2, /* NULL/misaligned pointer, bad option, n out of range */
+    EBLC_CAPACITY = 3,         /* out_capacity smaller than the stream; required size returned */
+    EBLC_CORRUPT_STREAM = 4,   /* stream header or sections inconsistent with the plan */
+    EBLC_DEVICE_ERROR = 5,     /* a HIP runtime call failed */
+    EBLC_OUT_OF_MEMORY = 6     /* workspace allocation failed at plan creation */
+} eblc_status;
+
+/* Where the pointers live ("Provider layout": HOST uses host pointers and a thread count and
+ * no stream; CUDA/HIP use device-accessible pointers and an optional native stream).  This
+ * provider implements HIP only; HOST and CUDA return EBLC_UNSUPPORTED. */
+typedef enum {
+    EBLC_EXECUTION_HOST = 0,
+    EBLC_EXECUTION_CUDA = 1,
+    EBLC_EXECUTION_HIP = 2
+} eblc_execution_kind;
+
+typedef struct {
+    eblc_execution_kind kind;
+    int device;  /* HIP device ordinal the plan's workspace lives on */
+    int threads; /* ignored for HIP */
+} eblc_execution_t;
+
+/* Limits ("Provider layout": the provider reports its payload alignment, a nonzero power of
+ * two; "Dummy provider": the maximum compressed size is reported by the provider). */
+typedef struct {
+    size_t max_compressed_bytes; /* 128 + align16(4 n): a RAW stream, the largest possible */
+    size_t payload_alignment;    /* 16 */
+    size_t sidecar_bytes;        /* 0: the stream is self-describing */
+    size_t sidecar_alignment;    /* 1 */
+} eblc_limits_t;
+
+typedef enum { EBLC_FLOAT32 = 0 } eblc_dtype;
+
+/* Returns EBLC_ABI_VERSION of the library. */
+int eblc_abi_version(void);
+
+/* Create a plan.
+ *   exec     execution descriptor; kind must be EBLC_EXECUTION_HIP (else UNSUPPORTED).
+ *   dtype    EBLC_FLOAT32 (else UNSUPPORTED).
+ *   rank     1..4; dims[rank] > 0, slowest to fastest ("Provider layout": dimensions and
+ *            strides in slowest-to-fastest order, strides in elements).  n = prod(dims)
+ *            must be below 2^32 (outlier indices are u32).
+ *   strides  NULL, or exactly the row-major contiguous strides (else UNSUPPORTED).
+ *   options  NULL or "" -> relative error 1e-4 (the default bound named in "Priming");
+ *            a bare decimal -> relative error (what DevitoPRO passes, "Provider layout");
+ *            else ';'-separated key=value pairs:
+ *              rel=<eps> | abs=<eb>   exactly one; finite, >= 0; 0 means lossless (RAW)
+ *              block=<B>              Lorenzo reset period: 32, 64, ..., 2048 (power of two);
+ *                                     default 256
+ *              outlier_log2=<T>       codes with |q| >= 2^T escape; 1..30; default 30
+ *              side_max=<m>           largest outlier list; 0..n; default min(n, 2^23)
+ *            Unknown keys, repeated keys, NaN or negative values -> INVALID_ARGUMENT.
+ *   plan_out receives the plan.  The plan allocates its whole workspace here (about 4 n +
+ *            n/8 bytes plus small arrays) and nothing per call.
+ * The relative error is eps * (max - min) over the finite input values, resolved on the
+ * device at every compress call ("Priming": the quantizer's value-range scan). */
+eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int rank,
+                             const int64_t *dims, const int64_t *strides, const char *options,
+                             eblc_plan_t **plan_out);
+
+/* Fill *out with the plan's limits.  INVALID_ARGUMENT on NULL. */
+eblc_status eblc_plan_limits(const eblc_plan_t *plan, eblc_limits_t *out);
+
+/* 128 + align16(4 n); 0 for a NULL plan. */
+size_t eblc_max_compressed_bytes(const eblc_plan_t *plan);
+
+/* 16; 0 for a NULL plan. */
+size_t eblc_payload_alignment(const eblc_plan_t *plan);
+
+/* Compress n floats at device pointer `in` into device buffer `out` of out_capacity bytes,
+ * enqueued on `stream` (a hipStream_t; NULL = default stream).  The call waits for its own
+ * work once, to return *compressed_bytes (like the fused chunk encoder that syncs before
+ * returning the archive length, "nvrtc_chunk_fusion.h File Reference",
+ * launchGenericChunkFusion).  Returns OK with *compressed_bytes set, or CAPACITY with
+ * *compressed_bytes = the required size (then `out` holds no valid stream; nothing is
+ * written at or past out_capacity).  `in` and `out` must not overlap.  sidecar must be NULL.
+ * Output is deterministic: the same input and plan give the same bytes. */
+eblc_status eblc_compress(eblc_plan_t *plan, const float *in, void *out, size_t out_capacity,
+                          size_t *compressed_bytes, void *sidecar, void *stream);
+
+/* Decompress a stream of compressed_bytes at device pointer `in` into n floats at `out`,
+ * enqueued on `stream`; returns without waiting ("Provider layout": device work may remain
+ * queued on the supplied stream).  The host checks 128 + align16(nseg) <= compressed_bytes
+ * <= max_compressed_bytes (else CORRUPT_STREAM at once).  Header or section problems found
+ * on the device (wrong magic/version/dims/n/offsets, widths above 32, outlier indices not
+ * strictly ascending below n) set a sticky CORRUPT_STREAM that eblc_plan_status returns;
+ * the contents of `out` are then unspecified.  sidecar must be NULL. */
+eblc_status eblc_decompress(eblc_plan_t *plan, const void *in, size_t compressed_bytes,
+                            const void *sidecar, float *out, void *stream);
+
+/* Wait for `stream`, then return and clear the plan's sticky device error (OK if none). */
+eblc_status eblc_plan_status(eblc_plan_t *plan, void *stream);
+
+/* Wait for the device, then free the plan and its workspace.  NULL is a no-op. */
+void eblc_plan_destroy(eblc_plan_t *plan);
+
+/* Static string naming a status. */
+const char *eblc_status_string(eblc_status s);
+
+/* ---- measurement hooks (not part of the provider shape) --------------------------------
+ * With profiling on, every compress/decompress records a HIP event pair around each of its
+ * kernel launches on the caller's stream.  eblc_plan_kernel_times waits for the last call's
+ * events and writes up to max_kernels (name, milliseconds) pairs of that call in launch
+ * order; it returns how many kernels the call launched, or -1 on error.  Names are static
+ * strings. */
+eblc_status eblc_plan_set_profiling(eblc_plan_t *plan, int enable);
+int eblc_plan_kernel_times(eblc_plan_t *plan, const char **names, float *ms, int max_kernels);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EBLC_H */

@@ -1,0 +1,405 @@
+/*
+ * eblc_oracle.cpp -- plain single-threaded CPU oracle of the error-bounded float32 codec.
+ *
+ * TEST INFRASTRUCTURE ONLY (see eblc_oracle.h).  Slow on purpose: every step is its own
+ * loop over the whole array, in the order the method is described, with no blocking,
+ * fusion or reordering.  Built with g++ -O2 -ffp-contract=off -fno-fast-math.
+ */
+#include "eblc_oracle.h"
+
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+namespace {
+
+/* ---- stream layout constants, written out independently of the GPU library ---------- */
+const uint32_t kMagic = 0x434C4245u; /* "EBLC" little-endian */
+const uint16_t kVersion = 1;
+const uint16_t kHeaderBytes = 128;
+const uint8_t kModeLossy = 0;
+const uint8_t kModeRaw = 1;
+const uint32_t kSeg = 32; /* values per bitpack segment */
+
+uint64_t align16(uint64_t v) { return (v + 15u) / 16u * 16u; }
+
+void put_u8(uint8_t *p, uint64_t off, uint8_t v) { p[off] = v; }
+void put_u16(uint8_t *p, uint64_t off, uint16_t v) { std::memcpy(p + off, &v, 2); }
+void put_u32(uint8_t *p, uint64_t off, uint32_t v) { std::memcpy(p + off, &v, 4); }
+void put_u64(uint8_t *p, uint64_t off, uint64_t v) { std::memcpy(p + off, &v, 8); }
+void put_f32(uint8_t *p, uint64_t off, float v) { std::memcpy(p + off, &v, 4); }
+uint8_t get_u8(const uint8_t *p, uint64_t off) { return p[off]; }
+uint16_t get_u16(const uint8_t *p, uint64_t off) { uint16_t v; std::memcpy(&v, p + off, 2); return v; }
+uint32_t get_u32(const uint8_t *p, uint64_t off) { uint32_t v; std::memcpy(&v, p + off, 4); return v; }
+uint64_t get_u64(const uint8_t *p, uint64_t off) { uint64_t v; std::memcpy(&v, p + off, 8); return v; }
+float get_f32(const uint8_t *p, uint64_t off) { float v; std::memcpy(&v, p + off, 4); return v; }
+uint32_t f32_bits(float v) { uint32_t b; std::memcpy(&b, &v, 4); return b; }
+float bits_f32(uint32_t b) { float v; std::memcpy(&v, &b, 4); return v; }
+
+/* The decoder's reconstruction of a code: convert the int32 code to fp32 (round to nearest
+ * even), then multiply by the step s = 2*eb in fp32.  "Inverse declaration" on the
+ * Pipeline Specialization Internals page: the dequant step is 2*abs_eb and the harness
+ * multiplies the code by it. */
+float dequant(int32_t q, float s) {
+    float qf = (float)q;
+    float y = qf * s;
+    return y;
+}
+
+/* Acceptance test for a candidate code: the fp32 difference must be within eb, and the
+ * guard |x| >= |y|/2 keeps that fp32 difference exact (Sterbenz), so the test is exact. */
+bool accept(float x, float y, float eb_f) {
+    float diff = x - y;
+    bool within = std::fabs(diff) <= eb_f;
+    float half_y = 0.5f * std::fabs(y);
+    bool guard = std::fabs(x) >= half_y;
+    return within && guard;
+}
+
+} // namespace
+
+extern "C" {
+
+/* Step 1: bound resolution.  "Priming" on the Pipeline Specialization Internals page: the
+ * quantizer runs a value-range scan to resolve its bound before the fused kernel runs.
+ * The DevitoComp provider interface page ("Configuring the error tolerance") makes the
+ * user's error a non-negative relative tolerance; the relative bound is eps times the
+ * range of the finite values.  The fp64 bound is rounded toward zero to fp32 so that the
+ * fp32 bound never exceeds the requested one. */
+int oracle_resolve_bound(const float *x, uint64_t n, int rel, double eps,
+                         float *eb_f_out, float *s_out, float *r_out) {
+    double eb_d;
+    if (rel) {
+        bool any = false;
+        float mn = 0.0f, mx = 0.0f;
+        for (uint64_t i = 0; i < n; ++i) {
+            float v = x[i];
+            if (!std::isfinite(v)) continue;
+            if (!any) { mn = v; mx = v; any = true; continue; }
+            if (v < mn) mn = v;
+            if (v > mx) mx = v;
+        }
+        if (!any) {
+            *eb_f_out = 0.0f; *s_out = 0.0f; *r_out = 0.0f;
+            return 0;
+        }
+        double range = (double)mx - (double)mn;
+        eb_d = eps * range;
+    } else {
+        eb_d = eps;
+    }
+    float eb_f = (float)eb_d;
+    if (std::isfinite(eb_f) && (double)eb_f > eb_d) {
+        eb_f = std::nextafter(eb_f, 0.0f);
+    }
+    float s = 2.0f * eb_f;
+    double inv = 1.0 / (double)s;
+    float r = (float)inv;
+    int valid = std::isnormal(eb_f) && eb_f > 0.0f && std::isfinite(s) && std::isfinite(r);
+    if (!valid) {
+        *eb_f_out = 0.0f; *s_out = 0.0f; *r_out = 0.0f;
+        return 0;
+    }
+    *eb_f_out = eb_f; *s_out = s; *r_out = r;
+    return 1;
+}
+
+/* Step 2: linear quantization of one value ("Roles and strategies": the linear quantizer is
+ * Elementwise; "Conventions": it multiplies by inv2eb = 1/(2 eb) inside the predictor).
+ * The code is round-to-nearest-even of x*inv2eb, then checked against the decoder's exact
+ * reconstruction; if that misses the bound, the one neighbouring code toward x is tried; if
+ * both miss, or the value is not finite, or the code needs 2^T or more in magnitude, the
+ * value escapes to the outlier list. */
+int oracle_quantize_one(float x, float eb_f, float s, float r, int T, int32_t *q_out) {
+    float p = x * r;
+    float q0f = std::nearbyint(p);
+    /* non-finite x or product, or a code of 2^30 or more in magnitude */
+    if (!(std::fabs(q0f) < 1073741824.0f)) return 1;
+    int32_t q = (int32_t)q0f;
+    float y = dequant(q, s);
+    if (!accept(x, y, eb_f)) {
+        int32_t qn = (x > y) ? q + 1 : q - 1;
+        float yn = dequant(qn, s);
+        if (!accept(x, yn, eb_f)) return 1;
+        q = qn;
+    }
+    int64_t mag = q < 0 ? -(int64_t)q : (int64_t)q;
+    if (mag >= ((int64_t)1 << T)) return 1;
+    *q_out = q;
+    return 0;
+}
+
+/* Steps 2-5 over the array.  Lorenzo ("Roles and strategies": 1-D Lorenzo is RegionLocal
+ * with a region reset; "Inverse declaration": its undelta is a plain first difference
+ * inverse): d_i = q_i - q_{i-1}, except at a block start (i mod B == 0) where the
+ * prediction is 0 and d_i = q_i.  Zigzag (named as the interior transform in "The device
+ * policy contract"): z = (d << 1) ^ (d >> 31).  Width (AdaptiveBitpack is the SegmentCodec
+ * with one metadata byte per segment): the bit length of the OR of the segment's 32 z
+ * values, the tail past n counting as zeros. */
+void oracle_codes(const float *x, uint64_t n, float eb_f, float s, float r, int T, uint32_t B,
+                  int32_t *q, uint8_t *esc, int32_t *d, uint32_t *z, uint8_t *widths) {
+    /* quantize every value; an escaped value is coded as 0 */
+    for (uint64_t i = 0; i < n; ++i) {
+        int32_t qi = 0;
+        int e = oracle_quantize_one(x[i], eb_f, s, r, T, &qi);
+        esc[i] = (uint8_t)e;
+        q[i] = e ? 0 : qi;
+    }
+    /* Lorenzo deltas with a reset at every block start */
+    for (uint64_t i = 0; i < n; ++i) {
+        if (i % B == 0) d[i] = q[i];
+        else d[i] = q[i] - q[i - 1];
+    }
+    /* zigzag */
+    for (uint64_t i = 0; i < n; ++i) {
+        uint32_t du = (uint32_t)d[i];
+        uint32_t sign = (uint32_t)(d[i] >> 31);
+        z[i] = (du << 1) ^ sign;
+    }
+    /* one width per 32-value segment */
+    uint64_t nseg = (n + kSeg - 1) / kSeg;
+    for (uint64_t k = 0; k < nseg; ++k) {
+        uint32_t acc = 0;
+        for (uint64_t j = 0; j < kSeg; ++j) {
+            uint64_t i = k * kSeg + j;
+            if (i < n) acc |= z[i];
+        }
+        uint32_t w = 0;
+        while (w < 32 && (acc >> w) != 0) ++w;
+        widths[k] = (uint8_t)w;
+    }
+}
+
+/* Step 6: fixed-length packing.  Segment k holds w_k little-endian 32-bit words; value j of
+ * the segment occupies bits [j*w, j*w + w) of the segment's bit string, bit t living in
+ * word t/32 at position t%32.  Segments follow each other with no gap. */
+uint64_t oracle_pack(const uint32_t *z, uint64_t n, const uint8_t *widths, uint32_t *words) {
+    uint64_t nseg = (n + kSeg - 1) / kSeg;
+    uint64_t base = 0;
+    for (uint64_t k = 0; k < nseg; ++k) {
+        uint32_t w = widths[k];
+        for (uint32_t t = 0; t < w; ++t) words[base + t] = 0;
+        for (uint32_t j = 0; j < kSeg; ++j) {
+            uint64_t i = k * kSeg + j;
+            uint32_t v = (i < n) ? z[i] : 0u;
+            for (uint32_t b = 0; b < w; ++b) {
+                uint32_t bit = (v >> b) & 1u;
+                uint64_t t = (uint64_t)j * w + b;
+                words[base + t / 32] |= bit << (t % 32);
+            }
+        }
+        base += w;
+    }
+    return base;
+}
+
+uint32_t oracle_unpack_one(const uint32_t *words, uint32_t w, uint32_t j) {
+    uint32_t v = 0;
+    for (uint32_t b = 0; b < w; ++b) {
+        uint64_t t = (uint64_t)j * w + b;
+        uint32_t bit = (words[t / 32] >> (t % 32)) & 1u;
+        v |= bit << b;
+    }
+    return v;
+}
+
+uint64_t oracle_stream_bytes(uint64_t n, uint64_t sum_widths, uint64_t m) {
+    uint64_t nseg = (n + kSeg - 1) / kSeg;
+    uint64_t payload_off = kHeaderBytes + align16(nseg);
+    uint64_t oidx_off = payload_off + align16(4 * sum_widths);
+    uint64_t oval_off = oidx_off + align16(4 * m);
+    return oval_off + align16(4 * m);
+}
+
+uint64_t oracle_raw_bytes(uint64_t n) { return kHeaderBytes + align16(4 * n); }
+
+/* Steps 1-8: the whole compressor, in order.  The outlier list holds (u32 index, raw fp32
+ * bits) pairs in ascending index order (the "nvrtc_chunk_fusion.h File Reference" names the
+ * side list as u32 indices plus float values; the order is fixed here by index).  The stream
+ * falls back to a raw copy when the bound is unusable, when more values escape than the
+ * side list may hold, or when the coded stream would be larger than the raw one (the
+ * DevitoComp dummy provider reports the raw size as the maximum compressed size). */
+uint64_t oracle_compress(const float *x, int rank, const uint64_t *dims, int rel, double eps,
+                         uint32_t B, int T, uint64_t side_max,
+                         uint8_t *out, uint64_t cap, uint64_t *required) {
+    uint64_t n = 1;
+    for (int a = 0; a < rank; ++a) n *= dims[a];
+    uint64_t nseg = (n + kSeg - 1) / kSeg;
+
+    float eb_f = 0.0f, s = 0.0f, r = 0.0f;
+    int valid = oracle_resolve_bound(x, n, rel, eps, &eb_f, &s, &r);
+
+    std::vector<int32_t> q, d;
+    std::vector<uint8_t> esc, widths;
+    std::vector<uint32_t> z, words;
+    std::vector<uint32_t> oidx, oval;
+    uint64_t sum_w = 0;
+    bool raw = !valid;
+    if (!raw) {
+        q.resize(n); d.resize(n); esc.resize(n); z.resize(n); widths.resize(nseg);
+        oracle_codes(x, n, eb_f, s, r, T, B, q.data(), esc.data(), d.data(), z.data(), widths.data());
+        for (uint64_t k = 0; k < nseg; ++k) sum_w += widths[k];
+        words.assign(sum_w, 0u);
+        oracle_pack(z.data(), n, widths.data(), words.data());
+        for (uint64_t i = 0; i < n; ++i) {
+            if (esc[i]) { oidx.push_back((uint32_t)i); oval.push_back(f32_bits(x[i])); }
+        }
+        if (oidx.size() > side_max) raw = true;
+        else if (oracle_stream_bytes(n, sum_w, oidx.size()) > oracle_raw_bytes(n)) raw = true;
+    }
+
+    uint64_t total = raw ? oracle_raw_bytes(n) : oracle_stream_bytes(n, sum_w, oidx.size());
+    if (required) *required = total;
+    if (total > cap) return 0;
+
+    std::memset(out, 0, total);
+    put_u32(out, 0, kMagic);
+    put_u16(out, 4, kVersion);
+    put_u16(out, 6, kHeaderBytes);
+    put_u8(out, 8, raw ? kModeRaw : kModeLossy);
+    put_u8(out, 9, (uint8_t)rank);
+    put_u8(out, 10, 5);
+    put_u8(out, 11, (uint8_t)T);
+    put_u32(out, 12, B);
+    for (int a = 0; a < 4; ++a) put_u64(out, 16 + 8 * a, a < rank ? dims[a] : 0);
+    put_u64(out, 48, n);
+    put_f32(out, 56, eb_f);
+    put_f32(out, 60, s);
+    put_f32(out, 64, r);
+    put_u32(out, 68, 0);
+    put_u64(out, 88, kHeaderBytes);
+    if (raw) {
+        uint64_t end = oracle_raw_bytes(n);
+        put_u64(out, 72, 0);
+        put_u64(out, 80, 4 * n);
+        put_u64(out, 96, kHeaderBytes);
+        put_u64(out, 104, end);
+        put_u64(out, 112, end);
+        put_u64(out, 120, end);
+        std::memcpy(out + kHeaderBytes, x, 4 * n);
+        return total;
+    }
+    uint64_t m = oidx.size();
+    uint64_t payload_off = kHeaderBytes + align16(nseg);
+    uint64_t oidx_off = payload_off + align16(4 * sum_w);
+    uint64_t oval_off = oidx_off + align16(4 * m);
+    put_u64(out, 72, m);
+    put_u64(out, 80, 4 * sum_w);
+    put_u64(out, 96, payload_off);
+    put_u64(out, 104, oidx_off);
+    put_u64(out, 112, oval_off);
+    put_u64(out, 120, total);
+    for (uint64_t k = 0; k < nseg; ++k) out[kHeaderBytes + k] = widths[k];
+    for (uint64_t t = 0; t < sum_w; ++t) put_u32(out, payload_off + 4 * t, words[t]);
+    for (uint64_t k = 0; k < m; ++k) {
+        put_u32(out, oidx_off + 4 * k, oidx[k]);
+        put_u32(out, oval_off + 4 * k, oval[k]);
+    }
+    return total;
+}
+
+/* Header checks shared by oracle_decompress and oracle_stream_elements.  Returns n, or 0
+ * when the header is not one this codec writes. */
+static uint64_t check_header(const uint8_t *in, uint64_t len) {
+    if (len < kHeaderBytes) return 0;
+    if (get_u32(in, 0) != kMagic) return 0;
+    if (get_u16(in, 4) != kVersion || get_u16(in, 6) != kHeaderBytes) return 0;
+    uint8_t mode = get_u8(in, 8), rank = get_u8(in, 9), log2_seg = get_u8(in, 10), T = get_u8(in, 11);
+    uint32_t B = get_u32(in, 12);
+    if (mode != kModeLossy && mode != kModeRaw) return 0;
+    if (rank < 1 || rank > 4 || log2_seg != 5 || T < 1 || T > 30) return 0;
+    if (B < 32 || B % 32 != 0 || B > (1u << 20)) return 0;
+    uint64_t n = 1;
+    for (int a = 0; a < 4; ++a) {
+        uint64_t da = get_u64(in, 16 + 8 * a);
+        if (a < rank) {
+            if (da == 0 || da >= (1ull << 32)) return 0;
+            n *= da;
+            if (n >= (1ull << 32)) return 0;
+        } else if (da != 0) {
+            return 0;
+        }
+    }
+    if (get_u64(in, 48) != n) return 0;
+    if (get_u32(in, 68) != 0 || get_u64(in, 88) != kHeaderBytes) return 0;
+    uint64_t m = get_u64(in, 72), pb = get_u64(in, 80);
+    uint64_t po = get_u64(in, 96), oi = get_u64(in, 104), ov = get_u64(in, 112), tot = get_u64(in, 120);
+    if (mode == kModeRaw) {
+        uint64_t end = kHeaderBytes + align16(4 * n);
+        if (m != 0 || pb != 4 * n || po != kHeaderBytes || oi != end || ov != end || tot != end) return 0;
+    } else {
+        float eb_f = get_f32(in, 56), s = get_f32(in, 60);
+        if (!(std::isnormal(eb_f) && eb_f > 0.0f && std::isfinite(s) && s == 2.0f * eb_f)) return 0;
+        uint64_t nseg = (n + kSeg - 1) / kSeg;
+        if (m > n || pb % 4 != 0 || pb > 4ull * 32 * nseg) return 0;
+        if (po != kHeaderBytes + align16(nseg)) return 0;
+        if (oi != po + align16(pb) || ov != oi + align16(4 * m) || tot != ov + align16(4 * m)) return 0;
+    }
+    if (tot > len) return 0;
+    return n;
+}
+
+uint64_t oracle_stream_elements(const uint8_t *in, uint64_t len) { return check_header(in, len); }
+
+/* Step 9: the inverse.  Per segment: read its width, unpack its 32 values, undo the zigzag
+ * d = (z >> 1) ^ -(z & 1), then the code is the running sum of d from the block start
+ * (undelta of the first-difference predictor), and the value is f32(f32(q) * s)
+ * ("Inverse declaration": dequant step 2*eb).  Finally every outlier is written back with
+ * its exact bits. */
+int oracle_decompress(const uint8_t *in, uint64_t len, float *out, uint64_t n_out) {
+    uint64_t n = check_header(in, len);
+    if (n == 0) return ORACLE_CORRUPT;
+    if (n_out < n) return ORACLE_CAPACITY;
+    uint8_t mode = get_u8(in, 8);
+    if (mode == kModeRaw) {
+        std::memcpy(out, in + kHeaderBytes, 4 * n);
+        return ORACLE_OK;
+    }
+    uint32_t B = get_u32(in, 12);
+    float s = get_f32(in, 60);
+    uint64_t m = get_u64(in, 72), pb = get_u64(in, 80);
+    uint64_t po = get_u64(in, 96), oi = get_u64(in, 104), ov = get_u64(in, 112);
+    uint64_t nseg = (n + kSeg - 1) / kSeg;
+
+    /* widths, and the payload size they imply */
+    std::vector<uint8_t> widths(nseg);
+    uint64_t sum_w = 0;
+    for (uint64_t k = 0; k < nseg; ++k) {
+        widths[k] = in[kHeaderBytes + k];
+        if (widths[k] > 32) return ORACLE_CORRUPT;
+        sum_w += widths[k];
+    }
+    if (4 * sum_w != pb) return ORACLE_CORRUPT;
+
+    /* unpack + unzigzag */
+    std::vector<uint32_t> words(sum_w);
+    for (uint64_t t = 0; t < sum_w; ++t) words[t] = get_u32(in, po + 4 * t);
+    std::vector<int32_t> d(n);
+    uint64_t base = 0;
+    for (uint64_t k = 0; k < nseg; ++k) {
+        for (uint32_t j = 0; j < kSeg; ++j) {
+            uint64_t i = k * kSeg + j;
+            if (i >= n) break;
+            uint32_t zv = oracle_unpack_one(words.data() + base, widths[k], j);
+            d[i] = (int32_t)((zv >> 1) ^ (0u - (zv & 1u)));
+        }
+        base += widths[k];
+    }
+    /* undelta: running sum from each block start, then dequantize */
+    int32_t qprev = 0;
+    for (uint64_t i = 0; i < n; ++i) {
+        int32_t qi = (i % B == 0) ? d[i] : (int32_t)((uint32_t)qprev + (uint32_t)d[i]);
+        out[i] = dequant(qi, s);
+        qprev = qi;
+    }
+    /* outliers: strictly ascending indices below n */
+    for (uint64_t k = 0; k < m; ++k) {
+        uint32_t idx = get_u32(in, oi + 4 * k);
+        if (idx >= n) return ORACLE_CORRUPT;
+        if (k > 0 && idx <= get_u32(in, oi + 4 * (k - 1))) return ORACLE_CORRUPT;
+        out[idx] = bits_f32(get_u32(in, ov + 4 * k));
+    }
+    return ORACLE_OK;
+}
+
+} /* extern "C" */
