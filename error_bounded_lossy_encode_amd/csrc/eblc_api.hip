@@ -1,0 +1,430 @@
+/*
+ * eblc_api.hip -- host side of libeblc.so: the C ABI declared in include/eblc.h.
+ *
+ * The plan mirrors the provider plan of the "DevitoComp provider interface" page: created once
+ * per tensor shape and tolerance ("Configuring the error tolerance": the error is fixed at plan
+ * creation), it owns a workspace allocated up front (the PREALLOCATE policy of the FZGPUModules
+ * "Architecture" page, MemoryPool section), so compress and decompress allocate nothing.
+ * Compress enqueues range (relative mode) -> encode -> scan -> compaction -> outliers on the
+ * caller's stream and waits once to return the stream length; decompress enqueues sizes ->
+ * scan -> decode -> outlier patch and returns at once.
+ */
+#include "eblc.h"
+#include "eblc_internal.h"
+
+#include <cerrno>
+#include <cfloat>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+
+using namespace eblc;
+
+struct eblc_plan {
+    int device = 0;
+    int rank = 0;
+    int64_t dims[4] = {0, 0, 0, 0};
+    uint64_t n = 0;
+    bool rel = true;
+    double eps = 1e-4;
+    PlanArgs pa{};
+    Workspace ws{};
+    void *ws_base = nullptr;
+    DevInfo *host_info = nullptr; /* pinned */
+    bool profiling = false;
+    hipEvent_t ev[2 * kMaxKernelsPerCall] = {};
+    const char *names[kMaxKernelsPerCall] = {};
+    int nlaunch = 0;
+};
+
+namespace {
+
+uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+/* Device guard: switch to the plan's device for the call, restore the caller's afterwards. */
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) return;
+        ok = prev == dev || hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+bool parse_double(const std::string &s, double *out) {
+    if (s.empty()) return false;
+    const char *b = s.c_str();
+    char *e = nullptr;
+    errno = 0;
+    const double v = std::strtod(b, &e);
+    if (e == b || *e != '\0' || errno == ERANGE) return false;
+    *out = v;
+    return true;
+}
+
+bool parse_u64(const std::string &s, uint64_t *out) {
+    if (s.empty()) return false;
+    for (char ch : s)
+        if (ch < '0' || ch > '9') return false;
+    errno = 0;
+    char *e = nullptr;
+    const unsigned long long v = std::strtoull(s.c_str(), &e, 10);
+    if (errno == ERANGE || *e != '\0') return false;
+    *out = v;
+    return true;
+}
+
+std::string trim(const std::string &s) {
+    size_t a = 0, b = s.size();
+    while (a < b && (s[a] == ' ' || s[a] == '\t')) ++a;
+    while (b > a && (s[b - 1] == ' ' || s[b - 1] == '\t')) --b;
+    return s.substr(a, b - a);
+}
+
+struct Options {
+    bool rel = true;
+    double eps = 1e-4;
+    uint32_t B = 256;
+    uint32_t T = 30;
+    bool side_set = false;
+    uint64_t side_max = 0;
+};
+
+/* Options string ("Provider layout": a provider-defined string; DevitoPRO passes the relative
+ * error as a decimal, or NULL for the provider default). */
+eblc_status parse_options(const char *opts, Options *o) {
+    if (opts == nullptr) return EBLC_OK;
+    const std::string all = trim(opts);
+    if (all.empty()) return EBLC_OK;
+    double v;
+    if (parse_double(all, &v)) {
+        if (!std::isfinite(v) || v < 0) return EBLC_INVALID_ARGUMENT;
+        o->rel = true;
+        o->eps = v;
+        return EBLC_OK;
+    }
+    bool seen_eb = false, seen_block = false, seen_t = false;
+    size_t pos = 0;
+    for (;;) {
+        size_t end = all.find(';', pos);
+        const bool final_item = end == std::string::npos;
+        if (final_item) end = all.size();
+        const std::string item = trim(all.substr(pos, end - pos));
+        pos = end + 1;
+        if (!item.empty()) {
+            const size_t eq = item.find('=');
+            if (eq == std::string::npos) return EBLC_INVALID_ARGUMENT;
+            const std::string key = trim(item.substr(0, eq)), val = trim(item.substr(eq + 1));
+            if (key == "rel" || key == "abs") {
+                if (seen_eb || !parse_double(val, &v) || !std::isfinite(v) || v < 0) return EBLC_INVALID_ARGUMENT;
+                seen_eb = true;
+                o->rel = key == "rel";
+                o->eps = v;
+            } else if (key == "block") {
+                uint64_t b;
+                if (seen_block || !parse_u64(val, &b) || b < 32 || b > (uint64_t)kChunk || (b & (b - 1)) != 0)
+                    return EBLC_INVALID_ARGUMENT;
+                seen_block = true;
+                o->B = (uint32_t)b;
+            } else if (key == "outlier_log2") {
+                uint64_t t;
+                if (seen_t || !parse_u64(val, &t) || t < 1 || t > 30) return EBLC_INVALID_ARGUMENT;
+                seen_t = true;
+                o->T = (uint32_t)t;
+            } else if (key == "side_max") {
+                uint64_t m;
+                if (o->side_set || !parse_u64(val, &m)) return EBLC_INVALID_ARGUMENT;
+                o->side_set = true;
+                o->side_max = m;
+            } else {
+                return EBLC_INVALID_ARGUMENT;
+            }
+        }
+        if (final_item) break;
+    }
+    return EBLC_OK;
+}
+
+/* Absolute bound resolved on the host with the same fp64 -> fp32 round-toward-zero rule the
+ * device uses for the relative bound. */
+void resolve_abs(double eps, DevInfo *info) {
+    const double eb_d = eps;
+    float e = (float)eb_d;
+    if (std::fabs(e) <= FLT_MAX && (double)e > eb_d) e = std::nextafter(e, 0.0f);
+    const float s = 2.0f * e;
+    const double inv = 1.0 / (double)s;
+    const float r = (float)inv;
+    const bool valid = e >= FLT_MIN && e <= FLT_MAX && std::fabs(s) <= FLT_MAX && std::fabs(r) <= FLT_MAX;
+    info->eb_f = valid ? e : 0.0f;
+    info->s = valid ? s : 0.0f;
+    info->r = valid ? r : 0.0f;
+    info->valid = valid ? 1u : 0u;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+eblc_status hip_status(hipError_t e) { return e == hipSuccess ? EBLC_OK : EBLC_DEVICE_ERROR; }
+
+/* Profiling wrapper: event pair around one launch when enabled. */
+template <typename F>
+hipError_t timed(eblc_plan *p, hipStream_t st, const char *name, F &&launch) {
+    if (!p->profiling || p->nlaunch >= kMaxKernelsPerCall) return launch();
+    const int k = p->nlaunch++;
+    p->names[k] = name;
+    hipError_t e = hipEventRecord(p->ev[2 * k], st);
+    if (e != hipSuccess) return e;
+    e = launch();
+    if (e != hipSuccess) return e;
+    return hipEventRecord(p->ev[2 * k + 1], st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int eblc_abi_version(void) { return EBLC_ABI_VERSION; }
+
+const char *eblc_status_string(eblc_status s) {
+    switch (s) {
+        case EBLC_OK: return "ok";
+        case EBLC_UNSUPPORTED: return "unsupported";
+        case EBLC_INVALID_ARGUMENT: return "invalid argument";
+        case EBLC_CAPACITY: return "output capacity too small";
+        case EBLC_CORRUPT_STREAM: return "corrupt stream";
+        case EBLC_DEVICE_ERROR: return "device error";
+        case EBLC_OUT_OF_MEMORY: return "out of memory";
+    }
+    return "unknown status";
+}
+
+eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int rank,
+                             const int64_t *dims, const int64_t *strides, const char *options,
+                             eblc_plan_t **plan_out) {
+    if (plan_out == nullptr || exec == nullptr || dims == nullptr) return EBLC_INVALID_ARGUMENT;
+    *plan_out = nullptr;
+    if (exec->kind != EBLC_EXECUTION_HIP) return EBLC_UNSUPPORTED;
+    if (dtype != EBLC_FLOAT32) return EBLC_UNSUPPORTED;
+    if (rank < 1 || rank > 4) return EBLC_UNSUPPORTED;
+    uint64_t n = 1;
+    for (int a = 0; a < rank; ++a) {
+        if (dims[a] <= 0) return EBLC_INVALID_ARGUMENT;
+        if ((uint64_t)dims[a] >= (1ull << 32)) return EBLC_INVALID_ARGUMENT;
+        n *= (uint64_t)dims[a];
+        if (n >= (1ull << 32)) return EBLC_INVALID_ARGUMENT;
+    }
+    if (strides != nullptr) {
+        int64_t expect = 1;
+        for (int a = rank - 1; a >= 0; --a) {
+            if (strides[a] != expect) return EBLC_UNSUPPORTED;
+            expect *= dims[a];
+        }
+    }
+    Options o;
+    eblc_status st = parse_options(options, &o);
+    if (st != EBLC_OK) return st;
+    if (!o.side_set) o.side_max = n < (1ull << 23) ? n : (1ull << 23);
+    if (o.side_max > n) return EBLC_INVALID_ARGUMENT;
+
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || exec->device < 0 || exec->device >= ndev)
+        return EBLC_INVALID_ARGUMENT;
+    DeviceGuard guard(exec->device);
+    if (!guard.ok) return EBLC_DEVICE_ERROR;
+
+    eblc_plan *p = new (std::nothrow) eblc_plan();
+    if (p == nullptr) return EBLC_OUT_OF_MEMORY;
+    p->device = exec->device;
+    p->rank = rank;
+    for (int a = 0; a < rank; ++a) p->dims[a] = dims[a];
+    p->n = n;
+    p->rel = o.rel;
+    p->eps = o.eps;
+    PlanArgs &pa = p->pa;
+    pa.n = n;
+    pa.nseg = (n + 31) / 32;
+    for (int a = 0; a < 4; ++a) pa.dims[a] = a < rank ? (uint64_t)dims[a] : 0;
+    pa.rank = (uint32_t)rank;
+    pa.B = o.B;
+    pa.T = o.T;
+    pa.nchunks = (uint32_t)((n + kChunk - 1) / kChunk);
+    pa.ngroups = (pa.nchunks + kChunksPerGroup - 1) / kChunksPerGroup;
+    pa.side_max = o.side_max;
+
+    /* workspace: one allocation, carved into 256-byte aligned arrays */
+    const uint64_t nc = pa.nchunks, ng = pa.ngroups;
+    uint64_t off = 0;
+    auto carve = [&](uint64_t bytes) {
+        const uint64_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    const uint64_t o_info = carve(sizeof(DevInfo));
+    const uint64_t o_scratch = carve(nc * kChunk * 4);
+    const uint64_t o_cw = carve(nc * 4), o_ce = carve(nc * 4), o_ct = carve(nc * 4);
+    const uint64_t o_gw = carve(ng * 4), o_ge = carve(ng * 4);
+    const uint64_t o_pw = carve(ng * 4), o_pe = carve(ng * 4);
+    const uint64_t o_em = carve(nc * kSegsPerChunk * 4);
+    const uint64_t o_wd = carve(nc * kSegsPerChunk);
+    const uint64_t o_rp = carve(2 * kRangeBlocksMax * 4);
+    if (hipMalloc(&p->ws_base, off) != hipSuccess) {
+        delete p;
+        return EBLC_OUT_OF_MEMORY;
+    }
+    uint8_t *b = static_cast<uint8_t *>(p->ws_base);
+    Workspace &ws = p->ws;
+    ws.info = reinterpret_cast<DevInfo *>(b + o_info);
+    ws.scratch = reinterpret_cast<uint32_t *>(b + o_scratch);
+    ws.chunk_words = reinterpret_cast<uint32_t *>(b + o_cw);
+    ws.chunk_esc = reinterpret_cast<uint32_t *>(b + o_ce);
+    ws.chunk_tmask = reinterpret_cast<uint32_t *>(b + o_ct);
+    ws.group_words = reinterpret_cast<uint32_t *>(b + o_gw);
+    ws.group_esc = reinterpret_cast<uint32_t *>(b + o_ge);
+    ws.gpre_words = reinterpret_cast<uint32_t *>(b + o_pw);
+    ws.gpre_esc = reinterpret_cast<uint32_t *>(b + o_pe);
+    ws.emask = reinterpret_cast<uint32_t *>(b + o_em);
+    ws.widths = b + o_wd;
+    ws.range_part = reinterpret_cast<float *>(b + o_rp);
+
+    if (hipHostMalloc(reinterpret_cast<void **>(&p->host_info), sizeof(DevInfo), hipHostMallocDefault) != hipSuccess) {
+        (void)hipFree(p->ws_base);
+        delete p;
+        return EBLC_OUT_OF_MEMORY;
+    }
+    DevInfo init;
+    std::memset(&init, 0, sizeof(init));
+    if (!o.rel) resolve_abs(o.eps, &init);
+    if (hipMemcpy(ws.info, &init, sizeof(init), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipHostFree(p->host_info);
+        (void)hipFree(p->ws_base);
+        delete p;
+        return EBLC_DEVICE_ERROR;
+    }
+    *plan_out = p;
+    return EBLC_OK;
+}
+
+eblc_status eblc_plan_limits(const eblc_plan_t *plan, eblc_limits_t *out) {
+    if (plan == nullptr || out == nullptr) return EBLC_INVALID_ARGUMENT;
+    out->max_compressed_bytes = kHeaderBytes + align_up(4 * plan->n, 16);
+    out->payload_alignment = 16;
+    out->sidecar_bytes = 0;
+    out->sidecar_alignment = 1;
+    return EBLC_OK;
+}
+
+size_t eblc_max_compressed_bytes(const eblc_plan_t *plan) {
+    return plan == nullptr ? 0 : (size_t)(kHeaderBytes + align_up(4 * plan->n, 16));
+}
+
+size_t eblc_payload_alignment(const eblc_plan_t *plan) { return plan == nullptr ? 0 : 16; }
+
+eblc_status eblc_compress(eblc_plan_t *plan, const float *in, void *out, size_t out_capacity,
+                          size_t *compressed_bytes, void *sidecar, void *stream) {
+    if (plan == nullptr || in == nullptr || out == nullptr || compressed_bytes == nullptr) return EBLC_INVALID_ARGUMENT;
+    if (sidecar != nullptr || !aligned16(in) || !aligned16(out)) return EBLC_INVALID_ARGUMENT;
+    DeviceGuard guard(plan->device);
+    if (!guard.ok) return EBLC_DEVICE_ERROR;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const PlanArgs &pa = plan->pa;
+    const Workspace &ws = plan->ws;
+    uint8_t *o = static_cast<uint8_t *>(out);
+    const uint64_t widths_bytes = align_up(pa.nseg, 16);
+    const bool widths_direct = out_capacity >= kHeaderBytes + widths_bytes;
+    uint8_t *widths_dst = widths_direct ? o + kHeaderBytes : ws.widths;
+    plan->nlaunch = 0;
+    hipError_t e = hipSuccess;
+    if (plan->rel) e = timed(plan, st, "range", [&] { return launch_range(in, pa, ws, plan->eps, st); });
+    if (e == hipSuccess) e = timed(plan, st, "encode", [&] { return launch_encode(in, pa, ws, widths_dst, widths_bytes, st); });
+    if (e == hipSuccess) e = timed(plan, st, "scan", [&] { return launch_scan_compress(pa, ws, o, out_capacity, st); });
+    if (e == hipSuccess) e = timed(plan, st, "compact", [&] { return launch_compact(in, pa, ws, o, widths_direct ? nullptr : ws.widths, st); });
+    if (e == hipSuccess) e = timed(plan, st, "outliers", [&] { return launch_outliers(in, pa, ws, o, st); });
+    if (e == hipSuccess) e = hipMemcpyAsync(plan->host_info, ws.info, sizeof(DevInfo), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return EBLC_DEVICE_ERROR;
+    *compressed_bytes = (size_t)plan->host_info->total;
+    return plan->host_info->fits ? EBLC_OK : EBLC_CAPACITY;
+}
+
+eblc_status eblc_decompress(eblc_plan_t *plan, const void *in, size_t compressed_bytes,
+                            const void *sidecar, float *out, void *stream) {
+    if (plan == nullptr || in == nullptr || out == nullptr) return EBLC_INVALID_ARGUMENT;
+    if (sidecar != nullptr || !aligned16(in) || !aligned16(out)) return EBLC_INVALID_ARGUMENT;
+    const PlanArgs &pa = plan->pa;
+    if (compressed_bytes < kHeaderBytes + align_up(pa.nseg, 16) ||
+        compressed_bytes > kHeaderBytes + align_up(4 * pa.n, 16))
+        return EBLC_CORRUPT_STREAM;
+    DeviceGuard guard(plan->device);
+    if (!guard.ok) return EBLC_DEVICE_ERROR;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Workspace &ws = plan->ws;
+    const uint8_t *i = static_cast<const uint8_t *>(in);
+    plan->nlaunch = 0;
+    hipError_t e = timed(plan, st, "decode_sizes", [&] { return launch_decode_sizes(i, pa, ws, st); });
+    if (e == hipSuccess) e = timed(plan, st, "decode_scan", [&] { return launch_scan_decompress(i, compressed_bytes, pa, ws, st); });
+    if (e == hipSuccess) e = timed(plan, st, "decode", [&] { return launch_decode(i, pa, ws, out, st); });
+    if (e == hipSuccess) e = timed(plan, st, "patch", [&] { return launch_patch(i, pa, ws, out, st); });
+    return hip_status(e);
+}
+
+eblc_status eblc_plan_status(eblc_plan_t *plan, void *stream) {
+    if (plan == nullptr) return EBLC_INVALID_ARGUMENT;
+    DeviceGuard guard(plan->device);
+    if (!guard.ok) return EBLC_DEVICE_ERROR;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (hipStreamSynchronize(st) != hipSuccess) return EBLC_DEVICE_ERROR;
+    uint32_t sticky = 0;
+    if (hipMemcpy(&sticky, &plan->ws.info->sticky, 4, hipMemcpyDeviceToHost) != hipSuccess) return EBLC_DEVICE_ERROR;
+    if (sticky) {
+        const uint32_t zero = 0;
+        if (hipMemcpy(&plan->ws.info->sticky, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) return EBLC_DEVICE_ERROR;
+        return EBLC_CORRUPT_STREAM;
+    }
+    return EBLC_OK;
+}
+
+void eblc_plan_destroy(eblc_plan_t *plan) {
+    if (plan == nullptr) return;
+    {
+        DeviceGuard guard(plan->device);
+        (void)hipDeviceSynchronize();
+        for (auto &ev : plan->ev)
+            if (ev) (void)hipEventDestroy(ev);
+        if (plan->host_info) (void)hipHostFree(plan->host_info);
+        if (plan->ws_base) (void)hipFree(plan->ws_base);
+    }
+    delete plan;
+}
+
+eblc_status eblc_plan_set_profiling(eblc_plan_t *plan, int enable) {
+    if (plan == nullptr) return EBLC_INVALID_ARGUMENT;
+    DeviceGuard guard(plan->device);
+    if (!guard.ok) return EBLC_DEVICE_ERROR;
+    if (enable && plan->ev[0] == nullptr) {
+        for (auto &ev : plan->ev)
+            if (hipEventCreate(&ev) != hipSuccess) return EBLC_DEVICE_ERROR;
+    }
+    plan->profiling = enable != 0;
+    plan->nlaunch = 0;
+    return EBLC_OK;
+}
+
+int eblc_plan_kernel_times(eblc_plan_t *plan, const char **names, float *ms, int max_kernels) {
+    if (plan == nullptr || !plan->profiling) return -1;
+    DeviceGuard guard(plan->device);
+    if (!guard.ok) return -1;
+    for (int k = 0; k < plan->nlaunch && k < max_kernels; ++k) {
+        if (hipEventSynchronize(plan->ev[2 * k + 1]) != hipSuccess) return -1;
+        float t = 0.0f;
+        if (hipEventElapsedTime(&t, plan->ev[2 * k], plan->ev[2 * k + 1]) != hipSuccess) return -1;
+        if (names) names[k] = plan->names[k];
+        if (ms) ms[k] = t;
+    }
+    return plan->nlaunch;
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+/*
+ * eblc_internal.h -- shared between the host plan code and the gfx950 kernels of libeblc.so.
+ *
+ * Work decomposition (all sizes in 32-bit values):
+ *   tile   = 256 values = one wave64 step, 4 consecutive values per lane (one 128-bit load)
+ *   chunk  = 8 tiles = 2048 values = 64 bitpack segments; one wave owns one chunk
+ *   group  = 4 chunks = one 256-thread workgroup; the device-wide scan runs over groups
+ * The Lorenzo block B is a power of two in [32, 2048], so every chunk starts a block and the
+ * only cross-wave dependency of the codec is the exclusive scan of payload sizes and outlier
+ * counts.
+ */
+#ifndef EBLC_INTERNAL_H
+#define EBLC_INTERNAL_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eblc {
+
+constexpr int kWave = 64;
+constexpr int kTile = 256;
+constexpr int kTilesPerChunk = 8;
+constexpr int kChunk = kTile * kTilesPerChunk;   /* 2048 values */
+constexpr int kSegsPerChunk = kChunk / 32;       /* 64 segments */
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlockThreads = kWave * kWavesPerBlock;
+constexpr int kChunksPerGroup = kWavesPerBlock;
+constexpr int kScanThreads = 1024;
+constexpr int kRangeBlocksMax = 2048;
+constexpr int kPatchBlocksMax = 1024;
+constexpr uint32_t kHeaderBytes = 128;
+constexpr uint32_t kMagic = 0x434C4245u;          /* "EBLC" */
+constexpr uint32_t kVersion = 1;
+constexpr int kMaxKernelsPerCall = 8;
+
+/* Device-resident state of a plan (one per plan, in its workspace). */
+struct DevInfo {
+    /* resolved bound: abs mode writes it once at plan creation, rel mode at every compress */
+    float eb_f, s, r;
+    uint32_t valid;
+    /* outcome of the last compress, or the parsed header of the last decompress */
+    uint32_t mode;          /* 0 coded, 1 raw */
+    uint32_t err;           /* decompress: this call's stream is corrupt */
+    uint32_t sticky;        /* OR of err over calls since eblc_plan_status */
+    uint32_t range_ticket;  /* last-block counter of the range kernel (self-resetting) */
+    uint32_t width_bad;     /* decompress: a width byte above 32 was seen */
+    uint32_t fits;          /* compress: total <= out_capacity */
+    uint64_t m;
+    uint64_t payload_words;
+    uint64_t payload_off;
+    uint64_t oidx_off;
+    uint64_t oval_off;
+    uint64_t total;
+    float dec_s;            /* decompress: step read from the stream */
+    uint32_t pad_;
+};
+
+/* Plan constants passed by value to the kernels. */
+struct PlanArgs {
+    uint64_t n;
+    uint64_t nseg;
+    uint64_t dims[4];
+    uint32_t rank;
+    uint32_t B;             /* Lorenzo block, power of two 32..2048 */
+    uint32_t T;             /* outlier log2 */
+    uint32_t nchunks;
+    uint32_t ngroups;
+    uint32_t pad_;
+    uint64_t side_max;
+};
+
+/* Workspace pointers (all device memory owned by the plan). */
+struct Workspace {
+    DevInfo *info;
+    uint32_t *scratch;       /* nchunks * kChunk words: per-chunk packed payload slots */
+    uint32_t *chunk_words;   /* [nchunks] payload words per chunk */
+    uint32_t *chunk_esc;     /* [nchunks] escapes per chunk */
+    uint32_t *chunk_tmask;   /* [nchunks] bit t set if tile t of the chunk has an escape */
+    uint32_t *group_words;   /* [ngroups] */
+    uint32_t *group_esc;     /* [ngroups] */
+    uint32_t *gpre_words;    /* [ngroups] exclusive prefix */
+    uint32_t *gpre_esc;      /* [ngroups] exclusive prefix */
+    uint32_t *emask;         /* [nchunks * 64] escape bitmask per segment (tiles with escapes) */
+    uint8_t *widths;         /* [nchunks * 64] widths staging when the output is too small */
+    float *range_part;       /* [2 * kRangeBlocksMax] per-block min / max */
+};
+
+/* Kernel launchers (eblc_kernels.hip).  All enqueue on `stream` and return the launch error. */
+hipError_t launch_range(const float *x, const PlanArgs &pa, const Workspace &ws, double eps,
+                        hipStream_t stream);
+hipError_t launch_encode(const float *x, const PlanArgs &pa, const Workspace &ws,
+                         uint8_t *widths_dst, uint64_t widths_bytes, hipStream_t stream);
+hipError_t launch_scan_compress(const PlanArgs &pa, const Workspace &ws, uint8_t *out,
+                                uint64_t out_capacity, hipStream_t stream);
+hipError_t launch_compact(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *out,
+                          const uint8_t *widths_src, hipStream_t stream);
+hipError_t launch_outliers(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *out,
+                           hipStream_t stream);
+hipError_t launch_decode_sizes(const uint8_t *in, const PlanArgs &pa, const Workspace &ws,
+                               hipStream_t stream);
+hipError_t launch_scan_decompress(const uint8_t *in, uint64_t in_bytes, const PlanArgs &pa,
+                                  const Workspace &ws, hipStream_t stream);
+hipError_t launch_decode(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
+                         hipStream_t stream);
+hipError_t launch_patch(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
+                        hipStream_t stream);
+
+}  // namespace eblc
+
+#endif

@@ -1,0 +1,59 @@
+"""CPU checks of the library boundary: it loads, exports every declared symbol, and answers the
+calls that need no GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from error_bounded_lossy_encode_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "eblc.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(eblc_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.lib()
+    names = declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(binding.EXPORTS)
+
+
+def test_calls_without_gpu():
+    assert binding.eblc_abi_version() == 1
+    assert binding.eblc_status_string(binding.EBLC_CORRUPT_STREAM) == "corrupt stream"
+    assert binding.eblc_status_string(99) == "unknown status"
+    lib = binding.lib()
+    assert lib.eblc_max_compressed_bytes(None) == 0
+    assert lib.eblc_payload_alignment(None) == 0
+    assert lib.eblc_plan_limits(None, None) == binding.EBLC_INVALID_ARGUMENT
+    lib.eblc_plan_destroy(None)
+
+
+@pytest.mark.parametrize("kind", [binding.EBLC_EXECUTION_HOST, binding.EBLC_EXECUTION_CUDA])
+def test_unsupported_execution_kinds(kind):
+    st, plan = binding.eblc_plan_create([64, 64], "rel=1e-3", kind=kind)
+    assert st == binding.EBLC_UNSUPPORTED and plan is None
+
+
+@pytest.mark.parametrize("opts", ["rel=-1", "abs=nan", "rel=1e-3;abs=1", "block=48", "block=4096",
+                                  "outlier_log2=0", "outlier_log2=31", "bogus=1", "rel", "side_max=-3",
+                                  "block=256;block=128", "side_max=5000"])
+def test_invalid_options_rejected_before_any_device_call(opts):
+    st, plan = binding.eblc_plan_create([64, 64], opts)
+    assert st == binding.EBLC_INVALID_ARGUMENT and plan is None
+
+
+def test_shape_checks():
+    assert binding.eblc_plan_create([64, 0])[0] == binding.EBLC_INVALID_ARGUMENT
+    assert binding.eblc_plan_create([1] * 5)[0] == binding.EBLC_UNSUPPORTED
+    assert binding.eblc_plan_create([1 << 16, 1 << 16])[0] == binding.EBLC_INVALID_ARGUMENT
+    assert binding.eblc_plan_create([8, 8], strides=[16, 1])[0] == binding.EBLC_UNSUPPORTED
+    assert binding.eblc_plan_create([8, 8], dtype=3)[0] == binding.EBLC_UNSUPPORTED
