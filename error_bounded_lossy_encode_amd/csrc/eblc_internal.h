@@ -42,7 +42,7 @@ struct DevInfo {
     uint32_t mode;          /* 0 coded, 1 raw */
     uint32_t err;           /* decompress: this call's stream is corrupt */
     uint32_t sticky;        /* OR of err over calls since eblc_plan_status */
-    uint32_t range_ticket;  /* last-block counter of the range kernel (self-resetting) */
+    uint32_t reserved0;
     uint32_t width_bad;     /* decompress: a width byte above 32 was seen */
     uint32_t fits;          /* compress: total <= out_capacity */
     uint64_t m;

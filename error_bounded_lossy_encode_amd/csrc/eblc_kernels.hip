@@ -114,7 +114,7 @@ __device__ __forceinline__ bool accept(float x, float y, float eb) {
 /* Full rule for a value that missed the fast test: escape if not finite or the rounded code is
  * 2^30 or more in magnitude; else keep the rounded code if accepted, else its neighbour toward
  * x if accepted, else escape; finally escape codes of 2^T or more in magnitude. */
-__device__ __attribute__((noinline)) int32_t quantize_slow(float x, float q0f, QParams qp, uint32_t *esc) {
+__device__ __forceinline__ int32_t quantize_slow(float x, float q0f, QParams qp, uint32_t *esc) {
     if (!(fabsf(q0f) < 1073741824.0f)) {
         *esc = 1;
         return 0;
@@ -137,19 +137,6 @@ __device__ __attribute__((noinline)) int32_t quantize_slow(float x, float q0f, Q
     }
     *esc = 0;
     return q;
-}
-
-/* q = rint(x * inv2eb) when that code is accepted and below 2^T (the common case). */
-__device__ __forceinline__ int32_t quantize(float x, const QParams &qp, uint32_t *esc) {
-    const float p = x * qp.r;
-    const float q0f = rintf(p);
-    const float y = q0f * qp.s;
-    const bool fast = (fabsf(q0f) < qp.tlim) && accept(x, y, qp.eb);
-    if (fast) {
-        *esc = 0;
-        return (int32_t)q0f;
-    }
-    return quantize_slow(x, q0f, qp, esc);
 }
 
 __device__ __forceinline__ uint32_t zigzag(int32_t d) {
@@ -192,85 +179,211 @@ __device__ void resolve_bound(float mn, float mx, double eps, DevInfo *info) {
     info->valid = valid;
 }
 
+/* Finite-only running min / max.  Non-finite values are replaced by the neutral element. */
 __device__ __forceinline__ void minmax_finite(float v, float &mn, float &mx) {
-    if (fabsf(v) <= FLT_MAX) {
-        mn = fminf(mn, v);
-        mx = fmaxf(mx, v);
-    }
+    const bool fin = fabsf(v) <= FLT_MAX;
+    mn = fminf(mn, fin ? v : INFINITY);
+    mx = fmaxf(mx, fin ? v : -INFINITY);
 }
 
-/* K1: min / max over the finite values; the last block to finish resolves the bound. */
-__global__ __launch_bounds__(256) void range_kernel(const float *__restrict__ x, uint64_t n,
-                                                    float *__restrict__ part, DevInfo *info,
-                                                    double eps) {
+__device__ __forceinline__ void minmax4(const float4 &a, float &mn, float &mx) {
+    minmax_finite(a.x, mn, mx);
+    minmax_finite(a.y, mn, mx);
+    minmax_finite(a.z, mn, mx);
+    minmax_finite(a.w, mn, mx);
+}
+
+constexpr int kRangeUnroll = 8;
+
+/* K1a: per-block min / max over the finite values.  The sweep runs from the end of the array
+ * to its start (iteration k of every thread reads the k-th stride from the end), so the front
+ * of the field is the most recently read when the encode kernel starts on it. */
+__global__ __launch_bounds__(256) void range_partial_kernel(const float *__restrict__ x, uint64_t n,
+                                                            float *__restrict__ part) {
     __shared__ float s_mn[4], s_mx[4];
-    __shared__ uint32_t s_last;
-    float mn = INFINITY, mx = -INFINITY;
+    float mn[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     const uint64_t n4 = n / 4;
     const float4 *x4 = reinterpret_cast<const float4 *>(x);
     const uint64_t tid = (uint64_t)blockIdx.x * 256 + threadIdx.x;
     const uint64_t stride = (uint64_t)gridDim.x * 256;
-    uint64_t i = tid;
-    for (; i + 3 * stride < n4; i += 4 * stride) {
-        const float4 a = x4[i], b = x4[i + stride], c = x4[i + 2 * stride], d = x4[i + 3 * stride];
-        minmax_finite(a.x, mn, mx); minmax_finite(a.y, mn, mx);
-        minmax_finite(a.z, mn, mx); minmax_finite(a.w, mn, mx);
-        minmax_finite(b.x, mn, mx); minmax_finite(b.y, mn, mx);
-        minmax_finite(b.z, mn, mx); minmax_finite(b.w, mn, mx);
-        minmax_finite(c.x, mn, mx); minmax_finite(c.y, mn, mx);
-        minmax_finite(c.z, mn, mx); minmax_finite(c.w, mn, mx);
-        minmax_finite(d.x, mn, mx); minmax_finite(d.y, mn, mx);
-        minmax_finite(d.z, mn, mx); minmax_finite(d.w, mn, mx);
+    uint64_t k = tid;
+    for (; k + (kRangeUnroll - 1) * stride < n4; k += kRangeUnroll * stride) {
+        float4 v[kRangeUnroll];
+#pragma unroll
+        for (int u = 0; u < kRangeUnroll; ++u) v[u] = x4[n4 - 1 - (k + u * stride)];
+#pragma unroll
+        for (int u = 0; u < kRangeUnroll; ++u) minmax4(v[u], mn[u & 3], mx[u & 3]);
     }
-    for (; i < n4; i += stride) {
-        const float4 a = x4[i];
-        minmax_finite(a.x, mn, mx); minmax_finite(a.y, mn, mx);
-        minmax_finite(a.z, mn, mx); minmax_finite(a.w, mn, mx);
-    }
-    if (tid < n - 4 * n4) minmax_finite(x[4 * n4 + tid], mn, mx);
+    for (; k < n4; k += stride) minmax4(x4[n4 - 1 - k], mn[0], mx[0]);
+    if (tid < n - 4 * n4) minmax_finite(x[4 * n4 + tid], mn[1], mx[1]);
+    float a = fminf(fminf(mn[0], mn[1]), fminf(mn[2], mn[3]));
+    float b = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
     for (int o = 32; o >= 1; o >>= 1) {
-        mn = fminf(mn, __shfl_xor(mn, o));
-        mx = fmaxf(mx, __shfl_xor(mx, o));
+        a = fminf(a, __shfl_xor(a, o));
+        b = fmaxf(b, __shfl_xor(b, o));
     }
     const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (lane == 0) { s_mn[wave] = mn; s_mx[wave] = mx; }
+    if (lane == 0) { s_mn[wave] = a; s_mx[wave] = b; }
     __syncthreads();
     if (threadIdx.x == 0) {
-        mn = fminf(fminf(s_mn[0], s_mn[1]), fminf(s_mn[2], s_mn[3]));
-        mx = fmaxf(fmaxf(s_mx[0], s_mx[1]), fmaxf(s_mx[2], s_mx[3]));
-        part[2 * blockIdx.x] = mn;
-        part[2 * blockIdx.x + 1] = mx;
-        __threadfence();
-        const uint32_t ticket = atomicInc(&info->range_ticket, gridDim.x - 1);
-        s_last = (ticket == gridDim.x - 1) ? 1u : 0u;
+        part[2 * blockIdx.x] = fminf(fminf(s_mn[0], s_mn[1]), fminf(s_mn[2], s_mn[3]));
+        part[2 * blockIdx.x + 1] = fmaxf(fmaxf(s_mx[0], s_mx[1]), fmaxf(s_mx[2], s_mx[3]));
     }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    mn = INFINITY;
-    mx = -INFINITY;
-    const uint32_t *pu = reinterpret_cast<const uint32_t *>(part);
-    for (uint32_t b = threadIdx.x; b < gridDim.x; b += 256) {
-        const float a = __uint_as_float(__hip_atomic_load(pu + 2 * b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        const float c = __uint_as_float(__hip_atomic_load(pu + 2 * b + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        mn = fminf(mn, a);
-        mx = fmaxf(mx, c);
+}
+
+/* K1b: one workgroup folds the per-block partials and resolves the bound. */
+__global__ __launch_bounds__(256) void range_resolve_kernel(const float *__restrict__ part, uint32_t nparts,
+                                                            DevInfo *info, double eps) {
+    __shared__ float s_mn[4], s_mx[4];
+    float a = INFINITY, b = -INFINITY;
+    for (uint32_t i = threadIdx.x; i < nparts; i += 256) {
+        a = fminf(a, part[2 * i]);
+        b = fmaxf(b, part[2 * i + 1]);
     }
     for (int o = 32; o >= 1; o >>= 1) {
-        mn = fminf(mn, __shfl_xor(mn, o));
-        mx = fmaxf(mx, __shfl_xor(mx, o));
+        a = fminf(a, __shfl_xor(a, o));
+        b = fmaxf(b, __shfl_xor(b, o));
     }
-    __syncthreads();
-    if (lane == 0) { s_mn[wave] = mn; s_mx[wave] = mx; }
+    const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0) { s_mn[wave] = a; s_mx[wave] = b; }
     __syncthreads();
     if (threadIdx.x == 0) {
-        mn = fminf(fminf(s_mn[0], s_mn[1]), fminf(s_mn[2], s_mn[3]));
-        mx = fmaxf(fmaxf(s_mx[0], s_mx[1]), fmaxf(s_mx[2], s_mx[3]));
-        resolve_bound(mn, mx, eps, info);
+        a = fminf(fminf(s_mn[0], s_mn[1]), fminf(s_mn[2], s_mn[3]));
+        b = fmaxf(fmaxf(s_mx[0], s_mx[1]), fmaxf(s_mx[2], s_mx[3]));
+        resolve_bound(a, b, eps, info);
     }
 }
 
 /* ---- K2: fused encode ------------------------------------------------------------------------ */
+
+/* Per-wave state of the chunk being encoded. */
+struct EncState {
+    int32_t carry;    /* code of the value before the tile (Lorenzo predecessor of lane 0) */
+    uint32_t words;   /* payload words of the chunk so far */
+    uint32_t escs;    /* escapes in the chunk so far */
+    uint32_t tmask;   /* tiles with at least one escape */
+};
+
+/* One tile of 256 values: 4 consecutive values per lane.  FULL = every value of the tile is
+ * below n (no tail masking). */
+template <bool FULL>
+__device__ __forceinline__ void encode_tile(const float4 v, uint64_t e0, uint64_t n, const QParams &qp,
+                                            uint32_t bmask, int t, uint32_t *pay, uint8_t *wid,
+                                            uint32_t *emask_tile, EncState &st) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t j = lane & 7;
+    const float xs[4] = {v.x, v.y, v.z, v.w};
+    float q0f[4];
+    int32_t q[4];
+    bool fast[4];
+    /* quantize: rint(x * inv2eb); the fast test (code below 2^T and accepted) is branch free */
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float p = xs[k] * qp.r;
+        q0f[k] = rintf(p);
+        const float y = q0f[k] * qp.s;
+        const float diff = xs[k] - y;
+        const float half_y = 0.5f * fabsf(y);
+        fast[k] = ((uint32_t)(fabsf(q0f[k]) < qp.tlim) & (uint32_t)(fabsf(diff) <= qp.eb) &
+                   (uint32_t)(fabsf(xs[k]) >= half_y)) != 0;
+        q[k] = (int32_t)q0f[k];
+    }
+    uint32_t esc = 0;
+    const bool all_fast = ((uint32_t)fast[0] & (uint32_t)fast[1] & (uint32_t)fast[2] & (uint32_t)fast[3]) != 0;
+    if (__ballot(!all_fast)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (!fast[k]) {
+                uint32_t e;
+                q[k] = quantize_slow(xs[k], q0f[k], qp, &e);
+                esc |= e << k;
+            }
+        }
+    }
+    /* Lorenzo: previous value's code (previous lane, or the carry for lane 0), 0 at a block start */
+    const int32_t prev = (int32_t)dpp<kDppWaveShr1>((uint32_t)st.carry, (uint32_t)q[3]);
+    const bool reset = ((uint32_t)e0 & bmask) == 0;
+    uint32_t z[4];
+    z[0] = zigzag(reset ? q[0] : q[0] - prev);
+    z[1] = zigzag(q[1] - q[0]);
+    z[2] = zigzag(q[2] - q[1]);
+    z[3] = zigzag(q[3] - q[2]);
+    st.carry = (int32_t)readlane((uint32_t)q[3], 63);
+    if (!FULL) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (e0 + k >= n) z[k] = 0;
+    }
+    /* segment width: bit length of the OR of its 32 codes */
+    const uint32_t orv = or8(z[0] | z[1] | z[2] | z[3]);
+    const uint32_t w = orv ? 32u - (uint32_t)__builtin_clz(orv) : 0u;
+    /* word offset of the segment in the chunk: scan of widths over the tile's 8 segments */
+    const uint32_t incl = wave_incl_scan(j == 0 ? w : 0u);
+    const uint32_t seg_words = st.words + incl - w;
+    wid[t * 8 + (lane >> 3)] = (uint8_t)w;
+    /* pack: value k of lane j sits at bit (4j + k) w of its segment.  The lane's 4w bits are
+     * emitted low word first; only words holding bits are OR-ed into LDS (at most 5, and only
+     * the first and last can be shared with a neighbouring lane). */
+    const uint32_t bitpos = 32u * seg_words + 4u * w * j;
+    uint32_t wi = bitpos >> 5;
+    uint32_t nb = bitpos & 31u;
+    uint64_t acc = (uint64_t)z[0] << nb;
+    nb += w;
+#pragma unroll
+    for (int k = 1; k <= 4; ++k) {
+        if (nb >= 32) {
+            lds_or(pay + wi, (uint32_t)acc);
+            ++wi;
+            acc >>= 32;
+            nb -= 32;
+        }
+        if (k < 4) {
+            acc |= (uint64_t)z[k] << nb;
+            nb += w;
+        }
+    }
+    if (nb > 0) lds_or(pay + wi, (uint32_t)acc);
+    st.words += readlane(incl, 63);
+    /* escapes: per-segment bitmask (element 4j + k of the segment) and counts */
+    if (__ballot(esc != 0)) {
+        const uint32_t segm = or8(esc << (4 * j));
+        if (j == 0) emask_tile[lane >> 3] = segm;
+        st.escs += (uint32_t)(__popcll(__ballot(esc & 1u)) + __popcll(__ballot(esc & 2u)) +
+                              __popcll(__ballot(esc & 4u)) + __popcll(__ballot(esc & 8u)));
+        st.tmask |= 1u << t;
+    }
+}
+
+template <bool FULL>
+__device__ __forceinline__ void encode_chunk(const float *__restrict__ x, uint64_t cbase, uint64_t n,
+                                             const QParams &qp, uint32_t bmask, uint32_t *pay,
+                                             uint8_t *wid, uint32_t *emask_chunk, EncState &st) {
+    const uint32_t lane = threadIdx.x & 63;
+    float4 v[kTilesPerChunk];
+    if (FULL) {
+        const float4 *src = reinterpret_cast<const float4 *>(x + cbase) + lane;
+#pragma unroll
+        for (int t = 0; t < kTilesPerChunk; ++t) v[t] = src[t * (kTile / 4)];
+    } else {
+#pragma unroll
+        for (int t = 0; t < kTilesPerChunk; ++t) {
+            const uint64_t e = cbase + (uint64_t)t * kTile + 4 * lane;
+            v[t].x = e + 0 < n ? x[e + 0] : 0.0f;
+            v[t].y = e + 1 < n ? x[e + 1] : 0.0f;
+            v[t].z = e + 2 < n ? x[e + 2] : 0.0f;
+            v[t].w = e + 3 < n ? x[e + 3] : 0.0f;
+        }
+    }
+    wave_lds_sync();
+    const uint32_t ntiles = FULL ? kTilesPerChunk : (uint32_t)((n - cbase + kTile - 1) / kTile);
+#pragma unroll
+    for (int t = 0; t < kTilesPerChunk; ++t) {
+        if (FULL || (uint32_t)t < ntiles)
+            encode_tile<FULL>(v[t], cbase + (uint64_t)t * kTile + 4 * lane, n, qp, bmask, t, pay, wid,
+                              emask_chunk + t * 8, st);
+    }
+}
 
 /* One wave per chunk.  Per tile: quantize 4 values per lane, Lorenzo delta against the previous
  * value (previous lane by wave_shr, previous tile by a carried code, 0 at a block start),
@@ -281,7 +394,7 @@ __global__ __launch_bounds__(256) void range_kernel(const float *__restrict__ x,
 __global__ __launch_bounds__(kBlockThreads) void encode_kernel(
     const float *__restrict__ x, PlanArgs pa, Workspace ws, uint8_t *__restrict__ widths_dst,
     uint64_t widths_bytes) {
-    __shared__ uint4 s_pay4[kWavesPerBlock][kChunk / 4];
+    __shared__ uint4 s_pay4[kWavesPerBlock][kChunk / 4 + 1];
     __shared__ uint4 s_wid4[kWavesPerBlock][kSegsPerChunk / 16];
     __shared__ uint32_t s_grp[2][kWavesPerBlock];
 
@@ -289,7 +402,7 @@ __global__ __launch_bounds__(kBlockThreads) void encode_kernel(
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t c = blockIdx.x * kWavesPerBlock + wave;
     const DevInfo *info = ws.info;
-    uint32_t words = 0, escs = 0, tmask = 0;
+    EncState st = {0, 0, 0, 0};
 
     if (c < pa.nchunks && info->valid) {
         QParams qp;
@@ -304,116 +417,30 @@ __global__ __launch_bounds__(kBlockThreads) void encode_kernel(
 #pragma unroll
         for (int i = 0; i < kChunk / 4 / kWave; ++i) s_pay4[wave][lane + kWave * i] = zero4;
         if (lane < kSegsPerChunk / 16) s_wid4[wave][lane] = zero4;
-
         const uint64_t cbase = (uint64_t)c * kChunk;
-        const uint64_t n = pa.n;
-        const bool full = cbase + kChunk <= n;
-        const uint32_t ntiles = full ? kTilesPerChunk : (uint32_t)((n - cbase + kTile - 1) / kTile);
-        float4 v[kTilesPerChunk];
-        if (full) {
-            const float4 *src = reinterpret_cast<const float4 *>(x + cbase) + lane;
-#pragma unroll
-            for (int t = 0; t < kTilesPerChunk; ++t) v[t] = src[t * (kTile / 4)];
-        } else {
-#pragma unroll
-            for (int t = 0; t < kTilesPerChunk; ++t) {
-                const uint64_t e = cbase + (uint64_t)t * kTile + 4 * lane;
-                v[t].x = e + 0 < n ? x[e + 0] : 0.0f;
-                v[t].y = e + 1 < n ? x[e + 1] : 0.0f;
-                v[t].z = e + 2 < n ? x[e + 2] : 0.0f;
-                v[t].w = e + 3 < n ? x[e + 3] : 0.0f;
-            }
-        }
-        wave_lds_sync();
-
-        const uint32_t j = lane & 7;
-        const uint32_t seg_in_tile = lane >> 3;
-        const uint32_t bmask = pa.B - 1;
-        int32_t carry = 0;
-#pragma unroll
-        for (int t = 0; t < kTilesPerChunk; ++t) {
-            if ((uint32_t)t < ntiles) {
-                const uint64_t e0 = cbase + (uint64_t)t * kTile + 4 * lane;
-                const float xs[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
-                int32_t q[4];
-                uint32_t esc = 0;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    uint32_t e;
-                    q[k] = quantize(xs[k], qp, &e);
-                    esc |= e << k;
-                }
-                /* Lorenzo with a reset at block starts */
-                const int32_t prev = (int32_t)dpp<kDppWaveShr1>((uint32_t)carry, (uint32_t)q[3]);
-                const bool reset = ((uint32_t)e0 & bmask) == 0;
-                int32_t d[4];
-                d[0] = reset ? q[0] : q[0] - prev;
-                d[1] = q[1] - q[0];
-                d[2] = q[2] - q[1];
-                d[3] = q[3] - q[2];
-                carry = (int32_t)readlane((uint32_t)q[3], 63);
-                uint32_t z[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    z[k] = zigzag(d[k]);
-                    if (!full && e0 + k >= n) z[k] = 0;
-                }
-                /* segment width and word offsets */
-                const uint32_t orv = or8(z[0] | z[1] | z[2] | z[3]);
-                const uint32_t w = orv ? 32u - (uint32_t)__builtin_clz(orv) : 0u;
-                const uint32_t incl = wave_incl_scan(j == 0 ? w : 0u);
-                const uint32_t seg_excl = incl - w;
-                const uint32_t tile_words = readlane(incl, 63);
-                if (j == 0) wid[t * 8 + seg_in_tile] = (uint8_t)w;
-                /* pack: value k of this lane sits at bit 32*(words+seg_excl) + (4j+k)*w */
-                const uint32_t bitpos = 32u * (words + seg_excl) + 4u * w * j;
-                uint32_t wi = bitpos >> 5;
-                uint32_t nb = bitpos & 31u;
-                uint64_t acc = (uint64_t)z[0] << nb;
-                nb += w;
-#pragma unroll
-                for (int k = 1; k <= 4; ++k) {
-                    if (nb >= 32) {
-                        lds_or(pay + wi, (uint32_t)acc);
-                        ++wi;
-                        acc >>= 32;
-                        nb -= 32;
-                    }
-                    if (k < 4) {
-                        acc |= (uint64_t)z[k] << nb;
-                        nb += w;
-                    }
-                }
-                if (nb > 0) lds_or(pay + wi, (uint32_t)acc);
-                /* escapes: per-segment bitmask, counts */
-                if (__ballot(esc != 0)) {
-                    const uint32_t segm = or8(esc << (4 * j));
-                    if (j == 0) ws.emask[(cbase >> 5) + (uint32_t)t * 8 + seg_in_tile] = segm;
-                    escs += (uint32_t)(__popcll(__ballot(esc & 1u)) + __popcll(__ballot(esc & 2u)) +
-                                       __popcll(__ballot(esc & 4u)) + __popcll(__ballot(esc & 8u)));
-                    tmask |= 1u << t;
-                }
-                words += tile_words;
-            }
-        }
+        uint32_t *emask_chunk = ws.emask + (uint64_t)c * kSegsPerChunk;
+        if (cbase + kChunk <= pa.n)
+            encode_chunk<true>(x, cbase, pa.n, qp, pa.B - 1, pay, wid, emask_chunk, st);
+        else
+            encode_chunk<false>(x, cbase, pa.n, qp, pa.B - 1, pay, wid, emask_chunk, st);
         wave_lds_sync();
         /* chunk payload -> scratch slot, widths -> stream (or staging) */
         uint4 *dst = reinterpret_cast<uint4 *>(ws.scratch + cbase);
-        const uint32_t nvec = (words + 3) >> 2;
+        const uint32_t nvec = (st.words + 3) >> 2;
         for (uint32_t i = lane; i < nvec; i += kWave) dst[i] = s_pay4[wave][i];
         if (lane < kSegsPerChunk / 16) {
             const uint64_t off = (uint64_t)c * kSegsPerChunk + 16u * lane;
             if (off < widths_bytes) *reinterpret_cast<uint4 *>(widths_dst + off) = s_wid4[wave][lane];
         }
         if (lane == 0) {
-            ws.chunk_words[c] = words;
-            ws.chunk_esc[c] = escs;
-            ws.chunk_tmask[c] = tmask;
+            ws.chunk_words[c] = st.words;
+            ws.chunk_esc[c] = st.escs;
+            ws.chunk_tmask[c] = st.tmask;
         }
     }
     if (lane == 0) {
-        s_grp[0][wave] = words;
-        s_grp[1][wave] = escs;
+        s_grp[0][wave] = st.words;
+        s_grp[1][wave] = st.escs;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -851,10 +878,13 @@ __global__ __launch_bounds__(256) void patch_kernel(const uint8_t *__restrict__ 
 
 hipError_t launch_range(const float *x, const PlanArgs &pa, const Workspace &ws, double eps,
                         hipStream_t stream) {
-    uint64_t want = (pa.n / 4 + 256 * 8 - 1) / (256 * 8);
-    uint32_t grid = (uint32_t)(want < 1 ? 1 : (want > (uint64_t)kRangeBlocksMax ? kRangeBlocksMax : want));
-    hipLaunchKernelGGL(range_kernel, dim3(grid), dim3(256), 0, stream, x, pa.n, ws.range_part,
-                       ws.info, eps);
+    const uint64_t want = (pa.n / 4 + 256 * 16 - 1) / (256 * 16);
+    const uint32_t grid = (uint32_t)(want < 1 ? 1 : (want > (uint64_t)kRangeBlocksMax ? kRangeBlocksMax : want));
+    hipLaunchKernelGGL(range_partial_kernel, dim3(grid), dim3(256), 0, stream, x, pa.n, ws.range_part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(range_resolve_kernel, dim3(1), dim3(256), 0, stream, ws.range_part, grid, ws.info,
+                       eps);
     return hipGetLastError();
 }
 
