@@ -127,7 +127,7 @@ eblc_status parse_options(const char *opts, Options *o) {
                 o->eps = v;
             } else if (key == "block") {
                 uint64_t b;
-                if (seen_block || !parse_u64(val, &b) || b < 32 || b > (uint64_t)kChunk || (b & (b - 1)) != 0)
+                if (seen_block || !parse_u64(val, &b) || b < 32 || b > (uint64_t)kMaxBlock || (b & (b - 1)) != 0)
                     return EBLC_INVALID_ARGUMENT;
                 seen_block = true;
                 o->B = (uint32_t)b;
@@ -251,12 +251,15 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     pa.rank = (uint32_t)rank;
     pa.B = o.B;
     pa.T = o.T;
-    pa.nchunks = (uint32_t)((n + kChunk - 1) / kChunk);
-    pa.ngroups = (pa.nchunks + kChunksPerGroup - 1) / kChunksPerGroup;
+    pa.nchunks = (uint32_t)((n + kEncChunk - 1) / kEncChunk);
+    pa.ngroups = (pa.nchunks + kEncChunksPerGroup - 1) / kEncChunksPerGroup;
+    pa.dchunks = (uint32_t)((n + kDecChunk - 1) / kDecChunk);
+    pa.dgroups = (pa.dchunks + kDecChunksPerGroup - 1) / kDecChunksPerGroup;
     pa.side_max = o.side_max;
 
     /* workspace: one allocation, carved into 256-byte aligned arrays */
-    const uint64_t nc = pa.nchunks, ng = pa.ngroups;
+    const uint64_t nc = pa.nchunks > pa.dchunks ? pa.nchunks : pa.dchunks;
+    const uint64_t ng = pa.ngroups > pa.dgroups ? pa.ngroups : pa.dgroups;
     uint64_t off = 0;
     auto carve = [&](uint64_t bytes) {
         const uint64_t at = off;
@@ -264,13 +267,13 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
         return at;
     };
     const uint64_t o_info = carve(sizeof(DevInfo));
-    const uint64_t o_scratch = carve(nc * kChunk * 4);
+    const uint64_t o_scratch = carve(nc * kEncChunk * 4);
     const uint64_t o_cw = carve(nc * 4), o_ce = carve(nc * 4), o_ct = carve(nc * 4);
     const uint64_t o_gw = carve(ng * 4), o_ge = carve(ng * 4);
     const uint64_t o_pw = carve(ng * 4), o_pe = carve(ng * 4);
-    const uint64_t o_em = carve(nc * kSegsPerChunk * 4);
-    const uint64_t o_wd = carve(nc * kSegsPerChunk);
-    const uint64_t o_rp = carve(2 * kRangeBlocksMax * 4);
+    const uint64_t o_em = carve(nc * kEncSegs * 4);
+    const uint64_t o_wd = carve(nc * kEncSegs);
+    const uint64_t o_rp = carve(2 * (uint64_t)range_blocks(n) * 4);
     if (hipMalloc(&p->ws_base, off) != hipSuccess) {
         delete p;
         return EBLC_OUT_OF_MEMORY;

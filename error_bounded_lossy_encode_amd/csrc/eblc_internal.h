@@ -2,12 +2,18 @@
  * eblc_internal.h -- shared between the host plan code and the gfx950 kernels of libeblc.so.
  *
  * Work decomposition (all sizes in 32-bit values):
- *   tile   = 256 values = one wave64 step, 4 consecutive values per lane (one 128-bit load)
- *   chunk  = 8 tiles = 2048 values = 64 bitpack segments; one wave owns one chunk
- *   group  = 4 chunks = one 256-thread workgroup; the device-wide scan runs over groups
- * The Lorenzo block B is a power of two in [32, 2048], so every chunk starts a block and the
- * only cross-wave dependency of the codec is the exclusive scan of payload sizes and outlier
- * counts.
+ *   compress:   tile  = one wave64 step, kEncLaneVals consecutive values per lane (128-bit
+ *                       loads), so a 32-value bitpack segment is kSegLanes lanes
+ *               chunk = kEncTiles tiles; one wave owns one chunk
+ *               group = kEncWaves chunks = one encode workgroup
+ *   decompress: tile  = 256 values, 4 consecutive values per lane, a segment is 8 lanes
+ *               chunk = 8 tiles = 2048 values = 64 segments; one wave owns one chunk
+ *               group = 4 chunks = one 256-thread workgroup
+ * Both groups hold 8192 values; the device-wide scans run over groups.  The Lorenzo block B is
+ * a power of two in [32, 2048].  A decode chunk always starts a block; an encode chunk that
+ * does not (B larger than the chunk) takes its first prediction from the code of the value
+ * before it.  The only other cross-wave dependency is the exclusive scan of payload sizes and
+ * outlier counts.
  */
 #ifndef EBLC_INTERNAL_H
 #define EBLC_INTERNAL_H
@@ -19,14 +25,28 @@ namespace eblc {
 
 constexpr int kWave = 64;
 constexpr int kTile = 256;
-constexpr int kTilesPerChunk = 8;
-constexpr int kChunk = kTile * kTilesPerChunk;   /* 2048 values */
-constexpr int kSegsPerChunk = kChunk / 32;       /* 64 segments */
+constexpr int kEncLaneVals = 4;                  /* consecutive values per lane on compress */
+constexpr int kEncTile = kWave * kEncLaneVals;
+constexpr int kSegLanes = 32 / kEncLaneVals;     /* lanes per segment on compress */
+constexpr int kSegsPerEncTile = kEncTile / 32;
+constexpr int kEncChunk = 2048;                  /* values per encode chunk */
+constexpr int kEncTiles = kEncChunk / kEncTile;
+constexpr int kEncSegs = kEncChunk / 32;
+constexpr int kEncWaves = 8192 / kEncChunk;       /* waves (chunks) per encode workgroup */
+constexpr int kEncThreads = kWave * kEncWaves;
+constexpr int kEncChunksPerGroup = kEncWaves;
+constexpr int kDecTiles = 8;
+constexpr int kDecChunk = kTile * kDecTiles;     /* 2048 values */
+constexpr int kDecSegs = kDecChunk / 32;         /* 64 segments */
+constexpr int kMaxBlock = kDecChunk;             /* largest Lorenzo block */
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
-constexpr int kChunksPerGroup = kWavesPerBlock;
+constexpr int kDecChunksPerGroup = kWavesPerBlock;
 constexpr int kScanThreads = 1024;
-constexpr int kRangeBlocksMax = 2048;
+constexpr int kScanItems = 16;                   /* items per scan thread per round */
+constexpr int kRangeThreads = 256;
+constexpr int kRangeVec = 16;                    /* float4 loads per range thread */
+constexpr uint64_t kRangeSpan = (uint64_t)kRangeThreads * kRangeVec; /* float4 per range block */
 constexpr int kPatchBlocksMax = 1024;
 constexpr uint32_t kHeaderBytes = 128;
 constexpr uint32_t kMagic = 0x434C4245u;          /* "EBLC" */
@@ -63,27 +83,34 @@ struct PlanArgs {
     uint32_t rank;
     uint32_t B;             /* Lorenzo block, power of two 32..2048 */
     uint32_t T;             /* outlier log2 */
-    uint32_t nchunks;
-    uint32_t ngroups;
-    uint32_t pad_;
+    uint32_t nchunks;       /* encode chunks */
+    uint32_t ngroups;       /* encode groups */
+    uint32_t dchunks;       /* decode chunks */
+    uint32_t dgroups;       /* decode groups */
     uint64_t side_max;
 };
 
 /* Workspace pointers (all device memory owned by the plan). */
 struct Workspace {
     DevInfo *info;
-    uint32_t *scratch;       /* nchunks * kChunk words: per-chunk packed payload slots */
-    uint32_t *chunk_words;   /* [nchunks] payload words per chunk */
-    uint32_t *chunk_esc;     /* [nchunks] escapes per chunk */
-    uint32_t *chunk_tmask;   /* [nchunks] bit t set if tile t of the chunk has an escape */
+    uint32_t *scratch;       /* nchunks * kEncChunk words: per-chunk packed payload slots */
+    uint32_t *chunk_words;   /* [nchunks] payload words per chunk (encode or decode chunks) */
+    uint32_t *chunk_esc;     /* [nchunks] escapes per encode chunk */
+    uint32_t *chunk_tmask;   /* [nchunks] bit t set if tile t of the encode chunk has an escape */
     uint32_t *group_words;   /* [ngroups] */
     uint32_t *group_esc;     /* [ngroups] */
     uint32_t *gpre_words;    /* [ngroups] exclusive prefix */
     uint32_t *gpre_esc;      /* [ngroups] exclusive prefix */
-    uint32_t *emask;         /* [nchunks * 64] escape bitmask per segment (tiles with escapes) */
-    uint8_t *widths;         /* [nchunks * 64] widths staging when the output is too small */
-    float *range_part;       /* [2 * kRangeBlocksMax] per-block min / max */
+    uint32_t *emask;         /* [nchunks * kEncSegs] escape bitmask per segment (tiles with escapes) */
+    uint8_t *widths;         /* [nchunks * kEncSegs] widths staging when the output is too small */
+    float *range_part;       /* [2 * range_blocks(n)] per-block min / max */
 };
+
+/* Workgroups of the range pass: one per kRangeSpan float4 (16384 values), at least one. */
+inline uint32_t range_blocks(uint64_t n) {
+    const uint64_t b = (n / 4 + kRangeSpan - 1) / kRangeSpan;
+    return (uint32_t)(b < 1 ? 1 : b);
+}
 
 /* Kernel launchers (eblc_kernels.hip).  All enqueue on `stream` and return the launch error. */
 hipError_t launch_range(const float *x, const PlanArgs &pa, const Workspace &ws, double eps,

@@ -43,14 +43,6 @@ __device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xf, BOUND_CTRL);
 }
 
-/* OR over the 8 lanes of an aligned 8-lane group (one 32-value segment). */
-__device__ __forceinline__ uint32_t or8(uint32_t v) {
-    v |= dpp<kDppQuadXor1>(0, v);
-    v |= dpp<kDppQuadXor2>(0, v);
-    v |= dpp<kDppRowHalfMirror>(0, v);
-    return v;
-}
-
 /* Inclusive prefix sum over the 64 lanes (row-local Hillis-Steele, then row broadcasts). */
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
     v += dpp<kDppRowShr1, 0xf, true>(0, v);
@@ -95,6 +87,31 @@ __device__ __forceinline__ void lds_or(uint32_t *p, uint32_t v) {
 }
 
 __device__ __forceinline__ uint64_t align16(uint64_t v) { return (v + 15u) & ~(uint64_t)15u; }
+
+/* Non-temporal 128-bit global access, for data streamed exactly once (the field on compress,
+ * the reconstruction on decompress): the lines bypass cache allocation. */
+typedef float v4f32 __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 ld_nt(const float4 *p) {
+    const v4f32 t = __builtin_nontemporal_load(reinterpret_cast<const v4f32 *>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
+}
+
+__device__ __forceinline__ uint4 ld_nt(const uint4 *p) {
+    const v4u32 t = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+__device__ __forceinline__ void st_nt(float4 *p, const float4 &v) {
+    const v4f32 t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<v4f32 *>(p));
+}
+
+__device__ __forceinline__ void st_nt(uint4 *p, const uint4 &v) {
+    const v4u32 t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<v4u32 *>(p));
+}
 
 /* ---- quantizer ------------------------------------------------------------------------------ */
 
@@ -193,30 +210,33 @@ __device__ __forceinline__ void minmax4(const float4 &a, float &mn, float &mx) {
     minmax_finite(a.w, mn, mx);
 }
 
-constexpr int kRangeUnroll = 8;
-
-/* K1a: per-block min / max over the finite values.  The sweep runs from the end of the array
- * to its start (iteration k of every thread reads the k-th stride from the end), so the front
- * of the field is the most recently read when the encode kernel starts on it. */
-__global__ __launch_bounds__(256) void range_partial_kernel(const float *__restrict__ x, uint64_t n,
-                                                            float *__restrict__ part) {
-    __shared__ float s_mn[4], s_mx[4];
+/* K1a: per-workgroup min / max over the finite values.  Workgroup b reads float4 elements
+ * [b kRangeSpan, (b + 1) kRangeSpan), 16 per thread, all issued before any is used, with
+ * non-temporal loads: the field is streamed once and must not evict what the caches hold (on
+ * gfx950 a plain load of a line also forces out dirty lines left by earlier writes, which
+ * halves the read rate).  The last workgroup also takes the n mod 4 trailing values. */
+__global__ __launch_bounds__(kRangeThreads) void range_partial_kernel(const float *__restrict__ x,
+                                                                      uint64_t n,
+                                                                      float *__restrict__ part) {
+    __shared__ float s_mn[kRangeThreads / kWave], s_mx[kRangeThreads / kWave];
     float mn[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
     float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     const uint64_t n4 = n / 4;
     const float4 *x4 = reinterpret_cast<const float4 *>(x);
-    const uint64_t tid = (uint64_t)blockIdx.x * 256 + threadIdx.x;
-    const uint64_t stride = (uint64_t)gridDim.x * 256;
-    uint64_t k = tid;
-    for (; k + (kRangeUnroll - 1) * stride < n4; k += kRangeUnroll * stride) {
-        float4 v[kRangeUnroll];
+    const uint64_t base = (uint64_t)blockIdx.x * kRangeSpan + threadIdx.x;
+    if (base + (uint64_t)(kRangeVec - 1) * kRangeThreads < n4) {
+        float4 v[kRangeVec];
 #pragma unroll
-        for (int u = 0; u < kRangeUnroll; ++u) v[u] = x4[n4 - 1 - (k + u * stride)];
+        for (int u = 0; u < kRangeVec; ++u) v[u] = ld_nt(x4 + base + (uint64_t)u * kRangeThreads);
 #pragma unroll
-        for (int u = 0; u < kRangeUnroll; ++u) minmax4(v[u], mn[u & 3], mx[u & 3]);
+        for (int u = 0; u < kRangeVec; ++u) minmax4(v[u], mn[u & 3], mx[u & 3]);
+    } else {
+        for (int u = 0; u < kRangeVec; ++u) {
+            const uint64_t i = base + (uint64_t)u * kRangeThreads;
+            if (i < n4) minmax4(ld_nt(x4 + i), mn[u & 3], mx[u & 3]);
+        }
     }
-    for (; k < n4; k += stride) minmax4(x4[n4 - 1 - k], mn[0], mx[0]);
-    if (tid < n - 4 * n4) minmax_finite(x[4 * n4 + tid], mn[1], mx[1]);
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x < (n & 3u)) minmax_finite(x[4 * n4 + threadIdx.x], mn[1], mx[1]);
     float a = fminf(fminf(mn[0], mn[1]), fminf(mn[2], mn[3]));
     float b = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
     for (int o = 32; o >= 1; o >>= 1) {
@@ -227,19 +247,25 @@ __global__ __launch_bounds__(256) void range_partial_kernel(const float *__restr
     if (lane == 0) { s_mn[wave] = a; s_mx[wave] = b; }
     __syncthreads();
     if (threadIdx.x == 0) {
-        part[2 * blockIdx.x] = fminf(fminf(s_mn[0], s_mn[1]), fminf(s_mn[2], s_mn[3]));
-        part[2 * blockIdx.x + 1] = fmaxf(fmaxf(s_mx[0], s_mx[1]), fmaxf(s_mx[2], s_mx[3]));
+        for (int w = 1; w < kRangeThreads / kWave; ++w) {
+            a = fminf(a, s_mn[w]);
+            b = fmaxf(b, s_mx[w]);
+        }
+        part[2 * blockIdx.x] = a;
+        part[2 * blockIdx.x + 1] = b;
     }
 }
 
-/* K1b: one workgroup folds the per-block partials and resolves the bound. */
-__global__ __launch_bounds__(256) void range_resolve_kernel(const float *__restrict__ part, uint32_t nparts,
-                                                            DevInfo *info, double eps) {
-    __shared__ float s_mn[4], s_mx[4];
+/* K1b: one workgroup folds the per-workgroup partials and resolves the bound. */
+__global__ __launch_bounds__(kScanThreads) void range_resolve_kernel(const float *__restrict__ part,
+                                                                     uint32_t nparts, DevInfo *info,
+                                                                     double eps) {
+    __shared__ float s_mn[kScanThreads / kWave], s_mx[kScanThreads / kWave];
     float a = INFINITY, b = -INFINITY;
-    for (uint32_t i = threadIdx.x; i < nparts; i += 256) {
-        a = fminf(a, part[2 * i]);
-        b = fmaxf(b, part[2 * i + 1]);
+    for (uint32_t i = threadIdx.x; i < nparts; i += kScanThreads) {
+        const float2 v = reinterpret_cast<const float2 *>(part)[i];
+        a = fminf(a, v.x);
+        b = fmaxf(b, v.y);
     }
     for (int o = 32; o >= 1; o >>= 1) {
         a = fminf(a, __shfl_xor(a, o));
@@ -249,160 +275,215 @@ __global__ __launch_bounds__(256) void range_resolve_kernel(const float *__restr
     if (lane == 0) { s_mn[wave] = a; s_mx[wave] = b; }
     __syncthreads();
     if (threadIdx.x == 0) {
-        a = fminf(fminf(s_mn[0], s_mn[1]), fminf(s_mn[2], s_mn[3]));
-        b = fmaxf(fmaxf(s_mx[0], s_mx[1]), fmaxf(s_mx[2], s_mx[3]));
+        for (int w = 1; w < kScanThreads / kWave; ++w) {
+            a = fminf(a, s_mn[w]);
+            b = fmaxf(b, s_mx[w]);
+        }
         resolve_bound(a, b, eps, info);
     }
 }
 
 /* ---- K2: fused encode ------------------------------------------------------------------------ */
 
-/* Per-wave state of the chunk being encoded. */
+/* Per-wave totals of the chunk being encoded. */
 struct EncState {
-    int32_t carry;    /* code of the value before the tile (Lorenzo predecessor of lane 0) */
-    uint32_t words;   /* payload words of the chunk so far */
-    uint32_t escs;    /* escapes in the chunk so far */
+    uint32_t words;   /* payload words of the chunk */
+    uint32_t escs;    /* escapes in the chunk */
     uint32_t tmask;   /* tiles with at least one escape */
 };
 
-/* One tile of 256 values: 4 consecutive values per lane.  FULL = every value of the tile is
- * below n (no tail masking). */
+/* OR over the kSegLanes lanes (4 or 8, aligned) holding one 32-value segment on compress. */
+__device__ __forceinline__ uint32_t seg_or(uint32_t v) {
+    v |= dpp<kDppQuadXor1>(0, v);
+    v |= dpp<kDppQuadXor2>(0, v);
+    if (kSegLanes == 8) v |= dpp<kDppRowHalfMirror>(0, v);
+    return v;
+}
+
+/* Codes of one encode tile: kEncLaneVals consecutive values per lane.  Quantize
+ * (rint(x inv2eb), kept when a branch-free test passes; the full rule runs only in a wave where
+ * some value misses it), Lorenzo delta against the previous value (the previous lane's last
+ * value by wave_shr, the previous tile's through `carry`, 0 when `reset`), zigzag.  Writes the
+ * lane's zigzag codes to z and returns the bit width of its 32-value segment (kSegLanes
+ * lanes). */
 template <bool FULL>
-__device__ __forceinline__ void encode_tile(const float4 v, uint64_t e0, uint64_t n, const QParams &qp,
-                                            uint32_t bmask, int t, uint32_t *pay, uint8_t *wid,
-                                            uint32_t *emask_tile, EncState &st) {
+__device__ __forceinline__ uint32_t code_tile(const float xs[kEncLaneVals], uint64_t e0, uint64_t n,
+                                              const QParams &qp, bool reset, int t,
+                                              uint32_t *emask_tile, int32_t &carry,
+                                              uint32_t z[kEncLaneVals], EncState &st) {
+    constexpr int V = kEncLaneVals;
     const uint32_t lane = threadIdx.x & 63;
-    const uint32_t j = lane & 7;
-    const float xs[4] = {v.x, v.y, v.z, v.w};
-    float q0f[4];
-    int32_t q[4];
-    bool fast[4];
-    /* quantize: rint(x * inv2eb); the fast test (code below 2^T and accepted) is branch free */
+    const uint32_t j = lane & (kSegLanes - 1);
+    /* Fast test: rint(x inv2eb) is kept when its reconstruction is within eb and the lane's
+     * largest code is below 2^T.  This is the full rule's first acceptance exactly: its extra
+     * clause |x| >= |y|/2 cannot fail here.  For q0 = 0 it is trivial; for |q0| >= 2, |y| >=
+     * 4 eb and a rounded |x - y| <= eb forces |x - y| <= 2 eb; for |q0| = 1, rint gives 1 only
+     * when f32(x r) > 1/2, which with r within 2^-24 of 1/(2 eb) puts x above the largest float
+     * below eb.  NaN fails the eb test, infinities the 2^T test. */
+    float q0f[V];
+    int32_t q[V];
+    bool within[V];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < V; ++k) {
         const float p = xs[k] * qp.r;
         q0f[k] = rintf(p);
         const float y = q0f[k] * qp.s;
-        const float diff = xs[k] - y;
-        const float half_y = 0.5f * fabsf(y);
-        fast[k] = ((uint32_t)(fabsf(q0f[k]) < qp.tlim) & (uint32_t)(fabsf(diff) <= qp.eb) &
-                   (uint32_t)(fabsf(xs[k]) >= half_y)) != 0;
+        within[k] = fabsf(xs[k] - y) <= qp.eb;
         q[k] = (int32_t)q0f[k];
     }
-    uint32_t esc = 0;
-    const bool all_fast = ((uint32_t)fast[0] & (uint32_t)fast[1] & (uint32_t)fast[2] & (uint32_t)fast[3]) != 0;
-    if (__ballot(!all_fast)) {
+    float qmax = fabsf(q0f[0]);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (!fast[k]) {
+    for (int k = 1; k < V; ++k) qmax = fmaxf(qmax, fabsf(q0f[k]));
+    uint32_t all_within = 1;
+#pragma unroll
+    for (int k = 0; k < V; ++k) all_within &= (uint32_t)within[k];
+    const bool lane_fast = ((uint32_t)(qmax < qp.tlim) & all_within) != 0;
+    if (__ballot(!lane_fast)) {
+        uint32_t esc = 0;
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            if (!(within[k] && fabsf(q0f[k]) < qp.tlim)) {
                 uint32_t e;
                 q[k] = quantize_slow(xs[k], q0f[k], qp, &e);
                 esc |= e << k;
             }
         }
+        /* escapes: per-segment bitmask (value V j + k of the segment) and counts */
+        if (__ballot(esc != 0)) {
+            const uint32_t segm = seg_or(esc << (V * j));
+            if (j == 0) emask_tile[lane / kSegLanes] = segm;
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int k = 0; k < V; ++k) cnt += (uint32_t)__popcll(__ballot((esc >> k) & 1u));
+            st.escs += cnt;
+            st.tmask |= 1u << t;
+        }
     }
-    /* Lorenzo: previous value's code (previous lane, or the carry for lane 0), 0 at a block start */
-    const int32_t prev = (int32_t)dpp<kDppWaveShr1>((uint32_t)st.carry, (uint32_t)q[3]);
-    const bool reset = ((uint32_t)e0 & bmask) == 0;
-    uint32_t z[4];
+    const int32_t prev = (int32_t)dpp<kDppWaveShr1>((uint32_t)carry, (uint32_t)q[V - 1]);
     z[0] = zigzag(reset ? q[0] : q[0] - prev);
-    z[1] = zigzag(q[1] - q[0]);
-    z[2] = zigzag(q[2] - q[1]);
-    z[3] = zigzag(q[3] - q[2]);
-    st.carry = (int32_t)readlane((uint32_t)q[3], 63);
+#pragma unroll
+    for (int k = 1; k < V; ++k) z[k] = zigzag(q[k] - q[k - 1]);
+    carry = (int32_t)readlane((uint32_t)q[V - 1], 63);
     if (!FULL) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < V; ++k)
             if (e0 + k >= n) z[k] = 0;
     }
     /* segment width: bit length of the OR of its 32 codes */
-    const uint32_t orv = or8(z[0] | z[1] | z[2] | z[3]);
-    const uint32_t w = orv ? 32u - (uint32_t)__builtin_clz(orv) : 0u;
-    /* word offset of the segment in the chunk: scan of widths over the tile's 8 segments */
-    const uint32_t incl = wave_incl_scan(j == 0 ? w : 0u);
-    const uint32_t seg_words = st.words + incl - w;
-    wid[t * 8 + (lane >> 3)] = (uint8_t)w;
-    /* pack: value k of lane j sits at bit (4j + k) w of its segment.  The lane's 4w bits are
-     * emitted low word first; only words holding bits are OR-ed into LDS (at most 5, and only
-     * the first and last can be shared with a neighbouring lane). */
-    const uint32_t bitpos = 32u * seg_words + 4u * w * j;
-    uint32_t wi = bitpos >> 5;
-    uint32_t nb = bitpos & 31u;
-    uint64_t acc = (uint64_t)z[0] << nb;
-    nb += w;
+    uint32_t orv = z[0];
 #pragma unroll
-    for (int k = 1; k <= 4; ++k) {
-        if (nb >= 32) {
-            lds_or(pay + wi, (uint32_t)acc);
-            ++wi;
-            acc >>= 32;
-            nb -= 32;
+    for (int k = 1; k < V; ++k) orv |= z[k];
+    orv = seg_or(orv);
+    return orv ? 32u - (uint32_t)__builtin_clz(orv) : 0u;
+}
+
+/* OR n consecutive codes of width w, already joined into `bits` (code k at bit k w), into the
+ * LDS payload at bit position pos: the bits land in at most two words. */
+__device__ __forceinline__ void or_bits(uint32_t *pay, uint32_t pos, uint32_t bits) {
+    const uint64_t sh = (uint64_t)bits << (pos & 31u);
+    uint32_t *p = pay + (pos >> 5);
+    lds_or(p, (uint32_t)sh);
+    lds_or(p + 1, (uint32_t)(sh >> 32));
+}
+
+/* OR one lane's kEncLaneVals codes of width w into the chunk's LDS payload; code k of the lane
+ * sits at bit bit0 + k w (little-endian words, low bits first).  Codes are first joined into
+ * registers of at most 32 bits -- four at a time up to width 8, two up to width 16, else one --
+ * and each register lands in at most two words.  Only a lane's first and last word can be
+ * shared with its neighbours, hence the OR. */
+__device__ __forceinline__ void pack_lane(const uint32_t z[kEncLaneVals], uint32_t w, uint32_t bit0,
+                                          uint32_t *pay) {
+    if (w > 16) {
+#pragma unroll
+        for (int k = 0; k < kEncLaneVals; ++k) or_bits(pay, bit0 + (uint32_t)k * w, z[k]);
+    } else if (w > 8) {
+#pragma unroll
+        for (int k = 0; k < kEncLaneVals; k += 2) or_bits(pay, bit0 + (uint32_t)k * w, z[k] | (z[k + 1] << w));
+    } else if (w != 0) {
+#pragma unroll
+        for (int k = 0; k < kEncLaneVals; k += 4) {
+            const uint32_t joined = z[k] | (z[k + 1] << w) | (z[k + 2] << (2 * w)) | (z[k + 3] << (3 * w));
+            or_bits(pay, bit0 + (uint32_t)k * w, joined);
         }
-        if (k < 4) {
-            acc |= (uint64_t)z[k] << nb;
-            nb += w;
-        }
-    }
-    if (nb > 0) lds_or(pay + wi, (uint32_t)acc);
-    st.words += readlane(incl, 63);
-    /* escapes: per-segment bitmask (element 4j + k of the segment) and counts */
-    if (__ballot(esc != 0)) {
-        const uint32_t segm = or8(esc << (4 * j));
-        if (j == 0) emask_tile[lane >> 3] = segm;
-        st.escs += (uint32_t)(__popcll(__ballot(esc & 1u)) + __popcll(__ballot(esc & 2u)) +
-                              __popcll(__ballot(esc & 4u)) + __popcll(__ballot(esc & 8u)));
-        st.tmask |= 1u << t;
     }
 }
 
+/* One encode chunk of kEncTiles tiles.  Pass 1 codes every tile and records the segment widths
+ * in LDS (the codes stay in VGPRs); one wave scan of the widths gives every segment's word
+ * offset in the chunk; pass 2 packs each tile at those offsets.  `carry` is the code of the
+ * value before the chunk when the chunk does not start a Lorenzo block. */
 template <bool FULL>
 __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, uint64_t cbase, uint64_t n,
-                                             const QParams &qp, uint32_t bmask, uint32_t *pay,
-                                             uint8_t *wid, uint32_t *emask_chunk, EncState &st) {
+                                             const QParams &qp, uint32_t bmask, int32_t carry,
+                                             uint32_t *pay, uint8_t *wid, uint32_t *emask_chunk,
+                                             EncState &st) {
+    constexpr int V = kEncLaneVals;
     const uint32_t lane = threadIdx.x & 63;
-    float4 v[kTilesPerChunk];
+    const uint32_t j = lane & (kSegLanes - 1), g = lane / kSegLanes;
+    float xs[kEncTiles][V];
     if (FULL) {
-        const float4 *src = reinterpret_cast<const float4 *>(x + cbase) + lane;
+        const float4 *src = reinterpret_cast<const float4 *>(x + cbase) + (V / 4) * lane;
 #pragma unroll
-        for (int t = 0; t < kTilesPerChunk; ++t) v[t] = src[t * (kTile / 4)];
+        for (int t = 0; t < kEncTiles; ++t) {
+#pragma unroll
+            for (int h = 0; h < V / 4; ++h) {
+                const float4 a = ld_nt(src + t * (kEncTile / 4) + h);
+                xs[t][4 * h] = a.x; xs[t][4 * h + 1] = a.y; xs[t][4 * h + 2] = a.z; xs[t][4 * h + 3] = a.w;
+            }
+        }
     } else {
 #pragma unroll
-        for (int t = 0; t < kTilesPerChunk; ++t) {
-            const uint64_t e = cbase + (uint64_t)t * kTile + 4 * lane;
-            v[t].x = e + 0 < n ? x[e + 0] : 0.0f;
-            v[t].y = e + 1 < n ? x[e + 1] : 0.0f;
-            v[t].z = e + 2 < n ? x[e + 2] : 0.0f;
-            v[t].w = e + 3 < n ? x[e + 3] : 0.0f;
+        for (int t = 0; t < kEncTiles; ++t) {
+            const uint64_t e = cbase + (uint64_t)t * kEncTile + V * lane;
+#pragma unroll
+            for (int k = 0; k < V; ++k) xs[t][k] = e + k < n ? x[e + k] : 0.0f;
+        }
+    }
+    const uint32_t ntiles = FULL ? kEncTiles : (uint32_t)((n - cbase + kEncTile - 1) / kEncTile);
+    /* a lane's first value starts a block when its offset in the tile does and the tile does */
+    const bool lane_at_block = ((V * lane) & bmask) == 0;
+    uint32_t z[kEncTiles][V];
+    uint32_t w[kEncTiles];
+#pragma unroll
+    for (int t = 0; t < kEncTiles; ++t) {
+        if (FULL || (uint32_t)t < ntiles) {
+            const bool reset = lane_at_block && (((uint32_t)cbase + (uint32_t)t * kEncTile) & bmask) == 0;
+            w[t] = code_tile<FULL>(xs[t], cbase + (uint64_t)t * kEncTile + V * lane, n, qp, reset, t,
+                                   emask_chunk + t * kSegsPerEncTile, carry, z[t], st);
+            if (j == 0) wid[t * kSegsPerEncTile + g] = (uint8_t)w[t];
         }
     }
     wave_lds_sync();
-    const uint32_t ntiles = FULL ? kTilesPerChunk : (uint32_t)((n - cbase + kTile - 1) / kTile);
+    const uint32_t wl = lane < (uint32_t)kEncSegs ? (uint32_t)wid[lane] : 0u;
+    const uint32_t incl = wave_incl_scan(wl);
+    const uint32_t excl = incl - wl;
+    st.words = readlane(incl, kEncSegs - 1);
 #pragma unroll
-    for (int t = 0; t < kTilesPerChunk; ++t) {
-        if (FULL || (uint32_t)t < ntiles)
-            encode_tile<FULL>(v[t], cbase + (uint64_t)t * kTile + 4 * lane, n, qp, bmask, t, pay, wid,
-                              emask_chunk + t * 8, st);
+    for (int t = 0; t < kEncTiles; ++t) {
+        if (FULL || (uint32_t)t < ntiles) {
+            const uint32_t off =
+                (uint32_t)__builtin_amdgcn_ds_bpermute((int)((t * kSegsPerEncTile + g) * 4), (int)excl);
+            pack_lane(z[t], w[t], 32u * off + (uint32_t)V * w[t] * j, pay);
+        }
     }
 }
 
-/* One wave per chunk.  Per tile: quantize 4 values per lane, Lorenzo delta against the previous
- * value (previous lane by wave_shr, previous tile by a carried code, 0 at a block start),
- * zigzag, the segment width from an 8-lane OR, the segment's word offset from a wave scan, and
- * the packed bits OR-ed into the chunk's LDS buffer.  Outputs: the chunk's words in its scratch
- * slot, its 64 width bytes, its word and escape counts, the escape bitmask of every tile that
- * has an escape, and per-workgroup sums for the scan. */
-__global__ __launch_bounds__(kBlockThreads) void encode_kernel(
+/* One wave per encode chunk, kEncWaves chunks per workgroup.  Outputs per chunk: its packed
+ * words in its scratch slot, its width bytes (into the stream, or into staging when the output
+ * buffer cannot hold them), its word and escape counts and the escape bitmask of every tile
+ * with an escape; per workgroup, the sums the device-wide scan runs over. */
+__global__ __launch_bounds__(kEncThreads) void encode_kernel(
     const float *__restrict__ x, PlanArgs pa, Workspace ws, uint8_t *__restrict__ widths_dst,
     uint64_t widths_bytes) {
-    __shared__ uint4 s_pay4[kWavesPerBlock][kChunk / 4 + 1];
-    __shared__ uint4 s_wid4[kWavesPerBlock][kSegsPerChunk / 16];
-    __shared__ uint32_t s_grp[2][kWavesPerBlock];
+    __shared__ uint4 s_pay4[kEncWaves][kEncChunk / 4 + 1];
+    __shared__ uint4 s_wid4[kEncWaves][kEncSegs / 16];
+    __shared__ uint32_t s_grp[2][kEncWaves];
 
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = threadIdx.x >> 6;
-    const uint32_t c = blockIdx.x * kWavesPerBlock + wave;
+    const uint32_t c = blockIdx.x * kEncWaves + wave;
     const DevInfo *info = ws.info;
-    EncState st = {0, 0, 0, 0};
+    EncState st = {0, 0, 0};
 
     if (c < pa.nchunks && info->valid) {
         QParams qp;
@@ -415,21 +496,32 @@ __global__ __launch_bounds__(kBlockThreads) void encode_kernel(
         uint8_t *wid = reinterpret_cast<uint8_t *>(s_wid4[wave]);
         const uint4 zero4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < kChunk / 4 / kWave; ++i) s_pay4[wave][lane + kWave * i] = zero4;
-        if (lane < kSegsPerChunk / 16) s_wid4[wave][lane] = zero4;
-        const uint64_t cbase = (uint64_t)c * kChunk;
-        uint32_t *emask_chunk = ws.emask + (uint64_t)c * kSegsPerChunk;
-        if (cbase + kChunk <= pa.n)
-            encode_chunk<true>(x, cbase, pa.n, qp, pa.B - 1, pay, wid, emask_chunk, st);
+        for (int i = 0; i < kEncChunk / 4 / kWave; ++i) s_pay4[wave][lane + kWave * i] = zero4;
+        if (lane < kEncSegs / 16) s_wid4[wave][lane] = zero4;
+        wave_lds_sync();
+        const uint64_t cbase = (uint64_t)c * kEncChunk;
+        const uint32_t bmask = pa.B - 1;
+        /* Lorenzo predecessor of the chunk's first value: 0 at a block start, else the code of
+         * the value before the chunk (0 if that value escapes) */
+        int32_t carry = 0;
+        if (((uint32_t)cbase & bmask) != 0) {
+            const float xp = x[cbase - 1];
+            uint32_t e;
+            const int32_t qprev = quantize_slow(xp, rintf(xp * qp.r), qp, &e);
+            carry = e ? 0 : qprev;
+        }
+        uint32_t *emask_chunk = ws.emask + (uint64_t)c * kEncSegs;
+        if (cbase + kEncChunk <= pa.n)
+            encode_chunk<true>(x, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk, st);
         else
-            encode_chunk<false>(x, cbase, pa.n, qp, pa.B - 1, pay, wid, emask_chunk, st);
+            encode_chunk<false>(x, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk, st);
         wave_lds_sync();
         /* chunk payload -> scratch slot, widths -> stream (or staging) */
         uint4 *dst = reinterpret_cast<uint4 *>(ws.scratch + cbase);
         const uint32_t nvec = (st.words + 3) >> 2;
         for (uint32_t i = lane; i < nvec; i += kWave) dst[i] = s_pay4[wave][i];
-        if (lane < kSegsPerChunk / 16) {
-            const uint64_t off = (uint64_t)c * kSegsPerChunk + 16u * lane;
+        if (lane < kEncSegs / 16) {
+            const uint64_t off = (uint64_t)c * kEncSegs + 16u * lane;
             if (off < widths_bytes) *reinterpret_cast<uint4 *>(widths_dst + off) = s_wid4[wave][lane];
         }
         if (lane == 0) {
@@ -444,53 +536,94 @@ __global__ __launch_bounds__(kBlockThreads) void encode_kernel(
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        ws.group_words[blockIdx.x] = s_grp[0][0] + s_grp[0][1] + s_grp[0][2] + s_grp[0][3];
-        ws.group_esc[blockIdx.x] = s_grp[1][0] + s_grp[1][1] + s_grp[1][2] + s_grp[1][3];
+        uint32_t sw = 0, se = 0;
+#pragma unroll
+        for (int k = 0; k < kEncWaves; ++k) {
+            sw += s_grp[0][k];
+            se += s_grp[1][k];
+        }
+        ws.group_words[blockIdx.x] = sw;
+        ws.group_esc[blockIdx.x] = se;
     }
 }
 
 /* ---- K3 / K6b: single-workgroup exclusive scan over groups -------------------------------- */
 
-/* Exclusive prefix of a[0..ng) and b[0..ng) into pa_out / pb_out; returns the totals in
- * tot[0], tot[1] (visible to every thread after the call).  1024 threads, 4 items each per
- * round. */
+/* Exclusive prefix of a[0..ng) and b[0..ng) (b may be null) into pa_out / pb_out; returns the
+ * totals in tot[0], tot[1] (valid in every thread).  Each round covers kScanThreads *
+ * kScanItems items: a thread loads 16 consecutive items with 128-bit loads (the arrays are
+ * 256-byte aligned), sums them, the sums are scanned across the wave with DPP and across the
+ * 16 waves through LDS, and the thread writes its 16 exclusive prefixes back. */
 __device__ void block_scan2(const uint32_t *__restrict__ a, const uint32_t *__restrict__ b,
                             uint32_t *__restrict__ pa_out, uint32_t *__restrict__ pb_out,
                             uint32_t ng, uint32_t *tot) {
-    __shared__ uint32_t s_wa[kScanThreads / kWave], s_wb[kScanThreads / kWave];
+    constexpr int kWaves = kScanThreads / kWave;
+    constexpr int kV = kScanItems / 4;
+    __shared__ uint32_t s_wa[kWaves], s_wb[kWaves];
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t carry_a = 0, carry_b = 0;
-    for (uint32_t base = 0; base < ng; base += 4 * kScanThreads) {
-        const uint32_t i0 = base + 4 * tid;
-        uint32_t va[4], vb[4];
+    for (uint32_t base = 0; base < ng; base += kScanThreads * kScanItems) {
+        const uint32_t i0 = base + kScanItems * tid;
+        uint32_t va[kScanItems], vb[kScanItems];
+        if (i0 + kScanItems <= ng) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            va[k] = (i0 + k < ng) ? a[i0 + k] : 0u;
-            vb[k] = (b != nullptr && i0 + k < ng) ? b[i0 + k] : 0u;
+            for (int k = 0; k < kV; ++k) {
+                const uint4 t = reinterpret_cast<const uint4 *>(a + i0)[k];
+                va[4 * k] = t.x; va[4 * k + 1] = t.y; va[4 * k + 2] = t.z; va[4 * k + 3] = t.w;
+                const uint4 u = b != nullptr ? reinterpret_cast<const uint4 *>(b + i0)[k] : make_uint4(0, 0, 0, 0);
+                vb[4 * k] = u.x; vb[4 * k + 1] = u.y; vb[4 * k + 2] = u.z; vb[4 * k + 3] = u.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kScanItems; ++k) {
+                va[k] = (i0 + k < ng) ? a[i0 + k] : 0u;
+                vb[k] = (b != nullptr && i0 + k < ng) ? b[i0 + k] : 0u;
+            }
         }
-        const uint32_t ta = va[0] + va[1] + va[2] + va[3];
-        const uint32_t tb = vb[0] + vb[1] + vb[2] + vb[3];
+        uint32_t ta = 0, tb = 0;
+#pragma unroll
+        for (int k = 0; k < kScanItems; ++k) {
+            ta += va[k];
+            tb += vb[k];
+        }
         const uint32_t ia = wave_incl_scan(ta);
         const uint32_t ib = wave_incl_scan(tb);
         if (lane == 63) { s_wa[wave] = ia; s_wb[wave] = ib; }
         __syncthreads();
         uint32_t oa = 0, ob = 0, sa = 0, sb = 0;
-        for (uint32_t w = 0; w < kScanThreads / kWave; ++w) {
+#pragma unroll
+        for (uint32_t w = 0; w < (uint32_t)kWaves; ++w) {
             const uint32_t xa = s_wa[w], xb = s_wb[w];
-            if (w < wave) { oa += xa; ob += xb; }
+            oa += (w < wave) ? xa : 0u;
+            ob += (w < wave) ? xb : 0u;
             sa += xa;
             sb += xb;
         }
         uint32_t ea = carry_a + oa + ia - ta;
         uint32_t eb = carry_b + ob + ib - tb;
+        uint32_t pa[kScanItems], pb[kScanItems];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (i0 + k < ng) {
-                pa_out[i0 + k] = ea;
-                if (pb_out != nullptr) pb_out[i0 + k] = eb;
-            }
+        for (int k = 0; k < kScanItems; ++k) {
+            pa[k] = ea;
+            pb[k] = eb;
             ea += va[k];
             eb += vb[k];
+        }
+        if (i0 + kScanItems <= ng) {
+#pragma unroll
+            for (int k = 0; k < kV; ++k) {
+                reinterpret_cast<uint4 *>(pa_out + i0)[k] = make_uint4(pa[4 * k], pa[4 * k + 1], pa[4 * k + 2], pa[4 * k + 3]);
+                if (pb_out != nullptr)
+                    reinterpret_cast<uint4 *>(pb_out + i0)[k] = make_uint4(pb[4 * k], pb[4 * k + 1], pb[4 * k + 2], pb[4 * k + 3]);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kScanItems; ++k) {
+                if (i0 + k < ng) {
+                    pa_out[i0 + k] = pa[k];
+                    if (pb_out != nullptr) pb_out[i0 + k] = pb[k];
+                }
+            }
         }
         carry_a += sa;
         carry_b += sb;
@@ -565,67 +698,96 @@ __global__ __launch_bounds__(kScanThreads) void scan_compress_kernel(PlanArgs pa
 
 /* Word offset of chunk c in the packed payload (or outlier rank), from the group prefix plus
  * the chunks before c in its group. */
+template <int CPG>
 __device__ __forceinline__ uint32_t chunk_offset(const uint32_t *gpre, const uint32_t *per_chunk,
                                                  uint32_t c) {
-    const uint32_t g = c / kChunksPerGroup;
+    const uint32_t g = c / CPG;
     uint32_t o = gpre[g];
-    for (uint32_t k = g * kChunksPerGroup; k < c; ++k) o += per_chunk[k];
+    for (uint32_t k = g * CPG; k < c; ++k) o += per_chunk[k];
     return o;
 }
 
 /* ---- K4: compaction of the scratch slots (or the RAW copy) -------------------------------- */
 
+/* One workgroup per group of kEncChunksPerGroup encode chunks.  The group's payload words are
+ * contiguous in the stream (at the group's scanned offset), so its 256 threads copy them as one
+ * run: word i of the run comes from the chunk whose prefix range holds i.  In RAW mode the
+ * workgroup copies the group's input values instead.  The last group also zeroes the pad after
+ * the payload. */
 __global__ __launch_bounds__(kBlockThreads) void compact_kernel(const float *__restrict__ x,
                                                                 PlanArgs pa, Workspace ws,
                                                                 uint8_t *__restrict__ out,
                                                                 const uint8_t *__restrict__ widths_src) {
-    const uint32_t lane = threadIdx.x & 63;
-    const uint32_t c = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    if (c >= pa.nchunks) return;
+    constexpr int CPG = kEncChunksPerGroup;
+    __shared__ uint32_t s_o[CPG + 1];
+    const uint32_t tid = threadIdx.x;
+    const uint32_t grp = blockIdx.x;
     const DevInfo *info = ws.info;
     if (!info->fits) return;
     const uint64_t n = pa.n;
-    const uint64_t cbase = (uint64_t)c * kChunk;
-    const bool last = c == pa.nchunks - 1;
+    const uint64_t gbase = (uint64_t)grp * CPG * kEncChunk;
+    const bool last = grp == pa.ngroups - 1;
     if (info->mode == 1) {
-        const uint64_t cnt = (n - cbase < (uint64_t)kChunk) ? n - cbase : (uint64_t)kChunk;
-        uint32_t *dstw = reinterpret_cast<uint32_t *>(out + kHeaderBytes) + cbase;
-        const uint32_t *srcw = reinterpret_cast<const uint32_t *>(x) + cbase;
-        if (cnt == (uint64_t)kChunk) {
+        constexpr uint32_t kGroupVals = CPG * kEncChunk;
+        const uint64_t cnt = (n - gbase < (uint64_t)kGroupVals) ? n - gbase : (uint64_t)kGroupVals;
+        uint32_t *dstw = reinterpret_cast<uint32_t *>(out + kHeaderBytes) + gbase;
+        const uint32_t *srcw = reinterpret_cast<const uint32_t *>(x) + gbase;
+        if (cnt == (uint64_t)kGroupVals) {
+            constexpr int kPer = kGroupVals / 4 / kBlockThreads;
             const uint4 *s4 = reinterpret_cast<const uint4 *>(srcw);
             uint4 *d4 = reinterpret_cast<uint4 *>(dstw);
+            uint4 t[kPer];
 #pragma unroll
-            for (int i = 0; i < kChunk / 4 / kWave; ++i) d4[lane + kWave * i] = s4[lane + kWave * i];
+            for (int i = 0; i < kPer; ++i) t[i] = ld_nt(s4 + tid + kBlockThreads * i);
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) st_nt(d4 + tid + kBlockThreads * i, t[i]);
         } else {
-            for (uint32_t i = lane; i < cnt; i += kWave) dstw[i] = srcw[i];
+            for (uint32_t i = tid; i < cnt; i += kBlockThreads) dstw[i] = srcw[i];
         }
         if (last) {
             const uint64_t end = kHeaderBytes + 4 * n;
             const uint64_t pad = align16(4 * n) - 4 * n;
-            if (lane < pad / 4) reinterpret_cast<uint32_t *>(out + end)[lane] = 0u;
+            if (tid < pad / 4) reinterpret_cast<uint32_t *>(out + end)[tid] = 0u;
         }
         return;
     }
-    const uint32_t W = chunk_offset(ws.gpre_words, ws.chunk_words, c);
-    const uint32_t P = ws.chunk_words[c];
-    uint32_t *dst = reinterpret_cast<uint32_t *>(out + info->payload_off) + W;
-    const uint32_t *src = ws.scratch + cbase;
-    for (uint32_t i = lane; i < P; i += kWave) dst[i] = src[i];
-    if (widths_src != nullptr && lane < kSegsPerChunk / 16) {
-        const uint64_t off = (uint64_t)c * kSegsPerChunk + 16u * lane;
-        if (off < align16(pa.nseg))
-            *reinterpret_cast<uint4 *>(out + kHeaderBytes + off) =
-                *reinterpret_cast<const uint4 *>(widths_src + off);
+    const uint32_t c0 = grp * CPG;
+    if (tid == 0) {
+        uint32_t o = 0;
+        s_o[0] = 0;
+        for (int k = 0; k < CPG; ++k) {
+            o += (c0 + k < pa.nchunks) ? ws.chunk_words[c0 + k] : 0u;
+            s_o[k + 1] = o;
+        }
+    }
+    __syncthreads();
+    const uint32_t total = s_o[CPG];
+    uint32_t *dst = reinterpret_cast<uint32_t *>(out + info->payload_off) + ws.gpre_words[grp];
+    for (uint32_t i = tid; i < total; i += kBlockThreads) {
+        uint32_t k = 0;
+#pragma unroll
+        for (int b = CPG / 2; b >= 1; b /= 2)
+            if (i >= s_o[k + b]) k += b;
+        dst[i] = ws.scratch[(uint64_t)(c0 + k) * kEncChunk + (i - s_o[k])];
+    }
+    if (widths_src != nullptr) {
+        constexpr uint32_t kGroupWidthVecs = CPG * kEncSegs / 16;
+        const uint64_t off = (uint64_t)c0 * kEncSegs + 16u * tid;
+        if (tid < kGroupWidthVecs && off < align16(pa.nseg))
+            *reinterpret_cast<uint4 *>(out + kHeaderBytes + off) = *reinterpret_cast<const uint4 *>(widths_src + off);
     }
     if (last) {
         const uint64_t pend = info->payload_off + 4 * info->payload_words;
         const uint64_t pad = info->oidx_off - pend;
-        if (lane < pad / 4) reinterpret_cast<uint32_t *>(out + pend)[lane] = 0u;
+        if (tid < pad / 4) reinterpret_cast<uint32_t *>(out + pend)[tid] = 0u;
     }
 }
 
 /* ---- K5: outliers in index order ------------------------------------------------------------ */
 
+/* One wave per encode chunk with escapes: lane l < 32 owns segment l of the chunk, takes its
+ * escape bitmask, ranks its escapes after the chunk's scanned offset and the lanes before it,
+ * and writes (index, raw bits) in ascending index order. */
 __global__ __launch_bounds__(kBlockThreads) void outlier_kernel(const float *__restrict__ x,
                                                                 PlanArgs pa, Workspace ws,
                                                                 uint8_t *__restrict__ out) {
@@ -645,12 +807,12 @@ __global__ __launch_bounds__(kBlockThreads) void outlier_kernel(const float *__r
         }
     }
     if (ws.chunk_esc[c] == 0) return;
-    const uint32_t O = chunk_offset(ws.gpre_esc, ws.chunk_esc, c);
+    const uint32_t O = chunk_offset<kEncChunksPerGroup>(ws.gpre_esc, ws.chunk_esc, c);
     const uint32_t tm = ws.chunk_tmask[c];
-    uint32_t mask = ((tm >> (lane >> 3)) & 1u) ? ws.emask[(uint64_t)c * kSegsPerChunk + lane] : 0u;
+    uint32_t mask = (lane < (uint32_t)kEncSegs && ((tm >> (lane / kSegsPerEncTile)) & 1u)) ? ws.emask[(uint64_t)c * kEncSegs + lane] : 0u;
     const uint32_t cnt = (uint32_t)__popc(mask);
     uint32_t rank = O + wave_incl_scan(cnt) - cnt;
-    const uint64_t segbase = (uint64_t)c * kChunk + 32u * lane;
+    const uint64_t segbase = (uint64_t)c * kEncChunk + 32u * lane;
     const uint32_t *xb = reinterpret_cast<const uint32_t *>(x);
     while (mask) {
         const uint32_t bit = (uint32_t)__builtin_ctz(mask);
@@ -664,17 +826,17 @@ __global__ __launch_bounds__(kBlockThreads) void outlier_kernel(const float *__r
 
 /* ---- K6a: decode sizes ---------------------------------------------------------------------- */
 
-/* One thread per chunk: payload words of the chunk = sum of its width bytes; a width above 32
+/* One thread per decode chunk: payload words of the chunk = sum of its width bytes; a width above 32
  * flags the stream.  Quads of threads form the groups the scan runs over. */
 __global__ __launch_bounds__(256) void decode_sizes_kernel(const uint8_t *__restrict__ in,
                                                            PlanArgs pa, Workspace ws) {
     const uint32_t c = blockIdx.x * 256 + threadIdx.x;
     uint32_t sum = 0, bad = 0;
-    if (c < pa.nchunks) {
-        const uint64_t s0 = (uint64_t)c * kSegsPerChunk;
-        const uint64_t segs = (pa.nseg - s0 < (uint64_t)kSegsPerChunk) ? pa.nseg - s0 : (uint64_t)kSegsPerChunk;
+    if (c < pa.dchunks) {
+        const uint64_t s0 = (uint64_t)c * kDecSegs;
+        const uint64_t segs = (pa.nseg - s0 < (uint64_t)kDecSegs) ? pa.nseg - s0 : (uint64_t)kDecSegs;
         const uint8_t *wp = in + kHeaderBytes + s0;
-        if (segs == (uint64_t)kSegsPerChunk) {
+        if (segs == (uint64_t)kDecSegs) {
             const uint4 *w4 = reinterpret_cast<const uint4 *>(wp);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -698,7 +860,7 @@ __global__ __launch_bounds__(256) void decode_sizes_kernel(const uint8_t *__rest
     uint32_t g = sum;
     g += dpp<kDppQuadXor1>(0, g);
     g += dpp<kDppQuadXor2>(0, g);
-    if ((threadIdx.x & 3) == 0 && c / kChunksPerGroup < pa.ngroups) ws.group_words[c / kChunksPerGroup] = g;
+    if ((threadIdx.x & 3) == 0 && c / kDecChunksPerGroup < pa.dgroups) ws.group_words[c / kDecChunksPerGroup] = g;
     if (bad) atomicOr(&ws.info->width_bad, 1u);
 }
 
@@ -712,7 +874,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_decompress_kernel(const uin
                                                                        uint64_t in_bytes, PlanArgs pa,
                                                                        Workspace ws) {
     uint32_t tot[2];
-    block_scan2(ws.group_words, nullptr, ws.gpre_words, nullptr, pa.ngroups, tot);
+    block_scan2(ws.group_words, nullptr, ws.gpre_words, nullptr, pa.dgroups, tot);
     if (threadIdx.x != 0) return;
     DevInfo *info = ws.info;
     const uint32_t *h = reinterpret_cast<const uint32_t *>(in);
@@ -760,34 +922,37 @@ __global__ __launch_bounds__(kScanThreads) void scan_decompress_kernel(const uin
 __global__ __launch_bounds__(kBlockThreads) void decode_kernel(const uint8_t *__restrict__ in,
                                                                PlanArgs pa, Workspace ws,
                                                                float *__restrict__ out) {
-    __shared__ uint4 s_pay4[kWavesPerBlock][kChunk / 4 + 2];
-    __shared__ uint32_t s_w[kWavesPerBlock][kSegsPerChunk];
-    __shared__ uint32_t s_so[kWavesPerBlock][kSegsPerChunk];
+    __shared__ uint4 s_pay4[kWavesPerBlock][kDecChunk / 4 + 2];
+    __shared__ uint32_t s_w[kWavesPerBlock][kDecSegs];
+    __shared__ uint32_t s_so[kWavesPerBlock][kDecSegs];
 
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t c = blockIdx.x * kWavesPerBlock + wave;
-    if (c >= pa.nchunks) return;
+    if (c >= pa.dchunks) return;
     const DevInfo *info = ws.info;
     if (info->err) return;
     const uint64_t n = pa.n;
-    const uint64_t cbase = (uint64_t)c * kChunk;
-    const bool full = cbase + kChunk <= n;
+    const uint64_t cbase = (uint64_t)c * kDecChunk;
+    const bool full = cbase + kDecChunk <= n;
     if (info->mode == 1) {
-        const uint64_t cnt = full ? (uint64_t)kChunk : n - cbase;
+        const uint64_t cnt = full ? (uint64_t)kDecChunk : n - cbase;
         const uint32_t *srcw = reinterpret_cast<const uint32_t *>(in + kHeaderBytes) + cbase;
         uint32_t *dstw = reinterpret_cast<uint32_t *>(out) + cbase;
         if (full) {
             const uint4 *s4 = reinterpret_cast<const uint4 *>(srcw);
             uint4 *d4 = reinterpret_cast<uint4 *>(dstw);
+            uint4 t[kDecChunk / 4 / kWave];
 #pragma unroll
-            for (int i = 0; i < kChunk / 4 / kWave; ++i) d4[lane + kWave * i] = s4[lane + kWave * i];
+            for (int i = 0; i < kDecChunk / 4 / kWave; ++i) t[i] = ld_nt(s4 + lane + kWave * i);
+#pragma unroll
+            for (int i = 0; i < kDecChunk / 4 / kWave; ++i) st_nt(d4 + lane + kWave * i, t[i]);
         } else {
             for (uint32_t i = lane; i < cnt; i += kWave) dstw[i] = srcw[i];
         }
         return;
     }
-    const uint32_t W = chunk_offset(ws.gpre_words, ws.chunk_words, c);
+    const uint32_t W = chunk_offset<kDecChunksPerGroup>(ws.gpre_words, ws.chunk_words, c);
     const uint32_t P = ws.chunk_words[c];
     const uint64_t sw = info->payload_off / 4 + W; /* stream word index of the chunk's first word */
     const uint64_t a0 = sw & ~(uint64_t)3;
@@ -795,7 +960,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(const uint8_t *__
     const uint32_t units = (lb + P + 3) >> 2;
     const uint4 *src = reinterpret_cast<const uint4 *>(in) + a0 / 4;
     for (uint32_t u = lane; u < units; u += kWave) s_pay4[wave][u] = src[u];
-    const uint64_t seg = (uint64_t)c * kSegsPerChunk + lane;
+    const uint64_t seg = (uint64_t)c * kDecSegs + lane;
     const uint32_t wl = seg < pa.nseg ? (uint32_t)in[kHeaderBytes + seg] : 0u;
     const uint32_t so = wave_incl_scan(wl) - wl;
     s_w[wave][lane] = wl;
@@ -807,11 +972,11 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(const uint8_t *__
     const uint32_t B = pa.B;
     const uint32_t seglen = (B / 4 < 64u) ? B / 4 : 64u;
     const uint32_t dist = lane & (seglen - 1);
-    const uint32_t ntiles = full ? kTilesPerChunk : (uint32_t)((n - cbase + kTile - 1) / kTile);
+    const uint32_t ntiles = full ? kDecTiles : (uint32_t)((n - cbase + kTile - 1) / kTile);
     const uint32_t j = lane & 7;
     int32_t carry = 0;
 #pragma unroll
-    for (int t = 0; t < kTilesPerChunk; ++t) {
+    for (int t = 0; t < kDecTiles; ++t) {
         if ((uint32_t)t < ntiles) {
             const uint32_t g = (uint32_t)t * 8 + (lane >> 3);
             const uint32_t w = s_w[wave][g];
@@ -842,7 +1007,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(const uint8_t *__
             o.w = (float)q[3] * s;
             const uint64_t e0 = cbase + (uint64_t)t * kTile + 4 * lane;
             if (full) {
-                *reinterpret_cast<float4 *>(out + e0) = o;
+                st_nt(reinterpret_cast<float4 *>(out + e0), o);
             } else {
                 if (e0 + 0 < n) out[e0 + 0] = o.x;
                 if (e0 + 1 < n) out[e0 + 1] = o.y;
@@ -878,19 +1043,19 @@ __global__ __launch_bounds__(256) void patch_kernel(const uint8_t *__restrict__ 
 
 hipError_t launch_range(const float *x, const PlanArgs &pa, const Workspace &ws, double eps,
                         hipStream_t stream) {
-    const uint64_t want = (pa.n / 4 + 256 * 16 - 1) / (256 * 16);
-    const uint32_t grid = (uint32_t)(want < 1 ? 1 : (want > (uint64_t)kRangeBlocksMax ? kRangeBlocksMax : want));
-    hipLaunchKernelGGL(range_partial_kernel, dim3(grid), dim3(256), 0, stream, x, pa.n, ws.range_part);
+    const uint32_t grid = range_blocks(pa.n);
+    hipLaunchKernelGGL(range_partial_kernel, dim3(grid), dim3(kRangeThreads), 0, stream, x, pa.n,
+                       ws.range_part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(range_resolve_kernel, dim3(1), dim3(256), 0, stream, ws.range_part, grid, ws.info,
-                       eps);
+    hipLaunchKernelGGL(range_resolve_kernel, dim3(1), dim3(kScanThreads), 0, stream, ws.range_part, grid,
+                       ws.info, eps);
     return hipGetLastError();
 }
 
 hipError_t launch_encode(const float *x, const PlanArgs &pa, const Workspace &ws,
                          uint8_t *widths_dst, uint64_t widths_bytes, hipStream_t stream) {
-    hipLaunchKernelGGL(encode_kernel, dim3(pa.ngroups), dim3(kBlockThreads), 0, stream, x, pa, ws,
+    hipLaunchKernelGGL(encode_kernel, dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa, ws,
                        widths_dst, widths_bytes);
     return hipGetLastError();
 }
@@ -911,14 +1076,14 @@ hipError_t launch_compact(const float *x, const PlanArgs &pa, const Workspace &w
 
 hipError_t launch_outliers(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *out,
                            hipStream_t stream) {
-    hipLaunchKernelGGL(outlier_kernel, dim3(pa.ngroups), dim3(kBlockThreads), 0, stream, x, pa, ws,
+    hipLaunchKernelGGL(outlier_kernel, dim3((pa.nchunks + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlockThreads), 0, stream, x, pa, ws,
                        out);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_sizes(const uint8_t *in, const PlanArgs &pa, const Workspace &ws,
                                hipStream_t stream) {
-    const uint32_t grid = (pa.nchunks + 255) / 256;
+    const uint32_t grid = (pa.dchunks + 255) / 256;
     hipLaunchKernelGGL(decode_sizes_kernel, dim3(grid), dim3(256), 0, stream, in, pa, ws);
     return hipGetLastError();
 }
@@ -932,7 +1097,7 @@ hipError_t launch_scan_decompress(const uint8_t *in, uint64_t in_bytes, const Pl
 
 hipError_t launch_decode(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
                          hipStream_t stream) {
-    hipLaunchKernelGGL(decode_kernel, dim3(pa.ngroups), dim3(kBlockThreads), 0, stream, in, pa, ws,
+    hipLaunchKernelGGL(decode_kernel, dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in, pa, ws,
                        out);
     return hipGetLastError();
 }
