@@ -72,7 +72,7 @@ struct DevInfo {
     uint64_t oval_off;
     uint64_t total;
     float dec_s;            /* decompress: step read from the stream */
-    uint32_t pad_;
+    uint32_t dec_B;         /* decompress: Lorenzo block read from the stream */
 };
 
 /* Plan constants passed by value to the kernels. */

@@ -911,6 +911,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_decompress_kernel(const uin
     info->oidx_off = oi;
     info->oval_off = ov;
     info->dec_s = s;
+    info->dec_B = B;
 }
 
 /* ---- K7: fused decode ------------------------------------------------------------------------ */
@@ -969,7 +970,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(const uint8_t *__
 
     const uint32_t *pay = reinterpret_cast<const uint32_t *>(s_pay4[wave]);
     const float s = info->dec_s;
-    const uint32_t B = pa.B;
+    const uint32_t B = info->dec_B; /* the stream's block, validated by the header check */
     const uint32_t seglen = (B / 4 < 64u) ? B / 4 : 64u;
     const uint32_t dist = lane & (seglen - 1);
     const uint32_t ntiles = full ? kDecTiles : (uint32_t)((n - cbase + kTile - 1) / kTile);
