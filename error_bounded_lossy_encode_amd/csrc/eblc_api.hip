@@ -5,7 +5,7 @@
  * per tensor shape and tolerance ("Configuring the error tolerance": the error is fixed at plan
  * creation), it owns a workspace allocated up front (the PREALLOCATE policy of the FZGPUModules
  * "Architecture" page, MemoryPool section), so compress and decompress allocate nothing.
- * Compress enqueues range (relative mode) -> encode -> scan -> compaction -> outliers on the
+ * Compress enqueues range (relative mode) -> encode -> scan -> compaction with outliers on the
  * caller's stream and waits once to return the stream length; decompress enqueues sizes ->
  * scan -> decode -> outlier patch and returns at once.
  */
@@ -273,6 +273,7 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     const uint64_t o_pw = carve(ng * 4), o_pe = carve(ng * 4);
     const uint64_t o_em = carve(nc * kEncSegs * 4);
     const uint64_t o_wd = carve(nc * kEncSegs);
+    const uint64_t o_si = carve(nc * kEscStage * 4), o_sv = carve(nc * kEscStage * 4);
     const uint64_t o_rp = carve(2 * (uint64_t)range_blocks(n) * 4);
     if (hipMalloc(&p->ws_base, off) != hipSuccess) {
         delete p;
@@ -291,6 +292,8 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     ws.gpre_esc = reinterpret_cast<uint32_t *>(b + o_pe);
     ws.emask = reinterpret_cast<uint32_t *>(b + o_em);
     ws.widths = b + o_wd;
+    ws.stage_idx = reinterpret_cast<uint32_t *>(b + o_si);
+    ws.stage_val = reinterpret_cast<uint32_t *>(b + o_sv);
     ws.range_part = reinterpret_cast<float *>(b + o_rp);
 
     if (hipHostMalloc(reinterpret_cast<void **>(&p->host_info), sizeof(DevInfo), hipHostMallocDefault) != hipSuccess) {
@@ -345,7 +348,6 @@ eblc_status eblc_compress(eblc_plan_t *plan, const float *in, void *out, size_t 
     if (e == hipSuccess) e = timed(plan, st, "encode", [&] { return launch_encode(in, pa, ws, widths_dst, widths_bytes, st); });
     if (e == hipSuccess) e = timed(plan, st, "scan", [&] { return launch_scan_compress(pa, ws, o, out_capacity, st); });
     if (e == hipSuccess) e = timed(plan, st, "compact", [&] { return launch_compact(in, pa, ws, o, widths_direct ? nullptr : ws.widths, st); });
-    if (e == hipSuccess) e = timed(plan, st, "outliers", [&] { return launch_outliers(in, pa, ws, o, st); });
     if (e == hipSuccess) e = hipMemcpyAsync(plan->host_info, ws.info, sizeof(DevInfo), hipMemcpyDeviceToHost, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return EBLC_DEVICE_ERROR;

@@ -42,6 +42,7 @@ constexpr int kMaxBlock = kDecChunk;             /* largest Lorenzo block */
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
 constexpr int kDecChunksPerGroup = kWavesPerBlock;
+constexpr int kEscStage = 64;                    /* escapes staged per encode chunk */
 constexpr int kScanThreads = 1024;
 constexpr int kScanItems = 16;                   /* items per scan thread per round */
 constexpr int kRangeThreads = 256;
@@ -102,6 +103,8 @@ struct Workspace {
     uint32_t *gpre_words;    /* [ngroups] exclusive prefix */
     uint32_t *gpre_esc;      /* [ngroups] exclusive prefix */
     uint32_t *emask;         /* [nchunks * kEncSegs] escape bitmask per segment (tiles with escapes) */
+    uint32_t *stage_idx;     /* [nchunks * kEscStage] first escapes of each chunk: index ... */
+    uint32_t *stage_val;     /* [nchunks * kEscStage] ... and raw value bits, in index order */
     uint8_t *widths;         /* [nchunks * kEncSegs] widths staging when the output is too small */
     float *range_part;       /* [2 * range_blocks(n)] per-block min / max */
 };
@@ -121,8 +124,6 @@ hipError_t launch_scan_compress(const PlanArgs &pa, const Workspace &ws, uint8_t
                                 uint64_t out_capacity, hipStream_t stream);
 hipError_t launch_compact(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *out,
                           const uint8_t *widths_src, hipStream_t stream);
-hipError_t launch_outliers(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *out,
-                           hipStream_t stream);
 hipError_t launch_decode_sizes(const uint8_t *in, const PlanArgs &pa, const Workspace &ws,
                                hipStream_t stream);
 hipError_t launch_scan_decompress(const uint8_t *in, uint64_t in_bytes, const PlanArgs &pa,

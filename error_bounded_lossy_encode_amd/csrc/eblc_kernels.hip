@@ -309,7 +309,8 @@ __device__ __forceinline__ uint32_t seg_or(uint32_t v) {
 template <bool FULL>
 __device__ __forceinline__ uint32_t code_tile(const float xs[kEncLaneVals], uint64_t e0, uint64_t n,
                                               const QParams &qp, bool reset, int t,
-                                              uint32_t *emask_tile, int32_t &carry,
+                                              uint32_t *emask_tile, uint32_t *stage_idx,
+                                              uint32_t *stage_val, int32_t &carry,
                                               uint32_t z[kEncLaneVals], EncState &st) {
     constexpr int V = kEncLaneVals;
     const uint32_t lane = threadIdx.x & 63;
@@ -348,14 +349,25 @@ __device__ __forceinline__ uint32_t code_tile(const float xs[kEncLaneVals], uint
                 esc |= e << k;
             }
         }
-        /* escapes: per-segment bitmask (value V j + k of the segment) and counts */
+        /* escapes: per-segment bitmask (value V j + k of the segment), the chunk's first
+         * kEscStage escapes staged as (index, bits) in index order, and the count */
         if (__ballot(esc != 0)) {
             const uint32_t segm = seg_or(esc << (V * j));
             if (j == 0) emask_tile[lane / kSegLanes] = segm;
-            uint32_t cnt = 0;
+            const uint32_t ecnt = (uint32_t)__popc(esc);
+            const uint32_t eincl = wave_incl_scan(ecnt);
+            uint32_t r = st.escs + eincl - ecnt;
 #pragma unroll
-            for (int k = 0; k < V; ++k) cnt += (uint32_t)__popcll(__ballot((esc >> k) & 1u));
-            st.escs += cnt;
+            for (int k = 0; k < V; ++k) {
+                if ((esc >> k) & 1u) {
+                    if (r < (uint32_t)kEscStage) {
+                        stage_idx[r] = (uint32_t)(e0 + k);
+                        stage_val[r] = __float_as_uint(xs[k]);
+                    }
+                    ++r;
+                }
+            }
+            st.escs += readlane(eincl, 63);
             st.tmask |= 1u << t;
         }
     }
@@ -416,7 +428,7 @@ template <bool FULL>
 __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, uint64_t cbase, uint64_t n,
                                              const QParams &qp, uint32_t bmask, int32_t carry,
                                              uint32_t *pay, uint8_t *wid, uint32_t *emask_chunk,
-                                             EncState &st) {
+                                             uint32_t *stage_idx, uint32_t *stage_val, EncState &st) {
     constexpr int V = kEncLaneVals;
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t j = lane & (kSegLanes - 1), g = lane / kSegLanes;
@@ -449,7 +461,8 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, uint64
         if (FULL || (uint32_t)t < ntiles) {
             const bool reset = lane_at_block && (((uint32_t)cbase + (uint32_t)t * kEncTile) & bmask) == 0;
             w[t] = code_tile<FULL>(xs[t], cbase + (uint64_t)t * kEncTile + V * lane, n, qp, reset, t,
-                                   emask_chunk + t * kSegsPerEncTile, carry, z[t], st);
+                                   emask_chunk + t * kSegsPerEncTile, stage_idx, stage_val, carry, z[t],
+                                   st);
             if (j == 0) wid[t * kSegsPerEncTile + g] = (uint8_t)w[t];
         }
     }
@@ -477,6 +490,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
     uint64_t widths_bytes) {
     __shared__ uint4 s_pay4[kEncWaves][kEncChunk / 4 + 1];
     __shared__ uint4 s_wid4[kEncWaves][kEncSegs / 16];
+    __shared__ uint32_t s_stage[kEncWaves][2][kEscStage];
     __shared__ uint32_t s_grp[2][kEncWaves];
 
     const uint32_t lane = threadIdx.x & 63;
@@ -511,10 +525,12 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
             carry = e ? 0 : qprev;
         }
         uint32_t *emask_chunk = ws.emask + (uint64_t)c * kEncSegs;
+        uint32_t *stage_idx = s_stage[wave][0];
+        uint32_t *stage_val = s_stage[wave][1];
         if (cbase + kEncChunk <= pa.n)
-            encode_chunk<true>(x, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk, st);
+            encode_chunk<true>(x, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk, stage_idx, stage_val, st);
         else
-            encode_chunk<false>(x, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk, st);
+            encode_chunk<false>(x, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk, stage_idx, stage_val, st);
         wave_lds_sync();
         /* chunk payload -> scratch slot, widths -> stream (or staging) */
         uint4 *dst = reinterpret_cast<uint4 *>(ws.scratch + cbase);
@@ -523,6 +539,10 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
         if (lane < kEncSegs / 16) {
             const uint64_t off = (uint64_t)c * kEncSegs + 16u * lane;
             if (off < widths_bytes) *reinterpret_cast<uint4 *>(widths_dst + off) = s_wid4[wave][lane];
+        }
+        if (lane < st.escs && lane < (uint32_t)kEscStage) {
+            ws.stage_idx[(uint64_t)c * kEscStage + lane] = stage_idx[lane];
+            ws.stage_val[(uint64_t)c * kEscStage + lane] = stage_val[lane];
         }
         if (lane == 0) {
             ws.chunk_words[c] = st.words;
@@ -707,27 +727,111 @@ __device__ __forceinline__ uint32_t chunk_offset(const uint32_t *gpre, const uin
     return o;
 }
 
-/* ---- K4: compaction of the scratch slots (or the RAW copy) -------------------------------- */
+/* ---- K4: compaction of the scratch slots and the ordered outliers (or the RAW copy) ------- */
 
-/* One workgroup per group of kEncChunksPerGroup encode chunks.  The group's payload words are
- * contiguous in the stream (at the group's scanned offset), so its 256 threads copy them as one
- * run: word i of the run comes from the chunk whose prefix range holds i.  In RAW mode the
- * workgroup copies the group's input values instead.  The last group also zeroes the pad after
- * the payload. */
+/* Outliers of encode chunk c (cnt of them, from outlier rank O on), written by one wave: copied
+ * from the encoder's staging when they all fit there; otherwise lane l < kEncSegs owns segment
+ * l, takes its escape bitmask, ranks its escapes after O and the lanes before it, and writes
+ * (index, raw bits) in ascending index order, re-reading the values from the input. */
+__device__ __forceinline__ void write_chunk_outliers(const float *__restrict__ x, const Workspace &ws,
+                                                     uint32_t c, uint32_t cnt, uint32_t O,
+                                                     uint32_t *oidx, uint32_t *oval) {
+    const uint32_t lane = threadIdx.x & 63;
+    if (cnt == 0) return;
+    if (cnt <= (uint32_t)kEscStage) {
+        /* all of the chunk's escapes were staged by the encoder, in index order */
+        const uint32_t *si = ws.stage_idx + (uint64_t)c * kEscStage;
+        const uint32_t *sv = ws.stage_val + (uint64_t)c * kEscStage;
+        if (lane < cnt) {
+            oidx[O + lane] = si[lane];
+            oval[O + lane] = sv[lane];
+        }
+        return;
+    }
+    const uint32_t tm = ws.chunk_tmask[c];
+    uint32_t mask = (lane < (uint32_t)kEncSegs && ((tm >> (lane / kSegsPerEncTile)) & 1u))
+                        ? ws.emask[(uint64_t)c * kEncSegs + lane] : 0u;
+    const uint32_t lcnt = (uint32_t)__popc(mask);
+    uint32_t rank = O + wave_incl_scan(lcnt) - lcnt;
+    const uint64_t segbase = (uint64_t)c * kEncChunk + 32u * lane;
+    const uint32_t *xb = reinterpret_cast<const uint32_t *>(x);
+    while (mask) {
+        const uint32_t bit = (uint32_t)__builtin_ctz(mask);
+        const uint64_t idx = segbase + bit;
+        oidx[rank] = (uint32_t)idx;
+        oval[rank] = xb[idx];
+        ++rank;
+        mask &= mask - 1;
+    }
+}
+
+/* Copy one chunk's P payload words from its 16-byte aligned scratch slot to stream word Dw of
+ * the (16-byte aligned) payload section, by one wave.  Destination words fall into a head
+ * [Dw, bs), whole 128-bit units [bs, be) and a tail [be, Dw + P), bs and be being Dw and Dw + P
+ * rounded up and down to 4 words.  Head and tail words can share a 16-byte unit with the
+ * neighbouring chunks, so they are stored one by one; each whole unit is assembled from two
+ * aligned source units shifted by the wave-uniform word offset (bs - Dw) mod 4. */
+__device__ __forceinline__ void copy_chunk_payload(const uint32_t *__restrict__ src, uint32_t P,
+                                                   uint64_t Dw, uint32_t *__restrict__ pay) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint64_t De = Dw + P;
+    const uint64_t bs = (Dw + 3) & ~(uint64_t)3;
+    const uint64_t be = De & ~(uint64_t)3;
+    const uint64_t head_end = bs < De ? bs : De;
+    if (lane < head_end - Dw) pay[Dw + lane] = src[lane];
+    const uint64_t tail_start = be > bs ? be : bs;
+    if (tail_start < De && lane < De - tail_start) pay[tail_start + lane] = src[tail_start - Dw + lane];
+    if (be <= bs) return;
+    const uint32_t units = (uint32_t)((be - bs) >> 2);
+    const uint32_t r = (uint32_t)(bs - Dw);          /* 0..3: source word offset of unit 0 */
+    const uint4 *s4 = reinterpret_cast<const uint4 *>(src);
+    uint4 *d4 = reinterpret_cast<uint4 *>(pay + bs);
+    if (r == 0) {
+        for (uint32_t t = lane; t < units; t += kWave) d4[t] = s4[t];
+    } else {
+        for (uint32_t t = lane; t < units; t += kWave) {
+            const uint4 A = s4[t], B = s4[t + 1];
+            uint4 o;
+            if (r == 1) o = make_uint4(A.y, A.z, A.w, B.x);
+            else if (r == 2) o = make_uint4(A.z, A.w, B.x, B.y);
+            else o = make_uint4(A.w, B.x, B.y, B.z);
+            d4[t] = o;
+        }
+    }
+}
+
+/* One workgroup per group of kEncChunksPerGroup encode chunks, one wave per chunk: the wave
+ * copies its chunk's payload to the chunk's scanned offset, then writes the chunk's outliers.
+ * In RAW mode the workgroup copies the group's input values instead.  The last group also
+ * zeroes the pads after the payload and after the outlier sections. */
 __global__ __launch_bounds__(kBlockThreads) void compact_kernel(const float *__restrict__ x,
                                                                 PlanArgs pa, Workspace ws,
                                                                 uint8_t *__restrict__ out,
                                                                 const uint8_t *__restrict__ widths_src) {
     constexpr int CPG = kEncChunksPerGroup;
-    __shared__ uint32_t s_o[CPG + 1];
+    static_assert(CPG == kBlockThreads / kWave, "one wave per chunk");
     const uint32_t tid = threadIdx.x;
     const uint32_t grp = blockIdx.x;
     const DevInfo *info = ws.info;
-    if (!info->fits) return;
+    /* every small input of the group up front, in one round of loads */
+    const uint32_t wave = tid >> 6;
+    const uint32_t c = grp * CPG + wave;
+    uint32_t words[CPG], escs[CPG];
+#pragma unroll
+    for (int k = 0; k < CPG; ++k) {
+        const uint32_t ck = grp * CPG + k;
+        words[k] = ck < pa.nchunks ? ws.chunk_words[ck] : 0u;
+        escs[k] = ck < pa.nchunks ? ws.chunk_esc[ck] : 0u;
+    }
+    const uint32_t gw = ws.gpre_words[grp], ge = ws.gpre_esc[grp];
+    const uint32_t fits = info->fits, mode = info->mode;
+    const uint64_t payload_off = info->payload_off, oidx_off = info->oidx_off, oval_off = info->oval_off;
+    const uint64_t m = info->m, payload_words = info->payload_words;
+    if (!fits) return;
     const uint64_t n = pa.n;
     const uint64_t gbase = (uint64_t)grp * CPG * kEncChunk;
     const bool last = grp == pa.ngroups - 1;
-    if (info->mode == 1) {
+    if (mode == 1) {
         constexpr uint32_t kGroupVals = CPG * kEncChunk;
         const uint64_t cnt = (n - gbase < (uint64_t)kGroupVals) ? n - gbase : (uint64_t)kGroupVals;
         uint32_t *dstw = reinterpret_cast<uint32_t *>(out + kHeaderBytes) + gbase;
@@ -751,76 +855,34 @@ __global__ __launch_bounds__(kBlockThreads) void compact_kernel(const float *__r
         }
         return;
     }
-    const uint32_t c0 = grp * CPG;
-    if (tid == 0) {
-        uint32_t o = 0;
-        s_o[0] = 0;
-        for (int k = 0; k < CPG; ++k) {
-            o += (c0 + k < pa.nchunks) ? ws.chunk_words[c0 + k] : 0u;
-            s_o[k + 1] = o;
-        }
-    }
-    __syncthreads();
-    const uint32_t total = s_o[CPG];
-    uint32_t *dst = reinterpret_cast<uint32_t *>(out + info->payload_off) + ws.gpre_words[grp];
-    for (uint32_t i = tid; i < total; i += kBlockThreads) {
-        uint32_t k = 0;
+    uint32_t W = gw, O = ge;
 #pragma unroll
-        for (int b = CPG / 2; b >= 1; b /= 2)
-            if (i >= s_o[k + b]) k += b;
-        dst[i] = ws.scratch[(uint64_t)(c0 + k) * kEncChunk + (i - s_o[k])];
+    for (int k = 0; k < CPG; ++k) {
+        W += (uint32_t)k < wave ? words[k] : 0u;
+        O += (uint32_t)k < wave ? escs[k] : 0u;
+    }
+    uint32_t *pay = reinterpret_cast<uint32_t *>(out + payload_off);
+    uint32_t *oidx = reinterpret_cast<uint32_t *>(out + oidx_off);
+    uint32_t *oval = reinterpret_cast<uint32_t *>(out + oval_off);
+    if (c < pa.nchunks) {
+        copy_chunk_payload(ws.scratch + (uint64_t)c * kEncChunk, words[wave], W, pay);
+        write_chunk_outliers(x, ws, c, escs[wave], O, oidx, oval);
     }
     if (widths_src != nullptr) {
         constexpr uint32_t kGroupWidthVecs = CPG * kEncSegs / 16;
-        const uint64_t off = (uint64_t)c0 * kEncSegs + 16u * tid;
+        const uint64_t off = (uint64_t)grp * CPG * kEncSegs + 16u * tid;
         if (tid < kGroupWidthVecs && off < align16(pa.nseg))
             *reinterpret_cast<uint4 *>(out + kHeaderBytes + off) = *reinterpret_cast<const uint4 *>(widths_src + off);
     }
     if (last) {
-        const uint64_t pend = info->payload_off + 4 * info->payload_words;
-        const uint64_t pad = info->oidx_off - pend;
+        const uint64_t pend = payload_off + 4 * payload_words;
+        const uint64_t pad = oidx_off - pend;
         if (tid < pad / 4) reinterpret_cast<uint32_t *>(out + pend)[tid] = 0u;
-    }
-}
-
-/* ---- K5: outliers in index order ------------------------------------------------------------ */
-
-/* One wave per encode chunk with escapes: lane l < 32 owns segment l of the chunk, takes its
- * escape bitmask, ranks its escapes after the chunk's scanned offset and the lanes before it,
- * and writes (index, raw bits) in ascending index order. */
-__global__ __launch_bounds__(kBlockThreads) void outlier_kernel(const float *__restrict__ x,
-                                                                PlanArgs pa, Workspace ws,
-                                                                uint8_t *__restrict__ out) {
-    const uint32_t lane = threadIdx.x & 63;
-    const uint32_t c = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    if (c >= pa.nchunks) return;
-    const DevInfo *info = ws.info;
-    if (!info->fits || info->mode == 1) return;
-    const uint64_t m = info->m;
-    uint32_t *oidx = reinterpret_cast<uint32_t *>(out + info->oidx_off);
-    uint32_t *oval = reinterpret_cast<uint32_t *>(out + info->oval_off);
-    if (c == pa.nchunks - 1) {
-        const uint64_t pad = (align16(4 * m) - 4 * m) / 4;
-        if (lane < pad) {
-            oidx[m + lane] = 0u;
-            oval[m + lane] = 0u;
+        const uint64_t opad = (align16(4 * m) - 4 * m) / 4;
+        if (tid < opad) {
+            oidx[m + tid] = 0u;
+            oval[m + tid] = 0u;
         }
-    }
-    if (ws.chunk_esc[c] == 0) return;
-    const uint32_t O = chunk_offset<kEncChunksPerGroup>(ws.gpre_esc, ws.chunk_esc, c);
-    const uint32_t tm = ws.chunk_tmask[c];
-    uint32_t mask = (lane < (uint32_t)kEncSegs && ((tm >> (lane / kSegsPerEncTile)) & 1u)) ? ws.emask[(uint64_t)c * kEncSegs + lane] : 0u;
-    const uint32_t cnt = (uint32_t)__popc(mask);
-    uint32_t rank = O + wave_incl_scan(cnt) - cnt;
-    const uint64_t segbase = (uint64_t)c * kEncChunk + 32u * lane;
-    const uint32_t *xb = reinterpret_cast<const uint32_t *>(x);
-    while (mask) {
-        const uint32_t bit = (uint32_t)__builtin_ctz(mask);
-        const uint64_t idx = segbase + bit;
-        oidx[rank] = (uint32_t)idx;
-        oval[rank] = xb[idx];
-        ++rank;
-        mask &= mask - 1;
     }
 }
 
@@ -1072,13 +1134,6 @@ hipError_t launch_compact(const float *x, const PlanArgs &pa, const Workspace &w
                           const uint8_t *widths_src, hipStream_t stream) {
     hipLaunchKernelGGL(compact_kernel, dim3(pa.ngroups), dim3(kBlockThreads), 0, stream, x, pa, ws,
                        out, widths_src);
-    return hipGetLastError();
-}
-
-hipError_t launch_outliers(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *out,
-                           hipStream_t stream) {
-    hipLaunchKernelGGL(outlier_kernel, dim3((pa.nchunks + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlockThreads), 0, stream, x, pa, ws,
-                       out);
     return hipGetLastError();
 }
 
