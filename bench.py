@@ -5,7 +5,10 @@ the path), with the inputs already resident in HBM.  The default workload is the
 wavefield snapshot (eight Ricker wavelets, 40 % quiescent zeros) at relative bound 1e-3, block
 256, outlier_log2 15.  Other workloads: c1 (2^20 sum of sines), c2 (4096^2 Gaussian random
 field), c4 (2^28 AR(1) with 1 % spikes), c5_1e-6 / c5_1e-2 (64 snapshots of 256^3 compressed
-back to back on one stream, then decompressed back to back).
+back to back on one stream, then decompressed back to back).  By default the fields are
+compressed with eblc_compress_batch (no host wait; lengths arrive in device result records) and
+decompressed with their buffers' capacity; --api sync uses eblc_compress, which waits once per
+field to return its length.
 
 Prints ONE JSON line: `value` is the round-trip throughput in GB/s of input bytes (input bytes
 / (compress + decompress time)); `compress_gbps`, `decompress_gbps` and `ratio` are given
@@ -150,6 +153,9 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=5)
+    ap.add_argument("--api", choices=["batch", "sync"], default="batch",
+                    help="batch: eblc_compress_batch (no host wait) and decompress by buffer capacity; "
+                         "sync: eblc_compress per field, which waits to return each length")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device to device once (counter calibration)")
     args = ap.parse_args()
@@ -176,15 +182,23 @@ def main() -> int:
     outs = [torch.empty(plan.max_bytes, dtype=torch.uint8, device=dev) for _ in items]
     ys = [torch.empty(n, dtype=torch.float32, device=dev) for _ in items]
     stream = torch.cuda.current_stream()
-    nbytes = [0] * len(items)
+    nbytes = [plan.max_bytes] * len(items)
+    xs = [x for x, _, _ in items]
+    records = torch.zeros(16 * len(items), dtype=torch.uint8, device=dev)
 
     def compress_all():
-        for i, (x, _, _) in enumerate(items):
+        if args.api == "batch":
+            st = binding.eblc_compress_batch(plan.handle, xs, outs, records, stream=stream)
+            assert st == binding.EBLC_OK, binding.eblc_status_string(st)
+            return
+        for i, x in enumerate(xs):
             st, nb = binding.eblc_compress(plan.handle, x, outs[i], stream=stream)
             assert st == binding.EBLC_OK, binding.eblc_status_string(st)
             nbytes[i] = nb
 
     def decompress_all():
+        # with the batch API the host never reads the lengths: each stream is decompressed with
+        # its buffer's capacity and its own length comes from its header on the device
         for i in range(len(items)):
             st = binding.eblc_decompress(plan.handle, outs[i], nbytes[i], ys[i], stream=stream)
             assert st == binding.EBLC_OK, binding.eblc_status_string(st)
@@ -213,6 +227,10 @@ def main() -> int:
     comp_ms = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
     decomp_ms = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
     in_bytes = 4 * n * len(items)
+    if args.api == "batch":
+        recs = binding.result_records(records)
+        assert all(status == binding.EBLC_OK for _, status in recs)
+        nbytes = [nb for nb, _ in recs]
     total_stream = sum(nbytes)
     log(f"[bench] step {wall * 1e3:.3f} ms; compress {comp_ms:.3f} ms; decompress {decomp_ms:.3f} ms; "
         f"streams {total_stream} B")
@@ -285,7 +303,9 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": desc, "fields": len(items), "n": n, "dims": dims0, "options": opts0,
-                   "step": "compress all fields, then decompress all streams"},
+                   "step": "compress all fields, then decompress all streams",
+                   "api": "eblc_compress_batch + eblc_decompress" if args.api == "batch"
+                   else "eblc_compress (waits per field) + eblc_decompress"},
         "compress_gbps": round(in_bytes / (comp_ms * 1e-3) / 1e9, 3),
         "decompress_gbps": round(in_bytes / (decomp_ms * 1e-3) / 1e9, 3),
         "ratio": round(in_bytes / total_stream, 4),

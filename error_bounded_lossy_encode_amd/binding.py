@@ -32,15 +32,20 @@ class eblc_execution_t(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("device", ctypes.c_int), ("threads", ctypes.c_int)]
 
 
+class eblc_result_t(ctypes.Structure):
+    _fields_ = [("compressed_bytes", ctypes.c_uint64), ("status", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
+
+
 class eblc_limits_t(ctypes.Structure):
     _fields_ = [("max_compressed_bytes", ctypes.c_size_t), ("payload_alignment", ctypes.c_size_t),
                 ("sidecar_bytes", ctypes.c_size_t), ("sidecar_alignment", ctypes.c_size_t)]
 
 
 EXPORTS = ["eblc_abi_version", "eblc_plan_create", "eblc_plan_limits", "eblc_max_compressed_bytes",
-           "eblc_payload_alignment", "eblc_compress", "eblc_decompress", "eblc_plan_status",
-           "eblc_plan_destroy", "eblc_status_string", "eblc_plan_set_profiling",
-           "eblc_plan_kernel_times"]
+           "eblc_payload_alignment", "eblc_compress", "eblc_compress_async", "eblc_compress_batch",
+           "eblc_decompress", "eblc_plan_status", "eblc_plan_destroy", "eblc_status_string",
+           "eblc_plan_set_profiling", "eblc_plan_kernel_times"]
 
 _lib = None
 
@@ -67,6 +72,10 @@ def lib():
     L.eblc_payload_alignment.restype = SZ
     L.eblc_compress.argtypes = [P, P, P, SZ, ctypes.POINTER(SZ), P, P]
     L.eblc_compress.restype = I
+    L.eblc_compress_async.argtypes = [P, P, P, SZ, P, P]
+    L.eblc_compress_async.restype = I
+    L.eblc_compress_batch.argtypes = [P, I, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(SZ), P, P]
+    L.eblc_compress_batch.restype = I
     L.eblc_decompress.argtypes = [P, P, SZ, P, P, P]
     L.eblc_decompress.restype = I
     L.eblc_plan_status.argtypes = [P, P]
@@ -141,6 +150,33 @@ def eblc_compress(plan, x, out, out_capacity: int | None = None, stream=None):
     st = lib().eblc_compress(plan, _ptr(x), _ptr(out), cap, ctypes.byref(nbytes), None,
                              _stream_handle(stream))
     return st, int(nbytes.value)
+
+
+def eblc_compress_async(plan, x, out, result, out_capacity: int | None = None, stream=None) -> int:
+    """x: float32 device tensor; out: uint8 device tensor; result: a device tensor of >= 16 bytes
+    (or a pinned host one) that receives the eblc_result_t record.  Returns the status."""
+    cap = out.numel() * out.element_size() if out_capacity is None else int(out_capacity)
+    return int(lib().eblc_compress_async(plan, _ptr(x), _ptr(out), cap, _ptr(result),
+                                         _stream_handle(stream)))
+
+
+def eblc_compress_batch(plan, xs, outs, results, capacities=None, stream=None) -> int:
+    """Enqueue len(xs) compressions back to back; results: one device (or pinned host) tensor
+    holding len(xs) eblc_result_t records (16 bytes each).  Returns the status."""
+    k = len(xs)
+    ins = (ctypes.c_void_p * max(k, 1))(*[t.data_ptr() for t in xs])
+    os_ = (ctypes.c_void_p * max(k, 1))(*[t.data_ptr() for t in outs])
+    caps = [t.numel() * t.element_size() for t in outs] if capacities is None else capacities
+    cs = (ctypes.c_size_t * max(k, 1))(*[int(c) for c in caps])
+    return int(lib().eblc_compress_batch(plan, k, ins, os_, cs, _ptr(results), _stream_handle(stream)))
+
+
+def result_records(results) -> list:
+    """[(compressed_bytes, status)] from a tensor of eblc_result_t records (copied to host)."""
+    import numpy as np
+    raw = results.cpu().numpy().view(np.uint8).reshape(-1)
+    recs = raw[: raw.size // 16 * 16].view(np.uint64).reshape(-1, 2)
+    return [(int(r[0]), int(r[1] & 0xFFFFFFFF)) for r in recs]
 
 
 def eblc_decompress(plan, stream_buf, compressed_bytes: int, out, stream=None) -> int:

@@ -32,7 +32,7 @@ struct eblc_plan {
     PlanArgs pa{};
     Workspace ws{};
     void *ws_base = nullptr;
-    DevInfo *host_info = nullptr; /* pinned */
+    eblc_result_t *host_result = nullptr; /* pinned host slot the synchronous compress reads */
     bool profiling = false;
     hipEvent_t ev[2 * kMaxKernelsPerCall] = {};
     const char *names[kMaxKernelsPerCall] = {};
@@ -183,6 +183,33 @@ hipError_t timed(eblc_plan *p, hipStream_t st, const char *name, F &&launch) {
     return hipEventRecord(p->ev[2 * k + 1], st);
 }
 
+eblc_status check_compress_args(const eblc_plan *plan, const float *in, const void *out) {
+    (void)plan;
+    if (in == nullptr || out == nullptr) return EBLC_INVALID_ARGUMENT;
+    if (!aligned16(in) || !aligned16(out)) return EBLC_INVALID_ARGUMENT;
+    return EBLC_OK;
+}
+
+/* Enqueue one compress on `st`: range (relative mode) -> encode -> scan (which writes the
+ * result record) -> compaction with outliers. */
+hipError_t enqueue_compress(eblc_plan *plan, const float *in, void *out, size_t out_capacity,
+                            eblc_result_t *result, hipStream_t st) {
+    const PlanArgs &pa = plan->pa;
+    const Workspace &ws = plan->ws;
+    uint8_t *o = static_cast<uint8_t *>(out);
+    const uint64_t widths_bytes = align_up(pa.nseg, 16);
+    const bool widths_direct = out_capacity >= kHeaderBytes + widths_bytes;
+    uint8_t *widths_dst = widths_direct ? o + kHeaderBytes : ws.widths;
+    uint64_t *res = reinterpret_cast<uint64_t *>(result);
+    plan->nlaunch = 0;
+    hipError_t e = hipSuccess;
+    if (plan->rel) e = timed(plan, st, "range", [&] { return launch_range(in, pa, ws, plan->eps, st); });
+    if (e == hipSuccess) e = timed(plan, st, "encode", [&] { return launch_encode(in, pa, ws, widths_dst, widths_bytes, st); });
+    if (e == hipSuccess) e = timed(plan, st, "scan", [&] { return launch_scan_compress(pa, ws, o, out_capacity, res, st); });
+    if (e == hipSuccess) e = timed(plan, st, "compact", [&] { return launch_compact(in, pa, ws, o, widths_direct ? nullptr : ws.widths, st); });
+    return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -296,7 +323,7 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     ws.stage_val = reinterpret_cast<uint32_t *>(b + o_sv);
     ws.range_part = reinterpret_cast<float *>(b + o_rp);
 
-    if (hipHostMalloc(reinterpret_cast<void **>(&p->host_info), sizeof(DevInfo), hipHostMallocDefault) != hipSuccess) {
+    if (hipHostMalloc(reinterpret_cast<void **>(&p->host_result), sizeof(eblc_result_t), hipHostMallocDefault) != hipSuccess) {
         (void)hipFree(p->ws_base);
         delete p;
         return EBLC_OUT_OF_MEMORY;
@@ -305,7 +332,7 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     std::memset(&init, 0, sizeof(init));
     if (!o.rel) resolve_abs(o.eps, &init);
     if (hipMemcpy(ws.info, &init, sizeof(init), hipMemcpyHostToDevice) != hipSuccess) {
-        (void)hipHostFree(p->host_info);
+        (void)hipHostFree(p->host_result);
         (void)hipFree(p->ws_base);
         delete p;
         return EBLC_DEVICE_ERROR;
@@ -331,28 +358,52 @@ size_t eblc_payload_alignment(const eblc_plan_t *plan) { return plan == nullptr 
 
 eblc_status eblc_compress(eblc_plan_t *plan, const float *in, void *out, size_t out_capacity,
                           size_t *compressed_bytes, void *sidecar, void *stream) {
-    if (plan == nullptr || in == nullptr || out == nullptr || compressed_bytes == nullptr) return EBLC_INVALID_ARGUMENT;
-    if (sidecar != nullptr || !aligned16(in) || !aligned16(out)) return EBLC_INVALID_ARGUMENT;
+    if (plan == nullptr || compressed_bytes == nullptr) return EBLC_INVALID_ARGUMENT;
+    if (sidecar != nullptr) return EBLC_INVALID_ARGUMENT;
+    eblc_status s0 = check_compress_args(plan, in, out);
+    if (s0 != EBLC_OK) return s0;
     DeviceGuard guard(plan->device);
     if (!guard.ok) return EBLC_DEVICE_ERROR;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const PlanArgs &pa = plan->pa;
-    const Workspace &ws = plan->ws;
-    uint8_t *o = static_cast<uint8_t *>(out);
-    const uint64_t widths_bytes = align_up(pa.nseg, 16);
-    const bool widths_direct = out_capacity >= kHeaderBytes + widths_bytes;
-    uint8_t *widths_dst = widths_direct ? o + kHeaderBytes : ws.widths;
-    plan->nlaunch = 0;
-    hipError_t e = hipSuccess;
-    if (plan->rel) e = timed(plan, st, "range", [&] { return launch_range(in, pa, ws, plan->eps, st); });
-    if (e == hipSuccess) e = timed(plan, st, "encode", [&] { return launch_encode(in, pa, ws, widths_dst, widths_bytes, st); });
-    if (e == hipSuccess) e = timed(plan, st, "scan", [&] { return launch_scan_compress(pa, ws, o, out_capacity, st); });
-    if (e == hipSuccess) e = timed(plan, st, "compact", [&] { return launch_compact(in, pa, ws, o, widths_direct ? nullptr : ws.widths, st); });
-    if (e == hipSuccess) e = hipMemcpyAsync(plan->host_info, ws.info, sizeof(DevInfo), hipMemcpyDeviceToHost, st);
+    /* the scan kernel writes the result record straight into the plan's pinned host slot */
+    plan->host_result->compressed_bytes = 0;
+    plan->host_result->status = EBLC_DEVICE_ERROR;
+    hipError_t e = enqueue_compress(plan, in, out, out_capacity, plan->host_result, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return EBLC_DEVICE_ERROR;
-    *compressed_bytes = (size_t)plan->host_info->total;
-    return plan->host_info->fits ? EBLC_OK : EBLC_CAPACITY;
+    *compressed_bytes = (size_t)plan->host_result->compressed_bytes;
+    return static_cast<eblc_status>(plan->host_result->status);
+}
+
+eblc_status eblc_compress_async(eblc_plan_t *plan, const float *in, void *out, size_t out_capacity,
+                                eblc_result_t *result, void *stream) {
+    if (plan == nullptr || result == nullptr || (reinterpret_cast<uintptr_t>(result) & 7u) != 0)
+        return EBLC_INVALID_ARGUMENT;
+    eblc_status s0 = check_compress_args(plan, in, out);
+    if (s0 != EBLC_OK) return s0;
+    DeviceGuard guard(plan->device);
+    if (!guard.ok) return EBLC_DEVICE_ERROR;
+    return hip_status(enqueue_compress(plan, in, out, out_capacity, result, static_cast<hipStream_t>(stream)));
+}
+
+eblc_status eblc_compress_batch(eblc_plan_t *plan, int count, const float *const *in, void *const *out,
+                                const size_t *out_capacity, eblc_result_t *results, void *stream) {
+    if (plan == nullptr || count < 0 || (count > 0 && (in == nullptr || out == nullptr ||
+                                                       out_capacity == nullptr || results == nullptr)))
+        return EBLC_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(results) & 7u) != 0) return EBLC_INVALID_ARGUMENT;
+    for (int k = 0; k < count; ++k) {
+        eblc_status s0 = check_compress_args(plan, in[k], out[k]);
+        if (s0 != EBLC_OK) return s0;
+    }
+    DeviceGuard guard(plan->device);
+    if (!guard.ok) return EBLC_DEVICE_ERROR;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int k = 0; k < count; ++k) {
+        hipError_t e = enqueue_compress(plan, in[k], out[k], out_capacity[k], results + k, st);
+        if (e != hipSuccess) return EBLC_DEVICE_ERROR;
+    }
+    return EBLC_OK;
 }
 
 eblc_status eblc_decompress(eblc_plan_t *plan, const void *in, size_t compressed_bytes,
@@ -399,7 +450,7 @@ void eblc_plan_destroy(eblc_plan_t *plan) {
         (void)hipDeviceSynchronize();
         for (auto &ev : plan->ev)
             if (ev) (void)hipEventDestroy(ev);
-        if (plan->host_info) (void)hipHostFree(plan->host_info);
+        if (plan->host_result) (void)hipHostFree(plan->host_result);
         if (plan->ws_base) (void)hipFree(plan->ws_base);
     }
     delete plan;

@@ -121,7 +121,7 @@ hipError_t launch_range(const float *x, const PlanArgs &pa, const Workspace &ws,
 hipError_t launch_encode(const float *x, const PlanArgs &pa, const Workspace &ws,
                          uint8_t *widths_dst, uint64_t widths_bytes, hipStream_t stream);
 hipError_t launch_scan_compress(const PlanArgs &pa, const Workspace &ws, uint8_t *out,
-                                uint64_t out_capacity, hipStream_t stream);
+                                uint64_t out_capacity, uint64_t *result, hipStream_t stream);
 hipError_t launch_compact(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *out,
                           const uint8_t *widths_src, hipStream_t stream);
 hipError_t launch_decode_sizes(const uint8_t *in, const PlanArgs &pa, const Workspace &ws,

@@ -655,7 +655,8 @@ __device__ void block_scan2(const uint32_t *__restrict__ a, const uint32_t *__re
 
 /* Compress finalize: totals -> stream layout, RAW decision, header. */
 __global__ __launch_bounds__(kScanThreads) void scan_compress_kernel(PlanArgs pa, Workspace ws,
-                                                                     uint8_t *out, uint64_t cap) {
+                                                                     uint8_t *out, uint64_t cap,
+                                                                     uint64_t *result) {
     __shared__ uint32_t s_hdr[32];
     __shared__ uint32_t s_fits;
     uint32_t tot[2];
@@ -689,6 +690,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_compress_kernel(PlanArgs pa
         info->total = f_tot;
         info->fits = fits;
         s_fits = fits;
+        if (result != nullptr) {
+            /* the caller's result record: length (or required capacity), then the status */
+            result[0] = f_tot;
+            result[1] = fits ? 0u : 3u;
+        }
         uint32_t *h = s_hdr;
         h[0] = kMagic;
         h[1] = kVersion | (kHeaderBytes << 16);
@@ -1124,9 +1130,9 @@ hipError_t launch_encode(const float *x, const PlanArgs &pa, const Workspace &ws
 }
 
 hipError_t launch_scan_compress(const PlanArgs &pa, const Workspace &ws, uint8_t *out,
-                                uint64_t out_capacity, hipStream_t stream) {
+                                uint64_t out_capacity, uint64_t *result, hipStream_t stream) {
     hipLaunchKernelGGL(scan_compress_kernel, dim3(1), dim3(kScanThreads), 0, stream, pa, ws, out,
-                       out_capacity);
+                       out_capacity, result);
     return hipGetLastError();
 }
 

@@ -85,6 +85,14 @@ typedef struct {
 
 typedef enum { EBLC_FLOAT32 = 0 } eblc_dtype;
 
+/* Result record of an asynchronous compress, written by the device when the call's work
+ * completes on its stream. */
+typedef struct {
+    uint64_t compressed_bytes; /* stream length; with status CAPACITY, the required capacity */
+    uint32_t status;           /* EBLC_OK or EBLC_CAPACITY */
+    uint32_t reserved;
+} eblc_result_t;
+
 /* Returns EBLC_ABI_VERSION of the library. */
 int eblc_abi_version(void);
 
@@ -132,13 +140,35 @@ size_t eblc_payload_alignment(const eblc_plan_t *plan);
 eblc_status eblc_compress(eblc_plan_t *plan, const float *in, void *out, size_t out_capacity,
                           size_t *compressed_bytes, void *sidecar, void *stream);
 
+/* Asynchronous compress: enqueues the same work as eblc_compress on `stream` and returns at
+ * once, without waiting ("Provider layout": device work may remain queued on the supplied
+ * stream).  When the work completes, the device writes the call's eblc_result_t at `result`,
+ * which must be 8-byte aligned device memory or pinned host memory (hipHostMalloc) that
+ * stays valid until then.  The plan's workspace is shared by its calls, so calls on one plan
+ * must be ordered on one stream.  Errors detectable on the host are returned at once
+ * (INVALID_ARGUMENT, DEVICE_ERROR); capacity is reported in the record. */
+eblc_status eblc_compress_async(eblc_plan_t *plan, const float *in, void *out, size_t out_capacity,
+                                eblc_result_t *result, void *stream);
+
+/* Batched asynchronous compress: count fields of the plan's shape, in[k] -> out[k] with
+ * capacity out_capacity[k], result record k at results + k, enqueued back to back on one
+ * stream with no host wait between them (the snapshot-batch case of a solver saving many time
+ * steps).  The three pointer arrays are host arrays of device pointers; `results` as for
+ * eblc_compress_async.  All arguments are checked before anything is enqueued. */
+eblc_status eblc_compress_batch(eblc_plan_t *plan, int count, const float *const *in, void *const *out,
+                                const size_t *out_capacity, eblc_result_t *results, void *stream);
+
 /* Decompress a stream of compressed_bytes at device pointer `in` into n floats at `out`,
  * enqueued on `stream`; returns without waiting ("Provider layout": device work may remain
- * queued on the supplied stream).  The host checks 128 + align16(nseg) <= compressed_bytes
- * <= max_compressed_bytes (else CORRUPT_STREAM at once).  Header or section problems found
- * on the device (wrong magic/version/dims/n/offsets, widths above 32, outlier indices not
- * strictly ascending below n) set a sticky CORRUPT_STREAM that eblc_plan_status returns;
- * the contents of `out` are then unspecified.  sidecar must be NULL. */
+ * queued on the supplied stream).  compressed_bytes may be the stream's length or any larger
+ * count of readable bytes up to max_compressed_bytes: the stream's own length is read from its
+ * header on the device and must not exceed it, so a stream from eblc_compress_async can be
+ * decompressed without the host ever reading its length.  The host checks 128 +
+ * align16(nseg) <= compressed_bytes <= max_compressed_bytes (else CORRUPT_STREAM at once).
+ * Header or section problems found on the device (wrong magic/version/dims/n/offsets, widths
+ * above 32, outlier indices not strictly ascending below n) set a sticky CORRUPT_STREAM that
+ * eblc_plan_status returns; the contents of `out` are then unspecified.  sidecar must be
+ * NULL. */
 eblc_status eblc_decompress(eblc_plan_t *plan, const void *in, size_t compressed_bytes,
                             const void *sidecar, float *out, void *stream);
 
