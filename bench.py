@@ -156,6 +156,9 @@ def main() -> int:
     ap.add_argument("--api", choices=["batch", "sync"], default="batch",
                     help="batch: eblc_compress_batch (no host wait) and decompress by buffer capacity; "
                          "sync: eblc_compress per field, which waits to return each length")
+    ap.add_argument("--halo", type=int, default=0, metavar="H",
+                    help="store each field inside a buffer padded by H elements on every side of every "
+                         "axis and compress / decompress through the padded strides")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device to device once (counter calibration)")
     args = ap.parse_args()
@@ -177,10 +180,26 @@ def main() -> int:
     dims0, opts0 = items[0][1], items[0][2]
     assert all(d == dims0 and o == opts0 for _, d, o in items)
     n = items[0][0].numel()
-    log(f"[bench] {len(items)} field(s), n={n} dims={dims0} opts={opts0}")
-    plan = binding.Plan(dims0, opts0, 0)
+    strides = None
+    contiguous_items = items
+    if args.halo > 0:
+        # the solver's view: each field lives inside a halo-padded array
+        h = args.halo
+        pdims = [d + 2 * h for d in dims0]
+        strides = [int(np.prod(pdims[a + 1:])) for a in range(len(pdims))]
+        offset = sum(h * s for s in strides)
+        span = 1 + sum((d - 1) * s for d, s in zip(dims0, strides))
+        padded = []
+        for x, dims, opts in items:
+            buf = torch.zeros(offset + span + 4, dtype=torch.float32, device=dev)
+            torch.as_strided(buf, dims0, strides, offset).copy_(x.reshape(dims0))
+            padded.append((buf[offset:], dims, opts))
+        items = padded
+        desc += f"; stored with a {h}-element halo on every side (strides {strides})"
+    log(f"[bench] {len(items)} field(s), n={n} dims={dims0} opts={opts0} strides={strides}")
+    plan = binding.Plan(dims0, opts0, 0, strides=strides)
     outs = [torch.empty(plan.max_bytes, dtype=torch.uint8, device=dev) for _ in items]
-    ys = [torch.empty(n, dtype=torch.float32, device=dev) for _ in items]
+    ys = [torch.empty_like(x) for x, _, _ in items]
     stream = torch.cuda.current_stream()
     nbytes = [plan.max_bytes] * len(items)
     xs = [x for x, _, _ in items]
@@ -268,8 +287,13 @@ def main() -> int:
     # round-trip property, checked outside the timed region: every value within its bound
     err_max = 0.0
     for i, (x, _, _) in enumerate(items[:4]):
-        fin = torch.isfinite(x)
-        e = float((ys[i] - x).abs()[fin].max())
+        if strides is not None:
+            xv = torch.as_strided(x, dims0, strides)
+            yv = torch.as_strided(ys[i], dims0, strides)
+        else:
+            xv, yv = x, ys[i]
+        fin = torch.isfinite(xv)
+        e = float((yv - xv).abs()[fin].max())
         assert e <= ebs[i], f"field {i}: max |x - x'| {e} above eb {ebs[i]}"
         err_max = max(err_max, e)
     log(f"[bench] eb={ebs[0]:.6g} max|x-x'|={err_max:.6g} outliers(first)={outliers[0]}")
@@ -303,6 +327,7 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": desc, "fields": len(items), "n": n, "dims": dims0, "options": opts0,
+                   "strides": strides,
                    "step": "compress all fields, then decompress all streams",
                    "api": "eblc_compress_batch + eblc_decompress" if args.api == "batch"
                    else "eblc_compress (waits per field) + eblc_decompress"},
@@ -320,7 +345,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(items, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(contiguous_items, args.cpu_budget)
     plan.close()
     if args.calibrate_copy > 0:
         # a plain device-to-device copy of known size, for scaling the HBM byte counters

@@ -211,8 +211,8 @@ def eblc_plan_kernel_times(plan, max_kernels: int = 8):
 class Plan:
     """Owning wrapper: a plan plus its limits; destroys the plan when closed."""
 
-    def __init__(self, dims, options: str | None = None, device: int = 0):
-        st, p = eblc_plan_create(dims, options, device)
+    def __init__(self, dims, options: str | None = None, device: int = 0, strides=None):
+        st, p = eblc_plan_create(dims, options, device, strides=strides)
         if st != EBLC_OK:
             raise ValueError(f"eblc_plan_create: {eblc_status_string(st)}")
         self.handle = p

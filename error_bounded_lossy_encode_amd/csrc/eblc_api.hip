@@ -167,6 +167,21 @@ void resolve_abs(double eps, DevInfo *info) {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+/* The field pointer of a call: 16-byte aligned for a contiguous plan; for a padded plan any
+ * 4-byte aligned pointer (a halo's first interior element often is not 16-byte aligned). */
+bool field_ptr_ok(const eblc_plan *plan, const void *p) {
+    return plan->pa.lay.strided ? aligned4(p) : aligned16(p);
+}
+
+/* The plan's kernel arguments for one call: 128-bit access to a padded field only when the
+ * call's pointer is 16-byte aligned too. */
+PlanArgs call_args(const eblc_plan *plan, const void *field) {
+    PlanArgs pa = plan->pa;
+    if (pa.lay.strided && !aligned16(field)) pa.lay.vec = 0;
+    return pa;
+}
 
 eblc_status hip_status(hipError_t e) { return e == hipSuccess ? EBLC_OK : EBLC_DEVICE_ERROR; }
 
@@ -184,9 +199,8 @@ hipError_t timed(eblc_plan *p, hipStream_t st, const char *name, F &&launch) {
 }
 
 eblc_status check_compress_args(const eblc_plan *plan, const float *in, const void *out) {
-    (void)plan;
     if (in == nullptr || out == nullptr) return EBLC_INVALID_ARGUMENT;
-    if (!aligned16(in) || !aligned16(out)) return EBLC_INVALID_ARGUMENT;
+    if (!field_ptr_ok(plan, in) || !aligned16(out)) return EBLC_INVALID_ARGUMENT;
     return EBLC_OK;
 }
 
@@ -194,7 +208,7 @@ eblc_status check_compress_args(const eblc_plan *plan, const float *in, const vo
  * result record) -> compaction with outliers. */
 hipError_t enqueue_compress(eblc_plan *plan, const float *in, void *out, size_t out_capacity,
                             eblc_result_t *result, hipStream_t st) {
-    const PlanArgs &pa = plan->pa;
+    const PlanArgs pa = call_args(plan, in);
     const Workspace &ws = plan->ws;
     uint8_t *o = static_cast<uint8_t *>(out);
     const uint64_t widths_bytes = align_up(pa.nseg, 16);
@@ -208,6 +222,56 @@ hipError_t enqueue_compress(eblc_plan *plan, const float *in, void *out, size_t 
     if (e == hipSuccess) e = timed(plan, st, "scan", [&] { return launch_scan_compress(pa, ws, o, out_capacity, res, st); });
     if (e == hipSuccess) e = timed(plan, st, "compact", [&] { return launch_compact(in, pa, ws, o, widths_direct ? nullptr : ws.widths, st); });
     return e;
+}
+
+/* floor(2^64 / d) + 1, the exact reciprocal for dividing 32-bit values by d >= 2; 0 for d = 1. */
+uint64_t reciprocal(uint64_t d) {
+    if (d <= 1) return 0;
+    return (uint64_t)(((unsigned __int128)1 << 64) / d) + 1;
+}
+
+/* Layout of the caller's array from dims and strides (slowest to fastest, strides in elements,
+ * "Provider layout").  Accepted: NULL or row-major strides with padding -- fastest stride 1 and
+ * each outer stride at least the extent times the stride of the dimension below it.  Anything
+ * else (transposed, overlapping, zero or negative strides) is UNSUPPORTED. */
+eblc_status make_layout(int rank, const int64_t *dims, const int64_t *strides, Layout *lay) {
+    *lay = Layout{};
+    lay->rank = (uint32_t)rank;
+    lay->L = (uint32_t)dims[rank - 1];
+    lay->vec = 1;
+    if (strides == nullptr) return EBLC_OK;
+    bool contiguous = true;
+    int64_t expect = 1;
+    for (int a = rank - 1; a >= 0; --a) {
+        if (strides[a] != expect) contiguous = false;
+        expect *= dims[a];
+    }
+    if (contiguous) return EBLC_OK;
+    if (strides[rank - 1] != 1) return EBLC_UNSUPPORTED;
+    unsigned __int128 span = 1;  /* elements a padded array of these strides covers */
+    for (int a = rank - 2; a >= 0; --a) {
+        if (strides[a] <= 0 || (unsigned __int128)strides[a] < (unsigned __int128)strides[a + 1] * (uint64_t)dims[a + 1])
+            return EBLC_UNSUPPORTED;
+    }
+    for (int a = 0; a < rank; ++a) span += (unsigned __int128)(dims[a] - 1) * (uint64_t)strides[a];
+    if (span >= ((unsigned __int128)1 << 62)) return EBLC_UNSUPPORTED;
+    lay->strided = 1;
+    bool vec = lay->L % 4 == 0;
+    for (int a = 0; a < rank - 1; ++a) vec = vec && strides[a] % 4 == 0;
+    lay->vec = vec ? 1u : 0u;
+    lay->mL = reciprocal(lay->L);
+    if (rank >= 2) lay->s1 = (uint64_t)strides[rank - 2];
+    if (rank >= 3) {
+        lay->o1 = (uint32_t)dims[rank - 2];
+        lay->m1 = reciprocal(lay->o1);
+        lay->s2 = (uint64_t)strides[rank - 3];
+    }
+    if (rank >= 4) {
+        lay->o2 = (uint32_t)dims[rank - 3];
+        lay->m2 = reciprocal(lay->o2);
+        lay->s3 = (uint64_t)strides[rank - 4];
+    }
+    return EBLC_OK;
 }
 
 }  // namespace
@@ -244,13 +308,9 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
         n *= (uint64_t)dims[a];
         if (n >= (1ull << 32)) return EBLC_INVALID_ARGUMENT;
     }
-    if (strides != nullptr) {
-        int64_t expect = 1;
-        for (int a = rank - 1; a >= 0; --a) {
-            if (strides[a] != expect) return EBLC_UNSUPPORTED;
-            expect *= dims[a];
-        }
-    }
+    Layout lay{};
+    eblc_status ls = make_layout(rank, dims, strides, &lay);
+    if (ls != EBLC_OK) return ls;
     Options o;
     eblc_status st = parse_options(options, &o);
     if (st != EBLC_OK) return st;
@@ -283,6 +343,7 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     pa.dchunks = (uint32_t)((n + kDecChunk - 1) / kDecChunk);
     pa.dgroups = (pa.dchunks + kDecChunksPerGroup - 1) / kDecChunksPerGroup;
     pa.side_max = o.side_max;
+    pa.lay = lay;
 
     /* workspace: one allocation, carved into 256-byte aligned arrays */
     const uint64_t nc = pa.nchunks > pa.dchunks ? pa.nchunks : pa.dchunks;
@@ -409,8 +470,8 @@ eblc_status eblc_compress_batch(eblc_plan_t *plan, int count, const float *const
 eblc_status eblc_decompress(eblc_plan_t *plan, const void *in, size_t compressed_bytes,
                             const void *sidecar, float *out, void *stream) {
     if (plan == nullptr || in == nullptr || out == nullptr) return EBLC_INVALID_ARGUMENT;
-    if (sidecar != nullptr || !aligned16(in) || !aligned16(out)) return EBLC_INVALID_ARGUMENT;
-    const PlanArgs &pa = plan->pa;
+    if (sidecar != nullptr || !aligned16(in) || !field_ptr_ok(plan, out)) return EBLC_INVALID_ARGUMENT;
+    const PlanArgs pa = call_args(plan, out);
     if (compressed_bytes < kHeaderBytes + align_up(pa.nseg, 16) ||
         compressed_bytes > kHeaderBytes + align_up(4 * pa.n, 16))
         return EBLC_CORRUPT_STREAM;

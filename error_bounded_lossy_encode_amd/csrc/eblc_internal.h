@@ -76,6 +76,20 @@ struct DevInfo {
     uint32_t dec_B;         /* decompress: Lorenzo block read from the stream */
 };
 
+/* Where the caller's values live.  The codec works on the row-major flattened index i over the
+ * dims; the array may be padded (each outer stride at least the extent below it, fastest stride
+ * 1), so value i sits at element offset(i) of the caller's pointer.  Divisions use exact
+ * reciprocals: for v < 2^32 and d >= 2, v / d = floor(v * (floor(2^64 / d) + 1) / 2^64). */
+struct Layout {
+    uint32_t strided;       /* 0: offset(i) = i */
+    uint32_t vec;           /* each 4-aligned group of 4 values is contiguous and 16-byte aligned */
+    uint32_t rank;
+    uint32_t L;             /* fastest extent */
+    uint32_t o1, o2;        /* extents of the next two dims, fast to slow (rank 4 uses both) */
+    uint64_t mL, m1, m2;    /* reciprocals of L, o1, o2 (0 when the divisor is 1) */
+    uint64_t s1, s2, s3;    /* strides of the outer dims, fast to slow */
+};
+
 /* Plan constants passed by value to the kernels. */
 struct PlanArgs {
     uint64_t n;
@@ -89,6 +103,7 @@ struct PlanArgs {
     uint32_t dchunks;       /* decode chunks */
     uint32_t dgroups;       /* decode groups */
     uint64_t side_max;
+    Layout lay;             /* memory layout of the compress input and decompress output */
 };
 
 /* Workspace pointers (all device memory owned by the plan). */

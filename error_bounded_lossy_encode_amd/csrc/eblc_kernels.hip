@@ -113,6 +113,78 @@ __device__ __forceinline__ void st_nt(uint4 *p, const uint4 &v) {
     __builtin_nontemporal_store(t, reinterpret_cast<v4u32 *>(p));
 }
 
+/* ---- the caller's memory layout ------------------------------------------------------------ */
+
+__device__ __forceinline__ uint32_t div_m(uint32_t v, uint64_t m) {
+    return m == 0 ? v : (uint32_t)__umul64hi((uint64_t)v, m);
+}
+
+/* Element offset of flattened value i (i < 2^32) in the caller's array; *col receives i's
+ * position in its row. */
+template <bool STRIDED>
+__device__ __forceinline__ uint64_t elem_off(const Layout &lo, uint64_t i, uint32_t *col_out = nullptr) {
+    if (!STRIDED) return i;
+    const uint32_t ii = (uint32_t)i;
+    const uint32_t row = div_m(ii, lo.mL);
+    const uint32_t col = ii - row * lo.L;
+    if (col_out != nullptr) *col_out = col;
+    if (lo.rank == 2) return col + (uint64_t)row * lo.s1;
+    const uint32_t r1 = div_m(row, lo.m1);
+    const uint32_t c1 = row - r1 * lo.o1;
+    if (lo.rank == 3) return col + (uint64_t)c1 * lo.s1 + (uint64_t)r1 * lo.s2;
+    const uint32_t r2 = div_m(r1, lo.m2);
+    const uint32_t c2 = r1 - r2 * lo.o2;
+    return col + (uint64_t)c1 * lo.s1 + (uint64_t)c2 * lo.s2 + (uint64_t)r2 * lo.s3;
+}
+
+/* 128-bit non-temporal access at a 4-byte aligned address (gfx950 executes dword-aligned
+ * multi-dword global accesses). */
+typedef float v4f32u __attribute__((ext_vector_type(4), aligned(4)));
+
+__device__ __forceinline__ float4 ld_nt_u(const float *p) {
+    const v4f32u t = __builtin_nontemporal_load(reinterpret_cast<const v4f32u *>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
+}
+
+__device__ __forceinline__ void st_nt_u(float *p, const float4 &v) {
+    const v4f32u t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<v4f32u *>(p));
+}
+
+/* Values i .. i+3 (i a multiple of 4, all below n), streamed once: one 128-bit access when they
+ * are contiguous in memory (16-byte aligned with a vectorisable layout, else whenever they sit
+ * in one row), one access per value when a row boundary splits them. */
+template <bool STRIDED>
+__device__ __forceinline__ float4 load4(const float *x, const Layout &lo, uint64_t i) {
+    if (!STRIDED) return ld_nt(reinterpret_cast<const float4 *>(x + i));
+    uint32_t col;
+    const uint64_t off = elem_off<true>(lo, i, &col);
+    if (lo.vec) return ld_nt(reinterpret_cast<const float4 *>(x + off));
+    if (col + 3 < lo.L) return ld_nt_u(x + off);
+    return make_float4(x[off], x[elem_off<true>(lo, i + 1)], x[elem_off<true>(lo, i + 2)],
+                       x[elem_off<true>(lo, i + 3)]);
+}
+
+template <bool STRIDED>
+__device__ __forceinline__ void store4(float *y, const Layout &lo, uint64_t i, const float4 &v) {
+    if (!STRIDED) {
+        st_nt(reinterpret_cast<float4 *>(y + i), v);
+        return;
+    }
+    uint32_t col;
+    const uint64_t off = elem_off<true>(lo, i, &col);
+    if (lo.vec) {
+        st_nt(reinterpret_cast<float4 *>(y + off), v);
+    } else if (col + 3 < lo.L) {
+        st_nt_u(y + off, v);
+    } else {
+        y[off] = v.x;
+        y[elem_off<true>(lo, i + 1)] = v.y;
+        y[elem_off<true>(lo, i + 2)] = v.z;
+        y[elem_off<true>(lo, i + 3)] = v.w;
+    }
+}
+
 /* ---- quantizer ------------------------------------------------------------------------------ */
 
 struct QParams {
@@ -215,28 +287,29 @@ __device__ __forceinline__ void minmax4(const float4 &a, float &mn, float &mx) {
  * non-temporal loads: the field is streamed once and must not evict what the caches hold (on
  * gfx950 a plain load of a line also forces out dirty lines left by earlier writes, which
  * halves the read rate).  The last workgroup also takes the n mod 4 trailing values. */
+template <bool STRIDED>
 __global__ __launch_bounds__(kRangeThreads) void range_partial_kernel(const float *__restrict__ x,
-                                                                      uint64_t n,
+                                                                      uint64_t n, Layout lo,
                                                                       float *__restrict__ part) {
     __shared__ float s_mn[kRangeThreads / kWave], s_mx[kRangeThreads / kWave];
     float mn[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
     float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     const uint64_t n4 = n / 4;
-    const float4 *x4 = reinterpret_cast<const float4 *>(x);
     const uint64_t base = (uint64_t)blockIdx.x * kRangeSpan + threadIdx.x;
     if (base + (uint64_t)(kRangeVec - 1) * kRangeThreads < n4) {
         float4 v[kRangeVec];
 #pragma unroll
-        for (int u = 0; u < kRangeVec; ++u) v[u] = ld_nt(x4 + base + (uint64_t)u * kRangeThreads);
+        for (int u = 0; u < kRangeVec; ++u) v[u] = load4<STRIDED>(x, lo, 4 * (base + (uint64_t)u * kRangeThreads));
 #pragma unroll
         for (int u = 0; u < kRangeVec; ++u) minmax4(v[u], mn[u & 3], mx[u & 3]);
     } else {
         for (int u = 0; u < kRangeVec; ++u) {
             const uint64_t i = base + (uint64_t)u * kRangeThreads;
-            if (i < n4) minmax4(ld_nt(x4 + i), mn[u & 3], mx[u & 3]);
+            if (i < n4) minmax4(load4<STRIDED>(x, lo, 4 * i), mn[u & 3], mx[u & 3]);
         }
     }
-    if (blockIdx.x == gridDim.x - 1 && threadIdx.x < (n & 3u)) minmax_finite(x[4 * n4 + threadIdx.x], mn[1], mx[1]);
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x < (n & 3u))
+        minmax_finite(x[elem_off<STRIDED>(lo, 4 * n4 + threadIdx.x)], mn[1], mx[1]);
     float a = fminf(fminf(mn[0], mn[1]), fminf(mn[2], mn[3]));
     float b = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
     for (int o = 32; o >= 1; o >>= 1) {
@@ -424,8 +497,8 @@ __device__ __forceinline__ void pack_lane(const uint32_t z[kEncLaneVals], uint32
  * in LDS (the codes stay in VGPRs); one wave scan of the widths gives every segment's word
  * offset in the chunk; pass 2 packs each tile at those offsets.  `carry` is the code of the
  * value before the chunk when the chunk does not start a Lorenzo block. */
-template <bool FULL>
-__device__ __forceinline__ void encode_chunk(const float *__restrict__ x, uint64_t cbase, uint64_t n,
+template <bool FULL, bool STRIDED>
+__device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const Layout &lo, uint64_t cbase, uint64_t n,
                                              const QParams &qp, uint32_t bmask, int32_t carry,
                                              uint32_t *pay, uint8_t *wid, uint32_t *emask_chunk,
                                              uint32_t *stage_idx, uint32_t *stage_val, EncState &st) {
@@ -434,12 +507,11 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, uint64
     const uint32_t j = lane & (kSegLanes - 1), g = lane / kSegLanes;
     float xs[kEncTiles][V];
     if (FULL) {
-        const float4 *src = reinterpret_cast<const float4 *>(x + cbase) + (V / 4) * lane;
 #pragma unroll
         for (int t = 0; t < kEncTiles; ++t) {
 #pragma unroll
             for (int h = 0; h < V / 4; ++h) {
-                const float4 a = ld_nt(src + t * (kEncTile / 4) + h);
+                const float4 a = load4<STRIDED>(x, lo, cbase + (uint64_t)t * kEncTile + V * lane + 4 * h);
                 xs[t][4 * h] = a.x; xs[t][4 * h + 1] = a.y; xs[t][4 * h + 2] = a.z; xs[t][4 * h + 3] = a.w;
             }
         }
@@ -448,7 +520,7 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, uint64
         for (int t = 0; t < kEncTiles; ++t) {
             const uint64_t e = cbase + (uint64_t)t * kEncTile + V * lane;
 #pragma unroll
-            for (int k = 0; k < V; ++k) xs[t][k] = e + k < n ? x[e + k] : 0.0f;
+            for (int k = 0; k < V; ++k) xs[t][k] = e + k < n ? x[elem_off<STRIDED>(lo, e + k)] : 0.0f;
         }
     }
     const uint32_t ntiles = FULL ? kEncTiles : (uint32_t)((n - cbase + kEncTile - 1) / kEncTile);
@@ -485,6 +557,7 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, uint64
  * words in its scratch slot, its width bytes (into the stream, or into staging when the output
  * buffer cannot hold them), its word and escape counts and the escape bitmask of every tile
  * with an escape; per workgroup, the sums the device-wide scan runs over. */
+template <bool STRIDED>
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(
     const float *__restrict__ x, PlanArgs pa, Workspace ws, uint8_t *__restrict__ widths_dst,
     uint64_t widths_bytes) {
@@ -519,7 +592,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
          * the value before the chunk (0 if that value escapes) */
         int32_t carry = 0;
         if (((uint32_t)cbase & bmask) != 0) {
-            const float xp = x[cbase - 1];
+            const float xp = x[elem_off<STRIDED>(pa.lay, cbase - 1)];
             uint32_t e;
             const int32_t qprev = quantize_slow(xp, rintf(xp * qp.r), qp, &e);
             carry = e ? 0 : qprev;
@@ -528,9 +601,11 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
         uint32_t *stage_idx = s_stage[wave][0];
         uint32_t *stage_val = s_stage[wave][1];
         if (cbase + kEncChunk <= pa.n)
-            encode_chunk<true>(x, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk, stage_idx, stage_val, st);
+            encode_chunk<true, STRIDED>(x, pa.lay, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk,
+                                        stage_idx, stage_val, st);
         else
-            encode_chunk<false>(x, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk, stage_idx, stage_val, st);
+            encode_chunk<false, STRIDED>(x, pa.lay, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk,
+                                         stage_idx, stage_val, st);
         wave_lds_sync();
         /* chunk payload -> scratch slot, widths -> stream (or staging) */
         uint4 *dst = reinterpret_cast<uint4 *>(ws.scratch + cbase);
@@ -739,7 +814,8 @@ __device__ __forceinline__ uint32_t chunk_offset(const uint32_t *gpre, const uin
  * from the encoder's staging when they all fit there; otherwise lane l < kEncSegs owns segment
  * l, takes its escape bitmask, ranks its escapes after O and the lanes before it, and writes
  * (index, raw bits) in ascending index order, re-reading the values from the input. */
-__device__ __forceinline__ void write_chunk_outliers(const float *__restrict__ x, const Workspace &ws,
+template <bool STRIDED>
+__device__ __forceinline__ void write_chunk_outliers(const float *__restrict__ x, const Layout &lo, const Workspace &ws,
                                                      uint32_t c, uint32_t cnt, uint32_t O,
                                                      uint32_t *oidx, uint32_t *oval) {
     const uint32_t lane = threadIdx.x & 63;
@@ -765,7 +841,7 @@ __device__ __forceinline__ void write_chunk_outliers(const float *__restrict__ x
         const uint32_t bit = (uint32_t)__builtin_ctz(mask);
         const uint64_t idx = segbase + bit;
         oidx[rank] = (uint32_t)idx;
-        oval[rank] = xb[idx];
+        oval[rank] = xb[elem_off<STRIDED>(lo, idx)];
         ++rank;
         mask &= mask - 1;
     }
@@ -810,6 +886,7 @@ __device__ __forceinline__ void copy_chunk_payload(const uint32_t *__restrict__ 
  * copies its chunk's payload to the chunk's scanned offset, then writes the chunk's outliers.
  * In RAW mode the workgroup copies the group's input values instead.  The last group also
  * zeroes the pads after the payload and after the outlier sections. */
+template <bool STRIDED>
 __global__ __launch_bounds__(kBlockThreads) void compact_kernel(const float *__restrict__ x,
                                                                 PlanArgs pa, Workspace ws,
                                                                 uint8_t *__restrict__ out,
@@ -842,7 +919,10 @@ __global__ __launch_bounds__(kBlockThreads) void compact_kernel(const float *__r
         const uint64_t cnt = (n - gbase < (uint64_t)kGroupVals) ? n - gbase : (uint64_t)kGroupVals;
         uint32_t *dstw = reinterpret_cast<uint32_t *>(out + kHeaderBytes) + gbase;
         const uint32_t *srcw = reinterpret_cast<const uint32_t *>(x) + gbase;
-        if (cnt == (uint64_t)kGroupVals) {
+        if (STRIDED) {
+            const uint32_t *xb = reinterpret_cast<const uint32_t *>(x);
+            for (uint32_t i = tid; i < cnt; i += kBlockThreads) dstw[i] = xb[elem_off<true>(pa.lay, gbase + i)];
+        } else if (cnt == (uint64_t)kGroupVals) {
             constexpr int kPer = kGroupVals / 4 / kBlockThreads;
             const uint4 *s4 = reinterpret_cast<const uint4 *>(srcw);
             uint4 *d4 = reinterpret_cast<uint4 *>(dstw);
@@ -872,7 +952,7 @@ __global__ __launch_bounds__(kBlockThreads) void compact_kernel(const float *__r
     uint32_t *oval = reinterpret_cast<uint32_t *>(out + oval_off);
     if (c < pa.nchunks) {
         copy_chunk_payload(ws.scratch + (uint64_t)c * kEncChunk, words[wave], W, pay);
-        write_chunk_outliers(x, ws, c, escs[wave], O, oidx, oval);
+        write_chunk_outliers<STRIDED>(x, pa.lay, ws, c, escs[wave], O, oidx, oval);
     }
     if (widths_src != nullptr) {
         constexpr uint32_t kGroupWidthVecs = CPG * kEncSegs / 16;
@@ -988,6 +1068,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_decompress_kernel(const uin
  * unpack each lane's 4 values, undo the zigzag, prefix-sum inside each block (in-lane, then a
  * segmented DPP scan across lanes, plus the carry from the previous tile when a block spans
  * tiles), dequantize with f32(f32(q) * s) and store 4 values with one 128-bit store. */
+template <bool STRIDED>
 __global__ __launch_bounds__(kBlockThreads) void decode_kernel(const uint8_t *__restrict__ in,
                                                                PlanArgs pa, Workspace ws,
                                                                float *__restrict__ out) {
@@ -1008,7 +1089,10 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(const uint8_t *__
         const uint64_t cnt = full ? (uint64_t)kDecChunk : n - cbase;
         const uint32_t *srcw = reinterpret_cast<const uint32_t *>(in + kHeaderBytes) + cbase;
         uint32_t *dstw = reinterpret_cast<uint32_t *>(out) + cbase;
-        if (full) {
+        if (STRIDED) {
+            uint32_t *ob = reinterpret_cast<uint32_t *>(out);
+            for (uint32_t i = lane; i < cnt; i += kWave) ob[elem_off<true>(pa.lay, cbase + i)] = srcw[i];
+        } else if (full) {
             const uint4 *s4 = reinterpret_cast<const uint4 *>(srcw);
             uint4 *d4 = reinterpret_cast<uint4 *>(dstw);
             uint4 t[kDecChunk / 4 / kWave];
@@ -1076,12 +1160,12 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(const uint8_t *__
             o.w = (float)q[3] * s;
             const uint64_t e0 = cbase + (uint64_t)t * kTile + 4 * lane;
             if (full) {
-                st_nt(reinterpret_cast<float4 *>(out + e0), o);
+                store4<STRIDED>(out, pa.lay, e0, o);
             } else {
-                if (e0 + 0 < n) out[e0 + 0] = o.x;
-                if (e0 + 1 < n) out[e0 + 1] = o.y;
-                if (e0 + 2 < n) out[e0 + 2] = o.z;
-                if (e0 + 3 < n) out[e0 + 3] = o.w;
+                if (e0 + 0 < n) out[elem_off<STRIDED>(pa.lay, e0 + 0)] = o.x;
+                if (e0 + 1 < n) out[elem_off<STRIDED>(pa.lay, e0 + 1)] = o.y;
+                if (e0 + 2 < n) out[elem_off<STRIDED>(pa.lay, e0 + 2)] = o.z;
+                if (e0 + 3 < n) out[elem_off<STRIDED>(pa.lay, e0 + 3)] = o.w;
             }
         }
     }
@@ -1089,6 +1173,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(const uint8_t *__
 
 /* ---- K8: outlier patch ------------------------------------------------------------------------ */
 
+template <bool STRIDED>
 __global__ __launch_bounds__(256) void patch_kernel(const uint8_t *__restrict__ in, PlanArgs pa,
                                                     Workspace ws, float *__restrict__ out) {
     DevInfo *info = ws.info;
@@ -1101,7 +1186,7 @@ __global__ __launch_bounds__(256) void patch_kernel(const uint8_t *__restrict__ 
     for (uint64_t k = (uint64_t)blockIdx.x * 256 + threadIdx.x; k < m; k += stride) {
         const uint32_t idx = oidx[k];
         const bool ok = idx < pa.n && (k == 0 || oidx[k - 1] < idx);
-        if (ok) ob[idx] = oval[k];
+        if (ok) ob[elem_off<STRIDED>(pa.lay, idx)] = oval[k];
         else atomicOr(&info->sticky, 1u);
     }
 }
@@ -1113,8 +1198,12 @@ __global__ __launch_bounds__(256) void patch_kernel(const uint8_t *__restrict__ 
 hipError_t launch_range(const float *x, const PlanArgs &pa, const Workspace &ws, double eps,
                         hipStream_t stream) {
     const uint32_t grid = range_blocks(pa.n);
-    hipLaunchKernelGGL(range_partial_kernel, dim3(grid), dim3(kRangeThreads), 0, stream, x, pa.n,
-                       ws.range_part);
+    if (pa.lay.strided)
+        hipLaunchKernelGGL(range_partial_kernel<true>, dim3(grid), dim3(kRangeThreads), 0, stream, x, pa.n,
+                           pa.lay, ws.range_part);
+    else
+        hipLaunchKernelGGL(range_partial_kernel<false>, dim3(grid), dim3(kRangeThreads), 0, stream, x, pa.n,
+                           pa.lay, ws.range_part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(range_resolve_kernel, dim3(1), dim3(kScanThreads), 0, stream, ws.range_part, grid,
@@ -1124,8 +1213,12 @@ hipError_t launch_range(const float *x, const PlanArgs &pa, const Workspace &ws,
 
 hipError_t launch_encode(const float *x, const PlanArgs &pa, const Workspace &ws,
                          uint8_t *widths_dst, uint64_t widths_bytes, hipStream_t stream) {
-    hipLaunchKernelGGL(encode_kernel, dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa, ws,
-                       widths_dst, widths_bytes);
+    if (pa.lay.strided)
+        hipLaunchKernelGGL(encode_kernel<true>, dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa, ws,
+                           widths_dst, widths_bytes);
+    else
+        hipLaunchKernelGGL(encode_kernel<false>, dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa, ws,
+                           widths_dst, widths_bytes);
     return hipGetLastError();
 }
 
@@ -1138,8 +1231,12 @@ hipError_t launch_scan_compress(const PlanArgs &pa, const Workspace &ws, uint8_t
 
 hipError_t launch_compact(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *out,
                           const uint8_t *widths_src, hipStream_t stream) {
-    hipLaunchKernelGGL(compact_kernel, dim3(pa.ngroups), dim3(kBlockThreads), 0, stream, x, pa, ws,
-                       out, widths_src);
+    if (pa.lay.strided)
+        hipLaunchKernelGGL(compact_kernel<true>, dim3(pa.ngroups), dim3(kBlockThreads), 0, stream, x, pa, ws,
+                           out, widths_src);
+    else
+        hipLaunchKernelGGL(compact_kernel<false>, dim3(pa.ngroups), dim3(kBlockThreads), 0, stream, x, pa, ws,
+                           out, widths_src);
     return hipGetLastError();
 }
 
@@ -1159,8 +1256,12 @@ hipError_t launch_scan_decompress(const uint8_t *in, uint64_t in_bytes, const Pl
 
 hipError_t launch_decode(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
                          hipStream_t stream) {
-    hipLaunchKernelGGL(decode_kernel, dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in, pa, ws,
-                       out);
+    if (pa.lay.strided)
+        hipLaunchKernelGGL(decode_kernel<true>, dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in, pa, ws,
+                           out);
+    else
+        hipLaunchKernelGGL(decode_kernel<false>, dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in, pa, ws,
+                           out);
     return hipGetLastError();
 }
 
@@ -1168,7 +1269,10 @@ hipError_t launch_patch(const uint8_t *in, const PlanArgs &pa, const Workspace &
                         hipStream_t stream) {
     uint64_t want = (pa.side_max + 255) / 256;
     uint32_t grid = (uint32_t)(want < 1 ? 1 : (want > (uint64_t)kPatchBlocksMax ? kPatchBlocksMax : want));
-    hipLaunchKernelGGL(patch_kernel, dim3(grid), dim3(256), 0, stream, in, pa, ws, out);
+    if (pa.lay.strided)
+        hipLaunchKernelGGL(patch_kernel<true>, dim3(grid), dim3(256), 0, stream, in, pa, ws, out);
+    else
+        hipLaunchKernelGGL(patch_kernel<false>, dim3(grid), dim3(256), 0, stream, in, pa, ws, out);
     return hipGetLastError();
 }
 

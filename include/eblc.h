@@ -28,7 +28,9 @@
  *
  * Threading: a plan is used by one host thread at a time; distinct plans may run
  * concurrently on distinct streams.  All device pointers must come from hipMalloc (or
- * torch) on the plan's device and be 16-byte aligned.
+ * torch) on the plan's device and be 16-byte aligned, except the field pointer of a padded
+ * plan (`in` of compress, `out` of decompress), which needs 4-byte alignment only.  The field
+ * pointer addresses the plan's layout (contiguous, or padded through its strides).
  */
 #ifndef EBLC_H
 #define EBLC_H
@@ -102,7 +104,13 @@ int eblc_abi_version(void);
  *   rank     1..4; dims[rank] > 0, slowest to fastest ("Provider layout": dimensions and
  *            strides in slowest-to-fastest order, strides in elements).  n = prod(dims)
  *            must be below 2^32 (outlier indices are u32).
- *   strides  NULL, or exactly the row-major contiguous strides (else UNSUPPORTED).
+ *   strides  NULL (contiguous), or row-major strides in elements with padding allowed: the
+ *            fastest stride is 1 and each outer stride is at least the extent times the stride
+ *            of the dimension below it (a solver's halo-padded array).  compress reads, and
+ *            decompress writes, the dims' values through these strides and touches no padding
+ *            element; 128-bit access is kept when the fastest extent and every outer stride are
+ *            multiples of 4.  Other layouts (transposed, overlapping, zero or negative strides)
+ *            are UNSUPPORTED.
  *   options  NULL or "" -> relative error 1e-4 (the default bound named in "Priming");
  *            a bare decimal -> relative error (what DevitoPRO passes, "Provider layout");
  *            else ';'-separated key=value pairs:

@@ -55,5 +55,9 @@ def test_shape_checks():
     assert binding.eblc_plan_create([64, 0])[0] == binding.EBLC_INVALID_ARGUMENT
     assert binding.eblc_plan_create([1] * 5)[0] == binding.EBLC_UNSUPPORTED
     assert binding.eblc_plan_create([1 << 16, 1 << 16])[0] == binding.EBLC_INVALID_ARGUMENT
-    assert binding.eblc_plan_create([8, 8], strides=[16, 1])[0] == binding.EBLC_UNSUPPORTED
+    # row-major with padding is a supported layout; these are not: fastest stride other than 1
+    # (transposed), overlapping rows, zero or negative strides
+    for dims, strides in (([8, 8], [1, 8]), ([8, 8], [4, 1]), ([8, 8], [16, 2]), ([8, 8], [0, 1]),
+                          ([4, 4, 4], [16, -4, 1]), ([4, 4, 4], [8, 4, 1])):
+        assert binding.eblc_plan_create(dims, strides=strides)[0] == binding.EBLC_UNSUPPORTED, strides
     assert binding.eblc_plan_create([8, 8], dtype=3)[0] == binding.EBLC_UNSUPPORTED

@@ -1,0 +1,151 @@
+"""Padded (halo) layouts through the C ABI: a plan created with row-major strides that include
+padding reads its input and writes its reconstruction through those strides.
+
+The stream of a padded field must equal the oracle's stream of the packed interior, and
+decompression must write exactly the interior elements, leaving the padding untouched.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from error_bounded_lossy_encode_amd import synth
+from helpers import CANARY, parse_options
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = np.float32(-7.25e33)
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    from error_bounded_lossy_encode_amd import binding
+    binding.lib()
+    return binding, torch
+
+
+def padded(interior: np.ndarray, strides):
+    """Place a C-contiguous interior array into a sentinel-filled buffer with the given element
+    strides (slowest to fastest); returns the flat buffer."""
+    dims = interior.shape
+    span = 1 + sum((d - 1) * s for d, s in zip(dims, strides))
+    buf = np.full(span + 8, SENTINEL, dtype=np.float32)
+    view = np.lib.stride_tricks.as_strided(buf, shape=dims, strides=[4 * s for s in strides])
+    view[...] = interior
+    return buf, view
+
+
+CASES = [
+    # dims, strides, options
+    ([300, 260], [272, 1], "rel=1e-3;block=128;outlier_log2=15"),            # vectorisable rows
+    ([97, 131], [140, 1], "abs=1e-2;block=64;outlier_log2=15"),              # odd rows: scalar path
+    ([20, 34, 44], [34 * 52 + 5 * 52, 52, 1], "rel=1e-4;block=256;outlier_log2=30"),  # 3-D halo
+    ([5, 7, 9, 66], [7 * 12 * 72, 12 * 72, 72, 1], "rel=1e-3;block=32;outlier_log2=15"),  # rank 4
+    ([64, 1000], [1024, 1], "abs=1e-4;block=256;outlier_log2=6"),            # heavy escapes
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_padded_layout_matches_packed_interior(env, case):
+    binding, torch = env
+    dims, strides, opts = CASES[case]
+    rng = np.random.default_rng(700 + case)
+    n = int(np.prod(dims))
+    interior = synth.tiny_array(rng, n, "smooth" if case != 4 else "normal").reshape(dims)
+    if case == 2:
+        interior.reshape(-1)[::501] = np.float32(np.nan)
+    buf, _ = padded(interior, strides)
+    o = parse_options(opts, n)
+    ref = oracle.compress(interior.reshape(-1), dims, o["rel"], o["eps"], o["B"], o["T"], o["side_max"])
+    st, ref_dec = oracle.decompress(ref)
+    st, plan = binding.eblc_plan_create(dims, opts, 0, strides=strides)
+    assert st == binding.EBLC_OK, binding.eblc_status_string(st)
+    try:
+        maxb = binding.eblc_max_compressed_bytes(plan)
+        xd = torch.from_numpy(buf).cuda()
+        out = torch.full((maxb + 64,), CANARY, dtype=torch.uint8, device="cuda")
+        st, nb = binding.eblc_compress(plan, xd, out)
+        assert st == binding.EBLC_OK
+        got = out.cpu().numpy()
+        assert nb == ref.size and np.array_equal(got[:nb], ref)
+        yd = torch.from_numpy(np.full_like(buf, SENTINEL)).cuda()
+        assert binding.eblc_decompress(plan, out, nb, yd) == binding.EBLC_OK
+        assert binding.eblc_plan_status(plan) == binding.EBLC_OK
+        ybuf = yd.cpu().numpy()
+        yview = np.lib.stride_tricks.as_strided(ybuf, shape=dims, strides=[4 * s for s in strides])
+        assert np.array_equal(np.ascontiguousarray(yview).reshape(-1).view(np.uint32), ref_dec.view(np.uint32))
+        # nothing outside the interior was written
+        mask = np.ones(ybuf.size, bool)
+        idx = np.lib.stride_tricks.as_strided(np.arange(ybuf.size), shape=dims,
+                                              strides=[8 * s for s in strides]).reshape(-1)
+        mask[idx] = False
+        assert (ybuf[mask].view(np.uint32) == SENTINEL.view(np.uint32)).all()
+    finally:
+        binding.eblc_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("shift", [1, 2, 3])
+def test_padded_field_pointer_off_16_byte_boundary(env, shift):
+    """A halo puts the first interior element at an arbitrary 4-byte boundary: the field pointer
+    of a padded plan needs 4-byte alignment only, and the result is the same."""
+    binding, torch = env
+    dims, strides = [24, 36, 40], [38 * 44, 44, 1]
+    opts = "rel=1e-3;block=64;outlier_log2=15"
+    rng = np.random.default_rng(40 + shift)
+    interior = synth.tiny_array(rng, int(np.prod(dims)), "smooth").reshape(dims)
+    buf, _ = padded(interior, strides)
+    o = parse_options(opts, interior.size)
+    ref = oracle.compress(interior.reshape(-1), dims, o["rel"], o["eps"], o["B"], o["T"], o["side_max"])
+    _, ref_dec = oracle.decompress(ref)
+    st, plan = binding.eblc_plan_create(dims, opts, 0, strides=strides)
+    assert st == binding.EBLC_OK
+    try:
+        maxb = binding.eblc_max_compressed_bytes(plan)
+        base = torch.from_numpy(np.concatenate([np.zeros(shift, np.float32), buf])).cuda()
+        xd = base[shift:]
+        assert xd.data_ptr() % 16 == 4 * shift
+        out = torch.zeros(maxb, dtype=torch.uint8, device="cuda")
+        st, nb = binding.eblc_compress(plan, xd, out)
+        assert st == binding.EBLC_OK and np.array_equal(out.cpu().numpy()[:nb], ref)
+        ybase = torch.from_numpy(np.full(buf.size + shift, SENTINEL, np.float32)).cuda()
+        yd = ybase[shift:]
+        assert binding.eblc_decompress(plan, out, nb, yd) == binding.EBLC_OK
+        assert binding.eblc_plan_status(plan) == binding.EBLC_OK
+        ybuf = yd.cpu().numpy()
+        yview = np.lib.stride_tricks.as_strided(ybuf, shape=dims, strides=[4 * s for s in strides])
+        assert np.array_equal(np.ascontiguousarray(yview).reshape(-1).view(np.uint32), ref_dec.view(np.uint32))
+        # a contiguous plan still requires 16-byte alignment
+        st, cplan = binding.eblc_plan_create(dims, opts, 0)
+        assert binding.eblc_compress(cplan, xd, out)[0] == binding.EBLC_INVALID_ARGUMENT
+        binding.eblc_plan_destroy(cplan)
+    finally:
+        binding.eblc_plan_destroy(plan)
+
+
+def test_padded_layout_raw_fallback(env):
+    """Random bit patterns do not compress: the RAW stream holds the packed interior."""
+    binding, torch = env
+    dims, strides = [33, 70], [75, 1]
+    rng = np.random.default_rng(77)
+    interior = rng.integers(0, 1 << 32, np.prod(dims), dtype=np.uint64).astype(np.uint32).view(np.float32)
+    interior = interior.reshape(dims)
+    buf, _ = padded(interior, strides)
+    opts = "abs=1e-30;block=64;outlier_log2=2;side_max=0"
+    ref = oracle.compress(interior.reshape(-1), dims, False, 1e-30, 64, 2, 0)
+    assert int(ref[8]) == 1
+    st, plan = binding.eblc_plan_create(dims, opts, 0, strides=strides)
+    assert st == binding.EBLC_OK
+    try:
+        maxb = binding.eblc_max_compressed_bytes(plan)
+        xd = torch.from_numpy(buf).cuda()
+        out = torch.zeros(maxb, dtype=torch.uint8, device="cuda")
+        st, nb = binding.eblc_compress(plan, xd, out)
+        assert st == binding.EBLC_OK and np.array_equal(out.cpu().numpy()[:nb], ref)
+        yd = torch.from_numpy(np.full_like(buf, SENTINEL)).cuda()
+        assert binding.eblc_decompress(plan, out, nb, yd) == binding.EBLC_OK
+        assert binding.eblc_plan_status(plan) == binding.EBLC_OK
+        ybuf = yd.cpu().numpy()
+        yview = np.lib.stride_tricks.as_strided(ybuf, shape=dims, strides=[4 * s for s in strides])
+        assert np.array_equal(np.ascontiguousarray(yview).view(np.uint32), interior.view(np.uint32))
+    finally:
+        binding.eblc_plan_destroy(plan)
