@@ -68,6 +68,18 @@ def lib():
         L.oracle_decompress.restype = i32
         L.oracle_stream_elements.argtypes = [P, u64]
         L.oracle_stream_elements.restype = u64
+        L.oracle_bitshuffle.argtypes = [P, u32, P]
+        L.oracle_bitshuffle.restype = None
+        L.oracle_unbitshuffle.argtypes = [P, u32, P]
+        L.oracle_unbitshuffle.restype = None
+        L.oracle_rze.argtypes = [P, u32, P]
+        L.oracle_rze.restype = u32
+        L.oracle_unrze.argtypes = [P, u32, u32, P]
+        L.oracle_unrze.restype = i32
+        L.oracle_chunk_stream_bytes.argtypes = [u64, u64, u64]
+        L.oracle_chunk_stream_bytes.restype = u64
+        L.oracle_compress_chunked.argtypes = [P, i32, P, i32, f64, u32, i32, u64, P, u64, P]
+        L.oracle_compress_chunked.restype = u64
         _lib = L
     return _lib
 
@@ -142,6 +154,58 @@ def compress(x: np.ndarray, dims, rel: bool, eps: float, B: int = 256, T: int = 
                                 side_max, _ptr(out), cap, _ptr(req))
     assert tot > 0, "oracle stream larger than the raw bound"
     return out[:tot].copy()
+
+
+def compress_chunked(x: np.ndarray, dims, rel: bool, eps: float, chunk_values: int = 2048, T: int = 30,
+                     side_max: int | None = None) -> np.ndarray:
+    """Whole compressor with the chunk-cooperative coder (chunk_values = 1024, 2048 or 4096)."""
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    dims = [int(v) for v in dims]
+    n = int(np.prod(dims))
+    assert n == x.size
+    if side_max is None:
+        side_max = min(n, 1 << 23)
+    d = np.asarray(dims, dtype=np.uint64)
+    cap = raw_bytes(n)
+    out = np.zeros(cap, np.uint8)
+    req = np.zeros(1, np.uint64)
+    tot = lib().oracle_compress_chunked(_ptr(x), len(dims), _ptr(d), int(rel), float(eps), chunk_values, T,
+                                        side_max, _ptr(out), cap, _ptr(req))
+    assert tot > 0, "oracle stream larger than the raw bound"
+    return out[:tot].copy()
+
+
+def bitshuffle(z: np.ndarray) -> np.ndarray:
+    z = np.ascontiguousarray(z, dtype=np.uint32)
+    w = np.zeros(z.size, np.uint32)
+    lib().oracle_bitshuffle(_ptr(z), z.size, _ptr(w))
+    return w
+
+
+def unbitshuffle(words: np.ndarray) -> np.ndarray:
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    z = np.zeros(words.size, np.uint32)
+    lib().oracle_unbitshuffle(_ptr(words), words.size, _ptr(z))
+    return z
+
+
+def rze(words: np.ndarray) -> np.ndarray:
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    out = np.zeros(words.size + words.size // 32, np.uint32)
+    k = lib().oracle_rze(_ptr(words), words.size, _ptr(out))
+    return out[:k].copy()
+
+
+def unrze(data: np.ndarray, W: int):
+    """Returns the W words, or None for an inconsistent input."""
+    data = np.ascontiguousarray(data, dtype=np.uint32)
+    words = np.zeros(W, np.uint32)
+    st = lib().oracle_unrze(_ptr(data) if data.size else None, data.size, W, _ptr(words))
+    return None if st != 0 else words
+
+
+def chunk_stream_bytes(nchunks: int, sum_words: int, m: int) -> int:
+    return int(lib().oracle_chunk_stream_bytes(nchunks, sum_words, m))
 
 
 def decompress(stream: np.ndarray, n: int | None = None):

@@ -19,6 +19,7 @@ const uint16_t kVersion = 1;
 const uint16_t kHeaderBytes = 128;
 const uint8_t kModeLossy = 0;
 const uint8_t kModeRaw = 1;
+const uint8_t kModeChunk = 2; /* the chunk-cooperative coder: Quant -> Diff -> Bitshuffle -> RZE */
 const uint32_t kSeg = 32; /* values per bitpack segment */
 
 uint64_t align16(uint64_t v) { return (v + 15u) / 16u * 16u; }
@@ -213,6 +214,113 @@ uint64_t oracle_stream_bytes(uint64_t n, uint64_t sum_widths, uint64_t m) {
 
 uint64_t oracle_raw_bytes(uint64_t n) { return kHeaderBytes + align16(4 * n); }
 
+/* Chunk coder, "Bitshuffle" ("Pipeline Specialization Internals", Chunk-cooperative path: a
+ * Transform between Diff and the coder).  The chunk's V codes (V a multiple of 32) form
+ * G = V / 32 groups of 32; word b * G + g of the output holds bit b of every code of group g,
+ * code j of the group at bit j.  So the output is the chunk's bit planes, plane 0 first, and
+ * planes above the widest code are zero words. */
+void oracle_bitshuffle(const uint32_t *z, uint32_t V, uint32_t *words) {
+    uint32_t G = V / 32;
+    for (uint32_t k = 0; k < V; ++k) words[k] = 0;
+    for (uint32_t g = 0; g < G; ++g) {
+        for (uint32_t j = 0; j < 32; ++j) {
+            uint32_t v = z[32 * g + j];
+            for (uint32_t b = 0; b < 32; ++b) {
+                uint32_t bit = (v >> b) & 1u;
+                words[b * G + g] |= bit << j;
+            }
+        }
+    }
+}
+
+void oracle_unbitshuffle(const uint32_t *words, uint32_t V, uint32_t *z) {
+    uint32_t G = V / 32;
+    for (uint32_t g = 0; g < G; ++g) {
+        for (uint32_t j = 0; j < 32; ++j) {
+            uint32_t v = 0;
+            for (uint32_t b = 0; b < 32; ++b) {
+                uint32_t bit = (words[b * G + g] >> j) & 1u;
+                v |= bit << b;
+            }
+            z[32 * g + j] = v;
+        }
+    }
+}
+
+/* Chunk coder, "RZE" (the SegmentCodec of the chunk chain): zero words are dropped.  Output:
+ * a bitmap of W / 32 words (bit k, in word k / 32 at position k % 32, is set when word k is
+ * nonzero), then the nonzero words in order.  Returns the output length in words. */
+uint32_t oracle_rze(const uint32_t *words, uint32_t W, uint32_t *out) {
+    uint32_t nbm = W / 32;
+    for (uint32_t i = 0; i < nbm; ++i) out[i] = 0;
+    uint32_t k = nbm;
+    for (uint32_t i = 0; i < W; ++i) {
+        if (words[i] != 0) {
+            out[i / 32] |= 1u << (i % 32);
+            out[k] = words[i];
+            ++k;
+        }
+    }
+    return k;
+}
+
+/* Inverse of RZE for one chunk of W words from len input words.  Returns 0, or -1 when the
+ * input is inconsistent (length not bitmap + popcount, or a zero word under a set bit). */
+int oracle_unrze(const uint32_t *in, uint32_t len, uint32_t W, uint32_t *words) {
+    uint32_t nbm = W / 32;
+    if (len < nbm) return -1;
+    uint32_t k = nbm;
+    for (uint32_t i = 0; i < W; ++i) {
+        uint32_t bit = (in[i / 32] >> (i % 32)) & 1u;
+        if (bit) {
+            if (k >= len) return -1;
+            words[i] = in[k];
+            if (words[i] == 0) return -1;
+            ++k;
+        } else {
+            words[i] = 0;
+        }
+    }
+    if (k != len) return -1;
+    return 0;
+}
+
+/* Size of a chunk-coder stream from its chunk count, total chunk words and outlier count. */
+uint64_t oracle_chunk_stream_bytes(uint64_t nchunks, uint64_t sum_words, uint64_t m) {
+    uint64_t payload_off = kHeaderBytes + align16(4 * nchunks);
+    uint64_t oidx_off = payload_off + align16(4 * sum_words);
+    uint64_t oval_off = oidx_off + align16(4 * m);
+    return oval_off + align16(4 * m);
+}
+
+/* The 128-byte header: magic, version, layout of the sections (all offsets from the start). */
+static void write_header(uint8_t *out, uint8_t mode, int rank, const uint64_t *dims, uint64_t n,
+                         uint8_t log2_seg, int T, uint32_t B, float eb_f, float s, float r,
+                         uint64_t m, uint64_t payload_bytes, uint64_t payload_off, uint64_t oidx_off,
+                         uint64_t oval_off, uint64_t total) {
+    put_u32(out, 0, kMagic);
+    put_u16(out, 4, kVersion);
+    put_u16(out, 6, kHeaderBytes);
+    put_u8(out, 8, mode);
+    put_u8(out, 9, (uint8_t)rank);
+    put_u8(out, 10, log2_seg);
+    put_u8(out, 11, (uint8_t)T);
+    put_u32(out, 12, B);
+    for (int a = 0; a < 4; ++a) put_u64(out, 16 + 8 * a, a < rank ? dims[a] : 0);
+    put_u64(out, 48, n);
+    put_f32(out, 56, eb_f);
+    put_f32(out, 60, s);
+    put_f32(out, 64, r);
+    put_u32(out, 68, 0);
+    put_u64(out, 72, m);
+    put_u64(out, 80, payload_bytes);
+    put_u64(out, 88, kHeaderBytes);
+    put_u64(out, 96, payload_off);
+    put_u64(out, 104, oidx_off);
+    put_u64(out, 112, oval_off);
+    put_u64(out, 120, total);
+}
+
 /* Steps 1-8: the whole compressor, in order.  The outlier list holds (u32 index, raw fp32
  * bits) pairs in ascending index order (the "nvrtc_chunk_fusion.h File Reference" names the
  * side list as u32 indices plus float values; the order is fixed here by index).  The stream
@@ -298,6 +406,79 @@ uint64_t oracle_compress(const float *x, int rank, const uint64_t *dims, int rel
     return total;
 }
 
+/* The chunk-cooperative coder, whole compressor ("Pipeline Specialization Internals",
+ * Chunk-cooperative path: Quant -> Diff -> Bitshuffle -> RZE over chunks of 4096, 8192 or
+ * 16384 input bytes, i.e. V = 1024, 2048 or 4096 float32 values).  Quant is the same verified
+ * linear quantizer with the same outlier escape; Diff is the first difference inside the chunk
+ * (0 predicts the chunk's first code), folded by the zigzag map so small magnitudes have empty
+ * high bits; Bitshuffle and RZE as above.  The last chunk is padded with zero codes to V.
+ * Stream: header (mode 2, log2_seg = log2 V, B = V), one u32 word count per chunk where the
+ * widths of the bitpack coder go, the chunks' RZE outputs back to back, then the outliers.
+ * RAW fallbacks as for the bitpack coder. */
+uint64_t oracle_compress_chunked(const float *x, int rank, const uint64_t *dims, int rel, double eps,
+                                 uint32_t V, int T, uint64_t side_max,
+                                 uint8_t *out, uint64_t cap, uint64_t *required) {
+    uint64_t n = 1;
+    for (int a = 0; a < rank; ++a) n *= dims[a];
+    uint64_t nchunks = (n + V - 1) / V;
+    uint8_t log2v = 0;
+    while ((1u << log2v) < V) ++log2v;
+
+    float eb_f = 0.0f, s = 0.0f, r = 0.0f;
+    int valid = oracle_resolve_bound(x, n, rel, eps, &eb_f, &s, &r);
+
+    std::vector<int32_t> q, d;
+    std::vector<uint8_t> esc, widths;
+    std::vector<uint32_t> z, payload, sizes;
+    std::vector<uint32_t> oidx, oval;
+    bool raw = !valid;
+    if (!raw) {
+        q.resize(n); d.resize(n); esc.resize(n); z.resize(n); widths.resize((n + 31) / 32);
+        /* Quant and Diff: the Lorenzo deltas with a reset every V values, zigzag-folded */
+        oracle_codes(x, n, eb_f, s, r, T, V, q.data(), esc.data(), d.data(), z.data(), widths.data());
+        std::vector<uint32_t> zc(V), words(V), cout(V + V / 32);
+        for (uint64_t c = 0; c < nchunks; ++c) {
+            for (uint32_t i = 0; i < V; ++i) {
+                uint64_t gi = c * V + i;
+                zc[i] = gi < n ? z[gi] : 0u;
+            }
+            oracle_bitshuffle(zc.data(), V, words.data());
+            uint32_t len = oracle_rze(words.data(), V, cout.data());
+            sizes.push_back(len);
+            for (uint32_t i = 0; i < len; ++i) payload.push_back(cout[i]);
+        }
+        for (uint64_t i = 0; i < n; ++i) {
+            if (esc[i]) { oidx.push_back((uint32_t)i); oval.push_back(f32_bits(x[i])); }
+        }
+        if (oidx.size() > side_max) raw = true;
+        else if (oracle_chunk_stream_bytes(nchunks, payload.size(), oidx.size()) > oracle_raw_bytes(n)) raw = true;
+    }
+
+    uint64_t total = raw ? oracle_raw_bytes(n) : oracle_chunk_stream_bytes(nchunks, payload.size(), oidx.size());
+    if (required) *required = total;
+    if (total > cap) return 0;
+    std::memset(out, 0, total);
+    if (raw) {
+        uint64_t end = oracle_raw_bytes(n);
+        write_header(out, kModeRaw, rank, dims, n, log2v, T, V, eb_f, s, r, 0, 4 * n, kHeaderBytes, end, end, end);
+        std::memcpy(out + kHeaderBytes, x, 4 * n);
+        return total;
+    }
+    uint64_t m = oidx.size();
+    uint64_t payload_off = kHeaderBytes + align16(4 * nchunks);
+    uint64_t oidx_off = payload_off + align16(4 * payload.size());
+    uint64_t oval_off = oidx_off + align16(4 * m);
+    write_header(out, kModeChunk, rank, dims, n, log2v, T, V, eb_f, s, r, m, 4 * payload.size(),
+                 payload_off, oidx_off, oval_off, total);
+    for (uint64_t c = 0; c < nchunks; ++c) put_u32(out, kHeaderBytes + 4 * c, sizes[c]);
+    for (uint64_t t = 0; t < payload.size(); ++t) put_u32(out, payload_off + 4 * t, payload[t]);
+    for (uint64_t k = 0; k < m; ++k) {
+        put_u32(out, oidx_off + 4 * k, oidx[k]);
+        put_u32(out, oval_off + 4 * k, oval[k]);
+    }
+    return total;
+}
+
 /* Header checks shared by oracle_decompress and oracle_stream_elements.  Returns n, or 0
  * when the header is not one this codec writes. */
 static uint64_t check_header(const uint8_t *in, uint64_t len) {
@@ -306,8 +487,12 @@ static uint64_t check_header(const uint8_t *in, uint64_t len) {
     if (get_u16(in, 4) != kVersion || get_u16(in, 6) != kHeaderBytes) return 0;
     uint8_t mode = get_u8(in, 8), rank = get_u8(in, 9), log2_seg = get_u8(in, 10), T = get_u8(in, 11);
     uint32_t B = get_u32(in, 12);
-    if (mode != kModeLossy && mode != kModeRaw) return 0;
-    if (rank < 1 || rank > 4 || log2_seg != 5 || T < 1 || T > 30) return 0;
+    if (mode != kModeLossy && mode != kModeRaw && mode != kModeChunk) return 0;
+    if (rank < 1 || rank > 4 || T < 1 || T > 30) return 0;
+    bool chunk_params = log2_seg >= 10 && log2_seg <= 12 && B == (1u << log2_seg);
+    if (mode == kModeChunk && !chunk_params) return 0;
+    if (mode == kModeLossy && log2_seg != 5) return 0;
+    if (mode == kModeRaw && log2_seg != 5 && !chunk_params) return 0;
     if (B < 32 || B % 32 != 0 || B > (1u << 20)) return 0;
     uint64_t n = 1;
     for (int a = 0; a < 4; ++a) {
@@ -330,9 +515,14 @@ static uint64_t check_header(const uint8_t *in, uint64_t len) {
     } else {
         float eb_f = get_f32(in, 56), s = get_f32(in, 60);
         if (!(std::isnormal(eb_f) && eb_f > 0.0f && std::isfinite(s) && s == 2.0f * eb_f)) return 0;
-        uint64_t nseg = (n + kSeg - 1) / kSeg;
-        if (m > n || pb % 4 != 0 || pb > 4ull * 32 * nseg) return 0;
-        if (po != kHeaderBytes + align16(nseg)) return 0;
+        if (m > n || pb % 4 != 0) return 0;
+        if (mode == kModeLossy) {
+            uint64_t nseg = (n + kSeg - 1) / kSeg;
+            if (pb > 4ull * 32 * nseg || po != kHeaderBytes + align16(nseg)) return 0;
+        } else {
+            uint64_t nchunks = (n + B - 1) / B;
+            if (pb > 4ull * nchunks * (B + B / 32) || po != kHeaderBytes + align16(4 * nchunks)) return 0;
+        }
         if (oi != po + align16(pb) || ov != oi + align16(4 * m) || tot != ov + align16(4 * m)) return 0;
     }
     if (tot > len) return 0;
@@ -340,6 +530,37 @@ static uint64_t check_header(const uint8_t *in, uint64_t len) {
 }
 
 uint64_t oracle_stream_elements(const uint8_t *in, uint64_t len) { return check_header(in, len); }
+
+/* The bitpack coder's inverse of steps 4-6: per segment read its width, unpack its 32 values
+ * and undo the zigzag into d.  Returns false when the widths are inconsistent. */
+static bool widths_to_deltas(const uint8_t *in, uint64_t n, uint64_t pb, uint64_t po, int32_t *d) {
+    uint64_t nseg = (n + kSeg - 1) / kSeg;
+
+    /* widths, and the payload size they imply */
+    std::vector<uint8_t> widths(nseg);
+    uint64_t sum_w = 0;
+    for (uint64_t k = 0; k < nseg; ++k) {
+        widths[k] = in[kHeaderBytes + k];
+        if (widths[k] > 32) return false;
+        sum_w += widths[k];
+    }
+    if (4 * sum_w != pb) return false;
+
+    /* unpack + unzigzag */
+    std::vector<uint32_t> words(sum_w);
+    for (uint64_t t = 0; t < sum_w; ++t) words[t] = get_u32(in, po + 4 * t);
+    uint64_t base = 0;
+    for (uint64_t k = 0; k < nseg; ++k) {
+        for (uint32_t j = 0; j < kSeg; ++j) {
+            uint64_t i = k * kSeg + j;
+            if (i >= n) break;
+            uint32_t zv = oracle_unpack_one(words.data() + base, widths[k], j);
+            d[i] = (int32_t)((zv >> 1) ^ (0u - (zv & 1u)));
+        }
+        base += widths[k];
+    }
+    return true;
+}
 
 /* Step 9: the inverse.  Per segment: read its width, unpack its 32 values, undo the zigzag
  * d = (z >> 1) ^ -(z & 1), then the code is the running sum of d from the block start
@@ -359,31 +580,32 @@ int oracle_decompress(const uint8_t *in, uint64_t len, float *out, uint64_t n_ou
     float s = get_f32(in, 60);
     uint64_t m = get_u64(in, 72), pb = get_u64(in, 80);
     uint64_t po = get_u64(in, 96), oi = get_u64(in, 104), ov = get_u64(in, 112);
-    uint64_t nseg = (n + kSeg - 1) / kSeg;
-
-    /* widths, and the payload size they imply */
-    std::vector<uint8_t> widths(nseg);
-    uint64_t sum_w = 0;
-    for (uint64_t k = 0; k < nseg; ++k) {
-        widths[k] = in[kHeaderBytes + k];
-        if (widths[k] > 32) return ORACLE_CORRUPT;
-        sum_w += widths[k];
-    }
-    if (4 * sum_w != pb) return ORACLE_CORRUPT;
-
-    /* unpack + unzigzag */
-    std::vector<uint32_t> words(sum_w);
-    for (uint64_t t = 0; t < sum_w; ++t) words[t] = get_u32(in, po + 4 * t);
     std::vector<int32_t> d(n);
-    uint64_t base = 0;
-    for (uint64_t k = 0; k < nseg; ++k) {
-        for (uint32_t j = 0; j < kSeg; ++j) {
-            uint64_t i = k * kSeg + j;
-            if (i >= n) break;
-            uint32_t zv = oracle_unpack_one(words.data() + base, widths[k], j);
-            d[i] = (int32_t)((zv >> 1) ^ (0u - (zv & 1u)));
+    if (mode == kModeChunk) {
+        /* chunk coder: per chunk, undo RZE and Bitshuffle, then the zigzag */
+        uint32_t V = B;
+        uint64_t nchunks = (n + V - 1) / V;
+        uint64_t sum = 0;
+        for (uint64_t c = 0; c < nchunks; ++c) sum += get_u32(in, kHeaderBytes + 4 * c);
+        if (4 * sum != pb) return ORACLE_CORRUPT;
+        std::vector<uint32_t> cin(V + V / 32), words(V), zc(V);
+        uint64_t base = 0;
+        for (uint64_t c = 0; c < nchunks; ++c) {
+            uint32_t len = get_u32(in, kHeaderBytes + 4 * c);
+            if (len < V / 32 || len > V + V / 32) return ORACLE_CORRUPT;
+            for (uint32_t t = 0; t < len; ++t) cin[t] = get_u32(in, po + 4 * (base + t));
+            if (oracle_unrze(cin.data(), len, V, words.data()) != 0) return ORACLE_CORRUPT;
+            oracle_unbitshuffle(words.data(), V, zc.data());
+            for (uint32_t i = 0; i < V; ++i) {
+                uint64_t gi = c * V + i;
+                if (gi >= n) break;
+                uint32_t zv = zc[i];
+                d[gi] = (int32_t)((zv >> 1) ^ (0u - (zv & 1u)));
+            }
+            base += len;
         }
-        base += widths[k];
+    } else {
+        if (!widths_to_deltas(in, n, pb, po, d.data())) return ORACLE_CORRUPT;
     }
     /* undelta: running sum from each block start, then dequantize */
     int32_t qprev = 0;

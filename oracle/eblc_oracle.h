@@ -21,7 +21,10 @@
  *   6. fixed-length bit packing of each segment,
  *   7. an outlier side list ordered by index,
  *   8. stream assembly (128-byte header + widths + payload + outlier indices + values),
- *   9. the exact inverse.
+ *   9. the exact inverse;
+ * and the second, chunk-cooperative coder of the same page ("Chunk-cooperative path (brief)"):
+ * the same quantizer, a first difference reset at every chunk, a bit-plane shuffle and zero-
+ * word elimination (RZE) per chunk.
  *
  * Floating point: fp32, IEEE round-to-nearest-even, no FMA contraction (built with
  * -ffp-contract=off), denormals preserved.  The bound is resolved in fp64.
@@ -78,7 +81,25 @@ uint64_t oracle_compress(const float *x, int rank, const uint64_t *dims, int rel
                          uint32_t B, int T, uint64_t side_max,
                          uint8_t *out, uint64_t cap, uint64_t *required);
 
-/* Whole decompressor.  Reads len bytes; writes n_out floats.  Returns ORACLE_OK,
+/* Chunk-cooperative coder steps (V codes per chunk, V a multiple of 32).  Bitshuffle: word
+ * b * (V/32) + g of `words` holds bit b of codes 32g .. 32g+31 (code j at bit j).  RZE: out =
+ * bitmap of the nonzero words (W/32 words), then those words in order; returns its length.
+ * oracle_unrze returns 0, or -1 for an inconsistent input. */
+void oracle_bitshuffle(const uint32_t *z, uint32_t V, uint32_t *words);
+void oracle_unbitshuffle(const uint32_t *words, uint32_t V, uint32_t *z);
+uint32_t oracle_rze(const uint32_t *words, uint32_t W, uint32_t *out);
+int oracle_unrze(const uint32_t *in, uint32_t len, uint32_t W, uint32_t *words);
+uint64_t oracle_chunk_stream_bytes(uint64_t nchunks, uint64_t sum_words, uint64_t m);
+
+/* Whole compressor with the chunk-cooperative coder: Quant -> Diff (first difference reset at
+ * every chunk, zigzag-folded) -> Bitshuffle -> RZE over chunks of V = 1024, 2048 or 4096
+ * values (4, 8 or 16 KiB of input).  Same bound, outlier and RAW rules as oracle_compress;
+ * stream mode 2.  Same return convention as oracle_compress. */
+uint64_t oracle_compress_chunked(const float *x, int rank, const uint64_t *dims, int rel, double eps,
+                                 uint32_t V, int T, uint64_t side_max,
+                                 uint8_t *out, uint64_t cap, uint64_t *required);
+
+/* Whole decompressor (either coder).  Reads len bytes; writes n_out floats.  Returns ORACLE_OK,
  * ORACLE_CORRUPT (header or sections inconsistent) or ORACLE_CAPACITY (n_out too small). */
 int oracle_decompress(const uint8_t *in, uint64_t len, float *out, uint64_t n_out);
 
