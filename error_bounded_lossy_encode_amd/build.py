@@ -9,7 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "libeblc.so")
-SOURCES = ["eblc_api.hip", "eblc_kernels.hip"]
+SOURCES = ["eblc_api.hip", "eblc_kernels.hip", "eblc_chunk.hip"]
 
 # -ffp-contract=off: the fp32 arithmetic must be the plain IEEE sequence (no FMA), both for the
 # quantizer's decisions and the reconstruction; denormals are kept (no flush to zero).

@@ -93,6 +93,8 @@ struct Options {
     uint32_t T = 30;
     bool side_set = false;
     uint64_t side_max = 0;
+    bool chunk_coder = false;   /* coder=chunk: Quant -> Diff -> Bitshuffle -> RZE */
+    uint32_t V = 0;             /* chunk coder: values per chunk */
 };
 
 /* Options string ("Provider layout": a provider-defined string; DevitoPRO passes the relative
@@ -108,7 +110,8 @@ eblc_status parse_options(const char *opts, Options *o) {
         o->eps = v;
         return EBLC_OK;
     }
-    bool seen_eb = false, seen_block = false, seen_t = false;
+    bool seen_eb = false, seen_block = false, seen_t = false, seen_coder = false, seen_chunk = false;
+    uint64_t chunk_bytes = 8192;
     size_t pos = 0;
     for (;;) {
         size_t end = all.find(';', pos);
@@ -136,6 +139,15 @@ eblc_status parse_options(const char *opts, Options *o) {
                 if (seen_t || !parse_u64(val, &t) || t < 1 || t > 30) return EBLC_INVALID_ARGUMENT;
                 seen_t = true;
                 o->T = (uint32_t)t;
+            } else if (key == "coder") {
+                if (seen_coder || (val != "bitpack" && val != "chunk")) return EBLC_INVALID_ARGUMENT;
+                seen_coder = true;
+                o->chunk_coder = val == "chunk";
+            } else if (key == "chunk_bytes") {
+                if (seen_chunk || !parse_u64(val, &chunk_bytes) ||
+                    (chunk_bytes != 4096 && chunk_bytes != 8192 && chunk_bytes != 16384))
+                    return EBLC_INVALID_ARGUMENT;
+                seen_chunk = true;
             } else if (key == "side_max") {
                 uint64_t m;
                 if (o->side_set || !parse_u64(val, &m)) return EBLC_INVALID_ARGUMENT;
@@ -146,6 +158,14 @@ eblc_status parse_options(const char *opts, Options *o) {
             }
         }
         if (final_item) break;
+    }
+    /* the chunk is the chunk coder's reset period: no block with it, no chunk without it */
+    if (o->chunk_coder) {
+        if (seen_block) return EBLC_INVALID_ARGUMENT;
+        o->V = (uint32_t)(chunk_bytes / 4);
+        o->B = o->V;
+    } else if (seen_chunk) {
+        return EBLC_INVALID_ARGUMENT;
     }
     return EBLC_OK;
 }
@@ -211,14 +231,18 @@ hipError_t enqueue_compress(eblc_plan *plan, const float *in, void *out, size_t 
     const PlanArgs pa = call_args(plan, in);
     const Workspace &ws = plan->ws;
     uint8_t *o = static_cast<uint8_t *>(out);
-    const uint64_t widths_bytes = align_up(pa.nseg, 16);
+    const uint64_t widths_bytes = pa.wsec;
     const bool widths_direct = out_capacity >= kHeaderBytes + widths_bytes;
     uint8_t *widths_dst = widths_direct ? o + kHeaderBytes : ws.widths;
     uint64_t *res = reinterpret_cast<uint64_t *>(result);
     plan->nlaunch = 0;
     hipError_t e = hipSuccess;
     if (plan->rel) e = timed(plan, st, "range", [&] { return launch_range(in, pa, ws, plan->eps, st); });
-    if (e == hipSuccess) e = timed(plan, st, "encode", [&] { return launch_encode(in, pa, ws, widths_dst, widths_bytes, st); });
+    if (e == hipSuccess)
+        e = timed(plan, st, "encode", [&] {
+            return pa.V ? launch_chunk_encode(in, pa, ws, widths_dst, widths_bytes, st)
+                        : launch_encode(in, pa, ws, widths_dst, widths_bytes, st);
+        });
     if (e == hipSuccess) e = timed(plan, st, "scan", [&] { return launch_scan_compress(pa, ws, o, out_capacity, res, st); });
     if (e == hipSuccess) e = timed(plan, st, "compact", [&] { return launch_compact(in, pa, ws, o, widths_direct ? nullptr : ws.widths, st); });
     return e;
@@ -340,7 +364,21 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     pa.T = o.T;
     pa.nchunks = (uint32_t)((n + kEncChunk - 1) / kEncChunk);
     pa.ngroups = (pa.nchunks + kEncChunksPerGroup - 1) / kEncChunksPerGroup;
-    pa.dchunks = (uint32_t)((n + kDecChunk - 1) / kDecChunk);
+    if (o.chunk_coder) {
+        pa.V = o.V;
+        pa.log2seg = (uint32_t)__builtin_ctz(o.V);
+        pa.slot = kEncChunk + kEncChunk / 32;
+        pa.wpg = 4u * (kEncChunksPerGroup * kEncChunk / o.V);
+        pa.dchunks = (uint32_t)((n + o.V - 1) / o.V);
+        pa.wsec = align_up(4ull * pa.dchunks, 16);
+    } else {
+        pa.V = 0;
+        pa.log2seg = 5;
+        pa.slot = kEncChunk;
+        pa.wpg = kEncChunksPerGroup * kEncSegs;
+        pa.dchunks = (uint32_t)((n + kDecChunk - 1) / kDecChunk);
+        pa.wsec = align_up(pa.nseg, 16);
+    }
     pa.dgroups = (pa.dchunks + kDecChunksPerGroup - 1) / kDecChunksPerGroup;
     pa.side_max = o.side_max;
     pa.lay = lay;
@@ -355,7 +393,8 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
         return at;
     };
     const uint64_t o_info = carve(sizeof(DevInfo));
-    const uint64_t o_scratch = carve(nc * kEncChunk * 4);
+    /* one spare slot: a 4096-value chunk of the chunk coder spills into its second wave's slot */
+    const uint64_t o_scratch = carve(((uint64_t)pa.nchunks + 1) * pa.slot * 4);
     const uint64_t o_cw = carve(nc * 4), o_ce = carve(nc * 4), o_ct = carve(nc * 4);
     const uint64_t o_gw = carve(ng * 4), o_ge = carve(ng * 4);
     const uint64_t o_pw = carve(ng * 4), o_pe = carve(ng * 4);
@@ -472,7 +511,7 @@ eblc_status eblc_decompress(eblc_plan_t *plan, const void *in, size_t compressed
     if (plan == nullptr || in == nullptr || out == nullptr) return EBLC_INVALID_ARGUMENT;
     if (sidecar != nullptr || !aligned16(in) || !field_ptr_ok(plan, out)) return EBLC_INVALID_ARGUMENT;
     const PlanArgs pa = call_args(plan, out);
-    if (compressed_bytes < kHeaderBytes + align_up(pa.nseg, 16) ||
+    if (compressed_bytes < kHeaderBytes + pa.wsec ||
         compressed_bytes > kHeaderBytes + align_up(4 * pa.n, 16))
         return EBLC_CORRUPT_STREAM;
     DeviceGuard guard(plan->device);
@@ -483,7 +522,10 @@ eblc_status eblc_decompress(eblc_plan_t *plan, const void *in, size_t compressed
     plan->nlaunch = 0;
     hipError_t e = timed(plan, st, "decode_sizes", [&] { return launch_decode_sizes(i, pa, ws, st); });
     if (e == hipSuccess) e = timed(plan, st, "decode_scan", [&] { return launch_scan_decompress(i, compressed_bytes, pa, ws, st); });
-    if (e == hipSuccess) e = timed(plan, st, "decode", [&] { return launch_decode(i, pa, ws, out, st); });
+    if (e == hipSuccess)
+        e = timed(plan, st, "decode", [&] {
+            return pa.V ? launch_chunk_decode(i, pa, ws, out, st) : launch_decode(i, pa, ws, out, st);
+        });
     if (e == hipSuccess) e = timed(plan, st, "patch", [&] { return launch_patch(i, pa, ws, out, st); });
     return hip_status(e);
 }

@@ -1,0 +1,424 @@
+/*
+ * eblc_chunk.hip -- gfx950 kernels of the chunk-cooperative coder: Quant -> Diff ->
+ * Bitshuffle -> RZE over chunks of 4096, 8192 or 16384 input bytes ("Pipeline Specialization
+ * Internals", FZGPUModules site, Chunk-cooperative path).  A chunk of V float32 values is coded
+ * on its own: the verified linear quantizer (same rule and escapes as the bitpack coder), the
+ * first difference inside the chunk (0 predicts its first code) folded by zigzag, the chunk's
+ * 32 bit planes (plane-major: word b * G + g holds bit b of the 32 codes of group g, G = V /
+ * 32, code j of a group at bit j), and zero-word elimination (a bitmap of the V words, then the
+ * nonzero words in order).  The scan, compaction and outlier kernels of the bitpack coder
+ * serve this coder unchanged; only the scratch slot stride and the size section differ.
+ *
+ * gfx950 mapping.  A tile is 64 consecutive values, one per lane.  Bitshuffle is a 32 x 32 bit
+ * transpose inside each half-wave (five butterfly stages: ds_swizzle or DPP for the partner
+ * lane, v_alignbit for the rotate, v_bfi for the merge), after which lane 32 h + b holds the
+ * plane-b word of the tile's group h: one LDS store per lane per tile puts it at its plane-major
+ * place.  LDS planes are padded by two words so those stores and the plane reads of RZE are
+ * free of bank conflicts.  RZE walks only the planes below the chunk's highest code bit: a
+ * ballot per 64 words gives two bitmap words, and mbcnt the compacted position.  Decoding runs
+ * the same steps backwards; the transpose is its own inverse.
+ */
+#include "eblc_device.h"
+
+namespace eblc {
+namespace {
+
+constexpr int kCTile = 64;                     /* values per tile: one per lane */
+constexpr int kCTilesPerWave = kEncChunk / kCTile;
+constexpr int kDppRowMirror = 0x140;
+
+template <int V>
+struct ChunkGeom {
+    static constexpr int G = V / 32;            /* groups of 32 codes = words per bit plane */
+    static constexpr int PS = G + 2;            /* LDS words per plane (2 words of padding) */
+    static constexpr int LDSW = 32 * PS;        /* LDS words of one chunk's planes */
+    static constexpr int BM = V / 32;           /* bitmap words of RZE */
+    static constexpr int BATCHES = (G + 63) / 64; /* 64-word batches per plane */
+    static constexpr int WAVES = V > kEncChunk ? V / kEncChunk : 1;      /* encode waves per chunk */
+    static constexpr int PER_WAVE = V < kEncChunk ? kEncChunk / V : 1;   /* chunks per encode wave */
+    static constexpr int TILES = V / kCTile;
+    static_assert(V == 1024 || V == 2048 || V == 4096, "chunk of 4, 8 or 16 KiB");
+    static_assert(PER_WAVE * (BM + V) <= WAVES * (kEncChunk + kEncChunk / 32), "scratch slots of 2112 words");
+};
+
+__device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+/* old with lane `at` (wave-uniform) replaced by the wave-uniform value v. */
+__device__ __forceinline__ uint32_t writelane(uint32_t old, uint32_t v, uint32_t at) {
+    return (threadIdx.x & 63u) == at ? v : old;
+}
+
+/* OR over all 64 lanes (DPP inside rows, then the four rows' lanes 0, 16, 32 and 48). */
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+    v |= dpp<kDppQuadXor1>(0, v);
+    v |= dpp<kDppQuadXor2>(0, v);
+    v |= dpp<kDppRowHalfMirror>(0, v);
+    v |= dpp<kDppRowMirror>(0, v);
+    return readlane(v, 0) | readlane(v, 16) | readlane(v, 32) | readlane(v, 48);
+}
+
+/* Per-lane constants of the five transpose stages s = 16, 8, 4, 2, 1: the lane keeps the bits
+ * of its own word under keep[k] and takes the rest from its partner (lane ^ s) rotated right by
+ * rot[k] -- a left rotate by s in the lower lane of the pair, a right rotate in the upper. */
+struct Transpose {
+    uint32_t keep[5], rot[5];
+    __device__ __forceinline__ explicit Transpose(uint32_t lane) {
+        const uint32_t m[5] = {0x0000FFFFu, 0x00FF00FFu, 0x0F0F0F0Fu, 0x33333333u, 0x55555555u};
+#pragma unroll
+        for (int k = 0; k < 5; ++k) {
+            const uint32_t s = 16u >> k;
+            const bool lower = (lane & s) == 0;
+            keep[k] = lower ? m[k] : ~m[k];
+            rot[k] = lower ? 32u - s : s;
+        }
+    }
+    /* 32 x 32 bit transpose inside each half-wave: on exit bit j of lane 32 h + b is bit b of
+     * lane 32 h + j's word on entry. */
+    __device__ __forceinline__ uint32_t operator()(uint32_t v) const {
+        uint32_t p;
+        p = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F); /* lane ^ 16 */
+        v = (v & keep[0]) | (__builtin_amdgcn_alignbit(p, p, rot[0]) & ~keep[0]);
+        p = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x201F); /* lane ^ 8 */
+        v = (v & keep[1]) | (__builtin_amdgcn_alignbit(p, p, rot[1]) & ~keep[1]);
+        p = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F); /* lane ^ 4 */
+        v = (v & keep[2]) | (__builtin_amdgcn_alignbit(p, p, rot[2]) & ~keep[2]);
+        p = dpp<kDppQuadXor2>(0, v);                                /* lane ^ 2 */
+        v = (v & keep[3]) | (__builtin_amdgcn_alignbit(p, p, rot[3]) & ~keep[3]);
+        p = dpp<kDppQuadXor1>(0, v);                                /* lane ^ 1 */
+        v = (v & keep[4]) | (__builtin_amdgcn_alignbit(p, p, rot[4]) & ~keep[4]);
+        return v;
+    }
+};
+
+__device__ __forceinline__ float ld_nt_f(const float *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_nt_f(float *p, float v) { __builtin_nontemporal_store(v, p); }
+
+/* ---- K2c: chunk encode ------------------------------------------------------------------------ */
+
+/* Workgroup of 4 waves over 8192 values; wave w owns the 2048 values of encode chunk c (the
+ * unit of the escape bookkeeping and of the scratch slots the compaction copies), which hold
+ * 2048 / V coder chunks, or half of one when V = 4096.  Phase 1 (every wave): load 32 values
+ * per lane, quantize, difference, zigzag and transpose each tile into the chunk's LDS planes,
+ * recording escapes as the bitpack encoder does.  Phase 2 (after a barrier; the wave owning a
+ * chunk's first values): RZE of the chunk's planes into the scratch slot -- bitmap, then the
+ * nonzero words -- and its word count into the size section (stream or staging).  A wave's
+ * chunks lie back to back in its slot, and a 4096-value chunk fills the slots of both its waves
+ * (the second reports 0 words), so the compaction's copy of each slot in order yields the chunks
+ * in order. */
+template <int V, bool STRIDED>
+__global__ __launch_bounds__(kEncThreads) void chunk_encode_kernel(const float *__restrict__ x, PlanArgs pa,
+                                                                   Workspace ws, uint8_t *__restrict__ sizes_dst,
+                                                                   uint64_t sizes_bytes) {
+    using Gm = ChunkGeom<V>;
+    constexpr int kBufs = kEncWaves * kEncChunk / V;
+    __shared__ uint32_t s_words[kBufs][Gm::LDSW];
+    __shared__ uint32_t s_stage[kEncWaves][2][kEscStage];
+    __shared__ uint32_t s_or[kEncWaves][Gm::PER_WAVE];
+    __shared__ uint32_t s_grp[2][kEncWaves];
+
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t c = blockIdx.x * kEncWaves + wave;
+    const DevInfo *info = ws.info;
+    const uint64_t n = pa.n;
+    const uint64_t cbase = (uint64_t)c * kEncChunk;
+    uint32_t escs = 0, tmask = 0, wsum = 0;
+
+    if (info->valid) {  /* the same for every workgroup: the barrier below is uniform */
+        QParams qp;
+        qp.eb = info->eb_f;
+        qp.s = info->s;
+        qp.r = info->r;
+        qp.T = pa.T;
+        qp.tlim = (float)(1u << pa.T);
+        const Transpose tr(lane);
+        const bool full = cbase + kEncChunk <= n;
+        float xs[kCTilesPerWave];
+        if (full) {
+#pragma unroll
+            for (int t = 0; t < kCTilesPerWave; ++t)
+                xs[t] = ld_nt_f(x + elem_off<STRIDED>(pa.lay, cbase + (uint64_t)t * kCTile + lane));
+        } else {
+#pragma unroll
+            for (int t = 0; t < kCTilesPerWave; ++t) {
+                const uint64_t i = cbase + (uint64_t)t * kCTile + lane;
+                xs[t] = i < n ? x[elem_off<STRIDED>(pa.lay, i)] : 0.0f;
+            }
+        }
+        /* the predecessor of the wave's first value when it does not start a chunk (second half
+         * of a 4096-value chunk): the code of the value before it, 0 if that value escapes */
+        int32_t carry = 0;
+        if ((cbase & (uint64_t)(V - 1)) != 0 && cbase < n) {
+            const float xp = x[elem_off<STRIDED>(pa.lay, cbase - 1)];
+            uint32_t e;
+            const int32_t qprev = quantize_slow(xp, rintf(xp * qp.r), qp, &e);
+            carry = e ? 0 : qprev;
+        }
+        uint32_t emask = 0;           /* lane l: escape bitmask of 32-value segment l */
+        uint32_t orz[Gm::PER_WAVE];
+#pragma unroll
+        for (int k = 0; k < Gm::PER_WAVE; ++k) orz[k] = 0;
+        const uint32_t h = lane >> 5, b = lane & 31;
+#pragma unroll
+        for (int t = 0; t < kCTilesPerWave; ++t) {
+            const float xv = xs[t];
+            /* Quant: the fast test of the bitpack encoder (exactly the full rule's acceptance),
+             * the full rule in a wave where some lane misses it */
+            const float q0f = rintf(xv * qp.r);
+            const bool fast = (fabsf(xv - q0f * qp.s) <= qp.eb) && (fabsf(q0f) < qp.tlim);
+            int32_t q = (int32_t)q0f;
+            if (__ballot(!fast)) {
+                uint32_t e = 0;
+                if (!fast) q = quantize_slow(xv, q0f, qp, &e);
+                const uint64_t M = __ballot(e != 0);
+                if (M) {
+                    emask = writelane(emask, (uint32_t)M, 2u * t);
+                    emask = writelane(emask, (uint32_t)(M >> 32), 2u * t + 1u);
+                    tmask |= 1u << (t / 4);
+                    const uint32_t r = escs + mbcnt64(M);
+                    if (e && r < (uint32_t)kEscStage) {
+                        s_stage[wave][0][r] = (uint32_t)(cbase + (uint64_t)t * kCTile + lane);
+                        s_stage[wave][1][r] = __float_as_uint(xv);
+                    }
+                    escs += (uint32_t)__popcll(M);
+                }
+            }
+            /* Diff: first difference, reset at the chunk's first value */
+            const uint32_t off = wave * kEncChunk + (uint32_t)t * kCTile; /* value offset in the group */
+            const bool reset = lane == 0 && (off & (uint32_t)(V - 1)) == 0;
+            const int32_t prev = (int32_t)dpp<kDppWaveShr1>((uint32_t)carry, (uint32_t)q);
+            uint32_t z = zigzag(reset ? q : q - prev);
+            carry = (int32_t)readlane((uint32_t)q, 63);
+            if (!full && cbase + (uint64_t)t * kCTile + lane >= n) z = 0; /* padding codes */
+            orz[(t * kCTile) / V] |= z;
+            /* Bitshuffle: lane 32 h + b -> plane b of group (off mod V) / 32 + h */
+            const uint32_t wd = tr(z);
+            const uint32_t buf = off / V;
+            const uint32_t g = (off & (uint32_t)(V - 1)) / 32u + h;
+            s_words[buf][b * Gm::PS + g] = wd;
+        }
+#pragma unroll
+        for (int k = 0; k < Gm::PER_WAVE; ++k) {
+            const uint32_t o = wave_or(orz[k]);
+            if (lane == 0) s_or[wave][k] = o;
+        }
+        __syncthreads();
+
+        /* RZE by the wave holding each chunk's first values */
+        const uint64_t ncv = (n + V - 1) / V;
+        if (Gm::WAVES == 1 || (wave & 1u) == 0) {
+            uint32_t *slot = ws.scratch + (uint64_t)c * pa.slot;
+#pragma unroll
+            for (int k = 0; k < Gm::PER_WAVE; ++k) {
+                const uint64_t cv = (cbase + (uint64_t)k * V) / V;
+                if (cv < ncv) {
+                    uint32_t orc = s_or[wave][k];
+                    if (Gm::WAVES == 2) orc |= s_or[wave + 1][0];
+                    const uint32_t wmax = orc ? 32u - (uint32_t)__builtin_clz(orc) : 0u;
+                    const uint32_t buf = (wave * kEncChunk + (uint32_t)k * V) / V;
+                    const uint32_t *pl = s_words[buf];
+                    uint32_t *dst = slot + wsum;
+                    uint32_t bm0 = 0, bm1 = 0;  /* lane l: bitmap word l (and 64 + l) */
+                    uint32_t run = 0;
+                    for (uint32_t pb = 0; pb < wmax; ++pb) {
+#pragma unroll
+                        for (int kk = 0; kk < Gm::BATCHES; ++kk) {
+                            const uint32_t gi = 64u * kk + lane;
+                            const uint32_t word = (Gm::G >= 64 || gi < (uint32_t)Gm::G) ? pl[pb * Gm::PS + gi] : 0u;
+                            const uint64_t M = __ballot(word != 0);
+                            if (word) dst[Gm::BM + run + mbcnt64(M)] = word;
+                            run += (uint32_t)__popcll(M);
+                            const uint32_t wi = (pb * Gm::G + 64u * kk) / 32u;
+                            if (wi < 64) bm0 = writelane(bm0, (uint32_t)M, wi);
+                            else bm1 = writelane(bm1, (uint32_t)M, wi - 64);
+                            if (Gm::G >= 64) {
+                                if (wi + 1 < 64) bm0 = writelane(bm0, (uint32_t)(M >> 32), wi + 1);
+                                else bm1 = writelane(bm1, (uint32_t)(M >> 32), wi + 1 - 64);
+                            }
+                        }
+                    }
+                    if (lane < (uint32_t)(Gm::BM < 64 ? Gm::BM : 64)) dst[lane] = bm0;
+                    if (Gm::BM > 64) dst[64 + lane] = bm1;
+                    const uint32_t size = Gm::BM + run;
+                    wsum += size;
+                    uint32_t *sz = reinterpret_cast<uint32_t *>(sizes_dst);
+                    if (lane == 0 && 4 * cv < sizes_bytes) sz[cv] = size;
+                    if (cv == ncv - 1) {
+                        /* zero the size section's pad up to its 16-byte end */
+                        const uint64_t pz = cv + 1 + lane;
+                        if (pz < align16(4 * ncv) / 4 && 4 * pz < sizes_bytes) sz[pz] = 0u;
+                    }
+                }
+            }
+        }
+        if (c < pa.nchunks) {
+            if (lane < escs && lane < (uint32_t)kEscStage) {
+                ws.stage_idx[(uint64_t)c * kEscStage + lane] = s_stage[wave][0][lane];
+                ws.stage_val[(uint64_t)c * kEscStage + lane] = s_stage[wave][1][lane];
+            }
+            if (tmask) ws.emask[(uint64_t)c * kEncSegs + lane] = emask;
+            if (lane == 0) {
+                ws.chunk_words[c] = wsum;
+                ws.chunk_esc[c] = escs;
+                ws.chunk_tmask[c] = tmask;
+            }
+        }
+    }
+    if (c >= pa.nchunks) {
+        wsum = 0;
+        escs = 0;
+    }
+    if (lane == 0) {
+        s_grp[0][wave] = wsum;
+        s_grp[1][wave] = escs;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t sw = 0, se = 0;
+#pragma unroll
+        for (int k = 0; k < kEncWaves; ++k) {
+            sw += s_grp[0][k];
+            se += s_grp[1][k];
+        }
+        ws.group_words[blockIdx.x] = sw;
+        ws.group_esc[blockIdx.x] = se;
+    }
+}
+
+/* ---- K7c: chunk decode ------------------------------------------------------------------------ */
+
+/* One wave per chunk.  The chunk's bitmap sits in two VGPRs (lane l: bitmap words l and
+ * 64 + l); its popcount must equal the chunk's word count minus the bitmap, else the stream is
+ * flagged.  Un-RZE rebuilds the planes below the highest nonzero one in LDS (per 64-word batch:
+ * the batch's bitmap bits, mbcnt for each present word's position); then per tile lane 32 h + b
+ * reads plane b of group 2 t + h, the transpose turns that into one code per lane, and the
+ * zigzag inverse, a wave prefix sum plus the previous tile's last code (the first difference
+ * undone from the chunk start) and f32(f32(q) * s) give the value. */
+template <int V, bool STRIDED>
+__global__ __launch_bounds__(kBlockThreads) void chunk_decode_kernel(const uint8_t *__restrict__ in, PlanArgs pa,
+                                                                     Workspace ws, float *__restrict__ out) {
+    using Gm = ChunkGeom<V>;
+    __shared__ uint32_t s_words[kWavesPerBlock][Gm::LDSW];
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t c = blockIdx.x * kWavesPerBlock + wave;
+    if (c >= pa.dchunks) return;
+    DevInfo *info = ws.info;
+    if (info->err) return;
+    const uint64_t n = pa.n;
+    const uint64_t cbase = (uint64_t)c * V;
+    const uint64_t cnt = (n - cbase < (uint64_t)V) ? n - cbase : (uint64_t)V;
+    if (info->mode == 1) {
+        const uint32_t *srcw = reinterpret_cast<const uint32_t *>(in + kHeaderBytes) + cbase;
+        uint32_t *ob = reinterpret_cast<uint32_t *>(out);
+        if (!STRIDED && cnt == (uint64_t)V) {
+            const uint4 *s4 = reinterpret_cast<const uint4 *>(srcw);
+            uint4 *d4 = reinterpret_cast<uint4 *>(ob + cbase);
+            uint4 t[V / 4 / kWave];
+#pragma unroll
+            for (int i = 0; i < V / 4 / kWave; ++i) t[i] = ld_nt(s4 + lane + kWave * i);
+#pragma unroll
+            for (int i = 0; i < V / 4 / kWave; ++i) st_nt(d4 + lane + kWave * i, t[i]);
+        } else {
+            for (uint32_t i = lane; i < cnt; i += kWave) ob[elem_off<STRIDED>(pa.lay, cbase + i)] = srcw[i];
+        }
+        return;
+    }
+    const uint32_t W = chunk_offset<kDecChunksPerGroup>(ws.gpre_words, ws.chunk_words, c);
+    const uint32_t P = ws.chunk_words[c];
+    const uint32_t *blob = reinterpret_cast<const uint32_t *>(in + info->payload_off) + W;
+    const uint32_t bm0 = lane < (uint32_t)(Gm::BM < 64 ? Gm::BM : 64) ? blob[lane] : 0u;
+    const uint32_t bm1 = Gm::BM > 64 ? blob[64 + lane] : 0u;
+    const uint32_t pc = wave_incl_scan((uint32_t)__popc(bm0) + (uint32_t)__popc(bm1));
+    if (readlane(pc, 63) + Gm::BM != P) {
+        if (lane == 0) atomicOr(&info->sticky, 1u);
+        return;
+    }
+    const uint64_t nz0 = __ballot(bm0 != 0), nz1 = __ballot(bm1 != 0);
+    int top = -1;
+    if (nz1) top = 64 + 63 - __clzll((long long)nz1);
+    else if (nz0) top = 63 - __clzll((long long)nz0);
+    const uint32_t wmax = top < 0 ? 0u : (uint32_t)top * 32u / Gm::G + 1u;
+    uint32_t *pl = s_words[wave];
+    uint32_t run = 0;
+    for (uint32_t pb = 0; pb < wmax; ++pb) {
+#pragma unroll
+        for (int kk = 0; kk < Gm::BATCHES; ++kk) {
+            const uint32_t wi = (pb * Gm::G + 64u * kk) / 32u;
+            const uint32_t lo = wi < 64 ? readlane(bm0, (int)wi) : readlane(bm1, (int)(wi - 64));
+            uint32_t hi = 0;
+            if (Gm::G >= 64) hi = wi + 1 < 64 ? readlane(bm0, (int)(wi + 1)) : readlane(bm1, (int)(wi + 1 - 64));
+            const uint64_t M = (uint64_t)lo | ((uint64_t)hi << 32);
+            const bool present = (M >> lane) & 1u;
+            const uint32_t word = present ? blob[Gm::BM + run + mbcnt64(M)] : 0u;
+            const uint32_t gi = 64u * kk + lane;
+            if (Gm::G >= 64 || gi < (uint32_t)Gm::G) pl[pb * Gm::PS + gi] = word;
+            run += (uint32_t)__popcll(M);
+        }
+    }
+    wave_lds_sync();
+    const Transpose tr(lane);
+    const float s = info->dec_s;
+    const uint32_t h = lane >> 5, b = lane & 31;
+    const uint32_t ntiles = (uint32_t)((cnt + kCTile - 1) / kCTile);
+    uint32_t carry = 0;
+    for (uint32_t t = 0; t < ntiles; ++t) {
+        const uint32_t word = b < wmax ? pl[b * Gm::PS + 2u * t + h] : 0u;
+        const uint32_t z = tr(word);
+        const uint32_t q = wave_incl_scan((uint32_t)unzigzag(z)) + carry;
+        carry = readlane(q, 63);
+        const float y = (float)(int32_t)q * s;
+        const uint64_t i = cbase + (uint64_t)t * kCTile + lane;
+        if (i < n) st_nt_f(out + elem_off<STRIDED>(pa.lay, i), y);
+    }
+}
+
+template <int V>
+hipError_t chunk_encode_v(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *sizes_dst,
+                          uint64_t sizes_bytes, hipStream_t stream) {
+    if (pa.lay.strided)
+        hipLaunchKernelGGL((chunk_encode_kernel<V, true>), dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa,
+                           ws, sizes_dst, sizes_bytes);
+    else
+        hipLaunchKernelGGL((chunk_encode_kernel<V, false>), dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa,
+                           ws, sizes_dst, sizes_bytes);
+    return hipGetLastError();
+}
+
+template <int V>
+hipError_t chunk_decode_v(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
+                          hipStream_t stream) {
+    if (pa.lay.strided)
+        hipLaunchKernelGGL((chunk_decode_kernel<V, true>), dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in,
+                           pa, ws, out);
+    else
+        hipLaunchKernelGGL((chunk_decode_kernel<V, false>), dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in,
+                           pa, ws, out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_encode(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *sizes_dst,
+                               uint64_t sizes_bytes, hipStream_t stream) {
+    switch (pa.V) {
+        case 1024: return chunk_encode_v<1024>(x, pa, ws, sizes_dst, sizes_bytes, stream);
+        case 2048: return chunk_encode_v<2048>(x, pa, ws, sizes_dst, sizes_bytes, stream);
+        case 4096: return chunk_encode_v<4096>(x, pa, ws, sizes_dst, sizes_bytes, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_decode(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
+                               hipStream_t stream) {
+    switch (pa.V) {
+        case 1024: return chunk_decode_v<1024>(in, pa, ws, out, stream);
+        case 2048: return chunk_decode_v<2048>(in, pa, ws, out, stream);
+        case 4096: return chunk_decode_v<4096>(in, pa, ws, out, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace eblc

@@ -1,0 +1,243 @@
+/*
+ * eblc_device.h -- device primitives shared by the gfx950 kernels of libeblc.so: wave-level
+ * DPP scans and moves, non-temporal global access, the caller's memory layout, and the
+ * quantizer ("Pipeline Specialization Internals", FZGPUModules site: linear quantization with
+ * step 2*eb, inv2eb = 1/(2*eb), the zigzag Transform).  Every function is inline and has
+ * internal linkage in each kernel source that includes it.
+ */
+#ifndef EBLC_DEVICE_H
+#define EBLC_DEVICE_H
+
+#include "eblc_internal.h"
+
+#include <float.h>
+
+namespace eblc {
+namespace {
+
+/* ---- wave-level primitives ---------------------------------------------------------------- */
+
+constexpr int kDppQuadXor1 = 0xB1;     /* quad_perm [1,0,3,2] */
+constexpr int kDppQuadXor2 = 0x4E;     /* quad_perm [2,3,0,1] */
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppWaveShr1 = 0x138;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xf, bool BOUND_CTRL = false>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xf, BOUND_CTRL);
+}
+
+/* Inclusive prefix sum over the 64 lanes (row-local Hillis-Steele, then row broadcasts). */
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    v += dpp<kDppRowShr1, 0xf, true>(0, v);
+    v += dpp<kDppRowShr2, 0xf, true>(0, v);
+    v += dpp<kDppRowShr4, 0xf, true>(0, v);
+    v += dpp<kDppRowShr8, 0xf, true>(0, v);
+    v += dpp<kDppRowBcast15, 0xa>(0, v);
+    v += dpp<kDppRowBcast31, 0xc>(0, v);
+    return v;
+}
+
+/* Inclusive prefix sum restricted to aligned segments of seglen lanes (8, 16, 32 or 64);
+ * dist = lane index within its segment. */
+__device__ __forceinline__ uint32_t wave_seg_scan(uint32_t v, uint32_t dist, uint32_t seglen) {
+    uint32_t t;
+    t = dpp<kDppRowShr1, 0xf, true>(0, v);
+    v += (dist >= 1) ? t : 0u;
+    t = dpp<kDppRowShr2, 0xf, true>(0, v);
+    v += (dist >= 2) ? t : 0u;
+    t = dpp<kDppRowShr4, 0xf, true>(0, v);
+    v += (dist >= 4) ? t : 0u;
+    t = dpp<kDppRowShr8, 0xf, true>(0, v);
+    v += (dist >= 8) ? t : 0u;
+    if (seglen >= 32) v += dpp<kDppRowBcast15, 0xa>(0, v);
+    if (seglen >= 64) v += dpp<kDppRowBcast31, 0xc>(0, v);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t readlane(uint32_t v, int lane) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
+/* Orders this wave's LDS traffic across lanes (compiler and hardware). */
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void lds_or(uint32_t *p, uint32_t v) {
+    __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
+
+__device__ __forceinline__ uint64_t align16(uint64_t v) { return (v + 15u) & ~(uint64_t)15u; }
+
+/* Non-temporal 128-bit global access, for data streamed exactly once (the field on compress,
+ * the reconstruction on decompress): the lines bypass cache allocation. */
+typedef float v4f32 __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 ld_nt(const float4 *p) {
+    const v4f32 t = __builtin_nontemporal_load(reinterpret_cast<const v4f32 *>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
+}
+
+__device__ __forceinline__ uint4 ld_nt(const uint4 *p) {
+    const v4u32 t = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+__device__ __forceinline__ void st_nt(float4 *p, const float4 &v) {
+    const v4f32 t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<v4f32 *>(p));
+}
+
+__device__ __forceinline__ void st_nt(uint4 *p, const uint4 &v) {
+    const v4u32 t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<v4u32 *>(p));
+}
+
+/* ---- the caller's memory layout ------------------------------------------------------------ */
+
+__device__ __forceinline__ uint32_t div_m(uint32_t v, uint64_t m) {
+    return m == 0 ? v : (uint32_t)__umul64hi((uint64_t)v, m);
+}
+
+/* Element offset of flattened value i (i < 2^32) in the caller's array; *col receives i's
+ * position in its row. */
+template <bool STRIDED>
+__device__ __forceinline__ uint64_t elem_off(const Layout &lo, uint64_t i, uint32_t *col_out = nullptr) {
+    if (!STRIDED) return i;
+    const uint32_t ii = (uint32_t)i;
+    const uint32_t row = div_m(ii, lo.mL);
+    const uint32_t col = ii - row * lo.L;
+    if (col_out != nullptr) *col_out = col;
+    if (lo.rank == 2) return col + (uint64_t)row * lo.s1;
+    const uint32_t r1 = div_m(row, lo.m1);
+    const uint32_t c1 = row - r1 * lo.o1;
+    if (lo.rank == 3) return col + (uint64_t)c1 * lo.s1 + (uint64_t)r1 * lo.s2;
+    const uint32_t r2 = div_m(r1, lo.m2);
+    const uint32_t c2 = r1 - r2 * lo.o2;
+    return col + (uint64_t)c1 * lo.s1 + (uint64_t)c2 * lo.s2 + (uint64_t)r2 * lo.s3;
+}
+
+/* 128-bit non-temporal access at a 4-byte aligned address (gfx950 executes dword-aligned
+ * multi-dword global accesses). */
+typedef float v4f32u __attribute__((ext_vector_type(4), aligned(4)));
+
+__device__ __forceinline__ float4 ld_nt_u(const float *p) {
+    const v4f32u t = __builtin_nontemporal_load(reinterpret_cast<const v4f32u *>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
+}
+
+__device__ __forceinline__ void st_nt_u(float *p, const float4 &v) {
+    const v4f32u t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<v4f32u *>(p));
+}
+
+/* Values i .. i+3 (i a multiple of 4, all below n), streamed once: one 128-bit access when they
+ * are contiguous in memory (16-byte aligned with a vectorisable layout, else whenever they sit
+ * in one row), one access per value when a row boundary splits them. */
+template <bool STRIDED>
+__device__ __forceinline__ float4 load4(const float *x, const Layout &lo, uint64_t i) {
+    if (!STRIDED) return ld_nt(reinterpret_cast<const float4 *>(x + i));
+    uint32_t col;
+    const uint64_t off = elem_off<true>(lo, i, &col);
+    if (lo.vec) return ld_nt(reinterpret_cast<const float4 *>(x + off));
+    if (col + 3 < lo.L) return ld_nt_u(x + off);
+    return make_float4(x[off], x[elem_off<true>(lo, i + 1)], x[elem_off<true>(lo, i + 2)],
+                       x[elem_off<true>(lo, i + 3)]);
+}
+
+template <bool STRIDED>
+__device__ __forceinline__ void store4(float *y, const Layout &lo, uint64_t i, const float4 &v) {
+    if (!STRIDED) {
+        st_nt(reinterpret_cast<float4 *>(y + i), v);
+        return;
+    }
+    uint32_t col;
+    const uint64_t off = elem_off<true>(lo, i, &col);
+    if (lo.vec) {
+        st_nt(reinterpret_cast<float4 *>(y + off), v);
+    } else if (col + 3 < lo.L) {
+        st_nt_u(y + off, v);
+    } else {
+        y[off] = v.x;
+        y[elem_off<true>(lo, i + 1)] = v.y;
+        y[elem_off<true>(lo, i + 2)] = v.z;
+        y[elem_off<true>(lo, i + 3)] = v.w;
+    }
+}
+
+/* ---- quantizer ------------------------------------------------------------------------------ */
+
+struct QParams {
+    float eb, s, r, tlim; /* tlim = 2^T */
+    uint32_t T;
+};
+
+/* A code is accepted when its fp32 reconstruction is within eb of x; the second clause
+ * (|x| >= |y|/2) makes the fp32 difference exact, so the test is exact. */
+__device__ __forceinline__ bool accept(float x, float y, float eb) {
+    const float diff = x - y;
+    const float half_y = 0.5f * fabsf(y);
+    return (fabsf(diff) <= eb) && (fabsf(x) >= half_y);
+}
+
+/* Full rule for a value that missed the fast test: escape if not finite or the rounded code is
+ * 2^30 or more in magnitude; else keep the rounded code if accepted, else its neighbour toward
+ * x if accepted, else escape; finally escape codes of 2^T or more in magnitude. */
+__device__ __forceinline__ int32_t quantize_slow(float x, float q0f, QParams qp, uint32_t *esc) {
+    if (!(fabsf(q0f) < 1073741824.0f)) {
+        *esc = 1;
+        return 0;
+    }
+    int32_t q = (int32_t)q0f;
+    const float y = q0f * qp.s;
+    if (!accept(x, y, qp.eb)) {
+        const int32_t qn = (x > y) ? q + 1 : q - 1;
+        const float yn = (float)qn * qp.s;
+        if (!accept(x, yn, qp.eb)) {
+            *esc = 1;
+            return 0;
+        }
+        q = qn;
+    }
+    const uint32_t mag = q < 0 ? (uint32_t)(-q) : (uint32_t)q;
+    if (mag >= (1u << qp.T)) {
+        *esc = 1;
+        return 0;
+    }
+    *esc = 0;
+    return q;
+}
+
+__device__ __forceinline__ uint32_t zigzag(int32_t d) {
+    return ((uint32_t)d << 1) ^ (uint32_t)(d >> 31);
+}
+
+__device__ __forceinline__ int32_t unzigzag(uint32_t z) {
+    return (int32_t)((z >> 1) ^ (0u - (z & 1u)));
+}
+
+/* Word offset of chunk c in the packed payload (or outlier rank), from the group prefix plus
+ * the chunks before c in its group. */
+template <int CPG>
+__device__ __forceinline__ uint32_t chunk_offset(const uint32_t *gpre, const uint32_t *per_chunk,
+                                                 uint32_t c) {
+    const uint32_t g = c / CPG;
+    uint32_t o = gpre[g];
+    for (uint32_t k = g * CPG; k < c; ++k) o += per_chunk[k];
+    return o;
+}
+
+}  // namespace
+}  // namespace eblc
+
+#endif

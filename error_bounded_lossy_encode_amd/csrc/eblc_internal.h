@@ -9,7 +9,9 @@
  *   decompress: tile  = 256 values, 4 consecutive values per lane, a segment is 8 lanes
  *               chunk = 8 tiles = 2048 values = 64 segments; one wave owns one chunk
  *               group = 4 chunks = one 256-thread workgroup
- * Both groups hold 8192 values; the device-wide scans run over groups.  The Lorenzo block B is
+ * Both groups hold 8192 values; the device-wide scans run over groups.  The chunk coder keeps
+ * the encode chunks and groups (its coder chunks of V values fill whole encode chunks, or two)
+ * and decodes one coder chunk per wave, four per group.  The Lorenzo block B is
  * a power of two in [32, 2048].  A decode chunk always starts a block; an encode chunk that
  * does not (B larger than the chunk) takes its first prediction from the code of the value
  * before it.  The only other cross-wave dependency is the exclusive scan of payload sizes and
@@ -60,7 +62,7 @@ struct DevInfo {
     float eb_f, s, r;
     uint32_t valid;
     /* outcome of the last compress, or the parsed header of the last decompress */
-    uint32_t mode;          /* 0 coded, 1 raw */
+    uint32_t mode;          /* 0 bitpack coder, 1 raw, 2 chunk coder */
     uint32_t err;           /* decompress: this call's stream is corrupt */
     uint32_t sticky;        /* OR of err over calls since eblc_plan_status */
     uint32_t reserved0;
@@ -96,11 +98,16 @@ struct PlanArgs {
     uint64_t nseg;
     uint64_t dims[4];
     uint32_t rank;
-    uint32_t B;             /* Lorenzo block, power of two 32..2048 */
+    uint32_t B;             /* Lorenzo block, power of two 32..2048 (the chunk, for the chunk coder) */
     uint32_t T;             /* outlier log2 */
+    uint32_t V;             /* chunk coder: values per chunk (1024, 2048, 4096); 0: bitpack coder */
+    uint32_t log2seg;       /* header field: 5 (32-value segments), or log2 V */
+    uint32_t slot;          /* scratch words per encode chunk: 2048, or 2112 for the chunk coder */
+    uint32_t wpg;           /* bytes of the size section per encode group */
+    uint64_t wsec;          /* bytes of the size section: align16(nseg), or align16(4 chunks) */
     uint32_t nchunks;       /* encode chunks */
     uint32_t ngroups;       /* encode groups */
-    uint32_t dchunks;       /* decode chunks */
+    uint32_t dchunks;       /* decode chunks (the coder's chunks for the chunk coder) */
     uint32_t dgroups;       /* decode groups */
     uint64_t side_max;
     Layout lay;             /* memory layout of the compress input and decompress output */
@@ -109,7 +116,7 @@ struct PlanArgs {
 /* Workspace pointers (all device memory owned by the plan). */
 struct Workspace {
     DevInfo *info;
-    uint32_t *scratch;       /* nchunks * kEncChunk words: per-chunk packed payload slots */
+    uint32_t *scratch;       /* (nchunks + 1) * slot words: per-chunk payload slots */
     uint32_t *chunk_words;   /* [nchunks] payload words per chunk (encode or decode chunks) */
     uint32_t *chunk_esc;     /* [nchunks] escapes per encode chunk */
     uint32_t *chunk_tmask;   /* [nchunks] bit t set if tile t of the encode chunk has an escape */
@@ -120,7 +127,7 @@ struct Workspace {
     uint32_t *emask;         /* [nchunks * kEncSegs] escape bitmask per segment (tiles with escapes) */
     uint32_t *stage_idx;     /* [nchunks * kEscStage] first escapes of each chunk: index ... */
     uint32_t *stage_val;     /* [nchunks * kEscStage] ... and raw value bits, in index order */
-    uint8_t *widths;         /* [nchunks * kEncSegs] widths staging when the output is too small */
+    uint8_t *widths;         /* [nchunks * kEncSegs] size section staging when the output is too small */
     float *range_part;       /* [2 * range_blocks(n)] per-block min / max */
 };
 
@@ -147,6 +154,13 @@ hipError_t launch_decode(const uint8_t *in, const PlanArgs &pa, const Workspace 
                          hipStream_t stream);
 hipError_t launch_patch(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
                         hipStream_t stream);
+
+/* The chunk coder (eblc_chunk.hip): encode in place of launch_encode, decode in place of
+ * launch_decode; the other stages are shared. */
+hipError_t launch_chunk_encode(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *sizes_dst,
+                               uint64_t sizes_bytes, hipStream_t stream);
+hipError_t launch_chunk_decode(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
+                               hipStream_t stream);
 
 }  // namespace eblc
 

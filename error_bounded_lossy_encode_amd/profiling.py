@@ -8,8 +8,8 @@ Two kinds of summary:
   WRITE_SIZE``, KiB per dispatch).  Each counter is scaled by what it reads for a plain device
   copy of known size run in the same process, so the traffic is in true bytes.
 
-A traffic summary records the SHA-256 of the kernel source it was measured on; the benchmark
-uses it only while the source is unchanged.
+A traffic summary records the SHA-256 of the kernel sources it was measured on; the benchmark
+uses it only while they are unchanged.
 """
 from __future__ import annotations
 
@@ -21,13 +21,18 @@ import sqlite3
 from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCE = os.path.join(HERE, "csrc", "eblc_kernels.hip")
+KERNEL_SOURCES = [os.path.join(HERE, "csrc", f) for f in
+                  ("eblc_internal.h", "eblc_device.h", "eblc_kernels.hip", "eblc_chunk.hip")]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
 def kernel_source_sha256() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """One digest over every file the kernels are compiled from, in a fixed order."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def short_name(full: str) -> str:

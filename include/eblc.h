@@ -16,11 +16,19 @@
  *   the variable segment sizes and compaction into one self-describing stream.  Decompress is
  *   the exact inverse.
  *
+ * A second coder, selected per plan (coder=chunk), follows the page's chunk-cooperative chain
+ * Quant -> Diff -> Bitshuffle -> RZE over chunks of 4, 8 or 16 KiB: the same quantizer and
+ * escapes, the first difference inside each chunk, zigzag, the chunk's 32 bit planes (word
+ * b*G+g holds bit b of the 32 codes of group g, G = V/32), and zero-word elimination (a bitmap
+ * of the V plane words, then the nonzero ones).
+ *
  * Stream (little-endian, every section 16-byte aligned, pad bytes zero):
  *   [0,128)            header (magic "EBLC", version 1, mode, rank, dims, n, eb, step,
  *                      outlier count, section offsets, total length)
- *   [128, +nseg)       one width byte per 32-value segment (nseg = ceil(n/32))
- *   payload            sum(widths) little-endian u32 words
+ *   [128, ...)         bitpack coder (mode 0): one width byte per 32-value segment
+ *                      (nseg = ceil(n/32)); chunk coder (mode 2): one u32 word count per chunk
+ *   payload            bitpack: sum(widths) u32 words; chunk: each chunk's bitmap and nonzero
+ *                      plane words, chunk after chunk (the last chunk padded with zero codes)
  *   outlier indices    m x u32, strictly ascending
  *   outlier values     m x u32 (raw float32 bits)
  * A RAW stream (bound unusable or 0, more outliers than side_max, or a coded stream that
@@ -119,6 +127,10 @@ int eblc_abi_version(void);
  *                                     default 256
  *              outlier_log2=<T>       codes with |q| >= 2^T escape; 1..30; default 30
  *              side_max=<m>           largest outlier list; 0..n; default min(n, 2^23)
+ *              coder=bitpack|chunk    bitpack (default) or the chunk coder
+ *              chunk_bytes=<b>        chunk coder only: 4096, 8192 (default) or 16384 input
+ *                                     bytes per chunk; the chunk is also the reset period of
+ *                                     the difference, so block= is refused with coder=chunk
  *            Unknown keys, repeated keys, NaN or negative values -> INVALID_ARGUMENT.
  *   plan_out receives the plan.  The plan allocates its whole workspace here (about 4 n +
  *            n/8 bytes plus small arrays) and nothing per call.
@@ -171,10 +183,13 @@ eblc_status eblc_compress_batch(eblc_plan_t *plan, int count, const float *const
  * queued on the supplied stream).  compressed_bytes may be the stream's length or any larger
  * count of readable bytes up to max_compressed_bytes: the stream's own length is read from its
  * header on the device and must not exceed it, so a stream from eblc_compress_async can be
- * decompressed without the host ever reading its length.  The host checks 128 +
- * align16(nseg) <= compressed_bytes <= max_compressed_bytes (else CORRUPT_STREAM at once).
+ * decompressed without the host ever reading its length.  The host checks 128 + (size of the
+ * width or word-count section) <= compressed_bytes <= max_compressed_bytes (else
+ * CORRUPT_STREAM at once).  A plan decodes RAW streams and coded streams of its own coder
+ * (and, for the chunk coder, of its own chunk size); any other stream is CORRUPT_STREAM.
  * Header or section problems found on the device (wrong magic/version/dims/n/offsets, widths
- * above 32, outlier indices not strictly ascending below n) set a sticky CORRUPT_STREAM that
+ * above 32, chunk word counts outside [V/32, V + V/32] or unequal to the bitmap's count,
+ * outlier indices not strictly ascending below n) set a sticky CORRUPT_STREAM that
  * eblc_plan_status returns; the contents of `out` are then unspecified.  sidecar must be
  * NULL. */
 eblc_status eblc_decompress(eblc_plan_t *plan, const void *in, size_t compressed_bytes,

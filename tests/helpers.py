@@ -8,8 +8,9 @@ CANARY = 0xA7
 
 
 def parse_options(opts: str, n: int):
-    """Options string -> oracle arguments (rel, eps, B, T, side_max), library defaults."""
-    out = {"rel": True, "eps": 1e-4, "B": 256, "T": 30, "side_max": min(n, 1 << 23)}
+    """Options string -> oracle arguments (rel, eps, B, T, side_max, V), library defaults.
+    V is the chunk coder's chunk in values (coder=chunk), else None."""
+    out = {"rel": True, "eps": 1e-4, "B": 256, "T": 30, "side_max": min(n, 1 << 23), "V": None}
     if opts is None or opts.strip() == "":
         return out
     try:
@@ -32,7 +33,26 @@ def parse_options(opts: str, n: int):
             out["T"] = int(v)
         elif k == "side_max":
             out["side_max"] = int(v)
+        elif k == "coder" and v == "chunk":
+            out["V"] = out["V"] or 2048
+        elif k == "chunk_bytes":
+            out["V"] = int(v) // 4
     return out
+
+
+def chunk_options(opts: str, chunk_bytes: int) -> str:
+    """A workload's options with its block replaced by the chunk coder of chunk_bytes."""
+    items = [t for t in opts.split(";") if t.strip() and not t.strip().startswith("block=")]
+    return ";".join(items + ["coder=chunk", f"chunk_bytes={chunk_bytes}"])
+
+
+def oracle_stream(oracle, x: np.ndarray, dims, opts: str) -> np.ndarray:
+    """The oracle's stream for the library's options string (either coder)."""
+    n = int(np.prod(dims))
+    o = parse_options(opts, n)
+    if o["V"] is not None:
+        return oracle.compress_chunked(x, dims, o["rel"], o["eps"], o["V"], o["T"], o["side_max"])
+    return oracle.compress(x, dims, o["rel"], o["eps"], o["B"], o["T"], o["side_max"])
 
 
 def header(stream: np.ndarray) -> dict:

@@ -45,7 +45,10 @@ def test_unsupported_execution_kinds(kind):
 
 @pytest.mark.parametrize("opts", ["rel=-1", "abs=nan", "rel=1e-3;abs=1", "block=48", "block=4096",
                                   "outlier_log2=0", "outlier_log2=31", "bogus=1", "rel", "side_max=-3",
-                                  "block=256;block=128", "side_max=5000"])
+                                  "block=256;block=128", "side_max=5000", "coder=huffman",
+                                  "coder=chunk;block=256", "chunk_bytes=8192", "coder=chunk;chunk_bytes=2048",
+                                  "coder=chunk;chunk_bytes=32768", "coder=chunk;coder=chunk",
+                                  "coder=chunk;chunk_bytes=4096;chunk_bytes=4096"])
 def test_invalid_options_rejected_before_any_device_call(opts):
     st, plan = binding.eblc_plan_create([64, 64], opts)
     assert st == binding.EBLC_INVALID_ARGUMENT and plan is None

@@ -1,0 +1,246 @@
+"""GPU parity of the chunk-cooperative coder (coder=chunk: Quant -> Diff -> Bitshuffle -> RZE
+over 4, 8 or 16 KiB chunks) against the oracle's chunk coder.
+
+Streams are compared byte for byte (header, per-chunk word counts, bitmaps and nonzero words,
+outliers, pads) and reconstructions bit for bit, on seeded inputs spanning several chunks and
+workgroups with ragged tails, every chunk size, both bound modes, escapes on both outlier
+paths (staged and bitmask), the RAW fallbacks, the asynchronous and batched entry points, a
+padded layout, and corrupt or mismatched streams.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from error_bounded_lossy_encode_amd import synth
+from helpers import CANARY, chunk_options, first_difference, gpu_roundtrip, header, oracle_stream
+
+pytestmark = pytest.mark.gpu
+
+CHUNK_BYTES = [4096, 8192, 16384]
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    from error_bounded_lossy_encode_amd import binding
+    binding.lib()
+    return binding, torch
+
+
+def check_case(env, x, dims, opts, label=""):
+    binding, torch = env
+    ref = oracle_stream(oracle, x, dims, opts)
+    st, ref_dec = oracle.decompress(ref)
+    assert st == oracle.OK
+    got, dec = gpu_roundtrip(binding, torch, x, dims, opts)
+    assert got.size == ref.size and np.array_equal(got, ref), f"{label} {opts}: {first_difference(got, ref)}"
+    bad = np.nonzero(dec.view(np.uint32) != ref_dec.view(np.uint32))[0]
+    assert bad.size == 0, f"{label} {opts}: reconstruction differs at {bad[:5]}"
+    return header(ref)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_chunk_tiny_fuzz(env, seed):
+    rng = np.random.default_rng(900 + seed)
+    kinds = ["smooth", "normal", "specials", "const", "ramp", "subnormal", "bits"]
+    for case in range(12):
+        cb = int(rng.choice(CHUNK_BYTES))
+        V = cb // 4
+        n = int(rng.integers(1, 3 * V + 300))
+        kind = kinds[(seed + case) % len(kinds)]
+        x = synth.tiny_array(rng, n, kind)
+        T = int(rng.choice([1, 2, 15, 30]))
+        side = int(rng.choice([0, 1, n]))
+        if rng.integers(0, 2):
+            eps = float(rng.choice([0.0, 1e-7, 1e-3, 0.3]))
+            bound = f"rel={eps!r}"
+        else:
+            eps = float(rng.choice([0.0, 1e-6, 1e-2, 5.0]))
+            bound = f"abs={eps!r}"
+        opts = f"{bound};coder=chunk;chunk_bytes={cb};outlier_log2={T};side_max={side}"
+        print(f"[chunk fuzz] seed {seed} case {case} kind {kind} n {n} {opts}", flush=True)
+        check_case(env, x, [n], opts, f"seed{seed} case{case} {kind} n={n}")
+
+
+@pytest.mark.parametrize("cb", CHUNK_BYTES)
+def test_chunk_several_groups_ragged(env, cb):
+    """Several 8192-value workgroups, a ragged last chunk, NaN/Inf escapes, both modes."""
+    rng = np.random.default_rng(cb)
+    n = 5 * 8192 + 777
+    x = synth.tiny_array(rng, n, "smooth")
+    x[::1237] = np.float32(np.nan)
+    x[5::4099] = np.float32(-np.inf)
+    for opts in (f"rel=1e-4;coder=chunk;chunk_bytes={cb}", f"rel=1e-2;coder=chunk;chunk_bytes={cb};outlier_log2=20"):
+        h = check_case(env, x, [n], opts, f"V={cb // 4}")
+        assert h["mode"] == 2 and h["m"] > 0
+
+
+@pytest.mark.parametrize("cb", CHUNK_BYTES)
+def test_chunk_many_escapes(env, cb):
+    """More than 64 escapes in an encode chunk takes the bitmask outlier path."""
+    rng = np.random.default_rng(40 + cb)
+    n = 3 * 8192 + 100
+    x = synth.tiny_array(rng, n, "smooth")
+    x[3::16] = np.float32(1e6)
+    h = check_case(env, x, [n], f"rel=1e-4;coder=chunk;chunk_bytes={cb};outlier_log2=8", f"V={cb // 4}")
+    assert h["mode"] == 2 and h["m"] > 64 * (n // 2048)
+
+
+@pytest.mark.parametrize("cb", CHUNK_BYTES)
+def test_chunk_multidim_and_widths(env, cb):
+    """Rank-3 field whose codes need many bit planes (tight bound), and a zero field."""
+    rng = np.random.default_rng(7 * cb)
+    dims = [9, 40, 72]
+    n = int(np.prod(dims))
+    x = synth.tiny_array(rng, n, "normal")
+    h = check_case(env, x, dims, f"rel=1e-6;coder=chunk;chunk_bytes={cb}", "tight")
+    assert h["mode"] in (1, 2)
+    z = np.zeros(n, np.float32)
+    h = check_case(env, z, dims, f"abs=1e-3;coder=chunk;chunk_bytes={cb}", "zeros")
+    assert h["mode"] == 2 and h["payload_bytes"] == 4 * (cb // 4 // 32) * ((n + cb // 4 - 1) // (cb // 4))
+
+
+@pytest.mark.parametrize("cb", CHUNK_BYTES)
+def test_chunk_raw_fallbacks(env, cb):
+    rng = np.random.default_rng(11 + cb)
+    n = 2 * 8192 + 3
+    bits = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    assert check_case(env, bits, [n], f"abs=1e-30;coder=chunk;chunk_bytes={cb};outlier_log2=2")["mode"] == 1
+    x = synth.tiny_array(rng, n, "smooth")
+    x[::50] = np.float32(np.inf)
+    assert check_case(env, x, [n], f"rel=1e-3;coder=chunk;chunk_bytes={cb};side_max=10")["mode"] == 1
+    assert check_case(env, x, [n], f"rel=0;coder=chunk;chunk_bytes={cb}")["mode"] == 1
+
+
+def test_chunk_async_batch_and_capacity_decode(env):
+    binding, torch = env
+    N = 40
+    dims, opts = [N, N, N], "rel=1e-3;coder=chunk;chunk_bytes=8192"
+    fields = []
+    for i in range(4):
+        x, _, _ = synth.c5_snapshot(i, N, 1e-3)
+        fields.append(x.numpy().copy())
+    fields[2][::97] = np.float32(np.nan)
+    st, plan = binding.eblc_plan_create(dims, opts, 0)
+    assert st == binding.EBLC_OK
+    try:
+        maxb = binding.eblc_max_compressed_bytes(plan)
+        xs = [torch.from_numpy(f).cuda() for f in fields]
+        outs = [torch.full((maxb,), CANARY, dtype=torch.uint8, device="cuda") for _ in fields]
+        res = torch.zeros(16 * len(fields), dtype=torch.uint8, device="cuda")
+        ys = [torch.full((N ** 3,), float("nan"), dtype=torch.float32, device="cuda") for _ in fields]
+        assert binding.eblc_compress_batch(plan, xs, outs, res) == binding.EBLC_OK
+        for i in range(len(fields)):
+            assert binding.eblc_decompress(plan, outs[i], maxb, ys[i]) == binding.EBLC_OK
+        assert binding.eblc_plan_status(plan) == binding.EBLC_OK
+        for i, (nb, status) in enumerate(binding.result_records(res)):
+            ref = oracle_stream(oracle, fields[i], dims, opts)
+            assert status == binding.EBLC_OK and nb == ref.size, i
+            assert np.array_equal(outs[i].cpu().numpy()[:nb], ref), i
+            _, ref_dec = oracle.decompress(ref)
+            assert np.array_equal(ys[i].cpu().numpy().view(np.uint32), ref_dec.view(np.uint32)), i
+        # a capacity below the stream: CAPACITY with the required size, nothing past the capacity
+        ref = oracle_stream(oracle, fields[0], dims, opts)
+        out = torch.full((maxb,), CANARY, dtype=torch.uint8, device="cuda")
+        st, nb = binding.eblc_compress(plan, xs[0], out, ref.size - 16)
+        assert st == binding.EBLC_CAPACITY and nb == ref.size
+        assert (out.cpu().numpy()[ref.size - 16:] == CANARY).all()
+    finally:
+        binding.eblc_plan_destroy(plan)
+
+
+def test_chunk_padded_layout(env):
+    binding, torch = env
+    dims, strides = [30, 50, 70], [52 * 76, 76, 1]
+    opts = "rel=1e-4;coder=chunk;chunk_bytes=16384"
+    rng = np.random.default_rng(3)
+    interior = synth.tiny_array(rng, int(np.prod(dims)), "smooth").reshape(dims)
+    span = 1 + sum((d - 1) * s for d, s in zip(dims, strides))
+    buf = np.full(span + 8, np.float32(-7.25e33), dtype=np.float32)
+    np.lib.stride_tricks.as_strided(buf, shape=dims, strides=[4 * s for s in strides])[...] = interior
+    ref = oracle_stream(oracle, interior.reshape(-1), dims, opts)
+    _, ref_dec = oracle.decompress(ref)
+    st, plan = binding.eblc_plan_create(dims, opts, 0, strides=strides)
+    assert st == binding.EBLC_OK
+    try:
+        maxb = binding.eblc_max_compressed_bytes(plan)
+        xd = torch.from_numpy(buf).cuda()
+        out = torch.zeros(maxb, dtype=torch.uint8, device="cuda")
+        st, nb = binding.eblc_compress(plan, xd, out)
+        assert st == binding.EBLC_OK and np.array_equal(out.cpu().numpy()[:nb], ref)
+        yd = torch.from_numpy(np.full_like(buf, np.float32(-7.25e33))).cuda()
+        assert binding.eblc_decompress(plan, out, nb, yd) == binding.EBLC_OK
+        assert binding.eblc_plan_status(plan) == binding.EBLC_OK
+        ybuf = yd.cpu().numpy()
+        yview = np.lib.stride_tricks.as_strided(ybuf, shape=dims, strides=[4 * s for s in strides])
+        assert np.array_equal(np.ascontiguousarray(yview).reshape(-1).view(np.uint32), ref_dec.view(np.uint32))
+        idx = np.lib.stride_tricks.as_strided(np.arange(ybuf.size), shape=dims,
+                                              strides=[8 * s for s in strides]).reshape(-1)
+        mask = np.ones(ybuf.size, bool)
+        mask[idx] = False
+        assert (ybuf[mask] == np.float32(-7.25e33)).all()
+    finally:
+        binding.eblc_plan_destroy(plan)
+
+
+def test_chunk_corrupt_and_mismatched_streams(env):
+    binding, torch = env
+    rng = np.random.default_rng(8)
+    n = 3 * 8192 + 11
+    x = synth.tiny_array(rng, n, "smooth")
+    opts = "rel=1e-4;coder=chunk;chunk_bytes=8192"
+    good = oracle_stream(oracle, x, [n], opts)
+    assert header(good)["mode"] == 2
+    st, plan = binding.eblc_plan_create([n], opts, 0)
+    assert st == binding.EBLC_OK
+    try:
+        y = torch.empty(n, dtype=torch.float32, device="cuda")
+
+        def status_of(stream):
+            d = torch.from_numpy(np.ascontiguousarray(stream)).cuda()
+            st = binding.eblc_decompress(plan, d, stream.size, y)
+            if st != binding.EBLC_OK:
+                return st
+            return binding.eblc_plan_status(plan)
+
+        def edited(fn):
+            t = good.copy()
+            fn(t)
+            return t
+
+        def put32(t, off, v):
+            t[off:off + 4] = np.array([v], np.uint32).view(np.uint8)
+
+        s0 = int(good[128:132].view(np.uint32)[0])
+        po = header(good)["payload_off"]
+        assert status_of(good) == binding.EBLC_OK
+        assert status_of(edited(lambda t: put32(t, 128, 63))) == binding.EBLC_CORRUPT_STREAM      # below the bitmap
+        assert status_of(edited(lambda t: put32(t, 128, 2048 + 65))) == binding.EBLC_CORRUPT_STREAM
+        assert status_of(edited(lambda t: put32(t, 128, s0 + 1))) == binding.EBLC_CORRUPT_STREAM  # sum off
+        assert status_of(edited(lambda t: t.__setitem__(po, t[po] ^ 1))) == binding.EBLC_CORRUPT_STREAM  # bitmap
+        # a stream of the bitpack coder, and one of another chunk size, are refused by this plan
+        other = oracle_stream(oracle, x, [n], "rel=1e-4;block=256")
+        assert status_of(other) == binding.EBLC_CORRUPT_STREAM
+        other = oracle_stream(oracle, x, [n], "rel=1e-4;coder=chunk;chunk_bytes=4096")
+        assert status_of(other) == binding.EBLC_CORRUPT_STREAM
+        # RAW streams of either coder decode
+        raw = oracle.compress(x, [n], True, 0.0, 256, 30, n)
+        assert header(raw)["mode"] == 1 and status_of(raw) == binding.EBLC_OK
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), x.view(np.uint32))
+        assert status_of(good) == binding.EBLC_OK
+        _, ref_dec = oracle.decompress(good)
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), ref_dec.view(np.uint32))
+    finally:
+        binding.eblc_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("cb", CHUNK_BYTES)
+def test_chunk_ricker_512cubed(env, cb):
+    """The 512^3 Ricker snapshot at full size, every chunk size."""
+    binding, torch = env
+    x, dims, opts = synth.c3_ricker(512, device="cuda")
+    x = x.cpu().numpy()
+    opts = chunk_options(opts, cb)
+    print(f"[full-size chunk] 512^3 {opts}", flush=True)
+    h = check_case(env, x, dims, opts, "512^3 Ricker")
+    assert h["mode"] == 2
