@@ -70,8 +70,9 @@ def build_items(name: str, device: str):
 
 
 def parse_opts(opts: str, n: int) -> dict:
-    """Options string -> the oracle's arguments (library defaults where absent)."""
-    o = {"rel": True, "eps": 1e-4, "B": 256, "T": 30, "side_max": min(n, 1 << 23)}
+    """Options string -> the oracle's arguments (library defaults where absent); V is the chunk
+    coder's chunk in values, None for the bitpack coder."""
+    o = {"rel": True, "eps": 1e-4, "B": 256, "T": 30, "side_max": min(n, 1 << 23), "V": None}
     for item in opts.split(";"):
         if "=" not in item:
             continue
@@ -84,7 +85,17 @@ def parse_opts(opts: str, n: int) -> dict:
             o["T"] = int(v)
         elif k == "side_max":
             o["side_max"] = int(v)
+        elif k == "coder" and v == "chunk":
+            o["V"] = o["V"] or 2048
+        elif k == "chunk_bytes":
+            o["V"] = int(v) // 4
     return o
+
+
+def with_chunk_coder(opts: str, chunk_bytes: int) -> str:
+    """A workload's options with its block replaced by the chunk coder."""
+    items = [t for t in opts.split(";") if t.strip() and not t.strip().startswith("block=")]
+    return ";".join(items + ["coder=chunk", f"chunk_bytes={chunk_bytes}"])
 
 
 def cpu_baseline(items, budget_s: float):
@@ -125,7 +136,10 @@ def cpu_baseline(items, budget_s: float):
     for xs, sdims, opts in samples:
         o = parse_opts(opts, xs.size)
         t0 = time.perf_counter()
-        s = oracle.compress(xs, sdims, o["rel"], o["eps"], o["B"], o["T"], min(o["side_max"], xs.size))
+        if o["V"] is not None:
+            s = oracle.compress_chunked(xs, sdims, o["rel"], o["eps"], o["V"], o["T"], min(o["side_max"], xs.size))
+        else:
+            s = oracle.compress(xs, sdims, o["rel"], o["eps"], o["B"], o["T"], min(o["side_max"], xs.size))
         t1 = time.perf_counter()
         st, _ = oracle.decompress(s)
         t2 = time.perf_counter()
@@ -159,6 +173,10 @@ def main() -> int:
     ap.add_argument("--halo", type=int, default=0, metavar="H",
                     help="store each field inside a buffer padded by H elements on every side of every "
                          "axis and compress / decompress through the padded strides")
+    ap.add_argument("--coder", choices=["bitpack", "chunk"], default="bitpack",
+                    help="bitpack: per-segment widths and fixed-length packing; chunk: the chunk-cooperative "
+                         "coder (Quant, Diff, Bitshuffle, RZE)")
+    ap.add_argument("--chunk-bytes", type=int, default=8192, choices=[4096, 8192, 16384])
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device to device once (counter calibration)")
     args = ap.parse_args()
@@ -177,6 +195,10 @@ def main() -> int:
     log(f"[bench] generating workload {args.workload}")
     items, desc = build_items(args.workload, dev)
     items = [(x.contiguous(), dims, opts) for x, dims, opts in items]
+    if args.coder == "chunk":
+        items = [(x, dims, with_chunk_coder(opts, args.chunk_bytes)) for x, dims, opts in items]
+        desc = desc.replace(", block 128", "").replace(", block 256", "").replace(", block 32", "")
+        desc += f"; chunk coder (Quant, Diff, Bitshuffle, RZE) over {args.chunk_bytes}-byte chunks"
     dims0, opts0 = items[0][1], items[0][2]
     assert all(d == dims0 and o == opts0 for _, d, o in items)
     n = items[0][0].numel()
@@ -283,7 +305,7 @@ def main() -> int:
         outliers.append(int(u64[9]))
         payload.append(int(u64[10]))
         ebs.append(float(hdr[56:60].view(np.float32)[0]))
-        assert int(hdr[8]) == 0, "stream fell back to RAW"
+        assert int(hdr[8]) == (2 if args.coder == "chunk" else 0), "stream fell back to RAW"
     # round-trip property, checked outside the timed region: every value within its bound
     err_max = 0.0
     for i, (x, _, _) in enumerate(items[:4]):
@@ -298,14 +320,23 @@ def main() -> int:
         err_max = max(err_max, e)
     log(f"[bench] eb={ebs[0]:.6g} max|x-x'|={err_max:.6g} outliers(first)={outliers[0]}")
 
-    # algorithmic bytes per launch: encode reads 4n and writes the width bytes and the payload
-    # words; decode reads the width bytes and payload words and writes 4n
+    # algorithmic bytes per launch: encode reads 4n and writes the size section (a width byte per
+    # segment, or a u32 word count per chunk) and the payload words; decode reads them and writes 4n
     avg_payload = float(np.mean(payload))
-    enc_bytes = 4 * n + nseg + avg_payload
-    dec_bytes = nseg + avg_payload + 4 * n
+    if args.coder == "chunk":
+        V = args.chunk_bytes // 4
+        sizes = 4 * ((n + V - 1) // V)
+        kernels = ("chunk_encode_kernel", "chunk_decode_kernel")
+        tag = f"{args.workload}_chunk{args.chunk_bytes}"
+    else:
+        sizes = nseg
+        kernels = ("encode_kernel", "decode_kernel")
+        tag = args.workload
+    enc_bytes = 4 * n + sizes + avg_payload
+    dec_bytes = sizes + avg_payload + 4 * n
     enc_gbps = enc_bytes / (kavg["encode"] * 1e-3) / 1e9
     dec_gbps = dec_bytes / (kavg["decode"] * 1e-3) / 1e9
-    traffic = profiling.read_traffic(os.path.join(PROFILES, f"traffic_{args.workload}.txt"))
+    traffic = profiling.read_traffic(os.path.join(PROFILES, f"traffic_{tag}.txt"))
 
     def roof(name, achieved, kernel_key):
         t = None if traffic is None else traffic.get(kernel_key)
@@ -337,8 +368,8 @@ def main() -> int:
         "compressed_bytes": total_stream,
         "outliers": int(sum(outliers)),
         "kernel_ms": {k: round(v, 5) for k, v in kavg.items()},
-        "roofline": roof("encode", enc_gbps, "encode_kernel"),
-        "roofline_decode": roof("decode", dec_gbps, "decode_kernel"),
+        "roofline": roof(kernels[0], enc_gbps, kernels[0]),
+        "roofline_decode": roof(kernels[1], dec_gbps, kernels[1]),
         "algorithmic_bytes_per_launch": {"encode": round(enc_bytes), "decode": round(dec_bytes)},
         "max_abs_err": err_max,
         "eb": ebs[0],

@@ -59,54 +59,165 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
     return readlane(v, 0) | readlane(v, 16) | readlane(v, 32) | readlane(v, 48);
 }
 
-/* Per-lane constants of the five transpose stages s = 16, 8, 4, 2, 1: the lane keeps the bits
- * of its own word under keep[k] and takes the rest from its partner (lane ^ s) rotated right by
- * rot[k] -- a left rotate by s in the lower lane of the pair, a right rotate in the upper. */
+/* 32 x 32 bit transpose inside each half-wave: on exit bit j of lane 32 h + b is bit b of lane
+ * 32 h + j's word on entry.  Five butterfly stages s = 16, 8, 4, 2, 1 pair lane l with l ^ s;
+ * the lower lane of a pair keeps its bits whose index has bit s clear and takes its partner's
+ * such bits shifted up by s, the upper lane keeps the others and takes its partner's shifted
+ * down.  For s = 16 and 8 both are byte moves, one v_perm_b32 each (selector bytes 0-3 pick
+ * the partner's bytes, 4-7 the lane's own); for s = 4, 2, 1 the partner's word is rotated by
+ * s (v_alignbit) and merged under the stage mask (v_bfi). */
 struct Transpose {
-    uint32_t keep[5], rot[5];
+    uint32_t sel16, sel8, keep[3], rot[3];
     __device__ __forceinline__ explicit Transpose(uint32_t lane) {
-        const uint32_t m[5] = {0x0000FFFFu, 0x00FF00FFu, 0x0F0F0F0Fu, 0x33333333u, 0x55555555u};
+        sel16 = (lane & 16u) ? 0x07060302u : 0x01000504u;
+        sel8 = (lane & 8u) ? 0x07030501u : 0x02060004u;
+        const uint32_t m[3] = {0x0F0F0F0Fu, 0x33333333u, 0x55555555u};
 #pragma unroll
-        for (int k = 0; k < 5; ++k) {
-            const uint32_t s = 16u >> k;
-            const bool lower = (lane & s) == 0;
+        for (int k = 0; k < 3; ++k) {
+            const uint32_t sh = 4u >> k;
+            const bool lower = (lane & sh) == 0;
             keep[k] = lower ? m[k] : ~m[k];
-            rot[k] = lower ? 32u - s : s;
+            rot[k] = lower ? 32u - sh : sh;
         }
     }
-    /* 32 x 32 bit transpose inside each half-wave: on exit bit j of lane 32 h + b is bit b of
-     * lane 32 h + j's word on entry. */
+    /* bits of a under m, of b elsewhere (one v_bfi_b32) */
+    static __device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
+        return b ^ ((a ^ b) & m);
+    }
     __device__ __forceinline__ uint32_t operator()(uint32_t v) const {
         uint32_t p;
         p = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F); /* lane ^ 16 */
-        v = (v & keep[0]) | (__builtin_amdgcn_alignbit(p, p, rot[0]) & ~keep[0]);
+        v = __builtin_amdgcn_perm(v, p, sel16);
         p = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x201F); /* lane ^ 8 */
-        v = (v & keep[1]) | (__builtin_amdgcn_alignbit(p, p, rot[1]) & ~keep[1]);
+        v = __builtin_amdgcn_perm(v, p, sel8);
         p = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F); /* lane ^ 4 */
-        v = (v & keep[2]) | (__builtin_amdgcn_alignbit(p, p, rot[2]) & ~keep[2]);
+        v = bfi(keep[0], v, __builtin_amdgcn_alignbit(p, p, rot[0]));
         p = dpp<kDppQuadXor2>(0, v);                                /* lane ^ 2 */
-        v = (v & keep[3]) | (__builtin_amdgcn_alignbit(p, p, rot[3]) & ~keep[3]);
+        v = bfi(keep[1], v, __builtin_amdgcn_alignbit(p, p, rot[1]));
         p = dpp<kDppQuadXor1>(0, v);                                /* lane ^ 1 */
-        v = (v & keep[4]) | (__builtin_amdgcn_alignbit(p, p, rot[4]) & ~keep[4]);
+        v = bfi(keep[2], v, __builtin_amdgcn_alignbit(p, p, rot[2]));
         return v;
     }
 };
+
+/* q minus the code of the lane to the left (lane 0: carry).  The subtraction must stay apart
+ * from the DPP move: where carry is known to be 0 the compiler folds the pair into one
+ * v_subrev_u32_dpp (wave_shr, bound_ctrl), and on gfx950 that returned the negated difference.
+ * The empty asm hides the moved value from that fold and emits nothing. */
+__device__ __forceinline__ int32_t diff_left(int32_t q, int32_t carry) {
+    uint32_t prev = dpp<kDppWaveShr1>((uint32_t)carry, (uint32_t)q);
+    asm("" : "+v"(prev));
+    return q - (int32_t)prev;
+}
 
 __device__ __forceinline__ float ld_nt_f(const float *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_nt_f(float *p, float v) { __builtin_nontemporal_store(v, p); }
 
 /* ---- K2c: chunk encode ------------------------------------------------------------------------ */
 
+/* Escape bookkeeping of one encode chunk, kept as in the bitpack encoder: the count, a bit per
+ * 256-value tile with an escape, and (lane l) the escape bitmask of 32-value segment l. */
+struct ChunkEsc {
+    uint32_t escs = 0, tmask = 0, emask = 0;
+};
+
+/* Phase 1 of the chunk encoder for one wave's 2048 values: per 64-value tile quantize, take
+ * the first difference (the carry supplies lane 0's predecessor: the previous tile's last code,
+ * 0 at a chunk's first value), zigzag, OR into the chunk's code OR, transpose, and store the
+ * 64 plane words at their plane-major LDS places.  FULL: all 2048 values lie below n. */
+template <int V, bool FULL, bool STRIDED>
+__device__ __forceinline__ void encode_tiles(const float *__restrict__ x, const Layout &lo, uint64_t cbase,
+                                             uint64_t n, const QParams &qp, int32_t carry, uint32_t wave,
+                                             uint32_t (*s_words)[ChunkGeom<V>::LDSW], uint32_t *stage_idx,
+                                             uint32_t *stage_val, uint32_t orz[ChunkGeom<V>::PER_WAVE],
+                                             ChunkEsc &es) {
+    using Gm = ChunkGeom<V>;
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t h = lane >> 5, b = lane & 31;
+    const Transpose tr(lane);
+    float xs[kCTilesPerWave];
+#pragma unroll
+    for (int t = 0; t < kCTilesPerWave; ++t) {
+        const uint64_t i = cbase + (uint64_t)t * kCTile + lane;
+        if (FULL) xs[t] = ld_nt_f(x + elem_off<STRIDED>(lo, i));
+        else xs[t] = i < n ? x[elem_off<STRIDED>(lo, i)] : 0.0f;
+    }
+#pragma unroll
+    for (int t = 0; t < kCTilesPerWave; ++t) {
+        const float xv = xs[t];
+        /* Quant: the bitpack encoder's fast test (exactly the full rule's acceptance), the full
+         * rule in a wave where some lane misses it */
+        const float q0f = rintf(xv * qp.r);
+        const bool fast = (fabsf(xv - q0f * qp.s) <= qp.eb) && (fabsf(q0f) < qp.tlim);
+        int32_t q = (int32_t)q0f;
+        if (__ballot(!fast)) {
+            uint32_t e = 0;
+            if (!fast) q = quantize_slow(xv, q0f, qp, &e);
+            const uint64_t M = __ballot(e != 0);
+            if (M) {
+                es.emask = writelane(es.emask, (uint32_t)M, 2u * t);
+                es.emask = writelane(es.emask, (uint32_t)(M >> 32), 2u * t + 1u);
+                es.tmask |= 1u << (t / 4);
+                const uint32_t r = es.escs + mbcnt64(M);
+                if (e && r < (uint32_t)kEscStage) {
+                    stage_idx[r] = (uint32_t)(cbase + (uint64_t)t * kCTile + lane);
+                    stage_val[r] = __float_as_uint(xv);
+                }
+                es.escs += (uint32_t)__popcll(M);
+            }
+        }
+        /* Diff: lane 0 takes the carry (0 at a chunk start), the others their left neighbour */
+        if (t > 0 && (t * kCTile) % V == 0) carry = 0;
+        uint32_t z = zigzag(diff_left(q, carry));
+        carry = (int32_t)readlane((uint32_t)q, 63);
+        if (!FULL && cbase + (uint64_t)t * kCTile + lane >= n) z = 0; /* padding codes */
+        orz[(t * kCTile) / V] |= z;
+        /* Bitshuffle: lane 32 h + b -> plane b of group (off mod V) / 32 + h */
+        const uint32_t wd = tr(z);
+        const uint32_t off = wave * kEncChunk + (uint32_t)t * kCTile; /* value offset in the group */
+        s_words[off / V][b * Gm::PS + (off & (uint32_t)(V - 1)) / 32u + h] = wd;
+    }
+}
+
+/* RZE of one chunk from its LDS planes into dst: the bitmap (V / 32 words; bit k of word k / 32
+ * set when plane word k is nonzero), then the nonzero words in order.  Planes at and above wmax
+ * are zero and skipped.  Returns the chunk's word count. */
+template <int V>
+__device__ __forceinline__ uint32_t rze_chunk(const uint32_t *pl, uint32_t wmax, uint32_t *dst) {
+    using Gm = ChunkGeom<V>;
+    const uint32_t lane = threadIdx.x & 63;
+    uint32_t bm0 = 0, bm1 = 0; /* lane l: bitmap word l (and 64 + l) */
+    uint32_t run = 0;
+    for (uint32_t pb = 0; pb < wmax; ++pb) {
+#pragma unroll
+        for (int kk = 0; kk < Gm::BATCHES; ++kk) {
+            const uint32_t gi = 64u * kk + lane;
+            const uint32_t word = (Gm::G >= 64 || gi < (uint32_t)Gm::G) ? pl[pb * Gm::PS + gi] : 0u;
+            const uint64_t M = __ballot(word != 0);
+            if (word) dst[Gm::BM + run + mbcnt64(M)] = word;
+            run += (uint32_t)__popcll(M);
+            const uint32_t wi = (pb * Gm::G + 64u * kk) / 32u;
+            if (wi < 64) bm0 = writelane(bm0, (uint32_t)M, wi);
+            else bm1 = writelane(bm1, (uint32_t)M, wi - 64);
+            if (Gm::G >= 64) {
+                if (wi + 1 < 64) bm0 = writelane(bm0, (uint32_t)(M >> 32), wi + 1);
+                else bm1 = writelane(bm1, (uint32_t)(M >> 32), wi + 1 - 64);
+            }
+        }
+    }
+    if (lane < (uint32_t)(Gm::BM < 64 ? Gm::BM : 64)) dst[lane] = bm0;
+    if (Gm::BM > 64) dst[64 + lane] = bm1;
+    return Gm::BM + run;
+}
+
 /* Workgroup of 4 waves over 8192 values; wave w owns the 2048 values of encode chunk c (the
  * unit of the escape bookkeeping and of the scratch slots the compaction copies), which hold
- * 2048 / V coder chunks, or half of one when V = 4096.  Phase 1 (every wave): load 32 values
- * per lane, quantize, difference, zigzag and transpose each tile into the chunk's LDS planes,
- * recording escapes as the bitpack encoder does.  Phase 2 (after a barrier; the wave owning a
- * chunk's first values): RZE of the chunk's planes into the scratch slot -- bitmap, then the
- * nonzero words -- and its word count into the size section (stream or staging).  A wave's
- * chunks lie back to back in its slot, and a 4096-value chunk fills the slots of both its waves
- * (the second reports 0 words), so the compaction's copy of each slot in order yields the chunks
- * in order. */
+ * 2048 / V coder chunks, or half of one when V = 4096.  Phase 1 (every wave): encode_tiles.
+ * Phase 2 (after a barrier; the wave owning a chunk's first values): RZE of the chunk into the
+ * scratch slot and its word count into the size section (stream or staging).  A wave's chunks
+ * lie back to back in its slot, and a 4096-value chunk fills the slots of both its waves (the
+ * second reports 0 words), so the compaction's copy of each slot in order yields the chunks in
+ * order. */
 template <int V, bool STRIDED>
 __global__ __launch_bounds__(kEncThreads) void chunk_encode_kernel(const float *__restrict__ x, PlanArgs pa,
                                                                    Workspace ws, uint8_t *__restrict__ sizes_dst,
@@ -124,7 +235,8 @@ __global__ __launch_bounds__(kEncThreads) void chunk_encode_kernel(const float *
     const DevInfo *info = ws.info;
     const uint64_t n = pa.n;
     const uint64_t cbase = (uint64_t)c * kEncChunk;
-    uint32_t escs = 0, tmask = 0, wsum = 0;
+    ChunkEsc es;
+    uint32_t wsum = 0;
 
     if (info->valid) {  /* the same for every workgroup: the barrier below is uniform */
         QParams qp;
@@ -133,20 +245,6 @@ __global__ __launch_bounds__(kEncThreads) void chunk_encode_kernel(const float *
         qp.r = info->r;
         qp.T = pa.T;
         qp.tlim = (float)(1u << pa.T);
-        const Transpose tr(lane);
-        const bool full = cbase + kEncChunk <= n;
-        float xs[kCTilesPerWave];
-        if (full) {
-#pragma unroll
-            for (int t = 0; t < kCTilesPerWave; ++t)
-                xs[t] = ld_nt_f(x + elem_off<STRIDED>(pa.lay, cbase + (uint64_t)t * kCTile + lane));
-        } else {
-#pragma unroll
-            for (int t = 0; t < kCTilesPerWave; ++t) {
-                const uint64_t i = cbase + (uint64_t)t * kCTile + lane;
-                xs[t] = i < n ? x[elem_off<STRIDED>(pa.lay, i)] : 0.0f;
-            }
-        }
         /* the predecessor of the wave's first value when it does not start a chunk (second half
          * of a 4096-value chunk): the code of the value before it, 0 if that value escapes */
         int32_t carry = 0;
@@ -156,49 +254,15 @@ __global__ __launch_bounds__(kEncThreads) void chunk_encode_kernel(const float *
             const int32_t qprev = quantize_slow(xp, rintf(xp * qp.r), qp, &e);
             carry = e ? 0 : qprev;
         }
-        uint32_t emask = 0;           /* lane l: escape bitmask of 32-value segment l */
         uint32_t orz[Gm::PER_WAVE];
 #pragma unroll
         for (int k = 0; k < Gm::PER_WAVE; ++k) orz[k] = 0;
-        const uint32_t h = lane >> 5, b = lane & 31;
-#pragma unroll
-        for (int t = 0; t < kCTilesPerWave; ++t) {
-            const float xv = xs[t];
-            /* Quant: the fast test of the bitpack encoder (exactly the full rule's acceptance),
-             * the full rule in a wave where some lane misses it */
-            const float q0f = rintf(xv * qp.r);
-            const bool fast = (fabsf(xv - q0f * qp.s) <= qp.eb) && (fabsf(q0f) < qp.tlim);
-            int32_t q = (int32_t)q0f;
-            if (__ballot(!fast)) {
-                uint32_t e = 0;
-                if (!fast) q = quantize_slow(xv, q0f, qp, &e);
-                const uint64_t M = __ballot(e != 0);
-                if (M) {
-                    emask = writelane(emask, (uint32_t)M, 2u * t);
-                    emask = writelane(emask, (uint32_t)(M >> 32), 2u * t + 1u);
-                    tmask |= 1u << (t / 4);
-                    const uint32_t r = escs + mbcnt64(M);
-                    if (e && r < (uint32_t)kEscStage) {
-                        s_stage[wave][0][r] = (uint32_t)(cbase + (uint64_t)t * kCTile + lane);
-                        s_stage[wave][1][r] = __float_as_uint(xv);
-                    }
-                    escs += (uint32_t)__popcll(M);
-                }
-            }
-            /* Diff: first difference, reset at the chunk's first value */
-            const uint32_t off = wave * kEncChunk + (uint32_t)t * kCTile; /* value offset in the group */
-            const bool reset = lane == 0 && (off & (uint32_t)(V - 1)) == 0;
-            const int32_t prev = (int32_t)dpp<kDppWaveShr1>((uint32_t)carry, (uint32_t)q);
-            uint32_t z = zigzag(reset ? q : q - prev);
-            carry = (int32_t)readlane((uint32_t)q, 63);
-            if (!full && cbase + (uint64_t)t * kCTile + lane >= n) z = 0; /* padding codes */
-            orz[(t * kCTile) / V] |= z;
-            /* Bitshuffle: lane 32 h + b -> plane b of group (off mod V) / 32 + h */
-            const uint32_t wd = tr(z);
-            const uint32_t buf = off / V;
-            const uint32_t g = (off & (uint32_t)(V - 1)) / 32u + h;
-            s_words[buf][b * Gm::PS + g] = wd;
-        }
+        if (cbase + kEncChunk <= n)
+            encode_tiles<V, true, STRIDED>(x, pa.lay, cbase, n, qp, carry, wave, s_words, s_stage[wave][0],
+                                           s_stage[wave][1], orz, es);
+        else
+            encode_tiles<V, false, STRIDED>(x, pa.lay, cbase, n, qp, carry, wave, s_words, s_stage[wave][0],
+                                            s_stage[wave][1], orz, es);
 #pragma unroll
         for (int k = 0; k < Gm::PER_WAVE; ++k) {
             const uint32_t o = wave_or(orz[k]);
@@ -206,10 +270,10 @@ __global__ __launch_bounds__(kEncThreads) void chunk_encode_kernel(const float *
         }
         __syncthreads();
 
-        /* RZE by the wave holding each chunk's first values */
         const uint64_t ncv = (n + V - 1) / V;
         if (Gm::WAVES == 1 || (wave & 1u) == 0) {
             uint32_t *slot = ws.scratch + (uint64_t)c * pa.slot;
+            uint32_t *sz = reinterpret_cast<uint32_t *>(sizes_dst);
 #pragma unroll
             for (int k = 0; k < Gm::PER_WAVE; ++k) {
                 const uint64_t cv = (cbase + (uint64_t)k * V) / V;
@@ -217,33 +281,9 @@ __global__ __launch_bounds__(kEncThreads) void chunk_encode_kernel(const float *
                     uint32_t orc = s_or[wave][k];
                     if (Gm::WAVES == 2) orc |= s_or[wave + 1][0];
                     const uint32_t wmax = orc ? 32u - (uint32_t)__builtin_clz(orc) : 0u;
-                    const uint32_t buf = (wave * kEncChunk + (uint32_t)k * V) / V;
-                    const uint32_t *pl = s_words[buf];
-                    uint32_t *dst = slot + wsum;
-                    uint32_t bm0 = 0, bm1 = 0;  /* lane l: bitmap word l (and 64 + l) */
-                    uint32_t run = 0;
-                    for (uint32_t pb = 0; pb < wmax; ++pb) {
-#pragma unroll
-                        for (int kk = 0; kk < Gm::BATCHES; ++kk) {
-                            const uint32_t gi = 64u * kk + lane;
-                            const uint32_t word = (Gm::G >= 64 || gi < (uint32_t)Gm::G) ? pl[pb * Gm::PS + gi] : 0u;
-                            const uint64_t M = __ballot(word != 0);
-                            if (word) dst[Gm::BM + run + mbcnt64(M)] = word;
-                            run += (uint32_t)__popcll(M);
-                            const uint32_t wi = (pb * Gm::G + 64u * kk) / 32u;
-                            if (wi < 64) bm0 = writelane(bm0, (uint32_t)M, wi);
-                            else bm1 = writelane(bm1, (uint32_t)M, wi - 64);
-                            if (Gm::G >= 64) {
-                                if (wi + 1 < 64) bm0 = writelane(bm0, (uint32_t)(M >> 32), wi + 1);
-                                else bm1 = writelane(bm1, (uint32_t)(M >> 32), wi + 1 - 64);
-                            }
-                        }
-                    }
-                    if (lane < (uint32_t)(Gm::BM < 64 ? Gm::BM : 64)) dst[lane] = bm0;
-                    if (Gm::BM > 64) dst[64 + lane] = bm1;
-                    const uint32_t size = Gm::BM + run;
+                    const uint32_t size = rze_chunk<V>(s_words[(wave * kEncChunk + (uint32_t)k * V) / V], wmax,
+                                                       slot + wsum);
                     wsum += size;
-                    uint32_t *sz = reinterpret_cast<uint32_t *>(sizes_dst);
                     if (lane == 0 && 4 * cv < sizes_bytes) sz[cv] = size;
                     if (cv == ncv - 1) {
                         /* zero the size section's pad up to its 16-byte end */
@@ -254,25 +294,25 @@ __global__ __launch_bounds__(kEncThreads) void chunk_encode_kernel(const float *
             }
         }
         if (c < pa.nchunks) {
-            if (lane < escs && lane < (uint32_t)kEscStage) {
+            if (lane < es.escs && lane < (uint32_t)kEscStage) {
                 ws.stage_idx[(uint64_t)c * kEscStage + lane] = s_stage[wave][0][lane];
                 ws.stage_val[(uint64_t)c * kEscStage + lane] = s_stage[wave][1][lane];
             }
-            if (tmask) ws.emask[(uint64_t)c * kEncSegs + lane] = emask;
+            if (es.tmask) ws.emask[(uint64_t)c * kEncSegs + lane] = es.emask;
             if (lane == 0) {
                 ws.chunk_words[c] = wsum;
-                ws.chunk_esc[c] = escs;
-                ws.chunk_tmask[c] = tmask;
+                ws.chunk_esc[c] = es.escs;
+                ws.chunk_tmask[c] = es.tmask;
             }
         }
     }
     if (c >= pa.nchunks) {
         wsum = 0;
-        escs = 0;
+        es.escs = 0;
     }
     if (lane == 0) {
         s_grp[0][wave] = wsum;
-        s_grp[1][wave] = escs;
+        s_grp[1][wave] = es.escs;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -289,13 +329,40 @@ __global__ __launch_bounds__(kEncThreads) void chunk_encode_kernel(const float *
 
 /* ---- K7c: chunk decode ------------------------------------------------------------------------ */
 
+/* Decode tiles [t0, t0 + NT) of a chunk: lane 32 h + b reads plane b of group 2 t + h (planes
+ * at and above wmax are zero), the transpose turns that into one code per lane, then the zigzag
+ * inverse and a wave prefix sum plus the carry (the previous tile's last code) undo the first
+ * difference, and f32(f32(q) * s) is stored.  The NT tiles' transposes and scans are
+ * independent; only the carry chains them. */
+template <int V, int NT, bool FULL, bool STRIDED>
+__device__ __forceinline__ void decode_tiles(const uint32_t *pl, uint32_t t0, uint32_t wmax, const Transpose &tr,
+                                             float s, uint32_t &carry, float *__restrict__ out, const Layout &lo,
+                                             uint32_t cbase, uint32_t n) {
+    using Gm = ChunkGeom<V>;
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t h = lane >> 5, b = lane & 31;
+    uint32_t incl[NT];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+        const uint32_t word = b < wmax ? pl[b * Gm::PS + 2u * (t0 + k) + h] : 0u;
+        incl[k] = wave_incl_scan((uint32_t)unzigzag(tr(word)));
+    }
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+        const uint32_t q = incl[k] + carry;
+        carry = readlane(q, 63);
+        const float y = (float)(int32_t)q * s;
+        const uint32_t i = cbase + (t0 + k) * kCTile + lane;
+        if (FULL || i < n) st_nt_f(out + elem_off<STRIDED>(lo, i), y);
+    }
+}
+
 /* One wave per chunk.  The chunk's bitmap sits in two VGPRs (lane l: bitmap words l and
  * 64 + l); its popcount must equal the chunk's word count minus the bitmap, else the stream is
- * flagged.  Un-RZE rebuilds the planes below the highest nonzero one in LDS (per 64-word batch:
- * the batch's bitmap bits, mbcnt for each present word's position); then per tile lane 32 h + b
- * reads plane b of group 2 t + h, the transpose turns that into one code per lane, and the
- * zigzag inverse, a wave prefix sum plus the previous tile's last code (the first difference
- * undone from the chunk start) and f32(f32(q) * s) give the value. */
+ * flagged.  Un-RZE rebuilds the planes below the highest nonzero one in LDS: per 64-word batch
+ * the batch's bitmap bits and mbcnt give each present word's position in the chunk; all of the
+ * chunk's loads are issued before the first LDS store.  Then decode_tiles, eight tiles at a
+ * time for a full chunk. */
 template <int V, bool STRIDED>
 __global__ __launch_bounds__(kBlockThreads) void chunk_decode_kernel(const uint8_t *__restrict__ in, PlanArgs pa,
                                                                      Workspace ws, float *__restrict__ out) {
@@ -307,13 +374,13 @@ __global__ __launch_bounds__(kBlockThreads) void chunk_decode_kernel(const uint8
     if (c >= pa.dchunks) return;
     DevInfo *info = ws.info;
     if (info->err) return;
-    const uint64_t n = pa.n;
-    const uint64_t cbase = (uint64_t)c * V;
-    const uint64_t cnt = (n - cbase < (uint64_t)V) ? n - cbase : (uint64_t)V;
+    const uint32_t n = (uint32_t)pa.n;
+    const uint32_t cbase = c * (uint32_t)V;
+    const uint32_t cnt = (n - cbase < (uint32_t)V) ? n - cbase : (uint32_t)V;
     if (info->mode == 1) {
         const uint32_t *srcw = reinterpret_cast<const uint32_t *>(in + kHeaderBytes) + cbase;
         uint32_t *ob = reinterpret_cast<uint32_t *>(out);
-        if (!STRIDED && cnt == (uint64_t)V) {
+        if (!STRIDED && cnt == (uint32_t)V) {
             const uint4 *s4 = reinterpret_cast<const uint4 *>(srcw);
             uint4 *d4 = reinterpret_cast<uint4 *>(ob + cbase);
             uint4 t[V / 4 / kWave];
@@ -342,36 +409,47 @@ __global__ __launch_bounds__(kBlockThreads) void chunk_decode_kernel(const uint8
     else if (nz0) top = 63 - __clzll((long long)nz0);
     const uint32_t wmax = top < 0 ? 0u : (uint32_t)top * 32u / Gm::G + 1u;
     uint32_t *pl = s_words[wave];
+    /* un-RZE: every plane's loads first (into registers), then the LDS stores */
+    uint32_t wv[32 * Gm::BATCHES];
     uint32_t run = 0;
-    for (uint32_t pb = 0; pb < wmax; ++pb) {
+#pragma unroll
+    for (int pb = 0; pb < 32; ++pb) {
 #pragma unroll
         for (int kk = 0; kk < Gm::BATCHES; ++kk) {
-            const uint32_t wi = (pb * Gm::G + 64u * kk) / 32u;
-            const uint32_t lo = wi < 64 ? readlane(bm0, (int)wi) : readlane(bm1, (int)(wi - 64));
-            uint32_t hi = 0;
-            if (Gm::G >= 64) hi = wi + 1 < 64 ? readlane(bm0, (int)(wi + 1)) : readlane(bm1, (int)(wi + 1 - 64));
-            const uint64_t M = (uint64_t)lo | ((uint64_t)hi << 32);
-            const bool present = (M >> lane) & 1u;
-            const uint32_t word = present ? blob[Gm::BM + run + mbcnt64(M)] : 0u;
-            const uint32_t gi = 64u * kk + lane;
-            if (Gm::G >= 64 || gi < (uint32_t)Gm::G) pl[pb * Gm::PS + gi] = word;
-            run += (uint32_t)__popcll(M);
+            uint32_t word = 0;
+            if ((uint32_t)pb < wmax) {
+                const uint32_t wi = (pb * Gm::G + 64 * kk) / 32;
+                const uint32_t lo = wi < 64 ? readlane(bm0, (int)wi) : readlane(bm1, (int)(wi - 64));
+                uint32_t hi = 0;
+                if (Gm::G >= 64) hi = wi + 1 < 64 ? readlane(bm0, (int)(wi + 1)) : readlane(bm1, (int)(wi + 1 - 64));
+                const uint64_t M = (uint64_t)lo | ((uint64_t)hi << 32);
+                if ((M >> lane) & 1u) word = blob[Gm::BM + run + mbcnt64(M)];
+                run += (uint32_t)__popcll(M);
+            }
+            wv[pb * Gm::BATCHES + kk] = word;
+        }
+    }
+#pragma unroll
+    for (int pb = 0; pb < 32; ++pb) {
+        if ((uint32_t)pb < wmax) {
+#pragma unroll
+            for (int kk = 0; kk < Gm::BATCHES; ++kk) {
+                const uint32_t gi = 64u * kk + lane;
+                if (Gm::G >= 64 || gi < (uint32_t)Gm::G) pl[pb * Gm::PS + gi] = wv[pb * Gm::BATCHES + kk];
+            }
         }
     }
     wave_lds_sync();
     const Transpose tr(lane);
     const float s = info->dec_s;
-    const uint32_t h = lane >> 5, b = lane & 31;
-    const uint32_t ntiles = (uint32_t)((cnt + kCTile - 1) / kCTile);
     uint32_t carry = 0;
-    for (uint32_t t = 0; t < ntiles; ++t) {
-        const uint32_t word = b < wmax ? pl[b * Gm::PS + 2u * t + h] : 0u;
-        const uint32_t z = tr(word);
-        const uint32_t q = wave_incl_scan((uint32_t)unzigzag(z)) + carry;
-        carry = readlane(q, 63);
-        const float y = (float)(int32_t)q * s;
-        const uint64_t i = cbase + (uint64_t)t * kCTile + lane;
-        if (i < n) st_nt_f(out + elem_off<STRIDED>(pa.lay, i), y);
+    if (cnt == (uint32_t)V) {
+        for (uint32_t t = 0; t < (uint32_t)Gm::TILES; t += 8)
+            decode_tiles<V, 8, true, STRIDED>(pl, t, wmax, tr, s, carry, out, pa.lay, cbase, n);
+    } else {
+        const uint32_t ntiles = (cnt + kCTile - 1) / kCTile;
+        for (uint32_t t = 0; t < ntiles; ++t)
+            decode_tiles<V, 1, false, STRIDED>(pl, t, wmax, tr, s, carry, out, pa.lay, cbase, n);
     }
 }
 

@@ -76,6 +76,19 @@ def test_chunk_several_groups_ragged(env, cb):
 
 
 @pytest.mark.parametrize("cb", CHUNK_BYTES)
+def test_chunk_signed_differences_at_chunk_starts(env, cb):
+    """Codes that step up and down by one in every tile, including each chunk's first tile
+    (where the first difference starts from 0): a sign error in the difference at a chunk start
+    swaps zigzag codes 1 and 2 and changes the stream."""
+    n = 3 * 4096 + 77
+    i = np.arange(n)
+    q = np.where(i % 7 == 3, 1, 0) - np.where(i % 11 == 5, 1, 0)
+    x = q.astype(np.float32)
+    h = check_case(env, x, [n], f"abs=0.5;coder=chunk;chunk_bytes={cb}", f"V={cb // 4}")
+    assert h["mode"] == 2 and h["m"] == 0
+
+
+@pytest.mark.parametrize("cb", CHUNK_BYTES)
 def test_chunk_many_escapes(env, cb):
     """More than 64 escapes in an encode chunk takes the bitmask outlier path."""
     rng = np.random.default_rng(40 + cb)
