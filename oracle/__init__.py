@@ -68,6 +68,12 @@ def lib():
         L.oracle_decompress.restype = i32
         L.oracle_stream_elements.argtypes = [P, u64]
         L.oracle_stream_elements.restype = u64
+        L.oracle_block_means.argtypes = [P, u64, u32, P]
+        L.oracle_block_means.restype = None
+        L.oracle_stream_bytes_centered.argtypes = [u64, u32, u64, u64]
+        L.oracle_stream_bytes_centered.restype = u64
+        L.oracle_compress_ex.argtypes = [P, i32, P, i32, f64, u32, i32, u64, i32, P, u64, P]
+        L.oracle_compress_ex.restype = u64
         L.oracle_bitshuffle.argtypes = [P, u32, P]
         L.oracle_bitshuffle.restype = None
         L.oracle_unbitshuffle.argtypes = [P, u32, P]
@@ -138,8 +144,8 @@ def raw_bytes(n: int) -> int:
 
 
 def compress(x: np.ndarray, dims, rel: bool, eps: float, B: int = 256, T: int = 30,
-             side_max: int | None = None) -> np.ndarray:
-    """Whole compressor; returns the stream as a uint8 array."""
+             side_max: int | None = None, center: bool = False) -> np.ndarray:
+    """Whole compressor; returns the stream as a uint8 array.  center: Lorenzo centering."""
     x = np.ascontiguousarray(x, dtype=np.float32).ravel()
     dims = [int(v) for v in dims]
     n = int(np.prod(dims))
@@ -150,8 +156,8 @@ def compress(x: np.ndarray, dims, rel: bool, eps: float, B: int = 256, T: int = 
     cap = raw_bytes(n)
     out = np.zeros(cap, np.uint8)
     req = np.zeros(1, np.uint64)
-    tot = lib().oracle_compress(_ptr(x), len(dims), _ptr(d), int(rel), float(eps), B, T,
-                                side_max, _ptr(out), cap, _ptr(req))
+    tot = lib().oracle_compress_ex(_ptr(x), len(dims), _ptr(d), int(rel), float(eps), B, T,
+                                   side_max, int(center), _ptr(out), cap, _ptr(req))
     assert tot > 0, "oracle stream larger than the raw bound"
     return out[:tot].copy()
 
@@ -173,6 +179,18 @@ def compress_chunked(x: np.ndarray, dims, rel: bool, eps: float, chunk_values: i
                                         side_max, _ptr(out), cap, _ptr(req))
     assert tot > 0, "oracle stream larger than the raw bound"
     return out[:tot].copy()
+
+
+def block_means(q: np.ndarray, B: int) -> np.ndarray:
+    """Lorenzo centering: each block's mean code, rounded half up."""
+    q = np.ascontiguousarray(q, dtype=np.int32)
+    out = np.zeros((q.size + B - 1) // B, np.int32)
+    lib().oracle_block_means(_ptr(q), q.size, B, _ptr(out))
+    return out
+
+
+def stream_bytes_centered(n: int, B: int, sum_widths: int, m: int) -> int:
+    return int(lib().oracle_stream_bytes_centered(n, B, sum_widths, m))
 
 
 def bitshuffle(z: np.ndarray) -> np.ndarray:

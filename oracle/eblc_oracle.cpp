@@ -214,6 +214,39 @@ uint64_t oracle_stream_bytes(uint64_t n, uint64_t sum_widths, uint64_t m) {
 
 uint64_t oracle_raw_bytes(uint64_t n) { return kHeaderBytes + align16(4 * n); }
 
+/* floor(a / b) for b > 0 (C++ division truncates toward zero). */
+static int64_t floor_div(int64_t a, int64_t b) {
+    int64_t qd = a / b;
+    if ((a % b) != 0 && a < 0) qd -= 1;
+    return qd;
+}
+
+/* Lorenzo centering ("Pipeline Specialization Internals", Inverse declaration, where the
+ * fused inverse excludes centeringActive(): a centered predictor's inverse is not the plain
+ * first-difference one).  Reading: the mean code of each block -- the exact mean of the
+ * block's codes (escaped values count as code 0) rounded half up, mu = floor((2 S + c) /
+ * (2 c)) for c codes summing to S -- is subtracted before the first difference, so the block's
+ * first code is predicted by mu instead of 0 and the other differences are unchanged.  The
+ * means are kept in a means stream (one i32 per block) and added back after the prefix sum. */
+void oracle_block_means(const int32_t *q, uint64_t n, uint32_t B, int32_t *means) {
+    uint64_t nblocks = (n + B - 1) / B;
+    for (uint64_t b = 0; b < nblocks; ++b) {
+        int64_t S = 0;
+        int64_t c = 0;
+        for (uint64_t i = b * B; i < n && i < (b + 1) * B; ++i) {
+            S += q[i];
+            c += 1;
+        }
+        means[b] = (int32_t)floor_div(2 * S + c, 2 * c);
+    }
+}
+
+/* Stream size of the bitpack coder with the optional means section (4 bytes per block). */
+uint64_t oracle_stream_bytes_centered(uint64_t n, uint32_t B, uint64_t sum_widths, uint64_t m) {
+    uint64_t nblocks = (n + B - 1) / B;
+    return oracle_stream_bytes(n, sum_widths, m) + align16(4 * nblocks);
+}
+
 /* Chunk coder, "Bitshuffle" ("Pipeline Specialization Internals", Chunk-cooperative path: a
  * Transform between Diff and the coder).  The chunk's V codes (V a multiple of 32) form
  * G = V / 32 groups of 32; word b * G + g of the output holds bit b of every code of group g,
@@ -326,18 +359,22 @@ static void write_header(uint8_t *out, uint8_t mode, int rank, const uint64_t *d
  * side list as u32 indices plus float values; the order is fixed here by index).  The stream
  * falls back to a raw copy when the bound is unusable, when more values escape than the
  * side list may hold, or when the coded stream would be larger than the raw one (the
- * DevitoComp dummy provider reports the raw size as the maximum compressed size). */
-uint64_t oracle_compress(const float *x, int rank, const uint64_t *dims, int rel, double eps,
-                         uint32_t B, int T, uint64_t side_max,
-                         uint8_t *out, uint64_t cap, uint64_t *required) {
+ * DevitoComp dummy provider reports the raw size as the maximum compressed size).  With
+ * `center`, the block means are taken from the codes (oracle_block_means), every block's first
+ * difference is taken against its mean, the widths follow from those codes, and the means
+ * stream sits between the widths and the payload; header word 68 (flags) is 1. */
+uint64_t oracle_compress_ex(const float *x, int rank, const uint64_t *dims, int rel, double eps,
+                            uint32_t B, int T, uint64_t side_max, int center,
+                            uint8_t *out, uint64_t cap, uint64_t *required) {
     uint64_t n = 1;
     for (int a = 0; a < rank; ++a) n *= dims[a];
     uint64_t nseg = (n + kSeg - 1) / kSeg;
+    uint64_t nblocks = (n + B - 1) / B;
 
     float eb_f = 0.0f, s = 0.0f, r = 0.0f;
     int valid = oracle_resolve_bound(x, n, rel, eps, &eb_f, &s, &r);
 
-    std::vector<int32_t> q, d;
+    std::vector<int32_t> q, d, means;
     std::vector<uint8_t> esc, widths;
     std::vector<uint32_t> z, words;
     std::vector<uint32_t> oidx, oval;
@@ -346,64 +383,73 @@ uint64_t oracle_compress(const float *x, int rank, const uint64_t *dims, int rel
     if (!raw) {
         q.resize(n); d.resize(n); esc.resize(n); z.resize(n); widths.resize(nseg);
         oracle_codes(x, n, eb_f, s, r, T, B, q.data(), esc.data(), d.data(), z.data(), widths.data());
+        if (center) {
+            /* centering: the first difference of each block against the block's mean code */
+            means.resize(nblocks);
+            oracle_block_means(q.data(), n, B, means.data());
+            for (uint64_t b = 0; b < nblocks; ++b) {
+                uint64_t i = b * B;
+                d[i] = (int32_t)((uint32_t)q[i] - (uint32_t)means[b]);
+                z[i] = ((uint32_t)d[i] << 1) ^ (uint32_t)(d[i] >> 31);
+            }
+            for (uint64_t k = 0; k < nseg; ++k) {
+                uint32_t acc = 0;
+                for (uint64_t j = 0; j < kSeg; ++j) {
+                    uint64_t i = k * kSeg + j;
+                    if (i < n) acc |= z[i];
+                }
+                uint32_t w = 0;
+                while (w < 32 && (acc >> w) != 0) ++w;
+                widths[k] = (uint8_t)w;
+            }
+        }
         for (uint64_t k = 0; k < nseg; ++k) sum_w += widths[k];
         words.assign(sum_w, 0u);
         oracle_pack(z.data(), n, widths.data(), words.data());
         for (uint64_t i = 0; i < n; ++i) {
             if (esc[i]) { oidx.push_back((uint32_t)i); oval.push_back(f32_bits(x[i])); }
         }
+        uint64_t coded = center ? oracle_stream_bytes_centered(n, B, sum_w, oidx.size())
+                                : oracle_stream_bytes(n, sum_w, oidx.size());
         if (oidx.size() > side_max) raw = true;
-        else if (oracle_stream_bytes(n, sum_w, oidx.size()) > oracle_raw_bytes(n)) raw = true;
+        else if (coded > oracle_raw_bytes(n)) raw = true;
     }
 
-    uint64_t total = raw ? oracle_raw_bytes(n) : oracle_stream_bytes(n, sum_w, oidx.size());
+    uint64_t m = raw ? 0 : oidx.size();
+    uint64_t msec = (!raw && center) ? align16(4 * nblocks) : 0;
+    uint64_t total = raw ? oracle_raw_bytes(n) : oracle_stream_bytes(n, sum_w, m) + msec;
     if (required) *required = total;
     if (total > cap) return 0;
 
     std::memset(out, 0, total);
-    put_u32(out, 0, kMagic);
-    put_u16(out, 4, kVersion);
-    put_u16(out, 6, kHeaderBytes);
-    put_u8(out, 8, raw ? kModeRaw : kModeLossy);
-    put_u8(out, 9, (uint8_t)rank);
-    put_u8(out, 10, 5);
-    put_u8(out, 11, (uint8_t)T);
-    put_u32(out, 12, B);
-    for (int a = 0; a < 4; ++a) put_u64(out, 16 + 8 * a, a < rank ? dims[a] : 0);
-    put_u64(out, 48, n);
-    put_f32(out, 56, eb_f);
-    put_f32(out, 60, s);
-    put_f32(out, 64, r);
-    put_u32(out, 68, 0);
-    put_u64(out, 88, kHeaderBytes);
     if (raw) {
         uint64_t end = oracle_raw_bytes(n);
-        put_u64(out, 72, 0);
-        put_u64(out, 80, 4 * n);
-        put_u64(out, 96, kHeaderBytes);
-        put_u64(out, 104, end);
-        put_u64(out, 112, end);
-        put_u64(out, 120, end);
+        write_header(out, kModeRaw, rank, dims, n, 5, T, B, eb_f, s, r, 0, 4 * n, kHeaderBytes, end, end, end);
         std::memcpy(out + kHeaderBytes, x, 4 * n);
         return total;
     }
-    uint64_t m = oidx.size();
-    uint64_t payload_off = kHeaderBytes + align16(nseg);
+    uint64_t means_off = kHeaderBytes + align16(nseg);
+    uint64_t payload_off = means_off + msec;
     uint64_t oidx_off = payload_off + align16(4 * sum_w);
     uint64_t oval_off = oidx_off + align16(4 * m);
-    put_u64(out, 72, m);
-    put_u64(out, 80, 4 * sum_w);
-    put_u64(out, 96, payload_off);
-    put_u64(out, 104, oidx_off);
-    put_u64(out, 112, oval_off);
-    put_u64(out, 120, total);
+    write_header(out, kModeLossy, rank, dims, n, 5, T, B, eb_f, s, r, m, 4 * sum_w, payload_off,
+                 oidx_off, oval_off, total);
+    if (center) put_u32(out, 68, 1u);
     for (uint64_t k = 0; k < nseg; ++k) out[kHeaderBytes + k] = widths[k];
+    if (center)
+        for (uint64_t b = 0; b < nblocks; ++b) put_u32(out, means_off + 4 * b, (uint32_t)means[b]);
     for (uint64_t t = 0; t < sum_w; ++t) put_u32(out, payload_off + 4 * t, words[t]);
     for (uint64_t k = 0; k < m; ++k) {
         put_u32(out, oidx_off + 4 * k, oidx[k]);
         put_u32(out, oval_off + 4 * k, oval[k]);
     }
     return total;
+}
+
+uint64_t oracle_compress(const float *x, int rank, const uint64_t *dims, int rel, double eps,
+                         uint32_t B, int T, uint64_t side_max,
+                         uint8_t *out, uint64_t cap, uint64_t *required) {
+    return oracle_compress_ex(x, rank, dims, rel, eps, B, T, side_max, 0, out, cap, required);
 }
 
 /* The chunk-cooperative coder, whole compressor ("Pipeline Specialization Internals",
@@ -506,7 +552,8 @@ static uint64_t check_header(const uint8_t *in, uint64_t len) {
         }
     }
     if (get_u64(in, 48) != n) return 0;
-    if (get_u32(in, 68) != 0 || get_u64(in, 88) != kHeaderBytes) return 0;
+    uint32_t flags = get_u32(in, 68);
+    if (flags > 1 || (flags == 1 && mode != kModeLossy) || get_u64(in, 88) != kHeaderBytes) return 0;
     uint64_t m = get_u64(in, 72), pb = get_u64(in, 80);
     uint64_t po = get_u64(in, 96), oi = get_u64(in, 104), ov = get_u64(in, 112), tot = get_u64(in, 120);
     if (mode == kModeRaw) {
@@ -518,7 +565,8 @@ static uint64_t check_header(const uint8_t *in, uint64_t len) {
         if (m > n || pb % 4 != 0) return 0;
         if (mode == kModeLossy) {
             uint64_t nseg = (n + kSeg - 1) / kSeg;
-            if (pb > 4ull * 32 * nseg || po != kHeaderBytes + align16(nseg)) return 0;
+            uint64_t msec = flags ? align16(4 * ((n + B - 1) / B)) : 0;
+            if (pb > 4ull * 32 * nseg || po != kHeaderBytes + align16(nseg) + msec) return 0;
         } else {
             uint64_t nchunks = (n + B - 1) / B;
             if (pb > 4ull * nchunks * (B + B / 32) || po != kHeaderBytes + align16(4 * nchunks)) return 0;
@@ -607,10 +655,19 @@ int oracle_decompress(const uint8_t *in, uint64_t len, float *out, uint64_t n_ou
     } else {
         if (!widths_to_deltas(in, n, pb, po, d.data())) return ORACLE_CORRUPT;
     }
-    /* undelta: running sum from each block start, then dequantize */
+    /* undelta: running sum from each block start (from the block's mean when the stream is
+     * centered, else from 0), then dequantize */
+    uint32_t flags = get_u32(in, 68);
+    uint64_t means_off = kHeaderBytes + align16((n + kSeg - 1) / kSeg);
     int32_t qprev = 0;
     for (uint64_t i = 0; i < n; ++i) {
-        int32_t qi = (i % B == 0) ? d[i] : (int32_t)((uint32_t)qprev + (uint32_t)d[i]);
+        int32_t qi;
+        if (i % B == 0) {
+            int32_t mu = flags ? (int32_t)get_u32(in, means_off + 4 * (i / B)) : 0;
+            qi = (int32_t)((uint32_t)mu + (uint32_t)d[i]);
+        } else {
+            qi = (int32_t)((uint32_t)qprev + (uint32_t)d[i]);
+        }
         out[i] = dequant(qi, s);
         qprev = qi;
     }

@@ -81,6 +81,18 @@ uint64_t oracle_compress(const float *x, int rank, const uint64_t *dims, int rel
                          uint32_t B, int T, uint64_t side_max,
                          uint8_t *out, uint64_t cap, uint64_t *required);
 
+/* Lorenzo centering: means[b] = floor((2 S + c) / (2 c)) for the c codes of block b summing to
+ * S (the block's mean code rounded half up; escaped values count as 0). */
+void oracle_block_means(const int32_t *q, uint64_t n, uint32_t B, int32_t *means);
+uint64_t oracle_stream_bytes_centered(uint64_t n, uint32_t B, uint64_t sum_widths, uint64_t m);
+
+/* oracle_compress with optional Lorenzo centering (center = 1): each block's first difference
+ * is taken against the block's mean code, and the means follow the widths as one i32 per block
+ * (header flags word = 1). */
+uint64_t oracle_compress_ex(const float *x, int rank, const uint64_t *dims, int rel, double eps,
+                            uint32_t B, int T, uint64_t side_max, int center,
+                            uint8_t *out, uint64_t cap, uint64_t *required);
+
 /* Chunk-cooperative coder steps (V codes per chunk, V a multiple of 32).  Bitshuffle: word
  * b * (V/32) + g of `words` holds bit b of codes 32g .. 32g+31 (code j at bit j).  RZE: out =
  * bitmap of the nonzero words (W/32 words), then those words in order; returns its length.
