@@ -72,7 +72,7 @@ def build_items(name: str, device: str):
 def parse_opts(opts: str, n: int) -> dict:
     """Options string -> the oracle's arguments (library defaults where absent); V is the chunk
     coder's chunk in values, None for the bitpack coder."""
-    o = {"rel": True, "eps": 1e-4, "B": 256, "T": 30, "side_max": min(n, 1 << 23), "V": None}
+    o = {"rel": True, "eps": 1e-4, "B": 256, "T": 30, "side_max": min(n, 1 << 23), "V": None, "center": False}
     for item in opts.split(";"):
         if "=" not in item:
             continue
@@ -89,6 +89,8 @@ def parse_opts(opts: str, n: int) -> dict:
             o["V"] = o["V"] or 2048
         elif k == "chunk_bytes":
             o["V"] = int(v) // 4
+        elif k == "center":
+            o["center"] = v == "1"
     return o
 
 
@@ -139,7 +141,8 @@ def cpu_baseline(items, budget_s: float):
         if o["V"] is not None:
             s = oracle.compress_chunked(xs, sdims, o["rel"], o["eps"], o["V"], o["T"], min(o["side_max"], xs.size))
         else:
-            s = oracle.compress(xs, sdims, o["rel"], o["eps"], o["B"], o["T"], min(o["side_max"], xs.size))
+            s = oracle.compress(xs, sdims, o["rel"], o["eps"], o["B"], o["T"], min(o["side_max"], xs.size),
+                                center=o["center"])
         t1 = time.perf_counter()
         st, _ = oracle.decompress(s)
         t2 = time.perf_counter()
@@ -177,6 +180,8 @@ def main() -> int:
                     help="bitpack: per-segment widths and fixed-length packing; chunk: the chunk-cooperative "
                          "coder (Quant, Diff, Bitshuffle, RZE)")
     ap.add_argument("--chunk-bytes", type=int, default=8192, choices=[4096, 8192, 16384])
+    ap.add_argument("--center", action="store_true",
+                    help="Lorenzo centering (bitpack coder): each block's first code against its mean")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device to device once (counter calibration)")
     args = ap.parse_args()
@@ -195,6 +200,11 @@ def main() -> int:
     log(f"[bench] generating workload {args.workload}")
     items, desc = build_items(args.workload, dev)
     items = [(x.contiguous(), dims, opts) for x, dims, opts in items]
+    if args.center and args.coder == "chunk":
+        raise SystemExit("--center applies to the bitpack coder only")
+    if args.center:
+        items = [(x, dims, opts + ";center=1") for x, dims, opts in items]
+        desc += "; Lorenzo centering (block means)"
     if args.coder == "chunk":
         items = [(x, dims, with_chunk_coder(opts, args.chunk_bytes)) for x, dims, opts in items]
         desc = desc.replace(", block 128", "").replace(", block 256", "").replace(", block 32", "")
@@ -332,6 +342,10 @@ def main() -> int:
         sizes = nseg
         kernels = ("encode_kernel", "decode_kernel")
         tag = args.workload
+        if args.center:
+            B = int(parse_opts(opts0, n)["B"])
+            sizes += 4 * ((n + B - 1) // B)   # the means stream
+            tag += "_center"
     enc_bytes = 4 * n + sizes + avg_payload
     dec_bytes = sizes + avg_payload + 4 * n
     enc_gbps = enc_bytes / (kavg["encode"] * 1e-3) / 1e9

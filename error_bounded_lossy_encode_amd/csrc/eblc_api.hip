@@ -94,6 +94,7 @@ struct Options {
     bool side_set = false;
     uint64_t side_max = 0;
     bool chunk_coder = false;   /* coder=chunk: Quant -> Diff -> Bitshuffle -> RZE */
+    bool center = false;        /* center=1: Lorenzo centering (bitpack coder) */
     uint32_t V = 0;             /* chunk coder: values per chunk */
 };
 
@@ -111,6 +112,7 @@ eblc_status parse_options(const char *opts, Options *o) {
         return EBLC_OK;
     }
     bool seen_eb = false, seen_block = false, seen_t = false, seen_coder = false, seen_chunk = false;
+    bool seen_center = false;
     uint64_t chunk_bytes = 8192;
     size_t pos = 0;
     for (;;) {
@@ -143,6 +145,10 @@ eblc_status parse_options(const char *opts, Options *o) {
                 if (seen_coder || (val != "bitpack" && val != "chunk")) return EBLC_INVALID_ARGUMENT;
                 seen_coder = true;
                 o->chunk_coder = val == "chunk";
+            } else if (key == "center") {
+                if (seen_center || (val != "0" && val != "1")) return EBLC_INVALID_ARGUMENT;
+                seen_center = true;
+                o->center = val == "1";
             } else if (key == "chunk_bytes") {
                 if (seen_chunk || !parse_u64(val, &chunk_bytes) ||
                     (chunk_bytes != 4096 && chunk_bytes != 8192 && chunk_bytes != 16384))
@@ -161,7 +167,7 @@ eblc_status parse_options(const char *opts, Options *o) {
     }
     /* the chunk is the chunk coder's reset period: no block with it, no chunk without it */
     if (o->chunk_coder) {
-        if (seen_block) return EBLC_INVALID_ARGUMENT;
+        if (seen_block || o->center) return EBLC_INVALID_ARGUMENT;
         o->V = (uint32_t)(chunk_bytes / 4);
         o->B = o->V;
     } else if (seen_chunk) {
@@ -380,6 +386,10 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
         pa.wsec = align_up(pa.nseg, 16);
     }
     pa.dgroups = (pa.dchunks + kDecChunksPerGroup - 1) / kDecChunksPerGroup;
+    pa.center = o.center ? 1u : 0u;
+    pa.log2B = (uint32_t)__builtin_ctz(pa.B);
+    pa.nblocks = (n + pa.B - 1) / pa.B;
+    pa.msec = o.center ? align_up(4 * pa.nblocks, 16) : 0;
     pa.side_max = o.side_max;
     pa.lay = lay;
 
@@ -402,6 +412,7 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     const uint64_t o_wd = carve(nc * kEncSegs);
     const uint64_t o_si = carve(nc * kEscStage * 4), o_sv = carve(nc * kEscStage * 4);
     const uint64_t o_rp = carve(2 * (uint64_t)range_blocks(n) * 4);
+    const uint64_t o_mu = carve(pa.nblocks * 4);
     if (hipMalloc(&p->ws_base, off) != hipSuccess) {
         delete p;
         return EBLC_OUT_OF_MEMORY;
@@ -422,6 +433,7 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     ws.stage_idx = reinterpret_cast<uint32_t *>(b + o_si);
     ws.stage_val = reinterpret_cast<uint32_t *>(b + o_sv);
     ws.range_part = reinterpret_cast<float *>(b + o_rp);
+    ws.means = reinterpret_cast<int32_t *>(b + o_mu);
 
     if (hipHostMalloc(reinterpret_cast<void **>(&p->host_result), sizeof(eblc_result_t), hipHostMallocDefault) != hipSuccess) {
         (void)hipFree(p->ws_base);

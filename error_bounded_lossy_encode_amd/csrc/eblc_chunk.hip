@@ -25,7 +25,6 @@ namespace {
 
 constexpr int kCTile = 64;                     /* values per tile: one per lane */
 constexpr int kCTilesPerWave = kEncChunk / kCTile;
-constexpr int kDppRowMirror = 0x140;
 
 template <int V>
 struct ChunkGeom {

@@ -24,6 +24,7 @@ constexpr int kDppRowShr2 = 0x112;
 constexpr int kDppRowShr4 = 0x114;
 constexpr int kDppRowShr8 = 0x118;
 constexpr int kDppWaveShr1 = 0x138;
+constexpr int kDppRowMirror = 0x140;
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowBcast15 = 0x142;
 constexpr int kDppRowBcast31 = 0x143;

@@ -65,7 +65,7 @@ struct DevInfo {
     uint32_t mode;          /* 0 bitpack coder, 1 raw, 2 chunk coder */
     uint32_t err;           /* decompress: this call's stream is corrupt */
     uint32_t sticky;        /* OR of err over calls since eblc_plan_status */
-    uint32_t reserved0;
+    uint32_t dec_flags;     /* decompress: the stream's flags word (bit 0: centered) */
     uint32_t width_bad;     /* decompress: a width byte above 32 was seen */
     uint32_t fits;          /* compress: total <= out_capacity */
     uint64_t m;
@@ -105,6 +105,10 @@ struct PlanArgs {
     uint32_t slot;          /* scratch words per encode chunk: 2048, or 2112 for the chunk coder */
     uint32_t wpg;           /* bytes of the size section per encode group */
     uint64_t wsec;          /* bytes of the size section: align16(nseg), or align16(4 chunks) */
+    uint32_t center;        /* Lorenzo centering: each block's first code predicted by its mean */
+    uint32_t log2B;         /* log2 of B */
+    uint64_t nblocks;       /* ceil(n / B) */
+    uint64_t msec;          /* bytes of the means section on compress: align16(4 nblocks), or 0 */
     uint32_t nchunks;       /* encode chunks */
     uint32_t ngroups;       /* encode groups */
     uint32_t dchunks;       /* decode chunks (the coder's chunks for the chunk coder) */
@@ -129,6 +133,7 @@ struct Workspace {
     uint32_t *stage_val;     /* [nchunks * kEscStage] ... and raw value bits, in index order */
     uint8_t *widths;         /* [nchunks * kEncSegs] size section staging when the output is too small */
     float *range_part;       /* [2 * range_blocks(n)] per-block min / max */
+    int32_t *means;          /* [nblocks] block means of a centered compress */
 };
 
 /* Workgroups of the range pass: one per kRangeSpan float4 (16384 values), at least one. */

@@ -171,7 +171,8 @@ __device__ __forceinline__ uint32_t code_tile(const float xs[kEncLaneVals], uint
                                               const QParams &qp, bool reset, int t,
                                               uint32_t *emask_tile, uint32_t *stage_idx,
                                               uint32_t *stage_val, int32_t &carry,
-                                              uint32_t z[kEncLaneVals], EncState &st) {
+                                              uint32_t z[kEncLaneVals], EncState &st,
+                                              uint32_t &slo, int32_t &shi) {
     constexpr int V = kEncLaneVals;
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t j = lane & (kSegLanes - 1);
@@ -231,6 +232,14 @@ __device__ __forceinline__ uint32_t code_tile(const float xs[kEncLaneVals], uint
             st.tmask |= 1u << t;
         }
     }
+    /* the lane's code sum in two exact halves (low 16 bits, and the rest), for centering */
+    slo = 0;
+    shi = 0;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        slo += (uint32_t)q[k] & 0xFFFFu;
+        shi += q[k] >> 16;
+    }
     const int32_t prev = (int32_t)dpp<kDppWaveShr1>((uint32_t)carry, (uint32_t)q[V - 1]);
     z[0] = zigzag(reset ? q[0] : q[0] - prev);
 #pragma unroll
@@ -280,15 +289,59 @@ __device__ __forceinline__ void pack_lane(const uint32_t z[kEncLaneVals], uint32
     }
 }
 
+/* Bit width of the segment (kSegLanes lanes) holding a lane's codes. */
+__device__ __forceinline__ uint32_t seg_width(const uint32_t z[kEncLaneVals]) {
+    uint32_t orv = z[0];
+#pragma unroll
+    for (int k = 1; k < kEncLaneVals; ++k) orv |= z[k];
+    orv = seg_or(orv);
+    return orv ? 32u - (uint32_t)__builtin_clz(orv) : 0u;
+}
+
+/* Sum over aligned groups of seglen lanes (8, 16, 32 or 64), returned in every lane of the
+ * group: DPP butterflies inside rows, ds_swizzle across the two rows of a half, readlane across
+ * the halves. */
+__device__ __forceinline__ uint32_t seg_allsum(uint32_t v, uint32_t seglen) {
+    v += dpp<kDppQuadXor1>(0, v);
+    v += dpp<kDppQuadXor2>(0, v);
+    v += dpp<kDppRowHalfMirror>(0, v);
+    if (seglen >= 16) v += dpp<kDppRowMirror>(0, v);
+    if (seglen >= 32) v += (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+    if (seglen >= 64) v = readlane(v, 0) + readlane(v, 32);
+    return v;
+}
+
+/* Lorenzo centering: the mean of a block's c codes rounded half up, floor((2 S + c) / (2 c)),
+ * from S = hi * 2^16 + lo; a shift when the block is whole (c = 2^log2B).  block_mean32 is the
+ * same for |S| < 2^29 (codes below 2^T with T + log2 B <= 29), in 32-bit arithmetic. */
+__device__ __forceinline__ int32_t block_mean32(int32_t S, uint32_t c, uint32_t log2B) {
+    const int32_t num = 2 * S + (int32_t)c;
+    if (c == (1u << log2B)) return num >> (log2B + 1);
+    const int32_t den = 2 * (int32_t)c;
+    int32_t qd = num / den;
+    if ((num % den) != 0 && num < 0) qd -= 1;
+    return qd;
+}
+
+__device__ __forceinline__ int32_t block_mean(uint32_t lo, int32_t hi, uint64_t c, uint32_t log2B) {
+    const int64_t num = 2 * ((int64_t)hi * 65536 + (int64_t)lo) + (int64_t)c;
+    if (c == (1ull << log2B)) return (int32_t)(num >> (log2B + 1));
+    const int64_t den = 2 * (int64_t)c;
+    int64_t qd = num / den;
+    if ((num % den) != 0 && num < 0) qd -= 1;
+    return (int32_t)qd;
+}
+
 /* One encode chunk of kEncTiles tiles.  Pass 1 codes every tile and records the segment widths
  * in LDS (the codes stay in VGPRs); one wave scan of the widths gives every segment's word
  * offset in the chunk; pass 2 packs each tile at those offsets.  `carry` is the code of the
  * value before the chunk when the chunk does not start a Lorenzo block. */
-template <bool FULL, bool STRIDED>
+template <bool FULL, bool STRIDED, bool CENTER>
 __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const Layout &lo, uint64_t cbase, uint64_t n,
                                              const QParams &qp, uint32_t bmask, int32_t carry,
                                              uint32_t *pay, uint8_t *wid, uint32_t *emask_chunk,
-                                             uint32_t *stage_idx, uint32_t *stage_val, EncState &st) {
+                                             uint32_t *stage_idx, uint32_t *stage_val, EncState &st,
+                                             uint32_t log2B, int32_t *__restrict__ means, bool narrow) {
     constexpr int V = kEncLaneVals;
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t j = lane & (kSegLanes - 1), g = lane / kSegLanes;
@@ -315,14 +368,77 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
     const bool lane_at_block = ((V * lane) & bmask) == 0;
     uint32_t z[kEncTiles][V];
     uint32_t w[kEncTiles];
+    /* Lorenzo centering: a block's first code was coded against 0 (z = zigzag(q)); it is
+     * recoded against the block's mean code, which goes to the means staging, and the segment
+     * widths follow.  Blocks lie inside the chunk (B <= 2048).  A block of at most one tile is
+     * finished with its tile; a longer one keeps its tiles' wave-uniform code sums until the
+     * tile loop ends. */
+    const uint32_t B = bmask + 1;
+    const bool in_tile = B <= (uint32_t)kEncTile;
+    uint32_t tlo[kEncTiles];
+    int32_t thi[kEncTiles];
 #pragma unroll
     for (int t = 0; t < kEncTiles; ++t) {
+        tlo[t] = 0;
+        thi[t] = 0;
         if (FULL || (uint32_t)t < ntiles) {
             const bool reset = lane_at_block && (((uint32_t)cbase + (uint32_t)t * kEncTile) & bmask) == 0;
+            uint32_t slo;
+            int32_t shi;
             w[t] = code_tile<FULL>(xs[t], cbase + (uint64_t)t * kEncTile + V * lane, n, qp, reset, t,
                                    emask_chunk + t * kSegsPerEncTile, stage_idx, stage_val, carry, z[t],
-                                   st);
+                                   st, slo, shi);
+            if (CENTER && in_tile) {
+                const uint32_t seglen = B / V; /* lanes per block */
+                /* narrow codes: one exact 32-bit sum; else the two halves */
+                uint32_t lo_s, hi_s = 0;
+                if (narrow) {
+                    lo_s = seg_allsum(slo + ((uint32_t)shi << 16), seglen);
+                } else {
+                    lo_s = seg_allsum(slo, seglen);
+                    hi_s = seg_allsum((uint32_t)shi, seglen);
+                }
+                const uint64_t e0 = cbase + (uint64_t)t * kEncTile + V * lane;
+                if (lane_at_block && e0 < n) {
+                    const uint64_t c = (n - e0 < (uint64_t)B) ? n - e0 : (uint64_t)B;
+                    const int32_t mu = narrow ? block_mean32((int32_t)lo_s, (uint32_t)c, log2B)
+                                              : block_mean(lo_s, (int32_t)hi_s, c, log2B);
+                    z[t][0] = zigzag((int32_t)((uint32_t)unzigzag(z[t][0]) - (uint32_t)mu));
+                    means[e0 >> log2B] = mu;
+                }
+                w[t] = seg_width(z[t]);
+            } else if (CENTER) {
+                tlo[t] = seg_allsum(slo, 64);
+                thi[t] = (int32_t)seg_allsum((uint32_t)shi, 64);
+            }
             if (j == 0) wid[t * kSegsPerEncTile + g] = (uint8_t)w[t];
+        }
+    }
+    if (CENTER && !in_tile) {
+        /* blocks of B / 256 tiles: each block's sum from its tiles' totals, at its first tile */
+        const uint32_t tpb = B / kEncTile;
+#pragma unroll
+        for (int t = 0; t < kEncTiles; ++t) {
+            const uint64_t bstart = cbase + (uint64_t)t * kEncTile;
+            if (((uint32_t)(t * kEncTile) & bmask) == 0 && bstart < n) {
+                uint32_t lo_s = 0;
+                int32_t hi_s = 0;
+#pragma unroll
+                for (int t2 = t; t2 < kEncTiles; ++t2) {
+                    if ((uint32_t)t2 < (uint32_t)t + tpb) {
+                        lo_s += tlo[t2];
+                        hi_s += thi[t2];
+                    }
+                }
+                const uint64_t c = (n - bstart < (uint64_t)B) ? n - bstart : (uint64_t)B;
+                const int32_t mu = block_mean(lo_s, hi_s, c, log2B);
+                if (lane == 0) {
+                    z[t][0] = zigzag((int32_t)((uint32_t)unzigzag(z[t][0]) - (uint32_t)mu));
+                    means[bstart >> log2B] = mu;
+                }
+                w[t] = seg_width(z[t]);
+                if (j == 0) wid[t * kSegsPerEncTile + g] = (uint8_t)w[t];
+            }
         }
     }
     wave_lds_sync();
@@ -344,7 +460,7 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
  * words in its scratch slot, its width bytes (into the stream, or into staging when the output
  * buffer cannot hold them), its word and escape counts and the escape bitmask of every tile
  * with an escape; per workgroup, the sums the device-wide scan runs over. */
-template <bool STRIDED>
+template <bool STRIDED, bool CENTER>
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(
     const float *__restrict__ x, PlanArgs pa, Workspace ws, uint8_t *__restrict__ widths_dst,
     uint64_t widths_bytes) {
@@ -375,6 +491,8 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
         wave_lds_sync();
         const uint64_t cbase = (uint64_t)c * kEncChunk;
         const uint32_t bmask = pa.B - 1;
+        /* centering: a block's code sum fits 32 bits (|S| < 2^29) when codes stay below 2^T */
+        const bool narrow = pa.T + pa.log2B <= 29;
         /* Lorenzo predecessor of the chunk's first value: 0 at a block start, else the code of
          * the value before the chunk (0 if that value escapes) */
         int32_t carry = 0;
@@ -388,11 +506,11 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
         uint32_t *stage_idx = s_stage[wave][0];
         uint32_t *stage_val = s_stage[wave][1];
         if (cbase + kEncChunk <= pa.n)
-            encode_chunk<true, STRIDED>(x, pa.lay, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk,
-                                        stage_idx, stage_val, st);
+            encode_chunk<true, STRIDED, CENTER>(x, pa.lay, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk,
+                                                stage_idx, stage_val, st, pa.log2B, ws.means, narrow);
         else
-            encode_chunk<false, STRIDED>(x, pa.lay, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk,
-                                         stage_idx, stage_val, st);
+            encode_chunk<false, STRIDED, CENTER>(x, pa.lay, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk,
+                                                 stage_idx, stage_val, st, pa.log2B, ws.means, narrow);
         wave_lds_sync();
         /* chunk payload -> scratch slot, widths -> stream (or staging) */
         uint4 *dst = reinterpret_cast<uint4 *>(ws.scratch + cbase);
@@ -528,7 +646,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_compress_kernel(PlanArgs pa
         const uint64_t n = pa.n;
         const uint64_t S = tot[0], m = tot[1];
         const uint64_t raw_total = kHeaderBytes + align16(4 * n);
-        const uint64_t payload_off = kHeaderBytes + pa.wsec;
+        const uint64_t payload_off = kHeaderBytes + pa.wsec + pa.msec;
         const uint64_t lossy_total = payload_off + align16(4 * S) + 2 * align16(4 * m);
         const bool valid = info->valid != 0;
         const bool raw = !valid || m > pa.side_max || lossy_total > raw_total;
@@ -572,7 +690,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_compress_kernel(PlanArgs pa
         h[14] = __float_as_uint(info->eb_f);
         h[15] = __float_as_uint(info->s);
         h[16] = __float_as_uint(info->r);
-        h[17] = 0;
+        h[17] = (!raw && pa.center) ? 1u : 0u; /* flags: bit 0 = centered */
         for (int a = 2; a < 8; ++a) {
             h[18 + 2 * (a - 2)] = (uint32_t)u64s[a];
             h[19 + 2 * (a - 2)] = (uint32_t)(u64s[a] >> 32);
@@ -737,6 +855,16 @@ __global__ __launch_bounds__(kBlockThreads) void compact_kernel(const float *__r
         if (tid < pa.wpg / 4 && off < pa.wsec)
             *reinterpret_cast<uint32_t *>(out + kHeaderBytes + off) = *reinterpret_cast<const uint32_t *>(widths_src + off);
     }
+    if (pa.center) {
+        /* the group's block means, staged by the encoder, into the means section */
+        const uint32_t mpg = (uint32_t)(CPG * kEncChunk) >> pa.log2B;
+        int32_t *mdst = reinterpret_cast<int32_t *>(out + kHeaderBytes + pa.wsec);
+        for (uint32_t k = tid; k < mpg; k += kBlockThreads) {
+            const uint64_t b = (uint64_t)grp * mpg + k;
+            if (b < pa.nblocks) mdst[b] = ws.means[b];
+        }
+        if (last && tid < (pa.msec - 4 * pa.nblocks) / 4) mdst[pa.nblocks + tid] = 0;
+    }
     if (last) {
         const uint64_t pend = payload_off + 4 * payload_words;
         const uint64_t pad = oidx_off - pend;
@@ -825,7 +953,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_decompress_kernel(const uin
     else if (pa.V == 0) ok = ok && mode == 0 && bitpack_params;
     else ok = ok && mode == 2 && chunk_params && B == pa.V;
     for (int a = 0; a < 4; ++a) ok = ok && ld64(hw, 4 + 2 * a) == pa.dims[a];
-    ok = ok && ld64(hw, 12) == n && hw[17] == 0 && ld64(hw, 22) == kHeaderBytes;
+    const uint32_t flags = hw[17];
+    ok = ok && ld64(hw, 12) == n && flags <= 1 && (flags == 0 || mode == 0) && ld64(hw, 22) == kHeaderBytes;
     const uint64_t m = ld64(hw, 18), pb = ld64(hw, 20), po = ld64(hw, 24), oi = ld64(hw, 26);
     const uint64_t ov = ld64(hw, 28), total = ld64(hw, 30);
     const float eb_f = __uint_as_float(hw[14]), s = __uint_as_float(hw[15]);
@@ -835,7 +964,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_decompress_kernel(const uin
     } else {
         ok = ok && eb_f >= FLT_MIN && eb_f <= FLT_MAX && fabsf(s) <= FLT_MAX && s == 2.0f * eb_f;
         ok = ok && m <= n && (pb & 3) == 0 && pb == 4 * (uint64_t)tot[0] && info->width_bad == 0;
-        ok = ok && po == kHeaderBytes + pa.wsec && oi == po + align16(pb);
+        const uint64_t msec = (flags && B) ? align16(4 * ((n + B - 1) / B)) : 0;
+        ok = ok && po == kHeaderBytes + pa.wsec + msec && oi == po + align16(pb);
         ok = ok && ov == oi + align16(4 * m) && total == ov + align16(4 * m);
     }
     ok = ok && total <= in_bytes;
@@ -850,14 +980,86 @@ __global__ __launch_bounds__(kScanThreads) void scan_decompress_kernel(const uin
     info->oval_off = ov;
     info->dec_s = s;
     info->dec_B = B;
+    info->dec_flags = flags;
 }
 
 /* ---- K7: fused decode ------------------------------------------------------------------------ */
 
-/* One wave per chunk: stage the chunk's packed words in LDS (128-bit loads), then per tile
- * unpack each lane's 4 values, undo the zigzag, prefix-sum inside each block (in-lane, then a
- * segmented DPP scan across lanes, plus the carry from the previous tile when a block spans
- * tiles), dequantize with f32(f32(q) * s) and store 4 values with one 128-bit store. */
+/* The tile loop of one decode chunk whose packed words and segment widths are staged in LDS:
+ * per tile unpack each lane's 4 values, undo the zigzag, prefix-sum inside each block (in-lane,
+ * then a segmented DPP scan across lanes, plus the carry from the previous tile when a block
+ * spans tiles; CENTERED: plus the block's mean code at its start), dequantize with
+ * f32(f32(q) * s) and store 4 values with one 128-bit store. */
+template <bool STRIDED, bool CENTERED>
+__device__ __forceinline__ void decode_tiles(const uint8_t *__restrict__ in, const PlanArgs &pa, const DevInfo *info,
+                                             const uint32_t *pay, const uint32_t *s_w, const uint32_t *s_so,
+                                             uint32_t lb, uint64_t cbase, bool full, float *__restrict__ out) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint64_t n = pa.n;
+    const float s = info->dec_s;
+    const uint32_t B = info->dec_B; /* the stream's block, validated by the header check */
+    const uint32_t log2B = (uint32_t)__builtin_ctz(B);
+    const int32_t *means = reinterpret_cast<const int32_t *>(in + kHeaderBytes + pa.wsec);
+    const uint32_t seglen = (B / 4 < 64u) ? B / 4 : 64u;
+    const uint32_t dist = lane & (seglen - 1);
+    const uint32_t ntiles = full ? kDecTiles : (uint32_t)((n - cbase + kTile - 1) / kTile);
+    const uint32_t j = lane & 7;
+    int32_t carry = 0;
+    /* a centered stream's blocks start from their mean code: each tile's means, loaded up front
+     * (lanes past n read nothing: their blocks' means may lie past the stream's end) */
+    int32_t mu[kDecTiles];
+#pragma unroll
+    for (int t = 0; t < kDecTiles; ++t) {
+        const uint64_t ev = cbase + (uint64_t)t * kTile + 4 * lane;
+        const bool starts = (((uint32_t)t * kTile) & (B - 1)) == 0;
+        mu[t] = (CENTERED && starts && ev < n) ? means[ev >> log2B] : 0;
+    }
+#pragma unroll
+    for (int t = 0; t < kDecTiles; ++t) {
+        if ((uint32_t)t < ntiles) {
+            const uint32_t g = (uint32_t)t * 8 + (lane >> 3);
+            const uint32_t w = s_w[g];
+            const uint32_t bp = 32u * (lb + s_so[g]) + 4u * w * j;
+            const uint32_t mask = w >= 32 ? 0xffffffffu : ((1u << w) - 1u);
+            int32_t cs[4];
+            int32_t run = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t pos = bp + (uint32_t)k * w;
+                const uint32_t wi = pos >> 5;
+                const uint64_t pair = (uint64_t)pay[wi] | ((uint64_t)pay[wi + 1] << 32);
+                const uint32_t z = (uint32_t)(pair >> (pos & 31u)) & mask;
+                run += unzigzag(z);
+                cs[k] = run;
+            }
+            const uint32_t incl = wave_seg_scan((uint32_t)cs[3], dist, seglen);
+            const bool open = (((uint32_t)t * kTile) & (B - 1)) != 0;
+            int32_t base = (int32_t)(incl - (uint32_t)cs[3]) + (open ? carry : 0);
+            if (CENTERED) base += mu[t];
+            int32_t q[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) q[k] = base + cs[k];
+            carry = (int32_t)readlane((uint32_t)q[3], 63);
+            float4 o;
+            o.x = (float)q[0] * s;
+            o.y = (float)q[1] * s;
+            o.z = (float)q[2] * s;
+            o.w = (float)q[3] * s;
+            const uint64_t e0 = cbase + (uint64_t)t * kTile + 4 * lane;
+            if (full) {
+                store4<STRIDED>(out, pa.lay, e0, o);
+            } else {
+                if (e0 + 0 < n) out[elem_off<STRIDED>(pa.lay, e0 + 0)] = o.x;
+                if (e0 + 1 < n) out[elem_off<STRIDED>(pa.lay, e0 + 1)] = o.y;
+                if (e0 + 2 < n) out[elem_off<STRIDED>(pa.lay, e0 + 2)] = o.z;
+                if (e0 + 3 < n) out[elem_off<STRIDED>(pa.lay, e0 + 3)] = o.w;
+            }
+        }
+    }
+}
+
+/* One wave per chunk: stage the chunk's packed words in LDS (128-bit loads) and its segment
+ * widths and word offsets, then decode_tiles (the centered copy for a centered stream). */
 template <bool STRIDED>
 __global__ __launch_bounds__(kBlockThreads) void decode_kernel(const uint8_t *__restrict__ in,
                                                                PlanArgs pa, Workspace ws,
@@ -911,54 +1113,11 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(const uint8_t *__
     wave_lds_sync();
 
     const uint32_t *pay = reinterpret_cast<const uint32_t *>(s_pay4[wave]);
-    const float s = info->dec_s;
-    const uint32_t B = info->dec_B; /* the stream's block, validated by the header check */
-    const uint32_t seglen = (B / 4 < 64u) ? B / 4 : 64u;
-    const uint32_t dist = lane & (seglen - 1);
-    const uint32_t ntiles = full ? kDecTiles : (uint32_t)((n - cbase + kTile - 1) / kTile);
-    const uint32_t j = lane & 7;
-    int32_t carry = 0;
-#pragma unroll
-    for (int t = 0; t < kDecTiles; ++t) {
-        if ((uint32_t)t < ntiles) {
-            const uint32_t g = (uint32_t)t * 8 + (lane >> 3);
-            const uint32_t w = s_w[wave][g];
-            const uint32_t bp = 32u * (lb + s_so[wave][g]) + 4u * w * j;
-            const uint32_t mask = w >= 32 ? 0xffffffffu : ((1u << w) - 1u);
-            int32_t cs[4];
-            int32_t run = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t pos = bp + (uint32_t)k * w;
-                const uint32_t wi = pos >> 5;
-                const uint64_t pair = (uint64_t)pay[wi] | ((uint64_t)pay[wi + 1] << 32);
-                const uint32_t z = (uint32_t)(pair >> (pos & 31u)) & mask;
-                run += unzigzag(z);
-                cs[k] = run;
-            }
-            const uint32_t incl = wave_seg_scan((uint32_t)cs[3], dist, seglen);
-            const bool open = (((uint32_t)t * kTile) & (B - 1)) != 0;
-            const int32_t base = (int32_t)(incl - (uint32_t)cs[3]) + (open ? carry : 0);
-            int32_t q[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) q[k] = base + cs[k];
-            carry = (int32_t)readlane((uint32_t)q[3], 63);
-            float4 o;
-            o.x = (float)q[0] * s;
-            o.y = (float)q[1] * s;
-            o.z = (float)q[2] * s;
-            o.w = (float)q[3] * s;
-            const uint64_t e0 = cbase + (uint64_t)t * kTile + 4 * lane;
-            if (full) {
-                store4<STRIDED>(out, pa.lay, e0, o);
-            } else {
-                if (e0 + 0 < n) out[elem_off<STRIDED>(pa.lay, e0 + 0)] = o.x;
-                if (e0 + 1 < n) out[elem_off<STRIDED>(pa.lay, e0 + 1)] = o.y;
-                if (e0 + 2 < n) out[elem_off<STRIDED>(pa.lay, e0 + 2)] = o.z;
-                if (e0 + 3 < n) out[elem_off<STRIDED>(pa.lay, e0 + 3)] = o.w;
-            }
-        }
-    }
+    /* a centered stream takes its own copy of the tile loop, so the plain one stays as it is */
+    if (info->dec_flags & 1u)
+        decode_tiles<STRIDED, true>(in, pa, info, pay, s_w[wave], s_so[wave], lb, cbase, full, out);
+    else
+        decode_tiles<STRIDED, false>(in, pa, info, pay, s_w[wave], s_so[wave], lb, cbase, full, out);
 }
 
 /* ---- K8: outlier patch ------------------------------------------------------------------------ */
@@ -1003,12 +1162,18 @@ hipError_t launch_range(const float *x, const PlanArgs &pa, const Workspace &ws,
 
 hipError_t launch_encode(const float *x, const PlanArgs &pa, const Workspace &ws,
                          uint8_t *widths_dst, uint64_t widths_bytes, hipStream_t stream) {
-    if (pa.lay.strided)
-        hipLaunchKernelGGL(encode_kernel<true>, dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa, ws,
+    if (pa.lay.strided && pa.center)
+        hipLaunchKernelGGL((encode_kernel<true, true>), dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa, ws,
+                           widths_dst, widths_bytes);
+    else if (pa.lay.strided)
+        hipLaunchKernelGGL((encode_kernel<true, false>), dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa, ws,
+                           widths_dst, widths_bytes);
+    else if (pa.center)
+        hipLaunchKernelGGL((encode_kernel<false, true>), dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa, ws,
                            widths_dst, widths_bytes);
     else
-        hipLaunchKernelGGL(encode_kernel<false>, dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa, ws,
-                           widths_dst, widths_bytes);
+        hipLaunchKernelGGL((encode_kernel<false, false>), dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa,
+                           ws, widths_dst, widths_bytes);
     return hipGetLastError();
 }
 

@@ -10,7 +10,8 @@ CANARY = 0xA7
 def parse_options(opts: str, n: int):
     """Options string -> oracle arguments (rel, eps, B, T, side_max, V), library defaults.
     V is the chunk coder's chunk in values (coder=chunk), else None."""
-    out = {"rel": True, "eps": 1e-4, "B": 256, "T": 30, "side_max": min(n, 1 << 23), "V": None}
+    out = {"rel": True, "eps": 1e-4, "B": 256, "T": 30, "side_max": min(n, 1 << 23), "V": None,
+           "center": False}
     if opts is None or opts.strip() == "":
         return out
     try:
@@ -37,6 +38,8 @@ def parse_options(opts: str, n: int):
             out["V"] = out["V"] or 2048
         elif k == "chunk_bytes":
             out["V"] = int(v) // 4
+        elif k == "center":
+            out["center"] = v == "1"
     return out
 
 
@@ -52,7 +55,7 @@ def oracle_stream(oracle, x: np.ndarray, dims, opts: str) -> np.ndarray:
     o = parse_options(opts, n)
     if o["V"] is not None:
         return oracle.compress_chunked(x, dims, o["rel"], o["eps"], o["V"], o["T"], o["side_max"])
-    return oracle.compress(x, dims, o["rel"], o["eps"], o["B"], o["T"], o["side_max"])
+    return oracle.compress(x, dims, o["rel"], o["eps"], o["B"], o["T"], o["side_max"], center=o["center"])
 
 
 def header(stream: np.ndarray) -> dict:

@@ -48,7 +48,8 @@ def test_unsupported_execution_kinds(kind):
                                   "block=256;block=128", "side_max=5000", "coder=huffman",
                                   "coder=chunk;block=256", "chunk_bytes=8192", "coder=chunk;chunk_bytes=2048",
                                   "coder=chunk;chunk_bytes=32768", "coder=chunk;coder=chunk",
-                                  "coder=chunk;chunk_bytes=4096;chunk_bytes=4096"])
+                                  "coder=chunk;chunk_bytes=4096;chunk_bytes=4096",
+                                  "center=2", "center=1;center=1", "center=yes", "coder=chunk;center=1"])
 def test_invalid_options_rejected_before_any_device_call(opts):
     st, plan = binding.eblc_plan_create([64, 64], opts)
     assert st == binding.EBLC_INVALID_ARGUMENT and plan is None

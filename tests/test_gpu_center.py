@@ -1,0 +1,163 @@
+"""GPU parity of Lorenzo centering (center=1) against the oracle's centered compressor.
+
+Streams byte for byte (header flags, widths, means section, payload, outliers, pads) and
+reconstructions bit for bit: tiny fuzz over every block size, ragged multi-chunk fields with a
+large offset, partial last blocks for blocks spanning several tiles, escapes, the 512^3 field at
+full size, a padded layout, and decoding across plans (a plain plan decodes a centered stream and
+the reverse) and corrupt flags.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from error_bounded_lossy_encode_amd import synth
+from helpers import first_difference, gpu_roundtrip, header, oracle_stream
+
+pytestmark = pytest.mark.gpu
+
+BLOCKS = [32, 64, 128, 256, 512, 1024, 2048]
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    from error_bounded_lossy_encode_amd import binding
+    binding.lib()
+    return binding, torch
+
+
+def check_case(env, x, dims, opts, label=""):
+    binding, torch = env
+    ref = oracle_stream(oracle, x, dims, opts)
+    st, ref_dec = oracle.decompress(ref)
+    assert st == oracle.OK
+    got, dec = gpu_roundtrip(binding, torch, x, dims, opts)
+    assert got.size == ref.size and np.array_equal(got, ref), f"{label} {opts}: {first_difference(got, ref)}"
+    bad = np.nonzero(dec.view(np.uint32) != ref_dec.view(np.uint32))[0]
+    assert bad.size == 0, f"{label} {opts}: reconstruction differs at {bad[:5]}"
+    return ref
+
+
+def flags(stream):
+    return int(np.ascontiguousarray(stream[68:72]).view(np.uint32)[0])
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_center_tiny_fuzz(env, seed):
+    rng = np.random.default_rng(1300 + seed)
+    kinds = ["smooth", "normal", "specials", "const", "ramp", "subnormal", "bits"]
+    for case in range(16):
+        B = int(rng.choice(BLOCKS))
+        n = int(rng.integers(1, 3 * 2048 + 300))
+        kind = kinds[(seed + case) % len(kinds)]
+        x = synth.tiny_array(rng, n, kind)
+        if case % 3 == 0:
+            with np.errstate(invalid="ignore"):   # inf + offset stays inf, nan stays nan
+                x = (x + np.float32(rng.choice([-5e3, 1e2, 7e4]))).astype(np.float32)
+        T = int(rng.choice([2, 15, 30]))
+        side = int(rng.choice([0, 1, n]))
+        if rng.integers(0, 2):
+            bound = f"rel={float(rng.choice([0.0, 1e-6, 1e-3, 0.3]))!r}"
+        else:
+            bound = f"abs={float(rng.choice([0.0, 1e-4, 1e-2, 5.0]))!r}"
+        opts = f"{bound};block={B};outlier_log2={T};side_max={side};center=1"
+        print(f"[center fuzz] seed {seed} case {case} kind {kind} n {n} {opts}", flush=True)
+        check_case(env, x, [n], opts, f"seed{seed} case{case} {kind} n={n}")
+
+
+@pytest.mark.parametrize("B", BLOCKS)
+def test_center_offset_field_ragged(env, B):
+    rng = np.random.default_rng(B)
+    n = 5 * 8192 + 1000 + B // 2          # partial last block for every B
+    x = (np.float32(2500.0) + synth.tiny_array(rng, n, "smooth") * np.float32(0.01)).astype(np.float32)
+    x[::997] = np.float32(np.nan)
+    ref = check_case(env, x, [n], f"abs=1e-3;block={B};outlier_log2=30;center=1", f"B={B}")
+    assert header(ref)["mode"] == 0 and flags(ref) == 1
+    plain = oracle_stream(oracle, x, [n], f"abs=1e-3;block={B};outlier_log2=30")
+    assert ref.size < plain.size
+
+
+@pytest.mark.parametrize("B", [64, 256, 1024])
+def test_center_escapes(env, B):
+    rng = np.random.default_rng(9 + B)
+    n = 4 * 8192 + 333
+    x = synth.tiny_array(rng, n, "smooth")
+    x[3::13] = np.float32(1e9)            # more than 64 escapes per chunk
+    ref = check_case(env, x, [n], f"abs=1e-2;block={B};outlier_log2=30;center=1", f"B={B}")
+    h = header(ref)
+    assert h["mode"] == 0 and h["m"] > 64 * (n // 2048)
+
+
+def test_center_ricker_512cubed(env):
+    binding, torch = env
+    x, dims, opts = synth.c3_ricker(512, device="cuda")
+    x = x.cpu().numpy()
+    opts = opts + ";center=1"
+    print(f"[full-size center] 512^3 {opts}", flush=True)
+    ref = check_case(env, x, dims, opts, "512^3 Ricker")
+    assert header(ref)["mode"] == 0 and flags(ref) == 1
+
+
+def test_center_padded_layout(env):
+    binding, torch = env
+    dims, strides = [20, 34, 44], [34 * 52 + 5 * 52, 52, 1]
+    opts = "rel=1e-4;block=512;outlier_log2=30;center=1"
+    rng = np.random.default_rng(12)
+    interior = (np.float32(40.0) + synth.tiny_array(rng, int(np.prod(dims)), "smooth")).astype(np.float32)
+    interior = interior.reshape(dims)
+    span = 1 + sum((d - 1) * s for d, s in zip(dims, strides))
+    buf = np.full(span + 8, np.float32(-7.25e33), dtype=np.float32)
+    np.lib.stride_tricks.as_strided(buf, shape=dims, strides=[4 * s for s in strides])[...] = interior
+    ref = oracle_stream(oracle, interior.reshape(-1), dims, opts)
+    _, ref_dec = oracle.decompress(ref)
+    st, plan = binding.eblc_plan_create(dims, opts, 0, strides=strides)
+    assert st == binding.EBLC_OK
+    try:
+        maxb = binding.eblc_max_compressed_bytes(plan)
+        xd = torch.from_numpy(buf).cuda()
+        out = torch.zeros(maxb, dtype=torch.uint8, device="cuda")
+        st, nb = binding.eblc_compress(plan, xd, out)
+        assert st == binding.EBLC_OK and np.array_equal(out.cpu().numpy()[:nb], ref)
+        yd = torch.from_numpy(np.full_like(buf, np.float32(-7.25e33))).cuda()
+        assert binding.eblc_decompress(plan, out, nb, yd) == binding.EBLC_OK
+        assert binding.eblc_plan_status(plan) == binding.EBLC_OK
+        yview = np.lib.stride_tricks.as_strided(yd.cpu().numpy(), shape=dims, strides=[4 * s for s in strides])
+        assert np.array_equal(np.ascontiguousarray(yview).reshape(-1).view(np.uint32), ref_dec.view(np.uint32))
+    finally:
+        binding.eblc_plan_destroy(plan)
+
+
+def test_center_cross_plan_decode_and_corrupt_flags(env):
+    binding, torch = env
+    rng = np.random.default_rng(21)
+    n = 3 * 8192 + 17
+    x = (np.float32(-900.0) + synth.tiny_array(rng, n, "smooth")).astype(np.float32)
+    cent = oracle_stream(oracle, x, [n], "rel=1e-4;block=128;center=1")
+    plain = oracle_stream(oracle, x, [n], "rel=1e-4;block=128")
+    _, dec = oracle.decompress(cent)
+    y = torch.empty(n, dtype=torch.float32, device="cuda")
+    for opts in ("rel=1e-4;block=128", "rel=1e-4;block=128;center=1"):
+        st, plan = binding.eblc_plan_create([n], opts, 0)
+        assert st == binding.EBLC_OK
+        try:
+            def status_of(stream):
+                d = torch.from_numpy(np.ascontiguousarray(stream)).cuda()
+                st = binding.eblc_decompress(plan, d, stream.size, y)
+                return st if st != binding.EBLC_OK else binding.eblc_plan_status(plan)
+
+            for stream in (cent, plain):
+                y.fill_(float("nan"))
+                assert status_of(stream) == binding.EBLC_OK
+                assert np.array_equal(y.cpu().numpy().view(np.uint32), dec.view(np.uint32))
+
+            def with_flags(t, v):
+                t = t.copy()
+                t[68:72] = np.array([v], np.uint32).view(np.uint8)
+                return t
+
+            assert status_of(with_flags(cent, 2)) == binding.EBLC_CORRUPT_STREAM
+            assert status_of(with_flags(cent, 0)) == binding.EBLC_CORRUPT_STREAM
+            assert status_of(with_flags(plain, 1)) == binding.EBLC_CORRUPT_STREAM
+            assert status_of(cent) == binding.EBLC_OK
+        finally:
+            binding.eblc_plan_destroy(plan)
