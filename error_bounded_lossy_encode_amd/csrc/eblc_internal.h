@@ -37,6 +37,7 @@ constexpr int kEncSegs = kEncChunk / 32;
 constexpr int kEncWaves = 8192 / kEncChunk;       /* waves (chunks) per encode workgroup */
 constexpr int kEncThreads = kWave * kEncWaves;
 constexpr int kEncChunksPerGroup = kEncWaves;
+constexpr int kEncPayWords = kEncChunk / 2 + 4;  /* LDS pack buffer per wave: half a chunk's worst case */
 constexpr int kDecTiles = 8;
 constexpr int kDecChunk = kTile * kDecTiles;     /* 2048 values */
 constexpr int kDecSegs = kDecChunk / 32;         /* 64 segments */

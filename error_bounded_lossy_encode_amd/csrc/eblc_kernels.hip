@@ -160,79 +160,56 @@ __device__ __forceinline__ uint32_t seg_or(uint32_t v) {
     return v;
 }
 
-/* Codes of one encode tile: kEncLaneVals consecutive values per lane.  Quantize
- * (rint(x inv2eb), kept when a branch-free test passes; the full rule runs only in a wave where
- * some value misses it), Lorenzo delta against the previous value (the previous lane's last
- * value by wave_shr, the previous tile's through `carry`, 0 when `reset`), zigzag.  Writes the
- * lane's zigzag codes to z and returns the bit width of its 32-value segment (kSegLanes
- * lanes). */
-template <bool FULL>
-__device__ __forceinline__ uint32_t code_tile(const float xs[kEncLaneVals], uint64_t e0, uint64_t n,
-                                              const QParams &qp, bool reset, int t,
-                                              uint32_t *emask_tile, uint32_t *stage_idx,
-                                              uint32_t *stage_val, int32_t &carry,
-                                              uint32_t z[kEncLaneVals], EncState &st,
-                                              uint32_t &slo, int32_t &shi) {
+/* The full quantization rule for the values of one encode tile that missed the fast test (bit k
+ * of `slow`: value k of the lane), and the tile's escapes: per-segment bitmask (value V j + k of
+ * the segment), the chunk's first kEscStage escapes staged as (index, bits) in index order, and
+ * the count.  e0 is the lane's first value index. */
+__device__ __forceinline__ void slow_tile(const float xs[kEncLaneVals], uint32_t slow, uint64_t e0,
+                                          const QParams &qp, int t, uint32_t *emask_tile,
+                                          uint32_t *stage_idx, uint32_t *stage_val,
+                                          int32_t q[kEncLaneVals], EncState &st) {
     constexpr int V = kEncLaneVals;
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t j = lane & (kSegLanes - 1);
-    /* Fast test: rint(x inv2eb) is kept when its reconstruction is within eb and the lane's
-     * largest code is below 2^T.  This is the full rule's first acceptance exactly: its extra
-     * clause |x| >= |y|/2 cannot fail here.  For q0 = 0 it is trivial; for |q0| >= 2, |y| >=
-     * 4 eb and a rounded |x - y| <= eb forces |x - y| <= 2 eb; for |q0| = 1, rint gives 1 only
-     * when f32(x r) > 1/2, which with r within 2^-24 of 1/(2 eb) puts x above the largest float
-     * below eb.  NaN fails the eb test, infinities the 2^T test. */
-    float q0f[V];
-    int32_t q[V];
-    bool within[V];
+    uint32_t esc = 0;
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-        const float p = xs[k] * qp.r;
-        q0f[k] = rintf(p);
-        const float y = q0f[k] * qp.s;
-        within[k] = fabsf(xs[k] - y) <= qp.eb;
-        q[k] = (int32_t)q0f[k];
+        if ((slow >> k) & 1u) {
+            uint32_t e;
+            q[k] = quantize_slow(xs[k], rintf(xs[k] * qp.r), qp, &e);
+            esc |= e << k;
+        }
     }
-    float qmax = fabsf(q0f[0]);
-#pragma unroll
-    for (int k = 1; k < V; ++k) qmax = fmaxf(qmax, fabsf(q0f[k]));
-    uint32_t all_within = 1;
-#pragma unroll
-    for (int k = 0; k < V; ++k) all_within &= (uint32_t)within[k];
-    const bool lane_fast = ((uint32_t)(qmax < qp.tlim) & all_within) != 0;
-    if (__ballot(!lane_fast)) {
-        uint32_t esc = 0;
+    if (__ballot(esc != 0)) {
+        const uint32_t segm = seg_or(esc << (V * j));
+        if (j == 0) emask_tile[lane / kSegLanes] = segm;
+        const uint32_t ecnt = (uint32_t)__popc(esc);
+        const uint32_t eincl = wave_incl_scan(ecnt);
+        uint32_t r = st.escs + eincl - ecnt;
 #pragma unroll
         for (int k = 0; k < V; ++k) {
-            if (!(within[k] && fabsf(q0f[k]) < qp.tlim)) {
-                uint32_t e;
-                q[k] = quantize_slow(xs[k], q0f[k], qp, &e);
-                esc |= e << k;
-            }
-        }
-        /* escapes: per-segment bitmask (value V j + k of the segment), the chunk's first
-         * kEscStage escapes staged as (index, bits) in index order, and the count */
-        if (__ballot(esc != 0)) {
-            const uint32_t segm = seg_or(esc << (V * j));
-            if (j == 0) emask_tile[lane / kSegLanes] = segm;
-            const uint32_t ecnt = (uint32_t)__popc(esc);
-            const uint32_t eincl = wave_incl_scan(ecnt);
-            uint32_t r = st.escs + eincl - ecnt;
-#pragma unroll
-            for (int k = 0; k < V; ++k) {
-                if ((esc >> k) & 1u) {
-                    if (r < (uint32_t)kEscStage) {
-                        stage_idx[r] = (uint32_t)(e0 + k);
-                        stage_val[r] = __float_as_uint(xs[k]);
-                    }
-                    ++r;
+            if ((esc >> k) & 1u) {
+                if (r < (uint32_t)kEscStage) {
+                    stage_idx[r] = (uint32_t)(e0 + k);
+                    stage_val[r] = __float_as_uint(xs[k]);
                 }
+                ++r;
             }
-            st.escs += readlane(eincl, 63);
-            st.tmask |= 1u << t;
         }
+        st.escs += readlane(eincl, 63);
+        st.tmask |= 1u << t;
     }
-    /* the lane's code sum in two exact halves (low 16 bits, and the rest), for centering */
+}
+
+/* Lorenzo delta of one tile's codes against the previous value (the previous lane's last value
+ * by wave_shr, the previous tile's through `carry`, 0 when `reset`), zigzag; codes past n are 0.
+ * Writes the zigzag codes to z, the lane's code sum in two exact halves (low 16 bits, and the
+ * rest) for centering, and returns the bit width of the lane's 32-value segment. */
+template <bool FULL>
+__device__ __forceinline__ uint32_t finish_tile(const int32_t q[kEncLaneVals], uint64_t e0, uint64_t n, bool reset,
+                                                int32_t &carry, uint32_t z[kEncLaneVals], uint32_t &slo,
+                                                int32_t &shi) {
+    constexpr int V = kEncLaneVals;
     slo = 0;
     shi = 0;
 #pragma unroll
@@ -341,7 +318,8 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
                                              const QParams &qp, uint32_t bmask, int32_t carry,
                                              uint32_t *pay, uint8_t *wid, uint32_t *emask_chunk,
                                              uint32_t *stage_idx, uint32_t *stage_val, EncState &st,
-                                             uint32_t log2B, int32_t *__restrict__ means, bool narrow) {
+                                             uint32_t log2B, int32_t *__restrict__ means, bool narrow,
+                                             uint32_t *__restrict__ slot) {
     constexpr int V = kEncLaneVals;
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t j = lane & (kSegLanes - 1), g = lane / kSegLanes;
@@ -368,6 +346,40 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
     const bool lane_at_block = ((V * lane) & bmask) == 0;
     uint32_t z[kEncTiles][V];
     uint32_t w[kEncTiles];
+    /* Quantize: rint(x inv2eb) is kept when its reconstruction is within eb and the code is below
+     * 2^T.  This is the full rule's first acceptance exactly: its extra clause |x| >= |y|/2
+     * cannot fail here.  For q0 = 0 it is trivial; for |q0| >= 2, |y| >= 4 eb and a rounded
+     * |x - y| <= eb forces |x - y| <= 2 eb; for |q0| = 1, rint gives 1 only when f32(x r) > 1/2,
+     * which with r within 2^-24 of 1/(2 eb) puts x above the largest float below eb.  NaN fails
+     * the eb test, infinities the 2^T test.  Every tile is tested first, without branches; the
+     * full rule runs only in a wave where some value missed the test. */
+    int32_t q[kEncTiles][V];
+    /* tested in groups of kTestGroup tiles: bit V (t mod kTestGroup) + k of the group's mask
+     * marks value k of tile t as missing the fast test */
+    constexpr int kTestGroup = 2;
+#pragma unroll
+    for (int t0 = 0; t0 < kEncTiles; t0 += kTestGroup) {
+        uint32_t slow = 0;
+#pragma unroll
+        for (int t = t0; t < t0 + kTestGroup; ++t) {
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float q0f = rintf(xs[t][k] * qp.r);
+                const bool ok = (fabsf(xs[t][k] - q0f * qp.s) <= qp.eb) && (fabsf(q0f) < qp.tlim);
+                q[t][k] = (int32_t)q0f;
+                slow |= (ok ? 0u : 1u) << (V * (t - t0) + k);
+            }
+        }
+        if (__ballot(slow != 0)) {
+#pragma unroll
+            for (int t = t0; t < t0 + kTestGroup; ++t) {
+                const uint32_t ts = (slow >> (V * (t - t0))) & ((1u << V) - 1u);
+                if ((FULL || (uint32_t)t < ntiles) && __ballot(ts != 0))
+                    slow_tile(xs[t], ts, cbase + (uint64_t)t * kEncTile + V * lane, qp, t,
+                              emask_chunk + t * kSegsPerEncTile, stage_idx, stage_val, q[t], st);
+            }
+        }
+    }
     /* Lorenzo centering: a block's first code was coded against 0 (z = zigzag(q)); it is
      * recoded against the block's mean code, which goes to the means staging, and the segment
      * widths follow.  Blocks lie inside the chunk (B <= 2048).  A block of at most one tile is
@@ -385,9 +397,8 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
             const bool reset = lane_at_block && (((uint32_t)cbase + (uint32_t)t * kEncTile) & bmask) == 0;
             uint32_t slo;
             int32_t shi;
-            w[t] = code_tile<FULL>(xs[t], cbase + (uint64_t)t * kEncTile + V * lane, n, qp, reset, t,
-                                   emask_chunk + t * kSegsPerEncTile, stage_idx, stage_val, carry, z[t],
-                                   st, slo, shi);
+            w[t] = finish_tile<FULL>(q[t], cbase + (uint64_t)t * kEncTile + V * lane, n, reset, carry, z[t],
+                                     slo, shi);
             if (CENTER && in_tile) {
                 const uint32_t seglen = B / V; /* lanes per block */
                 /* narrow codes: one exact 32-bit sum; else the two halves */
@@ -446,13 +457,39 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
     const uint32_t incl = wave_incl_scan(wl);
     const uint32_t excl = incl - wl;
     st.words = readlane(incl, kEncSegs - 1);
+    /* Pass 2: pack into the LDS buffer (kEncPayWords words), then 128-bit stores to the slot.
+     * A chunk whose words do not fit is packed in two halves (tiles 0-3, then 4-7): segments
+     * hold whole words, so the halves share none.  Only the words used are cleared. */
+    const uint32_t total = st.words;
+    const uint32_t half = readlane(incl, kEncSegs / 2 - 1);
+    const bool one_pass = total + 1 <= (uint32_t)kEncPayWords;
+    uint32_t offs[kEncTiles];
 #pragma unroll
-    for (int t = 0; t < kEncTiles; ++t) {
-        if (FULL || (uint32_t)t < ntiles) {
-            const uint32_t off =
-                (uint32_t)__builtin_amdgcn_ds_bpermute((int)((t * kSegsPerEncTile + g) * 4), (int)excl);
-            pack_lane(z[t], w[t], 32u * off + (uint32_t)V * w[t] * j, pay);
+    for (int t = 0; t < kEncTiles; ++t)
+        offs[t] = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((t * kSegsPerEncTile + g) * 4), (int)excl);
+    uint4 *pay4 = reinterpret_cast<uint4 *>(pay);
+    const uint4 zero4 = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (h == 1 && one_pass) break;
+        const uint32_t w0 = (one_pass || h == 0) ? 0u : half;                 /* first word of the pass */
+        const uint32_t nw = one_pass ? total : (h == 0 ? half : total - half); /* words of the pass */
+        for (uint32_t i = lane; i < (nw + 4) / 4; i += kWave) pay4[i] = zero4;
+        wave_lds_sync();
+#pragma unroll
+        for (int t = 0; t < kEncTiles; ++t) {
+            const bool mine = one_pass || (h == 0 ? t < kEncTiles / 2 : t >= kEncTiles / 2);
+            if ((FULL || (uint32_t)t < ntiles) && mine)
+                pack_lane(z[t], w[t], 32u * (offs[t] - w0) + (uint32_t)V * w[t] * j, pay);
         }
+        wave_lds_sync();
+        if (w0 == 0) {
+            uint4 *dst = reinterpret_cast<uint4 *>(slot);
+            for (uint32_t i = lane; i < (nw + 3) / 4; i += kWave) dst[i] = pay4[i];
+        } else {
+            for (uint32_t i = lane; i < nw; i += kWave) slot[w0 + i] = pay[i];
+        }
+        wave_lds_sync();
     }
 }
 
@@ -464,7 +501,7 @@ template <bool STRIDED, bool CENTER>
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(
     const float *__restrict__ x, PlanArgs pa, Workspace ws, uint8_t *__restrict__ widths_dst,
     uint64_t widths_bytes) {
-    __shared__ uint4 s_pay4[kEncWaves][kEncChunk / 4 + 1];
+    __shared__ uint4 s_pay4[kEncWaves][kEncPayWords / 4];
     __shared__ uint4 s_wid4[kEncWaves][kEncSegs / 16];
     __shared__ uint32_t s_stage[kEncWaves][2][kEscStage];
     __shared__ uint32_t s_grp[2][kEncWaves];
@@ -484,10 +521,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
         qp.tlim = (float)(1u << pa.T);
         uint32_t *pay = reinterpret_cast<uint32_t *>(s_pay4[wave]);
         uint8_t *wid = reinterpret_cast<uint8_t *>(s_wid4[wave]);
-        const uint4 zero4 = make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < kEncChunk / 4 / kWave; ++i) s_pay4[wave][lane + kWave * i] = zero4;
-        if (lane < kEncSegs / 16) s_wid4[wave][lane] = zero4;
+        if (lane < kEncSegs / 16) s_wid4[wave][lane] = make_uint4(0, 0, 0, 0);
         wave_lds_sync();
         const uint64_t cbase = (uint64_t)c * kEncChunk;
         const uint32_t bmask = pa.B - 1;
@@ -507,15 +541,13 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
         uint32_t *stage_val = s_stage[wave][1];
         if (cbase + kEncChunk <= pa.n)
             encode_chunk<true, STRIDED, CENTER>(x, pa.lay, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk,
-                                                stage_idx, stage_val, st, pa.log2B, ws.means, narrow);
+                                                stage_idx, stage_val, st, pa.log2B, ws.means, narrow,
+                                                ws.scratch + cbase);
         else
             encode_chunk<false, STRIDED, CENTER>(x, pa.lay, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk,
-                                                 stage_idx, stage_val, st, pa.log2B, ws.means, narrow);
-        wave_lds_sync();
-        /* chunk payload -> scratch slot, widths -> stream (or staging) */
-        uint4 *dst = reinterpret_cast<uint4 *>(ws.scratch + cbase);
-        const uint32_t nvec = (st.words + 3) >> 2;
-        for (uint32_t i = lane; i < nvec; i += kWave) dst[i] = s_pay4[wave][i];
+                                                 stage_idx, stage_val, st, pa.log2B, ws.means, narrow,
+                                                 ws.scratch + cbase);
+        /* widths -> stream (or staging) */
         if (lane < kEncSegs / 16) {
             const uint64_t off = (uint64_t)c * kEncSegs + 16u * lane;
             if (off < widths_bytes) *reinterpret_cast<uint4 *>(widths_dst + off) = s_wid4[wave][lane];
