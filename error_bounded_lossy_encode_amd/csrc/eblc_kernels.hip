@@ -160,6 +160,15 @@ __device__ __forceinline__ uint32_t seg_or(uint32_t v) {
     return v;
 }
 
+/* Number of significant bits of v (0 for 0): v_ffbh_u32 gives the leading-zero count, or
+ * 0xffffffff for 0, and 32 minus it with unsigned saturation is the bit length. */
+__device__ __forceinline__ uint32_t bit_length(uint32_t v) {
+    uint32_t lz, w;
+    asm("v_ffbh_u32 %0, %1" : "=v"(lz) : "v"(v));
+    asm("v_sub_u32_e64 %0, 32, %1 clamp" : "=v"(w) : "v"(lz));
+    return w;
+}
+
 /* The full quantization rule for the values of one encode tile that missed the fast test (bit k
  * of `slow`: value k of the lane), and the tile's escapes: per-segment bitmask (value V j + k of
  * the segment), the chunk's first kEscStage escapes staged as (index, bits) in index order, and
@@ -231,8 +240,7 @@ __device__ __forceinline__ uint32_t finish_tile(const int32_t q[kEncLaneVals], u
     uint32_t orv = z[0];
 #pragma unroll
     for (int k = 1; k < V; ++k) orv |= z[k];
-    orv = seg_or(orv);
-    return orv ? 32u - (uint32_t)__builtin_clz(orv) : 0u;
+    return bit_length(seg_or(orv));
 }
 
 /* OR n consecutive codes of width w, already joined into `bits` (code k at bit k w), into the
@@ -271,8 +279,7 @@ __device__ __forceinline__ uint32_t seg_width(const uint32_t z[kEncLaneVals]) {
     uint32_t orv = z[0];
 #pragma unroll
     for (int k = 1; k < kEncLaneVals; ++k) orv |= z[k];
-    orv = seg_or(orv);
-    return orv ? 32u - (uint32_t)__builtin_clz(orv) : 0u;
+    return bit_length(seg_or(orv));
 }
 
 /* Sum over aligned groups of seglen lanes (8, 16, 32 or 64), returned in every lane of the
@@ -354,26 +361,35 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
      * the eb test, infinities the 2^T test.  Every tile is tested first, without branches; the
      * full rule runs only in a wave where some value missed the test. */
     int32_t q[kEncTiles][V];
-    /* tested in groups of kTestGroup tiles: bit V (t mod kTestGroup) + k of the group's mask
-     * marks value k of tile t as missing the fast test */
+    /* tested in groups of kTestGroup tiles: a lane passes when all its values are within eb
+     * and its largest |code| is below 2^T; a wave with a failing lane re-tests value by value
+     * and runs the full rule where needed */
     constexpr int kTestGroup = 2;
 #pragma unroll
     for (int t0 = 0; t0 < kEncTiles; t0 += kTestGroup) {
-        uint32_t slow = 0;
+        bool lane_fast = true;
 #pragma unroll
         for (int t = t0; t < t0 + kTestGroup; ++t) {
+            float qabs = 0.0f;
 #pragma unroll
             for (int k = 0; k < V; ++k) {
                 const float q0f = rintf(xs[t][k] * qp.r);
-                const bool ok = (fabsf(xs[t][k] - q0f * qp.s) <= qp.eb) && (fabsf(q0f) < qp.tlim);
+                lane_fast = lane_fast && (fabsf(xs[t][k] - q0f * qp.s) <= qp.eb);
+                qabs = fmaxf(qabs, fabsf(q0f));
                 q[t][k] = (int32_t)q0f;
-                slow |= (ok ? 0u : 1u) << (V * (t - t0) + k);
             }
+            lane_fast = lane_fast && (qabs < qp.tlim);
         }
-        if (__ballot(slow != 0)) {
+        if (__ballot(!lane_fast)) {
 #pragma unroll
             for (int t = t0; t < t0 + kTestGroup; ++t) {
-                const uint32_t ts = (slow >> (V * (t - t0))) & ((1u << V) - 1u);
+                uint32_t ts = 0; /* bit k: value k missed the test */
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    const float q0f = rintf(xs[t][k] * qp.r);
+                    const bool ok = (fabsf(xs[t][k] - q0f * qp.s) <= qp.eb) && (fabsf(q0f) < qp.tlim);
+                    ts |= (ok ? 0u : 1u) << k;
+                }
                 if ((FULL || (uint32_t)t < ntiles) && __ballot(ts != 0))
                     slow_tile(xs[t], ts, cbase + (uint64_t)t * kEncTile + V * lane, qp, t,
                               emask_chunk + t * kSegsPerEncTile, stage_idx, stage_val, q[t], st);
