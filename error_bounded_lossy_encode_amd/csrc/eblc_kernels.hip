@@ -795,7 +795,22 @@ __device__ __forceinline__ void write_chunk_outliers(const float *__restrict__ x
  * [Dw, bs), whole 128-bit units [bs, be) and a tail [be, Dw + P), bs and be being Dw and Dw + P
  * rounded up and down to 4 words.  Head and tail words can share a 16-byte unit with the
  * neighbouring chunks, so they are stored one by one; each whole unit is assembled from two
- * aligned source units shifted by the wave-uniform word offset (bs - Dw) mod 4. */
+ * aligned source units shifted by the wave-uniform word offset (bs - Dw) mod 4.  A lane loads
+ * up to kCopyBatch units before storing any, so a chunk's loads are in flight together. */
+constexpr int kCopyBatch = 4;
+
+/* Words r..r+3 of the eight words A, B (r in 0..3), by selects on the bits of r.  The empty asm
+ * keeps both units whole in registers first: without it the compiler narrows the loads to the
+ * words each value of r uses and moves them into per-r branches, and one such build loaded the
+ * wrong word for r = 3. */
+__device__ __forceinline__ uint4 shift_units(uint4 A, uint4 B, uint32_t r) {
+    asm("" : "+v"(A.x), "+v"(A.y), "+v"(A.z), "+v"(A.w), "+v"(B.x), "+v"(B.y), "+v"(B.z));
+    const bool odd = (r & 1u) != 0;
+    const uint32_t w0 = odd ? A.y : A.x, w1 = odd ? A.z : A.y, w2 = odd ? A.w : A.z;
+    const uint32_t w3 = odd ? B.x : A.w, w4 = odd ? B.y : B.x, w5 = odd ? B.z : B.y;
+    return (r & 2u) != 0 ? make_uint4(w2, w3, w4, w5) : make_uint4(w0, w1, w2, w3);
+}
+
 __device__ __forceinline__ void copy_chunk_payload(const uint32_t *__restrict__ src, uint32_t P,
                                                    uint64_t Dw, uint32_t *__restrict__ pay) {
     const uint32_t lane = threadIdx.x & 63;
@@ -803,26 +818,34 @@ __device__ __forceinline__ void copy_chunk_payload(const uint32_t *__restrict__ 
     const uint64_t bs = (Dw + 3) & ~(uint64_t)3;
     const uint64_t be = De & ~(uint64_t)3;
     const uint64_t head_end = bs < De ? bs : De;
-    if (lane < head_end - Dw) pay[Dw + lane] = src[lane];
     const uint64_t tail_start = be > bs ? be : bs;
-    if (tail_start < De && lane < De - tail_start) pay[tail_start + lane] = src[tail_start - Dw + lane];
-    if (be <= bs) return;
-    const uint32_t units = (uint32_t)((be - bs) >> 2);
-    const uint32_t r = (uint32_t)(bs - Dw);          /* 0..3: source word offset of unit 0 */
+    const bool head = lane < head_end - Dw;
+    const bool tail = tail_start < De && lane < De - tail_start;
+    const uint32_t hv = head ? src[lane] : 0u;
+    const uint32_t tv = tail ? src[tail_start - Dw + lane] : 0u;
+    const uint32_t units = be > bs ? (uint32_t)((be - bs) >> 2) : 0u;
+    const uint32_t r = (uint32_t)(bs - Dw); /* 0..3: source word offset of unit 0 */
+    const uint32_t rn = r != 0 ? 1u : 0u;
     const uint4 *s4 = reinterpret_cast<const uint4 *>(src);
     uint4 *d4 = reinterpret_cast<uint4 *>(pay + bs);
-    if (r == 0) {
-        for (uint32_t t = lane; t < units; t += kWave) d4[t] = s4[t];
-    } else {
-        for (uint32_t t = lane; t < units; t += kWave) {
-            const uint4 A = s4[t], B = s4[t + 1];
-            uint4 o;
-            if (r == 1) o = make_uint4(A.y, A.z, A.w, B.x);
-            else if (r == 2) o = make_uint4(A.z, A.w, B.x, B.y);
-            else o = make_uint4(A.w, B.x, B.y, B.z);
-            d4[t] = o;
+    for (uint32_t t0 = 0; t0 < units; t0 += kCopyBatch * kWave) {
+        uint4 A[kCopyBatch], B[kCopyBatch];
+#pragma unroll
+        for (int k = 0; k < kCopyBatch; ++k) {
+            /* unconditional loads at clamped indices, so the batch issues without waits; the
+             * last source unit holding a needed word is units - 1 + rn, and B is A when r = 0 */
+            const uint32_t t = t0 + lane + kWave * k;
+            A[k] = s4[min(t, units - 1)];
+            B[k] = s4[min(t + rn, units - 1 + rn)];
+        }
+#pragma unroll
+        for (int k = 0; k < kCopyBatch; ++k) {
+            const uint32_t t = t0 + lane + kWave * k;
+            if (t < units) d4[t] = shift_units(A[k], B[k], r);
         }
     }
+    if (head) pay[Dw + lane] = hv;
+    if (tail) pay[tail_start + lane] = tv;
 }
 
 /* One workgroup per group of kEncChunksPerGroup encode chunks, one wave per chunk: the wave
@@ -840,7 +863,7 @@ __global__ __launch_bounds__(kBlockThreads) void compact_kernel(const float *__r
     const uint32_t grp = blockIdx.x;
     const DevInfo *info = ws.info;
     /* every small input of the group up front, in one round of loads */
-    const uint32_t wave = tid >> 6;
+    const uint32_t wave = tid >> 6, lane = tid & 63;
     const uint32_t c = grp * CPG + wave;
     uint32_t words[CPG], escs[CPG];
 #pragma unroll
@@ -894,8 +917,23 @@ __global__ __launch_bounds__(kBlockThreads) void compact_kernel(const float *__r
     uint32_t *oidx = reinterpret_cast<uint32_t *>(out + oidx_off);
     uint32_t *oval = reinterpret_cast<uint32_t *>(out + oval_off);
     if (c < pa.nchunks) {
+        /* a chunk whose escapes were all staged: their loads go out with the payload's */
+        const uint32_t cnt = escs[wave];
+        const bool staged = cnt != 0 && cnt <= (uint32_t)kEscStage;
+        uint32_t si = 0, sv = 0;
+        if (staged && lane < cnt) {
+            si = ws.stage_idx[(uint64_t)c * kEscStage + lane];
+            sv = ws.stage_val[(uint64_t)c * kEscStage + lane];
+        }
         copy_chunk_payload(ws.scratch + (uint64_t)c * pa.slot, words[wave], W, pay);
-        write_chunk_outliers<STRIDED>(x, pa.lay, ws, c, escs[wave], O, oidx, oval);
+        if (staged) {
+            if (lane < cnt) {
+                oidx[O + lane] = si;
+                oval[O + lane] = sv;
+            }
+        } else {
+            write_chunk_outliers<STRIDED>(x, pa.lay, ws, c, cnt, O, oidx, oval);
+        }
     }
     if (widths_src != nullptr) {
         /* the group's share of the size section, staged by the encoder */
