@@ -101,13 +101,18 @@ def with_chunk_coder(opts: str, chunk_bytes: int) -> str:
 
 
 def cpu_baseline(items, budget_s: float):
-    """The oracle as it stands, single-threaded, on a leading sample of the workload: whole
-    fields while they fit the budget, else whole slowest-axis planes of the first field (the
-    bound is resolved on the sample itself in relative mode).  A reported baseline, not a
-    parity check."""
+    """The oracle as it stands on a leading sample of the workload: whole fields while they fit
+    the budget, else whole slowest-axis planes of the first field (the bound is resolved on the
+    sample itself in relative mode).  It runs twice: single-threaded on the whole sample, then
+    on P threads over P block-aligned pieces of it under the sample's bound (P = the host cores,
+    at most 16), whose joined stream must equal the single-threaded one.  A reported baseline,
+    not a parity check of the GPU path."""
+    import os
+
     import numpy as np
 
     import oracle
+    from oracle import shards
 
     rate = 60e6  # values per second for compress + decompress together, a rough estimate
     budget_vals = budget_s * rate
@@ -133,31 +138,50 @@ def cpu_baseline(items, budget_s: float):
             taken += n
         else:
             break
-    tc = td = 0.0
+    P = max(1, min(16, os.cpu_count() or 1))
+    tc = td = pc = pd = 0.0
     nbytes = 0
+    joined_ok = 0
     for xs, sdims, opts in samples:
         o = parse_opts(opts, xs.size)
+        side_max = min(o["side_max"], xs.size)
         t0 = time.perf_counter()
         if o["V"] is not None:
-            s = oracle.compress_chunked(xs, sdims, o["rel"], o["eps"], o["V"], o["T"], min(o["side_max"], xs.size))
+            s = oracle.compress_chunked(xs, sdims, o["rel"], o["eps"], o["V"], o["T"], side_max)
         else:
-            s = oracle.compress(xs, sdims, o["rel"], o["eps"], o["B"], o["T"], min(o["side_max"], xs.size),
-                                center=o["center"])
+            s = oracle.compress(xs, sdims, o["rel"], o["eps"], o["B"], o["T"], side_max, center=o["center"])
         t1 = time.perf_counter()
-        st, _ = oracle.decompress(s)
+        st, y = oracle.decompress(s)
         t2 = time.perf_counter()
         assert st == oracle.OK
+        ok, _, bounds, streams = shards.code_pieces(xs, o["rel"], o["eps"], o["B"], o["T"], o["center"],
+                                                    o["V"], P, P)
+        t3 = time.perf_counter()
+        if ok:
+            yp = shards.decode_pieces(streams, P)
+        t4 = time.perf_counter()
+        if ok:
+            joined = shards.join(xs, sdims, o["T"], o["B"], side_max, o["center"], o["V"], bounds, streams)
+            if joined is not None:
+                assert np.array_equal(joined, s), "pieces do not join to the whole stream"
+                assert np.array_equal(yp.view(np.uint32), y.view(np.uint32))
+                joined_ok += 1
         tc += t1 - t0
         td += t2 - t1
+        pc += t3 - t2
+        pd += t4 - t3
         nbytes += 4 * xs.size
     return {
-        "value": round(nbytes / (tc + td) / 1e9, 4),
+        "value": round(nbytes / (pc + pd) / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": P,
         "kind": "oracle",
         "sample": (f"{len(samples)} field(s), {taken} values ({nbytes / 2**20:.0f} MiB) from the start of the "
-                   f"same workload; compress {nbytes / tc / 1e9:.4f} GB/s, decompress {nbytes / td / 1e9:.4f} "
-                   f"GB/s, one thread, round trip {tc + td:.1f} s"),
+                   f"same workload, coded as {P} block-aligned pieces on {P} threads: compress "
+                   f"{nbytes / pc / 1e9:.4f} GB/s, decompress {nbytes / pd / 1e9:.4f} GB/s (joined stream equal "
+                   f"to the one-thread stream on {joined_ok} of {len(samples)} field(s)); one thread on the "
+                   f"whole sample: compress {nbytes / tc / 1e9:.4f} GB/s, decompress {nbytes / td / 1e9:.4f} "
+                   f"GB/s, round trip {nbytes / (tc + td) / 1e9:.4f} GB/s"),
     }
 
 
@@ -182,6 +206,9 @@ def main() -> int:
     ap.add_argument("--chunk-bytes", type=int, default=8192, choices=[4096, 8192, 16384])
     ap.add_argument("--center", action="store_true",
                     help="Lorenzo centering (bitpack coder): each block's first code against its mean")
+    ap.add_argument("--cold-reps", type=int, default=3,
+                    help="repetitions of the MALL-cold measurement (a 1 GiB device write before every "
+                         "compress and decompress call); 0 skips it")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device to device once (counter calibration)")
     args = ap.parse_args()
@@ -304,6 +331,32 @@ def main() -> int:
     kavg = {k: float(np.mean(v)) for k, v in ktimes.items()}
     log("[bench] kernel ms: " + ", ".join(f"{k}={v:.4f}" for k, v in kavg.items()))
 
+    # MALL-cold figures: a 1 GiB device write before every call evicts the 256 MB last-level
+    # cache, so each call reads its input from HBM (fields up to 256 MB otherwise run from it)
+    cold = None
+    if args.cold_reps > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cc, cd = [], []
+        for k in range(args.cold_reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            flush.fill_(float(k))
+            e[0].record(stream)
+            compress_all()
+            e[1].record(stream)
+            flush.fill_(float(k) + 0.5)
+            e[2].record(stream)
+            decompress_all()
+            e[3].record(stream)
+            torch.cuda.synchronize()
+            cc.append(e[0].elapsed_time(e[1]))
+            cd.append(e[2].elapsed_time(e[3]))
+        del flush
+        assert binding.eblc_plan_status(plan.handle) == binding.EBLC_OK
+        cold = {"compress_gbps": round(in_bytes / (float(np.median(cc)) * 1e-3) / 1e9, 3),
+                "decompress_gbps": round(in_bytes / (float(np.median(cd)) * 1e-3) / 1e9, 3),
+                "reps": args.cold_reps, "flush": "1 GiB device write before every compress and decompress call"}
+        log(f"[bench] cold: compress {cold['compress_gbps']} GB/s, decompress {cold['decompress_gbps']} GB/s")
+
     # stream facts from the headers (host copies of 128 bytes, outside the timed region)
     nseg = (n + 31) // 32
     payload = []
@@ -385,6 +438,7 @@ def main() -> int:
         "roofline": roof(kernels[0], enc_gbps, kernels[0]),
         "roofline_decode": roof(kernels[1], dec_gbps, kernels[1]),
         "algorithmic_bytes_per_launch": {"encode": round(enc_bytes), "decode": round(dec_bytes)},
+        "cold": cold,
         "max_abs_err": err_max,
         "eb": ebs[0],
     }

@@ -1,0 +1,89 @@
+"""Pins of the oracle by piece invariance: every Lorenzo block, segment, chunk and outlier of the
+stream lies inside one piece of a field cut at multiples of the block (or chunk), so coding the
+pieces under the field's bound and joining their sections must give the field's stream byte for
+byte, and decoding the pieces must give the field's reconstruction.  A predecessor or a running
+sum carried across a block, an outlier index off by its piece's start, a mean taken over the
+wrong values, or a section placed by a wrong size breaks the equality.  The join itself
+(`oracle/shards.py`) is an independent reading of the stream layout."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import shards
+from error_bounded_lossy_encode_amd import synth
+
+
+def _field(seed: int, n: int, kind: str = "smooth", nan: int = 0, big: int = 0):
+    rng = np.random.default_rng(seed)
+    x = synth.tiny_array(rng, n, kind)
+    if nan:
+        x[rng.integers(0, n, nan)] = np.float32(np.nan)
+    if big:
+        x[rng.integers(0, n, big)] = np.float32(3e38)
+    return x
+
+
+@pytest.mark.parametrize("B", [32, 64, 256, 2048])
+@pytest.mark.parametrize("pieces", [1, 2, 5, 7])
+def test_bitpack_pieces_join_to_the_whole_stream(B, pieces):
+    n = 23 * 2048 + 77
+    x = _field(B + pieces, n, nan=25, big=15)
+    whole = oracle.compress(x, [n], True, 1e-3, B, 15, n)
+    ok, _, bounds, streams = shards.code_pieces(x, True, 1e-3, B, 15, False, None, pieces, 3)
+    assert ok and len(bounds) == min(pieces, (n + B - 1) // B)
+    assert all(a % B == 0 for a, _ in bounds)
+    joined = shards.join(x, [n], 15, B, n, False, None, bounds, streams)
+    assert joined is not None and joined.size == whole.size
+    assert np.array_equal(joined, whole)
+    _, y = oracle.decompress(whole)
+    assert np.array_equal(shards.decode_pieces(streams, 3).view(np.uint32), y.view(np.uint32))
+
+
+@pytest.mark.parametrize("B", [64, 256, 1024])
+def test_centered_pieces_join_to_the_whole_stream(B):
+    n = 17 * 1024 + 301
+    x = _field(7 * B, n, nan=9) + np.float32(40.0)
+    whole = oracle.compress(x, [n], True, 1e-3, B, 15, n, center=True)
+    ok, _, bounds, streams = shards.code_pieces(x, True, 1e-3, B, 15, True, None, 4, 2)
+    joined = shards.join(x, [n], 15, B, n, True, None, bounds, streams)
+    assert np.array_equal(joined, whole)
+    _, y = oracle.decompress(whole)
+    assert np.array_equal(shards.decode_pieces(streams, 2).view(np.uint32), y.view(np.uint32))
+
+
+@pytest.mark.parametrize("V", [1024, 2048, 4096])
+def test_chunk_coder_pieces_join_to_the_whole_stream(V):
+    n = 9 * 4096 + 1234
+    x = _field(V, n, kind="normal", nan=11, big=6)
+    whole = oracle.compress_chunked(x, [n], True, 1e-3, V, 15, n)
+    ok, _, bounds, streams = shards.code_pieces(x, True, 1e-3, 256, 15, False, V, 3, 3)
+    assert all(a % V == 0 for a, _ in bounds)
+    joined = shards.join(x, [n], 15, 256, n, False, V, bounds, streams)
+    assert np.array_equal(joined, whole)
+    _, y = oracle.decompress(whole)
+    assert np.array_equal(shards.decode_pieces(streams, 3).view(np.uint32), y.view(np.uint32))
+
+
+def test_multidim_header_and_raw_fallback_of_the_whole():
+    dims = [5, 33, 64]
+    n = int(np.prod(dims))
+    x = _field(3, n, nan=40)
+    whole = oracle.compress(x, dims, True, 1e-3, 128, 15, n)
+    ok, _, bounds, streams = shards.code_pieces(x, True, 1e-3, 128, 15, False, None, 3, 3)
+    assert np.array_equal(shards.join(x, dims, 15, 128, n, False, None, bounds, streams), whole)
+    # a side list too short for the field's escapes turns the whole stream into a raw copy,
+    # although every piece on its own stays coded
+    side_max = 20
+    whole_raw = oracle.compress(x, dims, True, 1e-3, 128, 15, side_max)
+    assert whole_raw[8] == 1
+    joined = shards.join(x, dims, 15, 128, side_max, False, None, bounds, streams)
+    assert np.array_equal(joined, whole_raw)
+
+
+def test_piece_bounds_cover_the_field_in_aligned_pieces():
+    for n, pieces, align in [(1, 4, 32), (31, 2, 32), (4096, 3, 256), (10**5 + 7, 16, 2048), (2048, 16, 2048)]:
+        b = shards.piece_bounds(n, pieces, align)
+        assert b[0][0] == 0 and b[-1][1] == n
+        assert all(b[k][1] == b[k + 1][0] for k in range(len(b) - 1))
+        assert all(a % align == 0 and a < e for a, e in b)
+        assert len(b) <= pieces
