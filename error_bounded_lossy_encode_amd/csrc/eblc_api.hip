@@ -532,7 +532,7 @@ eblc_status eblc_decompress(eblc_plan_t *plan, const void *in, size_t compressed
     const Workspace &ws = plan->ws;
     const uint8_t *i = static_cast<const uint8_t *>(in);
     plan->nlaunch = 0;
-    hipError_t e = timed(plan, st, "decode_sizes", [&] { return launch_decode_sizes(i, pa, ws, st); });
+    hipError_t e = timed(plan, st, "decode_sizes", [&] { return launch_decode_sizes(i, compressed_bytes, pa, ws, st); });
     if (e == hipSuccess) e = timed(plan, st, "decode_scan", [&] { return launch_scan_decompress(i, compressed_bytes, pa, ws, st); });
     if (e == hipSuccess)
         e = timed(plan, st, "decode", [&] {

@@ -56,6 +56,8 @@ constexpr uint32_t kHeaderBytes = 128;
 constexpr uint32_t kMagic = 0x434C4245u;          /* "EBLC" */
 constexpr uint32_t kVersion = 1;
 constexpr int kMaxKernelsPerCall = 8;
+constexpr uint64_t kTouchMax = 128ull << 20;    /* payloads the decoder's sizes pass pre-reads */
+constexpr int kTouchBatch = 8;                  /* lines in flight per thread in that pass */
 
 /* Device-resident state of a plan (one per plan, in its workspace). */
 struct DevInfo {
@@ -152,7 +154,7 @@ hipError_t launch_scan_compress(const PlanArgs &pa, const Workspace &ws, uint8_t
                                 uint64_t out_capacity, uint64_t *result, hipStream_t stream);
 hipError_t launch_compact(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *out,
                           const uint8_t *widths_src, hipStream_t stream);
-hipError_t launch_decode_sizes(const uint8_t *in, const PlanArgs &pa, const Workspace &ws,
+hipError_t launch_decode_sizes(const uint8_t *in, uint64_t in_bytes, const PlanArgs &pa, const Workspace &ws,
                                hipStream_t stream);
 hipError_t launch_scan_decompress(const uint8_t *in, uint64_t in_bytes, const PlanArgs &pa,
                                   const Workspace &ws, hipStream_t stream);

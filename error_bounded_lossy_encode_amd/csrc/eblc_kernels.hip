@@ -968,8 +968,33 @@ __global__ __launch_bounds__(kBlockThreads) void compact_kernel(const float *__r
 /* One thread per decode chunk: payload words of the chunk = sum of its width bytes; a width above 32
  * flags the stream.  Quads of threads form the groups the scan runs over. */
 __global__ __launch_bounds__(256) void decode_sizes_kernel(const uint8_t *__restrict__ in,
-                                                           PlanArgs pa, Workspace ws) {
+                                                           uint64_t in_bytes, PlanArgs pa, Workspace ws) {
     const uint32_t c = blockIdx.x * 256 + threadIdx.x;
+    /* Touch one word of every 128-byte line of a coded payload of at most kTouchMax bytes, eight
+     * lines in flight per thread, so that the decode kernel finds the stream in the 256 MB
+     * last-level cache even when it was written long before: at the decoder's occupancy its
+     * per-chunk staging loads are bound by their latency.  The header is not validated yet, so
+     * the range is clamped to the caller's bytes (every word read lies below in_bytes). */
+    uint32_t touched = 0;
+    {
+        const uint64_t po = *reinterpret_cast<const uint64_t *>(in + 96);
+        const uint64_t pb = *reinterpret_cast<const uint64_t *>(in + 80);
+        const uint64_t end = in_bytes & ~(uint64_t)3;
+        const bool coded = in[8] != 1 && po < end && pb <= end - po && pb <= kTouchMax;
+        const uint64_t t0 = po & ~(uint64_t)127, t1 = po + pb;
+        const uint64_t lines = coded && t1 > t0 ? (t1 - t0 + 127) / 128 : 0;
+        const uint64_t nthr = (uint64_t)gridDim.x * 256, tid = c;
+        for (uint64_t k = tid; k < lines; k += (uint64_t)kTouchBatch * nthr) {
+            uint32_t v[kTouchBatch];
+#pragma unroll
+            for (int u = 0; u < kTouchBatch; ++u) {
+                const uint64_t l = k + (uint64_t)u * nthr;
+                v[u] = l < lines ? *reinterpret_cast<const uint32_t *>(in + t0 + 128 * l) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < kTouchBatch; ++u) touched |= v[u];
+        }
+    }
     uint32_t sum = 0, bad = 0;
     if (pa.V != 0) {
         /* chunk coder: the stream holds each chunk's word count, bitmap included */
@@ -1009,6 +1034,7 @@ __global__ __launch_bounds__(256) void decode_sizes_kernel(const uint8_t *__rest
     g += dpp<kDppQuadXor2>(0, g);
     if ((threadIdx.x & 3) == 0 && c / kDecChunksPerGroup < pa.dgroups) ws.group_words[c / kDecChunksPerGroup] = g;
     if (bad) atomicOr(&ws.info->width_bad, 1u);
+    asm volatile("" ::"v"(touched));
 }
 
 /* ---- K6b: decode scan + header validation ------------------------------------------------- */
@@ -1281,10 +1307,10 @@ hipError_t launch_compact(const float *x, const PlanArgs &pa, const Workspace &w
     return hipGetLastError();
 }
 
-hipError_t launch_decode_sizes(const uint8_t *in, const PlanArgs &pa, const Workspace &ws,
+hipError_t launch_decode_sizes(const uint8_t *in, uint64_t in_bytes, const PlanArgs &pa, const Workspace &ws,
                                hipStream_t stream) {
     const uint32_t grid = (pa.dchunks + 255) / 256;
-    hipLaunchKernelGGL(decode_sizes_kernel, dim3(grid), dim3(256), 0, stream, in, pa, ws);
+    hipLaunchKernelGGL(decode_sizes_kernel, dim3(grid), dim3(256), 0, stream, in, in_bytes, pa, ws);
     return hipGetLastError();
 }
 
