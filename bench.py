@@ -207,7 +207,7 @@ def main() -> int:
     ap.add_argument("--center", action="store_true",
                     help="Lorenzo centering (bitpack coder): each block's first code against its mean")
     ap.add_argument("--cold-reps", type=int, default=3,
-                    help="repetitions of the MALL-cold measurement (a 1 GiB device write before every "
+                    help="repetitions of the MALL-cold measurement (a 1 GiB device read before every "
                          "compress and decompress call); 0 skips it")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device to device once (counter calibration)")
@@ -331,30 +331,34 @@ def main() -> int:
     kavg = {k: float(np.mean(v)) for k, v in ktimes.items()}
     log("[bench] kernel ms: " + ", ".join(f"{k}={v:.4f}" for k, v in kavg.items()))
 
-    # MALL-cold figures: a 1 GiB device write before every call evicts the 256 MB last-level
-    # cache, so each call reads its input from HBM (fields up to 256 MB otherwise run from it)
+    # MALL-cold figures: reading a 1 GiB buffer before every call evicts the 256 MB last-level
+    # cache, so each call reads its input from HBM (fields up to 256 MB otherwise run from it).
+    # The buffer is written once beforehand: a write before each call would leave dirty lines
+    # whose write-back then overlaps the timed call.
     cold = None
     if args.cold_reps > 0:
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        sink = torch.zeros(1, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
         cc, cd = [], []
         for k in range(args.cold_reps):
             e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            flush.fill_(float(k))
+            sink += flush.sum()
             e[0].record(stream)
             compress_all()
             e[1].record(stream)
-            flush.fill_(float(k) + 0.5)
+            sink += flush.sum()
             e[2].record(stream)
             decompress_all()
             e[3].record(stream)
             torch.cuda.synchronize()
             cc.append(e[0].elapsed_time(e[1]))
             cd.append(e[2].elapsed_time(e[3]))
-        del flush
+        del flush, sink
         assert binding.eblc_plan_status(plan.handle) == binding.EBLC_OK
         cold = {"compress_gbps": round(in_bytes / (float(np.median(cc)) * 1e-3) / 1e9, 3),
                 "decompress_gbps": round(in_bytes / (float(np.median(cd)) * 1e-3) / 1e9, 3),
-                "reps": args.cold_reps, "flush": "1 GiB device write before every compress and decompress call"}
+                "reps": args.cold_reps, "flush": "1 GiB device read before every compress and decompress call"}
         log(f"[bench] cold: compress {cold['compress_gbps']} GB/s, decompress {cold['decompress_gbps']} GB/s")
 
     # stream facts from the headers (host copies of 128 bytes, outside the timed region)
