@@ -356,6 +356,42 @@ __device__ __forceinline__ void decode_tiles(const uint32_t *pl, uint32_t t0, ui
     }
 }
 
+/* Decode 4 NQ full tiles from tile t0 on, four at a time: each tile's transpose gives one code
+ * per lane (value 64 t + lane), the four tiles' codes go through a 1 KB LDS scratch so that lane
+ * l holds values 4 l .. 4 l + 3 of the 256, and then one in-lane running sum, one wave scan of
+ * the lane totals and the carry undo the first difference for all four tiles, and one 128-bit
+ * store writes the lane's four values.  The scratch belongs to the wave; LDS accesses of one
+ * wave are performed in order, so the next group's writes cannot pass this group's read. */
+template <int V, int NQ, bool STRIDED>
+__device__ __forceinline__ void decode_quads(const uint32_t *pl, uint32_t t0, uint32_t wmax, const Transpose &tr,
+                                             float s, uint32_t &carry, float *__restrict__ out, const Layout &lo,
+                                             uint32_t cbase, uint32_t *sx) {
+    using Gm = ChunkGeom<V>;
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t h = lane >> 5, b = lane & 31;
+#pragma unroll
+    for (int g = 0; g < NQ; ++g) {
+        const uint32_t t = t0 + 4u * g;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t word = b < wmax ? pl[b * Gm::PS + 2u * (t + k) + h] : 0u;
+            sx[64 * k + lane] = (uint32_t)unzigzag(tr(word));
+        }
+        wave_lds_sync();
+        const uint4 v = reinterpret_cast<const uint4 *>(sx)[lane];
+        const uint32_t r1 = v.x + v.y, r2 = r1 + v.z, r3 = r2 + v.w;
+        const uint32_t incl = wave_incl_scan(r3);
+        const uint32_t base = carry + incl - r3;
+        carry += readlane(incl, 63);
+        float4 o;
+        o.x = (float)(int32_t)(base + v.x) * s;
+        o.y = (float)(int32_t)(base + r1) * s;
+        o.z = (float)(int32_t)(base + r2) * s;
+        o.w = (float)(int32_t)(base + r3) * s;
+        store4<STRIDED>(out, lo, (uint64_t)cbase + (uint64_t)t * kCTile + 4u * lane, o);
+    }
+}
+
 /* One wave per chunk.  The chunk's bitmap sits in two VGPRs (lane l: bitmap words l and
  * 64 + l); its popcount must equal the chunk's word count minus the bitmap, else the stream is
  * flagged.  Un-RZE rebuilds the planes below the highest nonzero one in LDS: per 64-word batch
@@ -367,6 +403,7 @@ __global__ __launch_bounds__(kBlockThreads) void chunk_decode_kernel(const uint8
                                                                      Workspace ws, float *__restrict__ out) {
     using Gm = ChunkGeom<V>;
     __shared__ uint32_t s_words[kWavesPerBlock][Gm::LDSW];
+    __shared__ uint4 s_x4[kWavesPerBlock][4 * kCTile / 4];
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t c = blockIdx.x * kWavesPerBlock + wave;
@@ -443,8 +480,9 @@ __global__ __launch_bounds__(kBlockThreads) void chunk_decode_kernel(const uint8
     const float s = info->dec_s;
     uint32_t carry = 0;
     if (cnt == (uint32_t)V) {
+        uint32_t *sx = reinterpret_cast<uint32_t *>(s_x4[wave]);
         for (uint32_t t = 0; t < (uint32_t)Gm::TILES; t += 8)
-            decode_tiles<V, 8, true, STRIDED>(pl, t, wmax, tr, s, carry, out, pa.lay, cbase, n);
+            decode_quads<V, 2, STRIDED>(pl, t, wmax, tr, s, carry, out, pa.lay, cbase, sx);
     } else {
         const uint32_t ntiles = (cnt + kCTile - 1) / kCTile;
         for (uint32_t t = 0; t < ntiles; ++t)
