@@ -970,21 +970,23 @@ __global__ __launch_bounds__(kBlockThreads) void compact_kernel(const float *__r
 __global__ __launch_bounds__(256) void decode_sizes_kernel(const uint8_t *__restrict__ in,
                                                            uint64_t in_bytes, PlanArgs pa, Workspace ws) {
     const uint32_t c = blockIdx.x * 256 + threadIdx.x;
-    /* Touch one word of every 128-byte line of a well-compressed payload (at most 128 bytes per
-     * decode chunk for each of the kTouchBatch loads a thread keeps in flight, and at most
-     * kTouchMax bytes in all), so that the decode kernel finds the stream in the 256 MB
-     * last-level cache even when it was written long before: with so few words per chunk, its
-     * staging loads are bound by their latency at its occupancy.  Such a payload takes one
-     * round of loads here.  The header is not validated yet, so the range is clamped to the
+    /* Touch one word of every 128-byte line of a well-compressed stream's sections after the
+     * header up to the payload's end -- sizes, block means, payload -- when they average at most
+     * 128 bytes per decode chunk for each of the kTouchBatch loads a thread keeps in flight (and
+     * at most kTouchMax bytes in all), so that the decode kernel finds them in the 256 MB
+     * last-level cache even when the stream was written long before: with so few words per
+     * chunk, its staging loads are bound by their latency at its occupancy.  Such a stream takes
+     * one round of loads here.  The header is not validated yet, so the range is clamped to the
      * caller's bytes (every word read lies below in_bytes). */
     uint32_t touched = 0;
     {
         const uint64_t po = *reinterpret_cast<const uint64_t *>(in + 96);
         const uint64_t pb = *reinterpret_cast<const uint64_t *>(in + 80);
         const uint64_t end = in_bytes & ~(uint64_t)3;
-        const bool coded = in[8] != 1 && po < end && pb <= end - po && pb <= kTouchMax &&
-                           pb <= (uint64_t)pa.dchunks * (128u * kTouchBatch);
-        const uint64_t t0 = po & ~(uint64_t)127, t1 = po + pb;
+        const bool coded = in[8] != 1 && po >= kHeaderBytes && po < end && pb <= end - po &&
+                           po + pb - kHeaderBytes <= kTouchMax &&
+                           po + pb - kHeaderBytes <= (uint64_t)pa.dchunks * (128u * kTouchBatch);
+        const uint64_t t0 = kHeaderBytes, t1 = po + pb;
         const uint64_t lines = coded && t1 > t0 ? (t1 - t0 + 127) / 128 : 0;
         const uint64_t nthr = (uint64_t)gridDim.x * 256, tid = c;
         for (uint64_t k = tid; k < lines; k += (uint64_t)kTouchBatch * nthr) {
