@@ -58,6 +58,7 @@ constexpr uint32_t kVersion = 1;
 constexpr int kMaxKernelsPerCall = 8;
 constexpr uint64_t kTouchMax = 128ull << 20;    /* payloads the decoder's sizes pass pre-reads */
 constexpr int kTouchBatch = 8;                  /* lines in flight per thread in that pass */
+constexpr int kResolveBatch = 8;                /* range partials in flight per thread of the resolve */
 
 /* Device-resident state of a plan (one per plan, in its workspace). */
 struct DevInfo {

@@ -122,10 +122,21 @@ __global__ __launch_bounds__(kScanThreads) void range_resolve_kernel(const float
                                                                      double eps) {
     __shared__ float s_mn[kScanThreads / kWave], s_mx[kScanThreads / kWave];
     float a = INFINITY, b = -INFINITY;
-    for (uint32_t i = threadIdx.x; i < nparts; i += kScanThreads) {
-        const float2 v = reinterpret_cast<const float2 *>(part)[i];
-        a = fminf(a, v.x);
-        b = fmaxf(b, v.y);
+    /* kResolveBatch partials per thread in flight before any is folded (min and max do not
+     * depend on the order) */
+    const float2 *p2 = reinterpret_cast<const float2 *>(part);
+    for (uint32_t i0 = threadIdx.x; i0 < nparts; i0 += kResolveBatch * kScanThreads) {
+        float2 v[kResolveBatch];
+#pragma unroll
+        for (int u = 0; u < kResolveBatch; ++u) {
+            const uint32_t i = i0 + (uint32_t)u * kScanThreads;
+            v[u] = i < nparts ? p2[i] : make_float2(INFINITY, -INFINITY);
+        }
+#pragma unroll
+        for (int u = 0; u < kResolveBatch; ++u) {
+            a = fminf(a, v[u].x);
+            b = fmaxf(b, v[u].y);
+        }
     }
     for (int o = 32; o >= 1; o >>= 1) {
         a = fminf(a, __shfl_xor(a, o));
@@ -687,16 +698,19 @@ __global__ __launch_bounds__(kScanThreads) void scan_compress_kernel(PlanArgs pa
                                                                      uint64_t *result) {
     __shared__ uint32_t s_hdr[32];
     __shared__ uint32_t s_fits;
+    DevInfo *info = ws.info;
+    /* the bound's fields, read before the scan so that their loads overlap it */
+    const uint32_t valid0 = info->valid;
+    const float eb0 = info->eb_f, s0 = info->s, r0 = info->r;
     uint32_t tot[2];
     block_scan2(ws.group_words, ws.group_esc, ws.gpre_words, ws.gpre_esc, pa.ngroups, tot);
-    DevInfo *info = ws.info;
     if (threadIdx.x == 0) {
         const uint64_t n = pa.n;
         const uint64_t S = tot[0], m = tot[1];
         const uint64_t raw_total = kHeaderBytes + align16(4 * n);
         const uint64_t payload_off = kHeaderBytes + pa.wsec + pa.msec;
         const uint64_t lossy_total = payload_off + align16(4 * S) + 2 * align16(4 * m);
-        const bool valid = info->valid != 0;
+        const bool valid = valid0 != 0;
         const bool raw = !valid || m > pa.side_max || lossy_total > raw_total;
         uint64_t f_m, f_pb, f_po, f_oi, f_ov, f_tot;
         if (raw) {
@@ -735,9 +749,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_compress_kernel(PlanArgs pa
         const uint64_t u64s[8] = {n, 0, f_m, f_pb, kHeaderBytes, f_po, f_oi, f_ov};
         h[12] = (uint32_t)u64s[0];
         h[13] = (uint32_t)(u64s[0] >> 32);
-        h[14] = __float_as_uint(info->eb_f);
-        h[15] = __float_as_uint(info->s);
-        h[16] = __float_as_uint(info->r);
+        h[14] = __float_as_uint(eb0);
+        h[15] = __float_as_uint(s0);
+        h[16] = __float_as_uint(r0);
         h[17] = (!raw && pa.center) ? 1u : 0u; /* flags: bit 0 = centered */
         for (int a = 2; a < 8; ++a) {
             h[18 + 2 * (a - 2)] = (uint32_t)u64s[a];
@@ -1051,13 +1065,16 @@ __device__ __forceinline__ uint64_t ld64(const uint32_t *h, int i) {
 __global__ __launch_bounds__(kScanThreads) void scan_decompress_kernel(const uint8_t *__restrict__ in,
                                                                        uint64_t in_bytes, PlanArgs pa,
                                                                        Workspace ws) {
+    /* the header, staged in LDS before the scan so that its loads overlap it (block_scan2
+     * synchronizes the workgroup before it returns) */
+    __shared__ uint32_t s_h[32];
+    if (threadIdx.x < 32) s_h[threadIdx.x] = reinterpret_cast<const uint32_t *>(in)[threadIdx.x];
     uint32_t tot[2];
     block_scan2(ws.group_words, nullptr, ws.gpre_words, nullptr, pa.dgroups, tot);
     if (threadIdx.x != 0) return;
     DevInfo *info = ws.info;
-    const uint32_t *h = reinterpret_cast<const uint32_t *>(in);
     uint32_t hw[32];
-    for (int i = 0; i < 32; ++i) hw[i] = h[i];
+    for (int i = 0; i < 32; ++i) hw[i] = s_h[i];
     const uint64_t n = pa.n;
     const uint32_t mode = hw[2] & 0xff, rank = (hw[2] >> 8) & 0xff, log2seg = (hw[2] >> 16) & 0xff;
     const uint32_t T = hw[2] >> 24, B = hw[3];
