@@ -327,11 +327,16 @@ __device__ __forceinline__ int32_t block_mean(uint32_t lo, int32_t hi, uint64_t 
     return (int32_t)qd;
 }
 
+/* Centering modes of the encoder: none; blocks of at most one tile whose code sums fit 32 bits
+ * (B <= 256 and T + log2 B <= 29, the defaults among them); any block.  The first keeps neither
+ * the per-tile totals nor the 64-bit mean of the last, and so fewer registers. */
+constexpr int kCenterOff = 0, kCenterTile = 1, kCenterAny = 2;
+
 /* One encode chunk of kEncTiles tiles.  Pass 1 codes every tile and records the segment widths
  * in LDS (the codes stay in VGPRs); one wave scan of the widths gives every segment's word
  * offset in the chunk; pass 2 packs each tile at those offsets.  `carry` is the code of the
  * value before the chunk when the chunk does not start a Lorenzo block. */
-template <bool FULL, bool STRIDED, bool CENTER>
+template <bool FULL, bool STRIDED, int CM>
 __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const Layout &lo, uint64_t cbase, uint64_t n,
                                              const QParams &qp, uint32_t bmask, int32_t carry,
                                              uint32_t *pay, uint8_t *wid, uint32_t *emask_chunk,
@@ -426,11 +431,12 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
             int32_t shi;
             w[t] = finish_tile<FULL>(q[t], cbase + (uint64_t)t * kEncTile + V * lane, n, reset, carry, z[t],
                                      slo, shi);
-            if (CENTER && in_tile) {
+            if (CM == kCenterTile || (CM == kCenterAny && in_tile)) {
                 const uint32_t seglen = B / V; /* lanes per block */
                 /* narrow codes: one exact 32-bit sum; else the two halves */
+                const bool narrow_sums = CM == kCenterTile || narrow;
                 uint32_t lo_s, hi_s = 0;
-                if (narrow) {
+                if (narrow_sums) {
                     lo_s = seg_allsum(slo + ((uint32_t)shi << 16), seglen);
                 } else {
                     lo_s = seg_allsum(slo, seglen);
@@ -439,20 +445,20 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
                 const uint64_t e0 = cbase + (uint64_t)t * kEncTile + V * lane;
                 if (lane_at_block && e0 < n) {
                     const uint64_t c = (n - e0 < (uint64_t)B) ? n - e0 : (uint64_t)B;
-                    const int32_t mu = narrow ? block_mean32((int32_t)lo_s, (uint32_t)c, log2B)
-                                              : block_mean(lo_s, (int32_t)hi_s, c, log2B);
+                    const int32_t mu = narrow_sums ? block_mean32((int32_t)lo_s, (uint32_t)c, log2B)
+                                                   : block_mean(lo_s, (int32_t)hi_s, c, log2B);
                     z[t][0] = zigzag((int32_t)((uint32_t)unzigzag(z[t][0]) - (uint32_t)mu));
                     means[e0 >> log2B] = mu;
                 }
                 w[t] = seg_width(z[t]);
-            } else if (CENTER) {
+            } else if (CM == kCenterAny) {
                 tlo[t] = seg_allsum(slo, 64);
                 thi[t] = (int32_t)seg_allsum((uint32_t)shi, 64);
             }
             if (j == 0) wid[t * kSegsPerEncTile + g] = (uint8_t)w[t];
         }
     }
-    if (CENTER && !in_tile) {
+    if (CM == kCenterAny && !in_tile) {
         /* blocks of B / 256 tiles: each block's sum from its tiles' totals, at its first tile */
         const uint32_t tpb = B / kEncTile;
 #pragma unroll
@@ -524,7 +530,7 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
  * words in its scratch slot, its width bytes (into the stream, or into staging when the output
  * buffer cannot hold them), its word and escape counts and the escape bitmask of every tile
  * with an escape; per workgroup, the sums the device-wide scan runs over. */
-template <bool STRIDED, bool CENTER>
+template <bool STRIDED, int CM>
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(
     const float *__restrict__ x, PlanArgs pa, Workspace ws, uint8_t *__restrict__ widths_dst,
     uint64_t widths_bytes) {
@@ -567,11 +573,11 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
         uint32_t *stage_idx = s_stage[wave][0];
         uint32_t *stage_val = s_stage[wave][1];
         if (cbase + kEncChunk <= pa.n)
-            encode_chunk<true, STRIDED, CENTER>(x, pa.lay, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk,
+            encode_chunk<true, STRIDED, CM>(x, pa.lay, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk,
                                                 stage_idx, stage_val, st, pa.log2B, ws.means, narrow,
                                                 ws.scratch + cbase);
         else
-            encode_chunk<false, STRIDED, CENTER>(x, pa.lay, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk,
+            encode_chunk<false, STRIDED, CM>(x, pa.lay, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk,
                                                  stage_idx, stage_val, st, pa.log2B, ws.means, narrow,
                                                  ws.scratch + cbase);
         /* widths -> stream (or staging) */
@@ -1296,18 +1302,24 @@ hipError_t launch_range(const float *x, const PlanArgs &pa, const Workspace &ws,
 
 hipError_t launch_encode(const float *x, const PlanArgs &pa, const Workspace &ws,
                          uint8_t *widths_dst, uint64_t widths_bytes, hipStream_t stream) {
-    if (pa.lay.strided && pa.center)
-        hipLaunchKernelGGL((encode_kernel<true, true>), dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa, ws,
-                           widths_dst, widths_bytes);
-    else if (pa.lay.strided)
-        hipLaunchKernelGGL((encode_kernel<true, false>), dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa, ws,
-                           widths_dst, widths_bytes);
-    else if (pa.center)
-        hipLaunchKernelGGL((encode_kernel<false, true>), dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa, ws,
-                           widths_dst, widths_bytes);
-    else
-        hipLaunchKernelGGL((encode_kernel<false, false>), dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa,
-                           ws, widths_dst, widths_bytes);
+    const int cm = !pa.center ? kCenterOff
+                   : (pa.B <= (uint32_t)kEncTile && pa.T + pa.log2B <= 29) ? kCenterTile : kCenterAny;
+    const dim3 grid(pa.ngroups), block(kEncThreads);
+    if (pa.lay.strided) {
+        if (cm == kCenterTile)
+            hipLaunchKernelGGL((encode_kernel<true, kCenterTile>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+        else if (cm == kCenterAny)
+            hipLaunchKernelGGL((encode_kernel<true, kCenterAny>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+        else
+            hipLaunchKernelGGL((encode_kernel<true, kCenterOff>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+    } else {
+        if (cm == kCenterTile)
+            hipLaunchKernelGGL((encode_kernel<false, kCenterTile>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+        else if (cm == kCenterAny)
+            hipLaunchKernelGGL((encode_kernel<false, kCenterAny>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+        else
+            hipLaunchKernelGGL((encode_kernel<false, kCenterOff>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+    }
     return hipGetLastError();
 }
 
