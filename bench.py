@@ -5,17 +5,19 @@ the path), with the inputs already resident in HBM.  The default workload is the
 wavefield snapshot (eight Ricker wavelets, 40 % quiescent zeros) at relative bound 1e-3, block
 256, outlier_log2 15.  Other workloads: c1 (2^20 sum of sines), c2 (4096^2 Gaussian random
 field), c4 (2^28 AR(1) with 1 % spikes), c5_1e-6 / c5_1e-2 (64 snapshots of 256^3 compressed
-back to back on one stream, then decompressed back to back).  By default the fields are
-compressed with eblc_compress_batch (no host wait; lengths arrive in device result records) and
-decompressed with their buffers' capacity; --api sync uses eblc_compress, which waits once per
-field to return its length.
+back to back, then decompressed back to back).  By default the fields are compressed with
+eblc_compress_batch (no host wait; lengths arrive in device result records) and decompressed
+with eblc_decompress_batch and their buffers' capacity; a workload of several fields uses the
+plan option lanes=4, which keeps four fields in flight on the plan's own streams.  --api sync
+uses eblc_compress, which waits once per field to return its length, and eblc_decompress.
 
 Prints ONE JSON line: `value` is the round-trip throughput in GB/s of input bytes (input bytes
 / (compress + decompress time)); `compress_gbps`, `decompress_gbps` and `ratio` are given
 separately; `roofline` is the encode kernel's achieved algorithmic bandwidth against the HBM
-peak (launch durations from HIP events the library records on the caller's stream), with the
-rocprofv3-measured traffic when a counter summary of the same kernel source exists under
-profiles/; `cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
+peak, from the mean duration of its launches in the timed steps (HIP event pairs the library
+records around every launch, on the stream the launch runs on), with the rocprofv3-measured
+traffic when a counter summary of the same kernel source exists under profiles/;
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -193,7 +195,16 @@ def main() -> int:
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-steps", type=int, default=5)
+    ap.add_argument("--lanes", type=int, default=4,
+                    help="plan option lanes=K for workloads of several fields: the batch calls keep K "
+                         "fields in flight on K streams (the streams are the same for every K)")
+    ap.add_argument("--kernel-events", choices=["on", "off"], default="on",
+                    help="on: the library records a HIP event pair around every encode and decode launch "
+                         "of the timed steps (up to 8192 launches), for the rooflines")
+    ap.add_argument("--breakdown-steps", type=int, default=2,
+                    help="untimed steps after the timed ones with an event pair around every launch, "
+                         "for the per-kernel breakdown (event records delay the stream, so the timed "
+                         "steps time only the two roofline kernels)")
     ap.add_argument("--api", choices=["batch", "sync"], default="batch",
                     help="batch: eblc_compress_batch (no host wait) and decompress by buffer capacity; "
                          "sync: eblc_compress per field, which waits to return each length")
@@ -255,8 +266,11 @@ def main() -> int:
             padded.append((buf[offset:], dims, opts))
         items = padded
         desc += f"; stored with a {h}-element halo on every side (strides {strides})"
-    log(f"[bench] {len(items)} field(s), n={n} dims={dims0} opts={opts0} strides={strides}")
-    plan = binding.Plan(dims0, opts0, 0, strides=strides)
+    plan_opts = opts0
+    if len(items) > 1 and args.lanes > 1:
+        plan_opts = opts0 + f";lanes={args.lanes}"
+    log(f"[bench] {len(items)} field(s), n={n} dims={dims0} opts={plan_opts} strides={strides}")
+    plan = binding.Plan(dims0, plan_opts, 0, strides=strides)
     outs = [torch.empty(plan.max_bytes, dtype=torch.uint8, device=dev) for _ in items]
     ys = [torch.empty_like(x) for x, _, _ in items]
     stream = torch.cuda.current_stream()
@@ -277,6 +291,10 @@ def main() -> int:
     def decompress_all():
         # with the batch API the host never reads the lengths: each stream is decompressed with
         # its buffer's capacity and its own length comes from its header on the device
+        if args.api == "batch":
+            st = binding.eblc_decompress_batch(plan.handle, outs, ys, nbytes, stream=stream)
+            assert st == binding.EBLC_OK, binding.eblc_status_string(st)
+            return
         for i in range(len(items)):
             st = binding.eblc_decompress(plan.handle, outs[i], nbytes[i], ys[i], stream=stream)
             assert st == binding.EBLC_OK, binding.eblc_status_string(st)
@@ -287,9 +305,14 @@ def main() -> int:
     torch.cuda.synchronize()
     assert binding.eblc_plan_status(plan.handle) == binding.EBLC_OK
 
-    # timed region: exactly K steps, bracketed by device syncs
+    # timed region: exactly K steps, bracketed by device syncs.  The library records an event
+    # pair around each kernel launch of these steps on the stream it runs on (its own lane
+    # streams included), up to 8192 launches: the per-kernel times below.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    timed_launches = min(8192, args.steps * len(items) * 2)
+    if args.kernel_events == "on":
+        assert binding.eblc_plan_set_profiling(plan.handle, timed_launches, "encode,decode") == binding.EBLC_OK
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -313,23 +336,23 @@ def main() -> int:
     log(f"[bench] step {wall * 1e3:.3f} ms; compress {comp_ms:.3f} ms; decompress {decomp_ms:.3f} ms; "
         f"streams {total_stream} B")
 
-    # per-kernel times: HIP event pairs the library records around each launch on this stream
-    binding.eblc_plan_set_profiling(plan.handle, True)
-    ktimes = {}
-    for _ in range(args.profile_steps):
-        for i, (x, _, _) in enumerate(items):
-            st, nb = binding.eblc_compress(plan.handle, x, outs[i], stream=stream)
-            assert st == binding.EBLC_OK
-            for name, ms in binding.eblc_plan_kernel_times(plan.handle):
-                ktimes.setdefault(name, []).append(ms)
-        for i in range(len(items)):
-            st = binding.eblc_decompress(plan.handle, outs[i], nbytes[i], ys[i], stream=stream)
-            assert st == binding.EBLC_OK
-            for name, ms in binding.eblc_plan_kernel_times(plan.handle):
-                ktimes.setdefault(name, []).append(ms)
-    binding.eblc_plan_set_profiling(plan.handle, False)
-    kavg = {k: float(np.mean(v)) for k, v in ktimes.items()}
-    log("[bench] kernel ms: " + ", ".join(f"{k}={v:.4f}" for k, v in kavg.items()))
+    # roofline kernels: mean duration of encode and decode over their launches in the timed steps
+    kavg, kcount = {}, {}
+    if args.kernel_events == "on":
+        for name, ms, cnt in binding.eblc_plan_kernel_times(plan.handle):
+            kavg[name], kcount[name] = ms, cnt
+        log("[bench] timed steps, kernel ms: " + ", ".join(f"{k}={v:.4f} (x{kcount[k]})" for k, v in kavg.items()))
+    # breakdown of every kernel, from extra steps after the timed ones
+    kall = {}
+    if args.breakdown_steps > 0:
+        assert binding.eblc_plan_set_profiling(plan.handle, min(8192, args.breakdown_steps * len(items) * 8)) \
+            == binding.EBLC_OK
+        for _ in range(args.breakdown_steps):
+            compress_all()
+            decompress_all()
+        kall = {name: ms for name, ms, _ in binding.eblc_plan_kernel_times(plan.handle)}
+        log("[bench] breakdown, kernel ms: " + ", ".join(f"{k}={v:.4f}" for k, v in kall.items()))
+    binding.eblc_plan_set_profiling(plan.handle, 0)
 
     # MALL-cold figures: reading a 1 GiB buffer before every call evicts the 256 MB last-level
     # cache, so each call reads its input from HBM (fields up to 256 MB otherwise run from it).
@@ -405,15 +428,17 @@ def main() -> int:
             tag += "_center"
     enc_bytes = 4 * n + sizes + avg_payload
     dec_bytes = sizes + avg_payload + 4 * n
-    enc_gbps = enc_bytes / (kavg["encode"] * 1e-3) / 1e9
-    dec_gbps = dec_bytes / (kavg["decode"] * 1e-3) / 1e9
     traffic = profiling.read_traffic(os.path.join(PROFILES, f"traffic_{tag}.txt"))
 
-    def roof(name, achieved, kernel_key):
-        t = None if traffic is None else traffic.get(kernel_key)
+    def roof(name, alg_bytes, key):
+        # algorithmic bytes per launch over the mean launch duration in the timed steps
+        if key not in kavg:
+            return None
+        achieved = alg_bytes / (kavg[key] * 1e-3) / 1e9
+        t = None if traffic is None else traffic.get(name)
         return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None if t is None else round(t),
-                "kernel": name}
+                "kernel": name, "launches": kcount[key]}
 
     result = {
         "metric": METRIC,
@@ -429,18 +454,20 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": desc, "fields": len(items), "n": n, "dims": dims0, "options": opts0,
-                   "strides": strides,
+                   "strides": strides, "lanes": args.lanes if len(items) > 1 else 1,
                    "step": "compress all fields, then decompress all streams",
-                   "api": "eblc_compress_batch + eblc_decompress" if args.api == "batch"
+                   "api": "eblc_compress_batch + eblc_decompress_batch" if args.api == "batch"
                    else "eblc_compress (waits per field) + eblc_decompress"},
         "compress_gbps": round(in_bytes / (comp_ms * 1e-3) / 1e9, 3),
         "decompress_gbps": round(in_bytes / (decomp_ms * 1e-3) / 1e9, 3),
         "ratio": round(in_bytes / total_stream, 4),
         "compressed_bytes": total_stream,
         "outliers": int(sum(outliers)),
-        "kernel_ms": {k: round(v, 5) for k, v in kavg.items()},
-        "roofline": roof(kernels[0], enc_gbps, kernels[0]),
-        "roofline_decode": roof(kernels[1], dec_gbps, kernels[1]),
+        "kernel_ms": {k: round(v, 5) for k, v in kall.items()},
+        "kernel_ms_note": "every kernel, event pairs in untimed steps after the timed ones; the rooflines use "
+                          "encode and decode launches timed inside the timed steps",
+        "roofline": roof(kernels[0], enc_bytes, "encode"),
+        "roofline_decode": roof(kernels[1], dec_bytes, "decode"),
         "algorithmic_bytes_per_launch": {"encode": round(enc_bytes), "decode": round(dec_bytes)},
         "cold": cold,
         "max_abs_err": err_max,

@@ -44,7 +44,7 @@ class eblc_limits_t(ctypes.Structure):
 
 EXPORTS = ["eblc_abi_version", "eblc_plan_create", "eblc_plan_limits", "eblc_max_compressed_bytes",
            "eblc_payload_alignment", "eblc_compress", "eblc_compress_async", "eblc_compress_batch",
-           "eblc_decompress", "eblc_plan_status", "eblc_plan_destroy", "eblc_status_string",
+           "eblc_decompress", "eblc_decompress_batch", "eblc_plan_status", "eblc_plan_destroy", "eblc_status_string",
            "eblc_plan_set_profiling", "eblc_plan_kernel_times"]
 
 _lib = None
@@ -78,16 +78,18 @@ def lib():
     L.eblc_compress_batch.restype = I
     L.eblc_decompress.argtypes = [P, P, SZ, P, P, P]
     L.eblc_decompress.restype = I
+    L.eblc_decompress_batch.argtypes = [P, I, ctypes.POINTER(P), ctypes.POINTER(SZ), ctypes.POINTER(P), P]
+    L.eblc_decompress_batch.restype = I
     L.eblc_plan_status.argtypes = [P, P]
     L.eblc_plan_status.restype = I
     L.eblc_plan_destroy.argtypes = [P]
     L.eblc_plan_destroy.restype = None
     L.eblc_status_string.argtypes = [I]
     L.eblc_status_string.restype = ctypes.c_char_p
-    L.eblc_plan_set_profiling.argtypes = [P, I]
+    L.eblc_plan_set_profiling.argtypes = [P, I, ctypes.c_char_p]
     L.eblc_plan_set_profiling.restype = I
     L.eblc_plan_kernel_times.argtypes = [P, ctypes.POINTER(ctypes.c_char_p),
-                                         ctypes.POINTER(ctypes.c_float), I]
+                                         ctypes.POINTER(ctypes.c_float), ctypes.POINTER(I), I]
     L.eblc_plan_kernel_times.restype = I
     _lib = L
     return L
@@ -171,6 +173,17 @@ def eblc_compress_batch(plan, xs, outs, results, capacities=None, stream=None) -
     return int(lib().eblc_compress_batch(plan, k, ins, os_, cs, _ptr(results), _stream_handle(stream)))
 
 
+def eblc_decompress_batch(plan, streams, ys, sizes=None, stream=None) -> int:
+    """Enqueue len(streams) decompressions (uint8 device tensors -> float32 device tensors);
+    sizes: readable bytes of each stream (default: its tensor's size).  Returns the status."""
+    k = len(streams)
+    ins = (ctypes.c_void_p * max(k, 1))(*[t.data_ptr() for t in streams])
+    outs = (ctypes.c_void_p * max(k, 1))(*[t.data_ptr() for t in ys])
+    szs = [t.numel() * t.element_size() for t in streams] if sizes is None else sizes
+    cs = (ctypes.c_size_t * max(k, 1))(*[int(c) for c in szs])
+    return int(lib().eblc_decompress_batch(plan, k, ins, cs, outs, _stream_handle(stream)))
+
+
 def result_records(results) -> list:
     """[(compressed_bytes, status)] from a tensor of eblc_result_t records (copied to host)."""
     import numpy as np
@@ -194,18 +207,23 @@ def eblc_plan_destroy(plan) -> None:
         lib().eblc_plan_destroy(plan)
 
 
-def eblc_plan_set_profiling(plan, enable: bool) -> int:
-    return int(lib().eblc_plan_set_profiling(plan, 1 if enable else 0))
+def eblc_plan_set_profiling(plan, max_launches: int, kernels: str | None = None) -> int:
+    """Record an event pair around each of the plan's next max_launches launches (0: off) of
+    the kernels named in the comma-separated `kernels` (None: every kernel)."""
+    return int(lib().eblc_plan_set_profiling(plan, int(max_launches),
+                                             None if kernels is None else kernels.encode()))
 
 
-def eblc_plan_kernel_times(plan, max_kernels: int = 8):
-    """[(kernel name, milliseconds)] of the last call, in launch order."""
+def eblc_plan_kernel_times(plan, max_kernels: int = 16):
+    """[(kernel name, mean milliseconds, launches)] over the launches recorded since the last
+    read, in order of first launch; clears the records."""
     names = (ctypes.c_char_p * max_kernels)()
     ms = (ctypes.c_float * max_kernels)()
-    k = lib().eblc_plan_kernel_times(plan, names, ms, max_kernels)
+    cnt = (ctypes.c_int * max_kernels)()
+    k = lib().eblc_plan_kernel_times(plan, names, ms, cnt, max_kernels)
     if k < 0:
         raise RuntimeError("kernel times unavailable (profiling off or device error)")
-    return [(names[i].decode(), float(ms[i])) for i in range(min(k, max_kernels))]
+    return [(names[i].decode(), float(ms[i]), int(cnt[i])) for i in range(min(k, max_kernels))]
 
 
 class Plan:

@@ -19,8 +19,18 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 using namespace eblc;
+
+namespace eblc {
+thread_local LaunchEvents g_launch_events;
+}  // namespace eblc
+
+namespace {
+constexpr int kMaxLanes = 8;               /* workspaces (and streams) a batch call may use */
+constexpr size_t kMaxTimedLaunches = 8192; /* event pairs the measurement hook may hold */
+}  // namespace
 
 struct eblc_plan {
     int device = 0;
@@ -30,13 +40,20 @@ struct eblc_plan {
     bool rel = true;
     double eps = 1e-4;
     PlanArgs pa{};
-    Workspace ws{};
+    /* lane k's workspace; single calls use lane 0 on the caller's stream, batch calls spread
+     * their fields over the lanes, each with its own stream */
+    int lanes = 1;
+    Workspace ws[kMaxLanes] = {};
     void *ws_base = nullptr;
+    hipStream_t lane_stream[kMaxLanes] = {};
+    hipEvent_t fork_ev = nullptr;
+    hipEvent_t join_ev[kMaxLanes] = {};
     eblc_result_t *host_result = nullptr; /* pinned host slot the synchronous compress reads */
-    bool profiling = false;
-    hipEvent_t ev[2 * kMaxKernelsPerCall] = {};
-    const char *names[kMaxKernelsPerCall] = {};
-    int nlaunch = 0;
+    /* measurement hook: an event pair per launch, up to the pool's size, since enabling */
+    std::vector<hipEvent_t> ev_pool;
+    std::vector<const char *> ev_names;
+    size_t ev_used = 0;
+    std::string ev_filter;      /* ",name,name," of the kernels to time; empty: every kernel */
 };
 
 namespace {
@@ -96,6 +113,7 @@ struct Options {
     bool chunk_coder = false;   /* coder=chunk: Quant -> Diff -> Bitshuffle -> RZE */
     bool center = false;        /* center=1: Lorenzo centering (bitpack coder) */
     uint32_t V = 0;             /* chunk coder: values per chunk */
+    uint32_t lanes = 1;         /* fields of a batch call in flight at once */
 };
 
 /* Options string ("Provider layout": a provider-defined string; DevitoPRO passes the relative
@@ -112,7 +130,7 @@ eblc_status parse_options(const char *opts, Options *o) {
         return EBLC_OK;
     }
     bool seen_eb = false, seen_block = false, seen_t = false, seen_coder = false, seen_chunk = false;
-    bool seen_center = false;
+    bool seen_center = false, seen_lanes = false;
     uint64_t chunk_bytes = 8192;
     size_t pos = 0;
     for (;;) {
@@ -154,6 +172,12 @@ eblc_status parse_options(const char *opts, Options *o) {
                     (chunk_bytes != 4096 && chunk_bytes != 8192 && chunk_bytes != 16384))
                     return EBLC_INVALID_ARGUMENT;
                 seen_chunk = true;
+            } else if (key == "lanes") {
+                uint64_t k;
+                if (seen_lanes || !parse_u64(val, &k) || k < 1 || k > (uint64_t)kMaxLanes)
+                    return EBLC_INVALID_ARGUMENT;
+                seen_lanes = true;
+                o->lanes = (uint32_t)k;
             } else if (key == "side_max") {
                 uint64_t m;
                 if (o->side_set || !parse_u64(val, &m)) return EBLC_INVALID_ARGUMENT;
@@ -211,17 +235,21 @@ PlanArgs call_args(const eblc_plan *plan, const void *field) {
 
 eblc_status hip_status(hipError_t e) { return e == hipSuccess ? EBLC_OK : EBLC_DEVICE_ERROR; }
 
-/* Profiling wrapper: event pair around one launch when enabled. */
+/* Measurement hook: the launcher's kernels record the next event pair of the plan's pool while
+ * it has room (see LaunchEvents). */
 template <typename F>
 hipError_t timed(eblc_plan *p, hipStream_t st, const char *name, F &&launch) {
-    if (!p->profiling || p->nlaunch >= kMaxKernelsPerCall) return launch();
-    const int k = p->nlaunch++;
-    p->names[k] = name;
-    hipError_t e = hipEventRecord(p->ev[2 * k], st);
-    if (e != hipSuccess) return e;
-    e = launch();
-    if (e != hipSuccess) return e;
-    return hipEventRecord(p->ev[2 * k + 1], st);
+    if (2 * p->ev_used + 2 > p->ev_pool.size()) return launch();
+    if (!p->ev_filter.empty() && p->ev_filter.find("," + std::string(name) + ",") == std::string::npos)
+        return launch();
+    (void)st;
+    const size_t k = p->ev_used++;
+    p->ev_names[k] = name;
+    g_launch_events.start = p->ev_pool[2 * k];
+    g_launch_events.stop = p->ev_pool[2 * k + 1];
+    const hipError_t e = launch();
+    g_launch_events = LaunchEvents{};
+    return e;
 }
 
 eblc_status check_compress_args(const eblc_plan *plan, const float *in, const void *out) {
@@ -230,18 +258,26 @@ eblc_status check_compress_args(const eblc_plan *plan, const float *in, const vo
     return EBLC_OK;
 }
 
-/* Enqueue one compress on `st`: range (relative mode) -> encode -> scan (which writes the
- * result record) -> compaction with outliers. */
-hipError_t enqueue_compress(eblc_plan *plan, const float *in, void *out, size_t out_capacity,
+eblc_status check_decompress_args(const eblc_plan *plan, const void *in, size_t compressed_bytes, const float *out) {
+    if (in == nullptr || out == nullptr) return EBLC_INVALID_ARGUMENT;
+    if (!aligned16(in) || !field_ptr_ok(plan, out)) return EBLC_INVALID_ARGUMENT;
+    if (compressed_bytes < kHeaderBytes + plan->pa.wsec ||
+        compressed_bytes > kHeaderBytes + align_up(4 * plan->pa.n, 16))
+        return EBLC_CORRUPT_STREAM;
+    return EBLC_OK;
+}
+
+/* Enqueue one compress on `st` with the workspace of `lane`: range (relative mode) ->
+ * encode -> scan (which writes the result record) -> compaction with outliers. */
+hipError_t enqueue_compress(eblc_plan *plan, int lane, const float *in, void *out, size_t out_capacity,
                             eblc_result_t *result, hipStream_t st) {
     const PlanArgs pa = call_args(plan, in);
-    const Workspace &ws = plan->ws;
+    const Workspace &ws = plan->ws[lane];
     uint8_t *o = static_cast<uint8_t *>(out);
     const uint64_t widths_bytes = pa.wsec;
     const bool widths_direct = out_capacity >= kHeaderBytes + widths_bytes;
     uint8_t *widths_dst = widths_direct ? o + kHeaderBytes : ws.widths;
     uint64_t *res = reinterpret_cast<uint64_t *>(result);
-    plan->nlaunch = 0;
     hipError_t e = hipSuccess;
     if (plan->rel) e = timed(plan, st, "range", [&] { return launch_range(in, pa, ws, plan->eps, st); });
     if (e == hipSuccess)
@@ -251,6 +287,48 @@ hipError_t enqueue_compress(eblc_plan *plan, const float *in, void *out, size_t 
         });
     if (e == hipSuccess) e = timed(plan, st, "scan", [&] { return launch_scan_compress(pa, ws, o, out_capacity, res, st); });
     if (e == hipSuccess) e = timed(plan, st, "compact", [&] { return launch_compact(in, pa, ws, o, widths_direct ? nullptr : ws.widths, st); });
+    return e;
+}
+
+/* Enqueue one decompress on `st` with the workspace of `lane`: sizes -> scan (which
+ * validates the header) -> decode -> outlier patch. */
+hipError_t enqueue_decompress(eblc_plan *plan, int lane, const void *in, size_t compressed_bytes,
+                              float *out, hipStream_t st) {
+    const PlanArgs pa = call_args(plan, out);
+    const Workspace &ws = plan->ws[lane];
+    const uint8_t *i = static_cast<const uint8_t *>(in);
+    hipError_t e = timed(plan, st, "decode_sizes", [&] { return launch_decode_sizes(i, compressed_bytes, pa, ws, st); });
+    if (e == hipSuccess) e = timed(plan, st, "decode_scan", [&] { return launch_scan_decompress(i, compressed_bytes, pa, ws, st); });
+    if (e == hipSuccess)
+        e = timed(plan, st, "decode", [&] {
+            return pa.V ? launch_chunk_decode(i, pa, ws, out, st) : launch_decode(i, pa, ws, out, st);
+        });
+    if (e == hipSuccess) e = timed(plan, st, "patch", [&] { return launch_patch(i, pa, ws, out, st); });
+    return e;
+}
+
+/* Run `count` calls of a batch: with one lane, back to back on `st`; with more, call k on
+ * lane k mod lanes, each lane's stream first waiting for the work already on `st`, and `st`
+ * then waiting for every lane, so work the caller enqueues afterwards follows the batch. */
+template <typename F>
+hipError_t run_batch(eblc_plan *plan, int count, hipStream_t st, F &&call) {
+    const int lanes = plan->lanes < count ? plan->lanes : count;
+    if (lanes <= 1) {
+        for (int k = 0; k < count; ++k) {
+            hipError_t e = call(k, 0, st);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    hipError_t e = hipEventRecord(plan->fork_ev, st);
+    for (int l = 0; l < lanes && e == hipSuccess; ++l) e = hipStreamWaitEvent(plan->lane_stream[l], plan->fork_ev, 0);
+    for (int k = 0; k < count && e == hipSuccess; ++k) e = call(k, k % lanes, plan->lane_stream[k % lanes]);
+    /* join even after a failed enqueue, so that `st` never runs ahead of queued lane work */
+    for (int l = 0; l < lanes; ++l) {
+        hipError_t j = hipEventRecord(plan->join_ev[l], plan->lane_stream[l]);
+        if (j == hipSuccess) j = hipStreamWaitEvent(st, plan->join_ev[l], 0);
+        if (e == hipSuccess) e = j;
+    }
     return e;
 }
 
@@ -413,12 +491,14 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     const uint64_t o_si = carve(nc * kEscStage * 4), o_sv = carve(nc * kEscStage * 4);
     const uint64_t o_rp = carve(2 * (uint64_t)range_blocks(n) * 4);
     const uint64_t o_mu = carve(pa.nblocks * 4);
-    if (hipMalloc(&p->ws_base, off) != hipSuccess) {
+    p->lanes = (int)o.lanes;
+    if (hipMalloc(&p->ws_base, off * o.lanes) != hipSuccess) {
         delete p;
         return EBLC_OUT_OF_MEMORY;
     }
-    uint8_t *b = static_cast<uint8_t *>(p->ws_base);
-    Workspace &ws = p->ws;
+    for (int lane = 0; lane < p->lanes; ++lane) {
+    uint8_t *b = static_cast<uint8_t *>(p->ws_base) + off * lane;
+    Workspace &ws = p->ws[lane];
     ws.info = reinterpret_cast<DevInfo *>(b + o_info);
     ws.scratch = reinterpret_cast<uint32_t *>(b + o_scratch);
     ws.chunk_words = reinterpret_cast<uint32_t *>(b + o_cw);
@@ -434,20 +514,31 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     ws.stage_val = reinterpret_cast<uint32_t *>(b + o_sv);
     ws.range_part = reinterpret_cast<float *>(b + o_rp);
     ws.means = reinterpret_cast<int32_t *>(b + o_mu);
+    }
 
     if (hipHostMalloc(reinterpret_cast<void **>(&p->host_result), sizeof(eblc_result_t), hipHostMallocDefault) != hipSuccess) {
-        (void)hipFree(p->ws_base);
-        delete p;
+        eblc_plan_destroy(p);
         return EBLC_OUT_OF_MEMORY;
     }
     DevInfo init;
     std::memset(&init, 0, sizeof(init));
     if (!o.rel) resolve_abs(o.eps, &init);
-    if (hipMemcpy(ws.info, &init, sizeof(init), hipMemcpyHostToDevice) != hipSuccess) {
-        (void)hipHostFree(p->host_result);
-        (void)hipFree(p->ws_base);
-        delete p;
-        return EBLC_DEVICE_ERROR;
+    for (int lane = 0; lane < p->lanes; ++lane) {
+        if (hipMemcpy(p->ws[lane].info, &init, sizeof(init), hipMemcpyHostToDevice) != hipSuccess) {
+            eblc_plan_destroy(p);
+            return EBLC_DEVICE_ERROR;
+        }
+    }
+    if (p->lanes > 1) {
+        /* default-priority streams that do not synchronise with the null stream */
+        bool ok = hipEventCreateWithFlags(&p->fork_ev, hipEventDisableTiming) == hipSuccess;
+        for (int lane = 0; ok && lane < p->lanes; ++lane)
+            ok = hipStreamCreateWithFlags(&p->lane_stream[lane], hipStreamNonBlocking) == hipSuccess &&
+                 hipEventCreateWithFlags(&p->join_ev[lane], hipEventDisableTiming) == hipSuccess;
+        if (!ok) {
+            eblc_plan_destroy(p);
+            return EBLC_DEVICE_ERROR;
+        }
     }
     *plan_out = p;
     return EBLC_OK;
@@ -480,7 +571,7 @@ eblc_status eblc_compress(eblc_plan_t *plan, const float *in, void *out, size_t 
     /* the scan kernel writes the result record straight into the plan's pinned host slot */
     plan->host_result->compressed_bytes = 0;
     plan->host_result->status = EBLC_DEVICE_ERROR;
-    hipError_t e = enqueue_compress(plan, in, out, out_capacity, plan->host_result, st);
+    hipError_t e = enqueue_compress(plan, 0, in, out, out_capacity, plan->host_result, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return EBLC_DEVICE_ERROR;
     *compressed_bytes = (size_t)plan->host_result->compressed_bytes;
@@ -495,7 +586,7 @@ eblc_status eblc_compress_async(eblc_plan_t *plan, const float *in, void *out, s
     if (s0 != EBLC_OK) return s0;
     DeviceGuard guard(plan->device);
     if (!guard.ok) return EBLC_DEVICE_ERROR;
-    return hip_status(enqueue_compress(plan, in, out, out_capacity, result, static_cast<hipStream_t>(stream)));
+    return hip_status(enqueue_compress(plan, 0, in, out, out_capacity, result, static_cast<hipStream_t>(stream)));
 }
 
 eblc_status eblc_compress_batch(eblc_plan_t *plan, int count, const float *const *in, void *const *out,
@@ -510,36 +601,34 @@ eblc_status eblc_compress_batch(eblc_plan_t *plan, int count, const float *const
     }
     DeviceGuard guard(plan->device);
     if (!guard.ok) return EBLC_DEVICE_ERROR;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    for (int k = 0; k < count; ++k) {
-        hipError_t e = enqueue_compress(plan, in[k], out[k], out_capacity[k], results + k, st);
-        if (e != hipSuccess) return EBLC_DEVICE_ERROR;
-    }
-    return EBLC_OK;
+    return hip_status(run_batch(plan, count, static_cast<hipStream_t>(stream), [&](int k, int lane, hipStream_t s) {
+        return enqueue_compress(plan, lane, in[k], out[k], out_capacity[k], results + k, s);
+    }));
 }
 
 eblc_status eblc_decompress(eblc_plan_t *plan, const void *in, size_t compressed_bytes,
                             const void *sidecar, float *out, void *stream) {
-    if (plan == nullptr || in == nullptr || out == nullptr) return EBLC_INVALID_ARGUMENT;
-    if (sidecar != nullptr || !aligned16(in) || !field_ptr_ok(plan, out)) return EBLC_INVALID_ARGUMENT;
-    const PlanArgs pa = call_args(plan, out);
-    if (compressed_bytes < kHeaderBytes + pa.wsec ||
-        compressed_bytes > kHeaderBytes + align_up(4 * pa.n, 16))
-        return EBLC_CORRUPT_STREAM;
+    if (plan == nullptr || sidecar != nullptr) return EBLC_INVALID_ARGUMENT;
+    eblc_status s0 = check_decompress_args(plan, in, compressed_bytes, out);
+    if (s0 != EBLC_OK) return s0;
     DeviceGuard guard(plan->device);
     if (!guard.ok) return EBLC_DEVICE_ERROR;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const Workspace &ws = plan->ws;
-    const uint8_t *i = static_cast<const uint8_t *>(in);
-    plan->nlaunch = 0;
-    hipError_t e = timed(plan, st, "decode_sizes", [&] { return launch_decode_sizes(i, compressed_bytes, pa, ws, st); });
-    if (e == hipSuccess) e = timed(plan, st, "decode_scan", [&] { return launch_scan_decompress(i, compressed_bytes, pa, ws, st); });
-    if (e == hipSuccess)
-        e = timed(plan, st, "decode", [&] {
-            return pa.V ? launch_chunk_decode(i, pa, ws, out, st) : launch_decode(i, pa, ws, out, st);
-        });
-    if (e == hipSuccess) e = timed(plan, st, "patch", [&] { return launch_patch(i, pa, ws, out, st); });
-    return hip_status(e);
+    return hip_status(enqueue_decompress(plan, 0, in, compressed_bytes, out, static_cast<hipStream_t>(stream)));
+}
+
+eblc_status eblc_decompress_batch(eblc_plan_t *plan, int count, const void *const *in,
+                                  const size_t *compressed_bytes, float *const *out, void *stream) {
+    if (plan == nullptr || count < 0 || (count > 0 && (in == nullptr || compressed_bytes == nullptr || out == nullptr)))
+        return EBLC_INVALID_ARGUMENT;
+    for (int k = 0; k < count; ++k) {
+        eblc_status s0 = check_decompress_args(plan, in[k], compressed_bytes[k], out[k]);
+        if (s0 != EBLC_OK) return s0;
+    }
+    DeviceGuard guard(plan->device);
+    if (!guard.ok) return EBLC_DEVICE_ERROR;
+    return hip_status(run_batch(plan, count, static_cast<hipStream_t>(stream), [&](int k, int lane, hipStream_t s) {
+        return enqueue_decompress(plan, lane, in[k], compressed_bytes[k], out[k], s);
+    }));
 }
 
 eblc_status eblc_plan_status(eblc_plan_t *plan, void *stream) {
@@ -548,54 +637,97 @@ eblc_status eblc_plan_status(eblc_plan_t *plan, void *stream) {
     if (!guard.ok) return EBLC_DEVICE_ERROR;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (hipStreamSynchronize(st) != hipSuccess) return EBLC_DEVICE_ERROR;
-    uint32_t sticky = 0;
-    if (hipMemcpy(&sticky, &plan->ws.info->sticky, 4, hipMemcpyDeviceToHost) != hipSuccess) return EBLC_DEVICE_ERROR;
-    if (sticky) {
-        const uint32_t zero = 0;
-        if (hipMemcpy(&plan->ws.info->sticky, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) return EBLC_DEVICE_ERROR;
-        return EBLC_CORRUPT_STREAM;
+    bool corrupt = false;
+    for (int lane = 0; lane < plan->lanes; ++lane) {
+        uint32_t sticky = 0;
+        uint32_t *at = &plan->ws[lane].info->sticky;
+        if (hipMemcpy(&sticky, at, 4, hipMemcpyDeviceToHost) != hipSuccess) return EBLC_DEVICE_ERROR;
+        if (sticky) {
+            const uint32_t zero = 0;
+            if (hipMemcpy(at, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) return EBLC_DEVICE_ERROR;
+            corrupt = true;
+        }
     }
-    return EBLC_OK;
+    return corrupt ? EBLC_CORRUPT_STREAM : EBLC_OK;
 }
+
+namespace {
+void free_events(eblc_plan *plan) {
+    for (hipEvent_t ev : plan->ev_pool)
+        if (ev) (void)hipEventDestroy(ev);
+    plan->ev_pool.clear();
+    plan->ev_names.clear();
+    plan->ev_used = 0;
+}
+}  // namespace
 
 void eblc_plan_destroy(eblc_plan_t *plan) {
     if (plan == nullptr) return;
     {
         DeviceGuard guard(plan->device);
         (void)hipDeviceSynchronize();
-        for (auto &ev : plan->ev)
-            if (ev) (void)hipEventDestroy(ev);
+        free_events(plan);
+        for (int lane = 0; lane < kMaxLanes; ++lane) {
+            if (plan->lane_stream[lane]) (void)hipStreamDestroy(plan->lane_stream[lane]);
+            if (plan->join_ev[lane]) (void)hipEventDestroy(plan->join_ev[lane]);
+        }
+        if (plan->fork_ev) (void)hipEventDestroy(plan->fork_ev);
         if (plan->host_result) (void)hipHostFree(plan->host_result);
         if (plan->ws_base) (void)hipFree(plan->ws_base);
     }
     delete plan;
 }
 
-eblc_status eblc_plan_set_profiling(eblc_plan_t *plan, int enable) {
-    if (plan == nullptr) return EBLC_INVALID_ARGUMENT;
+eblc_status eblc_plan_set_profiling(eblc_plan_t *plan, int max_launches, const char *kernels) {
+    if (plan == nullptr || max_launches < 0 || (size_t)max_launches > kMaxTimedLaunches)
+        return EBLC_INVALID_ARGUMENT;
     DeviceGuard guard(plan->device);
     if (!guard.ok) return EBLC_DEVICE_ERROR;
-    if (enable && plan->ev[0] == nullptr) {
-        for (auto &ev : plan->ev)
-            if (hipEventCreate(&ev) != hipSuccess) return EBLC_DEVICE_ERROR;
+    if (hipDeviceSynchronize() != hipSuccess) return EBLC_DEVICE_ERROR;
+    free_events(plan);
+    plan->ev_filter.clear();
+    if (kernels != nullptr && kernels[0] != '\0') plan->ev_filter = "," + std::string(kernels) + ",";
+    if (max_launches == 0) return EBLC_OK;
+    plan->ev_pool.assign(2 * (size_t)max_launches, nullptr);
+    plan->ev_names.assign((size_t)max_launches, nullptr);
+    for (auto &ev : plan->ev_pool) {
+        if (hipEventCreate(&ev) != hipSuccess) {
+            free_events(plan);
+            return EBLC_DEVICE_ERROR;
+        }
     }
-    plan->profiling = enable != 0;
-    plan->nlaunch = 0;
     return EBLC_OK;
 }
 
-int eblc_plan_kernel_times(eblc_plan_t *plan, const char **names, float *ms, int max_kernels) {
-    if (plan == nullptr || !plan->profiling) return -1;
+int eblc_plan_kernel_times(eblc_plan_t *plan, const char **names, float *ms, int *launches, int max_kernels) {
+    if (plan == nullptr || plan->ev_pool.empty() || max_kernels < 0) return -1;
     DeviceGuard guard(plan->device);
     if (!guard.ok) return -1;
-    for (int k = 0; k < plan->nlaunch && k < max_kernels; ++k) {
-        if (hipEventSynchronize(plan->ev[2 * k + 1]) != hipSuccess) return -1;
+    /* fold the recorded launches by kernel name, in order of first launch */
+    const char *kname[kMaxKernelsPerCall * 2] = {};
+    double total[kMaxKernelsPerCall * 2] = {};
+    int cnt[kMaxKernelsPerCall * 2] = {};
+    int nk = 0;
+    for (size_t k = 0; k < plan->ev_used; ++k) {
+        if (hipEventSynchronize(plan->ev_pool[2 * k + 1]) != hipSuccess) return -1;
         float t = 0.0f;
-        if (hipEventElapsedTime(&t, plan->ev[2 * k], plan->ev[2 * k + 1]) != hipSuccess) return -1;
-        if (names) names[k] = plan->names[k];
-        if (ms) ms[k] = t;
+        if (hipEventElapsedTime(&t, plan->ev_pool[2 * k], plan->ev_pool[2 * k + 1]) != hipSuccess) return -1;
+        int j = 0;
+        while (j < nk && std::strcmp(kname[j], plan->ev_names[k]) != 0) ++j;
+        if (j == nk) {
+            if (nk == kMaxKernelsPerCall * 2) return -1;
+            kname[nk++] = plan->ev_names[k];
+        }
+        total[j] += t;
+        cnt[j] += 1;
     }
-    return plan->nlaunch;
+    for (int j = 0; j < nk && j < max_kernels; ++j) {
+        if (names) names[j] = kname[j];
+        if (ms) ms[j] = (float)(total[j] / cnt[j]);
+        if (launches) launches[j] = cnt[j];
+    }
+    plan->ev_used = 0;
+    return nk;
 }
 
 }  // extern "C"

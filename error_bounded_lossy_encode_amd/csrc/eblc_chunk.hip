@@ -494,11 +494,11 @@ template <int V>
 hipError_t chunk_encode_v(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *sizes_dst,
                           uint64_t sizes_bytes, hipStream_t stream) {
     if (pa.lay.strided)
-        hipLaunchKernelGGL((chunk_encode_kernel<V, true>), dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa,
-                           ws, sizes_dst, sizes_bytes);
+        eblc_launch((chunk_encode_kernel<V, true>), dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa,
+                    ws, sizes_dst, sizes_bytes);
     else
-        hipLaunchKernelGGL((chunk_encode_kernel<V, false>), dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa,
-                           ws, sizes_dst, sizes_bytes);
+        eblc_launch((chunk_encode_kernel<V, false>), dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa,
+                    ws, sizes_dst, sizes_bytes);
     return hipGetLastError();
 }
 
@@ -506,11 +506,11 @@ template <int V>
 hipError_t chunk_decode_v(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
                           hipStream_t stream) {
     if (pa.lay.strided)
-        hipLaunchKernelGGL((chunk_decode_kernel<V, true>), dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in,
-                           pa, ws, out);
+        eblc_launch((chunk_decode_kernel<V, true>), dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in,
+                    pa, ws, out);
     else
-        hipLaunchKernelGGL((chunk_decode_kernel<V, false>), dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in,
-                           pa, ws, out);
+        eblc_launch((chunk_decode_kernel<V, false>), dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in,
+                    pa, ws, out);
     return hipGetLastError();
 }
 

@@ -20,6 +20,7 @@
 #ifndef EBLC_INTERNAL_H
 #define EBLC_INTERNAL_H
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -144,6 +145,26 @@ struct Workspace {
 inline uint32_t range_blocks(uint64_t n) {
     const uint64_t b = (n / 4 + kRangeSpan - 1) / kRangeSpan;
     return (uint32_t)(b < 1 ? 1 : b);
+}
+
+/* Events the next launcher's kernels record into, set by the host's measurement hook around
+ * one launcher call (both null otherwise).  The launcher's first kernel records its start in
+ * `start` and its last kernel its end in `stop`, through the kernel dispatch's own timestamps
+ * (hipExtLaunchKernel), so timing adds no marker packets to the stream. */
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+extern thread_local LaunchEvents g_launch_events;
+
+/* Launch one kernel; kLast = false for a launcher's kernels before its last one. */
+template <bool kLast = true, typename F, typename... Args>
+inline void eblc_launch(F kernel, const dim3 &grid, const dim3 &block, uint32_t shmem, hipStream_t stream,
+                        Args... args) {
+    const hipEvent_t start = g_launch_events.start;
+    g_launch_events.start = nullptr;
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, start, kLast ? g_launch_events.stop : nullptr, 0u,
+                          args...);
 }
 
 /* Kernel launchers (eblc_kernels.hip).  All enqueue on `stream` and return the launch error. */

@@ -1288,15 +1288,15 @@ hipError_t launch_range(const float *x, const PlanArgs &pa, const Workspace &ws,
                         hipStream_t stream) {
     const uint32_t grid = range_blocks(pa.n);
     if (pa.lay.strided)
-        hipLaunchKernelGGL(range_partial_kernel<true>, dim3(grid), dim3(kRangeThreads), 0, stream, x, pa.n,
+        eblc_launch<false>(range_partial_kernel<true>, dim3(grid), dim3(kRangeThreads), 0, stream, x, pa.n,
                            pa.lay, ws.range_part);
     else
-        hipLaunchKernelGGL(range_partial_kernel<false>, dim3(grid), dim3(kRangeThreads), 0, stream, x, pa.n,
+        eblc_launch<false>(range_partial_kernel<false>, dim3(grid), dim3(kRangeThreads), 0, stream, x, pa.n,
                            pa.lay, ws.range_part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(range_resolve_kernel, dim3(1), dim3(kScanThreads), 0, stream, ws.range_part, grid,
-                       ws.info, eps);
+    eblc_launch(range_resolve_kernel, dim3(1), dim3(kScanThreads), 0, stream, ws.range_part, grid,
+                ws.info, eps);
     return hipGetLastError();
 }
 
@@ -1307,62 +1307,62 @@ hipError_t launch_encode(const float *x, const PlanArgs &pa, const Workspace &ws
     const dim3 grid(pa.ngroups), block(kEncThreads);
     if (pa.lay.strided) {
         if (cm == kCenterTile)
-            hipLaunchKernelGGL((encode_kernel<true, kCenterTile>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+            eblc_launch((encode_kernel<true, kCenterTile>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
         else if (cm == kCenterAny)
-            hipLaunchKernelGGL((encode_kernel<true, kCenterAny>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+            eblc_launch((encode_kernel<true, kCenterAny>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
         else
-            hipLaunchKernelGGL((encode_kernel<true, kCenterOff>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+            eblc_launch((encode_kernel<true, kCenterOff>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
     } else {
         if (cm == kCenterTile)
-            hipLaunchKernelGGL((encode_kernel<false, kCenterTile>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+            eblc_launch((encode_kernel<false, kCenterTile>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
         else if (cm == kCenterAny)
-            hipLaunchKernelGGL((encode_kernel<false, kCenterAny>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+            eblc_launch((encode_kernel<false, kCenterAny>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
         else
-            hipLaunchKernelGGL((encode_kernel<false, kCenterOff>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+            eblc_launch((encode_kernel<false, kCenterOff>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_scan_compress(const PlanArgs &pa, const Workspace &ws, uint8_t *out,
                                 uint64_t out_capacity, uint64_t *result, hipStream_t stream) {
-    hipLaunchKernelGGL(scan_compress_kernel, dim3(1), dim3(kScanThreads), 0, stream, pa, ws, out,
-                       out_capacity, result);
+    eblc_launch(scan_compress_kernel, dim3(1), dim3(kScanThreads), 0, stream, pa, ws, out,
+                out_capacity, result);
     return hipGetLastError();
 }
 
 hipError_t launch_compact(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *out,
                           const uint8_t *widths_src, hipStream_t stream) {
     if (pa.lay.strided)
-        hipLaunchKernelGGL(compact_kernel<true>, dim3(pa.ngroups), dim3(kBlockThreads), 0, stream, x, pa, ws,
-                           out, widths_src);
+        eblc_launch(compact_kernel<true>, dim3(pa.ngroups), dim3(kBlockThreads), 0, stream, x, pa, ws,
+                    out, widths_src);
     else
-        hipLaunchKernelGGL(compact_kernel<false>, dim3(pa.ngroups), dim3(kBlockThreads), 0, stream, x, pa, ws,
-                           out, widths_src);
+        eblc_launch(compact_kernel<false>, dim3(pa.ngroups), dim3(kBlockThreads), 0, stream, x, pa, ws,
+                    out, widths_src);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_sizes(const uint8_t *in, uint64_t in_bytes, const PlanArgs &pa, const Workspace &ws,
                                hipStream_t stream) {
     const uint32_t grid = (pa.dchunks + 255) / 256;
-    hipLaunchKernelGGL(decode_sizes_kernel, dim3(grid), dim3(256), 0, stream, in, in_bytes, pa, ws);
+    eblc_launch(decode_sizes_kernel, dim3(grid), dim3(256), 0, stream, in, in_bytes, pa, ws);
     return hipGetLastError();
 }
 
 hipError_t launch_scan_decompress(const uint8_t *in, uint64_t in_bytes, const PlanArgs &pa,
                                   const Workspace &ws, hipStream_t stream) {
-    hipLaunchKernelGGL(scan_decompress_kernel, dim3(1), dim3(kScanThreads), 0, stream, in, in_bytes,
-                       pa, ws);
+    eblc_launch(scan_decompress_kernel, dim3(1), dim3(kScanThreads), 0, stream, in, in_bytes,
+                pa, ws);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
                          hipStream_t stream) {
     if (pa.lay.strided)
-        hipLaunchKernelGGL(decode_kernel<true>, dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in, pa, ws,
-                           out);
+        eblc_launch(decode_kernel<true>, dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in, pa, ws,
+                    out);
     else
-        hipLaunchKernelGGL(decode_kernel<false>, dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in, pa, ws,
-                           out);
+        eblc_launch(decode_kernel<false>, dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in, pa, ws,
+                    out);
     return hipGetLastError();
 }
 
@@ -1371,9 +1371,9 @@ hipError_t launch_patch(const uint8_t *in, const PlanArgs &pa, const Workspace &
     uint64_t want = (pa.side_max + 255) / 256;
     uint32_t grid = (uint32_t)(want < 1 ? 1 : (want > (uint64_t)kPatchBlocksMax ? kPatchBlocksMax : want));
     if (pa.lay.strided)
-        hipLaunchKernelGGL(patch_kernel<true>, dim3(grid), dim3(256), 0, stream, in, pa, ws, out);
+        eblc_launch(patch_kernel<true>, dim3(grid), dim3(256), 0, stream, in, pa, ws, out);
     else
-        hipLaunchKernelGGL(patch_kernel<false>, dim3(grid), dim3(256), 0, stream, in, pa, ws, out);
+        eblc_launch(patch_kernel<false>, dim3(grid), dim3(256), 0, stream, in, pa, ws, out);
     return hipGetLastError();
 }
 

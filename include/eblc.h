@@ -131,6 +131,12 @@ int eblc_abi_version(void);
  *              chunk_bytes=<b>        chunk coder only: 4096, 8192 (default) or 16384 input
  *                                     bytes per chunk; the chunk is also the reset period of
  *                                     the difference, so block= is refused with coder=chunk
+ *              center=0|1             bitpack coder only: predict each block's first code by
+ *                                     the block's mean code (kept in a means section) instead
+ *                                     of 0; default 0
+ *              lanes=<k>              1..8, default 1: workspaces (each with its own stream)
+ *                                     the batch calls spread their fields over, k fields in
+ *                                     flight at once; the streams are identical for every k
  *            Unknown keys, repeated keys, NaN or negative values -> INVALID_ARGUMENT.
  *   plan_out receives the plan.  The plan allocates its whole workspace here (about 4 n +
  *            n/8 bytes plus small arrays) and nothing per call.
@@ -171,10 +177,13 @@ eblc_status eblc_compress_async(eblc_plan_t *plan, const float *in, void *out, s
                                 eblc_result_t *result, void *stream);
 
 /* Batched asynchronous compress: count fields of the plan's shape, in[k] -> out[k] with
- * capacity out_capacity[k], result record k at results + k, enqueued back to back on one
- * stream with no host wait between them (the snapshot-batch case of a solver saving many time
- * steps).  The three pointer arrays are host arrays of device pointers; `results` as for
- * eblc_compress_async.  All arguments are checked before anything is enqueued. */
+ * capacity out_capacity[k], result record k at results + k, enqueued with no host wait between
+ * them (the snapshot-batch case of a solver saving many time steps).  With lanes=1 the fields
+ * run back to back on `stream`; with lanes=k, field j runs on the plan's lane j mod k, whose
+ * stream first waits for the work already on `stream`, and `stream` then waits for every lane,
+ * so work enqueued on `stream` afterwards follows the whole batch.  The three pointer arrays
+ * are host arrays of device pointers; `results` as for eblc_compress_async.  All arguments are
+ * checked before anything is enqueued. */
 eblc_status eblc_compress_batch(eblc_plan_t *plan, int count, const float *const *in, void *const *out,
                                 const size_t *out_capacity, eblc_result_t *results, void *stream);
 
@@ -195,6 +204,13 @@ eblc_status eblc_compress_batch(eblc_plan_t *plan, int count, const float *const
 eblc_status eblc_decompress(eblc_plan_t *plan, const void *in, size_t compressed_bytes,
                             const void *sidecar, float *out, void *stream);
 
+/* Batched decompress: count streams of the plan's shape, in[k] (compressed_bytes[k] readable
+ * bytes, as for eblc_decompress) -> out[k], enqueued without waiting, over the plan's lanes as
+ * eblc_compress_batch does.  The three arrays are host arrays.  All arguments are checked before
+ * anything is enqueued; device-side problems set the plan's sticky CORRUPT_STREAM. */
+eblc_status eblc_decompress_batch(eblc_plan_t *plan, int count, const void *const *in,
+                                  const size_t *compressed_bytes, float *const *out, void *stream);
+
 /* Wait for `stream`, then return and clear the plan's sticky device error (OK if none). */
 eblc_status eblc_plan_status(eblc_plan_t *plan, void *stream);
 
@@ -205,13 +221,20 @@ void eblc_plan_destroy(eblc_plan_t *plan);
 const char *eblc_status_string(eblc_status s);
 
 /* ---- measurement hooks (not part of the provider shape) --------------------------------
- * With profiling on, every compress/decompress records a HIP event pair around each of its
- * kernel launches on the caller's stream.  eblc_plan_kernel_times waits for the last call's
- * events and writes up to max_kernels (name, milliseconds) pairs of that call in launch
- * order; it returns how many kernels the call launched, or -1 on error.  Names are static
- * strings. */
-eblc_status eblc_plan_set_profiling(eblc_plan_t *plan, int enable);
-int eblc_plan_kernel_times(eblc_plan_t *plan, const char **names, float *ms, int max_kernels);
+ * eblc_plan_set_profiling(plan, k, kernels) with 0 < k <= 8192 waits for the device, then
+ * records a HIP event pair around each of the plan's next k kernel launches, on the stream that
+ * launch runs on; 0 turns recording off.  kernels is NULL or "" (every kernel), or a
+ * comma-separated list of the names to time (range, encode, scan, compact, decode_sizes,
+ * decode_scan, decode, patch): each event record costs the stream a few microseconds, so
+ * timing only the kernels of interest keeps the rest of the call undisturbed.
+ * eblc_plan_kernel_times waits for the recorded events and writes, for each kernel name in
+ * order of its first launch (at most max_kernels of them), the static name, the mean duration
+ * in milliseconds and the number of launches recorded; then it clears the records (recording
+ * goes on while k launches have not been recorded in all).  It returns how many kernel names
+ * were recorded, or -1 when recording is off or on error. */
+eblc_status eblc_plan_set_profiling(eblc_plan_t *plan, int max_launches, const char *kernels);
+int eblc_plan_kernel_times(eblc_plan_t *plan, const char **names, float *ms, int *launches,
+                           int max_kernels);
 
 #ifdef __cplusplus
 }

@@ -34,6 +34,10 @@ def test_calls_without_gpu():
     assert lib.eblc_max_compressed_bytes(None) == 0
     assert lib.eblc_payload_alignment(None) == 0
     assert lib.eblc_plan_limits(None, None) == binding.EBLC_INVALID_ARGUMENT
+    assert lib.eblc_compress_batch(None, 0, None, None, None, None, None) == binding.EBLC_INVALID_ARGUMENT
+    assert lib.eblc_decompress_batch(None, 0, None, None, None, None) == binding.EBLC_INVALID_ARGUMENT
+    assert lib.eblc_plan_set_profiling(None, 4, None) == binding.EBLC_INVALID_ARGUMENT
+    assert lib.eblc_plan_kernel_times(None, None, None, None, 0) == -1
     lib.eblc_plan_destroy(None)
 
 
@@ -49,7 +53,8 @@ def test_unsupported_execution_kinds(kind):
                                   "coder=chunk;block=256", "chunk_bytes=8192", "coder=chunk;chunk_bytes=2048",
                                   "coder=chunk;chunk_bytes=32768", "coder=chunk;coder=chunk",
                                   "coder=chunk;chunk_bytes=4096;chunk_bytes=4096",
-                                  "center=2", "center=1;center=1", "center=yes", "coder=chunk;center=1"])
+                                  "center=2", "center=1;center=1", "center=yes", "coder=chunk;center=1",
+                                  "lanes=0", "lanes=9", "lanes=-1", "lanes=2;lanes=2", "lanes=two"])
 def test_invalid_options_rejected_before_any_device_call(opts):
     st, plan = binding.eblc_plan_create([64, 64], opts)
     assert st == binding.EBLC_INVALID_ARGUMENT and plan is None

@@ -85,12 +85,15 @@ def test_async_capacity_error_in_record(env):
         binding.eblc_plan_destroy(plan)
 
 
-def test_batch_of_fields(env):
-    """Snapshots of different character through one plan, back to back, then decompressed
-    back to back; every stream and reconstruction matches the oracle's."""
+@pytest.mark.parametrize("lanes,dec", [(1, "loop"), (1, "batch"), (3, "loop"), (3, "batch"), (8, "batch")])
+def test_batch_of_fields(env, lanes, dec):
+    """Snapshots of different character through one plan, then decompressed; every stream and
+    reconstruction matches the oracle's, whether the fields run back to back (one lane) or
+    spread over the plan's lane streams."""
     binding, torch = env
     N = 40
     dims, opts = [N, N, N], "rel=1e-3;block=256;outlier_log2=15"
+    plan_opts = opts + f";lanes={lanes}"
     fields = []
     for i in range(6):
         x, _, _ = synth.c5_snapshot(i, N, 1e-3)
@@ -100,7 +103,8 @@ def test_batch_of_fields(env):
         if i == 4:
             x[:] = np.float32(3.0)                  # constant field: bound unusable -> RAW
         fields.append(x)
-    st, plan = binding.eblc_plan_create(dims, opts, 0)
+    st, plan = binding.eblc_plan_create(dims, plan_opts, 0)
+    assert st == binding.EBLC_OK
     try:
         maxb = binding.eblc_max_compressed_bytes(plan)
         xs = [torch.from_numpy(f).cuda() for f in fields]
@@ -108,8 +112,13 @@ def test_batch_of_fields(env):
         res = torch.zeros(16 * len(fields), dtype=torch.uint8, device="cuda")
         ys = [torch.full((N ** 3,), float("nan"), dtype=torch.float32, device="cuda") for _ in fields]
         assert binding.eblc_compress_batch(plan, xs, outs, res) == binding.EBLC_OK
-        for i in range(len(fields)):
-            assert binding.eblc_decompress(plan, outs[i], maxb, ys[i]) == binding.EBLC_OK
+        if dec == "batch":
+            assert binding.eblc_decompress_batch(plan, outs, ys, [maxb] * len(fields)) == binding.EBLC_OK
+        else:
+            for i in range(len(fields)):
+                assert binding.eblc_decompress(plan, outs[i], maxb, ys[i]) == binding.EBLC_OK
+        # no host wait before reading: the copies below follow the batch on the caller's stream
+        ycopy = [y.clone() for y in ys]
         assert binding.eblc_plan_status(plan) == binding.EBLC_OK
         recs = binding.result_records(res)
         for i, f in enumerate(fields):
@@ -118,8 +127,78 @@ def test_batch_of_fields(env):
             assert status == binding.EBLC_OK and nb == ref.size, i
             assert np.array_equal(outs[i].cpu().numpy()[:nb], ref), i
             _, ref_dec = oracle.decompress(ref)
-            assert np.array_equal(ys[i].cpu().numpy().view(np.uint32), ref_dec.view(np.uint32)), i
+            assert np.array_equal(ycopy[i].cpu().numpy().view(np.uint32), ref_dec.view(np.uint32)), i
         assert int(outs[4].cpu().numpy()[8]) == 1  # the constant field went RAW
         assert binding.eblc_compress_batch(plan, [], [], res) == binding.EBLC_OK
+        assert binding.eblc_decompress_batch(plan, [], []) == binding.EBLC_OK
+    finally:
+        binding.eblc_plan_destroy(plan)
+
+
+def test_batch_lanes_report_corrupt_stream_of_any_lane(env):
+    """A corrupt stream decoded on a lane other than the first sets the plan's sticky status,
+    which eblc_plan_status returns once and then clears; the other streams still decode."""
+    binding, torch = env
+    N = 32
+    dims, opts = [N, N, N], "rel=1e-3;block=256;outlier_log2=15;lanes=4"
+    st, plan = binding.eblc_plan_create(dims, opts, 0)
+    assert st == binding.EBLC_OK
+    try:
+        maxb = binding.eblc_max_compressed_bytes(plan)
+        fields = [synth.c5_snapshot(i, N, 1e-3)[0].numpy().copy() for i in range(6)]
+        xs = [torch.from_numpy(f).cuda() for f in fields]
+        outs = [torch.zeros((maxb,), dtype=torch.uint8, device="cuda") for _ in fields]
+        res = torch.zeros(16 * len(fields), dtype=torch.uint8, device="cuda")
+        assert binding.eblc_compress_batch(plan, xs, outs, res) == binding.EBLC_OK
+        outs[5][0] ^= 0xFF                      # field 5 runs on lane 1: bad magic
+        ys = [torch.zeros((N ** 3,), dtype=torch.float32, device="cuda") for _ in fields]
+        assert binding.eblc_decompress_batch(plan, outs, ys) == binding.EBLC_OK
+        assert binding.eblc_plan_status(plan) == binding.EBLC_CORRUPT_STREAM
+        assert binding.eblc_plan_status(plan) == binding.EBLC_OK
+        for i in range(5):
+            _, ref_dec = oracle.decompress(oracle_stream(fields[i], dims, opts.rsplit(";", 1)[0]))
+            assert np.array_equal(ys[i].cpu().numpy().view(np.uint32), ref_dec.view(np.uint32)), i
+        # arguments are checked before anything is enqueued
+        bad = [outs[0], outs[1]]
+        assert binding.eblc_decompress_batch(plan, bad, ys[:2], [maxb, 64]) == binding.EBLC_CORRUPT_STREAM
+    finally:
+        binding.eblc_plan_destroy(plan)
+
+
+def test_kernel_time_records_cover_every_lane(env):
+    """The measurement hook records every launch of a batch on the lane streams and folds the
+    records by kernel name."""
+    binding, torch = env
+    N = 32
+    dims = [N, N, N]
+    st, plan = binding.eblc_plan_create(dims, "rel=1e-3;lanes=3", 0)
+    assert st == binding.EBLC_OK
+    try:
+        maxb = binding.eblc_max_compressed_bytes(plan)
+        xs = [synth.c5_snapshot(i, N, 1e-3)[0].cuda() for i in range(5)]
+        outs = [torch.zeros((maxb,), dtype=torch.uint8, device="cuda") for _ in xs]
+        ys = [torch.zeros((N ** 3,), dtype=torch.float32, device="cuda") for _ in xs]
+        res = torch.zeros(16 * len(xs), dtype=torch.uint8, device="cuda")
+        assert binding.eblc_plan_set_profiling(plan, 1000) == binding.EBLC_OK
+        assert binding.eblc_compress_batch(plan, xs, outs, res) == binding.EBLC_OK
+        assert binding.eblc_decompress_batch(plan, outs, ys) == binding.EBLC_OK
+        rec = binding.eblc_plan_kernel_times(plan)
+        names = [r[0] for r in rec]
+        assert names == ["range", "encode", "scan", "compact", "decode_sizes", "decode_scan", "decode", "patch"]
+        assert all(cnt == 5 and ms > 0 for _, ms, cnt in rec)
+        assert binding.eblc_plan_kernel_times(plan) == []       # records cleared by the read
+        assert binding.eblc_plan_set_profiling(plan, 3) == binding.EBLC_OK
+        assert binding.eblc_compress_batch(plan, xs, outs, res) == binding.EBLC_OK
+        assert sum(cnt for _, _, cnt in binding.eblc_plan_kernel_times(plan)) == 3  # pool of 3 launches
+        # only the named kernels are timed
+        assert binding.eblc_plan_set_profiling(plan, 1000, "decode,encode") == binding.EBLC_OK
+        assert binding.eblc_compress_batch(plan, xs, outs, res) == binding.EBLC_OK
+        assert binding.eblc_decompress_batch(plan, outs, ys) == binding.EBLC_OK
+        rec = binding.eblc_plan_kernel_times(plan)
+        assert [(r[0], r[2]) for r in rec] == [("encode", 5), ("decode", 5)]
+        assert binding.eblc_plan_set_profiling(plan, 0) == binding.EBLC_OK
+        with pytest.raises(RuntimeError):
+            binding.eblc_plan_kernel_times(plan)
+        assert binding.eblc_plan_status(plan) == binding.EBLC_OK
     finally:
         binding.eblc_plan_destroy(plan)
