@@ -8,7 +8,7 @@ field), c4 (2^28 AR(1) with 1 % spikes), c5_1e-6 / c5_1e-2 (64 snapshots of 256^
 back to back, then decompressed back to back).  By default the fields are compressed with
 eblc_compress_batch (no host wait; lengths arrive in device result records) and decompressed
 with eblc_decompress_batch and their buffers' capacity; a workload of several fields uses the
-plan option lanes=4, which keeps four fields in flight on the plan's own streams.  --api sync
+plan option lanes=8, which codes eight fields per kernel launch.  --api sync
 uses eblc_compress, which waits once per field to return its length, and eblc_decompress.
 
 Prints ONE JSON line: `value` is the round-trip throughput in GB/s of input bytes (input bytes
@@ -195,9 +195,10 @@ def main() -> int:
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--lanes", type=int, default=4,
-                    help="plan option lanes=K for workloads of several fields: the batch calls keep K "
-                         "fields in flight on K streams (the streams are the same for every K)")
+    ap.add_argument("--lanes", type=int, default=8,
+                    help="plan option lanes=K for workloads of several fields: the batch calls code K "
+                         "fields per kernel launch, each in its own workspace (the streams are the same "
+                         "for every K)")
     ap.add_argument("--kernel-events", choices=["on", "off"], default="on",
                     help="on: the library records a HIP event pair around every encode and decode launch "
                          "of the timed steps (up to 8192 launches), for the rooflines")
@@ -430,11 +431,15 @@ def main() -> int:
     dec_bytes = sizes + avg_payload + 4 * n
     traffic = profiling.read_traffic(os.path.join(PROFILES, f"traffic_{tag}.txt"))
 
+    # a launch codes up to `lanes` fields: the fields of a step over the launches of a stage
+    lanes = args.lanes if len(items) > 1 and args.api == "batch" else 1
+    per_launch = len(items) / -(-len(items) // lanes)
+
     def roof(name, alg_bytes, key):
         # algorithmic bytes per launch over the mean launch duration in the timed steps
         if key not in kavg:
             return None
-        achieved = alg_bytes / (kavg[key] * 1e-3) / 1e9
+        achieved = per_launch * alg_bytes / (kavg[key] * 1e-3) / 1e9
         t = None if traffic is None else traffic.get(name)
         return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None if t is None else round(t),
@@ -468,7 +473,8 @@ def main() -> int:
                           "encode and decode launches timed inside the timed steps",
         "roofline": roof(kernels[0], enc_bytes, "encode"),
         "roofline_decode": roof(kernels[1], dec_bytes, "decode"),
-        "algorithmic_bytes_per_launch": {"encode": round(enc_bytes), "decode": round(dec_bytes)},
+        "algorithmic_bytes_per_launch": {"encode": round(per_launch * enc_bytes), "decode": round(per_launch * dec_bytes)},
+        "fields_per_launch": per_launch,
         "cold": cold,
         "max_abs_err": err_max,
         "eb": ebs[0],

@@ -28,7 +28,7 @@ thread_local LaunchEvents g_launch_events;
 }  // namespace eblc
 
 namespace {
-constexpr int kMaxLanes = 8;               /* workspaces (and streams) a batch call may use */
+constexpr int kMaxLanes = kMaxFields;      /* fields (each with its workspace) of one launch */
 constexpr size_t kMaxTimedLaunches = 8192; /* event pairs the measurement hook may hold */
 }  // namespace
 
@@ -40,14 +40,12 @@ struct eblc_plan {
     bool rel = true;
     double eps = 1e-4;
     PlanArgs pa{};
-    /* lane k's workspace; single calls use lane 0 on the caller's stream, batch calls spread
-     * their fields over the lanes, each with its own stream */
+    /* lane 0's workspace; lane k's lies k * ws_stride bytes further on.  A launch codes up to
+     * `lanes` fields, field k in lane k's workspace; single calls use lane 0 */
     int lanes = 1;
-    Workspace ws[kMaxLanes] = {};
+    Workspace ws{};
+    uint64_t ws_stride = 0;
     void *ws_base = nullptr;
-    hipStream_t lane_stream[kMaxLanes] = {};
-    hipEvent_t fork_ev = nullptr;
-    hipEvent_t join_ev[kMaxLanes] = {};
     eblc_result_t *host_result = nullptr; /* pinned host slot the synchronous compress reads */
     /* measurement hook: an event pair per launch, up to the pool's size, since enabling */
     std::vector<hipEvent_t> ev_pool;
@@ -225,12 +223,9 @@ bool field_ptr_ok(const eblc_plan *plan, const void *p) {
     return plan->pa.lay.strided ? aligned4(p) : aligned16(p);
 }
 
-/* The plan's kernel arguments for one call: 128-bit access to a padded field only when the
- * call's pointer is 16-byte aligned too. */
-PlanArgs call_args(const eblc_plan *plan, const void *field) {
-    PlanArgs pa = plan->pa;
-    if (pa.lay.strided && !aligned16(field)) pa.lay.vec = 0;
-    return pa;
+/* Device address of lane k's DevInfo. */
+DevInfo *lane_info(const eblc_plan *plan, int k) {
+    return reinterpret_cast<DevInfo *>(reinterpret_cast<uint8_t *>(plan->ws.info) + (uint64_t)k * plan->ws_stride);
 }
 
 eblc_status hip_status(hipError_t e) { return e == hipSuccess ? EBLC_OK : EBLC_DEVICE_ERROR; }
@@ -267,69 +262,78 @@ eblc_status check_decompress_args(const eblc_plan *plan, const void *in, size_t 
     return EBLC_OK;
 }
 
-/* Enqueue one compress on `st` with the workspace of `lane`: range (relative mode) ->
- * encode -> scan (which writes the result record) -> compaction with outliers. */
-hipError_t enqueue_compress(eblc_plan *plan, int lane, const float *in, void *out, size_t out_capacity,
-                            eblc_result_t *result, hipStream_t st) {
-    const PlanArgs pa = call_args(plan, in);
-    const Workspace &ws = plan->ws[lane];
-    uint8_t *o = static_cast<uint8_t *>(out);
-    const uint64_t widths_bytes = pa.wsec;
-    const bool widths_direct = out_capacity >= kHeaderBytes + widths_bytes;
-    uint8_t *widths_dst = widths_direct ? o + kHeaderBytes : ws.widths;
-    uint64_t *res = reinterpret_cast<uint64_t *>(result);
+/* The plan's kernel arguments for a launch coding `fields`: 128-bit access to a padded field
+ * only when every field pointer of the launch is 16-byte aligned too. */
+PlanArgs launch_args(const eblc_plan *plan, const void *const *fields, int nf) {
+    PlanArgs pa = plan->pa;
+    for (int k = 0; k < nf; ++k)
+        if (pa.lay.strided && !aligned16(fields[k])) pa.lay.vec = 0;
+    return pa;
+}
+
+/* Enqueue the compress of nf <= lanes fields on `st`, field k in lane k's workspace, one
+ * launch per stage: range (relative mode) -> encode -> scan (which writes result record k at
+ * results + k) -> compaction with outliers. */
+hipError_t enqueue_compress(eblc_plan *plan, int nf, const float *const *in, void *const *out,
+                            const size_t *out_capacity, eblc_result_t *results, hipStream_t st) {
+    const PlanArgs pa = launch_args(plan, reinterpret_cast<const void *const *>(in), nf);
+    const Workspace &ws = plan->ws;
+    Fields fs{};
+    fs.ws_stride = plan->ws_stride;
+    for (int k = 0; k < nf; ++k) {
+        fs.src[k] = reinterpret_cast<const uint8_t *>(in[k]);
+        fs.dst[k] = static_cast<uint8_t *>(out[k]);
+        fs.bytes[k] = out_capacity[k];
+        fs.result[k] = reinterpret_cast<uint64_t *>(results + k);
+        /* the size section goes straight into the stream when the buffer holds it */
+        if (out_capacity[k] >= kHeaderBytes + pa.wsec) fs.wdirect |= 1u << k;
+    }
+    const uint32_t n = (uint32_t)nf;
     hipError_t e = hipSuccess;
-    if (plan->rel) e = timed(plan, st, "range", [&] { return launch_range(in, pa, ws, plan->eps, st); });
+    if (plan->rel) e = timed(plan, st, "range", [&] { return launch_range(fs, n, pa, ws, plan->eps, st); });
     if (e == hipSuccess)
         e = timed(plan, st, "encode", [&] {
-            return pa.V ? launch_chunk_encode(in, pa, ws, widths_dst, widths_bytes, st)
-                        : launch_encode(in, pa, ws, widths_dst, widths_bytes, st);
+            return pa.V ? launch_chunk_encode(fs, n, pa, ws, st) : launch_encode(fs, n, pa, ws, st);
         });
-    if (e == hipSuccess) e = timed(plan, st, "scan", [&] { return launch_scan_compress(pa, ws, o, out_capacity, res, st); });
-    if (e == hipSuccess) e = timed(plan, st, "compact", [&] { return launch_compact(in, pa, ws, o, widths_direct ? nullptr : ws.widths, st); });
+    if (e == hipSuccess) e = timed(plan, st, "scan", [&] { return launch_scan_compress(fs, n, pa, ws, st); });
+    if (e == hipSuccess) e = timed(plan, st, "compact", [&] { return launch_compact(fs, n, pa, ws, st); });
     return e;
 }
 
-/* Enqueue one decompress on `st` with the workspace of `lane`: sizes -> scan (which
- * validates the header) -> decode -> outlier patch. */
-hipError_t enqueue_decompress(eblc_plan *plan, int lane, const void *in, size_t compressed_bytes,
-                              float *out, hipStream_t st) {
-    const PlanArgs pa = call_args(plan, out);
-    const Workspace &ws = plan->ws[lane];
-    const uint8_t *i = static_cast<const uint8_t *>(in);
-    hipError_t e = timed(plan, st, "decode_sizes", [&] { return launch_decode_sizes(i, compressed_bytes, pa, ws, st); });
-    if (e == hipSuccess) e = timed(plan, st, "decode_scan", [&] { return launch_scan_decompress(i, compressed_bytes, pa, ws, st); });
+/* Enqueue the decompress of nf <= lanes streams on `st`, stream k in lane k's workspace:
+ * sizes -> scan (which validates the header) -> decode -> outlier patch. */
+hipError_t enqueue_decompress(eblc_plan *plan, int nf, const void *const *in, const size_t *compressed_bytes,
+                              float *const *out, hipStream_t st) {
+    const PlanArgs pa = launch_args(plan, reinterpret_cast<const void *const *>(out), nf);
+    const Workspace &ws = plan->ws;
+    Fields fs{};
+    fs.ws_stride = plan->ws_stride;
+    for (int k = 0; k < nf; ++k) {
+        fs.src[k] = static_cast<const uint8_t *>(in[k]);
+        fs.dst[k] = reinterpret_cast<uint8_t *>(out[k]);
+        fs.bytes[k] = compressed_bytes[k];
+    }
+    const uint32_t n = (uint32_t)nf;
+    hipError_t e = timed(plan, st, "decode_sizes", [&] { return launch_decode_sizes(fs, n, pa, ws, st); });
+    if (e == hipSuccess) e = timed(plan, st, "decode_scan", [&] { return launch_scan_decompress(fs, n, pa, ws, st); });
     if (e == hipSuccess)
         e = timed(plan, st, "decode", [&] {
-            return pa.V ? launch_chunk_decode(i, pa, ws, out, st) : launch_decode(i, pa, ws, out, st);
+            return pa.V ? launch_chunk_decode(fs, n, pa, ws, st) : launch_decode(fs, n, pa, ws, st);
         });
-    if (e == hipSuccess) e = timed(plan, st, "patch", [&] { return launch_patch(i, pa, ws, out, st); });
+    if (e == hipSuccess) e = timed(plan, st, "patch", [&] { return launch_patch(fs, n, pa, ws, st); });
     return e;
 }
 
-/* Run `count` calls of a batch: with one lane, back to back on `st`; with more, call k on
- * lane k mod lanes, each lane's stream first waiting for the work already on `st`, and `st`
- * then waiting for every lane, so work the caller enqueues afterwards follows the batch. */
+/* Run the `count` calls of a batch in groups of up to `lanes`, one group after another on
+ * `st`: call(first, nf) enqueues calls first .. first + nf - 1 as one launch per stage. */
 template <typename F>
-hipError_t run_batch(eblc_plan *plan, int count, hipStream_t st, F &&call) {
-    const int lanes = plan->lanes < count ? plan->lanes : count;
-    if (lanes <= 1) {
-        for (int k = 0; k < count; ++k) {
-            hipError_t e = call(k, 0, st);
-            if (e != hipSuccess) return e;
-        }
-        return hipSuccess;
+hipError_t run_batch(eblc_plan *plan, int count, F &&call) {
+    for (int k0 = 0; k0 < count; k0 += plan->lanes) {
+        const int nf = count - k0 < plan->lanes ? count - k0 : plan->lanes;
+        hipError_t e = call(k0, nf);
+        if (e != hipSuccess) return e;
     }
-    hipError_t e = hipEventRecord(plan->fork_ev, st);
-    for (int l = 0; l < lanes && e == hipSuccess; ++l) e = hipStreamWaitEvent(plan->lane_stream[l], plan->fork_ev, 0);
-    for (int k = 0; k < count && e == hipSuccess; ++k) e = call(k, k % lanes, plan->lane_stream[k % lanes]);
-    /* join even after a failed enqueue, so that `st` never runs ahead of queued lane work */
-    for (int l = 0; l < lanes; ++l) {
-        hipError_t j = hipEventRecord(plan->join_ev[l], plan->lane_stream[l]);
-        if (j == hipSuccess) j = hipStreamWaitEvent(st, plan->join_ev[l], 0);
-        if (e == hipSuccess) e = j;
-    }
-    return e;
+    return hipSuccess;
 }
 
 /* floor(2^64 / d) + 1, the exact reciprocal for dividing 32-bit values by d >= 2; 0 for d = 1. */
@@ -496,9 +500,9 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
         delete p;
         return EBLC_OUT_OF_MEMORY;
     }
-    for (int lane = 0; lane < p->lanes; ++lane) {
-    uint8_t *b = static_cast<uint8_t *>(p->ws_base) + off * lane;
-    Workspace &ws = p->ws[lane];
+    p->ws_stride = off;
+    uint8_t *b = static_cast<uint8_t *>(p->ws_base);
+    Workspace &ws = p->ws;
     ws.info = reinterpret_cast<DevInfo *>(b + o_info);
     ws.scratch = reinterpret_cast<uint32_t *>(b + o_scratch);
     ws.chunk_words = reinterpret_cast<uint32_t *>(b + o_cw);
@@ -514,7 +518,6 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     ws.stage_val = reinterpret_cast<uint32_t *>(b + o_sv);
     ws.range_part = reinterpret_cast<float *>(b + o_rp);
     ws.means = reinterpret_cast<int32_t *>(b + o_mu);
-    }
 
     if (hipHostMalloc(reinterpret_cast<void **>(&p->host_result), sizeof(eblc_result_t), hipHostMallocDefault) != hipSuccess) {
         eblc_plan_destroy(p);
@@ -524,18 +527,7 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     std::memset(&init, 0, sizeof(init));
     if (!o.rel) resolve_abs(o.eps, &init);
     for (int lane = 0; lane < p->lanes; ++lane) {
-        if (hipMemcpy(p->ws[lane].info, &init, sizeof(init), hipMemcpyHostToDevice) != hipSuccess) {
-            eblc_plan_destroy(p);
-            return EBLC_DEVICE_ERROR;
-        }
-    }
-    if (p->lanes > 1) {
-        /* default-priority streams that do not synchronise with the null stream */
-        bool ok = hipEventCreateWithFlags(&p->fork_ev, hipEventDisableTiming) == hipSuccess;
-        for (int lane = 0; ok && lane < p->lanes; ++lane)
-            ok = hipStreamCreateWithFlags(&p->lane_stream[lane], hipStreamNonBlocking) == hipSuccess &&
-                 hipEventCreateWithFlags(&p->join_ev[lane], hipEventDisableTiming) == hipSuccess;
-        if (!ok) {
+        if (hipMemcpy(lane_info(p, lane), &init, sizeof(init), hipMemcpyHostToDevice) != hipSuccess) {
             eblc_plan_destroy(p);
             return EBLC_DEVICE_ERROR;
         }
@@ -571,7 +563,9 @@ eblc_status eblc_compress(eblc_plan_t *plan, const float *in, void *out, size_t 
     /* the scan kernel writes the result record straight into the plan's pinned host slot */
     plan->host_result->compressed_bytes = 0;
     plan->host_result->status = EBLC_DEVICE_ERROR;
-    hipError_t e = enqueue_compress(plan, 0, in, out, out_capacity, plan->host_result, st);
+    void *outs[1] = {out};
+    const size_t caps[1] = {out_capacity};
+    hipError_t e = enqueue_compress(plan, 1, &in, outs, caps, plan->host_result, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return EBLC_DEVICE_ERROR;
     *compressed_bytes = (size_t)plan->host_result->compressed_bytes;
@@ -586,7 +580,9 @@ eblc_status eblc_compress_async(eblc_plan_t *plan, const float *in, void *out, s
     if (s0 != EBLC_OK) return s0;
     DeviceGuard guard(plan->device);
     if (!guard.ok) return EBLC_DEVICE_ERROR;
-    return hip_status(enqueue_compress(plan, 0, in, out, out_capacity, result, static_cast<hipStream_t>(stream)));
+    void *outs[1] = {out};
+    const size_t caps[1] = {out_capacity};
+    return hip_status(enqueue_compress(plan, 1, &in, outs, caps, result, static_cast<hipStream_t>(stream)));
 }
 
 eblc_status eblc_compress_batch(eblc_plan_t *plan, int count, const float *const *in, void *const *out,
@@ -601,8 +597,9 @@ eblc_status eblc_compress_batch(eblc_plan_t *plan, int count, const float *const
     }
     DeviceGuard guard(plan->device);
     if (!guard.ok) return EBLC_DEVICE_ERROR;
-    return hip_status(run_batch(plan, count, static_cast<hipStream_t>(stream), [&](int k, int lane, hipStream_t s) {
-        return enqueue_compress(plan, lane, in[k], out[k], out_capacity[k], results + k, s);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(run_batch(plan, count, [&](int k, int nf) {
+        return enqueue_compress(plan, nf, in + k, out + k, out_capacity + k, results + k, st);
     }));
 }
 
@@ -613,7 +610,7 @@ eblc_status eblc_decompress(eblc_plan_t *plan, const void *in, size_t compressed
     if (s0 != EBLC_OK) return s0;
     DeviceGuard guard(plan->device);
     if (!guard.ok) return EBLC_DEVICE_ERROR;
-    return hip_status(enqueue_decompress(plan, 0, in, compressed_bytes, out, static_cast<hipStream_t>(stream)));
+    return hip_status(enqueue_decompress(plan, 1, &in, &compressed_bytes, &out, static_cast<hipStream_t>(stream)));
 }
 
 eblc_status eblc_decompress_batch(eblc_plan_t *plan, int count, const void *const *in,
@@ -626,8 +623,9 @@ eblc_status eblc_decompress_batch(eblc_plan_t *plan, int count, const void *cons
     }
     DeviceGuard guard(plan->device);
     if (!guard.ok) return EBLC_DEVICE_ERROR;
-    return hip_status(run_batch(plan, count, static_cast<hipStream_t>(stream), [&](int k, int lane, hipStream_t s) {
-        return enqueue_decompress(plan, lane, in[k], compressed_bytes[k], out[k], s);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(run_batch(plan, count, [&](int k, int nf) {
+        return enqueue_decompress(plan, nf, in + k, compressed_bytes + k, out + k, st);
     }));
 }
 
@@ -640,7 +638,7 @@ eblc_status eblc_plan_status(eblc_plan_t *plan, void *stream) {
     bool corrupt = false;
     for (int lane = 0; lane < plan->lanes; ++lane) {
         uint32_t sticky = 0;
-        uint32_t *at = &plan->ws[lane].info->sticky;
+        uint32_t *at = &lane_info(plan, lane)->sticky;
         if (hipMemcpy(&sticky, at, 4, hipMemcpyDeviceToHost) != hipSuccess) return EBLC_DEVICE_ERROR;
         if (sticky) {
             const uint32_t zero = 0;
@@ -667,11 +665,6 @@ void eblc_plan_destroy(eblc_plan_t *plan) {
         DeviceGuard guard(plan->device);
         (void)hipDeviceSynchronize();
         free_events(plan);
-        for (int lane = 0; lane < kMaxLanes; ++lane) {
-            if (plan->lane_stream[lane]) (void)hipStreamDestroy(plan->lane_stream[lane]);
-            if (plan->join_ev[lane]) (void)hipEventDestroy(plan->join_ev[lane]);
-        }
-        if (plan->fork_ev) (void)hipEventDestroy(plan->fork_ev);
         if (plan->host_result) (void)hipHostFree(plan->host_result);
         if (plan->ws_base) (void)hipFree(plan->ws_base);
     }

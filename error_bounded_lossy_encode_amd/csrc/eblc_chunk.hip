@@ -218,9 +218,9 @@ __device__ __forceinline__ uint32_t rze_chunk(const uint32_t *pl, uint32_t wmax,
  * second reports 0 words), so the compaction's copy of each slot in order yields the chunks in
  * order. */
 template <int V, bool STRIDED>
-__global__ __launch_bounds__(kEncThreads) void chunk_encode_kernel(const float *__restrict__ x, PlanArgs pa,
-                                                                   Workspace ws, uint8_t *__restrict__ sizes_dst,
-                                                                   uint64_t sizes_bytes) {
+__device__ __forceinline__ void chunk_encode_body(const float *__restrict__ x, PlanArgs pa,
+                                                  Workspace ws, uint8_t *__restrict__ sizes_dst,
+                                                  uint64_t sizes_bytes) {
     using Gm = ChunkGeom<V>;
     constexpr int kBufs = kEncWaves * kEncChunk / V;
     __shared__ uint32_t s_words[kBufs][Gm::LDSW];
@@ -326,6 +326,14 @@ __global__ __launch_bounds__(kEncThreads) void chunk_encode_kernel(const float *
     }
 }
 
+template <int V, bool STRIDED>
+__global__ __launch_bounds__(kEncThreads) void chunk_encode_kernel(Fields fs, PlanArgs pa, Workspace ws) {
+    const uint32_t f = blockIdx.y;
+    const Workspace w = lane_ws(ws, f, fs.ws_stride);
+    uint8_t *sd = (fs.wdirect >> f) & 1u ? pick(fs.dst, f) + kHeaderBytes : w.widths;
+    chunk_encode_body<V, STRIDED>(reinterpret_cast<const float *>(pick(fs.src, f)), pa, w, sd, pa.wsec);
+}
+
 /* ---- K7c: chunk decode ------------------------------------------------------------------------ */
 
 /* Decode tiles [t0, t0 + NT) of a chunk: lane 32 h + b reads plane b of group 2 t + h (planes
@@ -399,8 +407,8 @@ __device__ __forceinline__ void decode_quads(const uint32_t *pl, uint32_t t0, ui
  * chunk's loads are issued before the first LDS store.  Then decode_tiles, eight tiles at a
  * time for a full chunk. */
 template <int V, bool STRIDED>
-__global__ __launch_bounds__(kBlockThreads) void chunk_decode_kernel(const uint8_t *__restrict__ in, PlanArgs pa,
-                                                                     Workspace ws, float *__restrict__ out) {
+__device__ __forceinline__ void chunk_decode_body(const uint8_t *__restrict__ in, PlanArgs pa,
+                                                  Workspace ws, float *__restrict__ out) {
     using Gm = ChunkGeom<V>;
     __shared__ uint32_t s_words[kWavesPerBlock][Gm::LDSW];
     __shared__ uint4 s_x4[kWavesPerBlock][4 * kCTile / 4];
@@ -490,48 +498,53 @@ __global__ __launch_bounds__(kBlockThreads) void chunk_decode_kernel(const uint8
     }
 }
 
+template <int V, bool STRIDED>
+__global__ __launch_bounds__(kBlockThreads) void chunk_decode_kernel(Fields fs, PlanArgs pa, Workspace ws) {
+    const uint32_t f = blockIdx.y;
+    chunk_decode_body<V, STRIDED>(pick(fs.src, f), pa, lane_ws(ws, f, fs.ws_stride),
+                                  reinterpret_cast<float *>(pick(fs.dst, f)));
+}
+
 template <int V>
-hipError_t chunk_encode_v(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *sizes_dst,
-                          uint64_t sizes_bytes, hipStream_t stream) {
+hipError_t chunk_encode_v(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
+                          hipStream_t stream) {
+    const dim3 grid(pa.ngroups, nf), block(kEncThreads);
     if (pa.lay.strided)
-        eblc_launch((chunk_encode_kernel<V, true>), dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa,
-                    ws, sizes_dst, sizes_bytes);
+        eblc_launch((chunk_encode_kernel<V, true>), grid, block, 0, stream, fs, pa, ws);
     else
-        eblc_launch((chunk_encode_kernel<V, false>), dim3(pa.ngroups), dim3(kEncThreads), 0, stream, x, pa,
-                    ws, sizes_dst, sizes_bytes);
+        eblc_launch((chunk_encode_kernel<V, false>), grid, block, 0, stream, fs, pa, ws);
     return hipGetLastError();
 }
 
 template <int V>
-hipError_t chunk_decode_v(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
+hipError_t chunk_decode_v(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                           hipStream_t stream) {
+    const dim3 grid(pa.dgroups, nf), block(kBlockThreads);
     if (pa.lay.strided)
-        eblc_launch((chunk_decode_kernel<V, true>), dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in,
-                    pa, ws, out);
+        eblc_launch((chunk_decode_kernel<V, true>), grid, block, 0, stream, fs, pa, ws);
     else
-        eblc_launch((chunk_decode_kernel<V, false>), dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in,
-                    pa, ws, out);
+        eblc_launch((chunk_decode_kernel<V, false>), grid, block, 0, stream, fs, pa, ws);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_chunk_encode(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *sizes_dst,
-                               uint64_t sizes_bytes, hipStream_t stream) {
+hipError_t launch_chunk_encode(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
+                               hipStream_t stream) {
     switch (pa.V) {
-        case 1024: return chunk_encode_v<1024>(x, pa, ws, sizes_dst, sizes_bytes, stream);
-        case 2048: return chunk_encode_v<2048>(x, pa, ws, sizes_dst, sizes_bytes, stream);
-        case 4096: return chunk_encode_v<4096>(x, pa, ws, sizes_dst, sizes_bytes, stream);
+        case 1024: return chunk_encode_v<1024>(fs, nf, pa, ws, stream);
+        case 2048: return chunk_encode_v<2048>(fs, nf, pa, ws, stream);
+        case 4096: return chunk_encode_v<4096>(fs, nf, pa, ws, stream);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_chunk_decode(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
+hipError_t launch_chunk_decode(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                                hipStream_t stream) {
     switch (pa.V) {
-        case 1024: return chunk_decode_v<1024>(in, pa, ws, out, stream);
-        case 2048: return chunk_decode_v<2048>(in, pa, ws, out, stream);
-        case 4096: return chunk_decode_v<4096>(in, pa, ws, out, stream);
+        case 1024: return chunk_decode_v<1024>(fs, nf, pa, ws, stream);
+        case 2048: return chunk_decode_v<2048>(fs, nf, pa, ws, stream);
+        case 4096: return chunk_decode_v<4096>(fs, nf, pa, ws, stream);
     }
     return hipErrorInvalidValue;
 }

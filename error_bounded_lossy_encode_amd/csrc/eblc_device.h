@@ -238,6 +238,47 @@ __device__ __forceinline__ uint32_t chunk_offset(const uint32_t *gpre, const uin
     return o;
 }
 
+/* ---- the fields of a launch ------------------------------------------------------------------ */
+
+/* Entry f of a kernel-argument array, by selects on the wave-uniform f: indexing the array
+ * directly with a value known only at run time would copy the argument to scratch memory. */
+template <typename T>
+__device__ __forceinline__ T pick(const T (&a)[kMaxFields], uint32_t f) {
+    T v = a[0];
+#pragma unroll
+    for (int k = 1; k < kMaxFields; ++k) v = f == (uint32_t)k ? a[k] : v;
+    return v;
+}
+
+/* p moved on by d bytes, by pointer arithmetic (an integer round trip would hide from the
+ * compiler that the result still points into global memory). */
+template <typename T>
+__device__ __forceinline__ T *shift(T *p, uint64_t d) {
+    return reinterpret_cast<T *>(reinterpret_cast<char *>(p) + d);
+}
+
+/* The workspace of lane f: every array of lane 0's, d = f * stride bytes further on. */
+__device__ __forceinline__ Workspace lane_ws(const Workspace &w, uint32_t f, uint64_t stride) {
+    const uint64_t d = (uint64_t)f * stride;
+    Workspace r;
+    r.info = shift(w.info, d);
+    r.scratch = shift(w.scratch, d);
+    r.chunk_words = shift(w.chunk_words, d);
+    r.chunk_esc = shift(w.chunk_esc, d);
+    r.chunk_tmask = shift(w.chunk_tmask, d);
+    r.group_words = shift(w.group_words, d);
+    r.group_esc = shift(w.group_esc, d);
+    r.gpre_words = shift(w.gpre_words, d);
+    r.gpre_esc = shift(w.gpre_esc, d);
+    r.emask = shift(w.emask, d);
+    r.stage_idx = shift(w.stage_idx, d);
+    r.stage_val = shift(w.stage_val, d);
+    r.widths = shift(w.widths, d);
+    r.range_part = shift(w.range_part, d);
+    r.means = shift(w.means, d);
+    return r;
+}
+
 }  // namespace
 }  // namespace eblc
 

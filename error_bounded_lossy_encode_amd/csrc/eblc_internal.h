@@ -147,6 +147,21 @@ inline uint32_t range_blocks(uint64_t n) {
     return (uint32_t)(b < 1 ? 1 : b);
 }
 
+/* The caller's buffers of the fields one launch codes: field f = blockIdx.y, f < gridDim.y <=
+ * kMaxFields, runs in the workspace of lane f, which lies f * ws_stride bytes after lane 0's.
+ * One call codes one field; a batch call codes up to kMaxFields fields per launch. */
+constexpr int kMaxFields = 8;
+struct Fields {
+    const uint8_t *src[kMaxFields];  /* compress: the field; decompress: the stream */
+    uint8_t *dst[kMaxFields];        /* compress: the stream; decompress: the field */
+    uint64_t bytes[kMaxFields];      /* compress: capacity of dst; decompress: readable bytes of src */
+    uint64_t *result[kMaxFields];    /* compress: the result record (length, status) */
+    uint64_t ws_stride;              /* bytes between the workspaces of consecutive lanes */
+    uint32_t wdirect;                /* compress: bit f set when field f's size section goes straight
+                                        into its stream (else into its workspace's staging) */
+    uint32_t pad;
+};
+
 /* Events the next launcher's kernels record into, set by the host's measurement hook around
  * one launcher call (both null otherwise).  The launcher's first kernel records its start in
  * `start` and its last kernel its end in `stop`, through the kernel dispatch's own timestamps
@@ -167,29 +182,30 @@ inline void eblc_launch(F kernel, const dim3 &grid, const dim3 &block, uint32_t 
                           args...);
 }
 
-/* Kernel launchers (eblc_kernels.hip).  All enqueue on `stream` and return the launch error. */
-hipError_t launch_range(const float *x, const PlanArgs &pa, const Workspace &ws, double eps,
+/* Kernel launchers (eblc_kernels.hip).  Each codes the first nf (1..kMaxFields) fields of fs,
+ * enqueued on `stream`, and returns the launch error. */
+hipError_t launch_range(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws, double eps,
                         hipStream_t stream);
-hipError_t launch_encode(const float *x, const PlanArgs &pa, const Workspace &ws,
-                         uint8_t *widths_dst, uint64_t widths_bytes, hipStream_t stream);
-hipError_t launch_scan_compress(const PlanArgs &pa, const Workspace &ws, uint8_t *out,
-                                uint64_t out_capacity, uint64_t *result, hipStream_t stream);
-hipError_t launch_compact(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *out,
-                          const uint8_t *widths_src, hipStream_t stream);
-hipError_t launch_decode_sizes(const uint8_t *in, uint64_t in_bytes, const PlanArgs &pa, const Workspace &ws,
-                               hipStream_t stream);
-hipError_t launch_scan_decompress(const uint8_t *in, uint64_t in_bytes, const PlanArgs &pa,
-                                  const Workspace &ws, hipStream_t stream);
-hipError_t launch_decode(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
+hipError_t launch_encode(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                          hipStream_t stream);
-hipError_t launch_patch(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
+hipError_t launch_scan_compress(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
+                                hipStream_t stream);
+hipError_t launch_compact(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
+                          hipStream_t stream);
+hipError_t launch_decode_sizes(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
+                               hipStream_t stream);
+hipError_t launch_scan_decompress(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
+                                  hipStream_t stream);
+hipError_t launch_decode(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
+                         hipStream_t stream);
+hipError_t launch_patch(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                         hipStream_t stream);
 
 /* The chunk coder (eblc_chunk.hip): encode in place of launch_encode, decode in place of
  * launch_decode; the other stages are shared. */
-hipError_t launch_chunk_encode(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *sizes_dst,
-                               uint64_t sizes_bytes, hipStream_t stream);
-hipError_t launch_chunk_decode(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
+hipError_t launch_chunk_encode(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
+                               hipStream_t stream);
+hipError_t launch_chunk_decode(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                                hipStream_t stream);
 
 }  // namespace eblc

@@ -75,9 +75,9 @@ __device__ __forceinline__ void minmax4(const float4 &a, float &mn, float &mx) {
  * gfx950 a plain load of a line also forces out dirty lines left by earlier writes, which
  * halves the read rate).  The last workgroup also takes the n mod 4 trailing values. */
 template <bool STRIDED>
-__global__ __launch_bounds__(kRangeThreads) void range_partial_kernel(const float *__restrict__ x,
-                                                                      uint64_t n, Layout lo,
-                                                                      float *__restrict__ part) {
+__device__ __forceinline__ void range_partial_body(const float *__restrict__ x,
+                                                   uint64_t n, Layout lo,
+                                                   float *__restrict__ part) {
     __shared__ float s_mn[kRangeThreads / kWave], s_mx[kRangeThreads / kWave];
     float mn[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
     float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -116,10 +116,18 @@ __global__ __launch_bounds__(kRangeThreads) void range_partial_kernel(const floa
     }
 }
 
+template <bool STRIDED>
+__global__ __launch_bounds__(kRangeThreads) void range_partial_kernel(Fields fs, uint64_t n, Layout lo,
+                                                                      Workspace ws) {
+    const uint32_t f = blockIdx.y;
+    range_partial_body<STRIDED>(reinterpret_cast<const float *>(pick(fs.src, f)), n, lo,
+                                lane_ws(ws, f, fs.ws_stride).range_part);
+}
+
 /* K1b: one workgroup folds the per-workgroup partials and resolves the bound. */
-__global__ __launch_bounds__(kScanThreads) void range_resolve_kernel(const float *__restrict__ part,
-                                                                     uint32_t nparts, DevInfo *info,
-                                                                     double eps) {
+__device__ __forceinline__ void range_resolve_body(const float *__restrict__ part,
+                                                   uint32_t nparts, DevInfo *info,
+                                                   double eps) {
     __shared__ float s_mn[kScanThreads / kWave], s_mx[kScanThreads / kWave];
     float a = INFINITY, b = -INFINITY;
     /* kResolveBatch partials per thread in flight before any is folded (min and max do not
@@ -152,6 +160,12 @@ __global__ __launch_bounds__(kScanThreads) void range_resolve_kernel(const float
         }
         resolve_bound(a, b, eps, info);
     }
+}
+
+__global__ __launch_bounds__(kScanThreads) void range_resolve_kernel(Fields fs, Workspace ws, uint32_t nparts,
+                                                                     double eps) {
+    const Workspace w = lane_ws(ws, blockIdx.y, fs.ws_stride);
+    range_resolve_body(w.range_part, nparts, w.info, eps);
 }
 
 /* ---- K2: fused encode ------------------------------------------------------------------------ */
@@ -531,7 +545,7 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
  * buffer cannot hold them), its word and escape counts and the escape bitmask of every tile
  * with an escape; per workgroup, the sums the device-wide scan runs over. */
 template <bool STRIDED, int CM>
-__global__ __launch_bounds__(kEncThreads) void encode_kernel(
+__device__ __forceinline__ void encode_body(
     const float *__restrict__ x, PlanArgs pa, Workspace ws, uint8_t *__restrict__ widths_dst,
     uint64_t widths_bytes) {
     __shared__ uint4 s_pay4[kEncWaves][kEncPayWords / 4];
@@ -610,6 +624,14 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
         ws.group_words[blockIdx.x] = sw;
         ws.group_esc[blockIdx.x] = se;
     }
+}
+
+template <bool STRIDED, int CM>
+__global__ __launch_bounds__(kEncThreads) void encode_kernel(Fields fs, PlanArgs pa, Workspace ws) {
+    const uint32_t f = blockIdx.y;
+    const Workspace w = lane_ws(ws, f, fs.ws_stride);
+    uint8_t *wd = (fs.wdirect >> f) & 1u ? pick(fs.dst, f) + kHeaderBytes : w.widths;
+    encode_body<STRIDED, CM>(reinterpret_cast<const float *>(pick(fs.src, f)), pa, w, wd, pa.wsec);
 }
 
 /* ---- K3 / K6b: single-workgroup exclusive scan over groups -------------------------------- */
@@ -699,9 +721,9 @@ __device__ void block_scan2(const uint32_t *__restrict__ a, const uint32_t *__re
 }
 
 /* Compress finalize: totals -> stream layout, RAW decision, header. */
-__global__ __launch_bounds__(kScanThreads) void scan_compress_kernel(PlanArgs pa, Workspace ws,
-                                                                     uint8_t *out, uint64_t cap,
-                                                                     uint64_t *result) {
+__device__ __forceinline__ void scan_compress_body(PlanArgs pa, Workspace ws,
+                                                   uint8_t *out, uint64_t cap,
+                                                   uint64_t *result) {
     __shared__ uint32_t s_hdr[32];
     __shared__ uint32_t s_fits;
     DevInfo *info = ws.info;
@@ -768,6 +790,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_compress_kernel(PlanArgs pa
     }
     __syncthreads();
     if (s_fits && threadIdx.x < 32) reinterpret_cast<uint32_t *>(out)[threadIdx.x] = s_hdr[threadIdx.x];
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_compress_kernel(Fields fs, PlanArgs pa, Workspace ws) {
+    const uint32_t f = blockIdx.y;
+    scan_compress_body(pa, lane_ws(ws, f, fs.ws_stride), pick(fs.dst, f), pick(fs.bytes, f), pick(fs.result, f));
 }
 
 
@@ -873,10 +900,10 @@ __device__ __forceinline__ void copy_chunk_payload(const uint32_t *__restrict__ 
  * In RAW mode the workgroup copies the group's input values instead.  The last group also
  * zeroes the pads after the payload and after the outlier sections. */
 template <bool STRIDED>
-__global__ __launch_bounds__(kBlockThreads) void compact_kernel(const float *__restrict__ x,
-                                                                PlanArgs pa, Workspace ws,
-                                                                uint8_t *__restrict__ out,
-                                                                const uint8_t *__restrict__ widths_src) {
+__device__ __forceinline__ void compact_body(const float *__restrict__ x,
+                                             PlanArgs pa, Workspace ws,
+                                             uint8_t *__restrict__ out,
+                                             const uint8_t *__restrict__ widths_src) {
     constexpr int CPG = kEncChunksPerGroup;
     static_assert(CPG == kBlockThreads / kWave, "one wave per chunk");
     const uint32_t tid = threadIdx.x;
@@ -983,12 +1010,20 @@ __global__ __launch_bounds__(kBlockThreads) void compact_kernel(const float *__r
     }
 }
 
+template <bool STRIDED>
+__global__ __launch_bounds__(kBlockThreads) void compact_kernel(Fields fs, PlanArgs pa, Workspace ws) {
+    const uint32_t f = blockIdx.y;
+    const Workspace w = lane_ws(ws, f, fs.ws_stride);
+    compact_body<STRIDED>(reinterpret_cast<const float *>(pick(fs.src, f)), pa, w, pick(fs.dst, f),
+                          (fs.wdirect >> f) & 1u ? nullptr : w.widths);
+}
+
 /* ---- K6a: decode sizes ---------------------------------------------------------------------- */
 
 /* One thread per decode chunk: payload words of the chunk = sum of its width bytes; a width above 32
  * flags the stream.  Quads of threads form the groups the scan runs over. */
-__global__ __launch_bounds__(256) void decode_sizes_kernel(const uint8_t *__restrict__ in,
-                                                           uint64_t in_bytes, PlanArgs pa, Workspace ws) {
+__device__ __forceinline__ void decode_sizes_body(const uint8_t *__restrict__ in,
+                                                  uint64_t in_bytes, PlanArgs pa, Workspace ws) {
     const uint32_t c = blockIdx.x * 256 + threadIdx.x;
     /* Touch one word of every 128-byte line of a well-compressed stream's sections after the
      * header up to the payload's end -- sizes, block means, payload -- when they average at most
@@ -1062,15 +1097,20 @@ __global__ __launch_bounds__(256) void decode_sizes_kernel(const uint8_t *__rest
     asm volatile("" ::"v"(touched));
 }
 
+__global__ __launch_bounds__(256) void decode_sizes_kernel(Fields fs, PlanArgs pa, Workspace ws) {
+    const uint32_t f = blockIdx.y;
+    decode_sizes_body(pick(fs.src, f), pick(fs.bytes, f), pa, lane_ws(ws, f, fs.ws_stride));
+}
+
 /* ---- K6b: decode scan + header validation ------------------------------------------------- */
 
 __device__ __forceinline__ uint64_t ld64(const uint32_t *h, int i) {
     return (uint64_t)h[i] | ((uint64_t)h[i + 1] << 32);
 }
 
-__global__ __launch_bounds__(kScanThreads) void scan_decompress_kernel(const uint8_t *__restrict__ in,
-                                                                       uint64_t in_bytes, PlanArgs pa,
-                                                                       Workspace ws) {
+__device__ __forceinline__ void scan_decompress_body(const uint8_t *__restrict__ in,
+                                                     uint64_t in_bytes, PlanArgs pa,
+                                                     Workspace ws) {
     /* the header, staged in LDS before the scan so that its loads overlap it (block_scan2
      * synchronizes the workgroup before it returns) */
     __shared__ uint32_t s_h[32];
@@ -1121,6 +1161,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_decompress_kernel(const uin
     info->dec_s = s;
     info->dec_B = B;
     info->dec_flags = flags;
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_decompress_kernel(Fields fs, PlanArgs pa, Workspace ws) {
+    const uint32_t f = blockIdx.y;
+    scan_decompress_body(pick(fs.src, f), pick(fs.bytes, f), pa, lane_ws(ws, f, fs.ws_stride));
 }
 
 /* ---- K7: fused decode ------------------------------------------------------------------------ */
@@ -1201,9 +1246,9 @@ __device__ __forceinline__ void decode_tiles(const uint8_t *__restrict__ in, con
 /* One wave per chunk: stage the chunk's packed words in LDS (128-bit loads) and its segment
  * widths and word offsets, then decode_tiles (the centered copy for a centered stream). */
 template <bool STRIDED>
-__global__ __launch_bounds__(kBlockThreads) void decode_kernel(const uint8_t *__restrict__ in,
-                                                               PlanArgs pa, Workspace ws,
-                                                               float *__restrict__ out) {
+__device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in,
+                                            PlanArgs pa, Workspace ws,
+                                            float *__restrict__ out) {
     __shared__ uint4 s_pay4[kWavesPerBlock][kDecChunk / 4 + 2];
     __shared__ uint32_t s_w[kWavesPerBlock][kDecSegs];
     __shared__ uint32_t s_so[kWavesPerBlock][kDecSegs];
@@ -1260,11 +1305,18 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(const uint8_t *__
         decode_tiles<STRIDED, false>(in, pa, info, pay, s_w[wave], s_so[wave], lb, cbase, full, out);
 }
 
+template <bool STRIDED>
+__global__ __launch_bounds__(kBlockThreads) void decode_kernel(Fields fs, PlanArgs pa, Workspace ws) {
+    const uint32_t f = blockIdx.y;
+    decode_body<STRIDED>(pick(fs.src, f), pa, lane_ws(ws, f, fs.ws_stride),
+                         reinterpret_cast<float *>(pick(fs.dst, f)));
+}
+
 /* ---- K8: outlier patch ------------------------------------------------------------------------ */
 
 template <bool STRIDED>
-__global__ __launch_bounds__(256) void patch_kernel(const uint8_t *__restrict__ in, PlanArgs pa,
-                                                    Workspace ws, float *__restrict__ out) {
+__device__ __forceinline__ void patch_body(const uint8_t *__restrict__ in, PlanArgs pa,
+                                           Workspace ws, float *__restrict__ out) {
     DevInfo *info = ws.info;
     if (info->err || info->mode == 1) return;
     const uint64_t m = info->m;
@@ -1280,100 +1332,101 @@ __global__ __launch_bounds__(256) void patch_kernel(const uint8_t *__restrict__ 
     }
 }
 
+template <bool STRIDED>
+__global__ __launch_bounds__(256) void patch_kernel(Fields fs, PlanArgs pa, Workspace ws) {
+    const uint32_t f = blockIdx.y;
+    patch_body<STRIDED>(pick(fs.src, f), pa, lane_ws(ws, f, fs.ws_stride), reinterpret_cast<float *>(pick(fs.dst, f)));
+}
+
 }  // namespace
 
 /* ---- launchers ------------------------------------------------------------------------------- */
 
-hipError_t launch_range(const float *x, const PlanArgs &pa, const Workspace &ws, double eps,
+hipError_t launch_range(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws, double eps,
                         hipStream_t stream) {
     const uint32_t grid = range_blocks(pa.n);
     if (pa.lay.strided)
-        eblc_launch<false>(range_partial_kernel<true>, dim3(grid), dim3(kRangeThreads), 0, stream, x, pa.n,
-                           pa.lay, ws.range_part);
+        eblc_launch<false>(range_partial_kernel<true>, dim3(grid, nf), dim3(kRangeThreads), 0, stream, fs, pa.n,
+                           pa.lay, ws);
     else
-        eblc_launch<false>(range_partial_kernel<false>, dim3(grid), dim3(kRangeThreads), 0, stream, x, pa.n,
-                           pa.lay, ws.range_part);
+        eblc_launch<false>(range_partial_kernel<false>, dim3(grid, nf), dim3(kRangeThreads), 0, stream, fs, pa.n,
+                           pa.lay, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    eblc_launch(range_resolve_kernel, dim3(1), dim3(kScanThreads), 0, stream, ws.range_part, grid,
-                ws.info, eps);
+    eblc_launch(range_resolve_kernel, dim3(1, nf), dim3(kScanThreads), 0, stream, fs, ws, grid, eps);
     return hipGetLastError();
 }
 
-hipError_t launch_encode(const float *x, const PlanArgs &pa, const Workspace &ws,
-                         uint8_t *widths_dst, uint64_t widths_bytes, hipStream_t stream) {
+hipError_t launch_encode(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
+                         hipStream_t stream) {
     const int cm = !pa.center ? kCenterOff
                    : (pa.B <= (uint32_t)kEncTile && pa.T + pa.log2B <= 29) ? kCenterTile : kCenterAny;
-    const dim3 grid(pa.ngroups), block(kEncThreads);
+    const dim3 grid(pa.ngroups, nf), block(kEncThreads);
     if (pa.lay.strided) {
         if (cm == kCenterTile)
-            eblc_launch((encode_kernel<true, kCenterTile>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+            eblc_launch((encode_kernel<true, kCenterTile>), grid, block, 0, stream, fs, pa, ws);
         else if (cm == kCenterAny)
-            eblc_launch((encode_kernel<true, kCenterAny>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+            eblc_launch((encode_kernel<true, kCenterAny>), grid, block, 0, stream, fs, pa, ws);
         else
-            eblc_launch((encode_kernel<true, kCenterOff>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+            eblc_launch((encode_kernel<true, kCenterOff>), grid, block, 0, stream, fs, pa, ws);
     } else {
         if (cm == kCenterTile)
-            eblc_launch((encode_kernel<false, kCenterTile>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+            eblc_launch((encode_kernel<false, kCenterTile>), grid, block, 0, stream, fs, pa, ws);
         else if (cm == kCenterAny)
-            eblc_launch((encode_kernel<false, kCenterAny>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+            eblc_launch((encode_kernel<false, kCenterAny>), grid, block, 0, stream, fs, pa, ws);
         else
-            eblc_launch((encode_kernel<false, kCenterOff>), grid, block, 0, stream, x, pa, ws, widths_dst, widths_bytes);
+            eblc_launch((encode_kernel<false, kCenterOff>), grid, block, 0, stream, fs, pa, ws);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_scan_compress(const PlanArgs &pa, const Workspace &ws, uint8_t *out,
-                                uint64_t out_capacity, uint64_t *result, hipStream_t stream) {
-    eblc_launch(scan_compress_kernel, dim3(1), dim3(kScanThreads), 0, stream, pa, ws, out,
-                out_capacity, result);
+hipError_t launch_scan_compress(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
+                                hipStream_t stream) {
+    eblc_launch(scan_compress_kernel, dim3(1, nf), dim3(kScanThreads), 0, stream, fs, pa, ws);
     return hipGetLastError();
 }
 
-hipError_t launch_compact(const float *x, const PlanArgs &pa, const Workspace &ws, uint8_t *out,
-                          const uint8_t *widths_src, hipStream_t stream) {
+hipError_t launch_compact(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
+                          hipStream_t stream) {
+    const dim3 grid(pa.ngroups, nf), block(kBlockThreads);
     if (pa.lay.strided)
-        eblc_launch(compact_kernel<true>, dim3(pa.ngroups), dim3(kBlockThreads), 0, stream, x, pa, ws,
-                    out, widths_src);
+        eblc_launch(compact_kernel<true>, grid, block, 0, stream, fs, pa, ws);
     else
-        eblc_launch(compact_kernel<false>, dim3(pa.ngroups), dim3(kBlockThreads), 0, stream, x, pa, ws,
-                    out, widths_src);
+        eblc_launch(compact_kernel<false>, grid, block, 0, stream, fs, pa, ws);
     return hipGetLastError();
 }
 
-hipError_t launch_decode_sizes(const uint8_t *in, uint64_t in_bytes, const PlanArgs &pa, const Workspace &ws,
+hipError_t launch_decode_sizes(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                                hipStream_t stream) {
     const uint32_t grid = (pa.dchunks + 255) / 256;
-    eblc_launch(decode_sizes_kernel, dim3(grid), dim3(256), 0, stream, in, in_bytes, pa, ws);
+    eblc_launch(decode_sizes_kernel, dim3(grid, nf), dim3(256), 0, stream, fs, pa, ws);
     return hipGetLastError();
 }
 
-hipError_t launch_scan_decompress(const uint8_t *in, uint64_t in_bytes, const PlanArgs &pa,
-                                  const Workspace &ws, hipStream_t stream) {
-    eblc_launch(scan_decompress_kernel, dim3(1), dim3(kScanThreads), 0, stream, in, in_bytes,
-                pa, ws);
+hipError_t launch_scan_decompress(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
+                                  hipStream_t stream) {
+    eblc_launch(scan_decompress_kernel, dim3(1, nf), dim3(kScanThreads), 0, stream, fs, pa, ws);
     return hipGetLastError();
 }
 
-hipError_t launch_decode(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
+hipError_t launch_decode(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                          hipStream_t stream) {
+    const dim3 grid(pa.dgroups, nf), block(kBlockThreads);
     if (pa.lay.strided)
-        eblc_launch(decode_kernel<true>, dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in, pa, ws,
-                    out);
+        eblc_launch(decode_kernel<true>, grid, block, 0, stream, fs, pa, ws);
     else
-        eblc_launch(decode_kernel<false>, dim3(pa.dgroups), dim3(kBlockThreads), 0, stream, in, pa, ws,
-                    out);
+        eblc_launch(decode_kernel<false>, grid, block, 0, stream, fs, pa, ws);
     return hipGetLastError();
 }
 
-hipError_t launch_patch(const uint8_t *in, const PlanArgs &pa, const Workspace &ws, float *out,
+hipError_t launch_patch(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                         hipStream_t stream) {
     uint64_t want = (pa.side_max + 255) / 256;
     uint32_t grid = (uint32_t)(want < 1 ? 1 : (want > (uint64_t)kPatchBlocksMax ? kPatchBlocksMax : want));
     if (pa.lay.strided)
-        eblc_launch(patch_kernel<true>, dim3(grid), dim3(256), 0, stream, in, pa, ws, out);
+        eblc_launch(patch_kernel<true>, dim3(grid, nf), dim3(256), 0, stream, fs, pa, ws);
     else
-        eblc_launch(patch_kernel<false>, dim3(grid), dim3(256), 0, stream, in, pa, ws, out);
+        eblc_launch(patch_kernel<false>, dim3(grid, nf), dim3(256), 0, stream, fs, pa, ws);
     return hipGetLastError();
 }
 

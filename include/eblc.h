@@ -134,9 +134,9 @@ int eblc_abi_version(void);
  *              center=0|1             bitpack coder only: predict each block's first code by
  *                                     the block's mean code (kept in a means section) instead
  *                                     of 0; default 0
- *              lanes=<k>              1..8, default 1: workspaces (each with its own stream)
- *                                     the batch calls spread their fields over, k fields in
- *                                     flight at once; the streams are identical for every k
+ *              lanes=<k>              1..8, default 1: fields a batch call codes per kernel
+ *                                     launch, each in a workspace of its own (the workspace
+ *                                     grows k-fold); the streams are identical for every k
  *            Unknown keys, repeated keys, NaN or negative values -> INVALID_ARGUMENT.
  *   plan_out receives the plan.  The plan allocates its whole workspace here (about 4 n +
  *            n/8 bytes plus small arrays) and nothing per call.
@@ -177,11 +177,11 @@ eblc_status eblc_compress_async(eblc_plan_t *plan, const float *in, void *out, s
                                 eblc_result_t *result, void *stream);
 
 /* Batched asynchronous compress: count fields of the plan's shape, in[k] -> out[k] with
- * capacity out_capacity[k], result record k at results + k, enqueued with no host wait between
- * them (the snapshot-batch case of a solver saving many time steps).  With lanes=1 the fields
- * run back to back on `stream`; with lanes=k, field j runs on the plan's lane j mod k, whose
- * stream first waits for the work already on `stream`, and `stream` then waits for every lane,
- * so work enqueued on `stream` afterwards follows the whole batch.  The three pointer arrays
+ * capacity out_capacity[k], result record k at results + k, enqueued on `stream` with no host
+ * wait (the snapshot-batch case of a solver saving many time steps).  The fields are coded in
+ * groups of up to `lanes` (a plan option), one kernel launch per stage for each group, each
+ * field of a group in a workspace of its own, so the short single-workgroup stages of a group's
+ * fields run side by side and the launches are `lanes` times fewer.  The three pointer arrays
  * are host arrays of device pointers; `results` as for eblc_compress_async.  All arguments are
  * checked before anything is enqueued. */
 eblc_status eblc_compress_batch(eblc_plan_t *plan, int count, const float *const *in, void *const *out,
@@ -205,9 +205,10 @@ eblc_status eblc_decompress(eblc_plan_t *plan, const void *in, size_t compressed
                             const void *sidecar, float *out, void *stream);
 
 /* Batched decompress: count streams of the plan's shape, in[k] (compressed_bytes[k] readable
- * bytes, as for eblc_decompress) -> out[k], enqueued without waiting, over the plan's lanes as
- * eblc_compress_batch does.  The three arrays are host arrays.  All arguments are checked before
- * anything is enqueued; device-side problems set the plan's sticky CORRUPT_STREAM. */
+ * bytes, as for eblc_decompress) -> out[k], enqueued on `stream` without waiting, in groups of
+ * `lanes` streams per launch as eblc_compress_batch does.  The three arrays are host arrays.
+ * All arguments are checked before anything is enqueued; device-side problems set the plan's
+ * sticky CORRUPT_STREAM. */
 eblc_status eblc_decompress_batch(eblc_plan_t *plan, int count, const void *const *in,
                                   const size_t *compressed_bytes, float *const *out, void *stream);
 
