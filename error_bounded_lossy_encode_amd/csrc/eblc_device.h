@@ -228,13 +228,21 @@ __device__ __forceinline__ int32_t unzigzag(uint32_t z) {
 }
 
 /* Word offset of chunk c in the packed payload (or outlier rank), from the group prefix plus
- * the chunks before c in its group. */
+ * the chunks before c in its group; the loads are issued together, then summed. */
 template <int CPG>
 __device__ __forceinline__ uint32_t chunk_offset(const uint32_t *gpre, const uint32_t *per_chunk,
                                                  uint32_t c) {
-    const uint32_t g = c / CPG;
-    uint32_t o = gpre[g];
-    for (uint32_t k = g * CPG; k < c; ++k) o += per_chunk[k];
+    const uint32_t g0 = c / CPG * CPG;
+    uint32_t v[CPG];
+    v[0] = gpre[c / CPG];
+#pragma unroll
+    for (int k = 1; k < CPG; ++k) {
+        v[k] = 0;
+        if (g0 + (uint32_t)k - 1 < c) v[k] = per_chunk[g0 + k - 1];
+    }
+    uint32_t o = 0;
+#pragma unroll
+    for (int k = 0; k < CPG; ++k) o += v[k];
     return o;
 }
 

@@ -1289,10 +1289,25 @@ __device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in,
     const uint32_t lb = (uint32_t)(sw - a0);
     const uint32_t units = (lb + P + 3) >> 2;
     const uint4 *src = reinterpret_cast<const uint4 *>(in) + a0 / 4;
-    for (uint32_t u = lane; u < units; u += kWave) s_pay4[wave][u] = src[u];
     const uint64_t seg = (uint64_t)c * kDecSegs + lane;
     const uint32_t wl = seg < pa.nseg ? (uint32_t)in[kHeaderBytes + seg] : 0u;
+    /* every staging load of the chunk is issued before the first LDS store, so the chunk
+     * waits for one memory latency, not one per round of 64 units */
+    constexpr int kRounds = (kDecChunk / 4 + 1 + kWave) / kWave;
+    const uint32_t rounds = (units + kWave - 1) / kWave;
+    uint4 v[kRounds];
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+        const uint32_t u = lane + (uint32_t)r * kWave;
+        v[r] = make_uint4(0, 0, 0, 0);
+        if ((uint32_t)r < rounds && u < units) v[r] = src[u];
+    }
     const uint32_t so = wave_incl_scan(wl) - wl;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+        const uint32_t u = lane + (uint32_t)r * kWave;
+        if ((uint32_t)r < rounds && u < units) s_pay4[wave][u] = v[r];
+    }
     s_w[wave][lane] = wl;
     s_so[wave][lane] = so;
     wave_lds_sync();
