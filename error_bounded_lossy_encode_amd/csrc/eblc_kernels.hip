@@ -547,7 +547,7 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
 template <bool STRIDED, int CM>
 __device__ __forceinline__ void encode_body(
     const float *__restrict__ x, PlanArgs pa, Workspace ws, uint8_t *__restrict__ widths_dst,
-    uint64_t widths_bytes) {
+    uint64_t widths_bytes, uint32_t grp) {
     __shared__ uint4 s_pay4[kEncWaves][kEncPayWords / 4];
     __shared__ uint4 s_wid4[kEncWaves][kEncSegs / 16];
     __shared__ uint32_t s_stage[kEncWaves][2][kEscStage];
@@ -555,7 +555,7 @@ __device__ __forceinline__ void encode_body(
 
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = threadIdx.x >> 6;
-    const uint32_t c = blockIdx.x * kEncWaves + wave;
+    const uint32_t c = grp * kEncWaves + wave;
     const DevInfo *info = ws.info;
     EncState st = {0, 0, 0};
 
@@ -621,17 +621,21 @@ __device__ __forceinline__ void encode_body(
             sw += s_grp[0][k];
             se += s_grp[1][k];
         }
-        ws.group_words[blockIdx.x] = sw;
-        ws.group_esc[blockIdx.x] = se;
+        ws.group_words[grp] = sw;
+        ws.group_esc[grp] = se;
     }
 }
 
+/* The encoder walks a field's groups from the last to the first: the range pass has just read
+ * them first to last, so the workgroups dispatched first find the tail of the input in the
+ * last-level cache. */
 template <bool STRIDED, int CM>
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(Fields fs, PlanArgs pa, Workspace ws) {
     const uint32_t f = blockIdx.y;
     const Workspace w = lane_ws(ws, f, fs.ws_stride);
     uint8_t *wd = (fs.wdirect >> f) & 1u ? pick(fs.dst, f) + kHeaderBytes : w.widths;
-    encode_body<STRIDED, CM>(reinterpret_cast<const float *>(pick(fs.src, f)), pa, w, wd, pa.wsec);
+    encode_body<STRIDED, CM>(reinterpret_cast<const float *>(pick(fs.src, f)), pa, w, wd, pa.wsec,
+                             pa.ngroups - 1 - blockIdx.x);
 }
 
 /* ---- K3 / K6b: single-workgroup exclusive scan over groups -------------------------------- */
