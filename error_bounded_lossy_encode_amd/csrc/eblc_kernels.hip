@@ -205,13 +205,27 @@ __device__ __forceinline__ void slow_tile(const float xs[kEncLaneVals], uint32_t
     constexpr int V = kEncLaneVals;
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t j = lane & (kSegLanes - 1);
-    uint32_t esc = 0;
+    /* A rounded code above 2^T in magnitude (or NaN) escapes whatever the bound test and its
+     * neighbour give: the neighbour is at least 2^T too.  Such values skip the full rule; the
+     * rest of the missed values (near a cell boundary, or exactly 2^T) run it. */
+    uint32_t esc = 0, full = 0;
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-        if ((slow >> k) & 1u) {
-            uint32_t e;
-            q[k] = quantize_slow(xs[k], rintf(xs[k] * qp.r), qp, &e);
-            esc |= e << k;
+        const bool sure = !(fabsf(rintf(xs[k] * qp.r)) <= qp.tlim);
+        esc |= (((slow >> k) & 1u) && sure ? 1u : 0u) << k;
+        full |= (((slow >> k) & 1u) && !sure ? 1u : 0u) << k;
+    }
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        if ((esc >> k) & 1u) q[k] = 0;
+    if (__ballot(full != 0)) {
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            if ((full >> k) & 1u) {
+                uint32_t e;
+                q[k] = quantize_slow(xs[k], rintf(xs[k] * qp.r), qp, &e);
+                esc |= e << k;
+            }
         }
     }
     if (__ballot(esc != 0)) {
