@@ -429,11 +429,15 @@ def main() -> int:
             tag += "_center"
     enc_bytes = 4 * n + sizes + avg_payload
     dec_bytes = sizes + avg_payload + 4 * n
-    traffic = profiling.read_traffic(os.path.join(PROFILES, f"traffic_{tag}.txt"))
-
     # a launch codes up to `lanes` fields: the fields of a step over the launches of a stage
     lanes = args.lanes if len(items) > 1 and args.api == "batch" else 1
     per_launch = len(items) / -(-len(items) // lanes)
+    # a counter summary holds for its own launch configuration only
+    if args.halo > 0:
+        tag += f"_halo{args.halo}"
+    if len(items) > 1:
+        tag += f"_x{per_launch:g}"
+    traffic = profiling.read_traffic(os.path.join(PROFILES, f"traffic_{tag}.txt"))
 
     def roof(name, alg_bytes, key):
         # algorithmic bytes per launch over the mean launch duration in the timed steps
