@@ -1191,32 +1191,21 @@ __global__ __launch_bounds__(kScanThreads) void scan_decompress_kernel(Fields fs
 /* The tile loop of one decode chunk whose packed words and segment widths are staged in LDS:
  * per tile unpack each lane's 4 values, undo the zigzag, prefix-sum inside each block (in-lane,
  * then a segmented DPP scan across lanes, plus the carry from the previous tile when a block
- * spans tiles; CENTERED: plus the block's mean code at its start), dequantize with
+ * spans tiles; CENTERED: plus the block's mean code mu[t] at its start), dequantize with
  * f32(f32(q) * s) and store 4 values with one 128-bit store. */
 template <bool STRIDED, bool CENTERED>
-__device__ __forceinline__ void decode_tiles(const uint8_t *__restrict__ in, const PlanArgs &pa, const DevInfo *info,
+__device__ __forceinline__ void decode_tiles(const PlanArgs &pa, const DevInfo *info, const int32_t mu[kDecTiles],
                                              const uint32_t *pay, const uint32_t *s_w, const uint32_t *s_so,
                                              uint32_t lb, uint64_t cbase, bool full, float *__restrict__ out) {
     const uint32_t lane = threadIdx.x & 63;
     const uint64_t n = pa.n;
     const float s = info->dec_s;
     const uint32_t B = info->dec_B; /* the stream's block, validated by the header check */
-    const uint32_t log2B = (uint32_t)__builtin_ctz(B);
-    const int32_t *means = reinterpret_cast<const int32_t *>(in + kHeaderBytes + pa.wsec);
     const uint32_t seglen = (B / 4 < 64u) ? B / 4 : 64u;
     const uint32_t dist = lane & (seglen - 1);
     const uint32_t ntiles = full ? kDecTiles : (uint32_t)((n - cbase + kTile - 1) / kTile);
     const uint32_t j = lane & 7;
     int32_t carry = 0;
-    /* a centered stream's blocks start from their mean code: each tile's means, loaded up front
-     * (lanes past n read nothing: their blocks' means may lie past the stream's end) */
-    int32_t mu[kDecTiles];
-#pragma unroll
-    for (int t = 0; t < kDecTiles; ++t) {
-        const uint64_t ev = cbase + (uint64_t)t * kTile + 4 * lane;
-        const bool starts = (((uint32_t)t * kTile) & (B - 1)) == 0;
-        mu[t] = (CENTERED && starts && ev < n) ? means[ev >> log2B] : 0;
-    }
 #pragma unroll
     for (int t = 0; t < kDecTiles; ++t) {
         if ((uint32_t)t < ntiles) {
@@ -1309,6 +1298,23 @@ __device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in,
     const uint4 *src = reinterpret_cast<const uint4 *>(in) + a0 / 4;
     const uint64_t seg = (uint64_t)c * kDecSegs + lane;
     const uint32_t wl = seg < pa.nseg ? (uint32_t)in[kHeaderBytes + seg] : 0u;
+    /* a centered stream's blocks start from their mean code: in each tile that starts blocks,
+     * every lane takes its block's mean, loaded with the chunk's other loads (lanes past n read
+     * nothing: their blocks' means may lie past the stream's end) */
+    const bool centered = (info->dec_flags & 1u) != 0;
+    int32_t mu[kDecTiles];
+    {
+        const uint32_t B = info->dec_B;
+        const uint32_t log2B = (uint32_t)__builtin_ctz(B);
+        const int32_t *means = reinterpret_cast<const int32_t *>(in + kHeaderBytes + pa.wsec);
+#pragma unroll
+        for (int t = 0; t < kDecTiles; ++t) {
+            const uint64_t ev = cbase + (uint64_t)t * kTile + 4 * lane;
+            const bool starts = (((uint32_t)t * kTile) & (B - 1)) == 0;
+            mu[t] = 0;
+            if (centered && starts && ev < n) mu[t] = means[ev >> log2B];
+        }
+    }
     /* every staging load of the chunk is issued before the first LDS store, so the chunk
      * waits for one memory latency, not one per round of 64 units */
     constexpr int kRounds = (kDecChunk / 4 + 1 + kWave) / kWave;
@@ -1332,10 +1338,10 @@ __device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in,
 
     const uint32_t *pay = reinterpret_cast<const uint32_t *>(s_pay4[wave]);
     /* a centered stream takes its own copy of the tile loop, so the plain one stays as it is */
-    if (info->dec_flags & 1u)
-        decode_tiles<STRIDED, true>(in, pa, info, pay, s_w[wave], s_so[wave], lb, cbase, full, out);
+    if (centered)
+        decode_tiles<STRIDED, true>(pa, info, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out);
     else
-        decode_tiles<STRIDED, false>(in, pa, info, pay, s_w[wave], s_so[wave], lb, cbase, full, out);
+        decode_tiles<STRIDED, false>(pa, info, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out);
 }
 
 template <bool STRIDED>
