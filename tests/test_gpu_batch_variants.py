@@ -1,0 +1,134 @@
+"""Batched launches for every coder and layout: fields of one plan with lanes=3 go through
+eblc_compress_batch and eblc_decompress_batch as groups of three fields per launch and a ragged
+group, each field in its own lane's workspace.
+
+Each stream must equal the oracle's stream of that field alone, and each reconstruction the
+oracle decoder's, for the chunk coder at every chunk size, Lorenzo centering, and a padded
+(halo) layout whose batch mixes a 16-byte aligned field pointer with 4-byte aligned ones (the
+launch then takes the dword path for all its fields).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from error_bounded_lossy_encode_amd import synth
+from helpers import CANARY, oracle_stream
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = np.float32(-7.25e33)
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    from error_bounded_lossy_encode_amd import binding
+    binding.lib()
+    return binding, torch
+
+
+def make_fields(n, count, seed):
+    rng = np.random.default_rng(seed)
+    kinds = ["smooth", "normal", "ramp", "smooth", "specials", "smooth", "normal"]
+    fields = []
+    for k in range(count):
+        x = synth.tiny_array(rng, n, kinds[k % len(kinds)])
+        if k == 1:
+            x = x + np.float32(40.0)              # an offset field: centering changes the codes
+        if k == 3:
+            x[::37] = np.float32(np.inf)          # escapes in one field of the group
+        fields.append(np.ascontiguousarray(x, dtype=np.float32))
+    return fields
+
+
+VARIANTS = [
+    ("coder=chunk;chunk_bytes=4096;rel=1e-3;outlier_log2=15", [5 * 8192 + 777]),
+    ("coder=chunk;chunk_bytes=8192;abs=1e-2;outlier_log2=15", [3, 41, 339]),
+    ("coder=chunk;chunk_bytes=16384;rel=1e-4;outlier_log2=30", [2 * 16384 + 4100]),
+    ("center=1;rel=1e-3;block=64;outlier_log2=15", [7 * 2048 + 1234]),
+    ("center=1;abs=1e-3;block=2048;outlier_log2=30", [24, 1000]),
+    ("rel=1e-3;block=128;outlier_log2=15", [6 * 8192 + 3]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(VARIANTS)))
+def test_batch_lanes_variants_match_oracle(env, case):
+    binding, torch = env
+    opts, dims = VARIANTS[case]
+    n = int(np.prod(dims))
+    fields = make_fields(n, 7, 900 + case)
+    print(f"[batch-variants] {opts} dims={dims} fields={len(fields)} lanes=3", flush=True)
+    st, plan = binding.eblc_plan_create(dims, opts + ";lanes=3", 0)
+    assert st == binding.EBLC_OK, binding.eblc_status_string(st)
+    try:
+        maxb = binding.eblc_max_compressed_bytes(plan)
+        xs = [torch.from_numpy(f).cuda() for f in fields]
+        outs = [torch.full((maxb + 32,), CANARY, dtype=torch.uint8, device="cuda") for _ in fields]
+        ys = [torch.full((n + 8,), float("nan"), dtype=torch.float32, device="cuda") for _ in fields]
+        res = torch.zeros(16 * len(fields), dtype=torch.uint8, device="cuda")
+        assert binding.eblc_compress_batch(plan, xs, outs, res, capacities=[maxb] * len(fields)) == binding.EBLC_OK
+        assert binding.eblc_decompress_batch(plan, outs, ys, [maxb] * len(fields)) == binding.EBLC_OK
+        assert binding.eblc_plan_status(plan) == binding.EBLC_OK
+        recs = binding.result_records(res)
+        for k, f in enumerate(fields):
+            ref = oracle_stream(oracle, f, dims, opts)
+            nb, status = recs[k]
+            got = outs[k].cpu().numpy()
+            assert status == binding.EBLC_OK and nb == ref.size, (k, nb, ref.size)
+            assert np.array_equal(got[:nb], ref), f"field {k}: stream differs"
+            assert (got[maxb:] == CANARY).all(), f"field {k}: write past the capacity"
+            st, ref_dec = oracle.decompress(ref)
+            y = ys[k].cpu().numpy()
+            assert np.array_equal(y[:n].view(np.uint32), ref_dec.view(np.uint32)), f"field {k}: reconstruction"
+            assert np.isnan(y[n:]).all(), f"field {k}: decoder wrote past n"
+    finally:
+        binding.eblc_plan_destroy(plan)
+
+
+def test_batch_lanes_padded_fields_mixed_alignment(env):
+    binding, torch = env
+    dims, strides = [40, 36, 44], [36 * 52 + 3 * 52, 52, 1]
+    opts = "rel=1e-3;block=256;outlier_log2=15"
+    n = int(np.prod(dims))
+    span = 1 + sum((d - 1) * s for d, s in zip(dims, strides))
+    fields = make_fields(n, 5, 950)
+    # field k lives at element offset offs[k] of its buffer: 0 is 16-byte aligned, the others
+    # only 4-byte aligned, so each launch of three fields mixes them
+    offs = [0, 1, 4, 3, 2]
+    bufs, views = [], []
+    for f, o in zip(fields, offs):
+        buf = np.full(o + span + 8, SENTINEL, dtype=np.float32)
+        v = np.lib.stride_tricks.as_strided(buf[o:], shape=dims, strides=[4 * s for s in strides])
+        v[...] = f.reshape(dims)
+        bufs.append(buf)
+    st, plan = binding.eblc_plan_create(dims, opts + ";lanes=3", 0, strides=strides)
+    assert st == binding.EBLC_OK
+    try:
+        maxb = binding.eblc_max_compressed_bytes(plan)
+        xds = [torch.from_numpy(b).cuda() for b in bufs]
+        xs = [xd[o:] for xd, o in zip(xds, offs)]
+        outs = [torch.full((maxb,), CANARY, dtype=torch.uint8, device="cuda") for _ in fields]
+        yds = [torch.from_numpy(np.full_like(b, SENTINEL)).cuda() for b in bufs]
+        ys = [yd[o:] for yd, o in zip(yds, offs)]
+        res = torch.zeros(16 * len(fields), dtype=torch.uint8, device="cuda")
+        assert binding.eblc_compress_batch(plan, xs, outs, res) == binding.EBLC_OK
+        assert binding.eblc_decompress_batch(plan, outs, ys) == binding.EBLC_OK
+        assert binding.eblc_plan_status(plan) == binding.EBLC_OK
+        recs = binding.result_records(res)
+        for k, f in enumerate(fields):
+            ref = oracle_stream(oracle, f, dims, opts)
+            nb, status = recs[k]
+            assert status == binding.EBLC_OK and nb == ref.size
+            assert np.array_equal(outs[k].cpu().numpy()[:nb], ref), f"field {k}: stream differs"
+            st, ref_dec = oracle.decompress(ref)
+            ybuf = yds[k].cpu().numpy()
+            yv = np.lib.stride_tricks.as_strided(ybuf[offs[k]:], shape=dims, strides=[4 * s for s in strides])
+            assert np.array_equal(np.ascontiguousarray(yv).reshape(-1).view(np.uint32), ref_dec.view(np.uint32))
+            # only interior elements were written
+            touched = np.zeros(ybuf.size, bool)
+            idx = np.lib.stride_tricks.as_strided(np.arange(ybuf.size - offs[k]) + offs[k], shape=dims,
+                                                  strides=[8 * s for s in strides]).reshape(-1)
+            touched[idx] = True
+            assert (ybuf[~touched].view(np.uint32) == SENTINEL.view(np.uint32)).all(), f"field {k}: padding written"
+    finally:
+        binding.eblc_plan_destroy(plan)
