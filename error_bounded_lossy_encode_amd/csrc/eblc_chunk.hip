@@ -36,6 +36,9 @@ struct ChunkGeom {
     static constexpr int WAVES = V > kEncChunk ? V / kEncChunk : 1;      /* encode waves per chunk */
     static constexpr int PER_WAVE = V < kEncChunk ? kEncChunk / V : 1;   /* chunks per encode wave */
     static constexpr int TILES = V / kCTile;
+    static constexpr bool HALVES = V == 4096;   /* decoded half a chunk at a time */
+    static constexpr int PSH = 64 + 2;          /* LDS words per plane of a half */
+    static constexpr int DEC_LDSW = HALVES ? 32 * PSH : LDSW; /* decoder LDS words per wave */
     static_assert(V == 1024 || V == 2048 || V == 4096, "chunk of 4, 8 or 16 KiB");
     static_assert(PER_WAVE * (BM + V) <= WAVES * (kEncChunk + kEncChunk / 32), "scratch slots of 2112 words");
 };
@@ -341,17 +344,16 @@ __global__ __launch_bounds__(kEncThreads) void chunk_encode_kernel(Fields fs, Pl
  * inverse and a wave prefix sum plus the carry (the previous tile's last code) undo the first
  * difference, and f32(f32(q) * s) is stored.  The NT tiles' transposes and scans are
  * independent; only the carry chains them. */
-template <int V, int NT, bool FULL, bool STRIDED>
+template <int V, int NT, bool FULL, bool STRIDED, int PS = ChunkGeom<V>::PS>
 __device__ __forceinline__ void decode_tiles(const uint32_t *pl, uint32_t t0, uint32_t wmax, const Transpose &tr,
                                              float s, uint32_t &carry, float *__restrict__ out, const Layout &lo,
-                                             uint32_t cbase, uint32_t n) {
-    using Gm = ChunkGeom<V>;
+                                             uint32_t cbase, uint32_t n, uint32_t tl = 0) {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t h = lane >> 5, b = lane & 31;
     uint32_t incl[NT];
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
-        const uint32_t word = b < wmax ? pl[b * Gm::PS + 2u * (t0 + k) + h] : 0u;
+        const uint32_t word = b < wmax ? pl[b * PS + 2u * (t0 - tl + k) + h] : 0u;
         incl[k] = wave_incl_scan((uint32_t)unzigzag(tr(word)));
     }
 #pragma unroll
@@ -370,11 +372,10 @@ __device__ __forceinline__ void decode_tiles(const uint32_t *pl, uint32_t t0, ui
  * the lane totals and the carry undo the first difference for all four tiles, and one 128-bit
  * store writes the lane's four values.  The scratch belongs to the wave; LDS accesses of one
  * wave are performed in order, so the next group's writes cannot pass this group's read. */
-template <int V, int NQ, bool STRIDED>
+template <int V, int NQ, bool STRIDED, int PS = ChunkGeom<V>::PS>
 __device__ __forceinline__ void decode_quads(const uint32_t *pl, uint32_t t0, uint32_t wmax, const Transpose &tr,
                                              float s, uint32_t &carry, float *__restrict__ out, const Layout &lo,
-                                             uint32_t cbase, uint32_t *sx) {
-    using Gm = ChunkGeom<V>;
+                                             uint32_t cbase, uint32_t *sx, uint32_t tl = 0) {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t h = lane >> 5, b = lane & 31;
 #pragma unroll
@@ -382,7 +383,7 @@ __device__ __forceinline__ void decode_quads(const uint32_t *pl, uint32_t t0, ui
         const uint32_t t = t0 + 4u * g;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const uint32_t word = b < wmax ? pl[b * Gm::PS + 2u * (t + k) + h] : 0u;
+            const uint32_t word = b < wmax ? pl[b * PS + 2u * (t - tl + k) + h] : 0u;
             sx[64 * k + lane] = (uint32_t)unzigzag(tr(word));
         }
         wave_lds_sync();
@@ -410,7 +411,7 @@ template <int V, bool STRIDED>
 __device__ __forceinline__ void chunk_decode_body(const uint8_t *__restrict__ in, PlanArgs pa,
                                                   Workspace ws, float *__restrict__ out) {
     using Gm = ChunkGeom<V>;
-    __shared__ uint32_t s_words[kWavesPerBlock][Gm::LDSW];
+    __shared__ uint32_t s_words[kWavesPerBlock][Gm::DEC_LDSW];
     __shared__ uint4 s_x4[kWavesPerBlock][4 * kCTile / 4];
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = threadIdx.x >> 6;
@@ -453,48 +454,92 @@ __device__ __forceinline__ void chunk_decode_body(const uint8_t *__restrict__ in
     else if (nz0) top = 63 - __clzll((long long)nz0);
     const uint32_t wmax = top < 0 ? 0u : (uint32_t)top * 32u / Gm::G + 1u;
     uint32_t *pl = s_words[wave];
-    /* un-RZE: every plane's loads first (into registers), then the LDS stores */
-    uint32_t wv[32 * Gm::BATCHES];
-    uint32_t run = 0;
-#pragma unroll
-    for (int pb = 0; pb < 32; ++pb) {
-#pragma unroll
-        for (int kk = 0; kk < Gm::BATCHES; ++kk) {
-            uint32_t word = 0;
-            if ((uint32_t)pb < wmax) {
-                const uint32_t wi = (pb * Gm::G + 64 * kk) / 32;
-                const uint32_t lo = wi < 64 ? readlane(bm0, (int)wi) : readlane(bm1, (int)(wi - 64));
-                uint32_t hi = 0;
-                if (Gm::G >= 64) hi = wi + 1 < 64 ? readlane(bm0, (int)(wi + 1)) : readlane(bm1, (int)(wi + 1 - 64));
-                const uint64_t M = (uint64_t)lo | ((uint64_t)hi << 32);
-                if ((M >> lane) & 1u) word = blob[Gm::BM + run + mbcnt64(M)];
-                run += (uint32_t)__popcll(M);
-            }
-            wv[pb * Gm::BATCHES + kk] = word;
-        }
-    }
-#pragma unroll
-    for (int pb = 0; pb < 32; ++pb) {
-        if ((uint32_t)pb < wmax) {
-#pragma unroll
-            for (int kk = 0; kk < Gm::BATCHES; ++kk) {
-                const uint32_t gi = 64u * kk + lane;
-                if (Gm::G >= 64 || gi < (uint32_t)Gm::G) pl[pb * Gm::PS + gi] = wv[pb * Gm::BATCHES + kk];
-            }
-        }
-    }
-    wave_lds_sync();
     const Transpose tr(lane);
     const float s = info->dec_s;
     uint32_t carry = 0;
-    if (cnt == (uint32_t)V) {
-        uint32_t *sx = reinterpret_cast<uint32_t *>(s_x4[wave]);
-        for (uint32_t t = 0; t < (uint32_t)Gm::TILES; t += 8)
-            decode_quads<V, 2, STRIDED>(pl, t, wmax, tr, s, carry, out, pa.lay, cbase, sx);
-    } else {
+    uint32_t *sx = reinterpret_cast<uint32_t *>(s_x4[wave]);
+    if constexpr (Gm::HALVES) {
+        /* A 4096-value chunk goes through a half-size buffer: the planes' words of groups 0-63
+         * (tiles 0-31), then those of groups 64-127 (tiles 32-63), each half's loads issued
+         * before its LDS stores.  The running word count covers both halves' bitmap bits, and
+         * the running sum carries from the first half into the second. */
+        constexpr int PSH = Gm::PSH;
         const uint32_t ntiles = (cnt + kCTile - 1) / kCTile;
-        for (uint32_t t = 0; t < ntiles; ++t)
-            decode_tiles<V, 1, false, STRIDED>(pl, t, wmax, tr, s, carry, out, pa.lay, cbase, n);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const uint32_t t0 = 32u * hh;
+            if (t0 >= ntiles) break;
+            uint32_t wv[32];
+            uint32_t run = 0;
+#pragma unroll
+            for (int pb = 0; pb < 32; ++pb) {
+                wv[pb] = 0;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    if ((uint32_t)pb < wmax) {
+                        const uint32_t wi = (pb * Gm::G + 64 * kk) / 32;
+                        const uint32_t lo = wi < 64 ? readlane(bm0, (int)wi) : readlane(bm1, (int)(wi - 64));
+                        const uint32_t hi = wi + 1 < 64 ? readlane(bm0, (int)(wi + 1)) : readlane(bm1, (int)(wi + 1 - 64));
+                        const uint64_t M = (uint64_t)lo | ((uint64_t)hi << 32);
+                        if (kk == hh && ((M >> lane) & 1u)) wv[pb] = blob[Gm::BM + run + mbcnt64(M)];
+                        run += (uint32_t)__popcll(M);
+                    }
+                }
+            }
+            wave_lds_sync(); /* the first half's reads are done before the second half's stores */
+#pragma unroll
+            for (int pb = 0; pb < 32; ++pb)
+                if ((uint32_t)pb < wmax) pl[pb * PSH + lane] = wv[pb];
+            wave_lds_sync();
+            if (cnt == (uint32_t)V) {
+                for (uint32_t t = t0; t < t0 + 32u; t += 8)
+                    decode_quads<V, 2, STRIDED, PSH>(pl, t, wmax, tr, s, carry, out, pa.lay, cbase, sx, t0);
+            } else {
+                const uint32_t te = ntiles < t0 + 32u ? ntiles : t0 + 32u;
+                for (uint32_t t = t0; t < te; ++t)
+                    decode_tiles<V, 1, false, STRIDED, PSH>(pl, t, wmax, tr, s, carry, out, pa.lay, cbase, n, t0);
+            }
+        }
+    } else {
+        /* un-RZE: every plane's loads first (into registers), then the LDS stores */
+        uint32_t wv[32 * Gm::BATCHES];
+        uint32_t run = 0;
+#pragma unroll
+        for (int pb = 0; pb < 32; ++pb) {
+#pragma unroll
+            for (int kk = 0; kk < Gm::BATCHES; ++kk) {
+                uint32_t word = 0;
+                if ((uint32_t)pb < wmax) {
+                    const uint32_t wi = (pb * Gm::G + 64 * kk) / 32;
+                    const uint32_t lo = wi < 64 ? readlane(bm0, (int)wi) : readlane(bm1, (int)(wi - 64));
+                    uint32_t hi = 0;
+                    if (Gm::G >= 64) hi = wi + 1 < 64 ? readlane(bm0, (int)(wi + 1)) : readlane(bm1, (int)(wi + 1 - 64));
+                    const uint64_t M = (uint64_t)lo | ((uint64_t)hi << 32);
+                    if ((M >> lane) & 1u) word = blob[Gm::BM + run + mbcnt64(M)];
+                    run += (uint32_t)__popcll(M);
+                }
+                wv[pb * Gm::BATCHES + kk] = word;
+            }
+        }
+#pragma unroll
+        for (int pb = 0; pb < 32; ++pb) {
+            if ((uint32_t)pb < wmax) {
+#pragma unroll
+                for (int kk = 0; kk < Gm::BATCHES; ++kk) {
+                    const uint32_t gi = 64u * kk + lane;
+                    if (Gm::G >= 64 || gi < (uint32_t)Gm::G) pl[pb * Gm::PS + gi] = wv[pb * Gm::BATCHES + kk];
+                }
+            }
+        }
+        wave_lds_sync();
+        if (cnt == (uint32_t)V) {
+            for (uint32_t t = 0; t < (uint32_t)Gm::TILES; t += 8)
+                decode_quads<V, 2, STRIDED>(pl, t, wmax, tr, s, carry, out, pa.lay, cbase, sx);
+        } else {
+            const uint32_t ntiles = (cnt + kCTile - 1) / kCTile;
+            for (uint32_t t = 0; t < ntiles; ++t)
+                decode_tiles<V, 1, false, STRIDED>(pl, t, wmax, tr, s, carry, out, pa.lay, cbase, n);
+        }
     }
 }
 
