@@ -36,9 +36,16 @@ struct ChunkGeom {
     static constexpr int WAVES = V > kEncChunk ? V / kEncChunk : 1;      /* encode waves per chunk */
     static constexpr int PER_WAVE = V < kEncChunk ? kEncChunk / V : 1;   /* chunks per encode wave */
     static constexpr int TILES = V / kCTile;
-    static constexpr bool HALVES = V == 4096;   /* decoded half a chunk at a time */
+    /* The decoder's LDS: 1024-value chunks are decoded from their words as staged (RAW: up to
+     * BM + V words from a 16-byte unit boundary, 3 words before and 3 after, then the bitmap's
+     * popcount prefix); 2048-value chunks from their rebuilt planes; 4096-value chunks from
+     * the rebuilt planes of half a chunk at a time (HALVES). */
+    static constexpr bool RAW = V == 1024;
+    static constexpr bool HALVES = V == 4096;
     static constexpr int PSH = 64 + 2;          /* LDS words per plane of a half */
-    static constexpr int DEC_LDSW = HALVES ? 32 * PSH : LDSW; /* decoder LDS words per wave */
+    static constexpr int RAWW = 4 * ((3 + BM + V + 3) / 4);
+    static constexpr int DEC_LDSW = RAW ? RAWW + BM : HALVES ? 32 * PSH : LDSW; /* per wave */
+    static_assert(DEC_LDSW % 4 == 0, "whole 16-byte units");
     static_assert(V == 1024 || V == 2048 || V == 4096, "chunk of 4, 8 or 16 KiB");
     static_assert(PER_WAVE * (BM + V) <= WAVES * (kEncChunk + kEncChunk / 32), "scratch slots of 2112 words");
 };
@@ -344,16 +351,39 @@ __global__ __launch_bounds__(kEncThreads) void chunk_encode_kernel(Fields fs, Pl
  * inverse and a wave prefix sum plus the carry (the previous tile's last code) undo the first
  * difference, and f32(f32(q) * s) is stored.  The NT tiles' transposes and scans are
  * independent; only the carry chains them. */
-template <int V, int NT, bool FULL, bool STRIDED, int PS = ChunkGeom<V>::PS>
-__device__ __forceinline__ void decode_tiles(const uint32_t *pl, uint32_t t0, uint32_t wmax, const Transpose &tr,
+/* Word g of bit plane b of a chunk (the word of the plane for group g), for the tile loops. */
+/* From planes rebuilt in LDS, PS words per plane, holding groups g0 onwards. */
+struct PlaneFetch {
+    const uint32_t *pl;
+    uint32_t ps, g0;
+    __device__ __forceinline__ uint32_t operator()(uint32_t b, uint32_t g) const { return pl[b * ps + g - g0]; }
+};
+
+/* From the chunk's RZE words staged as they lie in the stream (raw[0] = the first bitmap word)
+ * and the exclusive popcount prefix of the bitmap words: a word whose bitmap bit is clear is 0,
+ * else it is nonzero word number (prefix + the set bits below it in its bitmap word). */
+template <int V>
+struct RawFetch {
+    const uint32_t *raw;
+    const uint32_t *pre;
+    __device__ __forceinline__ uint32_t operator()(uint32_t b, uint32_t g) const {
+        const uint32_t wi = b * (uint32_t)ChunkGeom<V>::G + g, k = wi >> 5, j = wi & 31u;
+        const uint32_t bmw = raw[k];
+        const uint32_t below = (uint32_t)__popc(bmw & ((1u << j) - 1u));
+        return ((bmw >> j) & 1u) ? raw[ChunkGeom<V>::BM + pre[k] + below] : 0u;
+    }
+};
+
+template <int V, int NT, bool FULL, bool STRIDED, typename F>
+__device__ __forceinline__ void decode_tiles(const F &fetch, uint32_t t0, uint32_t wmax, const Transpose &tr,
                                              float s, uint32_t &carry, float *__restrict__ out, const Layout &lo,
-                                             uint32_t cbase, uint32_t n, uint32_t tl = 0) {
+                                             uint32_t cbase, uint32_t n) {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t h = lane >> 5, b = lane & 31;
     uint32_t incl[NT];
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
-        const uint32_t word = b < wmax ? pl[b * PS + 2u * (t0 - tl + k) + h] : 0u;
+        const uint32_t word = b < wmax ? fetch(b, 2u * (t0 + k) + h) : 0u;
         incl[k] = wave_incl_scan((uint32_t)unzigzag(tr(word)));
     }
 #pragma unroll
@@ -372,10 +402,10 @@ __device__ __forceinline__ void decode_tiles(const uint32_t *pl, uint32_t t0, ui
  * the lane totals and the carry undo the first difference for all four tiles, and one 128-bit
  * store writes the lane's four values.  The scratch belongs to the wave; LDS accesses of one
  * wave are performed in order, so the next group's writes cannot pass this group's read. */
-template <int V, int NQ, bool STRIDED, int PS = ChunkGeom<V>::PS>
-__device__ __forceinline__ void decode_quads(const uint32_t *pl, uint32_t t0, uint32_t wmax, const Transpose &tr,
+template <int V, int NQ, bool STRIDED, typename F>
+__device__ __forceinline__ void decode_quads(const F &fetch, uint32_t t0, uint32_t wmax, const Transpose &tr,
                                              float s, uint32_t &carry, float *__restrict__ out, const Layout &lo,
-                                             uint32_t cbase, uint32_t *sx, uint32_t tl = 0) {
+                                             uint32_t cbase, uint32_t *sx) {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t h = lane >> 5, b = lane & 31;
 #pragma unroll
@@ -383,7 +413,7 @@ __device__ __forceinline__ void decode_quads(const uint32_t *pl, uint32_t t0, ui
         const uint32_t t = t0 + 4u * g;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const uint32_t word = b < wmax ? pl[b * PS + 2u * (t - tl + k) + h] : 0u;
+            const uint32_t word = b < wmax ? fetch(b, 2u * (t + k) + h) : 0u;
             sx[64 * k + lane] = (uint32_t)unzigzag(tr(word));
         }
         wave_lds_sync();
@@ -403,15 +433,18 @@ __device__ __forceinline__ void decode_quads(const uint32_t *pl, uint32_t t0, ui
 
 /* One wave per chunk.  The chunk's bitmap sits in two VGPRs (lane l: bitmap words l and
  * 64 + l); its popcount must equal the chunk's word count minus the bitmap, else the stream is
- * flagged.  Un-RZE rebuilds the planes below the highest nonzero one in LDS: per 64-word batch
- * the batch's bitmap bits and mbcnt give each present word's position in the chunk; all of the
- * chunk's loads are issued before the first LDS store.  Then decode_tiles, eight tiles at a
- * time for a full chunk. */
+ * flagged.  A 1024-value chunk is staged in LDS as its words lie in the stream, loaded
+ * together with the bitmap, and each tile reads a plane word from it by its rank among the
+ * nonzero words (RawFetch).  Larger chunks rebuild their planes below the highest nonzero one
+ * in LDS (a 4096-value chunk half a chunk at a time): per 64-word batch the batch's bitmap bits
+ * and mbcnt give each present word's position (PlaneFetch); all of a rebuild's loads are issued
+ * before its LDS stores.  Then the tile loops, eight tiles at a time for a full chunk.  (A
+ * 2048-value chunk read in place was slower: 134 -> 149 us on the 512^3 field.) */
 template <int V, bool STRIDED>
 __device__ __forceinline__ void chunk_decode_body(const uint8_t *__restrict__ in, PlanArgs pa,
                                                   Workspace ws, float *__restrict__ out) {
     using Gm = ChunkGeom<V>;
-    __shared__ uint32_t s_words[kWavesPerBlock][Gm::DEC_LDSW];
+    __shared__ uint4 s_lds4[kWavesPerBlock][Gm::DEC_LDSW / 4];
     __shared__ uint4 s_x4[kWavesPerBlock][4 * kCTile / 4];
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = threadIdx.x >> 6;
@@ -443,6 +476,26 @@ __device__ __forceinline__ void chunk_decode_body(const uint8_t *__restrict__ in
     const uint32_t *blob = reinterpret_cast<const uint32_t *>(in + info->payload_off) + W;
     const uint32_t bm0 = lane < (uint32_t)(Gm::BM < 64 ? Gm::BM : 64) ? blob[lane] : 0u;
     const uint32_t bm1 = Gm::BM > 64 ? blob[64 + lane] : 0u;
+    /* RAW: all of the chunk's words, as they lie in the stream, are loaded with its bitmap
+     * (16-byte units from the unit holding its first word) */
+    constexpr int kRounds = Gm::RAW ? (Gm::RAWW / 4 + kWave - 1) / kWave : 1;
+    uint4 v[kRounds];
+    uint32_t lb = 0, units = 0;
+    if constexpr (Gm::RAW) {
+        const uint64_t sw = info->payload_off / 4 + W;
+        const uint64_t a0 = sw & ~(uint64_t)3;
+        lb = (uint32_t)(sw - a0);
+        units = (lb + P + 3) >> 2;
+        if (units > (uint32_t)(Gm::RAWW / 4)) units = Gm::RAWW / 4;
+        const uint4 *src = reinterpret_cast<const uint4 *>(in) + a0 / 4;
+        const uint32_t rounds = (units + kWave - 1) / kWave;
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            const uint32_t u = lane + (uint32_t)r * kWave;
+            v[r] = make_uint4(0, 0, 0, 0);
+            if ((uint32_t)r < rounds && u < units) v[r] = src[u];
+        }
+    }
     const uint32_t pc = wave_incl_scan((uint32_t)__popc(bm0) + (uint32_t)__popc(bm1));
     if (readlane(pc, 63) + Gm::BM != P) {
         if (lane == 0) atomicOr(&info->sticky, 1u);
@@ -453,7 +506,7 @@ __device__ __forceinline__ void chunk_decode_body(const uint8_t *__restrict__ in
     if (nz1) top = 64 + 63 - __clzll((long long)nz1);
     else if (nz0) top = 63 - __clzll((long long)nz0);
     const uint32_t wmax = top < 0 ? 0u : (uint32_t)top * 32u / Gm::G + 1u;
-    uint32_t *pl = s_words[wave];
+    uint32_t *pl = reinterpret_cast<uint32_t *>(s_lds4[wave]);
     const Transpose tr(lane);
     const float s = info->dec_s;
     uint32_t carry = 0;
@@ -491,14 +544,34 @@ __device__ __forceinline__ void chunk_decode_body(const uint8_t *__restrict__ in
             for (int pb = 0; pb < 32; ++pb)
                 if ((uint32_t)pb < wmax) pl[pb * PSH + lane] = wv[pb];
             wave_lds_sync();
+            const PlaneFetch fetch{pl, (uint32_t)PSH, 2u * t0};
             if (cnt == (uint32_t)V) {
                 for (uint32_t t = t0; t < t0 + 32u; t += 8)
-                    decode_quads<V, 2, STRIDED, PSH>(pl, t, wmax, tr, s, carry, out, pa.lay, cbase, sx, t0);
+                    decode_quads<V, 2, STRIDED>(fetch, t, wmax, tr, s, carry, out, pa.lay, cbase, sx);
             } else {
                 const uint32_t te = ntiles < t0 + 32u ? ntiles : t0 + 32u;
                 for (uint32_t t = t0; t < te; ++t)
-                    decode_tiles<V, 1, false, STRIDED, PSH>(pl, t, wmax, tr, s, carry, out, pa.lay, cbase, n, t0);
+                    decode_tiles<V, 1, false, STRIDED>(fetch, t, wmax, tr, s, carry, out, pa.lay, cbase, n);
             }
+        }
+    } else if constexpr (Gm::RAW) {
+        /* the staged words into LDS, the bitmap's exclusive popcount prefix after them; the
+         * tile loops then read each plane word in place */
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            const uint32_t u = lane + (uint32_t)r * kWave;
+            if (u < units) s_lds4[wave][u] = v[r];
+        }
+        if (lane < (uint32_t)Gm::BM) pl[Gm::RAWW + lane] = pc - (uint32_t)__popc(bm0);
+        wave_lds_sync();
+        const RawFetch<V> fetch{pl + lb, pl + Gm::RAWW};
+        if (cnt == (uint32_t)V) {
+            for (uint32_t t = 0; t < (uint32_t)Gm::TILES; t += 8)
+                decode_quads<V, 2, STRIDED>(fetch, t, wmax, tr, s, carry, out, pa.lay, cbase, sx);
+        } else {
+            const uint32_t ntiles = (cnt + kCTile - 1) / kCTile;
+            for (uint32_t t = 0; t < ntiles; ++t)
+                decode_tiles<V, 1, false, STRIDED>(fetch, t, wmax, tr, s, carry, out, pa.lay, cbase, n);
         }
     } else {
         /* un-RZE: every plane's loads first (into registers), then the LDS stores */
@@ -532,13 +605,14 @@ __device__ __forceinline__ void chunk_decode_body(const uint8_t *__restrict__ in
             }
         }
         wave_lds_sync();
+        const PlaneFetch fetch{pl, (uint32_t)Gm::PS, 0u};
         if (cnt == (uint32_t)V) {
             for (uint32_t t = 0; t < (uint32_t)Gm::TILES; t += 8)
-                decode_quads<V, 2, STRIDED>(pl, t, wmax, tr, s, carry, out, pa.lay, cbase, sx);
+                decode_quads<V, 2, STRIDED>(fetch, t, wmax, tr, s, carry, out, pa.lay, cbase, sx);
         } else {
             const uint32_t ntiles = (cnt + kCTile - 1) / kCTile;
             for (uint32_t t = 0; t < ntiles; ++t)
-                decode_tiles<V, 1, false, STRIDED>(pl, t, wmax, tr, s, carry, out, pa.lay, cbase, n);
+                decode_tiles<V, 1, false, STRIDED>(fetch, t, wmax, tr, s, carry, out, pa.lay, cbase, n);
         }
     }
 }
