@@ -370,7 +370,7 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
                                              uint32_t *pay, uint8_t *wid, uint32_t *emask_chunk,
                                              uint32_t *stage_idx, uint32_t *stage_val, EncState &st,
                                              uint32_t log2B, int32_t *__restrict__ means, bool narrow,
-                                             uint32_t *__restrict__ slot) {
+                                             uint32_t *__restrict__ slot, bool slot_nt) {
     constexpr int V = kEncLaneVals;
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t j = lane & (kSegLanes - 1), g = lane / kSegLanes;
@@ -546,13 +546,19 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
         wave_lds_sync();
         if (w0 == 0) {
             uint4 *dst = reinterpret_cast<uint4 *>(slot);
-            for (uint32_t i = lane; i < (nw + 3) / 4; i += kWave) dst[i] = pay4[i];
+            if (slot_nt) {
+                for (uint32_t i = lane; i < (nw + 3) / 4; i += kWave) st_nt(dst + i, pay4[i]);
+            } else {
+                for (uint32_t i = lane; i < (nw + 3) / 4; i += kWave) dst[i] = pay4[i];
+            }
         } else {
             for (uint32_t i = lane; i < nw; i += kWave) slot[w0 + i] = pay[i];
         }
         wave_lds_sync();
     }
 }
+
+constexpr uint64_t kSlotCacheBytes = 128ull << 20;
 
 /* One wave per encode chunk, kEncWaves chunks per workgroup.  Outputs per chunk: its packed
  * words in its scratch slot, its width bytes (into the stream, or into staging when the output
@@ -574,6 +580,11 @@ __device__ __forceinline__ void encode_body(
     EncState st = {0, 0, 0};
 
     if (c < pa.nchunks && info->valid) {
+        /* The scratch slots take plain stores, so the compaction finds them in the 256 MB
+         * last-level cache, unless the fields of this launch wrote more than kSlotCacheBytes of
+         * payload on their lanes' previous calls: payloads that large do not stay there, and
+         * non-temporal stores then write them faster (the stream does not depend on this). */
+        const bool slot_nt = (uint64_t)gridDim.y * info->payload_words * 4u > kSlotCacheBytes;
         QParams qp;
         qp.eb = info->eb_f;
         qp.s = info->s;
@@ -603,11 +614,11 @@ __device__ __forceinline__ void encode_body(
         if (cbase + kEncChunk <= pa.n)
             encode_chunk<true, STRIDED, CM>(x, pa.lay, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk,
                                                 stage_idx, stage_val, st, pa.log2B, ws.means, narrow,
-                                                ws.scratch + cbase);
+                                                ws.scratch + cbase, slot_nt);
         else
             encode_chunk<false, STRIDED, CM>(x, pa.lay, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk,
                                                  stage_idx, stage_val, st, pa.log2B, ws.means, narrow,
-                                                 ws.scratch + cbase);
+                                                 ws.scratch + cbase, slot_nt);
         /* widths -> stream (or staging) */
         if (lane < kEncSegs / 16) {
             const uint64_t off = (uint64_t)c * kEncSegs + 16u * lane;
