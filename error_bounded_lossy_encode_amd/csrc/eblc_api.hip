@@ -230,14 +230,20 @@ DevInfo *lane_info(const eblc_plan *plan, int k) {
 
 eblc_status hip_status(hipError_t e) { return e == hipSuccess ? EBLC_OK : EBLC_DEVICE_ERROR; }
 
+/* Whether the measurement hook's name filter (",name,name,"; empty: every kernel) names `name`. */
+bool timed_kernel(const eblc_plan *p, const char *name) {
+    if (p->ev_filter.empty()) return true;
+    const size_t len = std::strlen(name);
+    for (size_t at = p->ev_filter.find(name); at != std::string::npos; at = p->ev_filter.find(name, at + 1))
+        if (p->ev_filter[at - 1] == ',' && p->ev_filter[at + len] == ',') return true;
+    return false;
+}
+
 /* Measurement hook: the launcher's kernels record the next event pair of the plan's pool while
  * it has room (see LaunchEvents). */
 template <typename F>
-hipError_t timed(eblc_plan *p, hipStream_t st, const char *name, F &&launch) {
-    if (2 * p->ev_used + 2 > p->ev_pool.size()) return launch();
-    if (!p->ev_filter.empty() && p->ev_filter.find("," + std::string(name) + ",") == std::string::npos)
-        return launch();
-    (void)st;
+hipError_t timed(eblc_plan *p, const char *name, F &&launch) {
+    if (2 * p->ev_used + 2 > p->ev_pool.size() || !timed_kernel(p, name)) return launch();
     const size_t k = p->ev_used++;
     p->ev_names[k] = name;
     g_launch_events.start = p->ev_pool[2 * k];
@@ -290,13 +296,13 @@ hipError_t enqueue_compress(eblc_plan *plan, int nf, const float *const *in, voi
     }
     const uint32_t n = (uint32_t)nf;
     hipError_t e = hipSuccess;
-    if (plan->rel) e = timed(plan, st, "range", [&] { return launch_range(fs, n, pa, ws, plan->eps, st); });
+    if (plan->rel) e = timed(plan, "range", [&] { return launch_range(fs, n, pa, ws, plan->eps, st); });
     if (e == hipSuccess)
-        e = timed(plan, st, "encode", [&] {
+        e = timed(plan, "encode", [&] {
             return pa.V ? launch_chunk_encode(fs, n, pa, ws, st) : launch_encode(fs, n, pa, ws, st);
         });
-    if (e == hipSuccess) e = timed(plan, st, "scan", [&] { return launch_scan_compress(fs, n, pa, ws, st); });
-    if (e == hipSuccess) e = timed(plan, st, "compact", [&] { return launch_compact(fs, n, pa, ws, st); });
+    if (e == hipSuccess) e = timed(plan, "scan", [&] { return launch_scan_compress(fs, n, pa, ws, st); });
+    if (e == hipSuccess) e = timed(plan, "compact", [&] { return launch_compact(fs, n, pa, ws, st); });
     return e;
 }
 
@@ -314,13 +320,13 @@ hipError_t enqueue_decompress(eblc_plan *plan, int nf, const void *const *in, co
         fs.bytes[k] = compressed_bytes[k];
     }
     const uint32_t n = (uint32_t)nf;
-    hipError_t e = timed(plan, st, "decode_sizes", [&] { return launch_decode_sizes(fs, n, pa, ws, st); });
-    if (e == hipSuccess) e = timed(plan, st, "decode_scan", [&] { return launch_scan_decompress(fs, n, pa, ws, st); });
+    hipError_t e = timed(plan, "decode_sizes", [&] { return launch_decode_sizes(fs, n, pa, ws, st); });
+    if (e == hipSuccess) e = timed(plan, "decode_scan", [&] { return launch_scan_decompress(fs, n, pa, ws, st); });
     if (e == hipSuccess)
-        e = timed(plan, st, "decode", [&] {
+        e = timed(plan, "decode", [&] {
             return pa.V ? launch_chunk_decode(fs, n, pa, ws, st) : launch_decode(fs, n, pa, ws, st);
         });
-    if (e == hipSuccess) e = timed(plan, st, "patch", [&] { return launch_patch(fs, n, pa, ws, st); });
+    if (e == hipSuccess) e = timed(plan, "patch", [&] { return launch_patch(fs, n, pa, ws, st); });
     return e;
 }
 
