@@ -191,7 +191,9 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps; default: whole steps until at least 2 s have passed (at "
+                         "least 10), since the GPU reaches its steady clocks only under sustained load")
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -202,6 +204,10 @@ def main() -> int:
     ap.add_argument("--kernel-events", choices=["on", "off"], default="on",
                     help="on: the library records a HIP event pair around every encode and decode launch "
                          "of the timed steps (up to 8192 launches), for the rooflines")
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="time the encode and decode launches of every k-th compress and decompress "
+                         "launch sequence of the timed steps (each timed dispatch costs the stream a few "
+                         "microseconds)")
     ap.add_argument("--breakdown-steps", type=int, default=2,
                     help="untimed steps after the timed ones with an event pair around every launch, "
                          "for the per-kernel breakdown (event records delay the stream, so the timed "
@@ -300,9 +306,20 @@ def main() -> int:
             st = binding.eblc_decompress(plan.handle, outs[i], nbytes[i], ys[i], stream=stream)
             assert st == binding.EBLC_OK, binding.eblc_status_string(st)
 
-    for _ in range(args.warmup):
-        compress_all()
-        decompress_all()
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            compress_all()
+            decompress_all()
+    else:
+        args.warmup = 0
+        t_w = time.perf_counter()
+        while args.warmup < 10 or time.perf_counter() - t_w < 2.0:
+            compress_all()
+            decompress_all()
+            args.warmup += 1
+            if args.warmup % 10 == 0:
+                torch.cuda.synchronize()
+        log(f"[bench] {args.warmup} warmup steps")
     torch.cuda.synchronize()
     assert binding.eblc_plan_status(plan.handle) == binding.EBLC_OK
 
@@ -313,7 +330,8 @@ def main() -> int:
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     timed_launches = min(8192, args.steps * len(items) * 2)
     if args.kernel_events == "on":
-        assert binding.eblc_plan_set_profiling(plan.handle, timed_launches, "encode,decode") == binding.EBLC_OK
+        assert binding.eblc_plan_set_profiling(plan.handle, timed_launches, "encode,decode",
+                                               args.event_every) == binding.EBLC_OK
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):

@@ -86,7 +86,7 @@ def lib():
     L.eblc_plan_destroy.restype = None
     L.eblc_status_string.argtypes = [I]
     L.eblc_status_string.restype = ctypes.c_char_p
-    L.eblc_plan_set_profiling.argtypes = [P, I, ctypes.c_char_p]
+    L.eblc_plan_set_profiling.argtypes = [P, I, ctypes.c_char_p, I]
     L.eblc_plan_set_profiling.restype = I
     L.eblc_plan_kernel_times.argtypes = [P, ctypes.POINTER(ctypes.c_char_p),
                                          ctypes.POINTER(ctypes.c_float), ctypes.POINTER(I), I]
@@ -207,11 +207,12 @@ def eblc_plan_destroy(plan) -> None:
         lib().eblc_plan_destroy(plan)
 
 
-def eblc_plan_set_profiling(plan, max_launches: int, kernels: str | None = None) -> int:
+def eblc_plan_set_profiling(plan, max_launches: int, kernels: str | None = None, every: int = 1) -> int:
     """Record an event pair around each of the plan's next max_launches launches (0: off) of
-    the kernels named in the comma-separated `kernels` (None: every kernel)."""
+    the kernels named in the comma-separated `kernels` (None: every kernel), in every
+    every-th compress and decompress launch sequence."""
     return int(lib().eblc_plan_set_profiling(plan, int(max_launches),
-                                             None if kernels is None else kernels.encode()))
+                                             None if kernels is None else kernels.encode(), int(every)))
 
 
 def eblc_plan_kernel_times(plan, max_kernels: int = 16):

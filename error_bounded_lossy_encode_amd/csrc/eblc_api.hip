@@ -52,6 +52,9 @@ struct eblc_plan {
     std::vector<const char *> ev_names;
     size_t ev_used = 0;
     std::string ev_filter;      /* ",name,name," of the kernels to time; empty: every kernel */
+    uint32_t ev_every = 1;      /* time every ev_every-th compress and decompress call */
+    uint64_t ev_calls[2] = {0, 0};
+    bool ev_sampled = true;     /* the current call is timed */
 };
 
 namespace {
@@ -243,7 +246,7 @@ bool timed_kernel(const eblc_plan *p, const char *name) {
  * it has room (see LaunchEvents). */
 template <typename F>
 hipError_t timed(eblc_plan *p, const char *name, F &&launch) {
-    if (2 * p->ev_used + 2 > p->ev_pool.size() || !timed_kernel(p, name)) return launch();
+    if (2 * p->ev_used + 2 > p->ev_pool.size() || !p->ev_sampled || !timed_kernel(p, name)) return launch();
     const size_t k = p->ev_used++;
     p->ev_names[k] = name;
     g_launch_events.start = p->ev_pool[2 * k];
@@ -284,6 +287,7 @@ hipError_t enqueue_compress(eblc_plan *plan, int nf, const float *const *in, voi
                             const size_t *out_capacity, eblc_result_t *results, hipStream_t st) {
     const PlanArgs pa = launch_args(plan, reinterpret_cast<const void *const *>(in), nf);
     const Workspace &ws = plan->ws;
+    plan->ev_sampled = plan->ev_calls[0]++ % plan->ev_every == plan->ev_every - 1;
     Fields fs{};
     fs.ws_stride = plan->ws_stride;
     for (int k = 0; k < nf; ++k) {
@@ -312,6 +316,7 @@ hipError_t enqueue_decompress(eblc_plan *plan, int nf, const void *const *in, co
                               float *const *out, hipStream_t st) {
     const PlanArgs pa = launch_args(plan, reinterpret_cast<const void *const *>(out), nf);
     const Workspace &ws = plan->ws;
+    plan->ev_sampled = plan->ev_calls[1]++ % plan->ev_every == plan->ev_every - 1;
     Fields fs{};
     fs.ws_stride = plan->ws_stride;
     for (int k = 0; k < nf; ++k) {
@@ -677,8 +682,8 @@ void eblc_plan_destroy(eblc_plan_t *plan) {
     delete plan;
 }
 
-eblc_status eblc_plan_set_profiling(eblc_plan_t *plan, int max_launches, const char *kernels) {
-    if (plan == nullptr || max_launches < 0 || (size_t)max_launches > kMaxTimedLaunches)
+eblc_status eblc_plan_set_profiling(eblc_plan_t *plan, int max_launches, const char *kernels, int every) {
+    if (plan == nullptr || max_launches < 0 || (size_t)max_launches > kMaxTimedLaunches || every < 1)
         return EBLC_INVALID_ARGUMENT;
     DeviceGuard guard(plan->device);
     if (!guard.ok) return EBLC_DEVICE_ERROR;
@@ -686,6 +691,8 @@ eblc_status eblc_plan_set_profiling(eblc_plan_t *plan, int max_launches, const c
     free_events(plan);
     plan->ev_filter.clear();
     if (kernels != nullptr && kernels[0] != '\0') plan->ev_filter = "," + std::string(kernels) + ",";
+    plan->ev_every = (uint32_t)every;
+    plan->ev_calls[0] = plan->ev_calls[1] = 0;
     if (max_launches == 0) return EBLC_OK;
     plan->ev_pool.assign(2 * (size_t)max_launches, nullptr);
     plan->ev_names.assign((size_t)max_launches, nullptr);

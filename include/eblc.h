@@ -222,18 +222,20 @@ void eblc_plan_destroy(eblc_plan_t *plan);
 const char *eblc_status_string(eblc_status s);
 
 /* ---- measurement hooks (not part of the provider shape) --------------------------------
- * eblc_plan_set_profiling(plan, k, kernels) with 0 < k <= 8192 waits for the device, then
- * records a HIP event pair around each of the plan's next k kernel launches, on the stream that
- * launch runs on; 0 turns recording off.  kernels is NULL or "" (every kernel), or a
- * comma-separated list of the names to time (range, encode, scan, compact, decode_sizes,
- * decode_scan, decode, patch): each event record costs the stream a few microseconds, so
- * timing only the kernels of interest keeps the rest of the call undisturbed.
+ * eblc_plan_set_profiling(plan, k, kernels, every) with 0 < k <= 8192 and every >= 1 waits for
+ * the device, then binds a HIP event pair to each of the plan's next k timed kernel launches
+ * (the kernel dispatch itself records them, on the stream the launch runs on); k = 0 turns
+ * recording off.  kernels is NULL or "" (every kernel), or a comma-separated list of the names
+ * to time (range, encode, scan, compact, decode_sizes, decode_scan, decode, patch); only the
+ * every-th, 2·every-th, ... compress and decompress launch sequences (counted apart; a batch
+ * call makes one per group of fields) are timed.  A timed dispatch still costs the stream a few
+ * microseconds, so naming few kernels and sampling keep the rest of the work undisturbed.
  * eblc_plan_kernel_times waits for the recorded events and writes, for each kernel name in
  * order of its first launch (at most max_kernels of them), the static name, the mean duration
  * in milliseconds and the number of launches recorded; then it clears the records (recording
  * goes on while k launches have not been recorded in all).  It returns how many kernel names
  * were recorded, or -1 when recording is off or on error. */
-eblc_status eblc_plan_set_profiling(eblc_plan_t *plan, int max_launches, const char *kernels);
+eblc_status eblc_plan_set_profiling(eblc_plan_t *plan, int max_launches, const char *kernels, int every);
 int eblc_plan_kernel_times(eblc_plan_t *plan, const char **names, float *ms, int *launches,
                            int max_kernels);
 

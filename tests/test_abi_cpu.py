@@ -36,7 +36,7 @@ def test_calls_without_gpu():
     assert lib.eblc_plan_limits(None, None) == binding.EBLC_INVALID_ARGUMENT
     assert lib.eblc_compress_batch(None, 0, None, None, None, None, None) == binding.EBLC_INVALID_ARGUMENT
     assert lib.eblc_decompress_batch(None, 0, None, None, None, None) == binding.EBLC_INVALID_ARGUMENT
-    assert lib.eblc_plan_set_profiling(None, 4, None) == binding.EBLC_INVALID_ARGUMENT
+    assert lib.eblc_plan_set_profiling(None, 4, None, 1) == binding.EBLC_INVALID_ARGUMENT
     assert lib.eblc_plan_kernel_times(None, None, None, None, 0) == -1
     lib.eblc_plan_destroy(None)
 

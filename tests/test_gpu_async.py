@@ -196,6 +196,14 @@ def test_kernel_time_records_cover_every_lane(env):
         assert binding.eblc_decompress_batch(plan, outs, ys) == binding.EBLC_OK
         rec = binding.eblc_plan_kernel_times(plan)
         assert [(r[0], r[2]) for r in rec] == [("encode", 2), ("decode", 2)]
+        # sampled: every second launch sequence of each kind (two batches of two groups each)
+        assert binding.eblc_plan_set_profiling(plan, 1000, "encode,decode", 2) == binding.EBLC_OK
+        for _ in range(2):
+            assert binding.eblc_compress_batch(plan, xs, outs, res) == binding.EBLC_OK
+            assert binding.eblc_decompress_batch(plan, outs, ys) == binding.EBLC_OK
+        rec = binding.eblc_plan_kernel_times(plan)
+        assert [(r[0], r[2]) for r in rec] == [("encode", 2), ("decode", 2)]
+        assert binding.eblc_plan_set_profiling(plan, 10, None, 0) == binding.EBLC_INVALID_ARGUMENT
         assert binding.eblc_plan_set_profiling(plan, 0) == binding.EBLC_OK
         with pytest.raises(RuntimeError):
             binding.eblc_plan_kernel_times(plan)
