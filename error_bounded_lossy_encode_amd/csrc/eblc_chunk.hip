@@ -307,7 +307,9 @@ __device__ __forceinline__ void chunk_encode_body(const float *__restrict__ x, P
                 ws.stage_idx[(uint64_t)c * kEscStage + lane] = s_stage[wave][0][lane];
                 ws.stage_val[(uint64_t)c * kEscStage + lane] = s_stage[wave][1][lane];
             }
-            if (es.tmask) ws.emask[(uint64_t)c * kEncSegs + lane] = es.emask;
+            /* the escape bitmasks are read by the compaction only for a chunk with more escapes
+             * than the staging holds */
+            if (es.tmask && es.escs > (uint32_t)kEscStage) ws.emask[(uint64_t)c * kEncSegs + lane] = es.emask;
             if (lane == 0) {
                 ws.chunk_words[c] = wsum;
                 ws.chunk_esc[c] = es.escs;

@@ -133,7 +133,8 @@ struct Workspace {
     uint32_t *group_esc;     /* [ngroups] */
     uint32_t *gpre_words;    /* [ngroups] exclusive prefix */
     uint32_t *gpre_esc;      /* [ngroups] exclusive prefix */
-    uint32_t *emask;         /* [nchunks * kEncSegs] escape bitmask per segment (tiles with escapes) */
+    uint32_t *emask;         /* [nchunks * kEncSegs] escape bitmask per segment (chunks with more
+                                than kEscStage escapes, tiles with escapes) */
     uint32_t *stage_idx;     /* [nchunks * kEscStage] first escapes of each chunk: index ... */
     uint32_t *stage_val;     /* [nchunks * kEscStage] ... and raw value bits, in index order */
     uint8_t *widths;         /* [nchunks * kEncSegs] size section staging when the output is too small */

@@ -562,8 +562,9 @@ constexpr uint64_t kSlotCacheBytes = 128ull << 20;
 
 /* One wave per encode chunk, kEncWaves chunks per workgroup.  Outputs per chunk: its packed
  * words in its scratch slot, its width bytes (into the stream, or into staging when the output
- * buffer cannot hold them), its word and escape counts and the escape bitmask of every tile
- * with an escape; per workgroup, the sums the device-wide scan runs over. */
+ * buffer cannot hold them), its word and escape counts and, for a chunk with more escapes than
+ * the staging holds, the escape bitmask of every tile with an escape; per workgroup, the sums
+ * the device-wide scan runs over. */
 template <bool STRIDED, int CM>
 __device__ __forceinline__ void encode_body(
     const float *__restrict__ x, PlanArgs pa, Workspace ws, uint8_t *__restrict__ widths_dst,
@@ -571,6 +572,7 @@ __device__ __forceinline__ void encode_body(
     __shared__ uint4 s_pay4[kEncWaves][kEncPayWords / 4];
     __shared__ uint4 s_wid4[kEncWaves][kEncSegs / 16];
     __shared__ uint32_t s_stage[kEncWaves][2][kEscStage];
+    __shared__ uint32_t s_emask[kEncWaves][kEncSegs];
     __shared__ uint32_t s_grp[2][kEncWaves];
 
     const uint32_t lane = threadIdx.x & 63;
@@ -608,7 +610,7 @@ __device__ __forceinline__ void encode_body(
             const int32_t qprev = quantize_slow(xp, rintf(xp * qp.r), qp, &e);
             carry = e ? 0 : qprev;
         }
-        uint32_t *emask_chunk = ws.emask + (uint64_t)c * kEncSegs;
+        uint32_t *emask_chunk = s_emask[wave];
         uint32_t *stage_idx = s_stage[wave][0];
         uint32_t *stage_val = s_stage[wave][1];
         if (cbase + kEncChunk <= pa.n)
@@ -628,6 +630,10 @@ __device__ __forceinline__ void encode_body(
             ws.stage_idx[(uint64_t)c * kEscStage + lane] = stage_idx[lane];
             ws.stage_val[(uint64_t)c * kEscStage + lane] = stage_val[lane];
         }
+        /* the escape bitmasks of the tiles with escapes, gathered in LDS: the compaction reads
+         * them only for a chunk with more escapes than the staging holds */
+        if (st.escs > (uint32_t)kEscStage && ((st.tmask >> (lane / kSegsPerEncTile)) & 1u))
+            ws.emask[(uint64_t)c * kEncSegs + lane] = emask_chunk[lane];
         if (lane == 0) {
             ws.chunk_words[c] = st.words;
             ws.chunk_esc[c] = st.escs;
