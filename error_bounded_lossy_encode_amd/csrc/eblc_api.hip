@@ -150,8 +150,10 @@ eblc_status parse_options(const char *opts, Options *o) {
                 o->rel = key == "rel";
                 o->eps = v;
             } else if (key == "block") {
+                /* a multiple of 32 ("Pipeline Specialization Internals", Forward declaration: the
+                 * block size must be a multiple of 32) up to 1024, or 2048 */
                 uint64_t b;
-                if (seen_block || !parse_u64(val, &b) || b < 32 || b > (uint64_t)kMaxBlock || (b & (b - 1)) != 0)
+                if (seen_block || !parse_u64(val, &b) || !((b >= 32 && b <= 1024 && b % 32 == 0) || b == 2048))
                     return EBLC_INVALID_ARGUMENT;
                 seen_block = true;
                 o->B = (uint32_t)b;
@@ -199,6 +201,14 @@ eblc_status parse_options(const char *opts, Options *o) {
         return EBLC_INVALID_ARGUMENT;
     }
     return EBLC_OK;
+}
+
+/* The largest payload, in 32-bit words, a field of n values can take: 32 words per 32-value
+ * segment for the bitpack coder; for the chunk coder (V values per chunk) the bitmap and every
+ * plane word of every chunk, the last one padded. */
+uint64_t max_payload_words(uint64_t n, uint32_t V) {
+    if (V == 0) return 32 * ((n + 31) / 32);
+    return ((n + V - 1) / V) * (uint64_t)(V + V / 32);
 }
 
 /* Absolute bound resolved on the host with the same fp64 -> fp32 round-toward-zero rule the
@@ -439,10 +449,13 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     if (st != EBLC_OK) return st;
     if (!o.side_set) o.side_max = n < (1ull << 23) ? n : (1ull << 23);
     if (o.side_max > n) return EBLC_INVALID_ARGUMENT;
+    /* the scans add payload words in 32-bit arithmetic: the largest payload a field can take
+     * must stay below 2^32 words */
+    if (max_payload_words(n, o.chunk_coder ? o.V : 0) >= (1ull << 32)) return EBLC_INVALID_ARGUMENT;
 
     int ndev = 0;
-    if (hipGetDeviceCount(&ndev) != hipSuccess || exec->device < 0 || exec->device >= ndev)
-        return EBLC_INVALID_ARGUMENT;
+    if (hipGetDeviceCount(&ndev) != hipSuccess) return EBLC_DEVICE_ERROR;
+    if (exec->device < 0 || exec->device >= ndev) return EBLC_INVALID_ARGUMENT;
     DeviceGuard guard(exec->device);
     if (!guard.ok) return EBLC_DEVICE_ERROR;
 
@@ -480,7 +493,8 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     }
     pa.dgroups = (pa.dchunks + kDecChunksPerGroup - 1) / kDecChunksPerGroup;
     pa.center = o.center ? 1u : 0u;
-    pa.log2B = (uint32_t)__builtin_ctz(pa.B);
+    pa.log2B = 0; /* ceil(log2 B) */
+    while ((1u << pa.log2B) < pa.B) ++pa.log2B;
     pa.nblocks = (n + pa.B - 1) / pa.B;
     pa.msec = o.center ? align_up(4 * pa.nblocks, 16) : 0;
     pa.side_max = o.side_max;

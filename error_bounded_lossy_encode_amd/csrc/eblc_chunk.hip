@@ -402,8 +402,9 @@ __device__ __forceinline__ void decode_tiles(const F &fetch, uint32_t t0, uint32
  * per lane (value 64 t + lane), the four tiles' codes go through a 1 KB LDS scratch so that lane
  * l holds values 4 l .. 4 l + 3 of the 256, and then one in-lane running sum, one wave scan of
  * the lane totals and the carry undo the first difference for all four tiles, and one 128-bit
- * store writes the lane's four values.  The scratch belongs to the wave; LDS accesses of one
- * wave are performed in order, so the next group's writes cannot pass this group's read. */
+ * store writes the lane's four values.  The scratch belongs to the wave: a wave-level release /
+ * acquire after the stores and again after the read orders every lane's accesses, so the next
+ * group's stores cannot pass this group's read (by the compiler or by the LDS). */
 template <int V, int NQ, bool STRIDED, typename F>
 __device__ __forceinline__ void decode_quads(const F &fetch, uint32_t t0, uint32_t wmax, const Transpose &tr,
                                              float s, uint32_t &carry, float *__restrict__ out, const Layout &lo,
@@ -420,6 +421,7 @@ __device__ __forceinline__ void decode_quads(const F &fetch, uint32_t t0, uint32
         }
         wave_lds_sync();
         const uint4 v = reinterpret_cast<const uint4 *>(sx)[lane];
+        wave_lds_sync();
         const uint32_t r1 = v.x + v.y, r2 = r1 + v.z, r3 = r2 + v.w;
         const uint32_t incl = wave_incl_scan(r3);
         const uint32_t base = carry + incl - r3;

@@ -11,11 +11,12 @@
  *               group = 4 chunks = one 256-thread workgroup
  * Both groups hold 8192 values; the device-wide scans run over groups.  The chunk coder keeps
  * the encode chunks and groups (its coder chunks of V values fill whole encode chunks, or two)
- * and decodes one coder chunk per wave, four per group.  The Lorenzo block B is
- * a power of two in [32, 2048].  A decode chunk always starts a block; an encode chunk that
- * does not (B larger than the chunk) takes its first prediction from the code of the value
- * before it.  The only other cross-wave dependency is the exclusive scan of payload sizes and
- * outlier counts.
+ * and decodes one coder chunk per wave, four per group.  The Lorenzo block B is a multiple
+ * of 32 up to 1024, or 2048.  A power of two starts every chunk; any other block may start
+ * inside a chunk at a 32-value boundary and cross chunk ends.  An encode chunk that does not
+ * start a block takes its first prediction from the code of the value before it; a decode chunk
+ * that does not sums the deltas of the block's segments before it.  The only other cross-wave
+ * dependency is the exclusive scan of payload sizes and outlier counts.
  */
 #ifndef EBLC_INTERNAL_H
 #define EBLC_INTERNAL_H
@@ -42,7 +43,6 @@ constexpr int kEncPayWords = kEncChunk / 2 + 4;  /* LDS pack buffer per wave: ha
 constexpr int kDecTiles = 8;
 constexpr int kDecChunk = kTile * kDecTiles;     /* 2048 values */
 constexpr int kDecSegs = kDecChunk / 32;         /* 64 segments */
-constexpr int kMaxBlock = kDecChunk;             /* largest Lorenzo block */
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
 constexpr int kDecChunksPerGroup = kWavesPerBlock;
@@ -103,7 +103,8 @@ struct PlanArgs {
     uint64_t nseg;
     uint64_t dims[4];
     uint32_t rank;
-    uint32_t B;             /* Lorenzo block, power of two 32..2048 (the chunk, for the chunk coder) */
+    uint32_t B;             /* Lorenzo block: a multiple of 32 up to 1024, or 2048 (the chunk, for the
+                               chunk coder) */
     uint32_t T;             /* outlier log2 */
     uint32_t V;             /* chunk coder: values per chunk (1024, 2048, 4096); 0: bitpack coder */
     uint32_t log2seg;       /* header field: 5 (32-value segments), or log2 V */
@@ -111,7 +112,7 @@ struct PlanArgs {
     uint32_t wpg;           /* bytes of the size section per encode group */
     uint64_t wsec;          /* bytes of the size section: align16(nseg), or align16(4 chunks) */
     uint32_t center;        /* Lorenzo centering: each block's first code predicted by its mean */
-    uint32_t log2B;         /* log2 of B */
+    uint32_t log2B;         /* ceil(log2 B) */
     uint64_t nblocks;       /* ceil(n / B) */
     uint64_t msec;          /* bytes of the means section on compress: align16(4 nblocks), or 0 */
     uint32_t nchunks;       /* encode chunks */

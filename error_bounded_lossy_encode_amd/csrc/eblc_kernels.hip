@@ -335,20 +335,21 @@ __device__ __forceinline__ uint32_t seg_allsum(uint32_t v, uint32_t seglen) {
 }
 
 /* Lorenzo centering: the mean of a block's c codes rounded half up, floor((2 S + c) / (2 c)),
- * from S = hi * 2^16 + lo; a shift when the block is whole (c = 2^log2B).  block_mean32 is the
- * same for |S| < 2^29 (codes below 2^T with T + log2 B <= 29), in 32-bit arithmetic. */
-__device__ __forceinline__ int32_t block_mean32(int32_t S, uint32_t c, uint32_t log2B) {
+ * from S = hi * 2^16 + lo; an arithmetic shift when c is a power of two (a whole block of a
+ * power-of-two B).  block_mean32 is the same for |S| < 2^29 (codes below 2^T with
+ * T + log2 B <= 29), in 32-bit arithmetic. */
+__device__ __forceinline__ int32_t block_mean32(int32_t S, uint32_t c) {
     const int32_t num = 2 * S + (int32_t)c;
-    if (c == (1u << log2B)) return num >> (log2B + 1);
+    if ((c & (c - 1u)) == 0) return num >> (__builtin_ctz(c) + 1);
     const int32_t den = 2 * (int32_t)c;
     int32_t qd = num / den;
     if ((num % den) != 0 && num < 0) qd -= 1;
     return qd;
 }
 
-__device__ __forceinline__ int32_t block_mean(uint32_t lo, int32_t hi, uint64_t c, uint32_t log2B) {
+__device__ __forceinline__ int32_t block_mean(uint32_t lo, int32_t hi, uint64_t c) {
     const int64_t num = 2 * ((int64_t)hi * 65536 + (int64_t)lo) + (int64_t)c;
-    if (c == (1ull << log2B)) return (int32_t)(num >> (log2B + 1));
+    if ((c & (c - 1u)) == 0) return (int32_t)(num >> (__builtin_ctzll(c) + 1));
     const int64_t den = 2 * (int64_t)c;
     int64_t qd = num / den;
     if ((num % den) != 0 && num < 0) qd -= 1;
@@ -356,21 +357,41 @@ __device__ __forceinline__ int32_t block_mean(uint32_t lo, int32_t hi, uint64_t 
 }
 
 /* Centering modes of the encoder: none; blocks of at most one tile whose code sums fit 32 bits
- * (B <= 256 and T + log2 B <= 29, the defaults among them); any block.  The first keeps neither
- * the per-tile totals nor the 64-bit mean of the last, and so fewer registers. */
-constexpr int kCenterOff = 0, kCenterTile = 1, kCenterAny = 2;
+ * (B <= 256 and T + log2 B <= 29, the defaults among them); any power-of-two block; any block
+ * that is not a power of two.  The first keeps neither the per-tile totals nor the 64-bit mean
+ * of the last two, and so fewer registers. */
+constexpr int kCenterOff = 0, kCenterTile = 1, kCenterAny = 2, kCenterGen = 3;
+
+/* Where the Lorenzo blocks lie relative to an encode chunk (wave-uniform).  For a block B that
+ * is not a power of two, r0 is the chunk start's offset in its block, bk0 the block holding the
+ * chunk's first value, and mB = floor(2^32 / B) + 1, so that a / B is the high word of a mB for
+ * the small a (below 2^13) the chunk's offsets take. */
+struct BlockPos {
+    uint32_t B, log2B, r0, bk0, mB;
+};
+
+/* The code a value gets from the encoder: the fast test, else the full rule; 0 if it escapes. */
+__device__ __forceinline__ int32_t code_of(float xv, const QParams &qp) {
+    const float q0f = rintf(xv * qp.r);
+    if ((fabsf(xv - q0f * qp.s) <= qp.eb) && (fabsf(q0f) < qp.tlim)) return (int32_t)q0f;
+    uint32_t e;
+    const int32_t q = quantize_slow(xv, q0f, qp, &e);
+    return e ? 0 : q;
+}
 
 /* One encode chunk of kEncTiles tiles.  Pass 1 codes every tile and records the segment widths
  * in LDS (the codes stay in VGPRs); one wave scan of the widths gives every segment's word
  * offset in the chunk; pass 2 packs each tile at those offsets.  `carry` is the code of the
- * value before the chunk when the chunk does not start a Lorenzo block. */
-template <bool FULL, bool STRIDED, int CM>
+ * value before the chunk when the chunk does not start a Lorenzo block.  GB: the block is not a
+ * power of two, so a lane starts a block when (r0 + 256 t + 4 lane) mod B is 0. */
+template <bool FULL, bool STRIDED, int CM, bool GB>
 __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const Layout &lo, uint64_t cbase, uint64_t n,
-                                             const QParams &qp, uint32_t bmask, int32_t carry,
+                                             const QParams &qp, const BlockPos &bp, int32_t carry,
                                              uint32_t *pay, uint8_t *wid, uint32_t *emask_chunk,
                                              uint32_t *stage_idx, uint32_t *stage_val, EncState &st,
-                                             uint32_t log2B, int32_t *__restrict__ means, bool narrow,
+                                             int32_t *__restrict__ means, bool narrow,
                                              uint32_t *__restrict__ slot, bool slot_nt) {
+    const uint32_t bmask = bp.B - 1, log2B = bp.log2B;
     constexpr int V = kEncLaneVals;
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t j = lane & (kSegLanes - 1), g = lane / kSegLanes;
@@ -393,7 +414,8 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
         }
     }
     const uint32_t ntiles = FULL ? kEncTiles : (uint32_t)((n - cbase + kEncTile - 1) / kEncTile);
-    /* a lane's first value starts a block when its offset in the tile does and the tile does */
+    /* a lane's first value starts a block when its offset in the tile does and the tile does
+     * (a power-of-two block) */
     const bool lane_at_block = ((V * lane) & bmask) == 0;
     uint32_t z[kEncTiles][V];
     uint32_t w[kEncTiles];
@@ -442,19 +464,29 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
     }
     /* Lorenzo centering: a block's first code was coded against 0 (z = zigzag(q)); it is
      * recoded against the block's mean code, which goes to the means staging, and the segment
-     * widths follow.  Blocks lie inside the chunk (B <= 2048).  A block of at most one tile is
-     * finished with its tile; a longer one keeps its tiles' wave-uniform code sums until the
-     * tile loop ends. */
-    const uint32_t B = bmask + 1;
+     * widths follow.  A power-of-two block lies inside the chunk (B <= 2048): one of at most one
+     * tile is finished with its tile; a longer one keeps its tiles' wave-uniform code sums until
+     * the tile loop ends.  Any other block (kCenterGen) may cross the chunk's ends: the tile loop
+     * keeps a chunk-wide prefix of the lanes' code sums in the pack buffer (unused until pass 2),
+     * and the blocks are finished after it. */
+    const uint32_t B = bp.B;
     const bool in_tile = B <= (uint32_t)kEncTile;
     uint32_t tlo[kEncTiles];
     int32_t thi[kEncTiles];
+    uint32_t run_lo = 0, run_hi = 0;
+    uint32_t *pre_lo = pay, *pre_hi = pay + kEncTiles * kWave;
 #pragma unroll
     for (int t = 0; t < kEncTiles; ++t) {
         tlo[t] = 0;
         thi[t] = 0;
         if (FULL || (uint32_t)t < ntiles) {
-            const bool reset = lane_at_block && (((uint32_t)cbase + (uint32_t)t * kEncTile) & bmask) == 0;
+            bool reset;
+            if (GB) {
+                const uint32_t a = bp.r0 + (uint32_t)t * kEncTile + V * lane;
+                reset = a == __umulhi(a, bp.mB) * B;
+            } else {
+                reset = lane_at_block && (((uint32_t)cbase + (uint32_t)t * kEncTile) & bmask) == 0;
+            }
             uint32_t slo;
             int32_t shi;
             w[t] = finish_tile<FULL>(q[t], cbase + (uint64_t)t * kEncTile + V * lane, n, reset, carry, z[t],
@@ -473,8 +505,8 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
                 const uint64_t e0 = cbase + (uint64_t)t * kEncTile + V * lane;
                 if (lane_at_block && e0 < n) {
                     const uint64_t c = (n - e0 < (uint64_t)B) ? n - e0 : (uint64_t)B;
-                    const int32_t mu = narrow_sums ? block_mean32((int32_t)lo_s, (uint32_t)c, log2B)
-                                                   : block_mean(lo_s, (int32_t)hi_s, c, log2B);
+                    const int32_t mu = narrow_sums ? block_mean32((int32_t)lo_s, (uint32_t)c)
+                                                   : block_mean(lo_s, (int32_t)hi_s, c);
                     z[t][0] = zigzag((int32_t)((uint32_t)unzigzag(z[t][0]) - (uint32_t)mu));
                     means[e0 >> log2B] = mu;
                 }
@@ -482,6 +514,15 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
             } else if (CM == kCenterAny) {
                 tlo[t] = seg_allsum(slo, 64);
                 thi[t] = (int32_t)seg_allsum((uint32_t)shi, 64);
+            } else if (CM == kCenterGen) {
+                /* inclusive prefix over the chunk's lanes (wrapping u32 sums: every block's
+                 * difference of two prefixes is far inside the 32-bit range) */
+                const uint32_t il = wave_incl_scan(slo) + run_lo;
+                const uint32_t ih = wave_incl_scan((uint32_t)shi) + run_hi;
+                pre_lo[t * kWave + lane] = il;
+                pre_hi[t * kWave + lane] = ih;
+                run_lo = readlane(il, 63);
+                run_hi = readlane(ih, 63);
             }
             if (j == 0) wid[t * kSegsPerEncTile + g] = (uint8_t)w[t];
         }
@@ -503,10 +544,64 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
                     }
                 }
                 const uint64_t c = (n - bstart < (uint64_t)B) ? n - bstart : (uint64_t)B;
-                const int32_t mu = block_mean(lo_s, hi_s, c, log2B);
+                const int32_t mu = block_mean(lo_s, hi_s, c);
                 if (lane == 0) {
                     z[t][0] = zigzag((int32_t)((uint32_t)unzigzag(z[t][0]) - (uint32_t)mu));
                     means[bstart >> log2B] = mu;
+                }
+                w[t] = seg_width(z[t]);
+                if (j == 0) wid[t * kSegsPerEncTile + g] = (uint8_t)w[t];
+            }
+        }
+    }
+    if (CM == kCenterGen) {
+        wave_lds_sync();
+        /* The last block starting in the chunk may run on past it: its codes there are coded
+         * again here, by the same rule (an escape counts 0), to complete its sum.  Block starts
+         * lie on 32-value boundaries, so a lane's four values are all inside the block or all
+         * outside it; only n can cut them. */
+        uint32_t look_lo = 0, look_hi = 0;
+        const uint32_t f0 = bp.r0 == 0 ? 0u : B - bp.r0; /* first block start in the chunk */
+        if (f0 < (uint32_t)kEncChunk) {
+            const uint32_t last = f0 + B * __umulhi((uint32_t)kEncChunk - 1u - f0, bp.mB);
+            const uint64_t bend = cbase + last + B;
+            const uint64_t end = bend < n ? bend : n;
+            if (end > cbase + kEncChunk) {
+                for (uint64_t i = cbase + kEncChunk + V * lane; i < end; i += kEncTile) {
+#pragma unroll
+                    for (int k = 0; k < V; ++k) {
+                        if (i + k < end) {
+                            const int32_t qv = code_of(x[elem_off<STRIDED>(lo, i + k)], qp);
+                            look_lo += (uint32_t)qv & 0xFFFFu;
+                            look_hi += (uint32_t)(qv >> 16);
+                        }
+                    }
+                }
+                look_lo = readlane(wave_incl_scan(look_lo), 63);
+                look_hi = readlane(wave_incl_scan(look_hi), 63);
+            }
+        }
+        const uint32_t last_slot = ntiles * kWave - 1u;
+#pragma unroll
+        for (int t = 0; t < kEncTiles; ++t) {
+            if (FULL || (uint32_t)t < ntiles) {
+                const uint32_t a = bp.r0 + (uint32_t)t * kEncTile + V * lane;
+                const uint32_t qd = __umulhi(a, bp.mB);
+                const uint64_t e0 = cbase + (uint64_t)t * kEncTile + V * lane;
+                if (a == qd * B && e0 < n) {
+                    const uint32_t u0 = (uint32_t)t * kWave + lane;
+                    const uint32_t ue = u0 + B / V - 1u;
+                    const uint32_t uc = ue < last_slot ? ue : last_slot;
+                    uint32_t lo_s = pre_lo[uc] - (u0 ? pre_lo[u0 - 1] : 0u);
+                    uint32_t hi_s = pre_hi[uc] - (u0 ? pre_hi[u0 - 1] : 0u);
+                    if (ue > last_slot) {
+                        lo_s += look_lo;
+                        hi_s += look_hi;
+                    }
+                    const uint64_t c = (n - e0 < (uint64_t)B) ? n - e0 : (uint64_t)B;
+                    const int32_t mu = block_mean(lo_s, (int32_t)hi_s, c);
+                    z[t][0] = zigzag((int32_t)((uint32_t)unzigzag(z[t][0]) - (uint32_t)mu));
+                    means[bp.bk0 + qd] = mu;
                 }
                 w[t] = seg_width(z[t]);
                 if (j == 0) wid[t * kSegsPerEncTile + g] = (uint8_t)w[t];
@@ -565,7 +660,7 @@ constexpr uint64_t kSlotCacheBytes = 128ull << 20;
  * buffer cannot hold them), its word and escape counts and, for a chunk with more escapes than
  * the staging holds, the escape bitmask of every tile with an escape; per workgroup, the sums
  * the device-wide scan runs over. */
-template <bool STRIDED, int CM>
+template <bool STRIDED, int CM, bool GB>
 __device__ __forceinline__ void encode_body(
     const float *__restrict__ x, PlanArgs pa, Workspace ws, uint8_t *__restrict__ widths_dst,
     uint64_t widths_bytes, uint32_t grp) {
@@ -598,29 +693,35 @@ __device__ __forceinline__ void encode_body(
         if (lane < kEncSegs / 16) s_wid4[wave][lane] = make_uint4(0, 0, 0, 0);
         wave_lds_sync();
         const uint64_t cbase = (uint64_t)c * kEncChunk;
-        const uint32_t bmask = pa.B - 1;
+        BlockPos bp;
+        bp.B = pa.B;
+        bp.log2B = pa.log2B;
+        bp.r0 = 0;
+        bp.bk0 = 0;
+        bp.mB = 0;
+        if (GB) {
+            bp.bk0 = (uint32_t)cbase / pa.B;
+            bp.r0 = (uint32_t)cbase - bp.bk0 * pa.B;
+            bp.mB = 0xFFFFFFFFu / pa.B + 1u;
+        }
+        const bool at_block = GB ? bp.r0 == 0 : ((uint32_t)cbase & (pa.B - 1)) == 0;
         /* centering: a block's code sum fits 32 bits (|S| < 2^29) when codes stay below 2^T */
         const bool narrow = pa.T + pa.log2B <= 29;
         /* Lorenzo predecessor of the chunk's first value: 0 at a block start, else the code of
          * the value before the chunk (0 if that value escapes) */
         int32_t carry = 0;
-        if (((uint32_t)cbase & bmask) != 0) {
-            const float xp = x[elem_off<STRIDED>(pa.lay, cbase - 1)];
-            uint32_t e;
-            const int32_t qprev = quantize_slow(xp, rintf(xp * qp.r), qp, &e);
-            carry = e ? 0 : qprev;
-        }
+        if (!at_block) carry = code_of(x[elem_off<STRIDED>(pa.lay, cbase - 1)], qp);
         uint32_t *emask_chunk = s_emask[wave];
         uint32_t *stage_idx = s_stage[wave][0];
         uint32_t *stage_val = s_stage[wave][1];
         if (cbase + kEncChunk <= pa.n)
-            encode_chunk<true, STRIDED, CM>(x, pa.lay, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk,
-                                                stage_idx, stage_val, st, pa.log2B, ws.means, narrow,
-                                                ws.scratch + cbase, slot_nt);
+            encode_chunk<true, STRIDED, CM, GB>(x, pa.lay, cbase, pa.n, qp, bp, carry, pay, wid, emask_chunk,
+                                                stage_idx, stage_val, st, ws.means, narrow, ws.scratch + cbase,
+                                                slot_nt);
         else
-            encode_chunk<false, STRIDED, CM>(x, pa.lay, cbase, pa.n, qp, bmask, carry, pay, wid, emask_chunk,
-                                                 stage_idx, stage_val, st, pa.log2B, ws.means, narrow,
-                                                 ws.scratch + cbase, slot_nt);
+            encode_chunk<false, STRIDED, CM, GB>(x, pa.lay, cbase, pa.n, qp, bp, carry, pay, wid, emask_chunk,
+                                                 stage_idx, stage_val, st, ws.means, narrow, ws.scratch + cbase,
+                                                 slot_nt);
         /* widths -> stream (or staging) */
         if (lane < kEncSegs / 16) {
             const uint64_t off = (uint64_t)c * kEncSegs + 16u * lane;
@@ -660,12 +761,12 @@ __device__ __forceinline__ void encode_body(
 /* The encoder walks a field's groups from the last to the first: the range pass has just read
  * them first to last, so the workgroups dispatched first find the tail of the input in the
  * last-level cache. */
-template <bool STRIDED, int CM>
+template <bool STRIDED, int CM, bool GB>
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(Fields fs, PlanArgs pa, Workspace ws) {
     const uint32_t f = blockIdx.y;
     const Workspace w = lane_ws(ws, f, fs.ws_stride);
     uint8_t *wd = (fs.wdirect >> f) & 1u ? pick(fs.dst, f) + kHeaderBytes : w.widths;
-    encode_body<STRIDED, CM>(reinterpret_cast<const float *>(pick(fs.src, f)), pa, w, wd, pa.wsec,
+    encode_body<STRIDED, CM, GB>(reinterpret_cast<const float *>(pick(fs.src, f)), pa, w, wd, pa.wsec,
                              pa.ngroups - 1 - blockIdx.x);
 }
 
@@ -1024,13 +1125,14 @@ __device__ __forceinline__ void compact_body(const float *__restrict__ x,
             *reinterpret_cast<uint32_t *>(out + kHeaderBytes + off) = *reinterpret_cast<const uint32_t *>(widths_src + off);
     }
     if (pa.center) {
-        /* the group's block means, staged by the encoder, into the means section */
-        const uint32_t mpg = (uint32_t)(CPG * kEncChunk) >> pa.log2B;
+        /* the means of the blocks that start in the group, staged by the encoder, into the
+         * means section */
+        const uint64_t gend = gbase + (uint64_t)CPG * kEncChunk;
+        const uint64_t b0 = (gbase + pa.B - 1) / pa.B;
+        const uint64_t b1e = (gend + pa.B - 1) / pa.B;
+        const uint64_t b1 = b1e < pa.nblocks ? b1e : pa.nblocks;
         int32_t *mdst = reinterpret_cast<int32_t *>(out + kHeaderBytes + pa.wsec);
-        for (uint32_t k = tid; k < mpg; k += kBlockThreads) {
-            const uint64_t b = (uint64_t)grp * mpg + k;
-            if (b < pa.nblocks) mdst[b] = ws.means[b];
-        }
+        for (uint64_t b = b0 + tid; b < b1; b += kBlockThreads) mdst[b] = ws.means[b];
         if (last && tid < (pa.msec - 4 * pa.nblocks) / 4) mdst[pa.nblocks + tid] = 0;
     }
     if (last) {
@@ -1162,7 +1264,7 @@ __device__ __forceinline__ void scan_decompress_body(const uint8_t *__restrict__
     bool ok = hw[0] == kMagic && (hw[1] & 0xffff) == kVersion && (hw[1] >> 16) == kHeaderBytes;
     ok = ok && rank == pa.rank && T >= 1 && T <= 30;
     /* a plan decodes coded streams of its own coder (and chunk size), and every RAW stream */
-    const bool bitpack_params = log2seg == 5 && B >= 32 && B <= 2048 && (B & (B - 1)) == 0;
+    const bool bitpack_params = log2seg == 5 && ((B >= 32 && B <= 1024 && B % 32 == 0) || B == 2048);
     const bool chunk_params = log2seg >= 10 && log2seg <= 12 && B == (1u << log2seg);
     if (mode == 1) ok = ok && (bitpack_params || chunk_params);
     else if (pa.V == 0) ok = ok && mode == 0 && bitpack_params;
@@ -1207,13 +1309,20 @@ __global__ __launch_bounds__(kScanThreads) void scan_decompress_kernel(Fields fs
 
 /* The tile loop of one decode chunk whose packed words and segment widths are staged in LDS:
  * per tile unpack each lane's 4 values, undo the zigzag, prefix-sum inside each block (in-lane,
- * then a segmented DPP scan across lanes, plus the carry from the previous tile when a block
- * spans tiles; CENTERED: plus the block's mean code mu[t] at its start), dequantize with
- * f32(f32(q) * s) and store 4 values with one 128-bit store. */
-template <bool STRIDED, bool CENTERED>
+ * then across lanes, plus the carry from the previous tile when a block spans tiles; CENTERED:
+ * plus the block's mean code mu[t] at its start), dequantize with f32(f32(q) * s) and store 4
+ * values with one 128-bit store.
+ *   A power-of-two block (GB = false) starts a decode chunk, and its blocks are aligned groups
+ * of lanes: a segmented DPP scan.  Any other block (a multiple of 32, GB = true) may start at
+ * any 8-lane boundary: a lane's offset in its block is (r0 + 256 t + 4 lane) mod B, with r0 the
+ * chunk start's offset in its block; the lane's prefix is the plain wave scan minus the scan at
+ * its block's first lane (ds_bpermute), or plus the carry when its block began before the tile;
+ * carry starts at carry0, the code before the chunk when the chunk starts inside a block. */
+template <bool STRIDED, bool CENTERED, bool GB>
 __device__ __forceinline__ void decode_tiles(const PlanArgs &pa, const DevInfo *info, const int32_t mu[kDecTiles],
                                              const uint32_t *pay, const uint32_t *s_w, const uint32_t *s_so,
-                                             uint32_t lb, uint64_t cbase, bool full, float *__restrict__ out) {
+                                             uint32_t lb, uint64_t cbase, bool full, float *__restrict__ out,
+                                             int32_t carry0, uint32_t r0, uint32_t mB) {
     const uint32_t lane = threadIdx.x & 63;
     const uint64_t n = pa.n;
     const float s = info->dec_s;
@@ -1222,7 +1331,7 @@ __device__ __forceinline__ void decode_tiles(const PlanArgs &pa, const DevInfo *
     const uint32_t dist = lane & (seglen - 1);
     const uint32_t ntiles = full ? kDecTiles : (uint32_t)((n - cbase + kTile - 1) / kTile);
     const uint32_t j = lane & 7;
-    int32_t carry = 0;
+    int32_t carry = GB ? carry0 : 0;
 #pragma unroll
     for (int t = 0; t < kDecTiles; ++t) {
         if ((uint32_t)t < ntiles) {
@@ -1241,10 +1350,23 @@ __device__ __forceinline__ void decode_tiles(const PlanArgs &pa, const DevInfo *
                 run += unzigzag(z);
                 cs[k] = run;
             }
-            const uint32_t incl = wave_seg_scan((uint32_t)cs[3], dist, seglen);
-            const bool open = (((uint32_t)t * kTile) & (B - 1)) != 0;
-            int32_t base = (int32_t)(incl - (uint32_t)cs[3]) + (open ? carry : 0);
-            if (CENTERED) base += mu[t];
+            int32_t base;
+            if (GB) {
+                const uint32_t a = r0 + (uint32_t)t * kTile + 4u * lane;
+                const uint32_t rem = a - __umulhi(a, mB) * B; /* offset of the lane's first value in its block */
+                const uint32_t incl = wave_incl_scan((uint32_t)cs[3]);
+                const uint32_t excl = incl - (uint32_t)cs[3];
+                const bool opened = rem / 4u > lane;       /* the block began before this tile */
+                const uint32_t bsl = opened ? 0u : lane - rem / 4u;
+                const uint32_t e_bs = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(4u * bsl), (int)excl);
+                base = opened ? (int32_t)(excl + (uint32_t)carry) : (int32_t)(excl - e_bs);
+                if (CENTERED && !opened) base += mu[t];
+            } else {
+                const uint32_t incl = wave_seg_scan((uint32_t)cs[3], dist, seglen);
+                const bool open = (((uint32_t)t * kTile) & (B - 1)) != 0;
+                base = (int32_t)(incl - (uint32_t)cs[3]) + (open ? carry : 0);
+                if (CENTERED) base += mu[t];
+            }
             int32_t q[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) q[k] = base + cs[k];
@@ -1267,8 +1389,45 @@ __device__ __forceinline__ void decode_tiles(const PlanArgs &pa, const DevInfo *
     }
 }
 
+/* The code before a decode chunk that starts inside a block of a non-power-of-two B: the sum of
+ * the deltas of the block's r0 / 32 segments before the chunk (at most 31, the last segments of
+ * the previous chunk; r0 < B <= 1024), read from the stream just before the chunk's words.  Eight
+ * lanes take a segment, four values each, eight segments per round; a value's two words are
+ * read only when its bits span them, so no read leaves those segments' words. */
+__device__ __forceinline__ int32_t open_block_sum(const uint8_t *__restrict__ in, uint64_t seg_end, uint32_t nseg,
+                                                  const uint32_t *__restrict__ words_end) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t wpre = lane < nseg ? (uint32_t)in[kHeaderBytes + seg_end - nseg + lane] : 0u;
+    const uint32_t incl = wave_incl_scan(wpre);
+    const uint32_t total = readlane(incl, 63);
+    const uint32_t so = incl - wpre;
+    const uint32_t *pw = words_end - total;
+    const uint32_t j = lane & 7;
+    int32_t sum = 0;
+    for (uint32_t g0 = 0; g0 < nseg; g0 += 8) {
+        const uint32_t g = g0 + (lane >> 3);
+        const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(4u * (g & 63u)), (int)wpre);
+        const uint32_t o = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(4u * (g & 63u)), (int)so);
+        if (g < nseg && w != 0) {
+            const uint32_t mask = w >= 32 ? 0xffffffffu : ((1u << w) - 1u);
+            const uint32_t bp = 32u * o + 4u * w * j;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t pos = bp + (uint32_t)k * w;
+                const uint32_t wi = pos >> 5, sh = pos & 31u;
+                const uint32_t lo = pw[wi];
+                const uint32_t hi = sh + w > 32u ? pw[wi + 1] : 0u;
+                const uint64_t pair = (uint64_t)lo | ((uint64_t)hi << 32);
+                sum += unzigzag((uint32_t)(pair >> sh) & mask);
+            }
+        }
+    }
+    return (int32_t)readlane(wave_incl_scan((uint32_t)sum), 63);
+}
+
 /* One wave per chunk: stage the chunk's packed words in LDS (128-bit loads) and its segment
- * widths and word offsets, then decode_tiles (the centered copy for a centered stream). */
+ * widths and word offsets, then decode_tiles (the centered copy for a centered stream, the
+ * general-block copy for a block that is not a power of two). */
 template <bool STRIDED>
 __device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in,
                                             PlanArgs pa, Workspace ws,
@@ -1315,21 +1474,35 @@ __device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in,
     const uint4 *src = reinterpret_cast<const uint4 *>(in) + a0 / 4;
     const uint64_t seg = (uint64_t)c * kDecSegs + lane;
     const uint32_t wl = seg < pa.nseg ? (uint32_t)in[kHeaderBytes + seg] : 0u;
-    /* a centered stream's blocks start from their mean code: in each tile that starts blocks,
-     * every lane takes its block's mean, loaded with the chunk's other loads (lanes past n read
-     * nothing: their blocks' means may lie past the stream's end) */
+    /* the stream's block; for one that is not a power of two, the chunk start's offset in its
+     * block (r0), the block holding the chunk's first value (bk0) and the reciprocal of B for
+     * the small divisions of decode_tiles */
+    const uint32_t B = info->dec_B;
+    const bool gb = (B & (B - 1)) != 0;
+    uint32_t r0 = 0, bk0 = 0, mB = 0;
+    if (gb) {
+        mB = 0xFFFFFFFFu / B + 1u;
+        bk0 = (uint32_t)cbase / B;
+        r0 = (uint32_t)cbase - bk0 * B;
+    }
+    /* a centered stream's blocks start from their mean code: in each tile, every lane whose block
+     * starts in the tile takes its block's mean, loaded with the chunk's other loads (lanes past n
+     * read nothing: their blocks' means may lie past the stream's end) */
     const bool centered = (info->dec_flags & 1u) != 0;
+    const int32_t *means = reinterpret_cast<const int32_t *>(in + kHeaderBytes + pa.wsec);
     int32_t mu[kDecTiles];
-    {
-        const uint32_t B = info->dec_B;
-        const uint32_t log2B = (uint32_t)__builtin_ctz(B);
-        const int32_t *means = reinterpret_cast<const int32_t *>(in + kHeaderBytes + pa.wsec);
 #pragma unroll
-        for (int t = 0; t < kDecTiles; ++t) {
-            const uint64_t ev = cbase + (uint64_t)t * kTile + 4 * lane;
-            const bool starts = (((uint32_t)t * kTile) & (B - 1)) == 0;
-            mu[t] = 0;
-            if (centered && starts && ev < n) mu[t] = means[ev >> log2B];
+    for (int t = 0; t < kDecTiles; ++t) {
+        const uint64_t ev = cbase + (uint64_t)t * kTile + 4 * lane;
+        mu[t] = 0;
+        if (centered && ev < n) {
+            if (gb) {
+                const uint32_t a = r0 + (uint32_t)t * kTile + 4u * lane;
+                const uint32_t q = __umulhi(a, mB);
+                if ((a - q * B) / 4u <= lane) mu[t] = means[bk0 + q];
+            } else if ((((uint32_t)t * kTile) & (B - 1)) == 0) {
+                mu[t] = means[ev >> (uint32_t)__builtin_ctz(B)];
+            }
         }
     }
     /* every staging load of the chunk is issued before the first LDS store, so the chunk
@@ -1354,11 +1527,25 @@ __device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in,
     wave_lds_sync();
 
     const uint32_t *pay = reinterpret_cast<const uint32_t *>(s_pay4[wave]);
-    /* a centered stream takes its own copy of the tile loop, so the plain one stays as it is */
-    if (centered)
-        decode_tiles<STRIDED, true>(pa, info, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out);
-    else
-        decode_tiles<STRIDED, false>(pa, info, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out);
+    if (gb) {
+        int32_t carry0 = 0;
+        if (r0 != 0) {
+            carry0 = open_block_sum(in, (uint64_t)c * kDecSegs, r0 / 32u,
+                                    reinterpret_cast<const uint32_t *>(in) + sw);
+            if (centered) carry0 += means[bk0];
+        }
+        if (centered)
+            decode_tiles<STRIDED, true, true>(pa, info, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out, carry0,
+                                              r0, mB);
+        else
+            decode_tiles<STRIDED, false, true>(pa, info, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out, carry0,
+                                               r0, mB);
+    } else if (centered) {
+        /* a centered stream takes its own copy of the tile loop, so the plain one stays as it is */
+        decode_tiles<STRIDED, true, false>(pa, info, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out, 0, 0, 0);
+    } else {
+        decode_tiles<STRIDED, false, false>(pa, info, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out, 0, 0, 0);
+    }
 }
 
 template <bool STRIDED>
@@ -1415,24 +1602,26 @@ hipError_t launch_range(const Fields &fs, uint32_t nf, const PlanArgs &pa, const
 
 hipError_t launch_encode(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                          hipStream_t stream) {
+    const bool gb = (pa.B & (pa.B - 1)) != 0;
     const int cm = !pa.center ? kCenterOff
+                   : gb ? kCenterGen
                    : (pa.B <= (uint32_t)kEncTile && pa.T + pa.log2B <= 29) ? kCenterTile : kCenterAny;
     const dim3 grid(pa.ngroups, nf), block(kEncThreads);
+#define EBLC_ENCODE(S, C, G) eblc_launch((encode_kernel<S, C, G>), grid, block, 0, stream, fs, pa, ws)
     if (pa.lay.strided) {
-        if (cm == kCenterTile)
-            eblc_launch((encode_kernel<true, kCenterTile>), grid, block, 0, stream, fs, pa, ws);
-        else if (cm == kCenterAny)
-            eblc_launch((encode_kernel<true, kCenterAny>), grid, block, 0, stream, fs, pa, ws);
-        else
-            eblc_launch((encode_kernel<true, kCenterOff>), grid, block, 0, stream, fs, pa, ws);
+        if (cm == kCenterTile) EBLC_ENCODE(true, kCenterTile, false);
+        else if (cm == kCenterAny) EBLC_ENCODE(true, kCenterAny, false);
+        else if (cm == kCenterGen) EBLC_ENCODE(true, kCenterGen, true);
+        else if (gb) EBLC_ENCODE(true, kCenterOff, true);
+        else EBLC_ENCODE(true, kCenterOff, false);
     } else {
-        if (cm == kCenterTile)
-            eblc_launch((encode_kernel<false, kCenterTile>), grid, block, 0, stream, fs, pa, ws);
-        else if (cm == kCenterAny)
-            eblc_launch((encode_kernel<false, kCenterAny>), grid, block, 0, stream, fs, pa, ws);
-        else
-            eblc_launch((encode_kernel<false, kCenterOff>), grid, block, 0, stream, fs, pa, ws);
+        if (cm == kCenterTile) EBLC_ENCODE(false, kCenterTile, false);
+        else if (cm == kCenterAny) EBLC_ENCODE(false, kCenterAny, false);
+        else if (cm == kCenterGen) EBLC_ENCODE(false, kCenterGen, true);
+        else if (gb) EBLC_ENCODE(false, kCenterOff, true);
+        else EBLC_ENCODE(false, kCenterOff, false);
     }
+#undef EBLC_ENCODE
     return hipGetLastError();
 }
 

@@ -163,3 +163,42 @@ def tiny_array(rng: np.random.Generator, n: int, kind: str) -> np.ndarray:
     else:
         raise ValueError(kind)
     return x.astype(np.float32)
+
+
+def adversarial(rng: np.random.Generator, n: int, eb: float, s: float, T: int) -> np.ndarray:
+    """n float32 values placed where a quantizer with bound eb and step s = 2 eb must decide
+    carefully: on cell boundaries (k + 1/2) s, on grid points k s, at +-eb itself and within a
+    millionth of it (codes +-1 next to the bound), around the code limit 2^T (k = 2^T - 1, 2^T
+    and the boundary between them), small normal values, and special values (NaN, +-Inf, -0,
+    subnormals, values whose rounded code passes 2^30); each then nudged by 0, 1 or 2 ulps up
+    or down.  Codes stay mostly below min(2^T, 2^14) so that the field is coded rather than copied raw.
+    eb and s are taken as given (the caller resolves them); nothing here quantizes."""
+    f32 = np.float32
+    kmax = float(1 << min(T, 14))
+    # |k| log-uniform in [1, kmax), random sign
+    k = np.floor(np.exp(rng.uniform(0.0, np.log(kmax), n))) * rng.choice([-1.0, 1.0], n)
+    kind = rng.choice(8, n, p=[0.22, 0.18, 0.16, 0.16, 0.12, 0.06, 0.05, 0.05])
+    sgn = rng.choice([-1.0, 1.0], n)
+    v = np.zeros(n, np.float64)
+    v[kind == 0] = ((k + 0.5) * s)[kind == 0]
+    v[kind == 1] = (sgn * eb * (1.0 + rng.uniform(-1e-6, 1e-6, n)))[kind == 1]
+    v[kind == 2] = (k * s)[kind == 2]
+    v[kind == 3] = (rng.normal(0.0, 10.0, n) * s)[kind == 3]
+    v[kind == 4] = (sgn * eb)[kind == 4]
+    lim = float(1 << T)
+    edge = rng.choice([lim - 1.0, lim - 0.5, lim, lim + 0.5], n)
+    v[kind == 5] = (sgn * edge * s)[kind == 5]
+    v[kind == 6] = (k * s + rng.uniform(-1.0, 1.0, n) * eb)[kind == 6]
+    x = v.astype(f32)
+    sp = kind == 7
+    x[sp] = rng.choice(SPECIALS, int(sp.sum()))
+    # ulp nudges (FLT_MAX may step to infinity)
+    steps = rng.integers(-2, 3, n)
+    with np.errstate(over="ignore"):
+        for _ in range(2):
+            up = steps > 0
+            dn = steps < 0
+            x[up] = np.nextafter(x[up], f32(np.inf))
+            x[dn] = np.nextafter(x[dn], f32(-np.inf))
+            steps = steps - np.sign(steps)
+    return x.astype(f32)

@@ -123,8 +123,11 @@ int eblc_abi_version(void);
  *            a bare decimal -> relative error (what DevitoPRO passes, "Provider layout");
  *            else ';'-separated key=value pairs:
  *              rel=<eps> | abs=<eb>   exactly one; finite, >= 0; 0 means lossless (RAW)
- *              block=<B>              Lorenzo reset period: 32, 64, ..., 2048 (power of two);
- *                                     default 256
+ *              block=<B>              Lorenzo reset period: a multiple of 32 from 32 to 1024, or
+ *                                     2048 ("Pipeline Specialization Internals", Forward
+ *                                     declaration: the block size is a multiple of 32); a
+ *                                     block that is not a power of two may start anywhere on a
+ *                                     32-value boundary; default 256
  *              outlier_log2=<T>       codes with |q| >= 2^T escape; 1..30; default 30
  *              side_max=<m>           largest outlier list; 0..n; default min(n, 2^23)
  *              coder=bitpack|chunk    bitpack (default) or the chunk coder
@@ -140,19 +143,28 @@ int eblc_abi_version(void);
  *            Unknown keys, repeated keys, NaN or negative values -> INVALID_ARGUMENT.
  *   plan_out receives the plan.  The plan allocates its whole workspace here (about 4 n +
  *            n/8 bytes plus small arrays) and nothing per call.
+ * INVALID_ARGUMENT also when the field's largest payload would reach 2^32 words (the scans
+ * count in 32 bits): 32 words per 32-value segment for the bitpack coder, so n <= 2^32 - 32;
+ * for the chunk coder ceil(n / V) (V + V / 32) < 2^32.  DEVICE_ERROR when no HIP device can be
+ * queried.
  * The relative error is eps * (max - min) over the finite input values, resolved on the
  * device at every compress call ("Priming": the quantizer's value-range scan). */
 eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int rank,
                              const int64_t *dims, const int64_t *strides, const char *options,
                              eblc_plan_t **plan_out);
 
-/* Fill *out with the plan's limits.  INVALID_ARGUMENT on NULL. */
+/* Fill *out with the plan's limits ("DevitoComp provider interface", Provider layout: the
+ * provider reports its limits, among them the payload alignment, in a limits record; Dummy
+ * provider: a maximum compressed size, there the raw size).  INVALID_ARGUMENT on NULL. */
 eblc_status eblc_plan_limits(const eblc_plan_t *plan, eblc_limits_t *out);
 
-/* 128 + align16(4 n); 0 for a NULL plan. */
+/* The largest stream a compress of this plan writes: 128 + align16(4 n), a RAW stream ("DevitoComp
+ * provider interface", Dummy provider: the provider reports a maximum compressed size, the raw
+ * size for a copy).  0 for a NULL plan. */
 size_t eblc_max_compressed_bytes(const eblc_plan_t *plan);
 
-/* 16; 0 for a NULL plan. */
+/* The alignment the stream's start needs: 16 ("DevitoComp provider interface", Provider layout:
+ * the required compressed-payload alignment, a nonzero power of two).  0 for a NULL plan. */
 size_t eblc_payload_alignment(const eblc_plan_t *plan);
 
 /* Compress n floats at device pointer `in` into device buffer `out` of out_capacity bytes,
@@ -212,13 +224,21 @@ eblc_status eblc_decompress(eblc_plan_t *plan, const void *in, size_t compressed
 eblc_status eblc_decompress_batch(eblc_plan_t *plan, int count, const void *const *in,
                                   const size_t *compressed_bytes, float *const *out, void *stream);
 
-/* Wait for `stream`, then return and clear the plan's sticky device error (OK if none). */
+/* Wait for `stream`, then return and clear the plan's sticky device error (OK if none).  Device
+ * work may stay queued when a call returns ("DevitoComp provider interface", Provider layout), so
+ * problems only the device finds (a corrupt stream) are reported by this later call.
+ * INVALID_ARGUMENT on NULL; DEVICE_ERROR when the wait or the read of the record fails. */
 eblc_status eblc_plan_status(eblc_plan_t *plan, void *stream);
 
-/* Wait for the device, then free the plan and its workspace.  NULL is a no-op. */
+/* Wait for the device, then free the plan and its workspace.  Like the pool buffers of the
+ * "Architecture" page (FZGPUModules site, buffer ownership: valid until the pipeline is
+ * destroyed), the workspace lives until this call; streams already written stay the caller's.
+ * NULL is a no-op. */
 void eblc_plan_destroy(eblc_plan_t *plan);
 
-/* Static string naming a status. */
+/* Static string naming a status: the eblc_status codes above, UNSUPPORTED among them for the
+ * execution kinds and layouts this provider does not take ("DevitoComp provider interface",
+ * Provider layout); "unknown status" for any other value. */
 const char *eblc_status_string(eblc_status s);
 
 /* ---- measurement hooks (not part of the provider shape) --------------------------------

@@ -114,3 +114,30 @@ def gpu_roundtrip(binding, torch, x_np: np.ndarray, dims, opts: str, canary: int
         return host[:nbytes].copy(), yh[:n].copy()
     finally:
         binding.eblc_plan_destroy(plan)
+
+
+def oracle_threads() -> int:
+    """Threads for the sharded oracle: the host's cores, at most 16 (a GPU machine's CPU share)."""
+    import os
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_reference(oracle, shards, x: np.ndarray, dims, opts: str, threads: int | None = None):
+    """The oracle's stream and reconstruction for a full-size field, coded as block-aligned
+    pieces on several threads and joined (the join reproduces the whole-field stream byte for
+    byte; it is pinned against the one-thread oracle in test_oracle_shards.py).  A stream that
+    falls back to a raw copy is made by the one-thread oracle instead."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    n = int(np.prod(dims))
+    o = parse_options(opts, n)
+    threads = threads or oracle_threads()
+    ok, _, bounds, streams = shards.code_pieces(x, o["rel"], o["eps"], o["B"], o["T"], o["center"], o["V"],
+                                                threads, threads)
+    if ok:
+        joined = shards.join(x, dims, o["T"], o["B"], o["side_max"], o["center"], o["V"], bounds, streams)
+        if joined is not None and int(joined[8]) != 1:
+            return joined, shards.decode_pieces(streams, threads)
+    ref = oracle_stream(oracle, x, dims, opts)
+    st, y = oracle.decompress(ref)
+    assert st == oracle.OK
+    return ref, y

@@ -48,6 +48,7 @@ def test_unsupported_execution_kinds(kind):
 
 
 @pytest.mark.parametrize("opts", ["rel=-1", "abs=nan", "rel=1e-3;abs=1", "block=48", "block=4096",
+                                  "block=0", "block=16", "block=1056", "block=1536", "block=2016",
                                   "outlier_log2=0", "outlier_log2=31", "bogus=1", "rel", "side_max=-3",
                                   "block=256;block=128", "side_max=5000", "coder=huffman",
                                   "coder=chunk;block=256", "chunk_bytes=8192", "coder=chunk;chunk_bytes=2048",
@@ -70,3 +71,40 @@ def test_shape_checks():
                           ([4, 4, 4], [16, -4, 1]), ([4, 4, 4], [8, 4, 1])):
         assert binding.eblc_plan_create(dims, strides=strides)[0] == binding.EBLC_UNSUPPORTED, strides
     assert binding.eblc_plan_create([8, 8], dtype=3)[0] == binding.EBLC_UNSUPPORTED
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.parametrize("block", [32, 96, 160, 480, 992, 1024, 2048])
+def test_block_grammar_accepts_multiples_of_32(block):
+    """Every multiple of 32 up to 1024, and 2048, passes the option checks: without a GPU the
+    plan then stops at the device query."""
+    if _gpu_visible():
+        pytest.skip("checks the option parser on a host without a GPU")
+    st, plan = binding.eblc_plan_create([4096], f"rel=1e-3;block={block}")
+    assert st == binding.EBLC_DEVICE_ERROR and plan is None
+
+
+def test_payload_word_limit():
+    """The scans count payload words in 32 bits, so a plan is refused when its field's largest
+    payload reaches 2^32 words: 32 words per 32-value segment for the bitpack coder (n above
+    2^32 - 32), the bitmap and every plane word of every chunk for the chunk coder."""
+    if _gpu_visible():
+        pytest.skip("checks the plan limits on a host without a GPU")
+    lim_bitpack = (1 << 32) - 32
+    assert binding.eblc_plan_create([lim_bitpack + 1], "rel=1e-3")[0] == binding.EBLC_INVALID_ARGUMENT
+    assert binding.eblc_plan_create([lim_bitpack], "rel=1e-3")[0] == binding.EBLC_DEVICE_ERROR
+    for chunk_bytes in (4096, 8192, 16384):
+        V = chunk_bytes // 4
+        chunks = ((1 << 32) - 1) // (V + V // 32)     # the most chunks below the limit
+        opts = f"rel=1e-3;coder=chunk;chunk_bytes={chunk_bytes}"
+        n_ok = min(chunks * V, (1 << 32) - 1)
+        assert binding.eblc_plan_create([n_ok], opts)[0] == binding.EBLC_DEVICE_ERROR, chunk_bytes
+        if n_ok < (1 << 32) - 1:
+            assert binding.eblc_plan_create([n_ok + 1], opts)[0] == binding.EBLC_INVALID_ARGUMENT, chunk_bytes

@@ -48,6 +48,8 @@ VARIANTS = [
     ("center=1;rel=1e-3;block=64;outlier_log2=15", [7 * 2048 + 1234]),
     ("center=1;abs=1e-3;block=2048;outlier_log2=30", [24, 1000]),
     ("rel=1e-3;block=128;outlier_log2=15", [6 * 8192 + 3]),
+    ("center=1;rel=1e-3;block=480;outlier_log2=15", [5 * 8192 + 1111]),
+    ("abs=1e-3;block=96;outlier_log2=30", [3, 9000]),
 ]
 
 

@@ -15,7 +15,7 @@ from helpers import first_difference, gpu_roundtrip, header, oracle_stream
 
 pytestmark = pytest.mark.gpu
 
-BLOCKS = [32, 64, 128, 256, 512, 1024, 2048]
+BLOCKS = [32, 64, 96, 128, 160, 256, 480, 512, 992, 1024, 2048]
 
 
 @pytest.fixture(scope="module")

@@ -4,15 +4,15 @@ Every stream is compared with the oracle's byte for byte (header, widths, payloa
 outlier list, pads) and the GPU reconstruction with the oracle's decoder bit for bit.  The
 oracle is single-threaded C++, so these cases take seconds each; the fields are the
 benchmark's: 4096^2 Gaussian random field, 512^3 Ricker snapshot, 2^28 AR(1) with 2.7 M
-spikes escaping to the side list, and nine 256^3 snapshots of the 64-snapshot batch at both
-bounds through the batch calls with eight fields per launch.
+spikes escaping to the side list.  The 64-snapshot batch, the chunk coder and centering at full
+size are in test_gpu_full_coders.py.
 """
 import numpy as np
 import pytest
 
 import oracle
 from error_bounded_lossy_encode_amd import synth
-from helpers import CANARY, first_difference, gpu_roundtrip, header, parse_options
+from helpers import first_difference, gpu_roundtrip, header, parse_options
 
 pytestmark = pytest.mark.gpu
 
@@ -63,52 +63,3 @@ def test_ar1_spikes_2pow28(env):
     h = check_full(env, x, dims, opts, "2^28 AR(1) + spikes")
     # about 1 % of the values are spikes, all of which must escape to the side list
     assert h["mode"] == 0 and 2_600_000 < h["m"] <= 1 << 23
-
-
-@pytest.mark.parametrize("rel", [1e-6, 1e-2])
-def test_batch_snapshots_256cubed(env, rel):
-    """Nine snapshots of the batch through one plan with lanes=8, compressed and decompressed
-    with the batch calls as the benchmark runs them: one launch per stage codes eight fields,
-    a second one the ninth.  Whole streams of the first and last field of the full group and of
-    the lone field against the oracle's, bit-identical reconstructions, and every field within
-    its bound."""
-    binding, torch = env
-    ids = list(range(8)) + [63]
-    fields = [synth.c5_snapshot(i, 256, rel, device="cuda") for i in ids]
-    dims, opts = fields[0][1], fields[0][2]
-    n = int(np.prod(dims))
-    print(f"[full-size] batch of {len(ids)} 256^3 snapshots rel {rel}, lanes=8", flush=True)
-    st, plan = binding.eblc_plan_create(dims, opts + ";lanes=8", 0)
-    assert st == binding.EBLC_OK
-    try:
-        maxb = binding.eblc_max_compressed_bytes(plan)
-        xs = [f[0].reshape(-1).contiguous() for f in fields]
-        outs = [torch.full((maxb,), CANARY, dtype=torch.uint8, device="cuda") for _ in ids]
-        ys = [torch.full((n,), float("nan"), dtype=torch.float32, device="cuda") for _ in ids]
-        res = torch.zeros(16 * len(ids), dtype=torch.uint8, device="cuda")
-        assert binding.eblc_compress_batch(plan, xs, outs, res) == binding.EBLC_OK
-        assert binding.eblc_decompress_batch(plan, outs, ys) == binding.EBLC_OK
-        assert binding.eblc_plan_status(plan) == binding.EBLC_OK
-        recs = binding.result_records(res)
-        o = parse_options(opts, n)
-        for k, i in enumerate(ids):
-            nb, status = recs[k]
-            assert status == binding.EBLC_OK
-            got = outs[k].cpu().numpy()
-            assert (got[nb:] == CANARY).all(), f"snapshot {i}: write past the stream"
-            h = header(got)
-            assert h["mode"] == 0 and h["total"] == nb
-            eb = float(np.frombuffer(got[56:60].tobytes(), np.float32)[0])
-            err = float((ys[k] - xs[k]).abs().max())
-            assert err <= eb, f"snapshot {i}: max |x - x'| {err} above eb {eb}"
-            if k in (0, 7, 8):
-                x = xs[k].cpu().numpy()
-                ref = oracle.compress(x, dims, o["rel"], o["eps"], o["B"], o["T"], o["side_max"])
-                assert nb == ref.size and np.array_equal(got[:nb], ref), \
-                    f"snapshot {i}: {first_difference(got[:nb], ref)}"
-                st, ref_dec = oracle.decompress(ref)
-                assert st == oracle.OK
-                assert np.array_equal(ys[k].cpu().numpy().view(np.uint32), ref_dec.view(np.uint32)), \
-                    f"snapshot {i}: reconstruction differs"
-    finally:
-        binding.eblc_plan_destroy(plan)

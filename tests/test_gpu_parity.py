@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 from error_bounded_lossy_encode_amd import synth
-from helpers import first_difference, gpu_roundtrip, header, parse_options
+from helpers import first_difference, gpu_roundtrip, header, oracle_stream, parse_options
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def test_tiny_fuzz(env, seed):
         n = int(rng.integers(1, 301))
         kind = kinds[(seed + case) % len(kinds)]
         x = synth.tiny_array(rng, n, kind)
-        B = int(rng.choice([32, 64, 128, 256, 512, 1024, 2048]))
+        B = int(rng.choice([32, 64, 96, 128, 160, 256, 480, 512, 992, 1024, 2048]))
         T = int(rng.choice([1, 2, 15, 30]))
         side = int(rng.choice([0, 1, n]))
         if rng.integers(0, 2):
@@ -102,3 +102,65 @@ def test_small_configs(env):
     for rel in (1e-6, 1e-2):
         x, dims, opts = synth.c5_snapshot(0, 48, rel)
         check_case(env, x.numpy(), dims, opts, f"C5 48^3 rel={rel}")
+
+
+GENERAL_BLOCKS = [96, 160, 480, 992]
+
+
+def check_any(env, x, dims, opts, label=""):
+    """check_case for any options string (centering included)."""
+    binding, torch = env
+    ref = oracle_stream(oracle, x, dims, opts)
+    st, ref_dec = oracle.decompress(ref)
+    assert st == oracle.OK
+    got, dec = gpu_roundtrip(binding, torch, x, dims, opts)
+    assert got.size == ref.size and np.array_equal(got, ref), f"{label} {opts}: {first_difference(got, ref)}"
+    bad = np.nonzero(dec.view(np.uint32) != ref_dec.view(np.uint32))[0]
+    assert bad.size == 0, f"{label} {opts}: reconstruction differs at {bad[:5]}"
+    return header(ref)
+
+
+@pytest.mark.parametrize("B", GENERAL_BLOCKS)
+def test_general_blocks_ragged(env, B):
+    """Blocks that are multiples of 32 but not powers of two ("Pipeline Specialization
+    Internals", Forward declaration: the block is a multiple of 32): blocks then start inside
+    encode and decode chunks and cross their ends.  Ragged lengths over several workgroups,
+    both bound modes, escapes, and centering, whose means may need codes of the next chunk."""
+    rng = np.random.default_rng(900 + B)
+    for n in [B - 27, B + 1, 2049, 3 * 2048 + 777, 4 * 4 * 2048 + 5, (1 << 17) + 1234]:
+        for kind in ["smooth", "specials"]:
+            x = synth.tiny_array(rng, n, kind)
+            check_any(env, x, [n], f"rel=1e-3;block={B};outlier_log2=15", f"{kind} n={n}")
+            x = (x + np.float32(25.0)).astype(np.float32)
+            check_any(env, x, [n], f"rel=1e-4;block={B};outlier_log2=30;center=1", f"centered {kind} n={n}")
+        x = synth.tiny_array(rng, n, "normal")
+        check_any(env, x, [n], f"abs=0.01;block={B};outlier_log2=30", f"normal n={n}")
+        x = synth.tiny_array(rng, n, "smooth")
+        x[5::29] = np.float32(1e9)                # more than 64 escapes per chunk
+        check_any(env, x, [n], f"abs=0.01;block={B};outlier_log2=30;center=1", f"escapes n={n}")
+
+
+def test_general_blocks_decode_across_plans(env):
+    """A stream decodes with the block recorded in it, whichever block the decoding plan has:
+    streams of blocks that are not powers of two through a plan of block 256, and the reverse."""
+    binding, torch = env
+    rng = np.random.default_rng(31)
+    n = 3 * 8192 + 517
+    x = (synth.tiny_array(rng, n, "smooth") + np.float32(9.0)).astype(np.float32)
+    cases = [("rel=1e-3;block=96;outlier_log2=15", "rel=1e-3;block=256"),
+             ("rel=1e-3;block=480;center=1", "rel=1e-3;block=256"),
+             ("rel=1e-3;block=256;center=1", "rel=1e-3;block=160"),
+             ("rel=1e-3;block=2048", "rel=1e-3;block=992;center=1")]
+    for enc_opts, dec_opts in cases:
+        ref = oracle_stream(oracle, x, [n], enc_opts)
+        _, ref_dec = oracle.decompress(ref)
+        st, plan = binding.eblc_plan_create([n], dec_opts, 0)
+        assert st == binding.EBLC_OK
+        try:
+            stream = torch.from_numpy(ref).cuda()
+            y = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+            assert binding.eblc_decompress(plan, stream, ref.size, y) == binding.EBLC_OK
+            assert binding.eblc_plan_status(plan) == binding.EBLC_OK, (enc_opts, dec_opts)
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), ref_dec.view(np.uint32)), (enc_opts, dec_opts)
+        finally:
+            binding.eblc_plan_destroy(plan)

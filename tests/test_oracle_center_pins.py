@@ -14,7 +14,7 @@ from error_bounded_lossy_encode_amd import synth
 from test_oracle_pins import hdr
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-BLOCKS = [32, 64, 128, 256, 512, 1024, 2048]
+BLOCKS = [32, 64, 96, 128, 160, 256, 480, 512, 992, 1024, 2048]
 
 
 def read_codes(s):

@@ -1,7 +1,7 @@
 """Pins of the CPU oracle against facts that do not come from the oracle itself.
 
 Each test checks one step of the method (closed forms, brute force on tiny inputs, exact
-rational arithmetic, invariants, and two hand-derived streams under tests/golden/), chosen
+rational arithmetic, invariants, and three hand-derived streams under tests/golden/), chosen
 so that a plausible slip in the oracle -- a dropped term, a wrong sign or index, a transposed
 operand, an off-by-one width, a different bit order -- fails at least one of them.
 """
@@ -48,7 +48,7 @@ def parse_opts(inp):
 # Hand-derived streams
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["w1_ramp40.json", "w2_escapes64.json"])
+@pytest.mark.parametrize("name", ["w1_ramp40.json", "w2_escapes64.json", "w5_ramp200_block96.json"])
 def test_golden_stream(name):
     g = json.load(open(os.path.join(GOLDEN, name)))
     inp, exp = g["input"], g["expect"]
@@ -332,7 +332,7 @@ def test_bound_resolution():
 # Lorenzo with block reset
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("B", [32, 64, 128, 256, 2048])
+@pytest.mark.parametrize("B", [32, 64, 96, 128, 160, 256, 480, 992, 2048])
 def test_lorenzo_block_reset(B):
     rng = np.random.default_rng(B)
     n = 3 * B + 45
@@ -402,7 +402,7 @@ def test_roundtrip_tiny(seed):
         n = int(rng.integers(1, 301))
         kind = kinds[(seed + case) % len(kinds)]
         x = synth.tiny_array(rng, n, kind)
-        B = int(rng.choice([32, 64, 128, 256, 2048]))
+        B = int(rng.choice([32, 64, 96, 128, 160, 256, 480, 992, 2048]))
         T = int(rng.choice([1, 2, 15, 30]))
         rel = bool(rng.integers(0, 2))
         eps = float(rng.choice([0.0, 1e-7, 1e-3, 0.3])) if rel else float(rng.choice([0.0, 1e-6, 1e-2, 5.0]))

@@ -23,7 +23,7 @@ def _field(seed: int, n: int, kind: str = "smooth", nan: int = 0, big: int = 0):
     return x
 
 
-@pytest.mark.parametrize("B", [32, 64, 256, 2048])
+@pytest.mark.parametrize("B", [32, 64, 96, 256, 480, 2048])
 @pytest.mark.parametrize("pieces", [1, 2, 5, 7])
 def test_bitpack_pieces_join_to_the_whole_stream(B, pieces):
     n = 23 * 2048 + 77
@@ -39,7 +39,7 @@ def test_bitpack_pieces_join_to_the_whole_stream(B, pieces):
     assert np.array_equal(shards.decode_pieces(streams, 3).view(np.uint32), y.view(np.uint32))
 
 
-@pytest.mark.parametrize("B", [64, 256, 1024])
+@pytest.mark.parametrize("B", [64, 160, 256, 992, 1024])
 def test_centered_pieces_join_to_the_whole_stream(B):
     n = 17 * 1024 + 301
     x = _field(7 * B, n, nan=9) + np.float32(40.0)
