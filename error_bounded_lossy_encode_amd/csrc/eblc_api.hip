@@ -19,6 +19,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <string_view>
 #include <vector>
 
 using namespace eblc;
@@ -74,30 +75,37 @@ struct DeviceGuard {
     }
 };
 
-bool parse_double(const std::string &s, double *out) {
-    if (s.empty()) return false;
-    const char *b = s.c_str();
+/* The option parser works on views of the caller's string and copies a value into a stack
+ * buffer only to convert it, so parsing allocates nothing. */
+constexpr size_t kMaxValueChars = 63;
+
+bool parse_double(std::string_view s, double *out) {
+    if (s.empty() || s.size() > kMaxValueChars) return false;
+    char buf[kMaxValueChars + 1];
+    std::memcpy(buf, s.data(), s.size());
+    buf[s.size()] = '\0';
     char *e = nullptr;
     errno = 0;
-    const double v = std::strtod(b, &e);
-    if (e == b || *e != '\0' || errno == ERANGE) return false;
+    const double v = std::strtod(buf, &e);
+    if (e == buf || *e != '\0' || errno == ERANGE) return false;
     *out = v;
     return true;
 }
 
-bool parse_u64(const std::string &s, uint64_t *out) {
-    if (s.empty()) return false;
-    for (char ch : s)
+bool parse_u64(std::string_view s, uint64_t *out) {
+    if (s.empty() || s.size() > 20) return false;
+    uint64_t v = 0;
+    for (char ch : s) {
         if (ch < '0' || ch > '9') return false;
-    errno = 0;
-    char *e = nullptr;
-    const unsigned long long v = std::strtoull(s.c_str(), &e, 10);
-    if (errno == ERANGE || *e != '\0') return false;
+        const uint64_t d = (uint64_t)(ch - '0');
+        if (v > (UINT64_MAX - d) / 10) return false;
+        v = v * 10 + d;
+    }
     *out = v;
     return true;
 }
 
-std::string trim(const std::string &s) {
+std::string_view trim(std::string_view s) {
     size_t a = 0, b = s.size();
     while (a < b && (s[a] == ' ' || s[a] == '\t')) ++a;
     while (b > a && (s[b - 1] == ' ' || s[b - 1] == '\t')) --b;
@@ -121,7 +129,7 @@ struct Options {
  * error as a decimal, or NULL for the provider default). */
 eblc_status parse_options(const char *opts, Options *o) {
     if (opts == nullptr) return EBLC_OK;
-    const std::string all = trim(opts);
+    const std::string_view all = trim(std::string_view(opts));
     if (all.empty()) return EBLC_OK;
     double v;
     if (parse_double(all, &v)) {
@@ -136,14 +144,14 @@ eblc_status parse_options(const char *opts, Options *o) {
     size_t pos = 0;
     for (;;) {
         size_t end = all.find(';', pos);
-        const bool final_item = end == std::string::npos;
+        const bool final_item = end == std::string_view::npos;
         if (final_item) end = all.size();
-        const std::string item = trim(all.substr(pos, end - pos));
+        const std::string_view item = trim(all.substr(pos, end - pos));
         pos = end + 1;
         if (!item.empty()) {
             const size_t eq = item.find('=');
-            if (eq == std::string::npos) return EBLC_INVALID_ARGUMENT;
-            const std::string key = trim(item.substr(0, eq)), val = trim(item.substr(eq + 1));
+            if (eq == std::string_view::npos) return EBLC_INVALID_ARGUMENT;
+            const std::string_view key = trim(item.substr(0, eq)), val = trim(item.substr(eq + 1));
             if (key == "rel" || key == "abs") {
                 if (seen_eb || !parse_double(val, &v) || !std::isfinite(v) || v < 0) return EBLC_INVALID_ARGUMENT;
                 seen_eb = true;
