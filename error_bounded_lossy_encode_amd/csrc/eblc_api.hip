@@ -415,6 +415,108 @@ eblc_status make_layout(int rank, const int64_t *dims, const int64_t *strides, L
     return EBLC_OK;
 }
 
+/* Plan constants from the shape, strides and options, with every check that needs no device:
+ * rank 1..4, dims > 0 with n < 2^32, the layout, the options, side_max <= n and the 32-bit limit
+ * on payload words. */
+eblc_status setup_args(int rank, const int64_t *dims, const int64_t *strides, const char *options, Options *o,
+                       PlanArgs *out) {
+    if (rank < 1 || rank > 4) return EBLC_UNSUPPORTED;
+    uint64_t n = 1;
+    for (int a = 0; a < rank; ++a) {
+        if (dims[a] <= 0) return EBLC_INVALID_ARGUMENT;
+        if ((uint64_t)dims[a] >= (1ull << 32)) return EBLC_INVALID_ARGUMENT;
+        n *= (uint64_t)dims[a];
+        if (n >= (1ull << 32)) return EBLC_INVALID_ARGUMENT;
+    }
+    Layout lay{};
+    eblc_status ls = make_layout(rank, dims, strides, &lay);
+    if (ls != EBLC_OK) return ls;
+    eblc_status st = parse_options(options, o);
+    if (st != EBLC_OK) return st;
+    if (!o->side_set) o->side_max = n < (1ull << 23) ? n : (1ull << 23);
+    if (o->side_max > n) return EBLC_INVALID_ARGUMENT;
+    /* the scans add payload words in 32-bit arithmetic: the largest payload a field can take
+     * must stay below 2^32 words */
+    if (max_payload_words(n, o->chunk_coder ? o->V : 0) >= (1ull << 32)) return EBLC_INVALID_ARGUMENT;
+    PlanArgs &pa = *out;
+    pa = PlanArgs{};
+    pa.n = n;
+    pa.nseg = (n + 31) / 32;
+    for (int a = 0; a < 4; ++a) pa.dims[a] = a < rank ? (uint64_t)dims[a] : 0;
+    pa.rank = (uint32_t)rank;
+    pa.B = o->B;
+    pa.T = o->T;
+    pa.nchunks = (uint32_t)((n + kEncChunk - 1) / kEncChunk);
+    pa.ngroups = (pa.nchunks + kEncChunksPerGroup - 1) / kEncChunksPerGroup;
+    if (o->chunk_coder) {
+        pa.V = o->V;
+        pa.log2seg = (uint32_t)__builtin_ctz(o->V);
+        pa.slot = kEncChunk + kEncChunk / 32;
+        pa.wpg = 4u * (kEncChunksPerGroup * kEncChunk / o->V);
+        pa.dchunks = (uint32_t)((n + o->V - 1) / o->V);
+        pa.wsec = align_up(4ull * pa.dchunks, 16);
+    } else {
+        pa.V = 0;
+        pa.log2seg = 5;
+        pa.slot = kEncChunk;
+        pa.wpg = kEncChunksPerGroup * kEncSegs;
+        pa.dchunks = (uint32_t)((n + kDecChunk - 1) / kDecChunk);
+        pa.wsec = align_up(pa.nseg, 16);
+    }
+    pa.dgroups = (pa.dchunks + kDecChunksPerGroup - 1) / kDecChunksPerGroup;
+    pa.center = o->center ? 1u : 0u;
+    pa.log2B = 0; /* ceil(log2 B) */
+    while ((1u << pa.log2B) < pa.B) ++pa.log2B;
+    pa.nblocks = (n + pa.B - 1) / pa.B;
+    pa.msec = o->center ? align_up(4 * pa.nblocks, 16) : 0;
+    pa.side_max = o->side_max;
+    pa.lay = lay;
+    return EBLC_OK;
+}
+
+/* Bytes of one lane's workspace, its arrays 256-byte aligned; with base non-null also the
+ * arrays' addresses from base on. */
+uint64_t carve_workspace(const PlanArgs &pa, uint8_t *base, Workspace *ws) {
+    const uint64_t nc = pa.nchunks > pa.dchunks ? pa.nchunks : pa.dchunks;
+    const uint64_t ng = pa.ngroups > pa.dgroups ? pa.ngroups : pa.dgroups;
+    uint64_t off = 0;
+    auto carve = [&](uint64_t bytes) {
+        const uint64_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    const uint64_t o_info = carve(sizeof(DevInfo));
+    /* one spare slot: a 4096-value chunk of the chunk coder spills into its second wave's slot */
+    const uint64_t o_scratch = carve(((uint64_t)pa.nchunks + 1) * pa.slot * 4);
+    const uint64_t o_cw = carve(nc * 4), o_ce = carve(nc * 4), o_ct = carve(nc * 4);
+    const uint64_t o_gw = carve(ng * 4), o_ge = carve(ng * 4);
+    const uint64_t o_pw = carve(ng * 4), o_pe = carve(ng * 4);
+    const uint64_t o_em = carve(nc * kEncSegs * 4);
+    const uint64_t o_wd = carve(nc * kEncSegs);
+    const uint64_t o_si = carve(nc * kEscStage * 4), o_sv = carve(nc * kEscStage * 4);
+    const uint64_t o_rp = carve(2 * (uint64_t)range_blocks(pa.n) * 4);
+    const uint64_t o_mu = carve(pa.nblocks * 4);
+    if (base != nullptr && ws != nullptr) {
+        uint8_t *b = base;
+        ws->info = reinterpret_cast<DevInfo *>(b + o_info);
+        ws->scratch = reinterpret_cast<uint32_t *>(b + o_scratch);
+        ws->chunk_words = reinterpret_cast<uint32_t *>(b + o_cw);
+        ws->chunk_esc = reinterpret_cast<uint32_t *>(b + o_ce);
+        ws->chunk_tmask = reinterpret_cast<uint32_t *>(b + o_ct);
+        ws->group_words = reinterpret_cast<uint32_t *>(b + o_gw);
+        ws->group_esc = reinterpret_cast<uint32_t *>(b + o_ge);
+        ws->gpre_words = reinterpret_cast<uint32_t *>(b + o_pw);
+        ws->gpre_esc = reinterpret_cast<uint32_t *>(b + o_pe);
+        ws->emask = reinterpret_cast<uint32_t *>(b + o_em);
+        ws->widths = b + o_wd;
+        ws->stage_idx = reinterpret_cast<uint32_t *>(b + o_si);
+        ws->stage_val = reinterpret_cast<uint32_t *>(b + o_sv);
+        ws->range_part = reinterpret_cast<float *>(b + o_rp);
+        ws->means = reinterpret_cast<int32_t *>(b + o_mu);
+    }
+    return off;
+}
+
 }  // namespace
 
 extern "C" {
@@ -441,25 +543,10 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     *plan_out = nullptr;
     if (exec->kind != EBLC_EXECUTION_HIP) return EBLC_UNSUPPORTED;
     if (dtype != EBLC_FLOAT32) return EBLC_UNSUPPORTED;
-    if (rank < 1 || rank > 4) return EBLC_UNSUPPORTED;
-    uint64_t n = 1;
-    for (int a = 0; a < rank; ++a) {
-        if (dims[a] <= 0) return EBLC_INVALID_ARGUMENT;
-        if ((uint64_t)dims[a] >= (1ull << 32)) return EBLC_INVALID_ARGUMENT;
-        n *= (uint64_t)dims[a];
-        if (n >= (1ull << 32)) return EBLC_INVALID_ARGUMENT;
-    }
-    Layout lay{};
-    eblc_status ls = make_layout(rank, dims, strides, &lay);
-    if (ls != EBLC_OK) return ls;
     Options o;
-    eblc_status st = parse_options(options, &o);
+    PlanArgs pa{};
+    eblc_status st = setup_args(rank, dims, strides, options, &o, &pa);
     if (st != EBLC_OK) return st;
-    if (!o.side_set) o.side_max = n < (1ull << 23) ? n : (1ull << 23);
-    if (o.side_max > n) return EBLC_INVALID_ARGUMENT;
-    /* the scans add payload words in 32-bit arithmetic: the largest payload a field can take
-     * must stay below 2^32 words */
-    if (max_payload_words(n, o.chunk_coder ? o.V : 0) >= (1ull << 32)) return EBLC_INVALID_ARGUMENT;
 
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess) return EBLC_DEVICE_ERROR;
@@ -472,85 +559,19 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     p->device = exec->device;
     p->rank = rank;
     for (int a = 0; a < rank; ++a) p->dims[a] = dims[a];
-    p->n = n;
+    p->n = pa.n;
     p->rel = o.rel;
     p->eps = o.eps;
-    PlanArgs &pa = p->pa;
-    pa.n = n;
-    pa.nseg = (n + 31) / 32;
-    for (int a = 0; a < 4; ++a) pa.dims[a] = a < rank ? (uint64_t)dims[a] : 0;
-    pa.rank = (uint32_t)rank;
-    pa.B = o.B;
-    pa.T = o.T;
-    pa.nchunks = (uint32_t)((n + kEncChunk - 1) / kEncChunk);
-    pa.ngroups = (pa.nchunks + kEncChunksPerGroup - 1) / kEncChunksPerGroup;
-    if (o.chunk_coder) {
-        pa.V = o.V;
-        pa.log2seg = (uint32_t)__builtin_ctz(o.V);
-        pa.slot = kEncChunk + kEncChunk / 32;
-        pa.wpg = 4u * (kEncChunksPerGroup * kEncChunk / o.V);
-        pa.dchunks = (uint32_t)((n + o.V - 1) / o.V);
-        pa.wsec = align_up(4ull * pa.dchunks, 16);
-    } else {
-        pa.V = 0;
-        pa.log2seg = 5;
-        pa.slot = kEncChunk;
-        pa.wpg = kEncChunksPerGroup * kEncSegs;
-        pa.dchunks = (uint32_t)((n + kDecChunk - 1) / kDecChunk);
-        pa.wsec = align_up(pa.nseg, 16);
-    }
-    pa.dgroups = (pa.dchunks + kDecChunksPerGroup - 1) / kDecChunksPerGroup;
-    pa.center = o.center ? 1u : 0u;
-    pa.log2B = 0; /* ceil(log2 B) */
-    while ((1u << pa.log2B) < pa.B) ++pa.log2B;
-    pa.nblocks = (n + pa.B - 1) / pa.B;
-    pa.msec = o.center ? align_up(4 * pa.nblocks, 16) : 0;
-    pa.side_max = o.side_max;
-    pa.lay = lay;
-
-    /* workspace: one allocation, carved into 256-byte aligned arrays */
-    const uint64_t nc = pa.nchunks > pa.dchunks ? pa.nchunks : pa.dchunks;
-    const uint64_t ng = pa.ngroups > pa.dgroups ? pa.ngroups : pa.dgroups;
-    uint64_t off = 0;
-    auto carve = [&](uint64_t bytes) {
-        const uint64_t at = off;
-        off = align_up(off + bytes, 256);
-        return at;
-    };
-    const uint64_t o_info = carve(sizeof(DevInfo));
-    /* one spare slot: a 4096-value chunk of the chunk coder spills into its second wave's slot */
-    const uint64_t o_scratch = carve(((uint64_t)pa.nchunks + 1) * pa.slot * 4);
-    const uint64_t o_cw = carve(nc * 4), o_ce = carve(nc * 4), o_ct = carve(nc * 4);
-    const uint64_t o_gw = carve(ng * 4), o_ge = carve(ng * 4);
-    const uint64_t o_pw = carve(ng * 4), o_pe = carve(ng * 4);
-    const uint64_t o_em = carve(nc * kEncSegs * 4);
-    const uint64_t o_wd = carve(nc * kEncSegs);
-    const uint64_t o_si = carve(nc * kEscStage * 4), o_sv = carve(nc * kEscStage * 4);
-    const uint64_t o_rp = carve(2 * (uint64_t)range_blocks(n) * 4);
-    const uint64_t o_mu = carve(pa.nblocks * 4);
+    p->pa = pa;
+    /* workspace: one allocation, carved into 256-byte aligned arrays, `lanes` times over */
+    const uint64_t bytes = carve_workspace(pa, nullptr, nullptr);
     p->lanes = (int)o.lanes;
-    if (hipMalloc(&p->ws_base, off * o.lanes) != hipSuccess) {
+    if (hipMalloc(&p->ws_base, bytes * o.lanes) != hipSuccess) {
         delete p;
         return EBLC_OUT_OF_MEMORY;
     }
-    p->ws_stride = off;
-    uint8_t *b = static_cast<uint8_t *>(p->ws_base);
-    Workspace &ws = p->ws;
-    ws.info = reinterpret_cast<DevInfo *>(b + o_info);
-    ws.scratch = reinterpret_cast<uint32_t *>(b + o_scratch);
-    ws.chunk_words = reinterpret_cast<uint32_t *>(b + o_cw);
-    ws.chunk_esc = reinterpret_cast<uint32_t *>(b + o_ce);
-    ws.chunk_tmask = reinterpret_cast<uint32_t *>(b + o_ct);
-    ws.group_words = reinterpret_cast<uint32_t *>(b + o_gw);
-    ws.group_esc = reinterpret_cast<uint32_t *>(b + o_ge);
-    ws.gpre_words = reinterpret_cast<uint32_t *>(b + o_pw);
-    ws.gpre_esc = reinterpret_cast<uint32_t *>(b + o_pe);
-    ws.emask = reinterpret_cast<uint32_t *>(b + o_em);
-    ws.widths = b + o_wd;
-    ws.stage_idx = reinterpret_cast<uint32_t *>(b + o_si);
-    ws.stage_val = reinterpret_cast<uint32_t *>(b + o_sv);
-    ws.range_part = reinterpret_cast<float *>(b + o_rp);
-    ws.means = reinterpret_cast<int32_t *>(b + o_mu);
+    p->ws_stride = bytes;
+    carve_workspace(pa, static_cast<uint8_t *>(p->ws_base), &p->ws);
 
     if (hipHostMalloc(reinterpret_cast<void **>(&p->host_result), sizeof(eblc_result_t), hipHostMallocDefault) != hipSuccess) {
         eblc_plan_destroy(p);
