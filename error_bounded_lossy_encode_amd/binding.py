@@ -20,6 +20,7 @@ EBLC_CAPACITY = 3
 EBLC_CORRUPT_STREAM = 4
 EBLC_DEVICE_ERROR = 5
 EBLC_OUT_OF_MEMORY = 6
+EBLC_TOO_LARGE = 7
 
 EBLC_EXECUTION_HOST = 0
 EBLC_EXECUTION_CUDA = 1
@@ -43,7 +44,8 @@ class eblc_limits_t(ctypes.Structure):
 
 
 EXPORTS = ["eblc_abi_version", "eblc_plan_create", "eblc_plan_limits", "eblc_max_compressed_bytes",
-           "eblc_payload_alignment", "eblc_compress", "eblc_compress_async", "eblc_compress_batch",
+           "eblc_payload_alignment", "eblc_compress", "eblc_compress_async", "eblc_compress_noalloc",
+           "eblc_compress_batch",
            "eblc_decompress", "eblc_decompress_batch", "eblc_plan_status", "eblc_plan_destroy", "eblc_status_string",
            "eblc_plan_set_profiling", "eblc_plan_kernel_times"]
 
@@ -74,6 +76,8 @@ def lib():
     L.eblc_compress.restype = I
     L.eblc_compress_async.argtypes = [P, P, P, SZ, P, P]
     L.eblc_compress_async.restype = I
+    L.eblc_compress_noalloc.argtypes = [ctypes.POINTER(eblc_execution_t), I, P, P, ctypes.c_char_p, P, P, SZ, P, P]
+    L.eblc_compress_noalloc.restype = I
     L.eblc_compress_batch.argtypes = [P, I, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(SZ), P, P]
     L.eblc_compress_batch.restype = I
     L.eblc_decompress.argtypes = [P, P, SZ, P, P, P]
@@ -160,6 +164,21 @@ def eblc_compress_async(plan, x, out, result, out_capacity: int | None = None, s
     cap = out.numel() * out.element_size() if out_capacity is None else int(out_capacity)
     return int(lib().eblc_compress_async(plan, _ptr(x), _ptr(out), cap, _ptr(result),
                                          _stream_handle(stream)))
+
+
+def eblc_compress_noalloc(dims, options, x, out, result, out_capacity: int | None = None, device: int = 0,
+                          strides=None, stream=None) -> int:
+    """Plan-less compress into the library's static scratch: x float32 device tensor, out uint8
+    device tensor, result a device (or pinned host) tensor of >= 16 bytes receiving the
+    eblc_result_t record.  Returns the status."""
+    dims = [int(d) for d in dims]
+    d = (ctypes.c_int64 * max(1, len(dims)))(*dims)
+    s = None if strides is None else (ctypes.c_int64 * len(strides))(*[int(v) for v in strides])
+    ex = eblc_execution_t(EBLC_EXECUTION_HIP, device, 0)
+    cap = out.numel() * out.element_size() if out_capacity is None else int(out_capacity)
+    return int(lib().eblc_compress_noalloc(ctypes.byref(ex), len(dims), d, s,
+                                           None if options is None else options.encode(), _ptr(x), _ptr(out),
+                                           cap, _ptr(result), _stream_handle(stream)))
 
 
 def eblc_compress_batch(plan, xs, outs, results, capacities=None, stream=None) -> int:

@@ -17,6 +17,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <string_view>
@@ -517,6 +518,39 @@ uint64_t carve_workspace(const PlanArgs &pa, uint8_t *base, Workspace *ws) {
     return off;
 }
 
+/* ---- the compress entry point that allocates nothing -------------------------------------- */
+
+constexpr uint64_t kScratchBytes = 24ull << 20;    /* the static scratch: one workspace */
+constexpr uint64_t kScratchMaxValues = 1ull << 22; /* largest field it takes */
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+/* The workspace of eblc_compress_noalloc: every device the library runs that call on holds one
+ * copy until the process ends.  Host code never hands this name to a kernel -- on the host it
+ * is only a stand-in for the symbol; a device's copy is addressed through the pointer that
+ * hipGetSymbolAddress returns on that device. */
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+void *g_scratch_dev[kMaxDevices] = {};
+
+/* Device address of `scratch` on device dev, which must be current: looked up once per device,
+ * at the first call there. */
+eblc_status scratch_address(int dev, void **out) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_dev[dev] == nullptr) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+            return EBLC_DEVICE_ERROR;
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return EBLC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -532,6 +566,7 @@ const char *eblc_status_string(eblc_status s) {
         case EBLC_CORRUPT_STREAM: return "corrupt stream";
         case EBLC_DEVICE_ERROR: return "device error";
         case EBLC_OUT_OF_MEMORY: return "out of memory";
+        case EBLC_TOO_LARGE: return "field too large for the static scratch";
     }
     return "unknown status";
 }
@@ -637,6 +672,53 @@ eblc_status eblc_compress_async(eblc_plan_t *plan, const float *in, void *out, s
     void *outs[1] = {out};
     const size_t caps[1] = {out_capacity};
     return hip_status(enqueue_compress(plan, 1, &in, outs, caps, result, static_cast<hipStream_t>(stream)));
+}
+
+eblc_status eblc_compress_noalloc(const eblc_execution_t *exec, int rank, const int64_t *dims,
+                                  const int64_t *strides, const char *options, const float *in, void *out,
+                                  size_t out_capacity, eblc_result_t *result, void *stream) {
+    if (exec == nullptr || dims == nullptr || result == nullptr || (reinterpret_cast<uintptr_t>(result) & 7u) != 0)
+        return EBLC_INVALID_ARGUMENT;
+    if (exec->kind != EBLC_EXECUTION_HIP) return EBLC_UNSUPPORTED;
+    Options o;
+    PlanArgs pa{};
+    eblc_status st = setup_args(rank, dims, strides, options, &o, &pa);
+    if (st != EBLC_OK) return st;
+    if (o.lanes != 1) return EBLC_INVALID_ARGUMENT; /* a batch option */
+    const uint64_t bytes = carve_workspace(pa, nullptr, nullptr);
+    if (pa.n > kScratchMaxValues || bytes > kScratchBytes) return EBLC_TOO_LARGE;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess) return EBLC_DEVICE_ERROR;
+    if (exec->device < 0 || exec->device >= ndev || exec->device >= kMaxDevices) return EBLC_INVALID_ARGUMENT;
+    DeviceGuard guard(exec->device);
+    if (!guard.ok) return EBLC_DEVICE_ERROR;
+    void *base = nullptr;
+    st = scratch_address(exec->device, &base);
+    if (st != EBLC_OK) return st;
+    /* a plan on the stack over the static scratch: no workspace or events of its own */
+    eblc_plan job;
+    job.device = exec->device;
+    job.rank = rank;
+    for (int a = 0; a < rank; ++a) job.dims[a] = dims[a];
+    job.n = pa.n;
+    job.rel = o.rel;
+    job.eps = o.eps;
+    job.pa = pa;
+    job.lanes = 1;
+    job.ws_stride = bytes;
+    carve_workspace(pa, static_cast<uint8_t *>(base), &job.ws);
+    st = check_compress_args(&job, in, out);
+    if (st != EBLC_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    /* a relative bound is resolved by the range pass; an absolute one by one small kernel, since
+     * the scratch holds the previous call's bound */
+    if (!o.rel) {
+        const hipError_t e = launch_resolve_abs(job.ws, o.eps, hs);
+        if (e != hipSuccess) return EBLC_DEVICE_ERROR;
+    }
+    void *outs[1] = {out};
+    const size_t caps[1] = {out_capacity};
+    return hip_status(enqueue_compress(&job, 1, &in, outs, caps, result, hs));
 }
 
 eblc_status eblc_compress_batch(eblc_plan_t *plan, int count, const float *const *in, void *const *out,

@@ -188,6 +188,9 @@ inline void eblc_launch(F kernel, const dim3 &grid, const dim3 &block, uint32_t 
  * enqueued on `stream`, and returns the launch error. */
 hipError_t launch_range(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws, double eps,
                         hipStream_t stream);
+/* The bound of an absolute eps, resolved on the device into the workspace's DevInfo (one field,
+ * lane 0) by the rule the host applies at plan creation. */
+hipError_t launch_resolve_abs(const Workspace &ws, double eps, hipStream_t stream);
 hipError_t launch_encode(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                          hipStream_t stream);
 hipError_t launch_scan_compress(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,

@@ -128,6 +128,11 @@ __global__ __launch_bounds__(kRangeThreads) void range_partial_kernel(Fields fs,
 __device__ __forceinline__ void range_resolve_body(const float *__restrict__ part,
                                                    uint32_t nparts, DevInfo *info,
                                                    double eps) {
+    if (nparts == 0) {
+        /* an absolute bound: the same rule with a range of exactly 1 (eps * 1.0 = eps) */
+        if (threadIdx.x == 0) resolve_bound(0.0f, 1.0f, eps, info);
+        return;
+    }
     __shared__ float s_mn[kScanThreads / kWave], s_mx[kScanThreads / kWave];
     float a = INFINITY, b = -INFINITY;
     /* kResolveBatch partials per thread in flight before any is folded (min and max do not
@@ -1597,6 +1602,12 @@ hipError_t launch_range(const Fields &fs, uint32_t nf, const PlanArgs &pa, const
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     eblc_launch(range_resolve_kernel, dim3(1, nf), dim3(kScanThreads), 0, stream, fs, ws, grid, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_resolve_abs(const Workspace &ws, double eps, hipStream_t stream) {
+    Fields fs{};
+    eblc_launch(range_resolve_kernel, dim3(1, 1), dim3(kScanThreads), 0, stream, fs, ws, 0u, eps);
     return hipGetLastError();
 }
 

@@ -66,7 +66,8 @@ typedef enum {
     EBLC_CAPACITY = 3,         /* out_capacity smaller than the stream; required size returned */
     EBLC_CORRUPT_STREAM = 4,   /* stream header or sections inconsistent with the plan */
     EBLC_DEVICE_ERROR = 5,     /* a HIP runtime call failed */
-    EBLC_OUT_OF_MEMORY = 6     /* workspace allocation failed at plan creation */
+    EBLC_OUT_OF_MEMORY = 6,    /* workspace allocation failed at plan creation */
+    EBLC_TOO_LARGE = 7         /* eblc_compress_noalloc: field larger than its static scratch */
 } eblc_status;
 
 /* Where the pointers live ("Provider layout": HOST uses host pointers and a thread count and
@@ -187,6 +188,24 @@ eblc_status eblc_compress(eblc_plan_t *plan, const float *in, void *out, size_t 
  * (INVALID_ARGUMENT, DEVICE_ERROR); capacity is reported in the record. */
 eblc_status eblc_compress_async(eblc_plan_t *plan, const float *in, void *out, size_t out_capacity,
                                 eblc_result_t *result, void *stream);
+
+/* Compress without allocating anything, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation).  The same
+ * work as eblc_compress_async on a plan created with exec, rank, dims, strides and options, with
+ * the same arguments, checks, stream and result record, but no plan: the call's workspace is a
+ * static device array of 24 MiB that the library holds on every device it runs this call on
+ * until the process ends, and the option string is parsed without heap allocation.  Fields of
+ * up to 2^22 values (every coder and option) fit it; a larger one returns EBLC_TOO_LARGE before
+ * anything is enqueued.  The option lanes is refused (INVALID_ARGUMENT).  The device's address
+ * of the array is looked up at the first call on that device.  All calls on one device share the
+ * array: calls that overlap on one device (on different streams, or from different host threads
+ * without ordering) race and may corrupt each other's streams; calls ordered on one stream are
+ * safe.  Nothing in the array needs clearing between calls: every value a call reads there is
+ * written earlier in the same call (the previous call's payload size only picks a store
+ * policy).  Decompress the stream with any plan of the same shape and coder. */
+eblc_status eblc_compress_noalloc(const eblc_execution_t *exec, int rank, const int64_t *dims,
+                                  const int64_t *strides, const char *options, const float *in, void *out,
+                                  size_t out_capacity, eblc_result_t *result, void *stream);
 
 /* Batched asynchronous compress: count fields of the plan's shape, in[k] -> out[k] with
  * capacity out_capacity[k], result record k at results + k, enqueued on `stream` with no host

@@ -108,3 +108,23 @@ def test_payload_word_limit():
         assert binding.eblc_plan_create([n_ok], opts)[0] == binding.EBLC_DEVICE_ERROR, chunk_bytes
         if n_ok < (1 << 32) - 1:
             assert binding.eblc_plan_create([n_ok + 1], opts)[0] == binding.EBLC_INVALID_ARGUMENT, chunk_bytes
+
+
+@pytest.mark.parametrize("opts", ["rel=1e-3;block=32;center=1", "rel=1e-3;block=96;center=1",
+                                  "rel=1e-3;coder=chunk;chunk_bytes=4096", "rel=1e-3;coder=chunk;chunk_bytes=16384",
+                                  "abs=1e-3;block=2048"])
+def test_noalloc_scratch_limit(opts):
+    """eblc_compress_noalloc checks the field against its static scratch before any device call:
+    every coder and option fits at 2^22 values (the call then stops at the device query), one
+    more value is refused."""
+    if _gpu_visible():
+        pytest.skip("checks the size limit on a host without a GPU")
+    lib = binding.lib()
+    ex = binding.eblc_execution_t(binding.EBLC_EXECUTION_HIP, 0, 0)
+    res = ctypes.create_string_buffer(32)
+    addr = (ctypes.addressof(res) + 15) // 16 * 16
+    for n, want in (((1 << 22), binding.EBLC_DEVICE_ERROR), ((1 << 22) + 1, binding.EBLC_TOO_LARGE)):
+        d = (ctypes.c_int64 * 1)(n)
+        st = lib.eblc_compress_noalloc(ctypes.byref(ex), 1, d, None, opts.encode(), None, None, 0,
+                                       ctypes.c_void_p(addr), None)
+        assert st == want, (n, st)
