@@ -246,6 +246,8 @@ def main() -> int:
     ap.add_argument("--chunk-bytes", type=int, default=8192, choices=[4096, 8192, 16384])
     ap.add_argument("--center", action="store_true",
                     help="Lorenzo centering (bitpack coder): each block's first code against its mean")
+    ap.add_argument("--extra-options", default="",
+                    help="plan options appended to the workload's (e.g. lookback=0)")
     ap.add_argument("--cold-reps", type=int, default=3,
                     help="repetitions of the MALL-cold measurement (a 1 GiB device read before every "
                          "compress and decompress call); 0 skips it")
@@ -276,6 +278,9 @@ def main() -> int:
         items = [(x, dims, with_chunk_coder(opts, args.chunk_bytes)) for x, dims, opts in items]
         desc = desc.replace(", block 128", "").replace(", block 256", "").replace(", block 32", "")
         desc += f"; chunk coder (Quant, Diff, Bitshuffle, RZE) over {args.chunk_bytes}-byte chunks"
+    if args.extra_options:
+        items = [(x, dims, opts + ";" + args.extra_options) for x, dims, opts in items]
+        desc += f"; options {args.extra_options}"
     dims0, opts0 = items[0][1], items[0][2]
     assert all(d == dims0 and o == opts0 for _, d, o in items)
     n = items[0][0].numel()
