@@ -978,14 +978,12 @@ __device__ __forceinline__ void write_chunk_outliers(const float *__restrict__ x
     }
 }
 
-/* Copy one chunk's P payload words from its 16-byte aligned scratch slot to stream word Dw of
- * the (16-byte aligned) payload section, by one wave.  Destination words fall into a head
- * [Dw, bs), whole 128-bit units [bs, be) and a tail [be, Dw + P), bs and be being Dw and Dw + P
- * rounded up and down to 4 words.  Head and tail words can share a 16-byte unit with the
- * neighbouring chunks, so they are stored one by one; each whole unit is assembled from two
- * aligned source units shifted by the wave-uniform word offset (bs - Dw) mod 4.  A lane loads
- * up to kCopyBatch units before storing any, so a chunk's loads are in flight together. */
-constexpr int kCopyBatch = 4;
+/* A chunk's payload of P words goes from its 16-byte aligned scratch slot to stream word Dw of
+ * the (16-byte aligned) payload section.  Destination words fall into a head [Dw, bs), whole
+ * 128-bit units [bs, be) and a tail [be, Dw + P), bs and be being Dw and Dw + P rounded up and
+ * down to 4 words.  Head and tail words can share a 16-byte unit with the neighbouring chunks, so
+ * they are stored one by one; each whole unit is assembled from two aligned source units shifted
+ * by the wave-uniform word offset (bs - Dw) mod 4. */
 
 /* Words r..r+3 of the eight words A, B (r in 0..3), by selects on the bits of r.  The empty asm
  * keeps both units whole in registers first: without it the compiler narrows the loads to the
@@ -999,60 +997,198 @@ __device__ __forceinline__ uint4 shift_units(uint4 A, uint4 B, uint32_t r) {
     return (r & 2u) != 0 ? make_uint4(w2, w3, w4, w5) : make_uint4(w0, w1, w2, w3);
 }
 
-__device__ __forceinline__ void copy_chunk_payload(const uint32_t *__restrict__ src, uint32_t P,
-                                                   uint64_t Dw, uint32_t *__restrict__ pay) {
+
+/* The payloads of a group whose chunks are all small (at most 64 destination units each), copied
+ * by one wave (chunk k from its slot src + k slot words to stream word dw[k]): the loads of every
+ * chunk (both source units of each destination unit, the head and tail words) are issued before
+ * the first store, so the group waits for one memory latency. */
+template <int CPG>
+__device__ __forceinline__ void copy_group_payload(const uint32_t *__restrict__ src, uint32_t slot,
+                                                   const uint32_t words[CPG], const uint64_t dw[CPG],
+                                                   uint32_t *__restrict__ pay) {
     const uint32_t lane = threadIdx.x & 63;
-    const uint64_t De = Dw + P;
-    const uint64_t bs = (Dw + 3) & ~(uint64_t)3;
-    const uint64_t be = De & ~(uint64_t)3;
-    const uint64_t head_end = bs < De ? bs : De;
-    const uint64_t tail_start = be > bs ? be : bs;
-    const bool head = lane < head_end - Dw;
-    const bool tail = tail_start < De && lane < De - tail_start;
-    const uint32_t hv = head ? src[lane] : 0u;
-    const uint32_t tv = tail ? src[tail_start - Dw + lane] : 0u;
-    const uint32_t units = be > bs ? (uint32_t)((be - bs) >> 2) : 0u;
-    const uint32_t r = (uint32_t)(bs - Dw); /* 0..3: source word offset of unit 0 */
-    const uint32_t rn = r != 0 ? 1u : 0u;
-    const uint4 *s4 = reinterpret_cast<const uint4 *>(src);
-    uint4 *d4 = reinterpret_cast<uint4 *>(pay + bs);
-    for (uint32_t t0 = 0; t0 < units; t0 += kCopyBatch * kWave) {
-        uint4 A[kCopyBatch], B[kCopyBatch];
+    uint4 A[CPG], B[CPG];
+    uint32_t hv[CPG], tv[CPG];
 #pragma unroll
-        for (int k = 0; k < kCopyBatch; ++k) {
-            /* unconditional loads at clamped indices, so the batch issues without waits; the
-             * last source unit holding a needed word is units - 1 + rn, and B is A when r = 0 */
-            const uint32_t t = t0 + lane + kWave * k;
-            A[k] = s4[min(t, units - 1)];
-            B[k] = s4[min(t + rn, units - 1 + rn)];
-        }
-#pragma unroll
-        for (int k = 0; k < kCopyBatch; ++k) {
-            const uint32_t t = t0 + lane + kWave * k;
-            if (t < units) d4[t] = shift_units(A[k], B[k], r);
+    for (int k = 0; k < CPG; ++k) {
+        const uint32_t *sk = src + (uint64_t)k * slot;
+        const uint64_t De = dw[k] + words[k];
+        const uint64_t bs = (dw[k] + 3) & ~(uint64_t)3, be = De & ~(uint64_t)3;
+        const uint64_t head_end = bs < De ? bs : De;
+        const uint64_t tail_start = be > bs ? be : bs;
+        const uint32_t units = be > bs ? (uint32_t)((be - bs) >> 2) : 0u;
+        const uint32_t rn = bs != dw[k] ? 1u : 0u;
+        hv[k] = lane < head_end - dw[k] ? sk[lane] : 0u;
+        tv[k] = tail_start < De && lane < De - tail_start ? sk[tail_start - dw[k] + lane] : 0u;
+        A[k] = B[k] = make_uint4(0, 0, 0, 0);
+        if (units != 0) {
+            /* clamped indices: the last source unit holding a needed word is units - 1 + rn */
+            const uint4 *s4 = reinterpret_cast<const uint4 *>(sk);
+            A[k] = s4[min(lane, units - 1)];
+            B[k] = s4[min(lane + rn, units - 1 + rn)];
         }
     }
-    if (head) pay[Dw + lane] = hv;
-    if (tail) pay[tail_start + lane] = tv;
+#pragma unroll
+    for (int k = 0; k < CPG; ++k) {
+        const uint64_t De = dw[k] + words[k];
+        const uint64_t bs = (dw[k] + 3) & ~(uint64_t)3, be = De & ~(uint64_t)3;
+        const uint64_t head_end = bs < De ? bs : De;
+        const uint64_t tail_start = be > bs ? be : bs;
+        const uint32_t units = be > bs ? (uint32_t)((be - bs) >> 2) : 0u;
+        if (lane < units) reinterpret_cast<uint4 *>(pay + bs)[lane] = shift_units(A[k], B[k], (uint32_t)(bs - dw[k]));
+        if (lane < head_end - dw[k]) pay[dw[k] + lane] = hv[k];
+        if (tail_start < De && lane < De - tail_start) pay[tail_start + lane] = tv[k];
+    }
 }
 
-/* One workgroup per group of kEncChunksPerGroup encode chunks, one wave per chunk: the wave
- * copies its chunk's payload to the chunk's scanned offset, then writes the chunk's outliers.
- * In RAW mode the workgroup copies the group's input values instead.  The last group also
- * zeroes the pads after the payload and after the outlier sections. */
+/* One round of a chunk's copy: destination units [t0, t0 + 256) of the chunk's whole units, four
+ * per lane, with the source words they need; the first round also carries the head and tail
+ * words.  Unit t takes source words r .. r+3 of source units t and t+1: unit t+1 comes from the
+ * next lane (DPP wave_shl1), or for the last lane from the next batch's first unit, or from one
+ * more unit loaded for the round. */
+constexpr int kCopyBatch = 2; /* units per lane per round of a larger chunk's copy */
+
+struct CopyRound {
+    uint4 A[kCopyBatch];
+    uint4 E;
+    uint32_t hv, tv;
+};
+
+struct ChunkGeom {
+    const uint32_t *src;
+    uint64_t dw, bs, tail_start, de;
+    uint32_t units, r, rn;
+};
+
+__device__ __forceinline__ ChunkGeom chunk_geom(const uint32_t *src, uint32_t P, uint64_t dw) {
+    ChunkGeom g;
+    g.src = src;
+    g.dw = dw;
+    g.de = dw + P;
+    g.bs = (dw + 3) & ~(uint64_t)3;
+    const uint64_t be = g.de & ~(uint64_t)3;
+    g.tail_start = be > g.bs ? be : g.bs;
+    g.units = be > g.bs ? (uint32_t)((be - g.bs) >> 2) : 0u;
+    g.r = (uint32_t)(g.bs - dw);
+    g.rn = g.r != 0 ? 1u : 0u;
+    return g;
+}
+
+__device__ __forceinline__ void load_round(const ChunkGeom &g, uint32_t t0, CopyRound &R) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint4 *s4 = reinterpret_cast<const uint4 *>(g.src);
+    /* the last source unit holding a needed word is units - 1 + rn; indices clamp to it */
+    const uint32_t lastu = g.units - 1 + g.rn;
+#pragma unroll
+    for (int i = 0; i < kCopyBatch; ++i) R.A[i] = s4[min(t0 + lane + (uint32_t)(kWave * i), lastu)];
+    R.E = s4[min(t0 + (uint32_t)(kWave * kCopyBatch), lastu)];
+    R.hv = R.tv = 0;
+    if (t0 == 0) {
+        const uint64_t head_end = g.bs < g.de ? g.bs : g.de;
+        if (lane < head_end - g.dw) R.hv = g.src[lane];
+        if (g.tail_start < g.de && lane < g.de - g.tail_start) R.tv = g.src[g.tail_start - g.dw + lane];
+    }
+}
+
+__device__ __forceinline__ uint32_t shl1(uint32_t v, uint32_t last_lane_value) {
+    return dpp<0x130>(last_lane_value, v); /* wave_shl1: lane l takes lane l + 1's value */
+}
+
+__device__ __forceinline__ void store_round(const ChunkGeom &g, uint32_t t0, const CopyRound &R,
+                                            uint32_t *__restrict__ pay) {
+    const uint32_t lane = threadIdx.x & 63;
+    uint4 *d4 = reinterpret_cast<uint4 *>(pay + g.bs);
+#pragma unroll
+    for (int i = 0; i < kCopyBatch; ++i) {
+        const uint4 nx = i + 1 < kCopyBatch ? R.A[i + 1 < kCopyBatch ? i + 1 : i] : R.E;
+        uint4 B;
+        B.x = shl1(R.A[i].x, readlane(nx.x, 0));
+        B.y = shl1(R.A[i].y, readlane(nx.y, 0));
+        B.z = shl1(R.A[i].z, readlane(nx.z, 0));
+        B.w = shl1(R.A[i].w, readlane(nx.w, 0));
+        const uint32_t t = t0 + lane + (uint32_t)(kWave * i);
+        if (t < g.units) d4[t] = shift_units(R.A[i], B, g.r);
+    }
+    if (t0 == 0) {
+        const uint64_t head_end = g.bs < g.de ? g.bs : g.de;
+        if (lane < head_end - g.dw) pay[g.dw + lane] = R.hv;
+        if (g.tail_start < g.de && lane < g.de - g.tail_start) pay[g.tail_start + lane] = R.tv;
+    }
+}
+
+/* The payloads of the chunks of a group in `mask` (bit k: chunk k, from src + k slot words to
+ * stream word dw[k]), one round after another, each round's loads issued before the previous
+ * round's stores. */
+template <int CPG>
+__device__ __forceinline__ void copy_chunks_pipelined(const uint32_t *__restrict__ src, uint32_t slot,
+                                                      const uint32_t words[CPG], const uint64_t dw[CPG],
+                                                      uint32_t mask, uint32_t *__restrict__ pay) {
+    constexpr uint32_t kRound = kCopyBatch * kWave;
+    /* the words and destination of chunk k, by selects on the wave-uniform k (an indexed read
+     * of the arrays would place them in memory) */
+#define EBLC_CHUNK_GEOM(K, OUT)                                       \
+    do {                                                              \
+        uint32_t P_ = words[0];                                       \
+        uint64_t d_ = dw[0];                                          \
+        _Pragma("unroll") for (int j_ = 1; j_ < CPG; ++j_) {          \
+            P_ = (K) == j_ ? words[j_] : P_;                          \
+            d_ = (K) == j_ ? dw[j_] : d_;                             \
+        }                                                             \
+        OUT = chunk_geom(src + (uint64_t)(K) * slot, P_, d_);         \
+    } while (0)
+    if (mask == 0) return;
+    int k = __builtin_ctz(mask);
+    mask &= mask - 1;
+    ChunkGeom g;
+    EBLC_CHUNK_GEOM(k, g);
+    uint32_t t0 = 0;
+    CopyRound cur;
+    load_round(g, 0, cur);
+#pragma unroll 1
+    for (;;) {
+        /* the next round: of this chunk, or the first of the next chunk */
+        ChunkGeom gn = g;
+        uint32_t tn = t0 + kRound;
+        bool more = tn < g.units;
+        if (!more && mask != 0) {
+            k = __builtin_ctz(mask);
+            mask &= mask - 1;
+            EBLC_CHUNK_GEOM(k, gn);
+            tn = 0;
+            more = true;
+        }
+        CopyRound nxt;
+        if (more) load_round(gn, tn, nxt);
+        store_round(g, t0, cur, pay);
+        if (!more) break;
+        g = gn;
+        t0 = tn;
+        cur = nxt;
+    }
+#undef EBLC_CHUNK_GEOM
+}
+
+/* Chunks of at most this many payload words and kEscStage escapes are small. */
+constexpr uint32_t kSmallChunkWords = 4 * kWave;
+
+/* One wave per group of kEncChunksPerGroup encode chunks, kWavesPerBlock groups per workgroup.  A
+ * group of small chunks -- most groups of a well-compressed field -- issues the loads of all four
+ * chunks together (copy_group_payload), so it waits for one memory latency; a group with a larger
+ * chunk copies its chunks one after another (copy_chunk_payload), with their outliers.  (A wave
+ * per chunk left every wave waiting on its own chain of loads, twice the chains in all on the
+ * 512^3 field.)  In RAW mode the wave copies the group's input values instead.  The last group
+ * also zeroes the pads after the payload and after the outlier sections. */
 template <bool STRIDED>
 __device__ __forceinline__ void compact_body(const float *__restrict__ x,
                                              PlanArgs pa, Workspace ws,
                                              uint8_t *__restrict__ out,
                                              const uint8_t *__restrict__ widths_src) {
     constexpr int CPG = kEncChunksPerGroup;
-    static_assert(CPG == kBlockThreads / kWave, "one wave per chunk");
-    const uint32_t tid = threadIdx.x;
-    const uint32_t grp = blockIdx.x;
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t grp = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    if (grp >= pa.ngroups) return;
     const DevInfo *info = ws.info;
     /* every small input of the group up front, in one round of loads */
-    const uint32_t wave = tid >> 6, lane = tid & 63;
-    const uint32_t c = grp * CPG + wave;
     uint32_t words[CPG], escs[CPG];
 #pragma unroll
     for (int k = 0; k < CPG; ++k) {
@@ -1075,59 +1211,90 @@ __device__ __forceinline__ void compact_body(const float *__restrict__ x,
         const uint32_t *srcw = reinterpret_cast<const uint32_t *>(x) + gbase;
         if (STRIDED) {
             const uint32_t *xb = reinterpret_cast<const uint32_t *>(x);
-            for (uint32_t i = tid; i < cnt; i += kBlockThreads) dstw[i] = xb[elem_off<true>(pa.lay, gbase + i)];
+            for (uint32_t i = lane; i < cnt; i += kWave) dstw[i] = xb[elem_off<true>(pa.lay, gbase + i)];
         } else if (cnt == (uint64_t)kGroupVals) {
-            constexpr int kPer = kGroupVals / 4 / kBlockThreads;
+            constexpr int kPer = 4; /* 128-bit units per lane per round */
             const uint4 *s4 = reinterpret_cast<const uint4 *>(srcw);
             uint4 *d4 = reinterpret_cast<uint4 *>(dstw);
-            uint4 t[kPer];
+            for (uint32_t b = 0; b < kGroupVals / 4; b += kPer * kWave) {
+                uint4 t[kPer];
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) t[i] = ld_nt(s4 + tid + kBlockThreads * i);
+                for (int i = 0; i < kPer; ++i) t[i] = ld_nt(s4 + b + lane + kWave * i);
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) st_nt(d4 + tid + kBlockThreads * i, t[i]);
+                for (int i = 0; i < kPer; ++i) st_nt(d4 + b + lane + kWave * i, t[i]);
+            }
         } else {
-            for (uint32_t i = tid; i < cnt; i += kBlockThreads) dstw[i] = srcw[i];
+            for (uint32_t i = lane; i < cnt; i += kWave) dstw[i] = srcw[i];
         }
         if (last) {
             const uint64_t end = kHeaderBytes + 4 * n;
             const uint64_t pad = align16(4 * n) - 4 * n;
-            if (tid < pad / 4) reinterpret_cast<uint32_t *>(out + end)[tid] = 0u;
+            if (lane < pad / 4) reinterpret_cast<uint32_t *>(out + end)[lane] = 0u;
         }
         return;
     }
-    uint32_t W = gw, O = ge;
+    uint64_t dw[CPG];
+    uint32_t O[CPG];
+    bool small = true;
+    {
+        uint32_t W = gw, E = ge;
 #pragma unroll
-    for (int k = 0; k < CPG; ++k) {
-        W += (uint32_t)k < wave ? words[k] : 0u;
-        O += (uint32_t)k < wave ? escs[k] : 0u;
+        for (int k = 0; k < CPG; ++k) {
+            dw[k] = W;
+            O[k] = E;
+            W += words[k];
+            E += escs[k];
+            small = small && words[k] <= kSmallChunkWords && escs[k] <= (uint32_t)kEscStage;
+        }
     }
     uint32_t *pay = reinterpret_cast<uint32_t *>(out + payload_off);
     uint32_t *oidx = reinterpret_cast<uint32_t *>(out + oidx_off);
     uint32_t *oval = reinterpret_cast<uint32_t *>(out + oval_off);
-    if (c < pa.nchunks) {
-        /* a chunk whose escapes were all staged: their loads go out with the payload's */
-        const uint32_t cnt = escs[wave];
-        const bool staged = cnt != 0 && cnt <= (uint32_t)kEscStage;
-        uint32_t si = 0, sv = 0;
-        if (staged && lane < cnt) {
-            si = ws.stage_idx[(uint64_t)c * kEscStage + lane];
-            sv = ws.stage_val[(uint64_t)c * kEscStage + lane];
-        }
-        copy_chunk_payload(ws.scratch + (uint64_t)c * pa.slot, words[wave], W, pay);
-        if (staged) {
-            if (lane < cnt) {
-                oidx[O + lane] = si;
-                oval[O + lane] = sv;
+    if (small) {
+        copy_group_payload<CPG>(ws.scratch + (uint64_t)grp * CPG * pa.slot, pa.slot, words, dw, pay);
+    } else {
+        uint32_t mask = 0;
+#pragma unroll
+        for (int k = 0; k < CPG; ++k)
+            if (grp * CPG + (uint32_t)k < pa.nchunks && words[k] != 0) mask |= 1u << k;
+        copy_chunks_pipelined<CPG>(ws.scratch + (uint64_t)grp * CPG * pa.slot, pa.slot, words, dw, mask, pay);
+    }
+    /* the outliers, after the payload (few groups have any): the chunks' staged escapes, loaded
+     * together, or for a chunk with more, its escapes ranked from its segments' bitmasks */
+    uint32_t any_esc = 0;
+#pragma unroll
+    for (int k = 0; k < CPG; ++k) any_esc |= escs[k];
+    if (any_esc != 0) {
+        uint32_t si[CPG], sv[CPG];
+#pragma unroll
+        for (int k = 0; k < CPG; ++k) {
+            const uint64_t ck = (uint64_t)grp * CPG + k;
+            si[k] = sv[k] = 0;
+            if (escs[k] <= (uint32_t)kEscStage && lane < escs[k]) {
+                si[k] = ws.stage_idx[ck * kEscStage + lane];
+                sv[k] = ws.stage_val[ck * kEscStage + lane];
             }
-        } else {
-            write_chunk_outliers<STRIDED>(x, pa.lay, ws, c, cnt, O, oidx, oval);
+        }
+#pragma unroll
+        for (int k = 0; k < CPG; ++k) {
+            const uint32_t ck = grp * CPG + k;
+            if (escs[k] <= (uint32_t)kEscStage) {
+                if (lane < escs[k]) {
+                    oidx[O[k] + lane] = si[k];
+                    oval[O[k] + lane] = sv[k];
+                }
+            } else if (ck < pa.nchunks) {
+                write_chunk_outliers<STRIDED>(x, pa.lay, ws, ck, escs[k], O[k], oidx, oval);
+            }
         }
     }
     if (widths_src != nullptr) {
         /* the group's share of the size section, staged by the encoder */
-        const uint64_t off = (uint64_t)grp * pa.wpg + 4u * tid;
-        if (tid < pa.wpg / 4 && off < pa.wsec)
-            *reinterpret_cast<uint32_t *>(out + kHeaderBytes + off) = *reinterpret_cast<const uint32_t *>(widths_src + off);
+        for (uint32_t i = lane; i < pa.wpg / 4; i += kWave) {
+            const uint64_t off = (uint64_t)grp * pa.wpg + 4u * i;
+            if (off < pa.wsec)
+                *reinterpret_cast<uint32_t *>(out + kHeaderBytes + off) = *reinterpret_cast<const uint32_t *>(widths_src + off);
+        }
     }
     if (pa.center) {
         /* the means of the blocks that start in the group, staged by the encoder, into the
@@ -1137,17 +1304,17 @@ __device__ __forceinline__ void compact_body(const float *__restrict__ x,
         const uint64_t b1e = (gend + pa.B - 1) / pa.B;
         const uint64_t b1 = b1e < pa.nblocks ? b1e : pa.nblocks;
         int32_t *mdst = reinterpret_cast<int32_t *>(out + kHeaderBytes + pa.wsec);
-        for (uint64_t b = b0 + tid; b < b1; b += kBlockThreads) mdst[b] = ws.means[b];
-        if (last && tid < (pa.msec - 4 * pa.nblocks) / 4) mdst[pa.nblocks + tid] = 0;
+        for (uint64_t b = b0 + lane; b < b1; b += kWave) mdst[b] = ws.means[b];
+        if (last && lane < (pa.msec - 4 * pa.nblocks) / 4) mdst[pa.nblocks + lane] = 0;
     }
     if (last) {
         const uint64_t pend = payload_off + 4 * payload_words;
         const uint64_t pad = oidx_off - pend;
-        if (tid < pad / 4) reinterpret_cast<uint32_t *>(out + pend)[tid] = 0u;
+        if (lane < pad / 4) reinterpret_cast<uint32_t *>(out + pend)[lane] = 0u;
         const uint64_t opad = (align16(4 * m) - 4 * m) / 4;
-        if (tid < opad) {
-            oidx[m + tid] = 0u;
-            oval[m + tid] = 0u;
+        if (lane < opad) {
+            oidx[m + lane] = 0u;
+            oval[m + lane] = 0u;
         }
     }
 }
@@ -1644,7 +1811,7 @@ hipError_t launch_scan_compress(const Fields &fs, uint32_t nf, const PlanArgs &p
 
 hipError_t launch_compact(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                           hipStream_t stream) {
-    const dim3 grid(pa.ngroups, nf), block(kBlockThreads);
+    const dim3 grid((pa.ngroups + kWavesPerBlock - 1) / kWavesPerBlock, nf), block(kBlockThreads);
     if (pa.lay.strided)
         eblc_launch(compact_kernel<true>, grid, block, 0, stream, fs, pa, ws);
     else
