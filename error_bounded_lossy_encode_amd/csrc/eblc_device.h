@@ -227,8 +227,23 @@ __device__ __forceinline__ int32_t unzigzag(uint32_t z) {
     return (int32_t)((z >> 1) ^ (0u - (z & 1u)));
 }
 
-/* Word offset of chunk c in the packed payload (or outlier rank), from the group prefix plus
- * the chunks before c in its group; the loads are issued together, then summed. */
+/* Sum over the wave of v (every lane gets it). */
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) { return readlane(wave_incl_scan(v), 63); }
+
+/* Exclusive prefix of group g from the scanned prefixes of the super-groups of kSuperGroups
+ * groups (spre) and the sums of the groups before g in its super-group (gsum), by one wave: lane
+ * l loads the sum of group (g rounded down to a super-group) + l when that group comes before g,
+ * and the wave adds them.  The loads do not depend on each other, so they go out with the
+ * caller's.  (Scalar loads of the same 64 sums were slower.) */
+__device__ __forceinline__ uint32_t group_prefix(const uint32_t *spre, const uint32_t *gsum, uint32_t g) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t g0 = g & ~(uint32_t)(kSuperGroups - 1);
+    const uint32_t v = g0 + lane < g ? gsum[g0 + lane] : 0u;
+    return spre[g / kSuperGroups] + wave_sum(v);
+}
+
+/* Word offset of chunk c in the packed payload, from its group's exclusive prefix plus the
+ * chunks before c in its group; the loads are issued together, then summed. */
 template <int CPG>
 __device__ __forceinline__ uint32_t chunk_offset(const uint32_t *gpre, const uint32_t *per_chunk,
                                                  uint32_t c) {

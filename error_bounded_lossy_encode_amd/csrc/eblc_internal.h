@@ -9,7 +9,9 @@
  *   decompress: tile  = 256 values, 4 consecutive values per lane, a segment is 8 lanes
  *               chunk = 8 tiles = 2048 values = 64 segments; one wave owns one chunk
  *               group = 4 chunks = one 256-thread workgroup
- * Both groups hold 8192 values; the device-wide scans run over groups.  The chunk coder keeps
+ * Both groups hold 8192 values; the device-wide scans run over groups (compress: it writes one
+ * prefix per super-group of 64 groups, and a group adds the sums of the groups before it in its
+ * super-group).  The chunk coder keeps
  * the encode chunks and groups (its coder chunks of V values fill whole encode chunks, or two)
  * and decodes one coder chunk per wave, four per group.  The Lorenzo block B is a multiple
  * of 32 up to 1024, or 2048.  A power of two starts every chunk; any other block may start
@@ -47,6 +49,7 @@ constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
 constexpr int kDecChunksPerGroup = kWavesPerBlock;
 constexpr int kEscStage = 64;                    /* escapes staged per encode chunk */
+constexpr int kSuperGroups = 64;                /* groups per super-group of the device-wide scans */
 constexpr int kScanThreads = 1024;
 constexpr int kScanItems = 16;                   /* items per scan thread per round */
 constexpr int kRangeThreads = 256;
@@ -132,8 +135,10 @@ struct Workspace {
     uint32_t *chunk_tmask;   /* [nchunks] bit t set if tile t of the encode chunk has an escape */
     uint32_t *group_words;   /* [ngroups] */
     uint32_t *group_esc;     /* [ngroups] */
-    uint32_t *gpre_words;    /* [ngroups] exclusive prefix */
-    uint32_t *gpre_esc;      /* [ngroups] exclusive prefix */
+    uint32_t *gpre_words;    /* compress: [nsuper] exclusive prefix of the words of each super-group of
+                                kSuperGroups groups (a group adds the sums of its super-group's groups
+                                before it); decompress: [ngroups] exclusive prefix of each group's words */
+    uint32_t *gpre_esc;      /* compress: [nsuper] the same for the escapes */
     uint32_t *emask;         /* [nchunks * kEncSegs] escape bitmask per segment (chunks with more
                                 than kEscStage escapes, tiles with escapes) */
     uint32_t *stage_idx;     /* [nchunks * kEscStage] first escapes of each chunk: index ... */

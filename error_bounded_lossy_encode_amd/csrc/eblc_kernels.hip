@@ -781,10 +781,13 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(Fields fs, PlanArgs
  * totals in tot[0], tot[1] (valid in every thread).  Each round covers kScanThreads *
  * kScanItems items: a thread loads 16 consecutive items with 128-bit loads (the arrays are
  * 256-byte aligned), sums them, the sums are scanned across the wave with DPP and across the
- * 16 waves through LDS, and the thread writes its 16 exclusive prefixes back. */
+ * 16 waves through LDS, and the thread writes its 16 exclusive prefixes back -- or, SUPER, only
+ * the prefix of every kSuperGroups-th item, at index item / kSuperGroups. */
+template <bool SUPER>
 __device__ void block_scan2(const uint32_t *__restrict__ a, const uint32_t *__restrict__ b,
                             uint32_t *__restrict__ pa_out, uint32_t *__restrict__ pb_out,
                             uint32_t ng, uint32_t *tot) {
+    static_assert(kSuperGroups % kScanItems == 0, "a thread's items lie in one super-group");
     constexpr int kWaves = kScanThreads / kWave;
     constexpr int kV = kScanItems / 4;
     __shared__ uint32_t s_wa[kWaves], s_wb[kWaves];
@@ -837,7 +840,12 @@ __device__ void block_scan2(const uint32_t *__restrict__ a, const uint32_t *__re
             ea += va[k];
             eb += vb[k];
         }
-        if (i0 + kScanItems <= ng) {
+        if (SUPER) {
+            if (i0 < ng && (i0 % kSuperGroups) == 0) {
+                pa_out[i0 / kSuperGroups] = pa[0];
+                if (pb_out != nullptr) pb_out[i0 / kSuperGroups] = pb[0];
+            }
+        } else if (i0 + kScanItems <= ng) {
 #pragma unroll
             for (int k = 0; k < kV; ++k) {
                 reinterpret_cast<uint4 *>(pa_out + i0)[k] = make_uint4(pa[4 * k], pa[4 * k + 1], pa[4 * k + 2], pa[4 * k + 3]);
@@ -872,7 +880,7 @@ __device__ __forceinline__ void scan_compress_body(PlanArgs pa, Workspace ws,
     const uint32_t valid0 = info->valid;
     const float eb0 = info->eb_f, s0 = info->s, r0 = info->r;
     uint32_t tot[2];
-    block_scan2(ws.group_words, ws.group_esc, ws.gpre_words, ws.gpre_esc, pa.ngroups, tot);
+    block_scan2<true>(ws.group_words, ws.group_esc, ws.gpre_words, ws.gpre_esc, pa.ngroups, tot);
     if (threadIdx.x == 0) {
         const uint64_t n = pa.n;
         const uint64_t S = tot[0], m = tot[1];
@@ -1196,7 +1204,8 @@ __device__ __forceinline__ void compact_body(const float *__restrict__ x,
         words[k] = ck < pa.nchunks ? ws.chunk_words[ck] : 0u;
         escs[k] = ck < pa.nchunks ? ws.chunk_esc[ck] : 0u;
     }
-    const uint32_t gw = ws.gpre_words[grp], ge = ws.gpre_esc[grp];
+    const uint32_t gw = group_prefix(ws.gpre_words, ws.group_words, grp);
+    const uint32_t ge = group_prefix(ws.gpre_esc, ws.group_esc, grp);
     const uint32_t fits = info->fits, mode = info->mode;
     const uint64_t payload_off = info->payload_off, oidx_off = info->oidx_off, oval_off = info->oval_off;
     const uint64_t m = info->m, payload_words = info->payload_words;
@@ -1425,7 +1434,7 @@ __device__ __forceinline__ void scan_decompress_body(const uint8_t *__restrict__
     __shared__ uint32_t s_h[32];
     if (threadIdx.x < 32) s_h[threadIdx.x] = reinterpret_cast<const uint32_t *>(in)[threadIdx.x];
     uint32_t tot[2];
-    block_scan2(ws.group_words, nullptr, ws.gpre_words, nullptr, pa.dgroups, tot);
+    block_scan2<false>(ws.group_words, nullptr, ws.gpre_words, nullptr, pa.dgroups, tot);
     if (threadIdx.x != 0) return;
     DevInfo *info = ws.info;
     uint32_t hw[32];
