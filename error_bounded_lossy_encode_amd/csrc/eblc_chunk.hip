@@ -9,43 +9,44 @@
  * nonzero words in order).  The scan, compaction and outlier kernels of the bitpack coder
  * serve this coder unchanged; only the scratch slot stride and the size section differ.
  *
- * gfx950 mapping.  A tile is 64 consecutive values, one per lane.  Bitshuffle is a 32 x 32 bit
- * transpose inside each half-wave (five butterfly stages: ds_swizzle or DPP for the partner
- * lane, v_alignbit for the rotate, v_bfi for the merge), after which lane 32 h + b holds the
- * plane-b word of the tile's group h: one LDS store per lane per tile puts it at its plane-major
- * place.  LDS planes are padded by two words so those stores and the plane reads of RZE are
- * free of bank conflicts.  RZE walks only the planes below the chunk's highest code bit: a
- * ballot per 64 words gives two bitmap words, and mbcnt the compacted position.  Decoding runs
- * the same steps backwards; the transpose is its own inverse.
+ * gfx950 mapping.  Lane L of a wave owns group L of the wave's 2048 values (values 32 L .. 32 L
+ * + 31), so every step but RZE runs inside the lane, on its registers:
+ *  - the field arrives by coalesced 128-bit loads and passes through LDS, where group L's eight
+ *    16-byte quads sit in slots 8 L .. 8 L + 7 with the quad index XORed by (L ^ L / 8) mod 8:
+ *    the coalesced writes and each lane's reads of its own quads then hit distinct banks;
+ *  - Quant and Diff run over the lane's 32 values; the first value's predecessor is the last
+ *    code of the lane to the left (one DPP move);
+ *  - Bitshuffle is the transpose of the lane's 32 x 32 bit matrix: five stages of block swaps
+ *    between register pairs (v_perm_b32 for the 16- and 8-bit blocks, a shift and v_bfi_b32
+ *    for the 4-, 2- and 1-bit ones), after which register b holds the group's plane-b word;
+ *  - the zigzag fold is applied to planes: plane 0 of the folded codes is the sign plane of the
+ *    differences and plane b >= 1 is their plane b - 1 XOR the sign plane, one XOR per plane
+ *    instead of three operations per code;
+ *  - RZE walks the planes: a ballot of the wave's nonzero words gives the plane's bitmap bits,
+ *    and mbcnt the place of each nonzero word.
+ * A 1024-value chunk is half a wave; a 4096-value chunk spans two waves of a workgroup, which
+ * trade their per-plane word counts through LDS.  Decoding runs the steps backwards (the
+ * transpose is its own inverse): scalar loads read the bitmap plane by plane, each lane loads
+ * its group's nonzero words under it, unfolds the zigzag on planes, transposes, and sums its
+ * differences after a wave scan of the lane totals; the values go back through LDS in the same
+ * swizzled order for coalesced stores.
  */
 #include "eblc_device.h"
+
+#include <utility>
 
 namespace eblc {
 namespace {
 
-constexpr int kCTile = 64;                     /* values per tile: one per lane */
-constexpr int kCTilesPerWave = kEncChunk / kCTile;
+constexpr int kWaveQuads = kEncChunk / 4;      /* 16-byte quads of a wave's 2048 values */
+constexpr int kLaneQuads = kWaveQuads / kWave;  /* quads per lane in a coalesced pass */
 
 template <int V>
 struct ChunkGeom {
     static constexpr int G = V / 32;            /* groups of 32 codes = words per bit plane */
-    static constexpr int PS = G + 2;            /* LDS words per plane (2 words of padding) */
-    static constexpr int LDSW = 32 * PS;        /* LDS words of one chunk's planes */
     static constexpr int BM = V / 32;           /* bitmap words of RZE */
-    static constexpr int BATCHES = (G + 63) / 64; /* 64-word batches per plane */
-    static constexpr int WAVES = V > kEncChunk ? V / kEncChunk : 1;      /* encode waves per chunk */
-    static constexpr int PER_WAVE = V < kEncChunk ? kEncChunk / V : 1;   /* chunks per encode wave */
-    static constexpr int TILES = V / kCTile;
-    /* The decoder's LDS: 1024-value chunks are decoded from their words as staged (RAW: up to
-     * BM + V words from a 16-byte unit boundary, 3 words before and 3 after, then the bitmap's
-     * popcount prefix); 2048-value chunks from their rebuilt planes; 4096-value chunks from
-     * the rebuilt planes of half a chunk at a time (HALVES). */
-    static constexpr bool RAW = V == 1024;
-    static constexpr bool HALVES = V == 4096;
-    static constexpr int PSH = 64 + 2;          /* LDS words per plane of a half */
-    static constexpr int RAWW = 4 * ((3 + BM + V + 3) / 4);
-    static constexpr int DEC_LDSW = RAW ? RAWW + BM : HALVES ? 32 * PSH : LDSW; /* per wave */
-    static_assert(DEC_LDSW % 4 == 0, "whole 16-byte units");
+    static constexpr int WAVES = V > kEncChunk ? V / kEncChunk : 1;      /* waves per chunk */
+    static constexpr int PER_WAVE = V < kEncChunk ? kEncChunk / V : 1;   /* chunks per wave */
     static_assert(V == 1024 || V == 2048 || V == 4096, "chunk of 4, 8 or 16 KiB");
     static_assert(PER_WAVE * (BM + V) <= WAVES * (kEncChunk + kEncChunk / 32), "scratch slots of 2112 words");
 };
@@ -54,200 +55,351 @@ __device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-/* old with lane `at` (wave-uniform) replaced by the wave-uniform value v. */
-__device__ __forceinline__ uint32_t writelane(uint32_t old, uint32_t v, uint32_t at) {
-    return (threadIdx.x & 63u) == at ? v : old;
+/* old with lane AT replaced by the wave-uniform value v (one v_writelane_b32; its lane select is
+ * an immediate, as a second scalar operand would break the one-scalar-read limit).  v goes
+ * through readfirstlane, which is free for a value in an SGPR and otherwise makes sure the asm
+ * gets one: the compiler may keep a copy of a uniform value in a VGPR. */
+template <int AT>
+__device__ __forceinline__ uint32_t writelane(uint32_t old, uint32_t v) {
+    asm("v_writelane_b32 %0, %1, %2" : "+v"(old) : "s"(__builtin_amdgcn_readfirstlane(v)), "n"(AT));
+    return old;
 }
 
-/* OR over all 64 lanes (DPP inside rows, then the four rows' lanes 0, 16, 32 and 48). */
-__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-    v |= dpp<kDppQuadXor1>(0, v);
-    v |= dpp<kDppQuadXor2>(0, v);
-    v |= dpp<kDppRowHalfMirror>(0, v);
-    v |= dpp<kDppRowMirror>(0, v);
-    return readlane(v, 0) | readlane(v, 16) | readlane(v, 32) | readlane(v, 48);
+using Planes = std::make_integer_sequence<int, 32>;
+
+/* LDS slot (16 bytes) of quad g of a wave's 2048 values: group L = g / 8 keeps slots 8 L ..
+ * 8 L + 7 with the quad's index in its group XORed by (L ^ L / 8) mod 8.  Eight lanes reading
+ * quad j of their eight groups, and sixteen lanes writing 16 consecutive quads, then touch 128
+ * (256) distinct bytes modulo the bank width.  For g = 64 k + l (k < 8) the slot is 64 k +
+ * (quad_slot(l) ^ k), and for g = 8 L + j it is quad_slot(8 L) ^ j. */
+__device__ __forceinline__ uint32_t quad_slot(uint32_t g) {
+    const uint32_t L = g >> 3;
+    return (g & ~7u) | ((g ^ L ^ (L >> 3)) & 7u);
 }
 
-/* 32 x 32 bit transpose inside each half-wave: on exit bit j of lane 32 h + b is bit b of lane
- * 32 h + j's word on entry.  Five butterfly stages s = 16, 8, 4, 2, 1 pair lane l with l ^ s;
- * the lower lane of a pair keeps its bits whose index has bit s clear and takes its partner's
- * such bits shifted up by s, the upper lane keeps the others and takes its partner's shifted
- * down.  For s = 16 and 8 both are byte moves, one v_perm_b32 each (selector bytes 0-3 pick
- * the partner's bytes, 4-7 the lane's own); for s = 4, 2, 1 the partner's word is rotated by
- * s (v_alignbit) and merged under the stage mask (v_bfi). */
-struct Transpose {
-    uint32_t sel16, sel8, keep[3], rot[3];
-    __device__ __forceinline__ explicit Transpose(uint32_t lane) {
-        sel16 = (lane & 16u) ? 0x07060302u : 0x01000504u;
-        sel8 = (lane & 8u) ? 0x07030501u : 0x02060004u;
-        const uint32_t m[3] = {0x0F0F0F0Fu, 0x33333333u, 0x55555555u};
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+
+/* One stage of the transpose: for every register pair (k, k + J), k without bit J, the bits of
+ * k whose index has bit J set trade places with the bits of k + J whose index has it clear. */
+template <int J>
+__device__ __forceinline__ void swap_stage(uint32_t w[32], uint32_t m) {
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            const uint32_t sh = 4u >> k;
-            const bool lower = (lane & sh) == 0;
-            keep[k] = lower ? m[k] : ~m[k];
-            rot[k] = lower ? 32u - sh : sh;
-        }
+    for (int k = 0; k < 32; ++k) {
+        if (k & J) continue;
+        const uint32_t a = w[k], b = w[k + J];
+        w[k] = bfi(m, a, b << J);
+        w[k + J] = bfi(m, a >> J, b);
     }
-    /* bits of a under m, of b elsewhere (one v_bfi_b32) */
-    static __device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
-        return b ^ ((a ^ b) & m);
-    }
-    __device__ __forceinline__ uint32_t operator()(uint32_t v) const {
-        uint32_t p;
-        p = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F); /* lane ^ 16 */
-        v = __builtin_amdgcn_perm(v, p, sel16);
-        p = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x201F); /* lane ^ 8 */
-        v = __builtin_amdgcn_perm(v, p, sel8);
-        p = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F); /* lane ^ 4 */
-        v = bfi(keep[0], v, __builtin_amdgcn_alignbit(p, p, rot[0]));
-        p = dpp<kDppQuadXor2>(0, v);                                /* lane ^ 2 */
-        v = bfi(keep[1], v, __builtin_amdgcn_alignbit(p, p, rot[1]));
-        p = dpp<kDppQuadXor1>(0, v);                                /* lane ^ 1 */
-        v = bfi(keep[2], v, __builtin_amdgcn_alignbit(p, p, rot[2]));
-        return v;
-    }
-};
-
-/* q minus the code of the lane to the left (lane 0: carry).  The subtraction must stay apart
- * from the DPP move: where carry is known to be 0 the compiler folds the pair into one
- * v_subrev_u32_dpp (wave_shr, bound_ctrl), and on gfx950 that returned the negated difference.
- * The empty asm hides the moved value from that fold and emits nothing. */
-__device__ __forceinline__ int32_t diff_left(int32_t q, int32_t carry) {
-    uint32_t prev = dpp<kDppWaveShr1>((uint32_t)carry, (uint32_t)q);
-    asm("" : "+v"(prev));
-    return q - (int32_t)prev;
 }
 
-__device__ __forceinline__ float ld_nt_f(const float *p) { return __builtin_nontemporal_load(p); }
-__device__ __forceinline__ void st_nt_f(float *p, float v) { __builtin_nontemporal_store(v, p); }
+/* 32 x 32 bit transpose in place: on exit bit i of w[b] is bit b of w[i] on entry. */
+__device__ __forceinline__ void transpose32(uint32_t w[32]) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) { /* 16-bit blocks: (a.lo, b.lo) and (a.hi, b.hi) */
+        const uint32_t a = w[k], b = w[k + 16];
+        w[k] = __builtin_amdgcn_perm(b, a, 0x05040100u);
+        w[k + 16] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) { /* bytes: (a0, b0, a2, b2) and (a1, b1, a3, b3) */
+        if (k & 8) continue;
+        const uint32_t a = w[k], b = w[k + 8];
+        w[k] = __builtin_amdgcn_perm(b, a, 0x06020400u);
+        w[k + 8] = __builtin_amdgcn_perm(b, a, 0x07030501u);
+    }
+    swap_stage<4>(w, 0x0F0F0F0Fu);
+    swap_stage<2>(w, 0x33333333u);
+    swap_stage<1>(w, 0x55555555u);
+}
+
+/* The lane's group leaves LDS as 32 values in order; sx is the wave's 2048-value staging. */
+__device__ __forceinline__ void read_group(const uint4 *sx, uint32_t v[32]) {
+    const uint32_t s0 = quad_slot(8u * (threadIdx.x & 63));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint4 u = sx[s0 ^ (uint32_t)j];
+        v[4 * j] = u.x;
+        v[4 * j + 1] = u.y;
+        v[4 * j + 2] = u.z;
+        v[4 * j + 3] = u.w;
+    }
+}
+
+/* Word i of p, i < 2^30: the byte offset is formed in 32 bits, so the load takes the pointer in
+ * SGPRs and one VGPR offset. */
+__device__ __forceinline__ uint32_t word_at(const uint32_t *p, uint32_t i) {
+    return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(p) + 4u * i);
+}
+
+__device__ __forceinline__ uint32_t lds_value(const uint4 *sx, uint32_t v) {
+    return reinterpret_cast<const uint32_t *>(sx)[4u * quad_slot(v >> 2) + (v & 3u)];
+}
 
 /* ---- K2c: chunk encode ------------------------------------------------------------------------ */
 
-/* Escape bookkeeping of one encode chunk, kept as in the bitpack encoder: the count, a bit per
- * 256-value tile with an escape, and (lane l) the escape bitmask of 32-value segment l. */
-struct ChunkEsc {
-    uint32_t escs = 0, tmask = 0, emask = 0;
-};
-
-/* Phase 1 of the chunk encoder for one wave's 2048 values: per 64-value tile quantize, take
- * the first difference (the carry supplies lane 0's predecessor: the previous tile's last code,
- * 0 at a chunk's first value), zigzag, OR into the chunk's code OR, transpose, and store the
- * 64 plane words at their plane-major LDS places.  FULL: all 2048 values lie below n. */
-template <int V, bool FULL, bool STRIDED>
-__device__ __forceinline__ void encode_tiles(const float *__restrict__ x, const Layout &lo, uint64_t cbase,
-                                             uint64_t n, const QParams &qp, int32_t carry, uint32_t wave,
-                                             uint32_t (*s_words)[ChunkGeom<V>::LDSW], uint32_t *stage_idx,
-                                             uint32_t *stage_val, uint32_t orz[ChunkGeom<V>::PER_WAVE],
-                                             ChunkEsc &es) {
-    using Gm = ChunkGeom<V>;
+/* The wave's 2048 values from value cbase on (0 from n on) into LDS.  FULL: all below n. */
+template <bool FULL, bool STRIDED>
+__device__ __forceinline__ void stage_values(const float *__restrict__ x, const Layout &lo, uint64_t cbase,
+                                             uint64_t n, uint4 *sx) {
     const uint32_t lane = threadIdx.x & 63;
-    const uint32_t h = lane >> 5, b = lane & 31;
-    const Transpose tr(lane);
-    float xs[kCTilesPerWave];
+    if (FULL) {
+        float4 v[kLaneQuads];
 #pragma unroll
-    for (int t = 0; t < kCTilesPerWave; ++t) {
-        const uint64_t i = cbase + (uint64_t)t * kCTile + lane;
-        if (FULL) xs[t] = ld_nt_f(x + elem_off<STRIDED>(lo, i));
-        else xs[t] = i < n ? x[elem_off<STRIDED>(lo, i)] : 0.0f;
-    }
+        for (int k = 0; k < kLaneQuads; ++k) v[k] = load4<STRIDED>(x, lo, cbase + 4u * (kWave * k + lane));
+        const uint32_t s0 = quad_slot(lane);
 #pragma unroll
-    for (int t = 0; t < kCTilesPerWave; ++t) {
-        const float xv = xs[t];
-        /* Quant: the bitpack encoder's fast test (exactly the full rule's acceptance), the full
-         * rule in a wave where some lane misses it */
-        const float q0f = rintf(xv * qp.r);
-        const bool fast = (fabsf(xv - q0f * qp.s) <= qp.eb) && (fabsf(q0f) < qp.tlim);
-        int32_t q = (int32_t)q0f;
-        if (__ballot(!fast)) {
-            uint32_t e = 0;
-            if (!fast) q = quantize_slow(xv, q0f, qp, &e);
-            const uint64_t M = __ballot(e != 0);
-            if (M) {
-                es.emask = writelane(es.emask, (uint32_t)M, 2u * t);
-                es.emask = writelane(es.emask, (uint32_t)(M >> 32), 2u * t + 1u);
-                es.tmask |= 1u << (t / 4);
-                const uint32_t r = es.escs + mbcnt64(M);
-                if (e && r < (uint32_t)kEscStage) {
-                    stage_idx[r] = (uint32_t)(cbase + (uint64_t)t * kCTile + lane);
-                    stage_val[r] = __float_as_uint(xv);
-                }
-                es.escs += (uint32_t)__popcll(M);
-            }
+        for (int k = 0; k < kLaneQuads; ++k)
+            sx[kWave * k + (s0 ^ (uint32_t)k)] = make_uint4(__float_as_uint(v[k].x), __float_as_uint(v[k].y),
+                                                            __float_as_uint(v[k].z), __float_as_uint(v[k].w));
+    } else {
+        uint32_t *sw = reinterpret_cast<uint32_t *>(sx);
+#pragma unroll 4
+        for (int k = 0; k < kEncChunk / kWave; ++k) {
+            const uint32_t v = kWave * k + lane;
+            const uint64_t i = cbase + v;
+            const float xv = i < n ? x[elem_off<STRIDED>(lo, i)] : 0.0f;
+            sw[4u * quad_slot(v >> 2) + (v & 3u)] = __float_as_uint(xv);
         }
-        /* Diff: lane 0 takes the carry (0 at a chunk start), the others their left neighbour */
-        if (t > 0 && (t * kCTile) % V == 0) carry = 0;
-        uint32_t z = zigzag(diff_left(q, carry));
-        carry = (int32_t)readlane((uint32_t)q, 63);
-        if (!FULL && cbase + (uint64_t)t * kCTile + lane >= n) z = 0; /* padding codes */
-        orz[(t * kCTile) / V] |= z;
-        /* Bitshuffle: lane 32 h + b -> plane b of group (off mod V) / 32 + h */
-        const uint32_t wd = tr(z);
-        const uint32_t off = wave * kEncChunk + (uint32_t)t * kCTile; /* value offset in the group */
-        s_words[off / V][b * Gm::PS + (off & (uint32_t)(V - 1)) / 32u + h] = wd;
     }
+    wave_lds_sync();
 }
 
-/* RZE of one chunk from its LDS planes into dst: the bitmap (V / 32 words; bit k of word k / 32
- * set when plane word k is nonzero), then the nonzero words in order.  Planes at and above wmax
- * are zero and skipped.  Returns the chunk's word count. */
-template <int V>
-__device__ __forceinline__ uint32_t rze_chunk(const uint32_t *pl, uint32_t wmax, uint32_t *dst) {
-    using Gm = ChunkGeom<V>;
-    const uint32_t lane = threadIdx.x & 63;
-    uint32_t bm0 = 0, bm1 = 0; /* lane l: bitmap word l (and 64 + l) */
-    uint32_t run = 0;
-    for (uint32_t pb = 0; pb < wmax; ++pb) {
+/* Quant of the lane's group: q[i] is value i's code (0 if it escapes); returns the escape
+ * bitmask (bit i: value i).  The fast test is the full rule's first acceptance exactly (the
+ * bitpack encoder states why); the full rule runs only in a wave where a lane misses it, on
+ * values read again from LDS so that the first pass keeps no copy of them. */
+__device__ __forceinline__ uint32_t quantize_group(const uint4 *sx, const QParams &qp, int32_t q[32]) {
+    uint32_t xv[32];
+    read_group(sx, xv);
+    bool fast = true;
+    float qabs = 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < Gm::BATCHES; ++kk) {
-            const uint32_t gi = 64u * kk + lane;
-            const uint32_t word = (Gm::G >= 64 || gi < (uint32_t)Gm::G) ? pl[pb * Gm::PS + gi] : 0u;
-            const uint64_t M = __ballot(word != 0);
-            if (word) dst[Gm::BM + run + mbcnt64(M)] = word;
-            run += (uint32_t)__popcll(M);
-            const uint32_t wi = (pb * Gm::G + 64u * kk) / 32u;
-            if (wi < 64) bm0 = writelane(bm0, (uint32_t)M, wi);
-            else bm1 = writelane(bm1, (uint32_t)M, wi - 64);
-            if (Gm::G >= 64) {
-                if (wi + 1 < 64) bm0 = writelane(bm0, (uint32_t)(M >> 32), wi + 1);
-                else bm1 = writelane(bm1, (uint32_t)(M >> 32), wi + 1 - 64);
+    for (int i = 0; i < 32; ++i) {
+        const float x = __uint_as_float(xv[i]);
+        const float q0f = rintf(x * qp.r);
+        fast = fast && (fabsf(x - q0f * qp.s) <= qp.eb);
+        qabs = fmaxf(qabs, fabsf(q0f));
+        q[i] = (int32_t)q0f;
+    }
+    fast = fast && (qabs < qp.tlim);
+    uint32_t emask = 0;
+    if (__ballot(!fast)) {
+        wave_lds_sync();
+        read_group(sx, xv);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const float x = __uint_as_float(xv[i]);
+            const float q0f = rintf(x * qp.r);
+            if (!((fabsf(x - q0f * qp.s) <= qp.eb) && (fabsf(q0f) < qp.tlim))) {
+                uint32_t e;
+                q[i] = quantize_slow(x, q0f, qp, &e);
+                emask |= e << i;
             }
         }
     }
-    if (lane < (uint32_t)(Gm::BM < 64 ? Gm::BM : 64)) dst[lane] = bm0;
-    if (Gm::BM > 64) dst[64 + lane] = bm1;
-    return Gm::BM + run;
+    return emask;
 }
 
-/* Workgroup of 4 waves over 8192 values; wave w owns the 2048 values of encode chunk c (the
- * unit of the escape bookkeeping and of the scratch slots the compaction copies), which hold
- * 2048 / V coder chunks, or half of one when V = 4096.  Phase 1 (every wave): encode_tiles.
- * Phase 2 (after a barrier; the wave owning a chunk's first values): RZE of the chunk into the
- * scratch slot and its word count into the size section (stream or staging).  A wave's chunks
- * lie back to back in its slot, and a 4096-value chunk fills the slots of both its waves (the
- * second reports 0 words), so the compaction's copy of each slot in order yields the chunks in
- * order. */
+/* The chunk's first kEscStage escapes, in index order, into the staging of encode chunk c, and
+ * the escape count and tile mask (bit t: some value of 256-value tile t escapes). */
+__device__ __forceinline__ void stage_escapes(const uint4 *sx, uint32_t emask, uint64_t cbase, uint32_t c,
+                                              const Workspace &ws, uint32_t &escs, uint32_t &tmask) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t cnt = (uint32_t)__popc(emask);
+    const uint32_t incl = wave_incl_scan(cnt);
+    escs = readlane(incl, 63);
+    uint32_t r = incl - cnt;
+    uint32_t m = emask;
+    while (m && r < (uint32_t)kEscStage) {
+        const uint32_t i = (uint32_t)__builtin_ctz(m);
+        const uint32_t v = 32u * lane + i;
+        ws.stage_idx[(uint64_t)c * kEscStage + r] = (uint32_t)(cbase + v);
+        ws.stage_val[(uint64_t)c * kEscStage + r] = lds_value(sx, v);
+        ++r;
+        m &= m - 1;
+    }
+    const uint64_t E = __ballot(emask != 0);
+    tmask = 0;
+#pragma unroll
+    for (int t = 0; t < kEncChunk / kEncTile; ++t)
+        if ((E >> (kSegsPerEncTile * t)) & ((1u << kSegsPerEncTile) - 1u)) tmask |= 1u << t;
+}
+
+/* Diff of the lane's codes into w: the first value's predecessor is the last code of the lane to
+ * the left, `carry` for lane 0 (and 0 for lane 32 when it starts a 1024-value chunk).  Values at
+ * and after n (FULL: none) get difference 0, the padding codes.  The subtraction of the moved
+ * code stays apart from the DPP move: where carry is known to be 0 the compiler folds the pair
+ * into one v_subrev_u32_dpp (wave_shr, bound_ctrl), and on gfx950 that returned the negated
+ * difference.  The empty asm hides the moved value from that fold and emits nothing. */
+template <int V, bool FULL>
+__device__ __forceinline__ void diff_group(const int32_t q[32], uint32_t carry, uint64_t gbase, uint64_t n,
+                                           uint32_t w[32]) {
+    uint32_t prev = dpp<kDppWaveShr1>(carry, (uint32_t)q[31]);
+    asm("" : "+v"(prev));
+    if (V < kEncChunk && (threadIdx.x & 63) == 32) prev = 0;
+#pragma unroll
+    for (int i = 31; i > 0; --i) w[i] = (uint32_t)q[i] - (uint32_t)q[i - 1];
+    w[0] = (uint32_t)q[0] - prev;
+    if (!FULL) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            if (gbase + (uint64_t)i >= n) w[i] = 0;
+    }
+}
+
+/* Zigzag fold of the codes whose planes w holds, applied to the planes. */
+__device__ __forceinline__ void zigzag_planes(uint32_t w[32]) {
+    const uint32_t sgn = w[31];
+#pragma unroll
+    for (int b = 31; b > 0; --b) w[b] = w[b - 1] ^ sgn;
+    w[0] = sgn;
+}
+
+/* Its inverse. */
+__device__ __forceinline__ void unzigzag_planes(uint32_t w[32]) {
+    const uint32_t sgn = w[0];
+#pragma unroll
+    for (int b = 0; b < 31; ++b) w[b] = w[b + 1] ^ sgn;
+    w[31] = sgn;
+}
+
+/* RZE, plane by plane.  Plane B's words are the wave's w[B]; M = ballot(w[B] != 0).  A plane
+ * with no nonzero word only has its (zero) bitmap bits. */
+
+/* A 2048-value chunk (the wave's 64 groups): bitmap words 2 B, 2 B + 1 are M's halves. */
+template <int B>
+__device__ __forceinline__ void rze_wave_plane(const uint32_t w[32], uint32_t *__restrict__ dst, uint32_t &bm,
+                                               uint32_t &run) {
+    constexpr uint32_t BM = ChunkGeom<2048>::BM;
+    const uint64_t M = __ballot(w[B] != 0);
+    if (M) {
+        if (w[B] != 0) dst[BM + run + mbcnt64(M)] = w[B];
+        run += (uint32_t)__popcll(M);
+        bm = writelane<2 * B>(bm, (uint32_t)M);
+        bm = writelane<2 * B + 1>(bm, (uint32_t)(M >> 32));
+    }
+}
+
+/* Returns the chunk's word count. */
+template <int... B>
+__device__ __forceinline__ uint32_t rze_wave(std::integer_sequence<int, B...>, const uint32_t w[32],
+                                             uint32_t *__restrict__ dst) {
+    uint32_t bm = 0, run = 0;
+    (rze_wave_plane<B>(w, dst, bm, run), ...);
+    dst[threadIdx.x & 63] = bm;
+    return ChunkGeom<2048>::BM + run;
+}
+
+/* Two 1024-value chunks, A in lanes 0-31 and B in lanes 32-63, back to back (B from word sizeA
+ * on): bitmap word B of each is its half of M. */
+template <int B>
+__device__ __forceinline__ void rze_halves_plane(const uint32_t w[32], uint32_t sizeA, uint32_t *__restrict__ dst,
+                                                 uint32_t &bm, uint32_t &rA, uint32_t &rB) {
+    constexpr uint32_t BM = ChunkGeom<1024>::BM;
+    const uint64_t M = __ballot(w[B] != 0);
+    if (M) {
+        const uint32_t lo = (uint32_t)M, hi = (uint32_t)(M >> 32);
+        if (w[B] != 0) {
+            const uint32_t pos = (threadIdx.x & 32) ? sizeA + BM + rB + __builtin_amdgcn_mbcnt_hi(hi, 0u)
+                                                    : BM + rA + __builtin_amdgcn_mbcnt_lo(lo, 0u);
+            dst[pos] = w[B];
+        }
+        rA += (uint32_t)__popc(lo);
+        rB += (uint32_t)__popc(hi);
+        bm = writelane<B>(bm, lo);
+        bm = writelane<32 + B>(bm, hi);
+    }
+}
+
+/* Chunk B is present when hasB; the word counts go to sizes[0..1]. */
+template <int... B>
+__device__ __forceinline__ void rze_halves(std::integer_sequence<int, B...>, const uint32_t w[32], bool hasB,
+                                           uint32_t *__restrict__ dst, uint32_t sizes[2]) {
+    constexpr uint32_t BM = ChunkGeom<1024>::BM;
+    const uint32_t lane = threadIdx.x & 63;
+    uint32_t ra = 0;
+#pragma unroll
+    for (int b = 0; b < 32; ++b) ra += (uint32_t)__popc((uint32_t)__ballot(w[b] != 0));
+    const uint32_t sizeA = BM + ra;
+    uint32_t rA = 0, rB = 0, bm = 0;
+    (rze_halves_plane<B>(w, sizeA, dst, bm, rA, rB), ...);
+    if (lane < 32 || hasB) dst[lane < 32 ? lane : sizeA + lane - 32u] = bm;
+    sizes[0] = sizeA;
+    sizes[1] = hasB ? BM + rB : 0u;
+}
+
+/* A 4096-value chunk whose groups 64 p .. 64 p + 63 this wave holds: bitmap words 4 B + 2 p,
+ * 4 B + 2 p + 1 are M's halves, and the wave's words of plane B follow the partner's when p = 1.
+ * base (lane B) is the number of the chunk's words before them. */
+template <int B>
+__device__ __forceinline__ void rze_pair_plane(const uint32_t w[32], uint32_t base, uint32_t *__restrict__ dst,
+                                               uint32_t &bm) {
+    constexpr uint32_t BM = ChunkGeom<4096>::BM;
+    const uint64_t M = __ballot(w[B] != 0);
+    if (M) {
+        const uint32_t pb = readlane(base, B);
+        if (w[B] != 0) dst[BM + pb + mbcnt64(M)] = w[B];
+        bm = writelane<2 * B>(bm, (uint32_t)M);
+        bm = writelane<2 * B + 1>(bm, (uint32_t)(M >> 32));
+    }
+}
+
+template <int B>
+__device__ __forceinline__ void plane_count(const uint32_t w[32], uint32_t &cnt) {
+    cnt = writelane<B>(cnt, (uint32_t)__popcll(__ballot(w[B] != 0)));
+}
+
+/* p: the wave's parity; the partner (wave ^ 1 of the workgroup) holds the chunk's other half.
+ * The waves trade per-plane word counts through their LDS stagings (xs: this wave's, xp: the
+ * partner's), so both must make the call.  Writes when `live`; returns the chunk's word count
+ * for p = 0, else 0. */
+template <int... B>
+__device__ __forceinline__ uint32_t rze_pair(std::integer_sequence<int, B...>, const uint32_t w[32], uint32_t p,
+                                             bool live, uint32_t *xs, const uint32_t *xp,
+                                             uint32_t *__restrict__ dst) {
+    constexpr uint32_t BM = ChunkGeom<4096>::BM;
+    const uint32_t lane = threadIdx.x & 63;
+    uint32_t cnt = 0; /* lane b: this wave's nonzero words of plane b */
+    (plane_count<B>(w, cnt), ...);
+    wave_lds_sync();
+    if (lane < 32) xs[lane] = cnt;
+    __syncthreads();
+    const uint32_t other = lane < 32 ? xp[lane] : 0u;
+    const uint32_t c0 = p ? other : cnt;
+    const uint32_t tot = cnt + other;
+    const uint32_t incl = wave_incl_scan(tot);
+    const uint32_t base = incl - tot + (p ? c0 : 0u);
+    const uint32_t total = BM + readlane(incl, 63);
+    if (!live) return 0;
+    uint32_t bm = 0;
+    (rze_pair_plane<B>(w, base, dst, bm), ...);
+    dst[4u * (lane >> 1) + 2u * p + (lane & 1u)] = bm;
+    return p ? 0u : total;
+}
+
+/* Workgroup of 4 waves over 8192 values; wave w owns the 2048 values of encode chunk c (the unit
+ * of the escape bookkeeping and of the scratch slots the compaction copies), which hold 2048 / V
+ * coder chunks, or half of one when V = 4096.  A wave's chunks lie back to back in its slot, and
+ * a 4096-value chunk fills the slots of both its waves from the first one's (the second reports 0
+ * words), so the compaction's copy of each slot in order yields the chunks in order.  The LDS is
+ * the four waves' 8 KiB stagings and nothing else (32 KiB, five workgroups per CU); the group's
+ * word and escape sums reuse it at the end. */
 template <int V, bool STRIDED>
 __device__ __forceinline__ void chunk_encode_body(const float *__restrict__ x, PlanArgs pa,
                                                   Workspace ws, uint8_t *__restrict__ sizes_dst,
                                                   uint64_t sizes_bytes) {
-    using Gm = ChunkGeom<V>;
-    constexpr int kBufs = kEncWaves * kEncChunk / V;
-    __shared__ uint32_t s_words[kBufs][Gm::LDSW];
-    __shared__ uint32_t s_stage[kEncWaves][2][kEscStage];
-    __shared__ uint32_t s_or[kEncWaves][Gm::PER_WAVE];
-    __shared__ uint32_t s_grp[2][kEncWaves];
+    __shared__ uint4 s_x[kEncWaves][kWaveQuads];
 
     const uint32_t lane = threadIdx.x & 63;
-    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t c = blockIdx.x * kEncWaves + wave;
     const DevInfo *info = ws.info;
     const uint64_t n = pa.n;
     const uint64_t cbase = (uint64_t)c * kEncChunk;
-    ChunkEsc es;
-    uint32_t wsum = 0;
+    uint4 *sx = s_x[wave];
+    uint32_t wsum = 0, escs = 0;
 
-    if (info->valid) {  /* the same for every workgroup: the barrier below is uniform */
+    if (info->valid) {  /* the same for every workgroup: the barriers below are uniform */
         QParams qp;
         qp.eb = info->eb_f;
         qp.s = info->s;
@@ -256,82 +408,90 @@ __device__ __forceinline__ void chunk_encode_body(const float *__restrict__ x, P
         qp.tlim = (float)(1u << pa.T);
         /* the predecessor of the wave's first value when it does not start a chunk (second half
          * of a 4096-value chunk): the code of the value before it, 0 if that value escapes */
-        int32_t carry = 0;
-        if ((cbase & (uint64_t)(V - 1)) != 0 && cbase < n) {
+        uint32_t carry = 0;
+        if (V > kEncChunk && (cbase & (uint64_t)(V - 1)) != 0 && cbase < n) {
             const float xp = x[elem_off<STRIDED>(pa.lay, cbase - 1)];
             uint32_t e;
             const int32_t qprev = quantize_slow(xp, rintf(xp * qp.r), qp, &e);
-            carry = e ? 0 : qprev;
+            carry = e ? 0u : (uint32_t)qprev;
         }
-        uint32_t orz[Gm::PER_WAVE];
-#pragma unroll
-        for (int k = 0; k < Gm::PER_WAVE; ++k) orz[k] = 0;
-        if (cbase + kEncChunk <= n)
-            encode_tiles<V, true, STRIDED>(x, pa.lay, cbase, n, qp, carry, wave, s_words, s_stage[wave][0],
-                                           s_stage[wave][1], orz, es);
-        else
-            encode_tiles<V, false, STRIDED>(x, pa.lay, cbase, n, qp, carry, wave, s_words, s_stage[wave][0],
-                                            s_stage[wave][1], orz, es);
-#pragma unroll
-        for (int k = 0; k < Gm::PER_WAVE; ++k) {
-            const uint32_t o = wave_or(orz[k]);
-            if (lane == 0) s_or[wave][k] = o;
-        }
-        __syncthreads();
+        const bool full = cbase + kEncChunk <= n;
+        if (full) stage_values<true, STRIDED>(x, pa.lay, cbase, n, sx);
+        else stage_values<false, STRIDED>(x, pa.lay, cbase, n, sx);
+        int32_t q[32];
+        const uint32_t emask = quantize_group(sx, qp, q);
+        uint32_t tmask = 0;
+        if (c < pa.nchunks && __ballot(emask != 0)) stage_escapes(sx, emask, cbase, c, ws, escs, tmask);
+        uint32_t w[32];
+        const uint64_t gbase = cbase + 32u * lane;
+        if (full) diff_group<V, true>(q, carry, gbase, n, w);
+        else diff_group<V, false>(q, carry, gbase, n, w);
+        transpose32(w);
+        zigzag_planes(w);
 
+        uint32_t *sz = reinterpret_cast<uint32_t *>(sizes_dst);
         const uint64_t ncv = (n + V - 1) / V;
-        if (Gm::WAVES == 1 || (wave & 1u) == 0) {
-            uint32_t *slot = ws.scratch + (uint64_t)c * pa.slot;
-            uint32_t *sz = reinterpret_cast<uint32_t *>(sizes_dst);
-#pragma unroll
-            for (int k = 0; k < Gm::PER_WAVE; ++k) {
-                const uint64_t cv = (cbase + (uint64_t)k * V) / V;
-                if (cv < ncv) {
-                    uint32_t orc = s_or[wave][k];
-                    if (Gm::WAVES == 2) orc |= s_or[wave + 1][0];
-                    const uint32_t wmax = orc ? 32u - (uint32_t)__builtin_clz(orc) : 0u;
-                    const uint32_t size = rze_chunk<V>(s_words[(wave * kEncChunk + (uint32_t)k * V) / V], wmax,
-                                                       slot + wsum);
-                    wsum += size;
-                    if (lane == 0 && 4 * cv < sizes_bytes) sz[cv] = size;
-                    if (cv == ncv - 1) {
-                        /* zero the size section's pad up to its 16-byte end */
-                        const uint64_t pz = cv + 1 + lane;
-                        if (pz < align16(4 * ncv) / 4 && 4 * pz < sizes_bytes) sz[pz] = 0u;
-                    }
-                }
+        uint32_t last_cv = 0xFFFFFFFFu; /* the coder chunk this wave sized last */
+        if constexpr (V == 2048) {
+            if (c < pa.nchunks) {
+                wsum = rze_wave(Planes{}, w, ws.scratch + (uint64_t)c * pa.slot);
+                if (lane == 0 && 4ull * c < sizes_bytes) sz[c] = wsum;
+                last_cv = c;
             }
+        } else if constexpr (V == 1024) {
+            if (c < pa.nchunks) {
+                const bool hasB = 2ull * c + 1 < ncv;
+                uint32_t sizes[2];
+                rze_halves(Planes{}, w, hasB, ws.scratch + (uint64_t)c * pa.slot, sizes);
+                wsum = sizes[0] + sizes[1];
+                if (lane == 0 && 8ull * c < sizes_bytes) sz[2 * c] = sizes[0];
+                if (lane == 0 && hasB && 8ull * c + 4 < sizes_bytes) sz[2 * c + 1] = sizes[1];
+                last_cv = hasB ? 2 * c + 1 : 2 * c;
+            }
+        } else {
+            const uint32_t p = wave & 1u;
+            const uint32_t ce = c - p;
+            const bool live = ce < pa.nchunks;
+            wsum = rze_pair(Planes{}, w, p, live, reinterpret_cast<uint32_t *>(sx),
+                            reinterpret_cast<const uint32_t *>(s_x[wave ^ 1u]), ws.scratch + (uint64_t)ce * pa.slot);
+            if (live && p == 0) {
+                if (lane == 0 && 2ull * ce < sizes_bytes) sz[ce / 2] = wsum;
+                last_cv = ce / 2;
+            }
+        }
+        if ((uint64_t)last_cv == ncv - 1) {
+            /* zero the size section's pad up to its 16-byte end */
+            const uint64_t pz = ncv + lane;
+            if (pz < align16(4 * ncv) / 4 && 4 * pz < sizes_bytes) sz[pz] = 0u;
         }
         if (c < pa.nchunks) {
-            if (lane < es.escs && lane < (uint32_t)kEscStage) {
-                ws.stage_idx[(uint64_t)c * kEscStage + lane] = s_stage[wave][0][lane];
-                ws.stage_val[(uint64_t)c * kEscStage + lane] = s_stage[wave][1][lane];
-            }
             /* the escape bitmasks are read by the compaction only for a chunk with more escapes
              * than the staging holds */
-            if (es.tmask && es.escs > (uint32_t)kEscStage) ws.emask[(uint64_t)c * kEncSegs + lane] = es.emask;
+            if (tmask && escs > (uint32_t)kEscStage) ws.emask[(uint64_t)c * kEncSegs + lane] = emask;
             if (lane == 0) {
                 ws.chunk_words[c] = wsum;
-                ws.chunk_esc[c] = es.escs;
-                ws.chunk_tmask[c] = es.tmask;
+                ws.chunk_esc[c] = escs;
+                ws.chunk_tmask[c] = tmask;
             }
         }
     }
     if (c >= pa.nchunks) {
         wsum = 0;
-        es.escs = 0;
+        escs = 0;
     }
+    __syncthreads(); /* every wave is done with its staging; the group sums reuse wave 0's */
+    uint32_t *s_grp = reinterpret_cast<uint32_t *>(s_x[0]);
     if (lane == 0) {
-        s_grp[0][wave] = wsum;
-        s_grp[1][wave] = es.escs;
+        s_grp[wave] = wsum;
+        s_grp[kEncWaves + wave] = escs;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t sw = 0, se = 0;
 #pragma unroll
         for (int k = 0; k < kEncWaves; ++k) {
-            sw += s_grp[0][k];
-            se += s_grp[1][k];
+            sw += s_grp[k];
+            se += s_grp[kEncWaves + k];
         }
         ws.group_words[blockIdx.x] = sw;
         ws.group_esc[blockIdx.x] = se;
@@ -348,275 +508,230 @@ __global__ __launch_bounds__(kEncThreads) void chunk_encode_kernel(Fields fs, Pl
 
 /* ---- K7c: chunk decode ------------------------------------------------------------------------ */
 
-/* Decode tiles [t0, t0 + NT) of a chunk: lane 32 h + b reads plane b of group 2 t + h (planes
- * at and above wmax are zero), the transpose turns that into one code per lane, then the zigzag
- * inverse and a wave prefix sum plus the carry (the previous tile's last code) undo the first
- * difference, and f32(f32(q) * s) is stored.  The NT tiles' transposes and scans are
- * independent; only the carry chains them. */
-/* Word g of bit plane b of a chunk (the word of the plane for group g), for the tile loops. */
-/* From planes rebuilt in LDS, PS words per plane, holding groups g0 onwards. */
-struct PlaneFetch {
-    const uint32_t *pl;
-    uint32_t ps, g0;
-    __device__ __forceinline__ uint32_t operator()(uint32_t b, uint32_t g) const { return pl[b * ps + g - g0]; }
-};
+/* Un-RZE: group `lane`'s plane words, w[b] = plane b's word (0 where its bitmap bit is clear).
+ * The bitmap comes by one vector load (lane l: bitmap word l), its bit count is checked against
+ * the chunk's word count before any word is loaded under it (so a corrupt stream reads nothing
+ * outside its chunk), and each plane below the highest one with a nonzero word takes its bitmap
+ * bits and its running word count by readlane.  Returns false for a count mismatch.  The plane
+ * loop is unrolled: plane B's bitmap bits and count sit at compile-time lanes. */
 
-/* From the chunk's RZE words staged as they lie in the stream (raw[0] = the first bitmap word)
- * and the exclusive popcount prefix of the bitmap words: a word whose bitmap bit is clear is 0,
- * else it is nonzero word number (prefix + the set bits below it in its bitmap word). */
-template <int V>
-struct RawFetch {
-    const uint32_t *raw;
-    const uint32_t *pre;
-    __device__ __forceinline__ uint32_t operator()(uint32_t b, uint32_t g) const {
-        const uint32_t wi = b * (uint32_t)ChunkGeom<V>::G + g, k = wi >> 5, j = wi & 31u;
-        const uint32_t bmw = raw[k];
-        const uint32_t below = (uint32_t)__popc(bmw & ((1u << j) - 1u));
-        return ((bmw >> j) & 1u) ? raw[ChunkGeom<V>::BM + pre[k] + below] : 0u;
-    }
-};
-
-template <int V, int NT, bool FULL, bool STRIDED, typename F>
-__device__ __forceinline__ void decode_tiles(const F &fetch, uint32_t t0, uint32_t wmax, const Transpose &tr,
-                                             float s, uint32_t &carry, float *__restrict__ out, const Layout &lo,
-                                             uint32_t cbase, uint32_t n) {
-    const uint32_t lane = threadIdx.x & 63;
-    const uint32_t h = lane >> 5, b = lane & 31;
-    uint32_t incl[NT];
-#pragma unroll
-    for (int k = 0; k < NT; ++k) {
-        const uint32_t word = b < wmax ? fetch(b, 2u * (t0 + k) + h) : 0u;
-        incl[k] = wave_incl_scan((uint32_t)unzigzag(tr(word)));
-    }
-#pragma unroll
-    for (int k = 0; k < NT; ++k) {
-        const uint32_t q = incl[k] + carry;
-        carry = readlane(q, 63);
-        const float y = (float)(int32_t)q * s;
-        const uint32_t i = cbase + (t0 + k) * kCTile + lane;
-        if (FULL || i < n) st_nt_f(out + elem_off<STRIDED>(lo, i), y);
+/* A 2048-value chunk: plane B's bits are bitmap words 2 B and 2 B + 1. */
+template <int B>
+__device__ __forceinline__ void unrze_wave_plane(const uint32_t *blob, uint32_t bm, uint32_t pre, uint32_t wmax,
+                                                 uint32_t w[32]) {
+    constexpr uint32_t BM = ChunkGeom<2048>::BM;
+    w[B] = 0;
+    if ((uint32_t)B < wmax) {
+        const uint64_t M = (uint64_t)readlane(bm, 2 * B) | ((uint64_t)readlane(bm, 2 * B + 1) << 32);
+        if (__builtin_amdgcn_inverse_ballot_w64(M)) w[B] = word_at(blob, BM + readlane(pre, 2 * B) + mbcnt64(M));
     }
 }
 
-/* Decode 4 NQ full tiles from tile t0 on, four at a time: each tile's transpose gives one code
- * per lane (value 64 t + lane), the four tiles' codes go through a 1 KB LDS scratch so that lane
- * l holds values 4 l .. 4 l + 3 of the 256, and then one in-lane running sum, one wave scan of
- * the lane totals and the carry undo the first difference for all four tiles, and one 128-bit
- * store writes the lane's four values.  The scratch belongs to the wave: a wave-level release /
- * acquire after the stores and again after the read orders every lane's accesses, so the next
- * group's stores cannot pass this group's read (by the compiler or by the LDS). */
-template <int V, int NQ, bool STRIDED, typename F>
-__device__ __forceinline__ void decode_quads(const F &fetch, uint32_t t0, uint32_t wmax, const Transpose &tr,
-                                             float s, uint32_t &carry, float *__restrict__ out, const Layout &lo,
-                                             uint32_t cbase, uint32_t *sx) {
+template <int... B>
+__device__ __forceinline__ bool unrze_wave(std::integer_sequence<int, B...>, const uint32_t *blob, uint32_t P,
+                                           uint32_t w[32]) {
+    constexpr uint32_t BM = ChunkGeom<2048>::BM;
     const uint32_t lane = threadIdx.x & 63;
-    const uint32_t h = lane >> 5, b = lane & 31;
-#pragma unroll
-    for (int g = 0; g < NQ; ++g) {
-        const uint32_t t = t0 + 4u * g;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t word = b < wmax ? fetch(b, 2u * (t + k) + h) : 0u;
-            sx[64 * k + lane] = (uint32_t)unzigzag(tr(word));
+    const uint32_t bm = blob[lane];
+    const uint32_t pc = (uint32_t)__popc(bm);
+    const uint32_t incl = wave_incl_scan(pc);
+    if (readlane(incl, 63) + BM != P) return false;
+    const uint64_t nz = __ballot(bm != 0);
+    const uint32_t wmax = nz ? (uint32_t)(63 - __clzll((long long)nz)) / 2u + 1u : 0u;
+    (unrze_wave_plane<B>(blob, bm, incl - pc, wmax, w), ...);
+    return true;
+}
+
+/* Two 1024-value chunks: A (P words from blob) in lanes 0-31, B (P2 words from blob + P, absent
+ * when P2 = 0) in lanes 32-63; plane B's bits are word B of each bitmap. */
+template <int B>
+__device__ __forceinline__ void unrze_halves_plane(const uint32_t *blob, uint32_t P, uint32_t bm, uint32_t pre,
+                                                   uint32_t wmax, uint32_t w[32]) {
+    constexpr uint32_t BM = ChunkGeom<1024>::BM;
+    w[B] = 0;
+    if ((uint32_t)B < wmax) {
+        const uint32_t lo = readlane(bm, B), hi = readlane(bm, 32 + B);
+        const uint64_t M = (uint64_t)lo | ((uint64_t)hi << 32);
+        if (__builtin_amdgcn_inverse_ballot_w64(M)) {
+            const uint32_t off = (threadIdx.x & 32) ? P + BM + readlane(pre, 32 + B) + __builtin_amdgcn_mbcnt_hi(hi, 0u)
+                                                    : BM + readlane(pre, B) + __builtin_amdgcn_mbcnt_lo(lo, 0u);
+            w[B] = word_at(blob, off);
         }
-        wave_lds_sync();
-        const uint4 v = reinterpret_cast<const uint4 *>(sx)[lane];
-        wave_lds_sync();
-        const uint32_t r1 = v.x + v.y, r2 = r1 + v.z, r3 = r2 + v.w;
-        const uint32_t incl = wave_incl_scan(r3);
-        const uint32_t base = carry + incl - r3;
-        carry += readlane(incl, 63);
-        float4 o;
-        o.x = (float)(int32_t)(base + v.x) * s;
-        o.y = (float)(int32_t)(base + r1) * s;
-        o.z = (float)(int32_t)(base + r2) * s;
-        o.w = (float)(int32_t)(base + r3) * s;
-        store4<STRIDED>(out, lo, (uint64_t)cbase + (uint64_t)t * kCTile + 4u * lane, o);
     }
 }
 
-/* One wave per chunk.  The chunk's bitmap sits in two VGPRs (lane l: bitmap words l and
- * 64 + l); its popcount must equal the chunk's word count minus the bitmap, else the stream is
- * flagged.  A 1024-value chunk is staged in LDS as its words lie in the stream, loaded
- * together with the bitmap, and each tile reads a plane word from it by its rank among the
- * nonzero words (RawFetch).  Larger chunks rebuild their planes below the highest nonzero one
- * in LDS (a 4096-value chunk half a chunk at a time): per 64-word batch the batch's bitmap bits
- * and mbcnt give each present word's position (PlaneFetch); all of a rebuild's loads are issued
- * before its LDS stores.  Then the tile loops, eight tiles at a time for a full chunk.  (A
- * 2048-value chunk read in place was slower: 134 -> 149 us on the 512^3 field.) */
+template <int... B>
+__device__ __forceinline__ bool unrze_halves(std::integer_sequence<int, B...>, const uint32_t *blob, uint32_t P,
+                                             uint32_t P2, uint32_t w[32]) {
+    constexpr uint32_t BM = ChunkGeom<1024>::BM;
+    const uint32_t lane = threadIdx.x & 63;
+    uint32_t bm = 0;
+    if (lane < 32) bm = blob[lane];
+    else if (P2) bm = blob[P + lane - 32];
+    const uint32_t pc = (uint32_t)__popc(bm);
+    const uint32_t incl = wave_seg_scan(pc, lane & 31, 32);
+    if (readlane(incl, 31) + BM != P || (P2 && readlane(incl, 63) + BM != P2)) return false;
+    const uint64_t nz = __ballot(bm != 0);
+    const uint32_t nlo = (uint32_t)nz, nhi = (uint32_t)(nz >> 32);
+    const uint32_t top = (nlo | nhi) ? 31u - (uint32_t)__builtin_clz(nlo | nhi) + 1u : 0u;
+    (unrze_halves_plane<B>(blob, P, bm, incl - pc, top, w), ...);
+    return true;
+}
+
+/* A 4096-value chunk, half H (groups 64 H .. 64 H + 63): plane B's bits are bitmap words 4 B + 2 H
+ * and 4 B + 2 H + 1, which sit in bm0 (words 0-63) or bm1 (words 64-127) with their exclusive
+ * bit-count prefixes pre0, pre1. */
+template <int H, int B>
+__device__ __forceinline__ void unrze_quarter_plane(const uint32_t *blob, uint32_t bm0, uint32_t bm1, uint32_t pre0,
+                                                    uint32_t pre1, uint32_t wmax, uint32_t w[32]) {
+    constexpr uint32_t BM = ChunkGeom<4096>::BM;
+    constexpr int K = 4 * B + 2 * H;
+    w[B] = 0;
+    if ((uint32_t)B < wmax) {
+        const uint32_t bm = K < 64 ? bm0 : bm1, pre = K < 64 ? pre0 : pre1;
+        const uint64_t M = (uint64_t)readlane(bm, K & 63) | ((uint64_t)readlane(bm, (K & 63) + 1) << 32);
+        if (__builtin_amdgcn_inverse_ballot_w64(M)) w[B] = word_at(blob, BM + readlane(pre, K & 63) + mbcnt64(M));
+    }
+}
+
+template <int... B>
+__device__ __forceinline__ bool unrze_pair(std::integer_sequence<int, B...>, const uint32_t *blob, uint32_t P,
+                                           uint32_t w0[32], uint32_t w1[32]) {
+    constexpr uint32_t BM = ChunkGeom<4096>::BM;
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t bm0 = blob[lane], bm1 = blob[64 + lane];
+    const uint32_t c0 = (uint32_t)__popc(bm0), c1 = (uint32_t)__popc(bm1);
+    const uint32_t i0 = wave_incl_scan(c0), i1 = wave_incl_scan(c1);
+    const uint32_t t0 = readlane(i0, 63);
+    if (t0 + readlane(i1, 63) + BM != P) return false;
+    const uint64_t nz0 = __ballot(bm0 != 0), nz1 = __ballot(bm1 != 0);
+    const uint32_t top = nz1 ? 64u + (uint32_t)(63 - __clzll((long long)nz1)) : nz0 ? (uint32_t)(63 - __clzll((long long)nz0)) : 0u;
+    const uint32_t wmax = (nz0 | nz1) ? top / 4u + 1u : 0u;
+    (unrze_quarter_plane<0, B>(blob, bm0, bm1, i0 - c0, t0 + i1 - c1, wmax, w0), ...);
+    (unrze_quarter_plane<1, B>(blob, bm0, bm1, i0 - c0, t0 + i1 - c1, wmax, w1), ...);
+    return true;
+}
+
+/* Values of the lane's group from its plane words, in place: unfold, transpose, and sum the
+ * differences from the group's start, which the wave scan of the lane totals (segments of SEG
+ * lanes, one per chunk) and the carry give; w[i] becomes the bits of f32(f32(q_i) * s).  Returns
+ * the carry for what follows the wave's last group. */
+template <int SEG>
+__device__ __forceinline__ uint32_t decode_group(uint32_t w[32], uint32_t carry, float s) {
+    unzigzag_planes(w);
+    transpose32(w);
+    uint32_t tot = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) tot += w[i];
+    const uint32_t incl = SEG == 64 ? wave_incl_scan(tot) : wave_seg_scan(tot, threadIdx.x & 31, 32);
+    uint32_t run = carry + incl - tot;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        run += w[i];
+        w[i] = __float_as_uint((float)(int32_t)run * s);
+    }
+    return carry + readlane(incl, 63);
+}
+
+/* The wave's 2048 decoded values (lane: its group's 32, as bits) to out from value base on, cnt
+ * of them, through the LDS staging sy. */
+template <bool STRIDED>
+__device__ __forceinline__ void store_values(const uint32_t y[32], uint4 *sy, float *__restrict__ out,
+                                             const Layout &lo, uint32_t base, uint32_t cnt) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t s0 = quad_slot(8u * lane);
+    wave_lds_sync(); /* earlier reads of the staging are done */
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sy[s0 ^ (uint32_t)j] = make_uint4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
+    wave_lds_sync();
+    if (cnt == (uint32_t)kEncChunk) {
+        const uint32_t s1 = quad_slot(lane);
+#pragma unroll
+        for (int k = 0; k < kLaneQuads; ++k) {
+            const uint4 v = sy[kWave * k + (s1 ^ (uint32_t)k)];
+            store4<STRIDED>(out, lo, (uint64_t)base + 4u * (kWave * k + lane),
+                            make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                                        __uint_as_float(v.w)));
+        }
+    } else {
+#pragma unroll 4
+        for (int k = 0; k < kEncChunk / kWave; ++k) {
+            const uint32_t v = kWave * k + lane;
+            if (v < cnt) out[elem_off<STRIDED>(lo, (uint64_t)base + v)] = __uint_as_float(lds_value(sy, v));
+        }
+    }
+}
+
+/* One wave per 2048 values (two 1024-value chunks, or one 2048-value chunk), or per 4096-value
+ * chunk taken as two halves with the running sum carried from the first into the second. */
 template <int V, bool STRIDED>
 __device__ __forceinline__ void chunk_decode_body(const uint8_t *__restrict__ in, PlanArgs pa,
                                                   Workspace ws, float *__restrict__ out) {
-    using Gm = ChunkGeom<V>;
-    __shared__ uint4 s_lds4[kWavesPerBlock][Gm::DEC_LDSW / 4];
-    __shared__ uint4 s_x4[kWavesPerBlock][4 * kCTile / 4];
+    constexpr uint32_t U = V > kEncChunk ? V : kEncChunk; /* values per wave */
+    __shared__ uint4 s_y[kWavesPerBlock][kWaveQuads];
     const uint32_t lane = threadIdx.x & 63;
-    const uint32_t wave = threadIdx.x >> 6;
-    const uint32_t c = blockIdx.x * kWavesPerBlock + wave;
-    if (c >= pa.dchunks) return;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t u = blockIdx.x * kWavesPerBlock + wave;
+    const uint32_t n = (uint32_t)pa.n;
+    if ((uint64_t)u * U >= n) return;
+    const uint32_t ubase = u * U;
     DevInfo *info = ws.info;
     if (info->err) return;
-    const uint32_t n = (uint32_t)pa.n;
-    const uint32_t cbase = c * (uint32_t)V;
-    const uint32_t cnt = (n - cbase < (uint32_t)V) ? n - cbase : (uint32_t)V;
     if (info->mode == 1) {
-        const uint32_t *srcw = reinterpret_cast<const uint32_t *>(in + kHeaderBytes) + cbase;
+        const uint32_t cnt = n - ubase < U ? n - ubase : U;
+        const uint32_t *srcw = reinterpret_cast<const uint32_t *>(in + kHeaderBytes) + ubase;
         uint32_t *ob = reinterpret_cast<uint32_t *>(out);
-        if (!STRIDED && cnt == (uint32_t)V) {
+        if (!STRIDED && cnt == U) {
             const uint4 *s4 = reinterpret_cast<const uint4 *>(srcw);
-            uint4 *d4 = reinterpret_cast<uint4 *>(ob + cbase);
-            uint4 t[V / 4 / kWave];
+            uint4 *d4 = reinterpret_cast<uint4 *>(ob + ubase);
+            uint4 t[U / 4 / kWave];
 #pragma unroll
-            for (int i = 0; i < V / 4 / kWave; ++i) t[i] = ld_nt(s4 + lane + kWave * i);
+            for (int i = 0; i < (int)(U / 4 / kWave); ++i) t[i] = ld_nt(s4 + lane + kWave * i);
 #pragma unroll
-            for (int i = 0; i < V / 4 / kWave; ++i) st_nt(d4 + lane + kWave * i, t[i]);
+            for (int i = 0; i < (int)(U / 4 / kWave); ++i) st_nt(d4 + lane + kWave * i, t[i]);
         } else {
-            for (uint32_t i = lane; i < cnt; i += kWave) ob[elem_off<STRIDED>(pa.lay, cbase + i)] = srcw[i];
+            for (uint32_t i = lane; i < cnt; i += kWave) ob[elem_off<STRIDED>(pa.lay, ubase + i)] = srcw[i];
         }
         return;
     }
+    const uint32_t *pay = reinterpret_cast<const uint32_t *>(in + info->payload_off);
+    const float s = info->dec_s;
+    uint4 *sy = s_y[wave];
+    const uint32_t c = V < kEncChunk ? 2 * u : u;
     const uint32_t W = chunk_offset<kDecChunksPerGroup>(ws.gpre_words, ws.chunk_words, c);
     const uint32_t P = ws.chunk_words[c];
-    const uint32_t *blob = reinterpret_cast<const uint32_t *>(in + info->payload_off) + W;
-    const uint32_t bm0 = lane < (uint32_t)(Gm::BM < 64 ? Gm::BM : 64) ? blob[lane] : 0u;
-    const uint32_t bm1 = Gm::BM > 64 ? blob[64 + lane] : 0u;
-    /* RAW: all of the chunk's words, as they lie in the stream, are loaded with its bitmap
-     * (16-byte units from the unit holding its first word) */
-    constexpr int kRounds = Gm::RAW ? (Gm::RAWW / 4 + kWave - 1) / kWave : 1;
-    uint4 v[kRounds];
-    uint32_t lb = 0, units = 0;
-    if constexpr (Gm::RAW) {
-        const uint64_t sw = info->payload_off / 4 + W;
-        const uint64_t a0 = sw & ~(uint64_t)3;
-        lb = (uint32_t)(sw - a0);
-        units = (lb + P + 3) >> 2;
-        if (units > (uint32_t)(Gm::RAWW / 4)) units = Gm::RAWW / 4;
-        const uint4 *src = reinterpret_cast<const uint4 *>(in) + a0 / 4;
-        const uint32_t rounds = (units + kWave - 1) / kWave;
-#pragma unroll
-        for (int r = 0; r < kRounds; ++r) {
-            const uint32_t u = lane + (uint32_t)r * kWave;
-            v[r] = make_uint4(0, 0, 0, 0);
-            if ((uint32_t)r < rounds && u < units) v[r] = src[u];
+    const uint32_t *blob = pay + W;
+    const uint32_t cnt = n - ubase < (uint32_t)kEncChunk ? n - ubase : (uint32_t)kEncChunk;
+    uint32_t w[32];
+    if constexpr (V == 1024) {
+        const uint32_t P2 = c + 1 < pa.dchunks ? ws.chunk_words[c + 1] : 0u;
+        if (!unrze_halves(Planes{}, blob, P, P2, w)) {
+            if (lane == 0) atomicOr(&info->sticky, 1u);
+            return;
         }
-    }
-    const uint32_t pc = wave_incl_scan((uint32_t)__popc(bm0) + (uint32_t)__popc(bm1));
-    if (readlane(pc, 63) + Gm::BM != P) {
-        if (lane == 0) atomicOr(&info->sticky, 1u);
-        return;
-    }
-    const uint64_t nz0 = __ballot(bm0 != 0), nz1 = __ballot(bm1 != 0);
-    int top = -1;
-    if (nz1) top = 64 + 63 - __clzll((long long)nz1);
-    else if (nz0) top = 63 - __clzll((long long)nz0);
-    const uint32_t wmax = top < 0 ? 0u : (uint32_t)top * 32u / Gm::G + 1u;
-    uint32_t *pl = reinterpret_cast<uint32_t *>(s_lds4[wave]);
-    const Transpose tr(lane);
-    const float s = info->dec_s;
-    uint32_t carry = 0;
-    uint32_t *sx = reinterpret_cast<uint32_t *>(s_x4[wave]);
-    if constexpr (Gm::HALVES) {
-        /* A 4096-value chunk goes through a half-size buffer: the planes' words of groups 0-63
-         * (tiles 0-31), then those of groups 64-127 (tiles 32-63), each half's loads issued
-         * before its LDS stores.  The running word count covers both halves' bitmap bits, and
-         * the running sum carries from the first half into the second. */
-        constexpr int PSH = Gm::PSH;
-        const uint32_t ntiles = (cnt + kCTile - 1) / kCTile;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const uint32_t t0 = 32u * hh;
-            if (t0 >= ntiles) break;
-            uint32_t wv[32];
-            uint32_t run = 0;
-#pragma unroll
-            for (int pb = 0; pb < 32; ++pb) {
-                wv[pb] = 0;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    if ((uint32_t)pb < wmax) {
-                        const uint32_t wi = (pb * Gm::G + 64 * kk) / 32;
-                        const uint32_t lo = wi < 64 ? readlane(bm0, (int)wi) : readlane(bm1, (int)(wi - 64));
-                        const uint32_t hi = wi + 1 < 64 ? readlane(bm0, (int)(wi + 1)) : readlane(bm1, (int)(wi + 1 - 64));
-                        const uint64_t M = (uint64_t)lo | ((uint64_t)hi << 32);
-                        if (kk == hh && ((M >> lane) & 1u)) wv[pb] = blob[Gm::BM + run + mbcnt64(M)];
-                        run += (uint32_t)__popcll(M);
-                    }
-                }
-            }
-            wave_lds_sync(); /* the first half's reads are done before the second half's stores */
-#pragma unroll
-            for (int pb = 0; pb < 32; ++pb)
-                if ((uint32_t)pb < wmax) pl[pb * PSH + lane] = wv[pb];
-            wave_lds_sync();
-            const PlaneFetch fetch{pl, (uint32_t)PSH, 2u * t0};
-            if (cnt == (uint32_t)V) {
-                for (uint32_t t = t0; t < t0 + 32u; t += 8)
-                    decode_quads<V, 2, STRIDED>(fetch, t, wmax, tr, s, carry, out, pa.lay, cbase, sx);
-            } else {
-                const uint32_t te = ntiles < t0 + 32u ? ntiles : t0 + 32u;
-                for (uint32_t t = t0; t < te; ++t)
-                    decode_tiles<V, 1, false, STRIDED>(fetch, t, wmax, tr, s, carry, out, pa.lay, cbase, n);
-            }
+        decode_group<32>(w, 0, s);
+        store_values<STRIDED>(w, sy, out, pa.lay, ubase, cnt);
+    } else if constexpr (V == 2048) {
+        if (!unrze_wave(Planes{}, blob, P, w)) {
+            if (lane == 0) atomicOr(&info->sticky, 1u);
+            return;
         }
-    } else if constexpr (Gm::RAW) {
-        /* the staged words into LDS, the bitmap's exclusive popcount prefix after them; the
-         * tile loops then read each plane word in place */
-#pragma unroll
-        for (int r = 0; r < kRounds; ++r) {
-            const uint32_t u = lane + (uint32_t)r * kWave;
-            if (u < units) s_lds4[wave][u] = v[r];
-        }
-        if (lane < (uint32_t)Gm::BM) pl[Gm::RAWW + lane] = pc - (uint32_t)__popc(bm0);
-        wave_lds_sync();
-        const RawFetch<V> fetch{pl + lb, pl + Gm::RAWW};
-        if (cnt == (uint32_t)V) {
-            for (uint32_t t = 0; t < (uint32_t)Gm::TILES; t += 8)
-                decode_quads<V, 2, STRIDED>(fetch, t, wmax, tr, s, carry, out, pa.lay, cbase, sx);
-        } else {
-            const uint32_t ntiles = (cnt + kCTile - 1) / kCTile;
-            for (uint32_t t = 0; t < ntiles; ++t)
-                decode_tiles<V, 1, false, STRIDED>(fetch, t, wmax, tr, s, carry, out, pa.lay, cbase, n);
-        }
+        decode_group<64>(w, 0, s);
+        store_values<STRIDED>(w, sy, out, pa.lay, ubase, cnt);
     } else {
-        /* un-RZE: every plane's loads first (into registers), then the LDS stores */
-        uint32_t wv[32 * Gm::BATCHES];
-        uint32_t run = 0;
-#pragma unroll
-        for (int pb = 0; pb < 32; ++pb) {
-#pragma unroll
-            for (int kk = 0; kk < Gm::BATCHES; ++kk) {
-                uint32_t word = 0;
-                if ((uint32_t)pb < wmax) {
-                    const uint32_t wi = (pb * Gm::G + 64 * kk) / 32;
-                    const uint32_t lo = wi < 64 ? readlane(bm0, (int)wi) : readlane(bm1, (int)(wi - 64));
-                    uint32_t hi = 0;
-                    if (Gm::G >= 64) hi = wi + 1 < 64 ? readlane(bm0, (int)(wi + 1)) : readlane(bm1, (int)(wi + 1 - 64));
-                    const uint64_t M = (uint64_t)lo | ((uint64_t)hi << 32);
-                    if ((M >> lane) & 1u) word = blob[Gm::BM + run + mbcnt64(M)];
-                    run += (uint32_t)__popcll(M);
-                }
-                wv[pb * Gm::BATCHES + kk] = word;
-            }
+        /* both halves' words are loaded before either is decoded */
+        uint32_t w1[32];
+        if (!unrze_pair(Planes{}, blob, P, w, w1)) {
+            if (lane == 0) atomicOr(&info->sticky, 1u);
+            return;
         }
-#pragma unroll
-        for (int pb = 0; pb < 32; ++pb) {
-            if ((uint32_t)pb < wmax) {
-#pragma unroll
-                for (int kk = 0; kk < Gm::BATCHES; ++kk) {
-                    const uint32_t gi = 64u * kk + lane;
-                    if (Gm::G >= 64 || gi < (uint32_t)Gm::G) pl[pb * Gm::PS + gi] = wv[pb * Gm::BATCHES + kk];
-                }
-            }
-        }
-        wave_lds_sync();
-        const PlaneFetch fetch{pl, (uint32_t)Gm::PS, 0u};
-        if (cnt == (uint32_t)V) {
-            for (uint32_t t = 0; t < (uint32_t)Gm::TILES; t += 8)
-                decode_quads<V, 2, STRIDED>(fetch, t, wmax, tr, s, carry, out, pa.lay, cbase, sx);
-        } else {
-            const uint32_t ntiles = (cnt + kCTile - 1) / kCTile;
-            for (uint32_t t = 0; t < ntiles; ++t)
-                decode_tiles<V, 1, false, STRIDED>(fetch, t, wmax, tr, s, carry, out, pa.lay, cbase, n);
+        const uint32_t carry = decode_group<64>(w, 0, s);
+        store_values<STRIDED>(w, sy, out, pa.lay, ubase, cnt);
+        const uint32_t hbase = ubase + kEncChunk;
+        if (hbase < n) {
+            decode_group<64>(w1, carry, s);
+            store_values<STRIDED>(w1, sy, out, pa.lay, hbase,
+                                  n - hbase < (uint32_t)kEncChunk ? n - hbase : (uint32_t)kEncChunk);
         }
     }
 }
@@ -642,7 +757,9 @@ hipError_t chunk_encode_v(const Fields &fs, uint32_t nf, const PlanArgs &pa, con
 template <int V>
 hipError_t chunk_decode_v(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                           hipStream_t stream) {
-    const dim3 grid(pa.dgroups, nf), block(kBlockThreads);
+    /* waves: one per 2048 values (two 1024-value chunks), or one per chunk */
+    const uint32_t waves = V < kEncChunk ? (pa.dchunks + 1) / 2 : pa.dchunks;
+    const dim3 grid((waves + kWavesPerBlock - 1) / kWavesPerBlock, nf), block(kBlockThreads);
     if (pa.lay.strided)
         eblc_launch((chunk_decode_kernel<V, true>), grid, block, 0, stream, fs, pa, ws);
     else
