@@ -79,12 +79,13 @@ __device__ __forceinline__ uint32_t quad_slot(uint32_t g) {
 
 __device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
 
-/* One stage of the transpose: for every register pair (k, k + J), k without bit J, the bits of
- * k whose index has bit J set trade places with the bits of k + J whose index has it clear. */
-template <int J>
+/* One stage of the transpose: for every register pair (k, k + J) below N, k without bit J, the
+ * bits of k whose index has bit J set trade places with the bits of k + J whose index has it
+ * clear. */
+template <int J, int N>
 __device__ __forceinline__ void swap_stage(uint32_t w[32], uint32_t m) {
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
+    for (int k = 0; k < N; ++k) {
         if (k & J) continue;
         const uint32_t a = w[k], b = w[k + J];
         w[k] = bfi(m, a, b << J);
@@ -92,7 +93,23 @@ __device__ __forceinline__ void swap_stage(uint32_t w[32], uint32_t m) {
     }
 }
 
-/* 32 x 32 bit transpose in place: on exit bit i of w[b] is bit b of w[i] on entry. */
+/* The 8-, 4-, 2- and 1-bit stages on w[0..N). */
+template <int N>
+__device__ __forceinline__ void low_stages(uint32_t w[32]) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) { /* bytes: (a0, b0, a2, b2) and (a1, b1, a3, b3) */
+        if (k & 8) continue;
+        const uint32_t a = w[k], b = w[k + 8];
+        w[k] = __builtin_amdgcn_perm(b, a, 0x06020400u);
+        w[k + 8] = __builtin_amdgcn_perm(b, a, 0x07030501u);
+    }
+    swap_stage<4, N>(w, 0x0F0F0F0Fu);
+    swap_stage<2, N>(w, 0x33333333u);
+    swap_stage<1, N>(w, 0x55555555u);
+}
+
+/* 32 x 32 bit transpose in place: on exit bit i of w[b] is bit b of w[i] on entry.  (The stages
+ * act on different bits of the row and column indexes, so they commute.) */
 __device__ __forceinline__ void transpose32(uint32_t w[32]) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) { /* 16-bit blocks: (a.lo, b.lo) and (a.hi, b.hi) */
@@ -100,16 +117,16 @@ __device__ __forceinline__ void transpose32(uint32_t w[32]) {
         w[k] = __builtin_amdgcn_perm(b, a, 0x05040100u);
         w[k + 16] = __builtin_amdgcn_perm(b, a, 0x07060302u);
     }
+    low_stages<32>(w);
+}
+
+/* The transpose of 32 codes that are sign extensions of their low 16 bits, into planes 0-15
+ * (planes 16-31 would all equal plane 15): the 16-bit stage only gathers the low halves, and the
+ * other stages run on half the registers. */
+__device__ __forceinline__ void transpose_low16(uint32_t w[32]) {
 #pragma unroll
-    for (int k = 0; k < 32; ++k) { /* bytes: (a0, b0, a2, b2) and (a1, b1, a3, b3) */
-        if (k & 8) continue;
-        const uint32_t a = w[k], b = w[k + 8];
-        w[k] = __builtin_amdgcn_perm(b, a, 0x06020400u);
-        w[k + 8] = __builtin_amdgcn_perm(b, a, 0x07030501u);
-    }
-    swap_stage<4>(w, 0x0F0F0F0Fu);
-    swap_stage<2>(w, 0x33333333u);
-    swap_stage<1>(w, 0x55555555u);
+    for (int k = 0; k < 16; ++k) w[k] = __builtin_amdgcn_perm(w[k + 16], w[k], 0x05040100u);
+    low_stages<16>(w);
 }
 
 /* The lane's group leaves LDS as 32 values in order; sx is the wave's 2048-value staging. */
@@ -168,7 +185,7 @@ __device__ __forceinline__ void stage_values(const float *__restrict__ x, const 
  * bitmask (bit i: value i).  The fast test is the full rule's first acceptance exactly (the
  * bitpack encoder states why); the full rule runs only in a wave where a lane misses it, on
  * values read again from LDS so that the first pass keeps no copy of them. */
-__device__ __forceinline__ uint32_t quantize_group(const uint4 *sx, const QParams &qp, int32_t q[32]) {
+__device__ __forceinline__ uint32_t quantize_group(const uint4 *sx, const QParams &qp, int32_t q[32], float &qmax) {
     uint32_t xv[32];
     read_group(sx, xv);
     bool fast = true;
@@ -182,20 +199,31 @@ __device__ __forceinline__ uint32_t quantize_group(const uint4 *sx, const QParam
         q[i] = (int32_t)q0f;
     }
     fast = fast && (qabs < qp.tlim);
+    qmax = qabs;
     uint32_t emask = 0;
     if (__ballot(!fast)) {
+        /* the full rule, a quad at a time from LDS (the scheduling barriers keep each quad's read
+         * next to its use, so that the pass does not hold all 32 values next to the codes) */
         wave_lds_sync();
-        read_group(sx, xv);
+        const uint32_t s0 = quad_slot(8u * (threadIdx.x & 63));
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const float x = __uint_as_float(xv[i]);
-            const float q0f = rintf(x * qp.r);
-            if (!((fabsf(x - q0f * qp.s) <= qp.eb) && (fabsf(q0f) < qp.tlim))) {
-                uint32_t e;
-                q[i] = quantize_slow(x, q0f, qp, &e);
-                emask |= e << i;
+        for (int j = 0; j < 8; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            const uint4 u = sx[s0 ^ (uint32_t)j];
+            const float xf[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                                 __uint_as_float(u.w)};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = 4 * j + k;
+                const float q0f = rintf(xf[k] * qp.r);
+                if (!((fabsf(xf[k] - q0f * qp.s) <= qp.eb) && (fabsf(q0f) < qp.tlim))) {
+                    uint32_t e;
+                    q[i] = quantize_slow(xf[k], q0f, qp, &e);
+                    emask |= e << i;
+                }
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
     return emask;
 }
@@ -247,15 +275,17 @@ __device__ __forceinline__ void diff_group(const int32_t q[32], uint32_t carry, 
     }
 }
 
-/* Zigzag fold of the codes whose planes w holds, applied to the planes. */
+/* Zigzag fold of the codes whose planes w[0..NPL) hold, applied to the planes: NPL = 32, or 16
+ * for codes that are sign extensions of their low 16 bits (their folded planes 16-31 are 0). */
+template <int NPL>
 __device__ __forceinline__ void zigzag_planes(uint32_t w[32]) {
-    const uint32_t sgn = w[31];
+    const uint32_t sgn = w[NPL - 1];
 #pragma unroll
-    for (int b = 31; b > 0; --b) w[b] = w[b - 1] ^ sgn;
+    for (int b = NPL - 1; b > 0; --b) w[b] = w[b - 1] ^ sgn;
     w[0] = sgn;
 }
 
-/* Its inverse. */
+/* The inverse of the full fold. */
 __device__ __forceinline__ void unzigzag_planes(uint32_t w[32]) {
     const uint32_t sgn = w[0];
 #pragma unroll
@@ -319,7 +349,7 @@ __device__ __forceinline__ void rze_halves(std::integer_sequence<int, B...>, con
     const uint32_t lane = threadIdx.x & 63;
     uint32_t ra = 0;
 #pragma unroll
-    for (int b = 0; b < 32; ++b) ra += (uint32_t)__popc((uint32_t)__ballot(w[b] != 0));
+    for (int b = 0; b < (int)sizeof...(B); ++b) ra += (uint32_t)__popc((uint32_t)__ballot(w[b] != 0));
     const uint32_t sizeA = BM + ra;
     uint32_t rA = 0, rB = 0, bm = 0;
     (rze_halves_plane<B>(w, sizeA, dst, bm, rA, rB), ...);
@@ -377,6 +407,48 @@ __device__ __forceinline__ uint32_t rze_pair(std::integer_sequence<int, B...>, c
     return p ? 0u : total;
 }
 
+/* RZE of the wave's planes w[B...] into the scratch slot(s) of its coder chunk(s), and their
+ * word counts into the size section sz (of sizes_bytes bytes).  Returns the words the wave's
+ * slot takes; last_cv is the last coder chunk it sized (unchanged if none).  For V = 4096 both
+ * waves of the pair must call (they trade counts through LDS: xs is this wave's staging, xp the
+ * partner's). */
+template <int V, int... B>
+__device__ __forceinline__ uint32_t rze_chunks(std::integer_sequence<int, B...> planes, const uint32_t w[32],
+                                               uint32_t c, uint32_t wave, const PlanArgs &pa, const Workspace &ws,
+                                               uint4 *xs, const uint32_t *xp, uint32_t *sz, uint64_t sizes_bytes,
+                                               uint32_t &last_cv) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint64_t ncv = (pa.n + V - 1) / V;
+    uint32_t wsum = 0;
+    if constexpr (V == 2048) {
+        if (c < pa.nchunks) {
+            wsum = rze_wave(planes, w, ws.scratch + (uint64_t)c * pa.slot);
+            if (lane == 0 && 4ull * c < sizes_bytes) sz[c] = wsum;
+            last_cv = c;
+        }
+    } else if constexpr (V == 1024) {
+        if (c < pa.nchunks) {
+            const bool hasB = 2ull * c + 1 < ncv;
+            uint32_t sizes[2];
+            rze_halves(planes, w, hasB, ws.scratch + (uint64_t)c * pa.slot, sizes);
+            wsum = sizes[0] + sizes[1];
+            if (lane == 0 && 8ull * c < sizes_bytes) sz[2 * c] = sizes[0];
+            if (lane == 0 && hasB && 8ull * c + 4 < sizes_bytes) sz[2 * c + 1] = sizes[1];
+            last_cv = hasB ? 2 * c + 1 : 2 * c;
+        }
+    } else {
+        const uint32_t p = wave & 1u;
+        const uint32_t ce = c - p;
+        const bool live = ce < pa.nchunks;
+        wsum = rze_pair(planes, w, p, live, reinterpret_cast<uint32_t *>(xs), xp, ws.scratch + (uint64_t)ce * pa.slot);
+        if (live && p == 0) {
+            if (lane == 0 && 2ull * ce < sizes_bytes) sz[ce / 2] = wsum;
+            last_cv = ce / 2;
+        }
+    }
+    return wsum;
+}
+
 /* Workgroup of 4 waves over 8192 values; wave w owns the 2048 values of encode chunk c (the unit
  * of the escape bookkeeping and of the scratch slots the compaction copies), which hold 2048 / V
  * coder chunks, or half of one when V = 4096.  A wave's chunks lie back to back in its slot, and
@@ -419,45 +491,32 @@ __device__ __forceinline__ void chunk_encode_body(const float *__restrict__ x, P
         if (full) stage_values<true, STRIDED>(x, pa.lay, cbase, n, sx);
         else stage_values<false, STRIDED>(x, pa.lay, cbase, n, sx);
         int32_t q[32];
-        const uint32_t emask = quantize_group(sx, qp, q);
+        float qmax;
+        const uint32_t emask = quantize_group(sx, qp, q, qmax);
         uint32_t tmask = 0;
         if (c < pa.nchunks && __ballot(emask != 0)) stage_escapes(sx, emask, cbase, c, ws, escs, tmask);
         uint32_t w[32];
         const uint64_t gbase = cbase + 32u * lane;
         if (full) diff_group<V, true>(q, carry, gbase, n, w);
         else diff_group<V, false>(q, carry, gbase, n, w);
-        transpose32(w);
-        zigzag_planes(w);
-
+        /* Bitshuffle: codes within 16 bits (every |q| below 2^14, so every difference below
+         * 2^15) take the half transpose, and RZE skips their zero planes 16-31 */
+        const bool low16 = !__ballot(!(qmax < 16383.0f)) && carry + 16383u <= 32766u;
         uint32_t *sz = reinterpret_cast<uint32_t *>(sizes_dst);
         const uint64_t ncv = (n + V - 1) / V;
         uint32_t last_cv = 0xFFFFFFFFu; /* the coder chunk this wave sized last */
-        if constexpr (V == 2048) {
-            if (c < pa.nchunks) {
-                wsum = rze_wave(Planes{}, w, ws.scratch + (uint64_t)c * pa.slot);
-                if (lane == 0 && 4ull * c < sizes_bytes) sz[c] = wsum;
-                last_cv = c;
-            }
-        } else if constexpr (V == 1024) {
-            if (c < pa.nchunks) {
-                const bool hasB = 2ull * c + 1 < ncv;
-                uint32_t sizes[2];
-                rze_halves(Planes{}, w, hasB, ws.scratch + (uint64_t)c * pa.slot, sizes);
-                wsum = sizes[0] + sizes[1];
-                if (lane == 0 && 8ull * c < sizes_bytes) sz[2 * c] = sizes[0];
-                if (lane == 0 && hasB && 8ull * c + 4 < sizes_bytes) sz[2 * c + 1] = sizes[1];
-                last_cv = hasB ? 2 * c + 1 : 2 * c;
-            }
+        if (low16) {
+            transpose_low16(w);
+            zigzag_planes<16>(w);
+            wsum = rze_chunks<V>(std::make_integer_sequence<int, 16>{}, w, c, wave, pa, ws, sx,
+                                 reinterpret_cast<const uint32_t *>(s_x[wave ^ 1u]), sz, sizes_bytes, last_cv);
         } else {
-            const uint32_t p = wave & 1u;
-            const uint32_t ce = c - p;
-            const bool live = ce < pa.nchunks;
-            wsum = rze_pair(Planes{}, w, p, live, reinterpret_cast<uint32_t *>(sx),
-                            reinterpret_cast<const uint32_t *>(s_x[wave ^ 1u]), ws.scratch + (uint64_t)ce * pa.slot);
-            if (live && p == 0) {
-                if (lane == 0 && 2ull * ce < sizes_bytes) sz[ce / 2] = wsum;
-                last_cv = ce / 2;
-            }
+            transpose32(w);
+#pragma unroll
+            for (int b = 0; b < 32; ++b) asm volatile("" : "+v"(w[b]));
+            zigzag_planes<32>(w);
+            wsum = rze_chunks<V>(Planes{}, w, c, wave, pa, ws, sx, reinterpret_cast<const uint32_t *>(s_x[wave ^ 1u]),
+                                 sz, sizes_bytes, last_cv);
         }
         if ((uint64_t)last_cv == ncv - 1) {
             /* zero the size section's pad up to its 16-byte end */
@@ -499,7 +558,7 @@ __device__ __forceinline__ void chunk_encode_body(const float *__restrict__ x, P
 }
 
 template <int V, bool STRIDED>
-__global__ __launch_bounds__(kEncThreads) void chunk_encode_kernel(Fields fs, PlanArgs pa, Workspace ws) {
+__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(5))) void chunk_encode_kernel(Fields fs, PlanArgs pa, Workspace ws) {
     const uint32_t f = blockIdx.y;
     const Workspace w = lane_ws(ws, f, fs.ws_stride);
     uint8_t *sd = (fs.wdirect >> f) & 1u ? pick(fs.dst, f) + kHeaderBytes : w.widths;
@@ -573,8 +632,8 @@ __device__ __forceinline__ bool unrze_halves(std::integer_sequence<int, B...>, c
     if (readlane(incl, 31) + BM != P || (P2 && readlane(incl, 63) + BM != P2)) return false;
     const uint64_t nz = __ballot(bm != 0);
     const uint32_t nlo = (uint32_t)nz, nhi = (uint32_t)(nz >> 32);
-    const uint32_t top = (nlo | nhi) ? 31u - (uint32_t)__builtin_clz(nlo | nhi) + 1u : 0u;
-    (unrze_halves_plane<B>(blob, P, bm, incl - pc, top, w), ...);
+    const uint32_t wmax = (nlo | nhi) ? 31u - (uint32_t)__builtin_clz(nlo | nhi) + 1u : 0u;
+    (unrze_halves_plane<B>(blob, P, bm, incl - pc, wmax, w), ...);
     return true;
 }
 
@@ -737,7 +796,7 @@ __device__ __forceinline__ void chunk_decode_body(const uint8_t *__restrict__ in
 }
 
 template <int V, bool STRIDED>
-__global__ __launch_bounds__(kBlockThreads) void chunk_decode_kernel(Fields fs, PlanArgs pa, Workspace ws) {
+__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(5))) void chunk_decode_kernel(Fields fs, PlanArgs pa, Workspace ws) {
     const uint32_t f = blockIdx.y;
     chunk_decode_body<V, STRIDED>(pick(fs.src, f), pa, lane_ws(ws, f, fs.ws_stride),
                                   reinterpret_cast<float *>(pick(fs.dst, f)));
