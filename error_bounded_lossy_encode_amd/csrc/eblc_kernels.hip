@@ -256,20 +256,12 @@ __device__ __forceinline__ void slow_tile(const float xs[kEncLaneVals], uint32_t
 
 /* Lorenzo delta of one tile's codes against the previous value (the previous lane's last value
  * by wave_shr, the previous tile's through `carry`, 0 when `reset`), zigzag; codes past n are 0.
- * Writes the zigzag codes to z, the lane's code sum in two exact halves (low 16 bits, and the
- * rest) for centering, and returns the bit width of the lane's 32-value segment. */
-template <bool FULL>
+ * Writes the zigzag codes to z and returns the bit width of the lane's 32-value segment, or 0
+ * without WIDTH (centering changes a block's first code first). */
+template <bool FULL, bool WIDTH>
 __device__ __forceinline__ uint32_t finish_tile(const int32_t q[kEncLaneVals], uint64_t e0, uint64_t n, bool reset,
-                                                int32_t &carry, uint32_t z[kEncLaneVals], uint32_t &slo,
-                                                int32_t &shi) {
+                                                int32_t &carry, uint32_t z[kEncLaneVals]) {
     constexpr int V = kEncLaneVals;
-    slo = 0;
-    shi = 0;
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-        slo += (uint32_t)q[k] & 0xFFFFu;
-        shi += q[k] >> 16;
-    }
     const int32_t prev = (int32_t)dpp<kDppWaveShr1>((uint32_t)carry, (uint32_t)q[V - 1]);
     z[0] = zigzag(reset ? q[0] : q[0] - prev);
 #pragma unroll
@@ -280,11 +272,24 @@ __device__ __forceinline__ uint32_t finish_tile(const int32_t q[kEncLaneVals], u
         for (int k = 0; k < V; ++k)
             if (e0 + k >= n) z[k] = 0;
     }
+    if (!WIDTH) return 0;
     /* segment width: bit length of the OR of its 32 codes */
     uint32_t orv = z[0];
 #pragma unroll
     for (int k = 1; k < V; ++k) orv |= z[k];
     return bit_length(seg_or(orv));
+}
+
+/* A lane's code sum in two exact halves (the low 16 bits of each code, and the rest), for
+ * centering sums that may pass 32 bits. */
+__device__ __forceinline__ void split_sum(const int32_t q[kEncLaneVals], uint32_t &slo, int32_t &shi) {
+    slo = 0;
+    shi = 0;
+#pragma unroll
+    for (int k = 0; k < kEncLaneVals; ++k) {
+        slo += (uint32_t)q[k] & 0xFFFFu;
+        shi += q[k] >> 16;
+    }
 }
 
 /* OR n consecutive codes of width w, already joined into `bits` (code k at bit k w), into the
@@ -361,11 +366,12 @@ __device__ __forceinline__ int32_t block_mean(uint32_t lo, int32_t hi, uint64_t 
     return (int32_t)qd;
 }
 
-/* Centering modes of the encoder: none; blocks of at most one tile whose code sums fit 32 bits
- * (B <= 256 and T + log2 B <= 29, the defaults among them); any power-of-two block; any block
- * that is not a power of two.  The first keeps neither the per-tile totals nor the 64-bit mean
- * of the last two, and so fewer registers. */
-constexpr int kCenterOff = 0, kCenterTile = 1, kCenterAny = 2, kCenterGen = 3;
+/* Centering modes of the encoder: none; blocks shorter than a tile whose code sums fit 32 bits
+ * (B < 256 and T + log2 B <= 29); any power-of-two block; any block that is not a power of two;
+ * blocks of exactly one tile whose sums fit 32 bits (B = 256, the default, and T <= 21), whose
+ * sum and mean are wave-uniform.  The tile modes keep neither the per-tile totals nor the
+ * 64-bit mean of the others, and so fewer registers. */
+constexpr int kCenterOff = 0, kCenterTile = 1, kCenterAny = 2, kCenterGen = 3, kCenterWhole = 4;
 
 /* Where the Lorenzo blocks lie relative to an encode chunk (wave-uniform).  For a block B that
  * is not a power of two, r0 is the chunk start's offset in its block, bk0 the block holding the
@@ -492,16 +498,48 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
             } else {
                 reset = lane_at_block && (((uint32_t)cbase + (uint32_t)t * kEncTile) & bmask) == 0;
             }
-            uint32_t slo;
-            int32_t shi;
-            w[t] = finish_tile<FULL>(q[t], cbase + (uint64_t)t * kEncTile + V * lane, n, reset, carry, z[t],
-                                     slo, shi);
-            if (CM == kCenterTile || (CM == kCenterAny && in_tile)) {
+            /* a block inside the tile changes its first code before the segment width is taken */
+            constexpr bool kTileBlocks = CM == kCenterTile || CM == kCenterWhole;
+            constexpr bool kWholeTile = CM == kCenterWhole;
+            w[t] = finish_tile<FULL, !kTileBlocks>(q[t], cbase + (uint64_t)t * kEncTile + V * lane, n, reset, carry,
+                                                   z[t]);
+            uint32_t slo = 0;
+            int32_t shi = 0;
+            if (CM == kCenterAny || CM == kCenterGen) split_sum(q[t], slo, shi);
+            if (kTileBlocks || (CM == kCenterAny && in_tile)) {
                 const uint32_t seglen = B / V; /* lanes per block */
-                /* narrow codes: one exact 32-bit sum; else the two halves */
-                const bool narrow_sums = CM == kCenterTile || narrow;
+                /* narrow codes: one exact 32-bit sum (the codes' sum wraps exactly); else the two
+                 * halves */
+                const bool narrow_sums = kTileBlocks || narrow;
                 uint32_t lo_s, hi_s = 0;
-                if (narrow_sums) {
+                if (kTileBlocks) {
+                    uint32_t s32 = 0;
+#pragma unroll
+                    for (int k = 0; k < V; ++k) s32 += (uint32_t)q[t][k];
+                    if (kWholeTile) {
+                        /* the tile is the block: its sum, mean and recoded first code are
+                         * wave-uniform, and only lane 0's first code changes.  Segment 0's OR
+                         * leaves that code out and takes the recoded one. */
+                        const uint32_t S = wave_sum(s32);
+                        const uint64_t b0 = cbase + (uint64_t)t * kEncTile;
+                        uint32_t orv = z[t][1] | z[t][2] | z[t][3] | (lane == 0 ? 0u : z[t][0]);
+                        orv = seg_or(orv);
+                        if (FULL || b0 < n) {
+                            const uint32_t c = (FULL || n - b0 >= (uint64_t)B) ? B : (uint32_t)(n - b0);
+                            const int32_t mu = block_mean32((int32_t)S, c);
+                            const uint32_t z0 = zigzag((int32_t)(readlane((uint32_t)q[t][0], 0) - (uint32_t)mu));
+                            if (lane == 0) {
+                                z[t][0] = z0;
+                                means[b0 >> log2B] = mu;
+                            }
+                            if (lane < (uint32_t)kSegLanes) orv |= z0;
+                        }
+                        w[t] = bit_length(orv);
+                        if (j == 0) wid[t * kSegsPerEncTile + g] = (uint8_t)w[t];
+                        continue;
+                    }
+                    lo_s = seg_allsum(s32, seglen);
+                } else if (narrow_sums) {
                     lo_s = seg_allsum(slo + ((uint32_t)shi << 16), seglen);
                 } else {
                     lo_s = seg_allsum(slo, seglen);
@@ -509,10 +547,12 @@ __device__ __forceinline__ void encode_chunk(const float *__restrict__ x, const 
                 }
                 const uint64_t e0 = cbase + (uint64_t)t * kEncTile + V * lane;
                 if (lane_at_block && e0 < n) {
-                    const uint64_t c = (n - e0 < (uint64_t)B) ? n - e0 : (uint64_t)B;
+                    /* a whole block (every block of a full chunk) has c = B, a power of two */
+                    const uint64_t c = (FULL || n - e0 >= (uint64_t)B) ? (uint64_t)B : n - e0;
                     const int32_t mu = narrow_sums ? block_mean32((int32_t)lo_s, (uint32_t)c)
                                                    : block_mean(lo_s, (int32_t)hi_s, c);
-                    z[t][0] = zigzag((int32_t)((uint32_t)unzigzag(z[t][0]) - (uint32_t)mu));
+                    /* the block's first code, coded against its mean instead of 0 */
+                    z[t][0] = zigzag((int32_t)((uint32_t)q[t][0] - (uint32_t)mu));
                     means[e0 >> log2B] = mu;
                 }
                 w[t] = seg_width(z[t]);
@@ -1790,19 +1830,23 @@ hipError_t launch_resolve_abs(const Workspace &ws, double eps, hipStream_t strea
 hipError_t launch_encode(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                          hipStream_t stream) {
     const bool gb = (pa.B & (pa.B - 1)) != 0;
+    const bool narrow = pa.T + pa.log2B <= 29;
     const int cm = !pa.center ? kCenterOff
                    : gb ? kCenterGen
-                   : (pa.B <= (uint32_t)kEncTile && pa.T + pa.log2B <= 29) ? kCenterTile : kCenterAny;
+                   : (pa.B == (uint32_t)kEncTile && narrow) ? kCenterWhole
+                   : (pa.B < (uint32_t)kEncTile && narrow) ? kCenterTile : kCenterAny;
     const dim3 grid(pa.ngroups, nf), block(kEncThreads);
 #define EBLC_ENCODE(S, C, G) eblc_launch((encode_kernel<S, C, G>), grid, block, 0, stream, fs, pa, ws)
     if (pa.lay.strided) {
-        if (cm == kCenterTile) EBLC_ENCODE(true, kCenterTile, false);
+        if (cm == kCenterWhole) EBLC_ENCODE(true, kCenterWhole, false);
+        else if (cm == kCenterTile) EBLC_ENCODE(true, kCenterTile, false);
         else if (cm == kCenterAny) EBLC_ENCODE(true, kCenterAny, false);
         else if (cm == kCenterGen) EBLC_ENCODE(true, kCenterGen, true);
         else if (gb) EBLC_ENCODE(true, kCenterOff, true);
         else EBLC_ENCODE(true, kCenterOff, false);
     } else {
-        if (cm == kCenterTile) EBLC_ENCODE(false, kCenterTile, false);
+        if (cm == kCenterWhole) EBLC_ENCODE(false, kCenterWhole, false);
+        else if (cm == kCenterTile) EBLC_ENCODE(false, kCenterTile, false);
         else if (cm == kCenterAny) EBLC_ENCODE(false, kCenterAny, false);
         else if (cm == kCenterGen) EBLC_ENCODE(false, kCenterGen, true);
         else if (gb) EBLC_ENCODE(false, kCenterOff, true);

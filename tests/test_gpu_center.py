@@ -77,6 +77,22 @@ def test_center_offset_field_ragged(env, B):
     assert ref.size < plain.size
 
 
+@pytest.mark.parametrize("B", [64, 256])
+@pytest.mark.parametrize("T", [15, 21])
+def test_center_narrow_sums_ragged(env, B, T):
+    """Blocks of at most one tile with T + log2 B <= 29 take the encoder's one 32-bit block sum
+    (for B = 256 a wave-uniform one): ragged n with a partial last block, codes up to near 2^T, NaN
+    escapes and a partial last chunk."""
+    rng = np.random.default_rng(40 + B + T)
+    n = 3 * 8192 + 777 + B // 2
+    x = (np.float32(2500.0) + synth.tiny_array(rng, n, "smooth") * np.float32(0.01)).astype(np.float32)
+    x[::997] = np.float32(np.nan)
+    check_case(env, x, [n], f"abs=1e-3;block={B};outlier_log2={T};center=1", f"B={B} T={T}")
+    y = (rng.standard_normal(n) * float(1 << (T - 3)) * 2e-3).astype(np.float32)
+    ref = check_case(env, y, [n], f"abs=1e-3;block={B};outlier_log2={T};center=1", f"wide B={B} T={T}")
+    assert header(ref)["mode"] == 0
+
+
 @pytest.mark.parametrize("B", [64, 256, 1024])
 def test_center_escapes(env, B):
     rng = np.random.default_rng(9 + B)
