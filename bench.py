@@ -228,7 +228,8 @@ def main() -> int:
                          "of the timed steps (up to 8192 launches), for the rooflines")
     ap.add_argument("--event-every", type=int, default=4,
                     help="time the encode and decode launches of every k-th compress and decompress "
-                         "launch sequence of the timed steps (each timed dispatch costs the stream a few "
+                         "launch sequence of the timed steps, and split every k-th step into its compress "
+                         "and decompress time (each timed dispatch and each event costs the stream a few "
                          "microseconds)")
     ap.add_argument("--breakdown-steps", type=int, default=2,
                     help="untimed steps after the timed ones with an event pair around every launch, "
@@ -353,8 +354,13 @@ def main() -> int:
     # timed region: exactly K steps, bracketed by device syncs.  The library records an event
     # pair around each kernel launch of these steps on the stream it runs on (its own lane
     # streams included), up to 8192 launches: the per-kernel times below.
+    # the compress / decompress split: event triples on every event_every-th step, one step
+    # before those whose kernels the library times (so that the split holds no kernel events when
+    # event_every > 1), and on the first step; the other steps carry no markers
+    every = max(1, args.event_every)
+    sampled = [k % every == (every - 2) % every or k == 0 for k in range(args.steps)]
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+           torch.cuda.Event(enable_timing=True)) if sampled[k] else None for k in range(args.steps)]
     timed_launches = min(8192, args.steps * len(items) * 2)
     if args.kernel_events == "on":
         assert binding.eblc_plan_set_profiling(plan.handle, timed_launches, "encode,decode",
@@ -362,6 +368,10 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        if ev[k] is None:
+            compress_all()
+            decompress_all()
+            continue
         ev[k][0].record(stream)
         compress_all()
         ev[k][1].record(stream)
@@ -369,6 +379,7 @@ def main() -> int:
         ev[k][2].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    ev = [e for e in ev if e is not None]
     assert binding.eblc_plan_status(plan.handle) == binding.EBLC_OK
     wall = (t1 - t0) / args.steps
     comp_ms = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
