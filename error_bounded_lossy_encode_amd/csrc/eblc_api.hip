@@ -344,8 +344,13 @@ hipError_t enqueue_decompress(eblc_plan *plan, int nf, const void *const *in, co
         fs.bytes[k] = compressed_bytes[k];
     }
     const uint32_t n = (uint32_t)nf;
-    hipError_t e = timed(plan, "decode_sizes", [&] { return launch_decode_sizes(fs, n, pa, ws, st); });
-    if (e == hipSuccess) e = timed(plan, "decode_scan", [&] { return launch_scan_decompress(fs, n, pa, ws, st); });
+    hipError_t e;
+    if (pa.dchunks <= kSizesScanChunks) {
+        e = timed(plan, "sizes_scan", [&] { return launch_sizes_scan(fs, n, pa, ws, st); });
+    } else {
+        e = timed(plan, "decode_sizes", [&] { return launch_decode_sizes(fs, n, pa, ws, st); });
+        if (e == hipSuccess) e = timed(plan, "decode_scan", [&] { return launch_scan_decompress(fs, n, pa, ws, st); });
+    }
     if (e == hipSuccess)
         e = timed(plan, "decode", [&] {
             return pa.V ? launch_chunk_decode(fs, n, pa, ws, st) : launch_decode(fs, n, pa, ws, st);

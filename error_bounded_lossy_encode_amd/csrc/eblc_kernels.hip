@@ -1380,6 +1380,45 @@ __global__ __launch_bounds__(kBlockThreads) void compact_kernel(Fields fs, PlanA
 
 /* One thread per decode chunk: payload words of the chunk = sum of its width bytes; a width above 32
  * flags the stream.  Quads of threads form the groups the scan runs over. */
+/* Payload words of decode chunk c < dchunks: the sum of its 64 width bytes (bitpack coder), or
+ * the word count the stream holds for it (chunk coder, bitmap included).  bad is set (and the
+ * size taken as 0 for the chunk coder) for a width above 32 or a count out of [V/32, V + V/32]. */
+__device__ __forceinline__ uint32_t chunk_size(const uint8_t *__restrict__ in, const PlanArgs &pa, uint32_t c,
+                                               uint32_t &bad) {
+    uint32_t sum = 0;
+    if (pa.V != 0) {
+        sum = reinterpret_cast<const uint32_t *>(in + kHeaderBytes)[c];
+        if (sum < pa.V / 32 || sum > pa.V + pa.V / 32) {
+            bad = 1u;
+            sum = 0;
+        }
+        return sum;
+    }
+    const uint64_t s0 = (uint64_t)c * kDecSegs;
+    const uint64_t segs = (pa.nseg - s0 < (uint64_t)kDecSegs) ? pa.nseg - s0 : (uint64_t)kDecSegs;
+    const uint8_t *wp = in + kHeaderBytes + s0;
+    if (segs == (uint64_t)kDecSegs) {
+        const uint4 *w4 = reinterpret_cast<const uint4 *>(wp);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 v = w4[i];
+            const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                sum = __builtin_amdgcn_sad_u8(vv[k], 0u, sum);
+                bad |= (((vv[k] & 0x7F7F7F7Fu) + 0x5F5F5F5Fu) | vv[k]) & 0x80808080u;
+            }
+        }
+    } else {
+        for (uint64_t k = 0; k < segs; ++k) {
+            const uint32_t w = wp[k];
+            sum += w;
+            bad |= w > 32 ? 1u : 0u;
+        }
+    }
+    return sum;
+}
+
 __device__ __forceinline__ void decode_sizes_body(const uint8_t *__restrict__ in,
                                                   uint64_t in_bytes, PlanArgs pa, Workspace ws) {
     const uint32_t c = blockIdx.x * 256 + threadIdx.x;
@@ -1413,40 +1452,9 @@ __device__ __forceinline__ void decode_sizes_body(const uint8_t *__restrict__ in
             for (int u = 0; u < kTouchBatch; ++u) touched |= v[u];
         }
     }
-    uint32_t sum = 0, bad = 0;
-    if (pa.V != 0) {
-        /* chunk coder: the stream holds each chunk's word count, bitmap included */
-        if (c < pa.dchunks) {
-            sum = reinterpret_cast<const uint32_t *>(in + kHeaderBytes)[c];
-            bad = (sum < pa.V / 32 || sum > pa.V + pa.V / 32) ? 1u : 0u;
-            if (bad) sum = 0;
-            ws.chunk_words[c] = sum;
-        }
-    } else if (c < pa.dchunks) {
-        const uint64_t s0 = (uint64_t)c * kDecSegs;
-        const uint64_t segs = (pa.nseg - s0 < (uint64_t)kDecSegs) ? pa.nseg - s0 : (uint64_t)kDecSegs;
-        const uint8_t *wp = in + kHeaderBytes + s0;
-        if (segs == (uint64_t)kDecSegs) {
-            const uint4 *w4 = reinterpret_cast<const uint4 *>(wp);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 v = w4[i];
-                const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    sum = __builtin_amdgcn_sad_u8(vv[k], 0u, sum);
-                    bad |= (((vv[k] & 0x7F7F7F7Fu) + 0x5F5F5F5Fu) | vv[k]) & 0x80808080u;
-                }
-            }
-        } else {
-            for (uint64_t k = 0; k < segs; ++k) {
-                const uint32_t w = wp[k];
-                sum += w;
-                bad |= w > 32 ? 1u : 0u;
-            }
-        }
-        ws.chunk_words[c] = sum;
-    }
+    uint32_t bad = 0;
+    const uint32_t sum = c < pa.dchunks ? chunk_size(in, pa, c, bad) : 0u;
+    if (c < pa.dchunks) ws.chunk_words[c] = sum;
     uint32_t g = sum;
     g += dpp<kDppQuadXor1>(0, g);
     g += dpp<kDppQuadXor2>(0, g);
@@ -1468,7 +1476,7 @@ __device__ __forceinline__ uint64_t ld64(const uint32_t *h, int i) {
 
 __device__ __forceinline__ void scan_decompress_body(const uint8_t *__restrict__ in,
                                                      uint64_t in_bytes, PlanArgs pa,
-                                                     Workspace ws) {
+                                                     Workspace ws, bool sizes_bad = false) {
     /* the header, staged in LDS before the scan so that its loads overlap it (block_scan2
      * synchronizes the workgroup before it returns) */
     __shared__ uint32_t s_h[32];
@@ -1501,7 +1509,7 @@ __device__ __forceinline__ void scan_decompress_body(const uint8_t *__restrict__
         ok = ok && m == 0 && pb == 4 * n && po == kHeaderBytes && oi == end && ov == end && total == end;
     } else {
         ok = ok && eb_f >= FLT_MIN && eb_f <= FLT_MAX && fabsf(s) <= FLT_MAX && s == 2.0f * eb_f;
-        ok = ok && m <= n && (pb & 3) == 0 && pb == 4 * (uint64_t)tot[0] && info->width_bad == 0;
+        ok = ok && m <= n && (pb & 3) == 0 && pb == 4 * (uint64_t)tot[0] && info->width_bad == 0 && !sizes_bad;
         const uint64_t msec = (flags && B) ? align16(4 * ((n + B - 1) / B)) : 0;
         ok = ok && po == kHeaderBytes + pa.wsec + msec && oi == po + align16(pb);
         ok = ok && ov == oi + align16(4 * m) && total == ov + align16(4 * m);
@@ -1524,6 +1532,41 @@ __device__ __forceinline__ void scan_decompress_body(const uint8_t *__restrict__
 __global__ __launch_bounds__(kScanThreads) void scan_decompress_kernel(Fields fs, PlanArgs pa, Workspace ws) {
     const uint32_t f = blockIdx.y;
     scan_decompress_body(pick(fs.src, f), pick(fs.bytes, f), pa, lane_ws(ws, f, fs.ws_stride));
+}
+
+/* K6 for small fields (dchunks <= kSizesScanChunks): one workgroup per field takes the sizes of
+ * every decode chunk, kSizesBatch per thread with their loads issued together, and then runs the
+ * scan and header validation, one launch instead of two.  The group sums it writes are read by
+ * the scan after the barrier; its bad-width flag reaches the validation through LDS. */
+constexpr int kSizesBatch = 4;
+__global__ __launch_bounds__(kScanThreads) void sizes_scan_kernel(Fields fs, PlanArgs pa, Workspace ws) {
+    __shared__ uint32_t s_bad;
+    const uint32_t f = blockIdx.y;
+    const uint8_t *in = pick(fs.src, f);
+    const Workspace w = lane_ws(ws, f, fs.ws_stride);
+    if (threadIdx.x == 0) s_bad = 0;
+    __syncthreads();
+    uint32_t bad = 0;
+    for (uint32_t base = 0; base < pa.dchunks; base += kSizesBatch * kScanThreads) {
+        uint32_t sum[kSizesBatch];
+#pragma unroll
+        for (int j = 0; j < kSizesBatch; ++j) {
+            const uint32_t c = base + (uint32_t)j * kScanThreads + threadIdx.x;
+            sum[j] = c < pa.dchunks ? chunk_size(in, pa, c, bad) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kSizesBatch; ++j) {
+            const uint32_t c = base + (uint32_t)j * kScanThreads + threadIdx.x;
+            if (c < pa.dchunks) w.chunk_words[c] = sum[j];
+            uint32_t g = sum[j];
+            g += dpp<kDppQuadXor1>(0, g);
+            g += dpp<kDppQuadXor2>(0, g);
+            if ((threadIdx.x & 3) == 0 && c / kDecChunksPerGroup < pa.dgroups) w.group_words[c / kDecChunksPerGroup] = g;
+        }
+    }
+    if (bad) atomicOr(&s_bad, 1u);
+    __syncthreads();
+    scan_decompress_body(in, pick(fs.bytes, f), pa, w, s_bad != 0);
 }
 
 /* ---- K7: fused decode ------------------------------------------------------------------------ */
@@ -1882,6 +1925,12 @@ hipError_t launch_decode_sizes(const Fields &fs, uint32_t nf, const PlanArgs &pa
 hipError_t launch_scan_decompress(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                                   hipStream_t stream) {
     eblc_launch(scan_decompress_kernel, dim3(1, nf), dim3(kScanThreads), 0, stream, fs, pa, ws);
+    return hipGetLastError();
+}
+
+hipError_t launch_sizes_scan(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
+                             hipStream_t stream) {
+    eblc_launch(sizes_scan_kernel, dim3(1, nf), dim3(kScanThreads), 0, stream, fs, pa, ws);
     return hipGetLastError();
 }
 
