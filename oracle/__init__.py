@@ -82,7 +82,7 @@ def lib():
         L.oracle_rze.restype = u32
         L.oracle_unrze.argtypes = [P, u32, u32, P]
         L.oracle_unrze.restype = i32
-        L.oracle_chunk_stream_bytes.argtypes = [u64, u64, u64]
+        L.oracle_chunk_stream_bytes.argtypes = [u64, u32, u64, u64]
         L.oracle_chunk_stream_bytes.restype = u64
         L.oracle_compress_chunked.argtypes = [P, i32, P, i32, f64, u32, i32, u64, P, u64, P]
         L.oracle_compress_chunked.restype = u64
@@ -222,8 +222,8 @@ def unrze(data: np.ndarray, W: int):
     return None if st != 0 else words
 
 
-def chunk_stream_bytes(nchunks: int, sum_words: int, m: int) -> int:
-    return int(lib().oracle_chunk_stream_bytes(nchunks, sum_words, m))
+def chunk_stream_bytes(n: int, V: int, sum_words: int, m: int) -> int:
+    return int(lib().oracle_chunk_stream_bytes(n, V, sum_words, m))
 
 
 def decompress(stream: np.ndarray, n: int | None = None):

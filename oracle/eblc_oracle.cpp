@@ -15,7 +15,7 @@ namespace {
 
 /* ---- stream layout constants, written out independently of the GPU library ---------- */
 const uint32_t kMagic = 0x434C4245u; /* "EBLC" little-endian */
-const uint16_t kVersion = 1;
+const uint16_t kVersion = 2;
 const uint16_t kHeaderBytes = 128;
 const uint8_t kModeLossy = 0;
 const uint8_t kModeRaw = 1;
@@ -23,6 +23,31 @@ const uint8_t kModeChunk = 2; /* the chunk-cooperative coder: Quant -> Diff -> B
 const uint32_t kSeg = 32; /* values per bitpack segment */
 
 uint64_t align16(uint64_t v) { return (v + 15u) / 16u * 16u; }
+
+/* The offset table, an index of this codec's own container (the pages' concatenated output
+ * records each buffer's size ahead of its data, "Architecture", Execution Flow, Compression,
+ * so that a file describes itself): the payload words that precede each group of
+ * kGroupValues values, one u32 per group after the first, in a section of its own after the
+ * outlier values, padded to 16 bytes.  A decoder takes any group's payload offset from it. */
+const uint64_t kGroupValues = 8192;
+
+uint64_t table_bytes(uint64_t n) {
+    uint64_t groups = (n + kGroupValues - 1) / kGroupValues;
+    return groups > 1 ? align16(4 * (groups - 1)) : 0;
+}
+
+/* The table's entries from the payload words of each coded unit (a segment of the bitpack
+ * coder, a chunk of the chunk coder), units_per_group units to a group: entry g - 1 is the
+ * sum over the units before group g. */
+std::vector<uint32_t> table_entries(const std::vector<uint64_t> &unit_words, uint64_t units_per_group) {
+    std::vector<uint32_t> t;
+    uint64_t acc = 0;
+    for (uint64_t u = 0; u < unit_words.size(); ++u) {
+        if (u > 0 && u % units_per_group == 0) t.push_back((uint32_t)acc);
+        acc += unit_words[u];
+    }
+    return t;
+}
 
 void put_u8(uint8_t *p, uint64_t off, uint8_t v) { p[off] = v; }
 void put_u16(uint8_t *p, uint64_t off, uint16_t v) { std::memcpy(p + off, &v, 2); }
@@ -209,7 +234,7 @@ uint64_t oracle_stream_bytes(uint64_t n, uint64_t sum_widths, uint64_t m) {
     uint64_t payload_off = kHeaderBytes + align16(nseg);
     uint64_t oidx_off = payload_off + align16(4 * sum_widths);
     uint64_t oval_off = oidx_off + align16(4 * m);
-    return oval_off + align16(4 * m);
+    return oval_off + align16(4 * m) + table_bytes(n);
 }
 
 uint64_t oracle_raw_bytes(uint64_t n) { return kHeaderBytes + align16(4 * n); }
@@ -318,12 +343,14 @@ int oracle_unrze(const uint32_t *in, uint32_t len, uint32_t W, uint32_t *words) 
     return 0;
 }
 
-/* Size of a chunk-coder stream from its chunk count, total chunk words and outlier count. */
-uint64_t oracle_chunk_stream_bytes(uint64_t nchunks, uint64_t sum_words, uint64_t m) {
+/* Size of a chunk-coder stream of n values in chunks of V from its total chunk words and
+ * outlier count. */
+uint64_t oracle_chunk_stream_bytes(uint64_t n, uint32_t V, uint64_t sum_words, uint64_t m) {
+    uint64_t nchunks = (n + V - 1) / V;
     uint64_t payload_off = kHeaderBytes + align16(4 * nchunks);
     uint64_t oidx_off = payload_off + align16(4 * sum_words);
     uint64_t oval_off = oidx_off + align16(4 * m);
-    return oval_off + align16(4 * m);
+    return oval_off + align16(4 * m) + table_bytes(n);
 }
 
 /* The 128-byte header: magic, version, layout of the sections (all offsets from the start). */
@@ -443,6 +470,11 @@ uint64_t oracle_compress_ex(const float *x, int rank, const uint64_t *dims, int 
         put_u32(out, oidx_off + 4 * k, oidx[k]);
         put_u32(out, oval_off + 4 * k, oval[k]);
     }
+    /* the offset table: segments of 32 values, kGroupValues / 32 to a group */
+    std::vector<uint64_t> seg_words(widths.begin(), widths.end());
+    std::vector<uint32_t> table = table_entries(seg_words, kGroupValues / kSeg);
+    uint64_t table_off = oval_off + align16(4 * m);
+    for (uint64_t g = 0; g < table.size(); ++g) put_u32(out, table_off + 4 * g, table[g]);
     return total;
 }
 
@@ -497,10 +529,10 @@ uint64_t oracle_compress_chunked(const float *x, int rank, const uint64_t *dims,
             if (esc[i]) { oidx.push_back((uint32_t)i); oval.push_back(f32_bits(x[i])); }
         }
         if (oidx.size() > side_max) raw = true;
-        else if (oracle_chunk_stream_bytes(nchunks, payload.size(), oidx.size()) > oracle_raw_bytes(n)) raw = true;
+        else if (oracle_chunk_stream_bytes(n, V, payload.size(), oidx.size()) > oracle_raw_bytes(n)) raw = true;
     }
 
-    uint64_t total = raw ? oracle_raw_bytes(n) : oracle_chunk_stream_bytes(nchunks, payload.size(), oidx.size());
+    uint64_t total = raw ? oracle_raw_bytes(n) : oracle_chunk_stream_bytes(n, V, payload.size(), oidx.size());
     if (required) *required = total;
     if (total > cap) return 0;
     std::memset(out, 0, total);
@@ -522,6 +554,11 @@ uint64_t oracle_compress_chunked(const float *x, int rank, const uint64_t *dims,
         put_u32(out, oidx_off + 4 * k, oidx[k]);
         put_u32(out, oval_off + 4 * k, oval[k]);
     }
+    /* the offset table: chunks of V values, kGroupValues / V to a group */
+    std::vector<uint64_t> chunk_words(sizes.begin(), sizes.end());
+    std::vector<uint32_t> table = table_entries(chunk_words, kGroupValues / V);
+    uint64_t table_off = oval_off + align16(4 * m);
+    for (uint64_t g = 0; g < table.size(); ++g) put_u32(out, table_off + 4 * g, table[g]);
     return total;
 }
 
@@ -571,7 +608,8 @@ static uint64_t check_header(const uint8_t *in, uint64_t len) {
             uint64_t nchunks = (n + B - 1) / B;
             if (pb > 4ull * nchunks * (B + B / 32) || po != kHeaderBytes + align16(4 * nchunks)) return 0;
         }
-        if (oi != po + align16(pb) || ov != oi + align16(4 * m) || tot != ov + align16(4 * m)) return 0;
+        if (oi != po + align16(pb) || ov != oi + align16(4 * m)) return 0;
+        if (tot != ov + align16(4 * m) + table_bytes(n)) return 0;
     }
     if (tot > len) return 0;
     return n;
@@ -654,6 +692,22 @@ int oracle_decompress(const uint8_t *in, uint64_t len, float *out, uint64_t n_ou
         }
     } else {
         if (!widths_to_deltas(in, n, pb, po, d.data())) return ORACLE_CORRUPT;
+    }
+    /* the offset table must index the payload the sizes section describes */
+    {
+        std::vector<uint64_t> unit_words;
+        uint64_t units_per_group;
+        if (mode == kModeChunk) {
+            for (uint64_t c = 0; c < (n + B - 1) / B; ++c) unit_words.push_back(get_u32(in, kHeaderBytes + 4 * c));
+            units_per_group = kGroupValues / B;
+        } else {
+            for (uint64_t k = 0; k < (n + kSeg - 1) / kSeg; ++k) unit_words.push_back(in[kHeaderBytes + k]);
+            units_per_group = kGroupValues / kSeg;
+        }
+        std::vector<uint32_t> table = table_entries(unit_words, units_per_group);
+        uint64_t table_off = ov + align16(4 * m);
+        for (uint64_t g = 0; g < table.size(); ++g)
+            if (get_u32(in, table_off + 4 * g) != table[g]) return ORACLE_CORRUPT;
     }
     /* undelta: running sum from each block start (from the block's mean when the stream is
      * centered, else from 0), then dequantize */

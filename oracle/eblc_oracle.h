@@ -70,7 +70,8 @@ uint64_t oracle_pack(const uint32_t *z, uint64_t n, const uint8_t *widths, uint3
 uint32_t oracle_unpack_one(const uint32_t *words, uint32_t w, uint32_t j);
 
 /* Size of the stream the oracle would write for these parameters, given sum of widths
- * and outlier count (closed form of the layout). */
+ * and outlier count (closed form of the layout, the offset table included: one u32 for each
+ * group of 8192 values after the first, padded to 16 bytes). */
 uint64_t oracle_stream_bytes(uint64_t n, uint64_t sum_widths, uint64_t m);
 uint64_t oracle_raw_bytes(uint64_t n);
 
@@ -101,7 +102,8 @@ void oracle_bitshuffle(const uint32_t *z, uint32_t V, uint32_t *words);
 void oracle_unbitshuffle(const uint32_t *words, uint32_t V, uint32_t *z);
 uint32_t oracle_rze(const uint32_t *words, uint32_t W, uint32_t *out);
 int oracle_unrze(const uint32_t *in, uint32_t len, uint32_t W, uint32_t *words);
-uint64_t oracle_chunk_stream_bytes(uint64_t nchunks, uint64_t sum_words, uint64_t m);
+/* Size of a chunk-coder stream of n values in chunks of V (offset table included). */
+uint64_t oracle_chunk_stream_bytes(uint64_t n, uint32_t V, uint64_t sum_words, uint64_t m);
 
 /* Whole compressor with the chunk-cooperative coder: Quant -> Diff (first difference reset at
  * every chunk, zigzag-folded) -> Bitshuffle -> RZE over chunks of V = 1024, 2048 or 4096

@@ -9,7 +9,7 @@ flattened index at multiples of the block (or chunk) length.  So the field can b
 piece with the oracle, all pieces under the bound resolved once on the whole field (passed in
 absolute mode: an fp32 bound given as eps is taken as it is), and the pieces' sections joined
 in order: widths (or chunk word counts), block means, payload words, outlier indices shifted by
-the piece's start, outlier values.  The joined stream must equal the whole-field stream byte for
+the piece's start, outlier values; the offset table is then taken again from the joined sizes.  The joined stream must equal the whole-field stream byte for
 byte, and the pieces can be coded on as many threads as there are pieces (ctypes releases the
 interpreter lock during each oracle call).
 """
@@ -22,6 +22,7 @@ import numpy as np
 import oracle
 
 HEADER = 128
+GROUP_VALUES = 8192  # values per entry of the stream's offset table
 
 
 def _align16(v: int) -> int:
@@ -111,7 +112,7 @@ def join(x: np.ndarray, dims, T: int, B: int, side_max: int, center: bool, V: in
     m = int(sum(h["m"] for h in hs))
     sum_words = pay.size // 4
     if V:
-        coded = oracle.chunk_stream_bytes((n + V - 1) // V, sum_words, m)
+        coded = oracle.chunk_stream_bytes(n, V, sum_words, m)
     elif center:
         coded = oracle.stream_bytes_centered(n, B, sum_words, m)
     else:
@@ -145,7 +146,13 @@ def join(x: np.ndarray, dims, T: int, B: int, side_max: int, center: bool, V: in
     po = HEADER + size_sec + msec
     oi = po + _align16(pay.size)
     ov = oi + _align16(4 * m)
-    total = ov + _align16(4 * m)
+    # the offset table: payload words before each group of GROUP_VALUES values after the first
+    unit_words = sizes.view(np.uint32).astype(np.int64) if V else sizes.astype(np.int64)
+    per_group = GROUP_VALUES // (V if V else 32)
+    starts = np.arange(per_group, unit_words.size, per_group)
+    table = np.concatenate([[0], np.cumsum(unit_words)])[starts].astype(np.uint32)
+    tab = ov + _align16(4 * m)
+    total = tab + _align16(4 * table.size)
     hu32[17] = 1 if (center and not V) else 0
     hu64[9], hu64[10], hu64[12], hu64[13], hu64[14], hu64[15] = m, pay.size, po, oi, ov, total
     out = np.zeros(total, np.uint8)
@@ -158,4 +165,5 @@ def join(x: np.ndarray, dims, T: int, B: int, side_max: int, center: bool, V: in
     if m:
         out[oi:oi + 4 * m] = np.concatenate(oidx).view(np.uint8)
         out[ov:ov + 4 * m] = np.concatenate(oval)
+    out[tab:tab + 4 * table.size] = table.view(np.uint8)
     return out

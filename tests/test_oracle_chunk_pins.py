@@ -58,7 +58,7 @@ def test_golden_chunk_stream():
     x = np.arange(n, dtype=np.float32)
     s = oracle.compress_chunked(x, inp["dims"], False, inp["eps"], inp["chunk_values"], inp["outlier_log2"])
     h = hdr(s)
-    assert h["magic"] == 0x434C4245 and h["version"] == 1 and h["header_bytes"] == 128
+    assert h["magic"] == 0x434C4245 and h["version"] == 2 and h["header_bytes"] == 128
     assert h["mode"] == exp["mode"] and h["log2_seg"] == exp["log2_seg"] and h["B"] == exp["B"]
     assert h["T"] == inp["outlier_log2"] and h["n"] == n and h["dims"] == [n, 0, 0, 0]
     assert h["eb_f_bits"] == int(exp["eb_f_bits"], 16)
@@ -196,7 +196,7 @@ def test_chunk_coder_reconstruction_equals_bitpack_coder(seed):
     nch = (n + V - 1) // V
     sizes = s[128:128 + 4 * nch].view(np.uint32).astype(np.int64)
     assert 4 * sizes.sum() == hs["payload_bytes"]
-    assert len(s) == oracle.chunk_stream_bytes(nch, int(sizes.sum()), hs["m"])
+    assert len(s) == oracle.chunk_stream_bytes(n, V, int(sizes.sum()), hs["m"])
     if hb["mode"] == 0:
         _, yb = oracle.decompress(b)
         assert np.array_equal(y.view(np.uint32), yb.view(np.uint32))
@@ -209,6 +209,42 @@ def test_chunk_coder_reconstruction_equals_bitpack_coder(seed):
     assert np.array_equal(y[~fin].view(np.uint32), x[~fin].view(np.uint32))
 
 
+def test_golden_chunk_table_stream():
+    """W7: the chunk coder over three 8192-value groups, hand-derived down to the offset table."""
+    g = json.load(open(os.path.join(GOLDEN, "w7_chunk_step20000_table.json")))
+    inp, exp = g["input"], g["expect"]
+    n = inp["n"]
+    x = np.empty(n, np.float32)
+    for a, b, v in inp["values"]:
+        x[a:b] = v
+    s = oracle.compress_chunked(x, inp["dims"], False, inp["eps"], inp["chunk_values"], inp["outlier_log2"], n)
+    h = hdr(s)
+    assert h["version"] == 2 and h["mode"] == exp["mode"] and h["B"] == exp["B"] and h["m"] == 0
+    assert h["payload_off"] == exp["payload_off"] and h["oidx_off"] == exp["oidx_off"]
+    assert h["oval_off"] == exp["oval_off"] and h["total"] == exp["total_bytes"] == len(s)
+    nch = len(exp["chunk_words"])
+    assert [int(v) for v in s[128:128 + 4 * nch].view(np.uint32)] == exp["chunk_words"]
+    assert h["payload_bytes"] == 4 * exp["payload_words_count"]
+    words = s[h["payload_off"]:h["payload_off"] + h["payload_bytes"]].view(np.uint32)
+    want = []
+    for cw in exp["chunk_words"]:
+        spec = exp["chunk_payload"][str(cw)]
+        bm = [0] * 32
+        for k, v in spec["bitmap_nonzero"].items():
+            bm[int(k)] = int(v, 16)
+        want += bm + [int(v, 16) for v in spec["words"]]
+    assert [int(v) for v in words] == want
+    t0 = exp["table_off"]
+    assert [int(v) for v in s[t0:t0 + 4 * len(exp["table"])].view(np.uint32)] == exp["table"]
+    assert not s[t0 + 4 * len(exp["table"]):].any()
+    st, y = oracle.decompress(s)
+    assert st == oracle.OK and np.array_equal(y, x)
+    for k in range(len(exp["table"])):
+        t = s.copy()
+        t[t0 + 4 * k:t0 + 4 * k + 4] = np.array([exp["table"][k] + 1], np.uint32).view(np.uint8)
+        assert oracle.decompress(t)[0] == oracle.CORRUPT, k
+
+
 @pytest.mark.parametrize("V", CHUNKS)
 def test_zero_codes_cost_the_bitmap_only(V):
     n = 3 * V - 5
@@ -217,8 +253,13 @@ def test_zero_codes_cost_the_bitmap_only(V):
     h = hdr(s)
     assert h["mode"] == 2
     assert [int(v) for v in s[128:128 + 12].view(np.uint32)] == [V // 32] * 3
-    assert h["payload_bytes"] == 3 * 4 * (V // 32) and not s[h["payload_off"]:].any()
-    assert len(s) == 128 + 16 + 3 * 4 * (V // 32)
+    assert h["payload_bytes"] == 3 * 4 * (V // 32) and not s[h["payload_off"]:h["oidx_off"]].any()
+    # the offset table: one entry per 8192-value group after the first, each the bitmap words
+    # of the chunks before its group (only the 16 KiB chunks span more than one group here)
+    table = [(8192 // V) * (V // 32)] if n > 8192 else []
+    tb = 16 * ((4 * len(table) + 15) // 16)
+    assert [int(v) for v in s[h["oval_off"]:h["oval_off"] + 4 * len(table)].view(np.uint32)] == table
+    assert len(s) == 128 + 16 + 3 * 4 * (V // 32) + tb
 
 
 def test_chunk_raw_fallbacks():

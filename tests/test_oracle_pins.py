@@ -60,7 +60,7 @@ def test_golden_stream(name):
         x[:4] = [1.0, 5.0, 2.0, np.float32(np.nan)]
     s = oracle.compress(x, inp["dims"], **parse_opts(inp))
     h = hdr(s)
-    assert h["magic"] == 0x434C4245 and h["version"] == 1 and h["header_bytes"] == 128
+    assert h["magic"] == 0x434C4245 and h["version"] == 2 and h["header_bytes"] == 128
     assert h["mode"] == exp["mode"] and h["rank"] == 1 and h["log2_seg"] == 5
     assert h["T"] == inp["outlier_log2"] and h["B"] == inp["block"]
     assert h["dims"] == [n, 0, 0, 0] and h["n"] == n and h["reserved"] == 0
@@ -90,6 +90,69 @@ def test_golden_stream(name):
     st, y = oracle.decompress(s)
     assert st == oracle.OK
     assert np.array_equal(y.view(np.uint32), x.view(np.uint32))
+
+
+def _step_field(inp):
+    x = np.empty(inp["n"], np.float32)
+    for a, b, v in inp["values"]:
+        x[a:b] = v
+    return x
+
+
+def test_golden_table_stream():
+    """W6: a field of three 8192-value groups, hand-derived down to the offset table."""
+    g = json.load(open(os.path.join(GOLDEN, "w6_step20000_table.json")))
+    inp, exp = g["input"], g["expect"]
+    n = inp["n"]
+    x = _step_field(inp)
+    s = oracle.compress(x, inp["dims"], False, inp["eps"], inp["block"], inp["outlier_log2"], n)
+    h = hdr(s)
+    assert h["version"] == 2 and h["mode"] == exp["mode"] and h["m"] == 0
+    assert h["eb_f_bits"] == int(exp["eb_f_bits"], 16) and h["s_bits"] == int(exp["s_bits"], 16)
+    assert h["payload_off"] == exp["payload_off"] and h["oidx_off"] == exp["oidx_off"]
+    assert h["oval_off"] == exp["oval_off"] and h["total"] == exp["total_bytes"] == len(s)
+    nseg = (n + 31) // 32
+    want_w = np.zeros(nseg, np.uint8)
+    want_w[0:8 * 32:8] = 5
+    want_w[8 * 32:8 * 79:8] = 4
+    assert np.array_equal(s[128:128 + nseg], want_w)
+    assert h["payload_bytes"] == 4 * exp["payload_words_count"]
+    words = s[h["payload_off"]:h["payload_off"] + h["payload_bytes"]].view(np.uint32)
+    want = np.zeros(exp["payload_words_count"], np.uint32)
+    for k, v in exp["payload_words_nonzero"].items():
+        want[int(k)] = int(v, 16)
+    assert np.array_equal(words, want)
+    t0 = exp["table_off"]
+    assert [int(v) for v in s[t0:t0 + 4 * len(exp["table"])].view(np.uint32)] == exp["table"]
+    assert not s[t0 + 4 * len(exp["table"]):].any()
+    st, y = oracle.decompress(s)
+    assert st == oracle.OK and np.array_equal(y, x)
+    # a table that does not index the payload is refused, entry by entry
+    for k in range(len(exp["table"])):
+        for delta in (1, -1):
+            t = s.copy()
+            t[t0 + 4 * k:t0 + 4 * k + 4] = np.array([exp["table"][k] + delta], np.uint32).view(np.uint8)
+            assert oracle.decompress(t)[0] == oracle.CORRUPT, (k, delta)
+    # and a stream cut before its table
+    assert oracle.decompress(s[:t0], n)[0] == oracle.CORRUPT
+
+
+@pytest.mark.parametrize("n", [8192, 8193, 16384, 16385, 40000])
+def test_table_size_closed_form(n):
+    """One entry per 8192-value group after the first, padded to 16 bytes; the entries are the
+    running sums of the widths at every 256th segment."""
+    rng = np.random.default_rng(n)
+    x = np.cumsum(rng.standard_normal(n)).astype(np.float32)
+    s = oracle.compress(x, [n], True, 1e-3, 256, 15, n)
+    h = hdr(s)
+    assert h["mode"] == 0
+    groups = (n + 8191) // 8192
+    assert h["total"] == h["oval_off"] + 16 * ((4 * h["m"] + 15) // 16) + 16 * ((4 * (groups - 1) + 15) // 16)
+    t0 = h["oval_off"] + 16 * ((4 * h["m"] + 15) // 16)
+    nseg = (n + 31) // 32
+    run = np.cumsum(s[128:128 + nseg].astype(np.int64))
+    got = s[t0:t0 + 4 * (groups - 1)].view(np.uint32)
+    assert [int(v) for v in got] == [int(run[256 * g - 1]) for g in range(1, groups)]
 
 
 # ---------------------------------------------------------------------------------------------
@@ -461,7 +524,7 @@ def test_corrupt_streams_rejected():
 
     bad = [
         mutate(0, np.uint32, 0x12345678),          # magic
-        mutate(4, np.uint16, 2),                   # version
+        mutate(4, np.uint16, 1),                   # version (streams of format 1 carry no offset table)
         mutate(8, np.uint8, 7),                    # mode
         mutate(10, np.uint8, 4),                   # log2 segment
         mutate(11, np.uint8, 31),                  # outlier log2
