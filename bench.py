@@ -510,10 +510,7 @@ def main() -> int:
     launches_per_stage = -(-len(items) // lanes)
     comp_kernels = ("range_partial_kernel", "range_resolve_kernel", kernels[0], "scan_compress_kernel",
                     "compact_kernel")
-    # fields of at most 2048 decode chunks take their sizes and scan in one launch
-    dchunks = -(-n // (args.chunk_bytes // 4 if args.coder == "chunk" else 2048))
-    sizes_kernels = ("sizes_scan_kernel",) if dchunks <= 2048 else ("decode_sizes_kernel", "scan_decompress_kernel")
-    dec_kernels = sizes_kernels + (kernels[1], "patch_kernel")
+    dec_kernels = (kernels[1], "patch_kernel")
 
     def call_frac(alg, ms, ks):
         secs = ms * 1e-3

@@ -6,8 +6,9 @@
  * creation), it owns a workspace allocated up front (the PREALLOCATE policy of the FZGPUModules
  * "Architecture" page, MemoryPool section), so compress and decompress allocate nothing.
  * Compress enqueues range (relative mode) -> encode -> scan -> compaction with outliers on the
- * caller's stream and waits once to return the stream length; decompress enqueues sizes ->
- * scan -> decode -> outlier patch and returns at once.
+ * caller's stream and waits once to return the stream length; decompress enqueues decode
+ * (which takes each group's payload offset from the stream's offset table) -> outlier patch and
+ * returns at once.
  */
 #include "eblc.h"
 #include "eblc_internal.h"
@@ -212,12 +213,24 @@ eblc_status parse_options(const char *opts, Options *o) {
     return EBLC_OK;
 }
 
-/* The largest payload, in 32-bit words, a field of n values can take: 32 words per 32-value
- * segment for the bitpack coder; for the chunk coder (V values per chunk) the bitmap and every
- * plane word of every chunk, the last one padded. */
-uint64_t max_payload_words(uint64_t n, uint32_t V) {
-    if (V == 0) return 32 * ((n + 31) / 32);
-    return ((n + V - 1) / V) * (uint64_t)(V + V / 32);
+
+/* The header words every stream this plan decodes holds, and their masks (DevInfo). */
+void header_template(const PlanArgs &pa, DevInfo *info) {
+    auto put = [&](int i, uint32_t want, uint32_t mask) {
+        info->hdr_want[i] = want;
+        info->hdr_mask[i] = mask;
+    };
+    put(0, kMagic, ~0u);
+    put(1, kVersion | (kHeaderBytes << 16), ~0u);
+    put(2, pa.rank << 8, 0xff00u); /* the rank byte; mode, segment and T are checked apart */
+    for (int a = 0; a < 4; ++a) {
+        put(4 + 2 * a, (uint32_t)pa.dims[a], ~0u);
+        put(5 + 2 * a, (uint32_t)(pa.dims[a] >> 32), ~0u);
+    }
+    put(12, (uint32_t)pa.n, ~0u);
+    put(13, (uint32_t)(pa.n >> 32), ~0u);
+    put(22, kHeaderBytes, ~0u);
+    put(23, 0u, ~0u);
 }
 
 /* Absolute bound resolved on the host with the same fp64 -> fp32 round-toward-zero rule the
@@ -284,7 +297,8 @@ eblc_status check_compress_args(const eblc_plan *plan, const float *in, const vo
 eblc_status check_decompress_args(const eblc_plan *plan, const void *in, size_t compressed_bytes, const float *out) {
     if (in == nullptr || out == nullptr) return EBLC_INVALID_ARGUMENT;
     if (!aligned16(in) || !field_ptr_ok(plan, out)) return EBLC_INVALID_ARGUMENT;
-    if (compressed_bytes < kHeaderBytes + plan->pa.wsec ||
+    /* every stream (RAW ones too) reaches past its header, size section and offset table */
+    if (compressed_bytes < kHeaderBytes + plan->pa.wsec + table_bytes(plan->pa.ngroups) ||
         compressed_bytes > kHeaderBytes + align_up(4 * plan->pa.n, 16))
         return EBLC_CORRUPT_STREAM;
     return EBLC_OK;
@@ -330,7 +344,8 @@ hipError_t enqueue_compress(eblc_plan *plan, int nf, const float *const *in, voi
 }
 
 /* Enqueue the decompress of nf <= lanes streams on `st`, stream k in lane k's workspace:
- * sizes -> scan (which validates the header) -> decode -> outlier patch. */
+ * decode (every workgroup checks the header and its group's entry of the offset table) ->
+ * outlier patch. */
 hipError_t enqueue_decompress(eblc_plan *plan, int nf, const void *const *in, const size_t *compressed_bytes,
                               float *const *out, hipStream_t st) {
     const PlanArgs pa = launch_args(plan, reinterpret_cast<const void *const *>(out), nf);
@@ -344,17 +359,9 @@ hipError_t enqueue_decompress(eblc_plan *plan, int nf, const void *const *in, co
         fs.bytes[k] = compressed_bytes[k];
     }
     const uint32_t n = (uint32_t)nf;
-    hipError_t e;
-    if (pa.dchunks <= kSizesScanChunks) {
-        e = timed(plan, "sizes_scan", [&] { return launch_sizes_scan(fs, n, pa, ws, st); });
-    } else {
-        e = timed(plan, "decode_sizes", [&] { return launch_decode_sizes(fs, n, pa, ws, st); });
-        if (e == hipSuccess) e = timed(plan, "decode_scan", [&] { return launch_scan_decompress(fs, n, pa, ws, st); });
-    }
-    if (e == hipSuccess)
-        e = timed(plan, "decode", [&] {
-            return pa.V ? launch_chunk_decode(fs, n, pa, ws, st) : launch_decode(fs, n, pa, ws, st);
-        });
+    hipError_t e = timed(plan, "decode", [&] {
+        return pa.V ? launch_chunk_decode(fs, n, pa, ws, st) : launch_decode(fs, n, pa, ws, st);
+    });
     if (e == hipSuccess) e = timed(plan, "patch", [&] { return launch_patch(fs, n, pa, ws, st); });
     return e;
 }
@@ -476,6 +483,7 @@ eblc_status setup_args(int rank, const int64_t *dims, const int64_t *strides, co
     pa.nblocks = (n + pa.B - 1) / pa.B;
     pa.msec = o->center ? align_up(4 * pa.nblocks, 16) : 0;
     pa.side_max = o->side_max;
+    pa.max_pw = max_payload_words(n, pa.V);
     pa.lay = lay;
     return EBLC_OK;
 }
@@ -483,8 +491,7 @@ eblc_status setup_args(int rank, const int64_t *dims, const int64_t *strides, co
 /* Bytes of one lane's workspace, its arrays 256-byte aligned; with base non-null also the
  * arrays' addresses from base on. */
 uint64_t carve_workspace(const PlanArgs &pa, uint8_t *base, Workspace *ws) {
-    const uint64_t nc = pa.nchunks > pa.dchunks ? pa.nchunks : pa.dchunks;
-    const uint64_t ng = pa.ngroups > pa.dgroups ? pa.ngroups : pa.dgroups;
+    const uint64_t nc = pa.nchunks, ng = pa.ngroups;
     uint64_t off = 0;
     auto carve = [&](uint64_t bytes) {
         const uint64_t at = off;
@@ -620,6 +627,7 @@ eblc_status eblc_plan_create(const eblc_execution_t *exec, eblc_dtype dtype, int
     DevInfo init;
     std::memset(&init, 0, sizeof(init));
     if (!o.rel) resolve_abs(o.eps, &init);
+    header_template(pa, &init);
     for (int lane = 0; lane < p->lanes; ++lane) {
         if (hipMemcpy(lane_info(p, lane), &init, sizeof(init), hipMemcpyHostToDevice) != hipSuccess) {
             eblc_plan_destroy(p);

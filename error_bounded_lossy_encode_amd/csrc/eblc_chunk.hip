@@ -568,11 +568,12 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(5))
 /* ---- K7c: chunk decode ------------------------------------------------------------------------ */
 
 /* Un-RZE: group `lane`'s plane words, w[b] = plane b's word (0 where its bitmap bit is clear).
- * The bitmap comes by one vector load (lane l: bitmap word l), its bit count is checked against
- * the chunk's word count before any word is loaded under it (so a corrupt stream reads nothing
- * outside its chunk), and each plane below the highest one with a nonzero word takes its bitmap
- * bits and its running word count by readlane.  Returns false for a count mismatch.  The plane
- * loop is unrolled: plane B's bitmap bits and count sit at compile-time lanes. */
+ * The bitmap comes by one vector load the caller issues (lane l: bitmap word l), its bit count
+ * is checked against the chunk's word count before any word is loaded under it (so a corrupt
+ * stream reads nothing outside its chunk), and each plane below the highest one with a nonzero
+ * word takes its bitmap bits and its running word count by readlane.  Returns false for a count
+ * mismatch.  The plane loop is unrolled: plane B's bitmap bits and count sit at compile-time
+ * lanes. */
 
 /* A 2048-value chunk: plane B's bits are bitmap words 2 B and 2 B + 1. */
 template <int B>
@@ -588,10 +589,8 @@ __device__ __forceinline__ void unrze_wave_plane(const uint32_t *blob, uint32_t 
 
 template <int... B>
 __device__ __forceinline__ bool unrze_wave(std::integer_sequence<int, B...>, const uint32_t *blob, uint32_t P,
-                                           uint32_t w[32]) {
+                                           uint32_t bm, uint32_t w[32]) {
     constexpr uint32_t BM = ChunkGeom<2048>::BM;
-    const uint32_t lane = threadIdx.x & 63;
-    const uint32_t bm = blob[lane];
     const uint32_t pc = (uint32_t)__popc(bm);
     const uint32_t incl = wave_incl_scan(pc);
     if (readlane(incl, 63) + BM != P) return false;
@@ -602,7 +601,8 @@ __device__ __forceinline__ bool unrze_wave(std::integer_sequence<int, B...>, con
 }
 
 /* Two 1024-value chunks: A (P words from blob) in lanes 0-31, B (P2 words from blob + P, absent
- * when P2 = 0) in lanes 32-63; plane B's bits are word B of each bitmap. */
+ * when P2 = 0) in lanes 32-63; plane B's bits are word B of each bitmap.  bm: lane l < 32 holds
+ * word l of A's bitmap, lane 32 + l word l of B's (0 without B). */
 template <int B>
 __device__ __forceinline__ void unrze_halves_plane(const uint32_t *blob, uint32_t P, uint32_t bm, uint32_t pre,
                                                    uint32_t wmax, uint32_t w[32]) {
@@ -621,12 +621,9 @@ __device__ __forceinline__ void unrze_halves_plane(const uint32_t *blob, uint32_
 
 template <int... B>
 __device__ __forceinline__ bool unrze_halves(std::integer_sequence<int, B...>, const uint32_t *blob, uint32_t P,
-                                             uint32_t P2, uint32_t w[32]) {
+                                             uint32_t P2, uint32_t bm, uint32_t w[32]) {
     constexpr uint32_t BM = ChunkGeom<1024>::BM;
     const uint32_t lane = threadIdx.x & 63;
-    uint32_t bm = 0;
-    if (lane < 32) bm = blob[lane];
-    else if (P2) bm = blob[P + lane - 32];
     const uint32_t pc = (uint32_t)__popc(bm);
     const uint32_t incl = wave_seg_scan(pc, lane & 31, 32);
     if (readlane(incl, 31) + BM != P || (P2 && readlane(incl, 63) + BM != P2)) return false;
@@ -655,10 +652,8 @@ __device__ __forceinline__ void unrze_quarter_plane(const uint32_t *blob, uint32
 
 template <int... B>
 __device__ __forceinline__ bool unrze_pair(std::integer_sequence<int, B...>, const uint32_t *blob, uint32_t P,
-                                           uint32_t w0[32], uint32_t w1[32]) {
+                                           uint32_t bm0, uint32_t bm1, uint32_t w0[32], uint32_t w1[32]) {
     constexpr uint32_t BM = ChunkGeom<4096>::BM;
-    const uint32_t lane = threadIdx.x & 63;
-    const uint32_t bm0 = blob[lane], bm1 = blob[64 + lane];
     const uint32_t c0 = (uint32_t)__popc(bm0), c1 = (uint32_t)__popc(bm1);
     const uint32_t i0 = wave_incl_scan(c0), i1 = wave_incl_scan(c1);
     const uint32_t t0 = readlane(i0, 63);
@@ -724,9 +719,10 @@ __device__ __forceinline__ void store_values(const uint32_t y[32], uint4 *sy, fl
 /* One wave per 2048 values (two 1024-value chunks, or one 2048-value chunk), or per 4096-value
  * chunk taken as two halves with the running sum carried from the first into the second. */
 template <int V, bool STRIDED>
-__device__ __forceinline__ void chunk_decode_body(const uint8_t *__restrict__ in, PlanArgs pa,
+__device__ __forceinline__ void chunk_decode_body(const uint8_t *__restrict__ in, uint64_t in_bytes, PlanArgs pa,
                                                   Workspace ws, float *__restrict__ out) {
     constexpr uint32_t U = V > kEncChunk ? V : kEncChunk; /* values per wave */
+    constexpr uint32_t CPT = kEncChunksPerGroup * kEncChunk / V; /* chunks per offset-table group */
     __shared__ uint4 s_y[kWavesPerBlock][kWaveQuads];
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -735,8 +731,44 @@ __device__ __forceinline__ void chunk_decode_body(const uint8_t *__restrict__ in
     if ((uint64_t)u * U >= n) return;
     const uint32_t ubase = u * U;
     DevInfo *info = ws.info;
-    if (info->err) return;
-    if (info->mode == 1) {
+    /* The chunk's place in the payload: its group's offset from the offset table plus the word
+     * counts of the group's chunks before it.  Lane l < CPT loads the count of the group's chunk
+     * l, so every wave of the group sees the same counts.  The header, the table entries and the
+     * counts come in one round of loads (all lie inside the bytes the host lets through) and the
+     * chunk's bitmap loads go out next; a bitmap load that would leave the caller's bytes is not
+     * issued (no valid stream asks for one).  Every wave checks its group's counts against the
+     * table; the whole header is checked (and a bad one reported) by the outlier patch. */
+    const uint32_t c = V < kEncChunk ? 2 * u : u;
+    const uint32_t g = c / CPT, k = c % CPT;
+    const uint32_t cl = g * CPT + lane;
+    const uint32_t hv = load_header_lanes(in, pa, g);
+    const uint32_t cw = lane < CPT && cl < pa.dchunks ? reinterpret_cast<const uint32_t *>(in + kHeaderBytes)[cl] : 0u;
+    const uint32_t gincl = wave_incl_scan(cw);
+    const uint32_t gtot = readlane(gincl, 63);
+    const StreamView H = view_header(hv);
+    const uint64_t W = (uint64_t)(g > 0 ? readlane(hv, 32) : 0u) + (k > 0 ? readlane(gincl, (int)k - 1) : 0u);
+    const uint32_t P = readlane(cw, (int)k);
+    const uint32_t P2 = V == 1024 ? readlane(cw, (int)k + 1) : 0u; /* 0 past the last chunk */
+    const bool cbad = lane < CPT && cl < pa.dchunks && (cw < V / 32 || cw > V + V / 32);
+    const bool any_bad = __ballot(cbad) != 0;
+    const uint64_t ws0 = H.po / 4 + W; /* stream word index of the chunk's first word */
+    const bool inb = !any_bad && ws0 <= in_bytes / 4 && (uint64_t)P + P2 <= in_bytes / 4 - ws0;
+    const uint32_t *blob = reinterpret_cast<const uint32_t *>(in) + ws0;
+    uint32_t bm0 = 0, bm1 = 0;
+    if (inb) {
+        if constexpr (V == 1024) {
+            if (lane < 32) bm0 = blob[lane];
+            else if (P2) bm0 = blob[P + lane - 32];
+        } else if constexpr (V == 2048) {
+            bm0 = blob[lane];
+        } else {
+            bm0 = blob[lane];
+            bm1 = blob[64 + lane];
+        }
+    }
+    if (!H.sane) return;
+    if (H.mode == 1) {
+        if (kHeaderBytes + 4ull * n > in_bytes) return;
         const uint32_t cnt = n - ubase < U ? n - ubase : U;
         const uint32_t *srcw = reinterpret_cast<const uint32_t *>(in + kHeaderBytes) + ubase;
         uint32_t *ob = reinterpret_cast<uint32_t *>(out);
@@ -753,25 +785,31 @@ __device__ __forceinline__ void chunk_decode_body(const uint8_t *__restrict__ in
         }
         return;
     }
-    const uint32_t *pay = reinterpret_cast<const uint32_t *>(in + info->payload_off);
-    const float s = info->dec_s;
+    /* the group: each count in [V/32, V + V/32], and the table's range for it holds exactly its
+     * words and ends inside the payload (over every group, these accept exactly the tables that
+     * index the payload the counts describe) */
+    uint64_t t0, t1;
+    table_range(hv, g, pa.ngroups, H.pw, t0, t1);
+    if (any_bad || t0 > t1 || t1 > H.pw || t1 - t0 != gtot) {
+        if (k == 0 && lane == 0) atomicOr(&info->sticky, 1u);
+        return;
+    }
+    /* (a stream whose group passes reads nothing past the caller's bytes, unless its header is
+     * bad, which the outlier patch reports) */
+    if (!inb) return;
+    const float s = H.s;
     uint4 *sy = s_y[wave];
-    const uint32_t c = V < kEncChunk ? 2 * u : u;
-    const uint32_t W = chunk_offset<kDecChunksPerGroup>(ws.gpre_words, ws.chunk_words, c);
-    const uint32_t P = ws.chunk_words[c];
-    const uint32_t *blob = pay + W;
     const uint32_t cnt = n - ubase < (uint32_t)kEncChunk ? n - ubase : (uint32_t)kEncChunk;
     uint32_t w[32];
     if constexpr (V == 1024) {
-        const uint32_t P2 = c + 1 < pa.dchunks ? ws.chunk_words[c + 1] : 0u;
-        if (!unrze_halves(Planes{}, blob, P, P2, w)) {
+        if (!unrze_halves(Planes{}, blob, P, P2, bm0, w)) {
             if (lane == 0) atomicOr(&info->sticky, 1u);
             return;
         }
         decode_group<32>(w, 0, s);
         store_values<STRIDED>(w, sy, out, pa.lay, ubase, cnt);
     } else if constexpr (V == 2048) {
-        if (!unrze_wave(Planes{}, blob, P, w)) {
+        if (!unrze_wave(Planes{}, blob, P, bm0, w)) {
             if (lane == 0) atomicOr(&info->sticky, 1u);
             return;
         }
@@ -780,7 +818,7 @@ __device__ __forceinline__ void chunk_decode_body(const uint8_t *__restrict__ in
     } else {
         /* both halves' words are loaded before either is decoded */
         uint32_t w1[32];
-        if (!unrze_pair(Planes{}, blob, P, w, w1)) {
+        if (!unrze_pair(Planes{}, blob, P, bm0, bm1, w, w1)) {
             if (lane == 0) atomicOr(&info->sticky, 1u);
             return;
         }
@@ -798,7 +836,7 @@ __device__ __forceinline__ void chunk_decode_body(const uint8_t *__restrict__ in
 template <int V, bool STRIDED>
 __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(5))) void chunk_decode_kernel(Fields fs, PlanArgs pa, Workspace ws) {
     const uint32_t f = blockIdx.y;
-    chunk_decode_body<V, STRIDED>(pick(fs.src, f), pa, lane_ws(ws, f, fs.ws_stride),
+    chunk_decode_body<V, STRIDED>(pick(fs.src, f), pick(fs.bytes, f), pa, lane_ws(ws, f, fs.ws_stride),
                                   reinterpret_cast<float *>(pick(fs.dst, f)));
 }
 

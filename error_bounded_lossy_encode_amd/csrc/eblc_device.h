@@ -242,23 +242,122 @@ __device__ __forceinline__ uint32_t group_prefix(const uint32_t *spre, const uin
     return spre[g / kSuperGroups] + wave_sum(v);
 }
 
-/* Word offset of chunk c in the packed payload, from its group's exclusive prefix plus the
- * chunks before c in its group; the loads are issued together, then summed. */
-template <int CPG>
-__device__ __forceinline__ uint32_t chunk_offset(const uint32_t *gpre, const uint32_t *per_chunk,
-                                                 uint32_t c) {
-    const uint32_t g0 = c / CPG * CPG;
-    uint32_t v[CPG];
-    v[0] = gpre[c / CPG];
-#pragma unroll
-    for (int k = 1; k < CPG; ++k) {
-        v[k] = 0;
-        if (g0 + (uint32_t)k - 1 < c) v[k] = per_chunk[g0 + k - 1];
+/* ---- the stream header, read by each decoding workgroup ---------------------------------------- */
+
+__device__ __forceinline__ uint64_t ld64(const uint32_t *h, int i) {
+    return (uint64_t)h[i] | ((uint64_t)h[i + 1] << 32);
+}
+
+/* One load for the wave: lane l < 32 takes header word l, and lanes 32 and 33 take the
+ * offset-table entries a decoding workgroup of table group g needs (entries g - 1 and g, clamped
+ * into the table; a field of one group has no table and they load nothing).  The host refuses a
+ * stream shorter than its header, size section and offset table, so every word lies inside the
+ * caller's bytes before anything is checked. */
+__device__ __forceinline__ uint32_t load_header_lanes(const uint8_t *in, const PlanArgs &pa, uint32_t g) {
+    const uint32_t lane = threadIdx.x & 63;
+    uint64_t idx = lane;
+    if (lane >= 32) {
+        const uint32_t e = lane == 32 ? (g > 0 ? g - 1 : 0u) : (g + 1 < pa.ngroups ? g : pa.ngroups - 2);
+        idx = (kHeaderBytes + pa.wsec) / 4 + e;
     }
-    uint32_t o = 0;
-#pragma unroll
-    for (int k = 0; k < CPG; ++k) o += v[k];
-    return o;
+    const bool on = lane < 32 || (lane < 34 && pa.ngroups > 1);
+    return on ? reinterpret_cast<const uint32_t *>(in)[idx] : 0u;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint32_t v, int lane) {
+    return (uint64_t)readlane(v, lane) | ((uint64_t)readlane(v, lane + 1) << 32);
+}
+
+/* The plan's header template for lane l < 32 (DevInfo::hdr_want / hdr_mask), loaded with the
+ * header. */
+__device__ __forceinline__ uint2 load_header_template(const DevInfo *info) {
+    const uint32_t l = threadIdx.x & 31;
+    return make_uint2(info->hdr_want[l], info->hdr_mask[l]);
+}
+
+/* The 128-byte header (lanes 0-31 of hv, from load_header_lanes) checked against the plan:
+ * magic, format version, coder and its parameters (a plan decodes coded streams of its own coder
+ * and chunk size, and every RAW stream), rank, dims, n, the bound, and a layout of sections --
+ * sizes, offset table, block means, payload, outlier indices and values -- that ends inside the
+ * in_bytes the caller passed.  The words the plan fixes are compared lane by lane with the
+ * plan's template (tmpl, from load_header_template), the offsets with the layout the other
+ * fields give, in one ballot.  One wave per call makes this check, in the outlier-patch kernel,
+ * and reports a failure (the decoders, which would carry its registers into their tile loops,
+ * only bound their reads); it takes the plan's fields it needs as values (n, the coder's V, the
+ * size section's bytes, the table groups and the largest payload). */
+__device__ __forceinline__ bool header_ok(uint32_t hv, uint2 tmpl, uint64_t in_bytes, uint64_t n, uint32_t V,
+                                          uint64_t wsec, uint32_t ngroups, uint64_t max_pw) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t w2 = readlane(hv, 2), B = readlane(hv, 3), flags = readlane(hv, 17);
+    const float eb_f = __uint_as_float(readlane(hv, 14)), s = __uint_as_float(readlane(hv, 15));
+    const uint64_t m = readlane64(hv, 18), pb = readlane64(hv, 20), total = readlane64(hv, 30);
+    const uint32_t mode = w2 & 0xff, log2seg = (w2 >> 16) & 0xff, T = w2 >> 24;
+    bool ok = T >= 1 && T <= 30 && flags <= 1 && (flags == 0 || mode == 0);
+    const bool bitpack_params = log2seg == 5 && ((B >= 32 && B <= 1024 && B % 32 == 0) || B == 2048);
+    const bool chunk_params = log2seg >= 10 && log2seg <= 12 && B == (1u << (log2seg & 31));
+    const bool raw = mode == 1;
+    uint64_t po, oi, ov, end;
+    if (raw) {
+        /* the header, then the input bytes */
+        ok = ok && (bitpack_params || chunk_params) && m == 0 && pb == 4 * n;
+        po = kHeaderBytes;
+        oi = ov = end = kHeaderBytes + align16(4 * n);
+    } else {
+        /* sizes, offset table, block means (centered), payload, outlier indices and values; the
+         * payload holds at most every word the coder may write */
+        ok = ok && (V == 0 ? mode == 0 && bitpack_params : mode == 2 && chunk_params && B == V);
+        ok = ok && eb_f >= FLT_MIN && eb_f <= FLT_MAX && fabsf(s) <= FLT_MAX && s == 2.0f * eb_f;
+        ok = ok && m <= n && (pb & 3) == 0 && pb / 4 <= max_pw;
+        /* a centered stream's means: one per block of its B (n < 2^32: a 32-bit division) */
+        uint64_t msec = 0;
+        if (flags != 0 && B != 0) {
+            const uint32_t n32 = (uint32_t)n;
+            msec = align16(4ull * (n32 / B + (n32 % B != 0 ? 1u : 0u)));
+        }
+        po = kHeaderBytes + wsec + table_bytes(ngroups) + msec;
+        oi = po + align16(pb);
+        ov = oi + align16(4 * m);
+        end = ov + align16(4 * m);
+    }
+    ok = ok && total == end && total <= in_bytes;
+    /* lanes 24-29: the offsets of the payload, outlier indices and values */
+    const uint64_t off = lane < 26 ? po : lane < 28 ? oi : ov;
+    const uint32_t off32 = (lane & 1) ? (uint32_t)(off >> 32) : (uint32_t)off;
+    const bool bad = lane < 32 && ((hv & tmpl.y) != tmpl.x || (lane >= 24 && lane < 30 && hv != off32));
+    return ok && __ballot(bad) == 0;
+}
+
+/* The header fields a decoding wave works from, read from hv without the full check: each
+ * wave bounds every read it bases on them by the caller's bytes, and rejects (without a report)
+ * a mode, block or flags word no stream holds, so a stream whose header fails the full check --
+ * made once per call, by one wave of the outlier patch (header_ok) -- can only leave `out`
+ * unspecified. */
+struct StreamView {
+    bool sane;          /* mode 0-2, flags 0-1, B a multiple of 32 from 32 to 4096 */
+    uint32_t mode, flags, B;
+    float s;
+    uint64_t pw, po;
+};
+
+__device__ __forceinline__ StreamView view_header(uint32_t hv) {
+    StreamView V;
+    V.mode = readlane(hv, 2) & 0xff;
+    V.B = readlane(hv, 3);
+    V.flags = readlane(hv, 17);
+    V.s = __uint_as_float(readlane(hv, 15));
+    V.pw = readlane64(hv, 20) / 4;
+    V.po = readlane64(hv, 24);
+    V.sane = V.mode <= 2 && V.flags <= 1 && V.B >= 32 && V.B <= 4096 && V.B % 32 == 0;
+    return V;
+}
+
+/* Payload offset (in words) of table group g and of the group after it, from the entries
+ * load_header_lanes placed in lanes 32 and 33 of hv: group 0 starts at 0, and the group after
+ * the last ends at the payload's end, pw. */
+__device__ __forceinline__ void table_range(uint32_t hv, uint32_t g, uint32_t ngroups, uint64_t pw,
+                                            uint64_t &t0, uint64_t &t1) {
+    t0 = g > 0 ? readlane(hv, 32) : 0u;
+    t1 = g + 1 < ngroups ? (uint64_t)readlane(hv, 33) : pw;
 }
 
 /* ---- the fields of a launch ------------------------------------------------------------------ */

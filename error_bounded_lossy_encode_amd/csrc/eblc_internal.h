@@ -58,10 +58,8 @@ constexpr uint64_t kRangeSpan = (uint64_t)kRangeThreads * kRangeVec; /* float4 p
 constexpr int kPatchBlocksMax = 1024;
 constexpr uint32_t kHeaderBytes = 128;
 constexpr uint32_t kMagic = 0x434C4245u;          /* "EBLC" */
-constexpr uint32_t kVersion = 1;
+constexpr uint32_t kVersion = 2;               /* format 2: with the offset table */
 constexpr int kMaxKernelsPerCall = 8;
-constexpr uint64_t kTouchMax = 128ull << 20;    /* payloads the decoder's sizes pass pre-reads */
-constexpr int kTouchBatch = 8;                  /* lines in flight per thread in that pass */
 constexpr int kResolveBatch = 8;                /* range partials in flight per thread of the resolve */
 
 /* Device-resident state of a plan (one per plan, in its workspace). */
@@ -69,21 +67,22 @@ struct DevInfo {
     /* resolved bound: abs mode writes it once at plan creation, rel mode at every compress */
     float eb_f, s, r;
     uint32_t valid;
-    /* outcome of the last compress, or the parsed header of the last decompress */
+    /* outcome of the last compress */
     uint32_t mode;          /* 0 bitpack coder, 1 raw, 2 chunk coder */
-    uint32_t err;           /* decompress: this call's stream is corrupt */
-    uint32_t sticky;        /* OR of err over calls since eblc_plan_status */
-    uint32_t dec_flags;     /* decompress: the stream's flags word (bit 0: centered) */
-    uint32_t width_bad;     /* decompress: a width byte above 32 was seen */
+    uint32_t sticky;        /* decompress: set by a corrupt stream, until eblc_plan_status reads it */
     uint32_t fits;          /* compress: total <= out_capacity */
+    uint32_t pad;
     uint64_t m;
     uint64_t payload_words;
     uint64_t payload_off;
     uint64_t oidx_off;
     uint64_t oval_off;
     uint64_t total;
-    float dec_s;            /* decompress: step read from the stream */
-    uint32_t dec_B;         /* decompress: Lorenzo block read from the stream */
+    /* decompress: the header words a stream of the plan must hold, word i under mask i (magic,
+     * version and header size, rank, dims, n, the size section's offset; mask 0 elsewhere),
+     * written at plan creation so that each decoding wave compares them lane by lane */
+    uint32_t hdr_want[32];
+    uint32_t hdr_mask[32];
 };
 
 /* Where the caller's values live.  The codec works on the row-major flattened index i over the
@@ -123,6 +122,7 @@ struct PlanArgs {
     uint32_t dchunks;       /* decode chunks (the coder's chunks for the chunk coder) */
     uint32_t dgroups;       /* decode groups */
     uint64_t side_max;
+    uint64_t max_pw;        /* max_payload_words(n, V): the largest payload a stream can hold */
     Layout lay;             /* memory layout of the compress input and decompress output */
 };
 
@@ -130,15 +130,14 @@ struct PlanArgs {
 struct Workspace {
     DevInfo *info;
     uint32_t *scratch;       /* (nchunks + 1) * slot words: per-chunk payload slots */
-    uint32_t *chunk_words;   /* [nchunks] payload words per chunk (encode or decode chunks) */
+    uint32_t *chunk_words;   /* [nchunks] payload words per encode chunk */
     uint32_t *chunk_esc;     /* [nchunks] escapes per encode chunk */
     uint32_t *chunk_tmask;   /* [nchunks] bit t set if tile t of the encode chunk has an escape */
     uint32_t *group_words;   /* [ngroups] */
     uint32_t *group_esc;     /* [ngroups] */
-    uint32_t *gpre_words;    /* compress: [nsuper] exclusive prefix of the words of each super-group of
-                                kSuperGroups groups (a group adds the sums of its super-group's groups
-                                before it); decompress: [ngroups] exclusive prefix of each group's words */
-    uint32_t *gpre_esc;      /* compress: [nsuper] the same for the escapes */
+    uint32_t *gpre_words;    /* [nsuper] exclusive prefix of the words of each super-group of kSuperGroups
+                                groups (a group adds the sums of its super-group's groups before it) */
+    uint32_t *gpre_esc;      /* [nsuper] the same for the escapes */
     uint32_t *emask;         /* [nchunks * kEncSegs] escape bitmask per segment (chunks with more
                                 than kEscStage escapes, tiles with escapes) */
     uint32_t *stage_idx;     /* [nchunks * kEscStage] first escapes of each chunk: index ... */
@@ -147,6 +146,20 @@ struct Workspace {
     float *range_part;       /* [2 * range_blocks(n)] per-block min / max */
     int32_t *means;          /* [nblocks] block means of a centered compress */
 };
+
+/* The offset table right after the size section: one u32 per group of 8192 values (an encode
+ * and a decode group) after the first, the payload words before that group, padded to 16
+ * bytes.  The block means (centered streams) and the payload follow it. */
+__host__ __device__ inline uint64_t table_bytes(uint32_t ngroups) {
+    return ngroups > 1 ? (4ull * (ngroups - 1) + 15) & ~15ull : 0;
+}
+
+/* The most payload words a field of n values can take: 32 per segment (bitpack), or every plane
+ * word and bitmap word of every chunk (chunk coder with chunks of V values). */
+__host__ __device__ inline uint64_t max_payload_words(uint64_t n, uint32_t V) {
+    if (V == 0) return 32 * ((n + 31) / 32);
+    return ((n + V - 1) / V) * (uint64_t)(V + V / 32);
+}
 
 /* Workgroups of the range pass: one per kRangeSpan float4 (16384 values), at least one. */
 inline uint32_t range_blocks(uint64_t n) {
@@ -202,17 +215,6 @@ hipError_t launch_scan_compress(const Fields &fs, uint32_t nf, const PlanArgs &p
                                 hipStream_t stream);
 hipError_t launch_compact(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                           hipStream_t stream);
-hipError_t launch_decode_sizes(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
-                               hipStream_t stream);
-hipError_t launch_scan_decompress(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
-                                  hipStream_t stream);
-/* Decode sizes and scan in one single-workgroup launch, for fields of at most kSizesScanChunks
- * decode chunks (2^22 values): there one workgroup reads every size faster than two launches
- * take (2^20 values: 8.4 -> 5.9 us), while at 2^24 values it is slower (9.6 -> 12.4 us) and
- * misses the sizes pass's pre-read of the payload. */
-constexpr uint32_t kSizesScanChunks = 2048;
-hipError_t launch_sizes_scan(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
-                             hipStream_t stream);
 hipError_t launch_decode(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                          hipStream_t stream);
 hipError_t launch_patch(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,

@@ -815,15 +815,14 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(Fields fs, PlanArgs
                              pa.ngroups - 1 - blockIdx.x);
 }
 
-/* ---- K3 / K6b: single-workgroup exclusive scan over groups -------------------------------- */
+/* ---- K3: single-workgroup exclusive scan over groups ---------------------------------------- */
 
-/* Exclusive prefix of a[0..ng) and b[0..ng) (b may be null) into pa_out / pb_out; returns the
- * totals in tot[0], tot[1] (valid in every thread).  Each round covers kScanThreads *
- * kScanItems items: a thread loads 16 consecutive items with 128-bit loads (the arrays are
- * 256-byte aligned), sums them, the sums are scanned across the wave with DPP and across the
- * 16 waves through LDS, and the thread writes its 16 exclusive prefixes back -- or, SUPER, only
- * the prefix of every kSuperGroups-th item, at index item / kSuperGroups. */
-template <bool SUPER>
+/* Exclusive prefix of a[0..ng) and b[0..ng) at every kSuperGroups-th item, into pa_out /
+ * pb_out at index item / kSuperGroups; returns the totals in tot[0], tot[1] (valid in every
+ * thread).  Each round covers kScanThreads * kScanItems items: a thread loads 16 consecutive
+ * items with 128-bit loads (the arrays are 256-byte aligned), sums them, the sums are scanned
+ * across the wave with DPP and across the 16 waves through LDS, and the thread holding a
+ * super-group's first item writes its prefix. */
 __device__ void block_scan2(const uint32_t *__restrict__ a, const uint32_t *__restrict__ b,
                             uint32_t *__restrict__ pa_out, uint32_t *__restrict__ pb_out,
                             uint32_t ng, uint32_t *tot) {
@@ -870,36 +869,9 @@ __device__ void block_scan2(const uint32_t *__restrict__ a, const uint32_t *__re
             sa += xa;
             sb += xb;
         }
-        uint32_t ea = carry_a + oa + ia - ta;
-        uint32_t eb = carry_b + ob + ib - tb;
-        uint32_t pa[kScanItems], pb[kScanItems];
-#pragma unroll
-        for (int k = 0; k < kScanItems; ++k) {
-            pa[k] = ea;
-            pb[k] = eb;
-            ea += va[k];
-            eb += vb[k];
-        }
-        if (SUPER) {
-            if (i0 < ng && (i0 % kSuperGroups) == 0) {
-                pa_out[i0 / kSuperGroups] = pa[0];
-                if (pb_out != nullptr) pb_out[i0 / kSuperGroups] = pb[0];
-            }
-        } else if (i0 + kScanItems <= ng) {
-#pragma unroll
-            for (int k = 0; k < kV; ++k) {
-                reinterpret_cast<uint4 *>(pa_out + i0)[k] = make_uint4(pa[4 * k], pa[4 * k + 1], pa[4 * k + 2], pa[4 * k + 3]);
-                if (pb_out != nullptr)
-                    reinterpret_cast<uint4 *>(pb_out + i0)[k] = make_uint4(pb[4 * k], pb[4 * k + 1], pb[4 * k + 2], pb[4 * k + 3]);
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < kScanItems; ++k) {
-                if (i0 + k < ng) {
-                    pa_out[i0 + k] = pa[k];
-                    if (pb_out != nullptr) pb_out[i0 + k] = pb[k];
-                }
-            }
+        if (i0 < ng && (i0 % kSuperGroups) == 0) {
+            pa_out[i0 / kSuperGroups] = carry_a + oa + ia - ta;
+            if (pb_out != nullptr) pb_out[i0 / kSuperGroups] = carry_b + ob + ib - tb;
         }
         carry_a += sa;
         carry_b += sb;
@@ -920,12 +892,12 @@ __device__ __forceinline__ void scan_compress_body(PlanArgs pa, Workspace ws,
     const uint32_t valid0 = info->valid;
     const float eb0 = info->eb_f, s0 = info->s, r0 = info->r;
     uint32_t tot[2];
-    block_scan2<true>(ws.group_words, ws.group_esc, ws.gpre_words, ws.gpre_esc, pa.ngroups, tot);
+    block_scan2(ws.group_words, ws.group_esc, ws.gpre_words, ws.gpre_esc, pa.ngroups, tot);
     if (threadIdx.x == 0) {
         const uint64_t n = pa.n;
         const uint64_t S = tot[0], m = tot[1];
         const uint64_t raw_total = kHeaderBytes + align16(4 * n);
-        const uint64_t payload_off = kHeaderBytes + pa.wsec + pa.msec;
+        const uint64_t payload_off = kHeaderBytes + pa.wsec + table_bytes(pa.ngroups) + pa.msec;
         const uint64_t lossy_total = payload_off + align16(4 * S) + 2 * align16(4 * m);
         const bool valid = valid0 != 0;
         const bool raw = !valid || m > pa.side_max || lossy_total > raw_total;
@@ -1299,6 +1271,9 @@ __device__ __forceinline__ void compact_body(const float *__restrict__ x,
     uint32_t *pay = reinterpret_cast<uint32_t *>(out + payload_off);
     uint32_t *oidx = reinterpret_cast<uint32_t *>(out + oidx_off);
     uint32_t *oval = reinterpret_cast<uint32_t *>(out + oval_off);
+    /* the offset table's entry for the group: the payload words before it */
+    uint32_t *table = reinterpret_cast<uint32_t *>(out + kHeaderBytes + pa.wsec);
+    if (lane == 0 && grp != 0) table[grp - 1] = gw;
     if (small) {
         copy_group_payload<CPG>(ws.scratch + (uint64_t)grp * CPG * pa.slot, pa.slot, words, dw, pay);
     } else {
@@ -1352,7 +1327,7 @@ __device__ __forceinline__ void compact_body(const float *__restrict__ x,
         const uint64_t b0 = (gbase + pa.B - 1) / pa.B;
         const uint64_t b1e = (gend + pa.B - 1) / pa.B;
         const uint64_t b1 = b1e < pa.nblocks ? b1e : pa.nblocks;
-        int32_t *mdst = reinterpret_cast<int32_t *>(out + kHeaderBytes + pa.wsec);
+        int32_t *mdst = reinterpret_cast<int32_t *>(out + kHeaderBytes + pa.wsec + table_bytes(pa.ngroups));
         for (uint64_t b = b0 + lane; b < b1; b += kWave) mdst[b] = ws.means[b];
         if (last && lane < (pa.msec - 4 * pa.nblocks) / 4) mdst[pa.nblocks + lane] = 0;
     }
@@ -1365,6 +1340,8 @@ __device__ __forceinline__ void compact_body(const float *__restrict__ x,
             oidx[m + lane] = 0u;
             oval[m + lane] = 0u;
         }
+        const uint32_t entries = pa.ngroups - 1;
+        if (lane < table_bytes(pa.ngroups) / 4 - entries) table[entries + lane] = 0u;
     }
 }
 
@@ -1374,199 +1351,6 @@ __global__ __launch_bounds__(kBlockThreads) void compact_kernel(Fields fs, PlanA
     const Workspace w = lane_ws(ws, f, fs.ws_stride);
     compact_body<STRIDED>(reinterpret_cast<const float *>(pick(fs.src, f)), pa, w, pick(fs.dst, f),
                           (fs.wdirect >> f) & 1u ? nullptr : w.widths);
-}
-
-/* ---- K6a: decode sizes ---------------------------------------------------------------------- */
-
-/* One thread per decode chunk: payload words of the chunk = sum of its width bytes; a width above 32
- * flags the stream.  Quads of threads form the groups the scan runs over. */
-/* Payload words of decode chunk c < dchunks: the sum of its 64 width bytes (bitpack coder), or
- * the word count the stream holds for it (chunk coder, bitmap included).  bad is set (and the
- * size taken as 0 for the chunk coder) for a width above 32 or a count out of [V/32, V + V/32]. */
-__device__ __forceinline__ uint32_t chunk_size(const uint8_t *__restrict__ in, const PlanArgs &pa, uint32_t c,
-                                               uint32_t &bad) {
-    uint32_t sum = 0;
-    if (pa.V != 0) {
-        sum = reinterpret_cast<const uint32_t *>(in + kHeaderBytes)[c];
-        if (sum < pa.V / 32 || sum > pa.V + pa.V / 32) {
-            bad = 1u;
-            sum = 0;
-        }
-        return sum;
-    }
-    const uint64_t s0 = (uint64_t)c * kDecSegs;
-    const uint64_t segs = (pa.nseg - s0 < (uint64_t)kDecSegs) ? pa.nseg - s0 : (uint64_t)kDecSegs;
-    const uint8_t *wp = in + kHeaderBytes + s0;
-    if (segs == (uint64_t)kDecSegs) {
-        const uint4 *w4 = reinterpret_cast<const uint4 *>(wp);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint4 v = w4[i];
-            const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                sum = __builtin_amdgcn_sad_u8(vv[k], 0u, sum);
-                bad |= (((vv[k] & 0x7F7F7F7Fu) + 0x5F5F5F5Fu) | vv[k]) & 0x80808080u;
-            }
-        }
-    } else {
-        for (uint64_t k = 0; k < segs; ++k) {
-            const uint32_t w = wp[k];
-            sum += w;
-            bad |= w > 32 ? 1u : 0u;
-        }
-    }
-    return sum;
-}
-
-__device__ __forceinline__ void decode_sizes_body(const uint8_t *__restrict__ in,
-                                                  uint64_t in_bytes, PlanArgs pa, Workspace ws) {
-    const uint32_t c = blockIdx.x * 256 + threadIdx.x;
-    /* Touch one word of every 128-byte line of a well-compressed stream's sections after the
-     * header up to the payload's end -- sizes, block means, payload -- when they average at most
-     * 128 bytes per decode chunk for each of the kTouchBatch loads a thread keeps in flight (and
-     * at most kTouchMax bytes in all), so that the decode kernel finds them in the 256 MB
-     * last-level cache even when the stream was written long before: with so few words per
-     * chunk, its staging loads are bound by their latency at its occupancy.  Such a stream takes
-     * one round of loads here.  The header is not validated yet, so the range is clamped to the
-     * caller's bytes (every word read lies below in_bytes). */
-    uint32_t touched = 0;
-    {
-        const uint64_t po = *reinterpret_cast<const uint64_t *>(in + 96);
-        const uint64_t pb = *reinterpret_cast<const uint64_t *>(in + 80);
-        const uint64_t end = in_bytes & ~(uint64_t)3;
-        const bool coded = in[8] != 1 && po >= kHeaderBytes && po < end && pb <= end - po &&
-                           po + pb - kHeaderBytes <= kTouchMax &&
-                           po + pb - kHeaderBytes <= (uint64_t)pa.dchunks * (128u * kTouchBatch);
-        const uint64_t t0 = kHeaderBytes, t1 = po + pb;
-        const uint64_t lines = coded && t1 > t0 ? (t1 - t0 + 127) / 128 : 0;
-        const uint64_t nthr = (uint64_t)gridDim.x * 256, tid = c;
-        for (uint64_t k = tid; k < lines; k += (uint64_t)kTouchBatch * nthr) {
-            uint32_t v[kTouchBatch];
-#pragma unroll
-            for (int u = 0; u < kTouchBatch; ++u) {
-                const uint64_t l = k + (uint64_t)u * nthr;
-                v[u] = l < lines ? *reinterpret_cast<const uint32_t *>(in + t0 + 128 * l) : 0u;
-            }
-#pragma unroll
-            for (int u = 0; u < kTouchBatch; ++u) touched |= v[u];
-        }
-    }
-    uint32_t bad = 0;
-    const uint32_t sum = c < pa.dchunks ? chunk_size(in, pa, c, bad) : 0u;
-    if (c < pa.dchunks) ws.chunk_words[c] = sum;
-    uint32_t g = sum;
-    g += dpp<kDppQuadXor1>(0, g);
-    g += dpp<kDppQuadXor2>(0, g);
-    if ((threadIdx.x & 3) == 0 && c / kDecChunksPerGroup < pa.dgroups) ws.group_words[c / kDecChunksPerGroup] = g;
-    if (bad) atomicOr(&ws.info->width_bad, 1u);
-    asm volatile("" ::"v"(touched));
-}
-
-__global__ __launch_bounds__(256) void decode_sizes_kernel(Fields fs, PlanArgs pa, Workspace ws) {
-    const uint32_t f = blockIdx.y;
-    decode_sizes_body(pick(fs.src, f), pick(fs.bytes, f), pa, lane_ws(ws, f, fs.ws_stride));
-}
-
-/* ---- K6b: decode scan + header validation ------------------------------------------------- */
-
-__device__ __forceinline__ uint64_t ld64(const uint32_t *h, int i) {
-    return (uint64_t)h[i] | ((uint64_t)h[i + 1] << 32);
-}
-
-__device__ __forceinline__ void scan_decompress_body(const uint8_t *__restrict__ in,
-                                                     uint64_t in_bytes, PlanArgs pa,
-                                                     Workspace ws, bool sizes_bad = false) {
-    /* the header, staged in LDS before the scan so that its loads overlap it (block_scan2
-     * synchronizes the workgroup before it returns) */
-    __shared__ uint32_t s_h[32];
-    if (threadIdx.x < 32) s_h[threadIdx.x] = reinterpret_cast<const uint32_t *>(in)[threadIdx.x];
-    uint32_t tot[2];
-    block_scan2<false>(ws.group_words, nullptr, ws.gpre_words, nullptr, pa.dgroups, tot);
-    if (threadIdx.x != 0) return;
-    DevInfo *info = ws.info;
-    uint32_t hw[32];
-    for (int i = 0; i < 32; ++i) hw[i] = s_h[i];
-    const uint64_t n = pa.n;
-    const uint32_t mode = hw[2] & 0xff, rank = (hw[2] >> 8) & 0xff, log2seg = (hw[2] >> 16) & 0xff;
-    const uint32_t T = hw[2] >> 24, B = hw[3];
-    bool ok = hw[0] == kMagic && (hw[1] & 0xffff) == kVersion && (hw[1] >> 16) == kHeaderBytes;
-    ok = ok && rank == pa.rank && T >= 1 && T <= 30;
-    /* a plan decodes coded streams of its own coder (and chunk size), and every RAW stream */
-    const bool bitpack_params = log2seg == 5 && ((B >= 32 && B <= 1024 && B % 32 == 0) || B == 2048);
-    const bool chunk_params = log2seg >= 10 && log2seg <= 12 && B == (1u << log2seg);
-    if (mode == 1) ok = ok && (bitpack_params || chunk_params);
-    else if (pa.V == 0) ok = ok && mode == 0 && bitpack_params;
-    else ok = ok && mode == 2 && chunk_params && B == pa.V;
-    for (int a = 0; a < 4; ++a) ok = ok && ld64(hw, 4 + 2 * a) == pa.dims[a];
-    const uint32_t flags = hw[17];
-    ok = ok && ld64(hw, 12) == n && flags <= 1 && (flags == 0 || mode == 0) && ld64(hw, 22) == kHeaderBytes;
-    const uint64_t m = ld64(hw, 18), pb = ld64(hw, 20), po = ld64(hw, 24), oi = ld64(hw, 26);
-    const uint64_t ov = ld64(hw, 28), total = ld64(hw, 30);
-    const float eb_f = __uint_as_float(hw[14]), s = __uint_as_float(hw[15]);
-    if (mode == 1) {
-        const uint64_t end = kHeaderBytes + align16(4 * n);
-        ok = ok && m == 0 && pb == 4 * n && po == kHeaderBytes && oi == end && ov == end && total == end;
-    } else {
-        ok = ok && eb_f >= FLT_MIN && eb_f <= FLT_MAX && fabsf(s) <= FLT_MAX && s == 2.0f * eb_f;
-        ok = ok && m <= n && (pb & 3) == 0 && pb == 4 * (uint64_t)tot[0] && info->width_bad == 0 && !sizes_bad;
-        const uint64_t msec = (flags && B) ? align16(4 * ((n + B - 1) / B)) : 0;
-        ok = ok && po == kHeaderBytes + pa.wsec + msec && oi == po + align16(pb);
-        ok = ok && ov == oi + align16(4 * m) && total == ov + align16(4 * m);
-    }
-    ok = ok && total <= in_bytes;
-    const uint32_t err = ok ? 0u : 1u;
-    info->err = err;
-    info->sticky |= err;
-    info->width_bad = 0;
-    info->mode = mode;
-    info->m = ok ? m : 0;
-    info->payload_off = po;
-    info->oidx_off = oi;
-    info->oval_off = ov;
-    info->dec_s = s;
-    info->dec_B = B;
-    info->dec_flags = flags;
-}
-
-__global__ __launch_bounds__(kScanThreads) void scan_decompress_kernel(Fields fs, PlanArgs pa, Workspace ws) {
-    const uint32_t f = blockIdx.y;
-    scan_decompress_body(pick(fs.src, f), pick(fs.bytes, f), pa, lane_ws(ws, f, fs.ws_stride));
-}
-
-/* K6 for small fields (dchunks <= kSizesScanChunks): one workgroup per field takes the sizes of
- * every decode chunk, kSizesBatch per thread with their loads issued together, and then runs the
- * scan and header validation, one launch instead of two.  The group sums it writes are read by
- * the scan after the barrier; its bad-width flag reaches the validation through LDS. */
-constexpr int kSizesBatch = 4;
-__global__ __launch_bounds__(kScanThreads) void sizes_scan_kernel(Fields fs, PlanArgs pa, Workspace ws) {
-    __shared__ uint32_t s_bad;
-    const uint32_t f = blockIdx.y;
-    const uint8_t *in = pick(fs.src, f);
-    const Workspace w = lane_ws(ws, f, fs.ws_stride);
-    if (threadIdx.x == 0) s_bad = 0;
-    __syncthreads();
-    uint32_t bad = 0;
-    for (uint32_t base = 0; base < pa.dchunks; base += kSizesBatch * kScanThreads) {
-        uint32_t sum[kSizesBatch];
-#pragma unroll
-        for (int j = 0; j < kSizesBatch; ++j) {
-            const uint32_t c = base + (uint32_t)j * kScanThreads + threadIdx.x;
-            sum[j] = c < pa.dchunks ? chunk_size(in, pa, c, bad) : 0u;
-        }
-#pragma unroll
-        for (int j = 0; j < kSizesBatch; ++j) {
-            const uint32_t c = base + (uint32_t)j * kScanThreads + threadIdx.x;
-            if (c < pa.dchunks) w.chunk_words[c] = sum[j];
-            uint32_t g = sum[j];
-            g += dpp<kDppQuadXor1>(0, g);
-            g += dpp<kDppQuadXor2>(0, g);
-            if ((threadIdx.x & 3) == 0 && c / kDecChunksPerGroup < pa.dgroups) w.group_words[c / kDecChunksPerGroup] = g;
-        }
-    }
-    if (bad) atomicOr(&s_bad, 1u);
-    __syncthreads();
-    scan_decompress_body(in, pick(fs.bytes, f), pa, w, s_bad != 0);
 }
 
 /* ---- K7: fused decode ------------------------------------------------------------------------ */
@@ -1583,14 +1367,13 @@ __global__ __launch_bounds__(kScanThreads) void sizes_scan_kernel(Fields fs, Pla
  * its block's first lane (ds_bpermute), or plus the carry when its block began before the tile;
  * carry starts at carry0, the code before the chunk when the chunk starts inside a block. */
 template <bool STRIDED, bool CENTERED, bool GB>
-__device__ __forceinline__ void decode_tiles(const PlanArgs &pa, const DevInfo *info, const int32_t mu[kDecTiles],
+__device__ __forceinline__ void decode_tiles(const PlanArgs &pa, float s, uint32_t B, const int32_t mu[kDecTiles],
                                              const uint32_t *pay, const uint32_t *s_w, const uint32_t *s_so,
                                              uint32_t lb, uint64_t cbase, bool full, float *__restrict__ out,
                                              int32_t carry0, uint32_t r0, uint32_t mB) {
     const uint32_t lane = threadIdx.x & 63;
     const uint64_t n = pa.n;
-    const float s = info->dec_s;
-    const uint32_t B = info->dec_B; /* the stream's block, validated by the header check */
+    /* s and B are the stream's, validated by the header check */
     const uint32_t seglen = (B / 4 < 64u) ? B / 4 : 64u;
     const uint32_t dist = lane & (seglen - 1);
     const uint32_t ntiles = full ? kDecTiles : (uint32_t)((n - cbase + kTile - 1) / kTile);
@@ -1659,12 +1442,16 @@ __device__ __forceinline__ void decode_tiles(const PlanArgs &pa, const DevInfo *
  * lanes take a segment, four values each, eight segments per round; a value's two words are
  * read only when its bits span them, so no read leaves those segments' words. */
 __device__ __forceinline__ int32_t open_block_sum(const uint8_t *__restrict__ in, uint64_t seg_end, uint32_t nseg,
-                                                  const uint32_t *__restrict__ words_end) {
+                                                  const uint32_t *__restrict__ words_end, uint64_t limit, bool &ok) {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wpre = lane < nseg ? (uint32_t)in[kHeaderBytes + seg_end - nseg + lane] : 0u;
     const uint32_t incl = wave_incl_scan(wpre);
     const uint32_t total = readlane(incl, 63);
     const uint32_t so = incl - wpre;
+    /* those segments' words lie inside the payload (limit words precede the chunk's) and their
+     * widths are at most 32, or the stream is corrupt */
+    ok = __ballot(wpre > 32u) == 0 && total <= limit;
+    if (!ok) return 0;
     const uint32_t *pw = words_end - total;
     const uint32_t j = lane & 7;
     int32_t sum = 0;
@@ -1693,7 +1480,7 @@ __device__ __forceinline__ int32_t open_block_sum(const uint8_t *__restrict__ in
  * widths and word offsets, then decode_tiles (the centered copy for a centered stream, the
  * general-block copy for a block that is not a power of two). */
 template <bool STRIDED>
-__device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in,
+__device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in, uint64_t in_bytes,
                                             PlanArgs pa, Workspace ws,
                                             float *__restrict__ out) {
     __shared__ uint4 s_pay4[kWavesPerBlock][kDecChunk / 4 + 2];
@@ -1701,15 +1488,55 @@ __device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in,
     __shared__ uint32_t s_so[kWavesPerBlock][kDecSegs];
 
     const uint32_t lane = threadIdx.x & 63;
-    const uint32_t wave = threadIdx.x >> 6;
-    const uint32_t c = blockIdx.x * kWavesPerBlock + wave;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t grp = blockIdx.x;
+    const uint32_t c = grp * kWavesPerBlock + wave;
     if (c >= pa.dchunks) return;
-    const DevInfo *info = ws.info;
-    if (info->err) return;
+    /* The chunk's place in the payload: its group's offset from the offset table plus the sizes
+     * of the group's chunks before it.  Lane l sums the width bytes of the group's segments
+     * 4l .. 4l+3 (chunk l / 16; bytes past the last segment count 0), so every wave of the group
+     * sees the group's four sizes.  The header, the table entries and the widths come in one
+     * round of loads (all lie inside the bytes the host lets through) and the chunk's staging
+     * loads go out next; a staging load that would leave the caller's bytes or the LDS buffer
+     * is not issued (no valid stream asks for one).  Every wave checks its group's sizes against
+     * the table; the whole header is checked (and a bad one reported) by the outlier patch. */
+    const uint32_t hv = load_header_lanes(in, pa, grp);
+    const uint64_t gseg = (uint64_t)grp * (kDecChunksPerGroup * kDecSegs) + 4u * lane;
+    uint32_t wq = gseg < pa.nseg ? *reinterpret_cast<const uint32_t *>(in + kHeaderBytes + gseg) : 0u;
+    const uint64_t seg = (uint64_t)c * kDecSegs + lane;
+    const uint32_t wl = seg < pa.nseg ? (uint32_t)in[kHeaderBytes + seg] : 0u;
+    if (gseg < pa.nseg && pa.nseg - gseg < 4) wq &= (1u << (8u * (uint32_t)(pa.nseg - gseg))) - 1u;
+    const uint32_t gincl = wave_incl_scan(__builtin_amdgcn_sad_u8(wq, 0u, 0u));
+    const uint32_t before = wave > 0 ? readlane(gincl, 16 * (int)wave - 1) : 0u;
+    const uint32_t P = readlane(gincl, 16 * (int)wave + 15) - before;
+    const uint32_t gtot = readlane(gincl, 63);
+    const StreamView H = view_header(hv);
+    const uint64_t W = (uint64_t)(grp > 0 ? readlane(hv, 32) : 0u) + before;
+    const uint64_t sw = H.po / 4 + W; /* stream word index of the chunk's first word */
+    const uint64_t a0 = sw & ~(uint64_t)3;
+    const uint32_t lb = (uint32_t)(sw - a0);
+    uint32_t units = (lb + P + 3) >> 2;
+    const uint64_t lim = in_bytes / 16;
+    const bool staged = P <= (uint32_t)kDecChunk && a0 / 4 <= lim && units <= lim - a0 / 4;
+    if (!staged) units = 0;
+    const uint4 *src = reinterpret_cast<const uint4 *>(in) + a0 / 4;
+    /* every staging load of the chunk is issued before the first LDS store, so the chunk
+     * waits for one memory latency, not one per round of 64 units */
+    constexpr int kRounds = (kDecChunk / 4 + 1 + kWave) / kWave;
+    const uint32_t rounds = (units + kWave - 1) / kWave;
+    uint4 v[kRounds];
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+        const uint32_t u = lane + (uint32_t)r * kWave;
+        v[r] = make_uint4(0, 0, 0, 0);
+        if ((uint32_t)r < rounds && u < units) v[r] = src[u];
+    }
     const uint64_t n = pa.n;
+    if (!H.sane) return;
     const uint64_t cbase = (uint64_t)c * kDecChunk;
     const bool full = cbase + kDecChunk <= n;
-    if (info->mode == 1) {
+    if (H.mode == 1) {
+        if (kHeaderBytes + 4 * n > in_bytes) return;
         const uint64_t cnt = full ? (uint64_t)kDecChunk : n - cbase;
         const uint32_t *srcw = reinterpret_cast<const uint32_t *>(in + kHeaderBytes) + cbase;
         uint32_t *dstw = reinterpret_cast<uint32_t *>(out) + cbase;
@@ -1729,19 +1556,23 @@ __device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in,
         }
         return;
     }
-    const uint32_t W = chunk_offset<kDecChunksPerGroup>(ws.gpre_words, ws.chunk_words, c);
-    const uint32_t P = ws.chunk_words[c];
-    const uint64_t sw = info->payload_off / 4 + W; /* stream word index of the chunk's first word */
-    const uint64_t a0 = sw & ~(uint64_t)3;
-    const uint32_t lb = (uint32_t)(sw - a0);
-    const uint32_t units = (lb + P + 3) >> 2;
-    const uint4 *src = reinterpret_cast<const uint4 *>(in) + a0 / 4;
-    const uint64_t seg = (uint64_t)c * kDecSegs + lane;
-    const uint32_t wl = seg < pa.nseg ? (uint32_t)in[kHeaderBytes + seg] : 0u;
+    /* the group: no width above 32, and the table's range for it holds exactly its words and
+     * ends inside the payload (over every group, these accept exactly the tables that index the
+     * payload the widths describe) */
+    uint64_t t0, t1;
+    table_range(hv, grp, pa.ngroups, H.pw, t0, t1);
+    const uint32_t wbad = (((wq & 0x7F7F7F7Fu) + 0x5F5F5F5Fu) | wq) & 0x80808080u;
+    if (__ballot(wbad != 0) != 0 || t0 > t1 || t1 > H.pw || t1 - t0 != gtot) {
+        if (wave == 0 && lane == 0) atomicOr(&ws.info->sticky, 1u);
+        return;
+    }
+    /* (a stream whose group passes reads nothing past the caller's bytes, unless its header is
+     * bad, which the outlier patch reports) */
+    if (!staged) return;
     /* the stream's block; for one that is not a power of two, the chunk start's offset in its
      * block (r0), the block holding the chunk's first value (bk0) and the reciprocal of B for
      * the small divisions of decode_tiles */
-    const uint32_t B = info->dec_B;
+    const uint32_t B = H.B;
     const bool gb = (B & (B - 1)) != 0;
     uint32_t r0 = 0, bk0 = 0, mB = 0;
     if (gb) {
@@ -1750,10 +1581,13 @@ __device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in,
         r0 = (uint32_t)cbase - bk0 * B;
     }
     /* a centered stream's blocks start from their mean code: in each tile, every lane whose block
-     * starts in the tile takes its block's mean, loaded with the chunk's other loads (lanes past n
-     * read nothing: their blocks' means may lie past the stream's end) */
-    const bool centered = (info->dec_flags & 1u) != 0;
-    const int32_t *means = reinterpret_cast<const int32_t *>(in + kHeaderBytes + pa.wsec);
+     * starts in the tile takes its block's mean, loaded once the header is checked, while the
+     * staging loads are still in flight (lanes past n read nothing: their blocks' means may lie
+     * past the stream's end) */
+    const bool centered = (H.flags & 1u) != 0;
+    const uint64_t mbase = kHeaderBytes + pa.wsec + table_bytes(pa.ngroups);
+    const int32_t *means = reinterpret_cast<const int32_t *>(in + mbase);
+    const uint64_t mlim = in_bytes > mbase ? (in_bytes - mbase) / 4 : 0; /* means inside the caller's bytes */
     int32_t mu[kDecTiles];
 #pragma unroll
     for (int t = 0; t < kDecTiles; ++t) {
@@ -1763,22 +1597,12 @@ __device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in,
             if (gb) {
                 const uint32_t a = r0 + (uint32_t)t * kTile + 4u * lane;
                 const uint32_t q = __umulhi(a, mB);
-                if ((a - q * B) / 4u <= lane) mu[t] = means[bk0 + q];
+                if ((a - q * B) / 4u <= lane && bk0 + q < mlim) mu[t] = means[bk0 + q];
             } else if ((((uint32_t)t * kTile) & (B - 1)) == 0) {
-                mu[t] = means[ev >> (uint32_t)__builtin_ctz(B)];
+                const uint64_t b = ev >> (uint32_t)__builtin_ctz(B);
+                if (b < mlim) mu[t] = means[b];
             }
         }
-    }
-    /* every staging load of the chunk is issued before the first LDS store, so the chunk
-     * waits for one memory latency, not one per round of 64 units */
-    constexpr int kRounds = (kDecChunk / 4 + 1 + kWave) / kWave;
-    const uint32_t rounds = (units + kWave - 1) / kWave;
-    uint4 v[kRounds];
-#pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-        const uint32_t u = lane + (uint32_t)r * kWave;
-        v[r] = make_uint4(0, 0, 0, 0);
-        if ((uint32_t)r < rounds && u < units) v[r] = src[u];
     }
     const uint32_t so = wave_incl_scan(wl) - wl;
 #pragma unroll
@@ -1794,41 +1618,56 @@ __device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in,
     if (gb) {
         int32_t carry0 = 0;
         if (r0 != 0) {
+            bool ok;
             carry0 = open_block_sum(in, (uint64_t)c * kDecSegs, r0 / 32u,
-                                    reinterpret_cast<const uint32_t *>(in) + sw);
-            if (centered) carry0 += means[bk0];
+                                    reinterpret_cast<const uint32_t *>(in) + sw, W, ok);
+            if (!ok) {
+                if (lane == 0) atomicOr(&ws.info->sticky, 1u);
+                return;
+            }
+            if (centered && bk0 < mlim) carry0 += means[bk0];
         }
         if (centered)
-            decode_tiles<STRIDED, true, true>(pa, info, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out, carry0,
+            decode_tiles<STRIDED, true, true>(pa, H.s, B, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out, carry0,
                                               r0, mB);
         else
-            decode_tiles<STRIDED, false, true>(pa, info, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out, carry0,
+            decode_tiles<STRIDED, false, true>(pa, H.s, B, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out, carry0,
                                                r0, mB);
     } else if (centered) {
         /* a centered stream takes its own copy of the tile loop, so the plain one stays as it is */
-        decode_tiles<STRIDED, true, false>(pa, info, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out, 0, 0, 0);
+        decode_tiles<STRIDED, true, false>(pa, H.s, B, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out, 0, 0, 0);
     } else {
-        decode_tiles<STRIDED, false, false>(pa, info, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out, 0, 0, 0);
+        decode_tiles<STRIDED, false, false>(pa, H.s, B, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out, 0, 0, 0);
     }
 }
 
 template <bool STRIDED>
 __global__ __launch_bounds__(kBlockThreads) void decode_kernel(Fields fs, PlanArgs pa, Workspace ws) {
     const uint32_t f = blockIdx.y;
-    decode_body<STRIDED>(pick(fs.src, f), pa, lane_ws(ws, f, fs.ws_stride),
+    decode_body<STRIDED>(pick(fs.src, f), pick(fs.bytes, f), pa, lane_ws(ws, f, fs.ws_stride),
                          reinterpret_cast<float *>(pick(fs.dst, f)));
 }
 
 /* ---- K8: outlier patch ------------------------------------------------------------------------ */
 
 template <bool STRIDED>
-__device__ __forceinline__ void patch_body(const uint8_t *__restrict__ in, PlanArgs pa,
+__device__ __forceinline__ void patch_body(const uint8_t *__restrict__ in, uint64_t in_bytes, PlanArgs pa,
                                            Workspace ws, float *__restrict__ out) {
     DevInfo *info = ws.info;
-    if (info->err || info->mode == 1) return;
-    const uint64_t m = info->m;
-    const uint32_t *oidx = reinterpret_cast<const uint32_t *>(in + info->oidx_off);
-    const uint32_t *oval = reinterpret_cast<const uint32_t *>(in + info->oval_off);
+    const uint32_t hv = load_header_lanes(in, pa, 0);
+    /* the first wave checks the whole header and reports a bad one (the decoders only bound
+     * their reads); the others need only the outlier sections inside the caller's bytes */
+    if (blockIdx.x == 0 && threadIdx.x < kWave &&
+        !header_ok(hv, load_header_template(info), in_bytes, pa.n, pa.V, pa.wsec, pa.ngroups, pa.max_pw)) {
+        if (threadIdx.x == 0) atomicOr(&info->sticky, 1u);
+        return;
+    }
+    const StreamView V = view_header(hv);
+    const uint64_t m = readlane64(hv, 18), oi = readlane64(hv, 26), ov = readlane64(hv, 28);
+    const uint64_t q = in_bytes / 4;
+    if (!V.sane || V.mode == 1 || m > q || (oi | ov) % 4 != 0 || oi / 4 > q - m || ov / 4 > q - m) return;
+    const uint32_t *oidx = reinterpret_cast<const uint32_t *>(in + oi);
+    const uint32_t *oval = reinterpret_cast<const uint32_t *>(in + ov);
     uint32_t *ob = reinterpret_cast<uint32_t *>(out);
     const uint64_t stride = (uint64_t)gridDim.x * 256;
     for (uint64_t k = (uint64_t)blockIdx.x * 256 + threadIdx.x; k < m; k += stride) {
@@ -1842,7 +1681,8 @@ __device__ __forceinline__ void patch_body(const uint8_t *__restrict__ in, PlanA
 template <bool STRIDED>
 __global__ __launch_bounds__(256) void patch_kernel(Fields fs, PlanArgs pa, Workspace ws) {
     const uint32_t f = blockIdx.y;
-    patch_body<STRIDED>(pick(fs.src, f), pa, lane_ws(ws, f, fs.ws_stride), reinterpret_cast<float *>(pick(fs.dst, f)));
+    patch_body<STRIDED>(pick(fs.src, f), pick(fs.bytes, f), pa, lane_ws(ws, f, fs.ws_stride),
+                        reinterpret_cast<float *>(pick(fs.dst, f)));
 }
 
 }  // namespace
@@ -1912,25 +1752,6 @@ hipError_t launch_compact(const Fields &fs, uint32_t nf, const PlanArgs &pa, con
         eblc_launch(compact_kernel<true>, grid, block, 0, stream, fs, pa, ws);
     else
         eblc_launch(compact_kernel<false>, grid, block, 0, stream, fs, pa, ws);
-    return hipGetLastError();
-}
-
-hipError_t launch_decode_sizes(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
-                               hipStream_t stream) {
-    const uint32_t grid = (pa.dchunks + 255) / 256;
-    eblc_launch(decode_sizes_kernel, dim3(grid, nf), dim3(256), 0, stream, fs, pa, ws);
-    return hipGetLastError();
-}
-
-hipError_t launch_scan_decompress(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
-                                  hipStream_t stream) {
-    eblc_launch(scan_decompress_kernel, dim3(1, nf), dim3(kScanThreads), 0, stream, fs, pa, ws);
-    return hipGetLastError();
-}
-
-hipError_t launch_sizes_scan(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
-                             hipStream_t stream) {
-    eblc_launch(sizes_scan_kernel, dim3(1, nf), dim3(kScanThreads), 0, stream, fs, pa, ws);
     return hipGetLastError();
 }
 

@@ -224,11 +224,12 @@ eblc_status eblc_compress_batch(eblc_plan_t *plan, int count, const float *const
  * count of readable bytes up to max_compressed_bytes: the stream's own length is read from its
  * header on the device and must not exceed it, so a stream from eblc_compress_async can be
  * decompressed without the host ever reading its length.  The host checks 128 + (size of the
- * width or word-count section) <= compressed_bytes <= max_compressed_bytes (else
- * CORRUPT_STREAM at once).  A plan decodes RAW streams and coded streams of its own coder
- * (and, for the chunk coder, of its own chunk size); any other stream is CORRUPT_STREAM.
- * Header or section problems found on the device (wrong magic/version/dims/n/offsets, widths
- * above 32, chunk word counts outside [V/32, V + V/32] or unequal to the bitmap's count,
+ * width or word-count section) + (size of the offset table) <= compressed_bytes <=
+ * max_compressed_bytes (else CORRUPT_STREAM at once).  A plan decodes RAW streams and coded
+ * streams of its own coder (and, for the chunk coder, of its own chunk size); any other stream
+ * is CORRUPT_STREAM.  Header or section problems found on the device (wrong magic/version/
+ * dims/n/offsets, widths above 32, chunk word counts outside [V/32, V + V/32] or unequal to the
+ * bitmap's count, an offset-table entry that does not index the payload the sizes describe,
  * outlier indices not strictly ascending below n) set a sticky CORRUPT_STREAM that
  * eblc_plan_status returns; the contents of `out` are then unspecified.  sidecar must be
  * NULL. */
@@ -265,7 +266,7 @@ const char *eblc_status_string(eblc_status s);
  * the device, then binds a HIP event pair to each of the plan's next k timed kernel launches
  * (the kernel dispatch itself records them, on the stream the launch runs on); k = 0 turns
  * recording off.  kernels is NULL or "" (every kernel), or a comma-separated list of the names
- * to time (range, encode, scan, compact, decode_sizes, decode_scan, decode, patch); only the
+ * to time (range, encode, scan, compact, decode, patch); only the
  * every-th, 2·every-th, ... compress and decompress launch sequences (counted apart; a batch
  * call makes one per group of fields) are timed.  A timed dispatch still costs the stream a few
  * microseconds, so naming few kernels and sampling keep the rest of the work undisturbed.

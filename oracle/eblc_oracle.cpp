@@ -27,8 +27,9 @@ uint64_t align16(uint64_t v) { return (v + 15u) / 16u * 16u; }
 /* The offset table, an index of this codec's own container (the pages' concatenated output
  * records each buffer's size ahead of its data, "Architecture", Execution Flow, Compression,
  * so that a file describes itself): the payload words that precede each group of
- * kGroupValues values, one u32 per group after the first, in a section of its own after the
- * outlier values, padded to 16 bytes.  A decoder takes any group's payload offset from it. */
+ * kGroupValues values, one u32 per group after the first, in a section of its own right after
+ * the size section (widths or chunk word counts), padded to 16 bytes.  A decoder takes any
+ * group's payload offset from it. */
 const uint64_t kGroupValues = 8192;
 
 uint64_t table_bytes(uint64_t n) {
@@ -231,10 +232,10 @@ uint32_t oracle_unpack_one(const uint32_t *words, uint32_t w, uint32_t j) {
 
 uint64_t oracle_stream_bytes(uint64_t n, uint64_t sum_widths, uint64_t m) {
     uint64_t nseg = (n + kSeg - 1) / kSeg;
-    uint64_t payload_off = kHeaderBytes + align16(nseg);
+    uint64_t payload_off = kHeaderBytes + align16(nseg) + table_bytes(n);
     uint64_t oidx_off = payload_off + align16(4 * sum_widths);
     uint64_t oval_off = oidx_off + align16(4 * m);
-    return oval_off + align16(4 * m) + table_bytes(n);
+    return oval_off + align16(4 * m);
 }
 
 uint64_t oracle_raw_bytes(uint64_t n) { return kHeaderBytes + align16(4 * n); }
@@ -347,10 +348,10 @@ int oracle_unrze(const uint32_t *in, uint32_t len, uint32_t W, uint32_t *words) 
  * outlier count. */
 uint64_t oracle_chunk_stream_bytes(uint64_t n, uint32_t V, uint64_t sum_words, uint64_t m) {
     uint64_t nchunks = (n + V - 1) / V;
-    uint64_t payload_off = kHeaderBytes + align16(4 * nchunks);
+    uint64_t payload_off = kHeaderBytes + align16(4 * nchunks) + table_bytes(n);
     uint64_t oidx_off = payload_off + align16(4 * sum_words);
     uint64_t oval_off = oidx_off + align16(4 * m);
-    return oval_off + align16(4 * m) + table_bytes(n);
+    return oval_off + align16(4 * m);
 }
 
 /* The 128-byte header: magic, version, layout of the sections (all offsets from the start). */
@@ -455,7 +456,8 @@ uint64_t oracle_compress_ex(const float *x, int rank, const uint64_t *dims, int 
         std::memcpy(out + kHeaderBytes, x, 4 * n);
         return total;
     }
-    uint64_t means_off = kHeaderBytes + align16(nseg);
+    uint64_t table_off = kHeaderBytes + align16(nseg);
+    uint64_t means_off = table_off + table_bytes(n);
     uint64_t payload_off = means_off + msec;
     uint64_t oidx_off = payload_off + align16(4 * sum_w);
     uint64_t oval_off = oidx_off + align16(4 * m);
@@ -473,7 +475,6 @@ uint64_t oracle_compress_ex(const float *x, int rank, const uint64_t *dims, int 
     /* the offset table: segments of 32 values, kGroupValues / 32 to a group */
     std::vector<uint64_t> seg_words(widths.begin(), widths.end());
     std::vector<uint32_t> table = table_entries(seg_words, kGroupValues / kSeg);
-    uint64_t table_off = oval_off + align16(4 * m);
     for (uint64_t g = 0; g < table.size(); ++g) put_u32(out, table_off + 4 * g, table[g]);
     return total;
 }
@@ -543,7 +544,8 @@ uint64_t oracle_compress_chunked(const float *x, int rank, const uint64_t *dims,
         return total;
     }
     uint64_t m = oidx.size();
-    uint64_t payload_off = kHeaderBytes + align16(4 * nchunks);
+    uint64_t table_off = kHeaderBytes + align16(4 * nchunks);
+    uint64_t payload_off = table_off + table_bytes(n);
     uint64_t oidx_off = payload_off + align16(4 * payload.size());
     uint64_t oval_off = oidx_off + align16(4 * m);
     write_header(out, kModeChunk, rank, dims, n, log2v, T, V, eb_f, s, r, m, 4 * payload.size(),
@@ -557,7 +559,6 @@ uint64_t oracle_compress_chunked(const float *x, int rank, const uint64_t *dims,
     /* the offset table: chunks of V values, kGroupValues / V to a group */
     std::vector<uint64_t> chunk_words(sizes.begin(), sizes.end());
     std::vector<uint32_t> table = table_entries(chunk_words, kGroupValues / V);
-    uint64_t table_off = oval_off + align16(4 * m);
     for (uint64_t g = 0; g < table.size(); ++g) put_u32(out, table_off + 4 * g, table[g]);
     return total;
 }
@@ -603,13 +604,13 @@ static uint64_t check_header(const uint8_t *in, uint64_t len) {
         if (mode == kModeLossy) {
             uint64_t nseg = (n + kSeg - 1) / kSeg;
             uint64_t msec = flags ? align16(4 * ((n + B - 1) / B)) : 0;
-            if (pb > 4ull * 32 * nseg || po != kHeaderBytes + align16(nseg) + msec) return 0;
+            if (pb > 4ull * 32 * nseg || po != kHeaderBytes + align16(nseg) + table_bytes(n) + msec) return 0;
         } else {
             uint64_t nchunks = (n + B - 1) / B;
-            if (pb > 4ull * nchunks * (B + B / 32) || po != kHeaderBytes + align16(4 * nchunks)) return 0;
+            if (pb > 4ull * nchunks * (B + B / 32) || po != kHeaderBytes + align16(4 * nchunks) + table_bytes(n))
+                return 0;
         }
-        if (oi != po + align16(pb) || ov != oi + align16(4 * m)) return 0;
-        if (tot != ov + align16(4 * m) + table_bytes(n)) return 0;
+        if (oi != po + align16(pb) || ov != oi + align16(4 * m) || tot != ov + align16(4 * m)) return 0;
     }
     if (tot > len) return 0;
     return n;
@@ -705,14 +706,15 @@ int oracle_decompress(const uint8_t *in, uint64_t len, float *out, uint64_t n_ou
             units_per_group = kGroupValues / kSeg;
         }
         std::vector<uint32_t> table = table_entries(unit_words, units_per_group);
-        uint64_t table_off = ov + align16(4 * m);
+        uint64_t table_off = kHeaderBytes + (mode == kModeChunk ? align16(4 * ((n + B - 1) / B))
+                                                                : align16((n + kSeg - 1) / kSeg));
         for (uint64_t g = 0; g < table.size(); ++g)
             if (get_u32(in, table_off + 4 * g) != table[g]) return ORACLE_CORRUPT;
     }
     /* undelta: running sum from each block start (from the block's mean when the stream is
      * centered, else from 0), then dequantize */
     uint32_t flags = get_u32(in, 68);
-    uint64_t means_off = kHeaderBytes + align16((n + kSeg - 1) / kSeg);
+    uint64_t means_off = kHeaderBytes + align16((n + kSeg - 1) / kSeg) + table_bytes(n);
     int32_t qprev = 0;
     for (uint64_t i = 0; i < n; ++i) {
         int32_t qi;

@@ -102,8 +102,8 @@ def join(x: np.ndarray, dims, T: int, B: int, side_max: int, center: bool, V: in
             sizes.append(s[HEADER:HEADER + nseg])
             if center:
                 nb = (ni + B - 1) // B
-                moff = HEADER + _align16(nseg)
-                means.append(s[moff:moff + 4 * nb])
+                pm = HEADER + _align16(nseg) + _align16(4 * ((ni + GROUP_VALUES - 1) // GROUP_VALUES - 1))
+                means.append(s[pm:pm + 4 * nb])
         pay.append(s[h["po"]:h["po"] + h["pb"]])
         oidx.append(s[h["oi"]:h["oi"] + 4 * h["m"]].view(np.uint32) + np.uint32(a))
         oval.append(s[h["ov"]:h["ov"] + 4 * h["m"]])
@@ -142,17 +142,19 @@ def join(x: np.ndarray, dims, T: int, B: int, side_max: int, center: bool, V: in
     hdr[9], hdr[11] = rank, T
     hdr[10] = int(V).bit_length() - 1 if V else 5
     size_sec = _align16(sizes.size)
-    msec = _align16(4 * ((n + B - 1) // B)) if (center and not V) else 0
-    po = HEADER + size_sec + msec
-    oi = po + _align16(pay.size)
-    ov = oi + _align16(4 * m)
-    # the offset table: payload words before each group of GROUP_VALUES values after the first
+    # the offset table after the size section: payload words before each group of GROUP_VALUES
+    # values after the first
     unit_words = sizes.view(np.uint32).astype(np.int64) if V else sizes.astype(np.int64)
     per_group = GROUP_VALUES // (V if V else 32)
     starts = np.arange(per_group, unit_words.size, per_group)
     table = np.concatenate([[0], np.cumsum(unit_words)])[starts].astype(np.uint32)
-    tab = ov + _align16(4 * m)
-    total = tab + _align16(4 * table.size)
+    tab = HEADER + size_sec
+    msec = _align16(4 * ((n + B - 1) // B)) if (center and not V) else 0
+    moff = tab + _align16(4 * table.size)
+    po = moff + msec
+    oi = po + _align16(pay.size)
+    ov = oi + _align16(4 * m)
+    total = ov + _align16(4 * m)
     hu32[17] = 1 if (center and not V) else 0
     hu64[9], hu64[10], hu64[12], hu64[13], hu64[14], hu64[15] = m, pay.size, po, oi, ov, total
     out = np.zeros(total, np.uint8)
@@ -160,7 +162,7 @@ def join(x: np.ndarray, dims, T: int, B: int, side_max: int, center: bool, V: in
     out[HEADER:HEADER + sizes.size] = sizes
     if msec:
         mm = np.concatenate(means)
-        out[HEADER + size_sec:HEADER + size_sec + mm.size] = mm
+        out[moff:moff + mm.size] = mm
     out[po:po + pay.size] = pay
     if m:
         out[oi:oi + 4 * m] = np.concatenate(oidx).view(np.uint8)

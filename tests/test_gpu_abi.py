@@ -180,6 +180,14 @@ def _corrupt_cases(stream: np.ndarray, n: int):
     s = stream.copy(); s[96:104] = np.frombuffer(np.uint64(payload_off + 16).tobytes(), np.uint8)
     cases.append(("payload offset", s, total))
     cases.append(("truncated", stream.copy(), total - 16))
+    if n > 8192:
+        # the offset table after the widths: its entries must index the payload
+        tab = 128 + 16 * (((n + 31) // 32 + 15) // 16)
+        ent = int(stream[tab:tab + 4].view(np.uint32)[0])
+        s = stream.copy(); s[tab:tab + 4] = np.frombuffer(np.uint32(ent + 1).tobytes(), np.uint8)
+        cases.append(("offset table entry", s, total))
+        s = stream.copy(); s[tab:tab + 4] = np.frombuffer(np.uint32(1 << 30).tobytes(), np.uint8)
+        cases.append(("offset table entry past the payload", s, total))
     if m >= 2:
         idx = stream[oidx_off:oidx_off + 4 * m].view(np.uint32)
         s = stream.copy()

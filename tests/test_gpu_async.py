@@ -184,8 +184,7 @@ def test_kernel_time_records_cover_every_lane(env):
         assert binding.eblc_decompress_batch(plan, outs, ys) == binding.EBLC_OK
         rec = binding.eblc_plan_kernel_times(plan)
         names = [r[0] for r in rec]
-        # a field of at most 2048 decode chunks takes its sizes and scan in one launch
-        assert names == ["range", "encode", "scan", "compact", "sizes_scan", "decode", "patch"]
+        assert names == ["range", "encode", "scan", "compact", "decode", "patch"]
         assert all(cnt == 2 and ms > 0 for _, ms, cnt in rec)  # groups of 3 and 2 fields
         assert binding.eblc_plan_kernel_times(plan) == []       # records cleared by the read
         assert binding.eblc_plan_set_profiling(plan, 3) == binding.EBLC_OK

@@ -231,6 +231,12 @@ def test_chunk_corrupt_and_mismatched_streams(env):
         assert status_of(edited(lambda t: put32(t, 128, 2048 + 65))) == binding.EBLC_CORRUPT_STREAM
         assert status_of(edited(lambda t: put32(t, 128, s0 + 1))) == binding.EBLC_CORRUPT_STREAM  # sum off
         assert status_of(edited(lambda t: t.__setitem__(po, t[po] ^ 1))) == binding.EBLC_CORRUPT_STREAM  # bitmap
+        # the offset table (one entry per 8192-value group after the first) must index the payload
+        tab = 128 + 16 * ((4 * ((n + 2047) // 2048) + 15) // 16)
+        ent = good[tab:tab + 12].view(np.uint32).astype(np.int64)
+        for k in range(3):
+            assert status_of(edited(lambda t: put32(t, tab + 4 * k, int(ent[k]) + 1))) == binding.EBLC_CORRUPT_STREAM
+        assert status_of(edited(lambda t: put32(t, tab + 8, 1 << 30))) == binding.EBLC_CORRUPT_STREAM
         # a stream of the bitpack coder, and one of another chunk size, are refused by this plan
         other = oracle_stream(oracle, x, [n], "rel=1e-4;block=256")
         assert status_of(other) == binding.EBLC_CORRUPT_STREAM

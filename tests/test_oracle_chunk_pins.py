@@ -235,8 +235,10 @@ def test_golden_chunk_table_stream():
         want += bm + [int(v, 16) for v in spec["words"]]
     assert [int(v) for v in words] == want
     t0 = exp["table_off"]
+    assert t0 == 128 + 16 * ((4 * nch + 15) // 16)
     assert [int(v) for v in s[t0:t0 + 4 * len(exp["table"])].view(np.uint32)] == exp["table"]
-    assert not s[t0 + 4 * len(exp["table"]):].any()
+    assert not s[t0 + 4 * len(exp["table"]):h["payload_off"]].any()
+    assert not s[h["payload_off"] + h["payload_bytes"]:].any()
     st, y = oracle.decompress(s)
     assert st == oracle.OK and np.array_equal(y, x)
     for k in range(len(exp["table"])):
@@ -253,12 +255,13 @@ def test_zero_codes_cost_the_bitmap_only(V):
     h = hdr(s)
     assert h["mode"] == 2
     assert [int(v) for v in s[128:128 + 12].view(np.uint32)] == [V // 32] * 3
-    assert h["payload_bytes"] == 3 * 4 * (V // 32) and not s[h["payload_off"]:h["oidx_off"]].any()
+    assert h["payload_bytes"] == 3 * 4 * (V // 32) and not s[h["payload_off"]:].any()
     # the offset table: one entry per 8192-value group after the first, each the bitmap words
     # of the chunks before its group (only the 16 KiB chunks span more than one group here)
     table = [(8192 // V) * (V // 32)] if n > 8192 else []
     tb = 16 * ((4 * len(table) + 15) // 16)
-    assert [int(v) for v in s[h["oval_off"]:h["oval_off"] + 4 * len(table)].view(np.uint32)] == table
+    assert [int(v) for v in s[144:144 + 4 * len(table)].view(np.uint32)] == table
+    assert h["payload_off"] == 144 + tb
     assert len(s) == 128 + 16 + 3 * 4 * (V // 32) + tb
 
 

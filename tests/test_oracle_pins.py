@@ -123,8 +123,10 @@ def test_golden_table_stream():
         want[int(k)] = int(v, 16)
     assert np.array_equal(words, want)
     t0 = exp["table_off"]
+    assert t0 == 128 + 16 * ((nseg + 15) // 16)
     assert [int(v) for v in s[t0:t0 + 4 * len(exp["table"])].view(np.uint32)] == exp["table"]
-    assert not s[t0 + 4 * len(exp["table"]):].any()
+    assert not s[t0 + 4 * len(exp["table"]):h["payload_off"]].any()
+    assert not s[h["payload_off"] + h["payload_bytes"]:].any()
     st, y = oracle.decompress(s)
     assert st == oracle.OK and np.array_equal(y, x)
     # a table that does not index the payload is refused, entry by entry
@@ -133,8 +135,8 @@ def test_golden_table_stream():
             t = s.copy()
             t[t0 + 4 * k:t0 + 4 * k + 4] = np.array([exp["table"][k] + delta], np.uint32).view(np.uint8)
             assert oracle.decompress(t)[0] == oracle.CORRUPT, (k, delta)
-    # and a stream cut before its table
-    assert oracle.decompress(s[:t0], n)[0] == oracle.CORRUPT
+    # and a stream cut inside its payload
+    assert oracle.decompress(s[:h["payload_off"] + 16], n)[0] == oracle.CORRUPT
 
 
 @pytest.mark.parametrize("n", [8192, 8193, 16384, 16385, 40000])
@@ -147,9 +149,10 @@ def test_table_size_closed_form(n):
     h = hdr(s)
     assert h["mode"] == 0
     groups = (n + 8191) // 8192
-    assert h["total"] == h["oval_off"] + 16 * ((4 * h["m"] + 15) // 16) + 16 * ((4 * (groups - 1) + 15) // 16)
-    t0 = h["oval_off"] + 16 * ((4 * h["m"] + 15) // 16)
     nseg = (n + 31) // 32
+    t0 = 128 + 16 * ((nseg + 15) // 16)
+    assert h["payload_off"] == t0 + 16 * ((4 * (groups - 1) + 15) // 16)
+    assert h["total"] == h["oval_off"] + 16 * ((4 * h["m"] + 15) // 16)
     run = np.cumsum(s[128:128 + nseg].astype(np.int64))
     got = s[t0:t0 + 4 * (groups - 1)].view(np.uint32)
     assert [int(v) for v in got] == [int(run[256 * g - 1]) for g in range(1, groups)]
