@@ -1476,67 +1476,43 @@ __device__ __forceinline__ int32_t open_block_sum(const uint8_t *__restrict__ in
     return (int32_t)readlane(wave_incl_scan((uint32_t)sum), 63);
 }
 
-/* One wave per chunk: stage the chunk's packed words in LDS (128-bit loads) and its segment
- * widths and word offsets, then decode_tiles (the centered copy for a centered stream, the
+/* One workgroup per table group, one wave per chunk: the workgroup stages the group's packed
+ * words in LDS (128-bit loads), each wave its chunk's segment widths and word offsets, then
+ * each wave runs decode_tiles on its chunk (the centered copy for a centered stream, the
  * general-block copy for a block that is not a power of two). */
 template <bool STRIDED>
 __device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in, uint64_t in_bytes,
                                             PlanArgs pa, Workspace ws,
                                             float *__restrict__ out) {
-    __shared__ uint4 s_pay4[kWavesPerBlock][kDecChunk / 4 + 2];
+    constexpr uint32_t kGroupUnits = kDecChunksPerGroup * kDecChunk / 4 + 2;
+    __shared__ uint4 s_pay4[kGroupUnits];
     __shared__ uint32_t s_w[kWavesPerBlock][kDecSegs];
     __shared__ uint32_t s_so[kWavesPerBlock][kDecSegs];
 
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t grp = blockIdx.x;
-    const uint32_t c = grp * kWavesPerBlock + wave;
-    if (c >= pa.dchunks) return;
-    /* The chunk's place in the payload: its group's offset from the offset table plus the sizes
-     * of the group's chunks before it.  Lane l sums the width bytes of the group's segments
-     * 4l .. 4l+3 (chunk l / 16; bytes past the last segment count 0), so every wave of the group
-     * sees the group's four sizes.  The header, the table entries and the widths come in one
-     * round of loads (all lie inside the bytes the host lets through) and the chunk's staging
-     * loads go out next; a staging load that would leave the caller's bytes or the LDS buffer
-     * is not issued (no valid stream asks for one).  Every wave checks its group's sizes against
-     * the table; the whole header is checked (and a bad one reported) by the outlier patch. */
+    const uint32_t c = grp * kWavesPerBlock + wave; /* may be past the last chunk in the last group */
+    /* The group's payload is the range the offset table gives it, so the workgroup's staging
+     * loads go out as soon as the header and the table entries are in (one round of loads: all
+     * lie inside the bytes the host lets through), while the widths are still on their way; a
+     * staging load that would leave the caller's bytes is not issued (no valid stream asks for
+     * one).  Lane l of every wave sums the width bytes of the group's segments 4l .. 4l+3 (chunk
+     * l / 16; bytes past the last segment count 0), which places each chunk in the group and
+     * checks the group: no width above 32 and exactly the words the table gives it.  The whole
+     * header is checked (and a bad one reported) by the outlier patch. */
     const uint32_t hv = load_header_lanes(in, pa, grp);
     const uint64_t gseg = (uint64_t)grp * (kDecChunksPerGroup * kDecSegs) + 4u * lane;
     uint32_t wq = gseg < pa.nseg ? *reinterpret_cast<const uint32_t *>(in + kHeaderBytes + gseg) : 0u;
     const uint64_t seg = (uint64_t)c * kDecSegs + lane;
     const uint32_t wl = seg < pa.nseg ? (uint32_t)in[kHeaderBytes + seg] : 0u;
-    if (gseg < pa.nseg && pa.nseg - gseg < 4) wq &= (1u << (8u * (uint32_t)(pa.nseg - gseg))) - 1u;
-    const uint32_t gincl = wave_incl_scan(__builtin_amdgcn_sad_u8(wq, 0u, 0u));
-    const uint32_t before = wave > 0 ? readlane(gincl, 16 * (int)wave - 1) : 0u;
-    const uint32_t P = readlane(gincl, 16 * (int)wave + 15) - before;
-    const uint32_t gtot = readlane(gincl, 63);
     const StreamView H = view_header(hv);
-    const uint64_t W = (uint64_t)(grp > 0 ? readlane(hv, 32) : 0u) + before;
-    const uint64_t sw = H.po / 4 + W; /* stream word index of the chunk's first word */
-    const uint64_t a0 = sw & ~(uint64_t)3;
-    const uint32_t lb = (uint32_t)(sw - a0);
-    uint32_t units = (lb + P + 3) >> 2;
-    const uint64_t lim = in_bytes / 16;
-    const bool staged = P <= (uint32_t)kDecChunk && a0 / 4 <= lim && units <= lim - a0 / 4;
-    if (!staged) units = 0;
-    const uint4 *src = reinterpret_cast<const uint4 *>(in) + a0 / 4;
-    /* every staging load of the chunk is issued before the first LDS store, so the chunk
-     * waits for one memory latency, not one per round of 64 units */
-    constexpr int kRounds = (kDecChunk / 4 + 1 + kWave) / kWave;
-    const uint32_t rounds = (units + kWave - 1) / kWave;
-    uint4 v[kRounds];
-#pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-        const uint32_t u = lane + (uint32_t)r * kWave;
-        v[r] = make_uint4(0, 0, 0, 0);
-        if ((uint32_t)r < rounds && u < units) v[r] = src[u];
-    }
     const uint64_t n = pa.n;
-    if (!H.sane) return;
+    if (!H.sane) return; /* the same in every wave of the workgroup, as every test before the barrier */
     const uint64_t cbase = (uint64_t)c * kDecChunk;
     const bool full = cbase + kDecChunk <= n;
     if (H.mode == 1) {
-        if (kHeaderBytes + 4 * n > in_bytes) return;
+        if (c >= pa.dchunks || kHeaderBytes + 4 * n > in_bytes) return;
         const uint64_t cnt = full ? (uint64_t)kDecChunk : n - cbase;
         const uint32_t *srcw = reinterpret_cast<const uint32_t *>(in + kHeaderBytes) + cbase;
         uint32_t *dstw = reinterpret_cast<uint32_t *>(out) + cbase;
@@ -1556,19 +1532,39 @@ __device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in, uint
         }
         return;
     }
-    /* the group: no width above 32, and the table's range for it holds exactly its words and
-     * ends inside the payload (over every group, these accept exactly the tables that index the
-     * payload the widths describe) */
     uint64_t t0, t1;
     table_range(hv, grp, pa.ngroups, H.pw, t0, t1);
+    const uint64_t gw0 = H.po / 4 + t0;  /* stream word index of the group's first word */
+    const uint64_t a0 = gw0 & ~(uint64_t)3;
+    const uint32_t lb = (uint32_t)(gw0 - a0);
+    const uint64_t lim = in_bytes / 16;
+    const bool range_ok = t0 <= t1 && t1 <= H.pw && t1 - t0 <= (uint64_t)(kDecChunksPerGroup * kDecChunk);
+    const uint32_t units = range_ok ? (uint32_t)((lb + (t1 - t0) + 3) >> 2) : 0u;
+    if (!range_ok || a0 / 4 > lim || units > lim - a0 / 4) {
+        if (wave == 0 && lane == 0 && !range_ok) atomicOr(&ws.info->sticky, 1u);
+        return;
+    }
+    /* every staging load of the group is issued before the first LDS store */
+    constexpr int kRounds = (kGroupUnits + kBlockThreads - 1) / kBlockThreads;
+    const uint4 *src = reinterpret_cast<const uint4 *>(in) + a0 / 4;
+    uint4 v[kRounds];
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+        const uint32_t u = threadIdx.x + (uint32_t)r * kBlockThreads;
+        v[r] = make_uint4(0, 0, 0, 0);
+        if (u < units) v[r] = src[u];
+    }
+    if (gseg < pa.nseg && pa.nseg - gseg < 4) wq &= (1u << (8u * (uint32_t)(pa.nseg - gseg))) - 1u;
+    const uint32_t gincl = wave_incl_scan(__builtin_amdgcn_sad_u8(wq, 0u, 0u));
+    const uint32_t before = wave > 0 ? readlane(gincl, 16 * (int)wave - 1) : 0u;
+    const uint32_t gtot = readlane(gincl, 63);
     const uint32_t wbad = (((wq & 0x7F7F7F7Fu) + 0x5F5F5F5Fu) | wq) & 0x80808080u;
-    if (__ballot(wbad != 0) != 0 || t0 > t1 || t1 > H.pw || t1 - t0 != gtot) {
+    if (__ballot(wbad != 0) != 0 || t1 - t0 != gtot) {
         if (wave == 0 && lane == 0) atomicOr(&ws.info->sticky, 1u);
         return;
     }
-    /* (a stream whose group passes reads nothing past the caller's bytes, unless its header is
-     * bad, which the outlier patch reports) */
-    if (!staged) return;
+    const uint64_t W = t0 + before;       /* payload words before the chunk */
+    const uint64_t sw = H.po / 4 + W;     /* stream word index of the chunk's first word */
     /* the stream's block; for one that is not a power of two, the chunk start's offset in its
      * block (r0), the block holding the chunk's first value (bk0) and the reciprocal of B for
      * the small divisions of decode_tiles */
@@ -1607,14 +1603,16 @@ __device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in, uint
     const uint32_t so = wave_incl_scan(wl) - wl;
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
-        const uint32_t u = lane + (uint32_t)r * kWave;
-        if ((uint32_t)r < rounds && u < units) s_pay4[wave][u] = v[r];
+        const uint32_t u = threadIdx.x + (uint32_t)r * kBlockThreads;
+        if (u < units) s_pay4[u] = v[r];
     }
     s_w[wave][lane] = wl;
     s_so[wave][lane] = so;
-    wave_lds_sync();
-
-    const uint32_t *pay = reinterpret_cast<const uint32_t *>(s_pay4[wave]);
+    __syncthreads();
+    if (c >= pa.dchunks) return;
+    /* the chunk's words sit at word lb + before of the group's staging */
+    const uint32_t *pay = reinterpret_cast<const uint32_t *>(s_pay4);
+    const uint32_t lbc = lb + before;
     if (gb) {
         int32_t carry0 = 0;
         if (r0 != 0) {
@@ -1628,16 +1626,16 @@ __device__ __forceinline__ void decode_body(const uint8_t *__restrict__ in, uint
             if (centered && bk0 < mlim) carry0 += means[bk0];
         }
         if (centered)
-            decode_tiles<STRIDED, true, true>(pa, H.s, B, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out, carry0,
+            decode_tiles<STRIDED, true, true>(pa, H.s, B, mu, pay, s_w[wave], s_so[wave], lbc, cbase, full, out, carry0,
                                               r0, mB);
         else
-            decode_tiles<STRIDED, false, true>(pa, H.s, B, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out, carry0,
+            decode_tiles<STRIDED, false, true>(pa, H.s, B, mu, pay, s_w[wave], s_so[wave], lbc, cbase, full, out, carry0,
                                                r0, mB);
     } else if (centered) {
         /* a centered stream takes its own copy of the tile loop, so the plain one stays as it is */
-        decode_tiles<STRIDED, true, false>(pa, H.s, B, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out, 0, 0, 0);
+        decode_tiles<STRIDED, true, false>(pa, H.s, B, mu, pay, s_w[wave], s_so[wave], lbc, cbase, full, out, 0, 0, 0);
     } else {
-        decode_tiles<STRIDED, false, false>(pa, H.s, B, mu, pay, s_w[wave], s_so[wave], lb, cbase, full, out, 0, 0, 0);
+        decode_tiles<STRIDED, false, false>(pa, H.s, B, mu, pay, s_w[wave], s_so[wave], lbc, cbase, full, out, 0, 0, 0);
     }
 }
 
