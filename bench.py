@@ -508,8 +508,9 @@ def main() -> int:
     comp_alg = in_bytes * (2 if rel_mode else 1) + total_stream
     decomp_alg = total_stream + in_bytes + 12 * total_m
     launches_per_stage = -(-len(items) // lanes)
-    comp_kernels = ("range_partial_kernel", "range_resolve_kernel", kernels[0], "scan_compress_kernel",
-                    "compact_kernel")
+    # a field of at most 2048 groups of 8192 values scans its group sums inside the compaction
+    tail = ("compact_scan_kernel",) if -(-n // 8192) <= 2048 else ("scan_compress_kernel", "compact_kernel")
+    comp_kernels = ("range_partial_kernel", "range_resolve_kernel", kernels[0]) + tail
     dec_kernels = (kernels[1], "patch_kernel")
 
     def call_frac(alg, ms, ks):

@@ -338,8 +338,12 @@ hipError_t enqueue_compress(eblc_plan *plan, int nf, const float *const *in, voi
         e = timed(plan, "encode", [&] {
             return pa.V ? launch_chunk_encode(fs, n, pa, ws, st) : launch_encode(fs, n, pa, ws, st);
         });
-    if (e == hipSuccess) e = timed(plan, "scan", [&] { return launch_scan_compress(fs, n, pa, ws, st); });
-    if (e == hipSuccess) e = timed(plan, "compact", [&] { return launch_compact(fs, n, pa, ws, st); });
+    if (compact_folds_scan(pa)) {
+        if (e == hipSuccess) e = timed(plan, "compact", [&] { return launch_compact_scan(fs, n, pa, ws, st); });
+    } else {
+        if (e == hipSuccess) e = timed(plan, "scan", [&] { return launch_scan_compress(fs, n, pa, ws, st); });
+        if (e == hipSuccess) e = timed(plan, "compact", [&] { return launch_compact(fs, n, pa, ws, st); });
+    }
     return e;
 }
 

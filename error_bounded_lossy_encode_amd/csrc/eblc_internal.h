@@ -215,6 +215,12 @@ hipError_t launch_scan_compress(const Fields &fs, uint32_t nf, const PlanArgs &p
                                 hipStream_t stream);
 hipError_t launch_compact(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                           hipStream_t stream);
+/* Scan and compaction in one launch, for fields of at most 2048 groups (2^24 values): each
+ * compaction workgroup scans the group sums itself; launch_compact_scan replaces
+ * launch_scan_compress + launch_compact when compact_folds_scan(pa). */
+bool compact_folds_scan(const PlanArgs &pa);
+hipError_t launch_compact_scan(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
+                               hipStream_t stream);
 hipError_t launch_decode(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
                          hipStream_t stream);
 hipError_t launch_patch(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,

@@ -881,6 +881,89 @@ __device__ void block_scan2(const uint32_t *__restrict__ a, const uint32_t *__re
     tot[1] = carry_b;
 }
 
+/* Where a compressed stream's sections go, from its payload words S and escapes m: RAW when
+ * the bound is unusable, when more values escape than the side list holds or when the coded
+ * stream would be larger than the raw one; fits when the whole stream fits the caller's cap. */
+struct StreamPlace {
+    bool raw;
+    uint32_t fits;
+    uint64_t m, pb, po, oi, ov, tot;
+};
+
+__device__ __forceinline__ StreamPlace place_stream(const PlanArgs &pa, uint64_t S, uint64_t m, bool valid,
+                                                    uint64_t cap) {
+    const uint64_t n = pa.n;
+    const uint64_t raw_total = kHeaderBytes + align16(4 * n);
+    const uint64_t payload_off = kHeaderBytes + pa.wsec + table_bytes(pa.ngroups) + pa.msec;
+    const uint64_t lossy_total = payload_off + align16(4 * S) + 2 * align16(4 * m);
+    StreamPlace P;
+    P.raw = !valid || m > pa.side_max || lossy_total > raw_total;
+    if (P.raw) {
+        P.m = 0; P.pb = 4 * n; P.po = kHeaderBytes;
+        P.oi = raw_total; P.ov = raw_total; P.tot = raw_total;
+    } else {
+        P.m = m; P.pb = 4 * S; P.po = payload_off;
+        P.oi = payload_off + align16(4 * S);
+        P.ov = P.oi + align16(4 * m);
+        P.tot = P.ov + align16(4 * m);
+    }
+    P.fits = P.tot <= cap ? 1u : 0u;
+    return P;
+}
+
+/* The placement as the compaction reads it back from the workspace. */
+__device__ __forceinline__ StreamPlace place_from_info(const DevInfo *info) {
+    StreamPlace P;
+    P.raw = info->mode == 1;
+    P.fits = info->fits;
+    P.m = info->m;
+    P.pb = 4 * info->payload_words;
+    P.po = info->payload_off;
+    P.oi = info->oidx_off;
+    P.ov = info->oval_off;
+    P.tot = info->total;
+    return P;
+}
+
+/* One thread: the placement into the workspace and the caller's result record (length, or
+ * the required capacity, then the status), and the 128-byte header into h. */
+__device__ __forceinline__ void publish_stream(const PlanArgs &pa, const StreamPlace &P, DevInfo *info,
+                                               uint64_t *result, uint32_t h[32]) {
+    info->mode = P.raw ? 1u : (pa.V ? 2u : 0u);
+    info->m = P.m;
+    info->payload_words = P.pb / 4;
+    info->payload_off = P.po;
+    info->oidx_off = P.oi;
+    info->oval_off = P.ov;
+    info->total = P.tot;
+    info->fits = P.fits;
+    if (result != nullptr) {
+        result[0] = P.tot;
+        result[1] = P.fits ? 0u : 3u;
+    }
+    h[0] = kMagic;
+    h[1] = kVersion | (kHeaderBytes << 16);
+    h[2] = (P.raw ? 1u : (pa.V ? 2u : 0u)) | (pa.rank << 8) | (pa.log2seg << 16) | (pa.T << 24);
+    h[3] = pa.B;
+    for (int a = 0; a < 4; ++a) {
+        h[4 + 2 * a] = (uint32_t)pa.dims[a];
+        h[5 + 2 * a] = (uint32_t)(pa.dims[a] >> 32);
+    }
+    const uint64_t u64s[8] = {pa.n, 0, P.m, P.pb, kHeaderBytes, P.po, P.oi, P.ov};
+    h[12] = (uint32_t)u64s[0];
+    h[13] = (uint32_t)(u64s[0] >> 32);
+    h[14] = __float_as_uint(info->eb_f);
+    h[15] = __float_as_uint(info->s);
+    h[16] = __float_as_uint(info->r);
+    h[17] = (!P.raw && pa.center) ? 1u : 0u; /* flags: bit 0 = centered */
+    for (int a = 2; a < 8; ++a) {
+        h[18 + 2 * (a - 2)] = (uint32_t)u64s[a];
+        h[19 + 2 * (a - 2)] = (uint32_t)(u64s[a] >> 32);
+    }
+    h[30] = (uint32_t)P.tot;
+    h[31] = (uint32_t)(P.tot >> 32);
+}
+
 /* Compress finalize: totals -> stream layout, RAW decision, header. */
 __device__ __forceinline__ void scan_compress_body(PlanArgs pa, Workspace ws,
                                                    uint8_t *out, uint64_t cap,
@@ -888,66 +971,14 @@ __device__ __forceinline__ void scan_compress_body(PlanArgs pa, Workspace ws,
     __shared__ uint32_t s_hdr[32];
     __shared__ uint32_t s_fits;
     DevInfo *info = ws.info;
-    /* the bound's fields, read before the scan so that their loads overlap it */
+    /* the bound's validity, read before the scan so that its load overlaps it */
     const uint32_t valid0 = info->valid;
-    const float eb0 = info->eb_f, s0 = info->s, r0 = info->r;
     uint32_t tot[2];
     block_scan2(ws.group_words, ws.group_esc, ws.gpre_words, ws.gpre_esc, pa.ngroups, tot);
     if (threadIdx.x == 0) {
-        const uint64_t n = pa.n;
-        const uint64_t S = tot[0], m = tot[1];
-        const uint64_t raw_total = kHeaderBytes + align16(4 * n);
-        const uint64_t payload_off = kHeaderBytes + pa.wsec + table_bytes(pa.ngroups) + pa.msec;
-        const uint64_t lossy_total = payload_off + align16(4 * S) + 2 * align16(4 * m);
-        const bool valid = valid0 != 0;
-        const bool raw = !valid || m > pa.side_max || lossy_total > raw_total;
-        uint64_t f_m, f_pb, f_po, f_oi, f_ov, f_tot;
-        if (raw) {
-            f_m = 0; f_pb = 4 * n; f_po = kHeaderBytes;
-            f_oi = raw_total; f_ov = raw_total; f_tot = raw_total;
-        } else {
-            f_m = m; f_pb = 4 * S; f_po = payload_off;
-            f_oi = payload_off + align16(4 * S);
-            f_ov = f_oi + align16(4 * m);
-            f_tot = f_ov + align16(4 * m);
-        }
-        const uint32_t fits = f_tot <= cap ? 1u : 0u;
-        info->mode = raw ? 1u : (pa.V ? 2u : 0u);
-        info->m = f_m;
-        info->payload_words = f_pb / 4;
-        info->payload_off = f_po;
-        info->oidx_off = f_oi;
-        info->oval_off = f_ov;
-        info->total = f_tot;
-        info->fits = fits;
-        s_fits = fits;
-        if (result != nullptr) {
-            /* the caller's result record: length (or required capacity), then the status */
-            result[0] = f_tot;
-            result[1] = fits ? 0u : 3u;
-        }
-        uint32_t *h = s_hdr;
-        h[0] = kMagic;
-        h[1] = kVersion | (kHeaderBytes << 16);
-        h[2] = (raw ? 1u : (pa.V ? 2u : 0u)) | (pa.rank << 8) | (pa.log2seg << 16) | (pa.T << 24);
-        h[3] = pa.B;
-        for (int a = 0; a < 4; ++a) {
-            h[4 + 2 * a] = (uint32_t)pa.dims[a];
-            h[5 + 2 * a] = (uint32_t)(pa.dims[a] >> 32);
-        }
-        const uint64_t u64s[8] = {n, 0, f_m, f_pb, kHeaderBytes, f_po, f_oi, f_ov};
-        h[12] = (uint32_t)u64s[0];
-        h[13] = (uint32_t)(u64s[0] >> 32);
-        h[14] = __float_as_uint(eb0);
-        h[15] = __float_as_uint(s0);
-        h[16] = __float_as_uint(r0);
-        h[17] = (!raw && pa.center) ? 1u : 0u; /* flags: bit 0 = centered */
-        for (int a = 2; a < 8; ++a) {
-            h[18 + 2 * (a - 2)] = (uint32_t)u64s[a];
-            h[19 + 2 * (a - 2)] = (uint32_t)(u64s[a] >> 32);
-        }
-        h[30] = (uint32_t)f_tot;
-        h[31] = (uint32_t)(f_tot >> 32);
+        const StreamPlace P = place_stream(pa, tot[0], tot[1], valid0 != 0, cap);
+        publish_stream(pa, P, info, result, s_hdr);
+        s_fits = P.fits;
     }
     __syncthreads();
     if (s_fits && threadIdx.x < 32) reinterpret_cast<uint32_t *>(out)[threadIdx.x] = s_hdr[threadIdx.x];
@@ -1202,12 +1233,10 @@ template <bool STRIDED>
 __device__ __forceinline__ void compact_body(const float *__restrict__ x,
                                              PlanArgs pa, Workspace ws,
                                              uint8_t *__restrict__ out,
-                                             const uint8_t *__restrict__ widths_src) {
+                                             const uint8_t *__restrict__ widths_src,
+                                             const StreamPlace &P, uint32_t grp, uint32_t gw, uint32_t ge) {
     constexpr int CPG = kEncChunksPerGroup;
     const uint32_t lane = threadIdx.x & 63;
-    const uint32_t grp = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    if (grp >= pa.ngroups) return;
-    const DevInfo *info = ws.info;
     /* every small input of the group up front, in one round of loads */
     uint32_t words[CPG], escs[CPG];
 #pragma unroll
@@ -1216,11 +1245,9 @@ __device__ __forceinline__ void compact_body(const float *__restrict__ x,
         words[k] = ck < pa.nchunks ? ws.chunk_words[ck] : 0u;
         escs[k] = ck < pa.nchunks ? ws.chunk_esc[ck] : 0u;
     }
-    const uint32_t gw = group_prefix(ws.gpre_words, ws.group_words, grp);
-    const uint32_t ge = group_prefix(ws.gpre_esc, ws.group_esc, grp);
-    const uint32_t fits = info->fits, mode = info->mode;
-    const uint64_t payload_off = info->payload_off, oidx_off = info->oidx_off, oval_off = info->oval_off;
-    const uint64_t m = info->m, payload_words = info->payload_words;
+    const uint32_t fits = P.fits, mode = P.raw ? 1u : 0u;
+    const uint64_t payload_off = P.po, oidx_off = P.oi, oval_off = P.ov;
+    const uint64_t m = P.m, payload_words = P.pb / 4;
     if (!fits) return;
     const uint64_t n = pa.n;
     const uint64_t gbase = (uint64_t)grp * CPG * kEncChunk;
@@ -1349,8 +1376,94 @@ template <bool STRIDED>
 __global__ __launch_bounds__(kBlockThreads) void compact_kernel(Fields fs, PlanArgs pa, Workspace ws) {
     const uint32_t f = blockIdx.y;
     const Workspace w = lane_ws(ws, f, fs.ws_stride);
+    const uint32_t grp = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    if (grp >= pa.ngroups) return;
+    const uint32_t gw = group_prefix(w.gpre_words, w.group_words, grp);
+    const uint32_t ge = group_prefix(w.gpre_esc, w.group_esc, grp);
     compact_body<STRIDED>(reinterpret_cast<const float *>(pick(fs.src, f)), pa, w, pick(fs.dst, f),
-                          (fs.wdirect >> f) & 1u ? nullptr : w.widths);
+                          (fs.wdirect >> f) & 1u ? nullptr : w.widths, place_from_info(w.info), grp, gw, ge);
+}
+
+/* Exclusive prefixes of a[0..ng) and b[0..ng), ng <= kFoldGroups, into LDS (s_a, s_b), and their
+ * totals (every thread): thread t sums items 8t .. 8t+7 (two 128-bit loads of each array, which
+ * are 256-byte aligned), a wave scan and the four waves' totals through LDS give its start. */
+constexpr uint32_t kFoldGroups = kBlockThreads * 8;
+__device__ __forceinline__ void fold_scan(const uint32_t *__restrict__ a, const uint32_t *__restrict__ b,
+                                          uint32_t ng, uint32_t *s_a, uint32_t *s_b, uint32_t &ta, uint32_t &tb) {
+    __shared__ uint32_t s_t[kWavesPerBlock][2];
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t i0 = 8 * tid;
+    uint32_t va[8], vb[8];
+    if (i0 + 8 <= ng) {
+        const uint4 a0 = reinterpret_cast<const uint4 *>(a + i0)[0], a1 = reinterpret_cast<const uint4 *>(a + i0)[1];
+        const uint4 b0 = reinterpret_cast<const uint4 *>(b + i0)[0], b1 = reinterpret_cast<const uint4 *>(b + i0)[1];
+        va[0] = a0.x; va[1] = a0.y; va[2] = a0.z; va[3] = a0.w; va[4] = a1.x; va[5] = a1.y; va[6] = a1.z; va[7] = a1.w;
+        vb[0] = b0.x; vb[1] = b0.y; vb[2] = b0.z; vb[3] = b0.w; vb[4] = b1.x; vb[5] = b1.y; vb[6] = b1.z; vb[7] = b1.w;
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            va[k] = i0 + k < ng ? a[i0 + k] : 0u;
+            vb[k] = i0 + k < ng ? b[i0 + k] : 0u;
+        }
+    }
+    uint32_t sa = 0, sb = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        sa += va[k];
+        sb += vb[k];
+    }
+    const uint32_t ia = wave_incl_scan(sa), ib = wave_incl_scan(sb);
+    if (lane == 63) {
+        s_t[wave][0] = ia;
+        s_t[wave][1] = ib;
+    }
+    __syncthreads();
+    uint32_t ea = ia - sa, eb = ib - sb;
+    ta = tb = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < (uint32_t)kWavesPerBlock; ++w) {
+        const uint32_t xa = s_t[w][0], xb = s_t[w][1];
+        ea += w < wave ? xa : 0u;
+        eb += w < wave ? xb : 0u;
+        ta += xa;
+        tb += xb;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        if (i0 + k < ng) {
+            s_a[i0 + k] = ea;
+            s_b[i0 + k] = eb;
+        }
+        ea += va[k];
+        eb += vb[k];
+    }
+    __syncthreads();
+}
+
+/* K3 + K4 for fields of at most kFoldGroups groups (2^24 values): every compaction workgroup
+ * scans the group sums itself (fold_scan) and places the stream (place_stream), the same in
+ * each, and workgroup 0 writes the placement, the result record and the header, so the
+ * single-workgroup scan launch is not needed. */
+template <bool STRIDED>
+__global__ __launch_bounds__(kBlockThreads) void compact_scan_kernel(Fields fs, PlanArgs pa, Workspace ws) {
+    __shared__ uint32_t s_pw[kFoldGroups], s_pe[kFoldGroups];
+    __shared__ uint32_t s_hdr[32];
+    const uint32_t f = blockIdx.y;
+    const Workspace w = lane_ws(ws, f, fs.ws_stride);
+    uint8_t *out = pick(fs.dst, f);
+    const uint32_t valid = w.info->valid;
+    uint32_t S, M;
+    fold_scan(w.group_words, w.group_esc, pa.ngroups, s_pw, s_pe, S, M);
+    const StreamPlace P = place_stream(pa, S, M, valid != 0, pick(fs.bytes, f));
+    if (blockIdx.x == 0) {
+        if (threadIdx.x == 0) publish_stream(pa, P, w.info, pick(fs.result, f), s_hdr);
+        __syncthreads();
+        if (P.fits && threadIdx.x < 32) reinterpret_cast<uint32_t *>(out)[threadIdx.x] = s_hdr[threadIdx.x];
+    }
+    const uint32_t grp = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    if (grp >= pa.ngroups) return;
+    compact_body<STRIDED>(reinterpret_cast<const float *>(pick(fs.src, f)), pa, w, out,
+                          (fs.wdirect >> f) & 1u ? nullptr : w.widths, P, grp, s_pw[grp], s_pe[grp]);
 }
 
 /* ---- K7: fused decode ------------------------------------------------------------------------ */
@@ -1750,6 +1863,18 @@ hipError_t launch_compact(const Fields &fs, uint32_t nf, const PlanArgs &pa, con
         eblc_launch(compact_kernel<true>, grid, block, 0, stream, fs, pa, ws);
     else
         eblc_launch(compact_kernel<false>, grid, block, 0, stream, fs, pa, ws);
+    return hipGetLastError();
+}
+
+bool compact_folds_scan(const PlanArgs &pa) { return pa.ngroups <= kFoldGroups; }
+
+hipError_t launch_compact_scan(const Fields &fs, uint32_t nf, const PlanArgs &pa, const Workspace &ws,
+                               hipStream_t stream) {
+    const dim3 grid((pa.ngroups + kWavesPerBlock - 1) / kWavesPerBlock, nf), block(kBlockThreads);
+    if (pa.lay.strided)
+        eblc_launch(compact_scan_kernel<true>, grid, block, 0, stream, fs, pa, ws);
+    else
+        eblc_launch(compact_scan_kernel<false>, grid, block, 0, stream, fs, pa, ws);
     return hipGetLastError();
 }
 

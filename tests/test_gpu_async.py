@@ -184,7 +184,8 @@ def test_kernel_time_records_cover_every_lane(env):
         assert binding.eblc_decompress_batch(plan, outs, ys) == binding.EBLC_OK
         rec = binding.eblc_plan_kernel_times(plan)
         names = [r[0] for r in rec]
-        assert names == ["range", "encode", "scan", "compact", "decode", "patch"]
+        # a field of at most 2048 groups scans its group sums inside the compaction
+        assert names == ["range", "encode", "compact", "decode", "patch"]
         assert all(cnt == 2 and ms > 0 for _, ms, cnt in rec)  # groups of 3 and 2 fields
         assert binding.eblc_plan_kernel_times(plan) == []       # records cleared by the read
         assert binding.eblc_plan_set_profiling(plan, 3) == binding.EBLC_OK
