@@ -666,7 +666,8 @@ eblc_status eblc_compress(eblc_plan_t *plan, const float *in, void *out, size_t 
     DeviceGuard guard(plan->device);
     if (!guard.ok) return EBLC_DEVICE_ERROR;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    /* the scan kernel writes the result record straight into the plan's pinned host slot */
+    /* the compress tail (scan, or the compaction that scans for itself) writes the result record
+     * straight into the plan's pinned host slot */
     plan->host_result->compressed_bytes = 0;
     plan->host_result->status = EBLC_DEVICE_ERROR;
     void *outs[1] = {out};
