@@ -23,10 +23,14 @@
  * of the V plane words, then the nonzero ones).
  *
  * Stream (little-endian, every section 16-byte aligned, pad bytes zero):
- *   [0,128)            header (magic "EBLC", version 1, mode, rank, dims, n, eb, step,
+ *   [0,128)            header (magic "EBLC", version 2, mode, rank, dims, n, eb, step,
  *                      outlier count, section offsets, total length)
  *   [128, ...)         bitpack coder (mode 0): one width byte per 32-value segment
  *                      (nseg = ceil(n/32)); chunk coder (mode 2): one u32 word count per chunk
+ *   offset table       one u32 per group of 8192 values after the first: the payload words
+ *                      before that group (ceil(n/8192) - 1 entries), so that a decoder finds
+ *                      any group's payload without a scan of the sizes
+ *   block means        centered streams only (center=1): one i32 per block
  *   payload            bitpack: sum(widths) u32 words; chunk: each chunk's bitmap and nonzero
  *                      plane words, chunk after chunk (the last chunk padded with zero codes)
  *   outlier indices    m x u32, strictly ascending
@@ -142,8 +146,10 @@ int eblc_abi_version(void);
  *                                     launch, each in a workspace of its own (the workspace
  *                                     grows k-fold); the streams are identical for every k
  *            Unknown keys, repeated keys, NaN or negative values -> INVALID_ARGUMENT.
- *   plan_out receives the plan.  The plan allocates its whole workspace here (about 4 n +
- *            n/8 bytes plus small arrays) and nothing per call.
+ *   plan_out receives the plan.  The plan allocates its whole workspace here and nothing
+ *            per call: about 4.4 n bytes per lane (the encoder's payload slots 4 n, its
+ *            escape staging n/4, escape masks n/8 and size staging n/32), plus 4 n / B for
+ *            the block means and small arrays.
  * INVALID_ARGUMENT also when the field's largest payload would reach 2^32 words (the scans
  * count in 32 bits): 32 words per 32-value segment for the bitpack coder, so n <= 2^32 - 32;
  * for the chunk coder ceil(n / V) (V + V / 32) < 2^32.  DEVICE_ERROR when no HIP device can be
