@@ -26,8 +26,9 @@
  *    and mbcnt the place of each nonzero word.
  * A 1024-value chunk is half a wave; a 4096-value chunk spans two waves of a workgroup, which
  * trade their per-plane word counts through LDS.  Decoding runs the steps backwards (the
- * transpose is its own inverse): scalar loads read the bitmap plane by plane, each lane loads
- * its group's nonzero words under it, unfolds the zigzag on planes, transposes, and sums its
+ * transpose is its own inverse): one vector load brings the chunk's bitmap words (lane k, word
+ * k), readlane hands each plane's bitmap to the whole wave, each lane loads its group's nonzero
+ * words under it, unfolds the zigzag on planes, transposes, and sums its
  * differences after a wave scan of the lane totals; the values go back through LDS in the same
  * swizzled order for coalesced stores.
  */

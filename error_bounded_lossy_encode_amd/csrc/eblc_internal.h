@@ -18,7 +18,8 @@
  * inside a chunk at a 32-value boundary and cross chunk ends.  An encode chunk that does not
  * start a block takes its first prediction from the code of the value before it; a decode chunk
  * that does not sums the deltas of the block's segments before it.  The only other cross-wave
- * dependency is the exclusive scan of payload sizes and outlier counts.
+ * dependency is the exclusive scan of payload sizes and outlier counts on compress; decompress
+ * has none, since the stream's offset table gives each group's payload start.
  */
 #ifndef EBLC_INTERNAL_H
 #define EBLC_INTERNAL_H

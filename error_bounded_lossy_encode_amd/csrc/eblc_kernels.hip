@@ -9,7 +9,9 @@
  * ("Inverse declaration").  Like the chunk encoder of "nvrtc_chunk_fusion.h File
  * Reference" (launchNvrtcChunkFusedEncode), the encode kernel fills a fixed-size scratch slot
  * and a size per chunk, and a separate scan and pack tail compacts the slots; unlike it, the
- * outlier list is written in index order by its own kernel, so the stream is deterministic.
+ * compaction writes the outlier list in index order, so the stream is deterministic.  The
+ * stream also carries an offset table (the payload words before each group of 8192 values),
+ * so the decoder needs no scan: it decodes, then a small kernel patches the outliers.
  *
  * gfx950 mapping: one wave64 owns a 2048-value chunk; a tile of 256 values is one 128-bit
  * load per lane (4 consecutive values); all intermediates stay in VGPRs; cross-lane work uses
@@ -1225,10 +1227,12 @@ constexpr uint32_t kSmallChunkWords = 4 * kWave;
 /* One wave per group of kEncChunksPerGroup encode chunks, kWavesPerBlock groups per workgroup.  A
  * group of small chunks -- most groups of a well-compressed field -- issues the loads of all four
  * chunks together (copy_group_payload), so it waits for one memory latency; a group with a larger
- * chunk copies its chunks one after another (copy_chunk_payload), with their outliers.  (A wave
- * per chunk left every wave waiting on its own chain of loads, twice the chains in all on the
- * 512^3 field.)  In RAW mode the wave copies the group's input values instead.  The last group
- * also zeroes the pads after the payload and after the outlier sections. */
+ * chunk copies its chunks in rounds, each round's loads issued before the previous round's
+ * stores (copy_chunks_pipelined).  (A wave per chunk left every wave waiting on its own chain of
+ * loads, twice the chains in all on the 512^3 field.)  Then the group's outliers, its
+ * offset-table entry, its share of the size section when it was staged and its block means.  In
+ * RAW mode the wave copies the group's input values instead.  The last group also zeroes the
+ * pads after the payload, the outlier sections and the offset table. */
 template <bool STRIDED>
 __device__ __forceinline__ void compact_body(const float *__restrict__ x,
                                              PlanArgs pa, Workspace ws,
