@@ -130,6 +130,29 @@ def c5_snapshot(i: int, N: int = 256, rel: float = 1e-6, device: str = "cpu"):
     return x, [N, N, N], f"rel={_fmt(rel)};block=256;outlier_log2=30"
 
 
+def largest_field(n: int, device: str = "cpu", piece: int = 1 << 27):
+    """A 1-D field of n values, up to the largest a plan takes (just under 2^32), for the
+    maximum-size test: sines of periods 8191 and 65521 (amplitudes 1 and 0.5) and 0.01 sin(0.7 i),
+    computed in float64 from each value's index and cast to float32, with +-1e30 (values that
+    escape) at indices 3, 2^31 - 1, 2^31, 2^31 + 7, n - 2 and n - 1 (those below n).  Built on
+    `device` (a torch device) in pieces of `piece` values; no random draws."""
+    import torch
+
+    x = torch.empty(n, dtype=torch.float32, device=device)
+    for a in range(0, n, piece):
+        b = min(n, a + piece)
+        i = torch.arange(a, b, dtype=torch.int64, device=device)
+        v = torch.sin((i % 8191).to(torch.float64) * (2 * math.pi / 8191))
+        v += 0.5 * torch.sin((i % 65521).to(torch.float64) * (2 * math.pi / 65521))
+        v += 0.01 * torch.sin(i.to(torch.float64) * 0.7)
+        x[a:b] = v.to(torch.float32)
+        del i, v
+    for k, idx in enumerate([3, (1 << 31) - 1, 1 << 31, (1 << 31) + 7, n - 2, n - 1]):
+        if 0 <= idx < n:
+            x[idx] = 1e30 if k % 2 == 0 else -1e30
+    return x
+
+
 # ---------------------------------------------------------------------------------------
 # Small adversarial inputs for fuzzing (tiny n, every special value).
 # ---------------------------------------------------------------------------------------
