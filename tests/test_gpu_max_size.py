@@ -1,10 +1,12 @@
-"""The largest field a plan takes, coded on the GPU and compared with the oracle byte for byte.
+"""The largest fields a plan takes, coded on the GPU and compared with the oracle byte for byte.
 
-A plan refuses a field whose payload could reach 2^32 words, the most the scans count; for the
-bitpack coder that leaves n <= 2^32 - 32. This test codes a 1-D field of 2^32 - 4133 values
-(16 GiB: 524288 groups of 8192 values and a ragged tail) with escapes at both ends and around
-index 2^31. Every 64-bit offset, 32-bit index and grid size on the path then meets its largest
-value.
+A plan refuses a field whose payload could reach 2^32 words, the most the scans count. For the
+bitpack coder that leaves n <= 2^32 - 32; for the chunk coder with V-value chunks,
+ceil(n / V) (V + V/32) < 2^32. These tests code 1-D fields just under those limits, with ragged
+tails: 2^32 - 4133 values (16 GiB, 524288 groups of 8192 values) for the bitpack coder, plain and
+with Lorenzo centering, and 2033601 * 2048 - 777 values for the chunk coder at 8 KiB chunks. The
+fields carry escapes at both ends and around index 2^31. Every 64-bit offset, 32-bit index and
+grid size on the path then meets its largest value.
 
 The stream must equal the oracle's byte for byte ("Pipeline Specialization Internals",
 validation requirements: byte-identical compress). The oracle codes the field in 256
@@ -26,8 +28,13 @@ from helpers import CANARY, first_difference, oracle_threads, parse_options
 
 pytestmark = pytest.mark.gpu
 
-N = (1 << 32) - 4133
-OPTS = "abs=1e-3;block=256;outlier_log2=15"
+N_BITPACK = (1 << 32) - 4133
+N_CHUNK = ((1 << 32) - 1) // 2112 * 2048 - 777
+CASES = [
+    ("abs=1e-3;block=256;outlier_log2=15", N_BITPACK),
+    ("abs=1e-3;block=256;outlier_log2=15;center=1", N_BITPACK),
+    ("coder=chunk;chunk_bytes=8192;abs=1e-3;outlier_log2=15", N_CHUNK),
+]
 PIECES = 256
 
 
@@ -39,9 +46,12 @@ def env():
     return binding, torch
 
 
-def test_largest_field_matches_oracle(env):
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_largest_field_matches_oracle(env, case):
     import psutil
     binding, torch = env
+    OPTS, N = CASES[case]
+    torch.cuda.empty_cache()
     free_dev, _ = torch.cuda.mem_get_info()
     if free_dev < 80 * 2**30 or psutil.virtual_memory().available < 48 * 2**30:
         pytest.skip("needs about 60 GB of device memory and 25 GB of free host memory")
@@ -51,11 +61,11 @@ def test_largest_field_matches_oracle(env):
     o = parse_options(OPTS, N)
     threads = oracle_threads()
     print(f"[max-size] oracle on {PIECES} pieces, {threads} threads", flush=True)
-    ok, _, bounds, streams = shards.code_pieces(x, o["rel"], o["eps"], o["B"], o["T"], False, None,
+    ok, _, bounds, streams = shards.code_pieces(x, o["rel"], o["eps"], o["B"], o["T"], o["center"], o["V"],
                                                 PIECES, threads)
     assert ok
-    ref = shards.join(x, [N], o["T"], o["B"], o["side_max"], False, None, bounds, streams)
-    assert ref is not None and int(ref[8]) == 0, "the field must be coded, not copied"
+    ref = shards.join(x, [N], o["T"], o["B"], o["side_max"], o["center"], o["V"], bounds, streams)
+    assert ref is not None and int(ref[8]) != 1, "the field must be coded, not copied"
     del x
     st, plan = binding.eblc_plan_create([N], OPTS, 0)
     assert st == binding.EBLC_OK, binding.eblc_status_string(st)
@@ -86,4 +96,5 @@ def test_largest_field_matches_oracle(env):
     print("[max-size] reconstruction against the oracle decoder", flush=True)
     with ThreadPoolExecutor(max_workers=threads) as ex:
         bad = [k for k, good in enumerate(ex.map(piece_ok, range(len(bounds)))) if not good]
+    del y
     assert not bad, f"pieces {bad[:8]} differ (of {len(bounds)}, starting at {[bounds[k][0] for k in bad[:4]]})"
