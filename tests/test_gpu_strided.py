@@ -2,7 +2,9 @@
 padding reads its input and writes its reconstruction through those strides.
 
 The stream of a padded field must equal the oracle's stream of the packed interior, and
-decompression must write exactly the interior elements, leaving the padding untouched.
+decompression must write exactly the interior elements, leaving the padding untouched: on small
+fields of every rank, and on the 512^3 snapshot at full size in the 4- and 3-element halos the
+benchmark times.
 """
 import numpy as np
 import pytest
@@ -147,5 +149,46 @@ def test_padded_layout_raw_fallback(env):
         ybuf = yd.cpu().numpy()
         yview = np.lib.stride_tricks.as_strided(ybuf, shape=dims, strides=[4 * s for s in strides])
         assert np.array_equal(np.ascontiguousarray(yview).view(np.uint32), interior.view(np.uint32))
+    finally:
+        binding.eblc_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("halo", [4, 3])
+def test_full_size_field_in_a_halo(env, halo):
+    """The 512^3 Ricker snapshot stored with a `halo`-element halo on every side, the layout the
+    benchmark's --halo option times. A 4-element halo keeps 128-bit access, since every stride
+    is a multiple of 4 and the interior starts 16-byte aligned. A 3-element halo does neither, so
+    the whole path takes 4-byte accesses. The stream must equal the oracle's stream of the packed
+    interior, the reconstruction must equal the oracle decoder's, and the halo must stay
+    untouched."""
+    import oracle.shards as shards
+    from helpers import oracle_reference
+    binding, torch = env
+    x, dims, opts = synth.c3_ricker(512, device="cuda")
+    print(f"[halo] 512^3 in a {halo}-element halo: {opts}", flush=True)
+    pdims = [d + 2 * halo for d in dims]
+    strides = [int(np.prod(pdims[a + 1:])) for a in range(3)]
+    offset = sum(halo * s for s in strides)
+    span = 1 + sum((d - 1) * s for d, s in zip(dims, strides))
+    buf = torch.full((offset + span + 4,), float(SENTINEL), dtype=torch.float32, device="cuda")
+    torch.as_strided(buf, dims, strides, offset).copy_(x.reshape(dims))
+    ref, ref_dec = oracle_reference(oracle, shards, x.cpu().numpy(), dims, opts)
+    st, plan = binding.eblc_plan_create(dims, opts, 0, strides=strides)
+    assert st == binding.EBLC_OK, binding.eblc_status_string(st)
+    try:
+        maxb = binding.eblc_max_compressed_bytes(plan)
+        out = torch.full((maxb,), CANARY, dtype=torch.uint8, device="cuda")
+        st, nb = binding.eblc_compress(plan, buf[offset:], out)
+        assert st == binding.EBLC_OK and nb == ref.size, (st, nb, ref.size)
+        assert np.array_equal(out[:nb].cpu().numpy(), ref)
+        ybuf = torch.full_like(buf, float(SENTINEL))
+        assert binding.eblc_decompress(plan, out, nb, ybuf[offset:]) == binding.EBLC_OK
+        assert binding.eblc_plan_status(plan) == binding.EBLC_OK
+        y = torch.as_strided(ybuf, dims, strides, offset).contiguous().reshape(-1)
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), ref_dec.view(np.uint32))
+        # the halo (every element outside the interior) still holds the sentinel
+        inside = torch.zeros(ybuf.numel(), dtype=torch.bool, device="cuda")
+        torch.as_strided(inside, dims, strides, offset).fill_(True)
+        assert bool((ybuf[~inside] == float(SENTINEL)).all())
     finally:
         binding.eblc_plan_destroy(plan)
